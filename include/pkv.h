@@ -1,0 +1,266 @@
+/*
+ * pkv.h — C ABI of libpkv: a paged KV cache and decode-phase PagedAttention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources the operations follow (cited by page title and section):
+ *   [FP8-128K] "Optimización de KV Cache con PagedAttention y Cuantización FP8
+ *              para Contextos Largos (128K)" (thecalata.com)
+ *   [PRIMER-8] "LLM Primer VI, Capítulo 8 — Gestión de caché KV de nueva
+ *              generación" (actionbridge.io)
+ *   [KV-SLOW]  "KV Cache y PagedAttention: por qué se reduce la velocidad de tu
+ *              servidor LLM" (gyaansetu.com, repost of a dev.to article)
+ *   [GLOSSARY] "PagedAttention y Gestión de KV-Cache" (gotburnout.io glossary)
+ *
+ * What the library computes
+ *   The KV cache is cut into fixed 16-token blocks held in one flat pool per
+ *   tensor (K and V); the physical blocks of a sequence need not be adjacent,
+ *   and a per-sequence block table maps logical block j to a physical block id
+ *   ([FP8-128K] §3; [PRIMER-8] §8.1; [GLOSSARY] §2 block-table figure).
+ *   The decode kernel takes that table as an extra input and gathers keys and
+ *   values through it instead of slicing a contiguous slab ([PRIMER-8] §8.1).
+ *   New K/V rows can be stored as fp16 or converted on the fly to 8-bit
+ *   floating point E4M3, halving the cache ([FP8-128K] §4, §6.2, §8).
+ *   One query token per sequence is decoded per call ([PRIMER-8], closing
+ *   section on Chapter 9; [KV-SLOW] "¿Qué es el KV cache?").
+ *
+ * Conventions for every function below
+ *   - Status codes: PKV_OK (0) or a negative pkv_status; nothing throws.
+ *   - Device pointers are caller-owned HIP device memory; the library never
+ *     allocates device memory.  "stream" is a hipStream_t passed as void*
+ *     (NULL = the null stream).  Device calls are asynchronous on that stream;
+ *     argument errors are detected on the host before anything is launched.
+ *   - Contents of device tables (block ids, lengths, slots) cannot be checked
+ *     on the host without a copy; kernels never access memory outside the
+ *     buffers described by the sizes passed in (out-of-range ids are skipped),
+ *     but the numerical result for invalid table contents is unspecified.
+ *   - Host handles (pkv_pool) are not thread-safe; the caller serialises.
+ *
+ * Cache layout (fixed by this library; the pages do not prescribe one)
+ *   block_size BS = 16 tokens, head_dim D = 128, element size e = 2 (fp16) or
+ *   1 (FP8).  Both pools are [num_blocks][num_kv_heads][BS*D] elements, so the
+ *   tile of one (block, kv head) is BS*D*e contiguous bytes (4 KiB fp16,
+ *   2 KiB FP8).  Inside a tile the element of token t (0..15) and channel
+ *   d (0..127) sits at element offset
+ *     K:  (d / x) * (BS * x) + t * x + (d % x),        x = 16 / e
+ *     V:  (n / v) * (64 * x) + ((t / 4) * 16 + d % 16) * x + (n % v) * 4 + t % 4,
+ *         n = d / 16, v = x / 4
+ *   i.e. both tiles are stored in the order the gfx950 matrix-core operands
+ *   consume them, so one wavefront reads a whole tile with 16-byte loads that
+ *   cover 1 KiB of contiguous memory per instruction.
+ *   A token's slot is phys_block * 16 + position % 16.
+ *
+ * FP8 encoding (PKV_FP8_E4M3FN)
+ *   OCP E4M3FN: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits,
+ *   exponent 0 subnormal, S.1111.111 NaN, no infinities, largest finite 448.
+ *   code = E4M3(u) with u = x / scale computed as a correctly rounded fp32
+ *   division; rounding to nearest, ties to the even code; finite values at or
+ *   above 448 in magnitude (and infinities) saturate to +-448; NaN maps to
+ *   0x7F | sign.  Decoding is code_value * scale.  One fp32 scale per pool
+ *   (a per-tensor scale), supplied by the caller ([FP8-128K] §8 describes the
+ *   dynamic and the calibrated ways of obtaining it).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_BLOCK_SIZE 16
+#define PKV_HEAD_DIM 128
+#define PKV_MAX_GQA_GROUP 16
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,    /* null/misaligned pointer, bad size or count */
+  PKV_ERR_UNSUPPORTED = -2,    /* block_size != 16, head_dim != 128, group > 16, unknown dtype */
+  PKV_ERR_NO_FREE_BLOCKS = -3, /* pool exhausted; state unchanged ([FP8-128K] §6.1) */
+  PKV_ERR_HIP = -4,            /* a HIP launch failed */
+  PKV_ERR_WORKSPACE = -5,      /* decode workspace smaller than required */
+  PKV_ERR_BAD_HANDLE = -6,     /* unknown or freed sequence id, null pool */
+  PKV_ERR_REFCOUNT = -7        /* refcount would underflow (double free) */
+};
+
+typedef enum { PKV_F16 = 0, PKV_FP8_E4M3FN = 1 } pkv_dtype;
+
+/* Geometry of one K pool and its V pool (they share it). */
+typedef struct {
+  int32_t num_blocks;   /* physical blocks in the pool */
+  int32_t block_size;   /* tokens per block; must be 16 for device calls */
+  int32_t num_kv_heads; /* KV heads stored per block */
+  int32_t head_dim;     /* must be 128 for device calls */
+  int32_t dtype;        /* pkv_dtype */
+} pkv_cache_layout;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pkv_status_string(pkv_status status);
+
+/* ------------------------------------------------------------------ sizing */
+
+/* Bytes of KV cache one token occupies across a model:
+ * 2 (K and V) * n_layers * n_kv_heads * d_head * elem_bytes
+ * ([FP8-128K] §2, the sizing formula and its Llama-3.1-70B example).
+ * Returns 0 if any argument is not positive. */
+uint64_t pkv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_head,
+                             int32_t elem_bytes);
+
+/* Bytes of ONE pool (K or V) with this layout; 0 for an invalid layout. */
+uint64_t pkv_pool_bytes(const pkv_cache_layout* layout);
+
+/* Partition length (tokens) the decode will use: `requested` if it is a
+ * positive multiple of 16, else (requested == 0) the library's choice for this
+ * shape; -1 if `requested` is invalid. */
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                  int32_t max_context_len, int32_t requested);
+
+/* Workspace bytes pkv_paged_attention_decode needs for this shape and
+ * partition request (same rules as pkv_decode_partition_size); 0 if the
+ * arguments are invalid. */
+uint64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t max_context_len,
+                                    int32_t partition_size);
+
+/* ------------------------------------------------------------ device calls */
+
+/* Store new K/V rows into their cache slots ([FP8-128K] §4: the new rows are
+ * converted to 8 bits as they are written; [PRIMER-8] §8.1: slots live in
+ * physical blocks named by the block table).
+ *   key, value    device fp16 [num_tokens][num_kv_heads][128], contiguous,
+ *                 16-byte aligned.
+ *   k_pool/v_pool device pools laid out as described at the top of this file.
+ *   slot_mapping  device int64 [num_tokens]; slot = block * 16 + offset;
+ *                 a negative slot means "skip this token"; slots at or beyond
+ *                 num_blocks * 16 are skipped as well.
+ *   k_scale/v_scale  per-tensor scales, used only for PKV_FP8_E4M3FN; must be
+ *                 finite and > 0 then.
+ * fp16 pools receive the 16 input bits unchanged; FP8 pools receive the code
+ * defined under "FP8 encoding" above.  num_tokens == 0 is a no-op. */
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
+                                 void* v_pool, const int64_t* slot_mapping,
+                                 int32_t num_tokens, const pkv_cache_layout* layout,
+                                 float k_scale, float v_scale, void* stream);
+
+/* Decode attention over the paged cache: for each sequence b and query head h,
+ *   out[b][h][:] = softmax_t( sm_scale * q[b][h] . K_t ) . V_t ,  t < L_b,
+ * with K_t, V_t the rows of KV head h / (num_q_heads / num_kv_heads) of the
+ * sequence's tokens in logical order, gathered through block_tables
+ * ([PRIMER-8] §8.1; grouped-query heads as in [FP8-128K] §2, where 8 query
+ * heads share each KV head).  FP8 rows are decoded as code * k_scale or
+ * code * v_scale.  L_b = 0 yields zeros.  The result equals ordinary attention
+ * over the same tokens in logical order, whatever physical blocks hold them.
+ *   out           device fp32 [num_seqs][num_q_heads][128]
+ *   q             device fp16 [num_seqs][num_q_heads][128], 16-byte aligned
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  device int32 [num_seqs]; L_b includes the token being
+ *                 decoded; values are clamped to [0, min(max_context_len,
+ *                 16 * max_blocks_per_seq)].
+ *   max_context_len  host upper bound on every L_b (sizes the workspace).
+ *   num_q_heads must be a multiple of layout->num_kv_heads with a group of at
+ *   most 16.
+ *   partition_size   tokens per split-KV partition: 0 = library choice, else
+ *                 a positive multiple of 16.  Each partition yields a partial
+ *                 (max, sum, unnormalised output) and a second kernel merges
+ *                 them with the log-sum-exp rule.
+ *   workspace     device scratch of at least pkv_decode_workspace_bytes(...)
+ *                 bytes, 256-byte aligned; its contents are internal.
+ * Launches the partition kernel and, when some sequence spans more than one
+ * partition, the merge kernel, both on `stream`. */
+pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_context_len,
+                                      const pkv_cache_layout* layout, float sm_scale,
+                                      float k_scale, float v_scale,
+                                      int32_t partition_size, void* workspace,
+                                      uint64_t workspace_bytes, void* stream);
+
+/* The two halves of pkv_paged_attention_decode, for callers that time or
+ * schedule them separately.  Same arguments and rules; calling
+ * pkv_decode_partitions then pkv_decode_reduce with identical arguments and
+ * workspace is exactly pkv_paged_attention_decode.  pkv_decode_partitions
+ * writes `out` directly for every sequence that fits one partition;
+ * pkv_decode_reduce writes the rest. */
+pkv_status pkv_decode_partitions(float* out, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len, const pkv_cache_layout* layout,
+                                 float sm_scale, float k_scale, float v_scale,
+                                 int32_t partition_size, void* workspace,
+                                 uint64_t workspace_bytes, void* stream);
+pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t max_context_len,
+                             int32_t max_blocks_per_seq, const pkv_cache_layout* layout,
+                             float v_scale, int32_t partition_size, void* workspace,
+                             uint64_t workspace_bytes, void* stream);
+
+/* Copy whole blocks (every KV head, K and V) for copy-on-write: a shared
+ * block is duplicated before a sequence writes into it ([KV-SLOW] "Cómo
+ * PagedAttention soluciona esto"; [GLOSSARY] §3.01).
+ *   src_dst_pairs device int32 [num_pairs][2] (source block, destination
+ *                 block); pairs with an id outside [0, num_blocks) are skipped.
+ * Destinations must be distinct and must not be sources of another pair. */
+pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const pkv_cache_layout* layout,
+                           const int32_t* src_dst_pairs, int32_t num_pairs, void* stream);
+
+/* ------------------------------------------------ host block pool and tables */
+
+/* A pool of physical block ids with reference counts, and the sequences that
+ * map logical blocks onto them ([PRIMER-8] §8.1: fixed blocks in a flat pool,
+ * per-sequence block tables, refcounted sharing; [KV-SLOW]: blocks are taken
+ * only as a sequence grows).  Host memory only; the caller copies block tables
+ * and slots to the device. */
+typedef struct pkv_pool pkv_pool;
+
+/* Create a pool of num_blocks free blocks of block_size tokens.  The free
+ * list is popped in ascending id order if shuffle_seed == 0, else in an order
+ * shuffled with that seed. */
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, uint64_t shuffle_seed,
+                           pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+int32_t pkv_pool_num_blocks(const pkv_pool* pool);
+int32_t pkv_pool_num_free(const pkv_pool* pool);
+/* Fraction of blocks in use, (num_blocks - num_free) / num_blocks: the cache
+ * usage gauge that [FP8-128K] §7 says to watch (alert above 0.90). */
+double pkv_pool_usage(const pkv_pool* pool);
+/* Reference count of a block (number of sequences whose table holds it);
+ * -1 for an id out of range. */
+int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t block);
+
+/* New empty sequence; its id is written to *seq_out. */
+pkv_status pkv_seq_create(pkv_pool* pool, int32_t* seq_out);
+/* New sequence sharing every block of `parent` (each refcount + 1), with the
+ * parent's length: the branching of [PRIMER-8] §8.1 and [GLOSSARY] §3.02. */
+pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* child_out);
+/* Extend a sequence by n_tokens and return their slots.
+ *   slots_out      host int64 [n_tokens] (may be NULL when n_tokens == 0)
+ *   cow_pairs_out  host int32 [2]: if the sequence's partially filled last block
+ *                  is shared, it is replaced by a fresh block and the pair
+ *                  (old, new) is written here for pkv_copy_blocks;
+ *   n_cow_out      number of pairs written (0 or 1).
+ * Blocks are taken from the free list only when a new block is needed.
+ * All or nothing: PKV_ERR_NO_FREE_BLOCKS leaves every state unchanged. */
+pkv_status pkv_seq_append(pkv_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                          int32_t* cow_pairs_out, int32_t* n_cow_out);
+/* Release a sequence: each of its blocks loses one reference and returns to
+ * the free list at zero ([GLOSSARY] §4.02: pages of a cancelled request go
+ * back to the pool at once, else memory leaks). */
+pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
+/* Copy a sequence's block table into out[0..n) with n = number of blocks;
+ * *n_out = n always; PKV_ERR_INVALID_ARG if cap < n (nothing copied). */
+pkv_status pkv_seq_block_table(const pkv_pool* pool, int32_t seq, int32_t* out, int32_t cap,
+                               int32_t* n_out);
+/* Tokens held by a sequence; -1 for an unknown id. */
+int64_t pkv_seq_len(const pkv_pool* pool, int32_t seq);
+/* Number of live sequences. */
+int32_t pkv_pool_num_seqs(const pkv_pool* pool);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,269 @@
+/*
+ * pkv_oracle.c — plain, slow CPU oracle for the paged KV cache hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or constant generator
+ * with the HIP implementation: every formula below is written from the pages
+ * and from the definition of the number format.
+ *
+ * Pages (cited by title and section):
+ *   [FP8-128K] "Optimización de KV Cache con PagedAttention y Cuantización FP8
+ *              para Contextos Largos (128K)"
+ *   [PRIMER-8] "LLM Primer VI, Capítulo 8 — Gestión de caché KV de nueva
+ *              generación"
+ *   [GLOSSARY] "PagedAttention y Gestión de KV-Cache"
+ *
+ * Arithmetic is fp64 throughout; the only narrow values are the ones the
+ * method itself stores (fp16 inputs, FP8 codes, the fp32 quotient x / scale).
+ *
+ * Parity pins (checked by tests/test_oracle_*.py, never by this file):
+ *   - e4m3 decode: all 256 codes against a library view-cast and the format's
+ *     landmark values;
+ *   - e4m3 encode: brute-force nearest-code search; pinned against a library
+ *     cast and against hand-derived tie and saturation cases;
+ *   - write: bytes land at the documented layout offsets (golden table);
+ *   - decode attention: a library scaled-dot-product attention on the
+ *     logically ordered rows, closed forms (one token, equal keys, zero
+ *     query, two tokens), and invariances (block permutation, shared vs
+ *     copied prefix, grouped-query vs repeated heads).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_BS 16 /* tokens per block: [FP8-128K] §3, [PRIMER-8] §8.1 */
+
+/* ------------------------------------------------------------------ numbers */
+
+/* IEEE binary16 bits -> value: 1 sign bit, 5 exponent bits (bias 15), 10
+ * mantissa bits; exponent 0 is subnormal, exponent 31 is inf/NaN. */
+double oracle_f16_to_double(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* m/1024 * 2^-14 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp(1.0 + m / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+/* OCP FP8 E4M3FN code -> value ([FP8-128K] §6.2 and §8 name the E4M3 format;
+ * the variant with largest finite 448 is the one whose scale is amax/448).
+ * Sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 holds the
+ * subnormals m/8 * 2^-6; S.1111.111 is NaN; there are no infinities. */
+double oracle_e4m3_decode(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7)
+    return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Nearest E4M3FN code to the fp32 value u, found by trying every finite
+ * non-negative code (the definition of round-to-nearest written out).  On an
+ * exact tie the code with mantissa LSB 0 (the even code) wins.  Values whose
+ * magnitude is at least the largest finite value 448, and infinities, take
+ * 448 (saturating conversion); NaN takes the NaN code 0x7F with u's sign. */
+uint8_t oracle_e4m3_encode(float u) {
+  uint8_t sign = signbit(u) ? 0x80 : 0x00;
+  if (isnan(u))
+    return (uint8_t)(0x7F | sign);
+  double a = fabs((double)u);
+  if (a >= 448.0)
+    return (uint8_t)(0x7E | sign);
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(oracle_e4m3_decode((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best_d = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(best | sign);
+}
+
+/* Element-wise oracle_e4m3_encode over an array of fp32 values. */
+void oracle_e4m3_encode_array(const float* u, int64_t n, uint8_t* codes) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i)
+    codes[i] = oracle_e4m3_encode(u[i]);
+}
+
+/* The fp32 quotient the write rounds: correctly rounded x / scale.  The
+ * division is done in fp64 and rounded once to fp32; with 53 >= 2*24 + 2 bits
+ * that equals the correctly rounded fp32 quotient. */
+float oracle_quotient(double x, float scale) { return (float)(x / (double)scale); }
+
+/* Encode n fp16 values with one scale (codes[i] = E4M3(x[i] / scale)).  The
+ * encoder depends only on the 16-bit input for a fixed scale, so each of the
+ * 65536 inputs is encoded once by the brute-force search and then looked up;
+ * the result is the same as calling oracle_e4m3_encode per element. */
+void oracle_quantize_f16(const uint16_t* x, int64_t n, float scale, uint8_t* codes) {
+  uint8_t* lut = (uint8_t*)malloc(65536);
+#pragma omp parallel for schedule(static)
+  for (int h = 0; h < 65536; ++h)
+    lut[h] = oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double((uint16_t)h), scale));
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i)
+    codes[i] = lut[x[i]];
+  free(lut);
+}
+
+/* ------------------------------------------------------------------- layout */
+
+/* Element offset of (token t, channel d) inside one (block, kv head) tile of
+ * BS x D elements; x = elements per 16 bytes (16 for FP8, 8 for fp16).  This
+ * is the layout libpkv documents for its pools (the pages prescribe none):
+ * K is chunked by 16-byte runs of channels, V is tiled in groups of 4 tokens
+ * by 16 channels. */
+static int64_t orc_k_offset(int t, int d, int x) {
+  return (int64_t)(d / x) * (ORC_BS * x) + (int64_t)t * x + d % x;
+}
+static int64_t orc_v_offset(int t, int d, int x) {
+  int n = d / 16, v = x / 4;
+  return (int64_t)(n / v) * (64 * x) + (int64_t)((t / 4) * 16 + d % 16) * x + (n % v) * 4 + t % 4;
+}
+int64_t oracle_k_offset(int t, int d, int elem_bytes) { return orc_k_offset(t, d, 16 / elem_bytes); }
+int64_t oracle_v_offset(int t, int d, int elem_bytes) { return orc_v_offset(t, d, 16 / elem_bytes); }
+
+/* Byte address of element (block, kv head, t, d) in a pool. */
+static int64_t orc_addr(int is_v, int64_t block, int h, int t, int d, int Hkv, int D, int e) {
+  int x = 16 / e;
+  int64_t tile = (block * Hkv + h) * (int64_t)(ORC_BS * D);
+  int64_t within = is_v ? orc_v_offset(t, d, x) : orc_k_offset(t, d, x);
+  return (tile + within) * e;
+}
+
+/* Read one cached element as a real number: fp16 bits widened, FP8 code
+ * decoded and multiplied by the tensor's scale ([FP8-128K] §4 and §8). */
+static double orc_load(const uint8_t* pool, int is_v, int64_t block, int h, int t, int d, int Hkv,
+                       int D, int fp8, double scale) {
+  if (fp8)
+    return oracle_e4m3_decode(pool[orc_addr(is_v, block, h, t, d, Hkv, D, 1)]) * scale;
+  uint16_t bits;
+  memcpy(&bits, pool + orc_addr(is_v, block, h, t, d, Hkv, D, 2), 2);
+  return oracle_f16_to_double(bits);
+}
+
+/* Slot of logical position pos of a sequence: its block table names the
+ * physical block of logical block pos / BS, and the token sits at pos % BS in
+ * it ([PRIMER-8] §8.1; [GLOSSARY] §2 figure: logical 0 -> 7, 1 -> 2, 2 -> 11). */
+int64_t oracle_slot(const int32_t* table_row, int64_t pos) {
+  return (int64_t)table_row[pos / ORC_BS] * ORC_BS + pos % ORC_BS;
+}
+
+/* -------------------------------------------------------------------- write */
+
+/* Store T new K/V rows ([T][Hkv][D] fp16 bits) into their slots.  fp16 pools
+ * get the bits as they are; FP8 pools get E4M3(x / scale) ([FP8-128K] §4:
+ * the new rows are turned into 8-bit values as they are written).  A negative
+ * slot, or one past the pool, is skipped. */
+void oracle_reshape_and_cache(const uint16_t* key, const uint16_t* value, uint8_t* k_pool,
+                              uint8_t* v_pool, const int64_t* slots, int T, int Hkv, int D,
+                              int num_blocks, int fp8, float k_scale, float v_scale) {
+  int e = fp8 ? 1 : 2;
+  for (int i = 0; i < T; ++i) {
+    int64_t s = slots[i];
+    if (s < 0 || s >= (int64_t)num_blocks * ORC_BS)
+      continue;
+    int64_t block = s / ORC_BS;
+    int t = (int)(s % ORC_BS);
+    for (int h = 0; h < Hkv; ++h)
+      for (int d = 0; d < D; ++d) {
+        int64_t src = ((int64_t)i * Hkv + h) * D + d;
+        int64_t ka = orc_addr(0, block, h, t, d, Hkv, D, e);
+        int64_t va = orc_addr(1, block, h, t, d, Hkv, D, e);
+        if (fp8) {
+          k_pool[ka] = oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double(key[src]), k_scale));
+          v_pool[va] = oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double(value[src]), v_scale));
+        } else {
+          memcpy(k_pool + ka, key + src, 2);
+          memcpy(v_pool + va, value + src, 2);
+        }
+      }
+  }
+}
+
+/* ------------------------------------------------------------------- decode */
+
+/* Decode attention for a batch, one query token per sequence.  For sequence b
+ * and query head h (KV head kv = h / G, G = Hq / Hkv consecutive query heads
+ * per KV head, the 8:1 grouping of [FP8-128K] §2):
+ *   k_t, v_t = cached rows of logical token t < L_b, found through the block
+ *              table ([PRIMER-8] §8.1: gathered by indirection),
+ *   s_t      = sm_scale * (q . k_t),
+ *   out      = sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s).
+ * L_b = 0 gives zeros.  out is fp64 [B][Hq][D].  The (b, h) pairs are
+ * independent and are spread over `threads` OpenMP threads (0 = default). */
+void oracle_paged_attention_decode(double* out, const uint16_t* q, const uint8_t* k_pool,
+                                   const uint8_t* v_pool, const int32_t* block_tables,
+                                   int max_blocks, const int32_t* context_lens, int B, int Hq,
+                                   int Hkv, int D, int fp8, float sm_scale, float k_scale,
+                                   float v_scale, int threads) {
+  int G = Hq / Hkv;
+  double ks = fp8 ? (double)k_scale : 1.0, vs = fp8 ? (double)v_scale : 1.0;
+#ifdef _OPENMP
+  if (threads > 0)
+    omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
+    int b = (int)(bh / Hq), h = (int)(bh % Hq), kv = h / G;
+    int L = context_lens[b];
+    double* o = out + bh * D;
+    for (int d = 0; d < D; ++d)
+      o[d] = 0.0;
+    if (L <= 0)
+      continue;
+    const int32_t* row = block_tables + (int64_t)b * max_blocks;
+    double* qd = (double*)malloc(sizeof(double) * D);
+    double* s = (double*)malloc(sizeof(double) * L);
+    for (int d = 0; d < D; ++d)
+      qd[d] = oracle_f16_to_double(q[bh * D + d]);
+    double m = -INFINITY;
+    for (int t = 0; t < L; ++t) {
+      int64_t block = row[t / ORC_BS];
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d)
+        dot += qd[d] * orc_load(k_pool, 0, block, kv, t % ORC_BS, d, Hkv, D, fp8, ks);
+      s[t] = (double)sm_scale * dot;
+      if (s[t] > m)
+        m = s[t];
+    }
+    double den = 0.0;
+    for (int t = 0; t < L; ++t) {
+      int64_t block = row[t / ORC_BS];
+      double w = exp(s[t] - m);
+      den += w;
+      for (int d = 0; d < D; ++d)
+        o[d] += w * orc_load(v_pool, 1, block, kv, t % ORC_BS, d, Hkv, D, fp8, vs);
+    }
+    for (int d = 0; d < D; ++d)
+      o[d] /= den;
+    free(qd);
+    free(s);
+  }
+}
+
+/* Number of OpenMP threads a parallel region would use (for reports). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
