@@ -250,6 +250,8 @@ class BlockPoolModel:
     def append(self, sid: int, n_tokens: int):
         blocks, n = self.seqs[sid]
         bs = self.block_size
+        if n_tokens == 0:      # nothing is written, so nothing needs copying
+            return [], []
         cow = n % bs != 0 and self.ref[blocks[-1]] > 1
         have = -(-n // bs)
         need = -(-(n + n_tokens) // bs) - have + (1 if cow else 0)
