@@ -1,0 +1,330 @@
+"""Python binding of libpkv (paged KV cache + decode PagedAttention for MI355X).
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels
+of ``libpkv.so``; PyTorch supplies device memory and streams.  The function
+names are those of the C ABI declared in ``include/pkv.h``.  If the library
+has not been built the import of any entry point raises: there is no
+fallback implementation.
+
+Build with ``python -m paged_kv_cache_270_amd.build`` (or
+``__graft_entry__.build()``).
+"""
+import ctypes
+import os
+
+__all__ = [
+    "PKV_F16", "PKV_FP8_E4M3FN", "PKV_OK", "PkvError", "CacheLayout", "BlockPool", "lib_path",
+    "load_library", "pkv_status_string", "pkv_bytes_per_token", "pkv_pool_bytes",
+    "pkv_decode_partition_size", "pkv_decode_workspace_bytes", "pkv_reshape_and_cache",
+    "pkv_paged_attention_decode", "pkv_decode_partitions", "pkv_decode_reduce",
+    "pkv_copy_blocks",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_NO_FREE_BLOCKS = -3
+PKV_ERR_HIP = -4
+PKV_ERR_WORKSPACE = -5
+PKV_ERR_BAD_HANDLE = -6
+PKV_ERR_REFCOUNT = -7
+PKV_F16 = 0
+PKV_FP8_E4M3FN = 1
+BLOCK_SIZE = 16
+HEAD_DIM = 128
+
+
+class CacheLayout(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+    def __init__(self, num_blocks, num_kv_heads, dtype=PKV_F16, block_size=BLOCK_SIZE,
+                 head_dim=HEAD_DIM):
+        super().__init__(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == PKV_F16 else 1
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pkv_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libpkv.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"libpkv.so not found at {lib_path}; build it with "
+                          "`python -m paged_kv_cache_270_amd.build`")
+    L = ctypes.CDLL(lib_path)
+    P, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    f32, f64 = ctypes.c_float, ctypes.c_double
+    LP = ctypes.POINTER(CacheLayout)
+    sig = {
+        "pkv_status_string": ([i32], ctypes.c_char_p),
+        "pkv_bytes_per_token": ([i32, i32, i32, i32], u64),
+        "pkv_pool_bytes": ([LP], u64),
+        "pkv_decode_partition_size": ([i32, i32, i32, i32], i32),
+        "pkv_decode_workspace_bytes": ([i32, i32, i32, i32, i32], u64),
+        "pkv_reshape_and_cache": ([P, P, P, P, P, i32, LP, f32, f32, P], i32),
+        "pkv_paged_attention_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, LP, f32, f32, f32,
+                                        i32, P, u64, P], i32),
+        "pkv_decode_partitions": ([P, P, P, P, P, i32, P, i32, i32, i32, LP, f32, f32, f32, i32,
+                                   P, u64, P], i32),
+        "pkv_decode_reduce": ([P, P, i32, i32, i32, i32, LP, f32, i32, P, u64, P], i32),
+        "pkv_copy_blocks": ([P, P, LP, P, i32, P], i32),
+        "pkv_pool_create": ([i32, i32, u64, ctypes.POINTER(P)], i32),
+        "pkv_pool_destroy": ([P], None),
+        "pkv_pool_num_blocks": ([P], i32),
+        "pkv_pool_num_free": ([P], i32),
+        "pkv_pool_usage": ([P], f64),
+        "pkv_pool_refcount": ([P, i32], i32),
+        "pkv_pool_num_seqs": ([P], i32),
+        "pkv_seq_create": ([P, ctypes.POINTER(i32)], i32),
+        "pkv_seq_fork": ([P, i32, ctypes.POINTER(i32)], i32),
+        "pkv_seq_append": ([P, i32, i32, P, P, ctypes.POINTER(i32)], i32),
+        "pkv_seq_free": ([P, i32], i32),
+        "pkv_seq_block_table": ([P, i32, P, i32, ctypes.POINTER(i32)], i32),
+        "pkv_seq_len": ([P, i32], i64),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != PKV_OK:
+        raise PkvError(status, where)
+
+
+def _ptr(x):
+    """Device (or host) address of a tensor / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("libpkv needs contiguous tensors")
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _require(t, dtype, name, device=True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+# --------------------------------------------------------------- sizing
+
+def pkv_status_string(status: int) -> str:
+    return load_library().pkv_status_string(status).decode()
+
+
+def pkv_bytes_per_token(n_layers: int, n_kv_heads: int, d_head: int, elem_bytes: int) -> int:
+    return load_library().pkv_bytes_per_token(n_layers, n_kv_heads, d_head, elem_bytes)
+
+
+def pkv_pool_bytes(layout: CacheLayout) -> int:
+    return load_library().pkv_pool_bytes(ctypes.byref(layout))
+
+
+def pkv_decode_partition_size(num_seqs, num_kv_heads, max_context_len, requested=0) -> int:
+    return load_library().pkv_decode_partition_size(num_seqs, num_kv_heads, max_context_len,
+                                                    requested)
+
+
+def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                               partition_size=0) -> int:
+    return load_library().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                     max_context_len, partition_size)
+
+
+# --------------------------------------------------------- device calls
+
+def pkv_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, layout: CacheLayout,
+                          k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """key/value: fp16 [T][Hkv][128]; slot_mapping: int64 [T] (device)."""
+    import torch
+    _require(key, torch.float16, "key")
+    _require(value, torch.float16, "value")
+    _require(slot_mapping, torch.int64, "slot_mapping")
+    T = key.shape[0]
+    if key.shape != value.shape or tuple(key.shape[1:]) != (layout.num_kv_heads, layout.head_dim):
+        raise ValueError("key/value must be [T][num_kv_heads][head_dim]")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must hold one slot per token")
+    _check(load_library().pkv_reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping), T,
+        ctypes.byref(layout), k_scale, v_scale, _stream(stream)), "pkv_reshape_and_cache")
+
+
+def _decode_args(out, q, block_tables, context_lens):
+    import torch
+    _require(out, torch.float32, "out")
+    _require(q, torch.float16, "q")
+    _require(block_tables, torch.int32, "block_tables")
+    _require(context_lens, torch.int32, "context_lens")
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must match q's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B][max_blocks], context_lens [B]")
+    return B, Hq, block_tables.shape[1]
+
+
+def _workspace(workspace, B, Hq, layout, max_context_len, partition_size):
+    need = pkv_decode_workspace_bytes(B, Hq, layout.num_kv_heads, max_context_len,
+                                      partition_size)
+    if workspace is None and need > 0:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, nbytes
+
+
+def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
+                               max_context_len: int, layout: CacheLayout, sm_scale: float,
+                               k_scale: float = 1.0, v_scale: float = 1.0,
+                               partition_size: int = 0, workspace=None, stream=None) -> None:
+    B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
+    workspace, nbytes = _workspace(workspace, B, Hq, layout, max_context_len, partition_size)
+    _check(load_library().pkv_paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
+        _ptr(context_lens), B, Hq, max_context_len, ctypes.byref(layout), sm_scale, k_scale,
+        v_scale, partition_size, _ptr(workspace), nbytes, _stream(stream)),
+        "pkv_paged_attention_decode")
+
+
+def pkv_decode_partitions(out, q, k_pool, v_pool, block_tables, context_lens,
+                          max_context_len: int, layout: CacheLayout, sm_scale: float,
+                          k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                          workspace=None, stream=None) -> None:
+    B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().pkv_decode_partitions(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
+        _ptr(context_lens), B, Hq, max_context_len, ctypes.byref(layout), sm_scale, k_scale,
+        v_scale, partition_size, _ptr(workspace), nbytes, _stream(stream)),
+        "pkv_decode_partitions")
+
+
+def pkv_decode_reduce(out, context_lens, max_context_len: int, max_blocks_per_seq: int,
+                      layout: CacheLayout, v_scale: float = 1.0, partition_size: int = 0,
+                      workspace=None, stream=None) -> None:
+    B, Hq = out.shape[0], out.shape[1]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().pkv_decode_reduce(
+        _ptr(out), _ptr(context_lens), B, Hq, max_context_len, max_blocks_per_seq,
+        ctypes.byref(layout), v_scale, partition_size, _ptr(workspace), nbytes,
+        _stream(stream)), "pkv_decode_reduce")
+
+
+def pkv_copy_blocks(k_pool, v_pool, layout: CacheLayout, src_dst_pairs, stream=None) -> None:
+    """src_dst_pairs: int32 [n][2] device tensor of (source, destination)."""
+    import torch
+    _require(src_dst_pairs, torch.int32, "src_dst_pairs")
+    n = src_dst_pairs.shape[0] if src_dst_pairs.dim() == 2 else src_dst_pairs.numel() // 2
+    _check(load_library().pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), ctypes.byref(layout),
+                                          _ptr(src_dst_pairs), n, _stream(stream)),
+           "pkv_copy_blocks")
+
+
+# ---------------------------------------------------------- block pool
+
+class BlockPool:
+    """Host block pool and sequence tables (pkv_pool_* / pkv_seq_*)."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE, shuffle_seed: int = 0):
+        self._L = load_library()
+        h = ctypes.c_void_p()
+        _check(self._L.pkv_pool_create(num_blocks, block_size, shuffle_seed, ctypes.byref(h)),
+               "pkv_pool_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            self._L.pkv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_blocks(self) -> int:
+        return self._L.pkv_pool_num_blocks(self._h)
+
+    def num_free(self) -> int:
+        return self._L.pkv_pool_num_free(self._h)
+
+    def usage(self) -> float:
+        return self._L.pkv_pool_usage(self._h)
+
+    def refcount(self, block: int) -> int:
+        return self._L.pkv_pool_refcount(self._h, block)
+
+    def num_seqs(self) -> int:
+        return self._L.pkv_pool_num_seqs(self._h)
+
+    def create(self) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pkv_seq_create(self._h, ctypes.byref(out)), "pkv_seq_create")
+        return out.value
+
+    def fork(self, parent: int) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pkv_seq_fork(self._h, parent, ctypes.byref(out)), "pkv_seq_fork")
+        return out.value
+
+    def append(self, seq: int, n_tokens: int):
+        """Returns (slots: list[int], cow_pairs: list[(old, new)])."""
+        slots = (ctypes.c_int64 * max(1, n_tokens))()
+        pairs = (ctypes.c_int32 * 2)()
+        n_cow = ctypes.c_int32()
+        _check(self._L.pkv_seq_append(self._h, seq, n_tokens, slots, pairs, ctypes.byref(n_cow)),
+               "pkv_seq_append")
+        cow = [(pairs[0], pairs[1])] if n_cow.value else []
+        return list(slots[:n_tokens]), cow
+
+    def free(self, seq: int) -> None:
+        _check(self._L.pkv_seq_free(self._h, seq), "pkv_seq_free")
+
+    def block_table(self, seq: int):
+        n = ctypes.c_int32()
+        st = self._L.pkv_seq_block_table(self._h, seq, None, 0, ctypes.byref(n))
+        if st not in (PKV_OK, PKV_ERR_INVALID_ARG):
+            _check(st, "pkv_seq_block_table")
+        buf = (ctypes.c_int32 * max(1, n.value))()
+        _check(self._L.pkv_seq_block_table(self._h, seq, buf, n.value, ctypes.byref(n)),
+               "pkv_seq_block_table")
+        return list(buf[:n.value])
+
+    def seq_len(self, seq: int) -> int:
+        return self._L.pkv_seq_len(self._h, seq)

@@ -1,0 +1,226 @@
+// pkv_host.cpp — host half of libpkv: status strings, sizing, and the block
+// pool with per-sequence block tables.
+//
+// The pool follows the paging scheme of "LLM Primer VI, Capítulo 8 — Gestión
+// de caché KV de nueva generación" §8.1 (fixed blocks in one flat pool, a
+// table per sequence from logical to physical block, refcounted sharing for
+// branching), the on-demand growth and copy-on-write of "KV Cache y
+// PagedAttention: por qué se reduce la velocidad de tu servidor LLM", and the
+// release-on-cancel rule of "PagedAttention y Gestión de KV-Cache" §4.02.
+// No HIP here: this file is plain C++17 and runs without a GPU.
+#include <cstdint>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv.h"
+
+extern "C" const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported layout or shape";
+    case PKV_ERR_NO_FREE_BLOCKS: return "no free cache blocks";
+    case PKV_ERR_HIP: return "HIP launch failed";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_BAD_HANDLE: return "unknown pool or sequence";
+    case PKV_ERR_REFCOUNT: return "block reference count underflow";
+    default: return "unknown status";
+  }
+}
+
+// ------------------------------------------------------------------ sizing
+
+// 2 (K and V) x layers x KV heads x head dim x element bytes: the formula of
+// "Optimización de KV Cache con PagedAttention y Cuantización FP8 ...", §2.
+extern "C" uint64_t pkv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_head,
+                                        int32_t elem_bytes) {
+  if (n_layers <= 0 || n_kv_heads <= 0 || d_head <= 0 || elem_bytes <= 0) return 0;
+  return 2ull * (uint64_t)n_layers * (uint64_t)n_kv_heads * (uint64_t)d_head *
+         (uint64_t)elem_bytes;
+}
+
+extern "C" uint64_t pkv_pool_bytes(const pkv_cache_layout* l) {
+  if (!l || l->num_blocks <= 0 || l->block_size <= 0 || l->num_kv_heads <= 0 ||
+      l->head_dim <= 0)
+    return 0;
+  uint64_t e;
+  if (l->dtype == PKV_F16)
+    e = 2;
+  else if (l->dtype == PKV_FP8_E4M3FN)
+    e = 1;
+  else
+    return 0;
+  return (uint64_t)l->num_blocks * (uint64_t)l->num_kv_heads * (uint64_t)l->block_size *
+         (uint64_t)l->head_dim * e;
+}
+
+// ------------------------------------------------------------- block pool
+
+namespace {
+
+struct Seq {
+  std::vector<int32_t> blocks;
+  int64_t len = 0;
+};
+
+uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+}  // namespace
+
+struct pkv_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::deque<int32_t> free_list;  // popped at the front, returned at the back
+  std::vector<int32_t> ref;
+  std::unordered_map<int32_t, Seq> seqs;
+  int32_t next_id = 0;
+};
+
+extern "C" pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
+                                      uint64_t shuffle_seed, pkv_pool** out) {
+  if (!out || num_blocks <= 0 || block_size <= 0) return PKV_ERR_INVALID_ARG;
+  pkv_pool* p = new (std::nothrow) pkv_pool();
+  if (!p) return PKV_ERR_INVALID_ARG;
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->ref.assign((size_t)num_blocks, 0);
+  std::vector<int32_t> order((size_t)num_blocks);
+  for (int32_t i = 0; i < num_blocks; ++i) order[(size_t)i] = i;
+  if (shuffle_seed != 0) {  // Fisher-Yates with a splitmix64 stream
+    uint64_t s = shuffle_seed;
+    for (int32_t i = num_blocks - 1; i > 0; --i) {
+      int32_t j = (int32_t)(splitmix64(s) % (uint64_t)(i + 1));
+      std::swap(order[(size_t)i], order[(size_t)j]);
+    }
+  }
+  p->free_list.assign(order.begin(), order.end());
+  *out = p;
+  return PKV_OK;
+}
+
+extern "C" void pkv_pool_destroy(pkv_pool* p) { delete p; }
+
+extern "C" int32_t pkv_pool_num_blocks(const pkv_pool* p) { return p ? p->num_blocks : -1; }
+
+extern "C" int32_t pkv_pool_num_free(const pkv_pool* p) {
+  return p ? (int32_t)p->free_list.size() : -1;
+}
+
+extern "C" double pkv_pool_usage(const pkv_pool* p) {
+  if (!p || p->num_blocks == 0) return 0.0;
+  return (double)(p->num_blocks - (int32_t)p->free_list.size()) / (double)p->num_blocks;
+}
+
+extern "C" int32_t pkv_pool_refcount(const pkv_pool* p, int32_t block) {
+  if (!p || block < 0 || block >= p->num_blocks) return -1;
+  return p->ref[(size_t)block];
+}
+
+extern "C" int32_t pkv_pool_num_seqs(const pkv_pool* p) {
+  return p ? (int32_t)p->seqs.size() : -1;
+}
+
+extern "C" pkv_status pkv_seq_create(pkv_pool* p, int32_t* seq_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (!seq_out) return PKV_ERR_INVALID_ARG;
+  int32_t id = p->next_id++;
+  p->seqs.emplace(id, Seq());
+  *seq_out = id;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_fork(pkv_pool* p, int32_t parent, int32_t* child_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (!child_out) return PKV_ERR_INVALID_ARG;
+  auto it = p->seqs.find(parent);
+  if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+  Seq child = it->second;  // same blocks, same length
+  for (int32_t b : child.blocks) p->ref[(size_t)b] += 1;
+  int32_t id = p->next_id++;
+  p->seqs.emplace(id, std::move(child));
+  *child_out = id;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_append(pkv_pool* p, int32_t seq, int32_t n_tokens,
+                                     int64_t* slots_out, int32_t* cow_pairs_out,
+                                     int32_t* n_cow_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (n_tokens < 0 || (n_tokens > 0 && !slots_out)) return PKV_ERR_INVALID_ARG;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+  Seq& s = it->second;
+  const int64_t bs = p->block_size;
+  if (n_cow_out) *n_cow_out = 0;
+  if (n_tokens == 0) return PKV_OK;
+  // Writing into a partially filled last block that another sequence also
+  // holds would change that sequence's tokens: copy the block first.
+  const bool cow = (s.len % bs) != 0 && p->ref[(size_t)s.blocks.back()] > 1;
+  if (cow && !cow_pairs_out) return PKV_ERR_INVALID_ARG;
+  const int64_t have = (s.len + bs - 1) / bs;
+  const int64_t want = (s.len + n_tokens + bs - 1) / bs;
+  const int64_t need = want - have + (cow ? 1 : 0);
+  if (need > (int64_t)p->free_list.size()) return PKV_ERR_NO_FREE_BLOCKS;  // nothing changed
+  if (cow) {
+    int32_t fresh = p->free_list.front();
+    p->free_list.pop_front();
+    int32_t old = s.blocks.back();
+    p->ref[(size_t)old] -= 1;
+    p->ref[(size_t)fresh] += 1;
+    s.blocks.back() = fresh;
+    cow_pairs_out[0] = old;
+    cow_pairs_out[1] = fresh;
+    if (n_cow_out) *n_cow_out = 1;
+  }
+  for (int64_t i = 0; i < n_tokens; ++i) {
+    const int64_t pos = s.len + i;
+    if (pos / bs >= (int64_t)s.blocks.size()) {  // the token opens a new block
+      int32_t b = p->free_list.front();
+      p->free_list.pop_front();
+      p->ref[(size_t)b] += 1;
+      s.blocks.push_back(b);
+    }
+    slots_out[i] = (int64_t)s.blocks[(size_t)(pos / bs)] * bs + pos % bs;
+  }
+  s.len += n_tokens;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_free(pkv_pool* p, int32_t seq) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+  for (int32_t b : it->second.blocks)
+    if (p->ref[(size_t)b] <= 0) return PKV_ERR_REFCOUNT;  // checked before any change
+  for (int32_t b : it->second.blocks) {
+    if (--p->ref[(size_t)b] == 0) p->free_list.push_back(b);
+  }
+  p->seqs.erase(it);
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_block_table(const pkv_pool* p, int32_t seq, int32_t* out,
+                                          int32_t cap, int32_t* n_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+  const int32_t n = (int32_t)it->second.blocks.size();
+  if (n_out) *n_out = n;
+  if (cap < n || (n > 0 && !out)) return PKV_ERR_INVALID_ARG;
+  if (n > 0) std::memcpy(out, it->second.blocks.data(), sizeof(int32_t) * (size_t)n);
+  return PKV_OK;
+}
+
+extern "C" int64_t pkv_seq_len(const pkv_pool* p, int32_t seq) {
+  if (!p) return -1;
+  auto it = p->seqs.find(seq);
+  return it == p->seqs.end() ? -1 : it->second.len;
+}

@@ -1,0 +1,698 @@
+// pkv_kernels.hip — gfx950 (MI355X) kernels and the device half of libpkv's
+// C ABI: the cache write, split-KV decode PagedAttention with its
+// log-sum-exp merge, and the block copy used for copy-on-write.
+//
+// Pages the kernels follow (cited by title and section):
+//   [FP8-128K] "Optimización de KV Cache con PagedAttention y Cuantización FP8
+//              para Contextos Largos (128K)"
+//   [PRIMER-8] "LLM Primer VI, Capítulo 8 — Gestión de caché KV de nueva
+//              generación"
+//
+// Design for CDNA4, in short:
+//   * one wavefront owns a (sequence, KV head) pair over a run of 16-token
+//     blocks and serves all G <= 16 query heads of the group at once: the
+//     group's queries form the B operand of a 16x16x32 fp16 MFMA, so each K/V
+//     tile is read from HBM once and shared by the whole group in registers;
+//   * tiles are stored in the order the MFMA operands consume them (see the
+//     layout in pkv.h), so a wave reads a 2 KiB FP8 tile with two 16-byte
+//     loads per lane, each instruction covering 1 KiB of contiguous memory;
+//   * FP8 codes become fp16 with integer bit operations (exact: every E4M3
+//     value is an fp16 value); the scales are folded into the logit scale
+//     and into the final output, never applied per element;
+//   * QK^T gives S^T (tokens x heads) in the accumulator layout that is
+//     exactly the B operand of the PV MFMA, so the online softmax runs on
+//     registers with two cross-row max reductions per block and no shuffles
+//     of the probabilities;
+//   * split-KV: four waves per workgroup share a partition and merge through
+//     LDS; partitions are merged by a second kernel with the log-sum-exp rule.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "pkv.h"
+
+namespace {
+
+constexpr int kBS = 16;      // tokens per block
+constexpr int kD = 128;      // head dim
+constexpr int kNW = 4;       // waves per decode workgroup
+constexpr int kWave = 64;
+constexpr int kMaxG = 16;    // MFMA N dimension: query heads per KV head
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------- FP8 codec
+
+// fp32 -> OCP E4M3FN code: round to nearest, ties to even, finite values
+// at or above 448 (and infinities) saturate to +-448, NaN -> 0x7F | sign.
+// Written from the format definition: below 2^-6 the codes are a uniform
+// grid of 2^-9 (subnormals), above it 3 mantissa bits are kept.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float u) {
+  const uint32_t bits = __float_as_uint(u);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t abits = bits & 0x7FFFFFFFu;
+  if (abits > 0x7F800000u) return sign | 0x7Fu;              // NaN
+  const float a = __uint_as_float(abits);
+  if (a >= 448.0f) return sign | 0x7Eu;                      // saturate
+  if (a < 0.015625f)                                         // < 2^-6
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);     // 0..8, exact scaling
+  // keep the top 3 mantissa bits, round the 20 dropped bits half-to-even;
+  // a carry moves into the exponent, which is what the code needs
+  const uint32_t r = abits + 0x7FFFFu + ((abits >> 20) & 1u);
+  return sign | ((r >> 20) - (120u << 3));                   // rebias 127 -> 7
+}
+
+// Four E4M3 codes (one dword) -> four fp16 values equal to code_value / 256.
+// fp16 bits s|0|eeee|mmm|0000000 read as binary16 are (1 + m/8) 2^(e-15)
+// (or m/8 * 2^-14 for e = 0), i.e. exactly 2^-8 times the E4M3 value.
+__device__ __forceinline__ f16x4 e4m3x4_to_f16_div256(uint32_t x) {
+  const uint32_t hi = ((x >> 1) & 0x3F3F3F3Fu) | (x & 0x80808080u);  // s 0 e e e e m m
+  const uint32_t lo = (x << 7) & 0x80808080u;                        // m0 0000000
+  u32x2 r;
+  r.x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // lo0 hi0 lo1 hi1
+  r.y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // lo2 hi2 lo3 hi3
+  return __builtin_bit_cast(f16x4, r);
+}
+
+// ------------------------------------------------------ reshape_and_cache
+
+// One thread per (token, kv head, run of 8 channels): 16 bytes of fp16 in.
+template <bool kFP8>
+__global__ void __launch_bounds__(256)
+reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                         uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                         const int64_t* __restrict__ slots, int64_t total, int hkv,
+                         int64_t num_slots, float k_scale, float v_scale) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int c = (int)(gid & 15);          // channels 8c .. 8c+7
+  const int64_t th = gid >> 4;            // token * hkv + head
+  const int64_t tok = th / hkv;
+  const int h = (int)(th - tok * hkv);
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int t = (int)(slot & 15);
+  const u32x4 kin = key[th * 16 + c];
+  const u32x4 vin = value[th * 16 + c];
+  const int n = c >> 1;                   // 16-channel group of these channels
+  const int j0 = (c & 1) * 8;             // channel within the group
+  if (!kFP8) {
+    uint16_t* kp = reinterpret_cast<uint16_t*>(k_pool) + (blk * hkv + h) * (kBS * kD);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(v_pool) + (blk * hkv + h) * (kBS * kD);
+    // K, x = 8: (d/8)*128 + t*8 + d%8 -> the 8 channels are contiguous
+    *reinterpret_cast<u32x4*>(kp + c * 128 + t * 8) = kin;
+    // V, x = 8: (n/2)*512 + ((t/4)*16 + d%16)*8 + (n%2)*4 + t%4
+    const uint16_t* vh = reinterpret_cast<const uint16_t*>(&vin);
+    uint16_t* vb = vp + (n >> 1) * 512 + ((t >> 2) * 16 + j0) * 8 + (n & 1) * 4 + (t & 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vb[i * 8] = vh[i];
+  } else {
+    uint8_t* kp = k_pool + (blk * hkv + h) * (kBS * kD);
+    uint8_t* vp = v_pool + (blk * hkv + h) * (kBS * kD);
+    const _Float16* kh = reinterpret_cast<const _Float16*>(&kin);
+    const _Float16* vh = reinterpret_cast<const _Float16*>(&vin);
+    uint32_t kc[8], vc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      kc[i] = e4m3_from_f32((float)kh[i] / k_scale);  // correctly rounded fp32 division
+      vc[i] = e4m3_from_f32((float)vh[i] / v_scale);
+    }
+    // K, x = 16: (d/16)*256 + t*16 + d%16 -> 8 contiguous bytes
+    u32x2 kw;
+    kw.x = kc[0] | (kc[1] << 8) | (kc[2] << 16) | (kc[3] << 24);
+    kw.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
+    *reinterpret_cast<u32x2*>(kp + n * 256 + t * 16 + j0) = kw;
+    // V, x = 16: (n/4)*1024 + ((t/4)*16 + d%16)*16 + (n%4)*4 + t%4
+    uint8_t* vb = vp + (n >> 2) * 1024 + ((t >> 2) * 16 + j0) * 16 + (n & 3) * 4 + (t & 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vb[i * 16] = (uint8_t)vc[i];
+  }
+}
+
+// ------------------------------------------------------------ copy_blocks
+
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
+                   const int32_t* __restrict__ pairs, int64_t vecs_per_block, int num_blocks) {
+  const int i = blockIdx.x;
+  const int src = pairs[2 * i], dst = pairs[2 * i + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t s0 = (int64_t)src * vecs_per_block, d0 = (int64_t)dst * vecs_per_block;
+  for (int64_t v = threadIdx.x; v < vecs_per_block; v += 256) {
+    k_pool[d0 + v] = k_pool[s0 + v];
+    v_pool[d0 + v] = v_pool[s0 + v];
+  }
+}
+
+// ----------------------------------------------------------------- decode
+
+struct DecodeArgs {
+  float* out;                  // [B][Hq][D]
+  const _Float16* q;           // [B][Hq][D]
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* block_tables; // [B][max_blocks]
+  const int32_t* context_lens; // [B]
+  float* ws_ml;                // [B][Hq][n_p_max][2]: running max (log2 units), sum
+  float* ws_o;                 // [B][Hq][n_p_max][D]: unnormalised output
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t hq, hkv, g;
+  int32_t max_ctx;             // clamp for context lengths
+  int32_t part;                // partition tokens (multiple of 16)
+  int32_t n_p_max;
+  float qk_scale;              // sm_scale * k_scale * log2(e) [* 256 for FP8]
+  float out_scale;             // v_scale [* 256 for FP8]
+};
+
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
+  int L = a.context_lens[b];
+  const int cap = min(a.max_ctx, a.max_blocks * kBS);
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int m) {
+  return __shfl_xor(v, m, kWave);
+}
+
+template <bool kFP8>
+struct TileRegs {
+  static constexpr int kVecs = kFP8 ? 2 : 4;  // 16-byte loads per lane per tile
+  u32x4 k[kVecs];
+  u32x4 v[kVecs];
+};
+
+template <bool kFP8>
+__device__ __forceinline__ void load_tile(TileRegs<kFP8>& r, const DecodeArgs& a, int phys,
+                                          int kvh, int lane) {
+  constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
+  if ((unsigned)phys < (unsigned)a.num_blocks) {
+    const int64_t off = ((int64_t)phys * a.hkv + kvh) * kTileBytes;
+    const u32x4* kt = reinterpret_cast<const u32x4*>(a.k_pool + off);
+    const u32x4* vt = reinterpret_cast<const u32x4*>(a.v_pool + off);
+#pragma unroll
+    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+      r.k[i] = __builtin_nontemporal_load(kt + i * kWave + lane);
+      r.v[i] = __builtin_nontemporal_load(vt + i * kWave + lane);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+      r.k[i] = u32x4{0, 0, 0, 0};
+      r.v[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// Decode partition kernel.  Grid (n_p_max, Hkv, B); kNW waves per workgroup.
+// Workgroup (p, kvh, b) covers tokens [p*P, min(L, (p+1)*P)) of sequence b
+// for the G query heads of KV head kvh.  Wave w takes the partition's blocks
+// w, w + kNW, ...  Lane (j = lane % 16, qg = lane / 16) serves query head
+// kvh*G + j and, in each tile, tokens 4qg .. 4qg+3.
+template <bool kFP8>
+__global__ void __launch_bounds__(kNW * kWave)
+decode_partition_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];  // [kNW][G][D] outputs, then [kNW][16] max and sum
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int qg = lane >> 4;
+  const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.g;
+
+  const int L = clamp_len(a, b);
+  const int n_p = (L + a.part - 1) / a.part;
+  const int tok0 = p * a.part;
+  const int64_t head0 = (int64_t)b * a.hq + (int64_t)kvh * G;  // first query head of the group
+  if (tok0 >= L) {
+    if (p == 0) {  // empty sequence: attention over nothing is defined as zeros
+      for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) a.out[head0 * kD + i] = 0.0f;
+    }
+    return;
+  }
+  const int tok1 = min(L, tok0 + a.part);
+  const int blk0 = tok0 / kBS;
+  const int nblk = (tok1 - tok0 + kBS - 1) / kBS;
+
+  // Query heads of the group as the MFMA B operand, in the channel order the
+  // K tile registers hold (FP8: runs of 16 channels; fp16: runs of 8).
+  f16x8 qop[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (j < G) {
+      const int d0 = kFP8 ? (m >> 1) * 64 + qg * 16 + (m & 1) * 8 : m * 32 + qg * 8;
+      qop[m] = *reinterpret_cast<const f16x8*>(a.q + (head0 + j) * kD + d0);
+    } else {
+      qop[m] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  float m_run = -INFINITY;  // running max of this lane's head (log2 units)
+  float l_run = 0.0f;       // running sum over this lane's tokens
+  f32x4 acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int my_n = w < nblk ? (nblk - w + kNW - 1) / kNW : 0;
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk0 + w;
+
+  for (int c0 = 0; c0 < my_n; c0 += kWave) {
+    const int cnt = min(kWave, my_n - c0);
+    // lane i holds the physical id of this wave's block c0 + i
+    const int tbl = lane < cnt ? trow[(int64_t)(c0 + lane) * kNW] : 0;
+    TileRegs<kFP8> cur, nxt;
+    load_tile<kFP8>(cur, a, __builtin_amdgcn_readfirstlane(tbl), kvh, lane);
+    for (int ii = 0; ii < cnt; ++ii) {
+      if (ii + 1 < cnt) load_tile<kFP8>(nxt, a, __builtin_amdgcn_readlane(tbl, ii + 1), kvh, lane);
+      const int tb = (blk0 + w + (c0 + ii) * kNW) * kBS;  // first token of the block
+
+      // S^T[t][g] = sum_d K[t][d] Q[g][d]: 4 MFMAs over the 128 channels
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f16x8 ka;
+        if (kFP8) {
+          const u32x4 raw = cur.k[m >> 1];
+          const f16x4 lo = e4m3x4_to_f16_div256((m & 1) ? raw.z : raw.x);
+          const f16x4 hi = e4m3x4_to_f16_div256((m & 1) ? raw.w : raw.y);
+          ka = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          ka = __builtin_bit_cast(f16x8, cur.k[m]);
+        }
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[m], s, 0, 0, 0);
+      }
+
+      // online softmax over this block's 16 tokens (lane: 4 tokens, one head)
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = (tb + qg * 4 + r < L) ? s[r] * a.qk_scale : -INFINITY;
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = fmaxf(bm, wave_shfl_xor(bm, 16));
+      bm = fmaxf(bm, wave_shfl_xor(bm, 32));
+      const float m_new = fmaxf(m_run, bm);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - m_new);
+      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m_run = m_new;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+      }
+      // probabilities as fp16 hi + lo so the PV product keeps ~22 bits
+      f16x4 ph, pl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ph[r] = (_Float16)pr[r];
+        pl[r] = (_Float16)(pr[r] - (float)ph[r]);
+      }
+      // O^T[d][g] += sum_t V^T[d][t] P^T[t][g]: 8 MFMAs of 16 channels
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        f16x4 va;
+        if (kFP8) {
+          const u32x4 raw = cur.v[n >> 2];
+          va = e4m3x4_to_f16_div256(raw[n & 3]);
+        } else {
+          const u32x4 raw = cur.v[n >> 1];
+          u32x2 two;
+          two.x = raw[(n & 1) * 2];
+          two.y = raw[(n & 1) * 2 + 1];
+          va = __builtin_bit_cast(f16x4, two);
+        }
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, acc[n], 0, 0, 0);
+      }
+      cur = nxt;
+    }
+  }
+
+  // sum of the four token rows of each head
+  l_run += wave_shfl_xor(l_run, 16);
+  l_run += wave_shfl_xor(l_run, 32);
+
+  // merge the kNW waves through LDS
+  float* so = smem;                        // [kNW][G][D]
+  float* sm = smem + kNW * G * kD;         // [kNW][16]
+  float* sl = sm + kNW * 16;               // [kNW][16]
+  if (j < G) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      *reinterpret_cast<f32x4*>(so + (w * G + j) * kD + n * 16 + qg * 4) = acc[n];
+    if (qg == 0) {
+      sm[w * 16 + j] = m_run;
+      sl[w * 16 + j] = l_run;
+    }
+  }
+  __syncthreads();
+  const bool single = n_p == 1;
+  for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) {
+    const int gg = i / kD, d = i - gg * kD;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kNW; ++ww) mx = fmaxf(mx, sm[ww * 16 + gg]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kNW; ++ww) {
+      const float f = __builtin_amdgcn_exp2f(sm[ww * 16 + gg] - mx);
+      num += so[(ww * G + gg) * kD + d] * f;
+      den += sl[ww * 16 + gg] * f;
+    }
+    const int64_t hrow = head0 + gg;
+    if (single) {
+      a.out[hrow * kD + d] = num / den * a.out_scale;
+    } else {
+      const int64_t prow = hrow * a.n_p_max + p;
+      a.ws_o[prow * kD + d] = num;
+      if (d == 0) {
+        a.ws_ml[prow * 2] = mx;
+        a.ws_ml[prow * 2 + 1] = den;
+      }
+    }
+  }
+}
+
+// Merge kernel.  Grid (Hq, B), 256 threads.  For sequences spanning n_p > 1
+// partitions: M = max m_p, out = out_scale * sum_p o_p 2^(m_p - M) /
+// sum_p l_p 2^(m_p - M).  Fixed summation order: results do not depend on
+// timing.
+__global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a) {
+  __shared__ float w_s[256];
+  __shared__ float red[256];
+  __shared__ f32x4 part[8][32];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int L = clamp_len(a, b);
+  const int n_p = (L + a.part - 1) / a.part;
+  if (n_p <= 1) return;  // written by the partition kernel
+  const int64_t row0 = ((int64_t)b * a.hq + h) * a.n_p_max;
+
+  float mx = -INFINITY;
+  for (int pp = tid; pp < n_p; pp += 256) mx = fmaxf(mx, a.ws_ml[(row0 + pp) * 2]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+
+  const int rg = tid >> 5, c4 = tid & 31;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.0f;
+  for (int cb = 0; cb < n_p; cb += 256) {
+    const int pp = cb + tid;
+    float wgt = 0.0f;
+    if (pp < n_p) {
+      wgt = __builtin_amdgcn_exp2f(a.ws_ml[(row0 + pp) * 2] - mx);
+      den += a.ws_ml[(row0 + pp) * 2 + 1] * wgt;
+    }
+    w_s[tid] = wgt;
+    __syncthreads();
+    const int rows = min(256, n_p - cb);
+    for (int r = rg; r < rows; r += 8) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + (row0 + cb + r) * kD + c4 * 4);
+      acc += o * w_s[r];
+    }
+    __syncthreads();
+  }
+  red[tid] = den;
+  part[rg][c4] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  if (tid < 32) {
+    f32x4 sum = part[0][tid];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) sum += part[r][tid];
+    const float scale = a.out_scale / red[0];
+    *reinterpret_cast<f32x4*>(a.out + ((int64_t)b * a.hq + h) * kD + tid * 4) = sum * scale;
+  }
+}
+
+// ------------------------------------------------------------- host side
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+int elem_bytes(int32_t dtype) {
+  return dtype == PKV_F16 ? 2 : (dtype == PKV_FP8_E4M3FN ? 1 : 0);
+}
+
+pkv_status check_layout(const pkv_cache_layout* l) {
+  if (!l) return PKV_ERR_INVALID_ARG;
+  if (l->block_size != kBS || l->head_dim != kD || elem_bytes(l->dtype) == 0)
+    return PKV_ERR_UNSUPPORTED;
+  if (l->num_blocks <= 0 || l->num_kv_heads <= 0 || l->num_kv_heads > 65535)
+    return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+pkv_status launch_status() {
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
+                          int32_t requested) {
+  if (requested < 0 || requested % kBS != 0) return -1;
+  if (requested > 0) return requested;
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_ctx;
+  return 512;
+}
+
+struct WsLayout {
+  uint64_t ml_bytes, o_bytes, total;
+  int32_t n_p_max;
+};
+
+WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32_t part) {
+  WsLayout w{0, 0, 0, 0};
+  w.n_p_max = max_ctx <= 0 ? 1 : (int32_t)(((int64_t)max_ctx + part - 1) / part);
+  if (w.n_p_max <= 1) return w;
+  const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)w.n_p_max;
+  w.ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+  w.o_bytes = rows * kD * sizeof(float);
+  w.total = w.ml_bytes + w.o_bytes;
+  return w;
+}
+
+struct DecodePlan {
+  DecodeArgs a;
+  bool fp8;
+  bool need_reduce;
+};
+
+pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale,
+                       float k_scale, float v_scale, int32_t partition_size, void* workspace,
+                       uint64_t workspace_bytes, bool need_pools, DecodePlan* plan) {
+  pkv_status st = check_layout(layout);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_seqs > 65535 || max_context_len < 0 || num_q_heads <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % layout->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  const int32_t G = num_q_heads / layout->num_kv_heads;
+  if (G > kMaxG) return PKV_ERR_UNSUPPORTED;
+  if (!out || !context_lens || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
+  if (need_pools) {
+    if (!q || !k_pool || !v_pool || !block_tables) return PKV_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+      return PKV_ERR_INVALID_ARG;
+    if (max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale)) return PKV_ERR_INVALID_ARG;
+  } else if (max_blocks_per_seq <= 0) {
+    return PKV_ERR_INVALID_ARG;
+  }
+  const bool fp8 = layout->dtype == PKV_FP8_E4M3FN;
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
+               v_scale > 0.0f))
+    return PKV_ERR_INVALID_ARG;
+  const int32_t part = resolve_partition(num_seqs, layout->num_kv_heads, max_context_len,
+                                         partition_size);
+  if (part <= 0) return PKV_ERR_INVALID_ARG;
+  const WsLayout wl = ws_layout(num_seqs, num_q_heads, max_context_len, part);
+  if (wl.total > 0) {
+    if (!workspace || workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PKV_ERR_INVALID_ARG;
+  }
+  DecodeArgs& a = plan->a;
+  a.out = out;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_ml = wl.total ? static_cast<float*>(workspace) : nullptr;
+  a.ws_o = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_bytes)
+                    : nullptr;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = layout->num_blocks;
+  a.hq = num_q_heads;
+  a.hkv = layout->num_kv_heads;
+  a.g = G;
+  a.max_ctx = max_context_len;
+  a.part = part;
+  a.n_p_max = wl.n_p_max;
+  const float log2e = 1.4426950408889634f;
+  a.qk_scale = sm_scale * (fp8 ? k_scale * 256.0f : 1.0f) * log2e;
+  a.out_scale = fp8 ? v_scale * 256.0f : 1.0f;
+  plan->fp8 = fp8;
+  plan->need_reduce = wl.n_p_max > 1;
+  return PKV_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                             int32_t max_context_len, int32_t requested) {
+  return resolve_partition(num_seqs, num_kv_heads, max_context_len, requested);
+}
+
+extern "C" uint64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t max_context_len,
+                                               int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
+  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+  if (part <= 0) return 0;
+  return ws_layout(num_seqs, num_q_heads, max_context_len, part).total;
+}
+
+extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
+                                            void* v_pool, const int64_t* slot_mapping,
+                                            int32_t num_tokens, const pkv_cache_layout* layout,
+                                            float k_scale, float v_scale, void* stream) {
+  pkv_status st = check_layout(layout);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_INVALID_ARG;
+  const bool fp8 = layout->dtype == PKV_FP8_E4M3FN;
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
+               v_scale > 0.0f))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t total = (int64_t)num_tokens * layout->num_kv_heads * 16;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return PKV_ERR_INVALID_ARG;
+  const int64_t num_slots = (int64_t)layout->num_blocks * kBS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (fp8)
+    reshape_and_cache_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
+        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping, total,
+        layout->num_kv_heads, num_slots, k_scale, v_scale);
+  else
+    reshape_and_cache_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
+        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping, total,
+        layout->num_kv_heads, num_slots, 1.0f, 1.0f);
+  return launch_status();
+}
+
+static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStream_t s) {
+  if (num_seqs == 0) return PKV_OK;
+  const dim3 grid((unsigned)pl.a.n_p_max, (unsigned)pl.a.hkv, (unsigned)num_seqs);
+  const size_t lds = (size_t)(kNW * pl.a.g * kD + 2 * kNW * 16) * sizeof(float);
+  (void)hipGetLastError();
+  if (pl.fp8)
+    decode_partition_kernel<true><<<grid, dim3(kNW * kWave), lds, s>>>(pl.a);
+  else
+    decode_partition_kernel<false><<<grid, dim3(kNW * kWave), lds, s>>>(pl.a);
+  return launch_status();
+}
+
+static pkv_status run_reduce(const DecodePlan& pl, int32_t num_seqs, hipStream_t s) {
+  if (num_seqs == 0 || !pl.need_reduce) return PKV_OK;
+  (void)hipGetLastError();
+  decode_reduce_kernel<<<dim3((unsigned)pl.a.hq, (unsigned)num_seqs), dim3(256), 0, s>>>(pl.a);
+  return launch_status();
+}
+
+extern "C" pkv_status pkv_decode_partitions(float* out, const void* q, const void* k_pool,
+                                            const void* v_pool, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t max_context_len,
+                                            const pkv_cache_layout* layout, float sm_scale,
+                                            float k_scale, float v_scale,
+                                            int32_t partition_size, void* workspace,
+                                            uint64_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                              context_lens, num_seqs, num_q_heads, max_context_len, layout,
+                              sm_scale, k_scale, v_scale, partition_size, workspace,
+                              workspace_bytes, true, &pl);
+  if (st != PKV_OK) return st;
+  return run_partitions(pl, num_seqs, static_cast<hipStream_t>(stream));
+}
+
+extern "C" pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t max_context_len, int32_t max_blocks_per_seq,
+                                        const pkv_cache_layout* layout, float v_scale,
+                                        int32_t partition_size, void* workspace,
+                                        uint64_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  pkv_status st = plan_decode(out, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq,
+                              context_lens, num_seqs, num_q_heads, max_context_len, layout,
+                              1.0f, 1.0f, v_scale, partition_size, workspace, workspace_bytes,
+                              false, &pl);
+  if (st != PKV_OK) return st;
+  return run_reduce(pl, num_seqs, static_cast<hipStream_t>(stream));
+}
+
+extern "C" pkv_status pkv_paged_attention_decode(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const pkv_cache_layout* layout, float sm_scale, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, uint64_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                              context_lens, num_seqs, num_q_heads, max_context_len, layout,
+                              sm_scale, k_scale, v_scale, partition_size, workspace,
+                              workspace_bytes, true, &pl);
+  if (st != PKV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_partitions(pl, num_seqs, s);
+  if (st != PKV_OK) return st;
+  return run_reduce(pl, num_seqs, s);
+}
+
+extern "C" pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const pkv_cache_layout* layout,
+                                      const int32_t* src_dst_pairs, int32_t num_pairs,
+                                      void* stream) {
+  pkv_status st = check_layout(layout);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src_dst_pairs || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(src_dst_pairs, 4))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t bytes = (int64_t)layout->num_kv_heads * kBS * kD * elem_bytes(layout->dtype);
+  (void)hipGetLastError();
+  copy_blocks_kernel<<<dim3((unsigned)num_pairs), dim3(256), 0,
+                       static_cast<hipStream_t>(stream)>>>(
+      static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), src_dst_pairs, bytes / 16,
+      layout->num_blocks);
+  return launch_status();
+}
