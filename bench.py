@@ -49,6 +49,19 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def copy_probe(mib: int) -> int:
+    """A plain copy of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": 5}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -58,7 +71,12 @@ def main() -> int:
     ap.add_argument("--cpu-sample-seqs", type=int, default=8,
                     help="sequences of the workload the CPU oracle baseline decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, 5 times (the "
+                         "reference kernel for scaling HBM byte counters), then exit")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        return copy_probe(args.copy_probe_mib)
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence or KV head with no exchange; see DESIGN.md)",
@@ -105,8 +123,8 @@ def main() -> int:
     d_lens = torch.full((B,), L, dtype=torch.int32, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     sm_scale = float(np.float32(1 / np.sqrt(D)))
-    P = pkv.pkv_decode_partition_size(B, Hkv, L, args.partition_size)
-    ws = torch.empty(max(1, pkv.pkv_decode_workspace_bytes(B, Hq, Hkv, L, P)),
+    P = pkv.pkv_decode_partition_size(B, Hkv, L, layout.dtype, args.partition_size)
+    ws = torch.empty(max(1, pkv.pkv_decode_workspace_bytes(B, Hq, Hkv, L, layout.dtype, P)),
                      dtype=torch.uint8, device=dev)
 
     # ---- bulk fill (prefill-sized write of 524288 tokens), timed on its own
@@ -134,17 +152,25 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # the timed region: K whole steps back to back, nothing else on the stream
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(args.steps):
-        step(kev[i])
+    for _ in range(args.steps):
+        step()
     end.record()
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / args.steps
-    kern_ms = [a.elapsed_time(b) for a, b in kev]
+    # a second timed region of K steps with events around the partition kernel
+    # (same stream) for its own duration; events add a few microseconds per
+    # step, so the step time above is taken without them
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(kev[i])
+    torch.cuda.synchronize()
+    kern_ms = sorted(a.elapsed_time(b) for a, b in kev)
     part_ms = sum(kern_ms) / len(kern_ms)
 
     kv_bytes = B * L * Hkv * D * 2 * 1

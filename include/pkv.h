@@ -110,18 +110,21 @@ uint64_t pkv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_hea
 /* Bytes of ONE pool (K or V) with this layout; 0 for an invalid layout. */
 uint64_t pkv_pool_bytes(const pkv_cache_layout* layout);
 
-/* Partition length (tokens) the decode will use: `requested` if it is a
- * positive multiple of 16, else (requested == 0) the library's choice for this
- * shape; -1 if `requested` is invalid. */
+/* Longest split-KV partition (tokens) the decode will use for this shape:
+ * `requested` if it is a positive multiple of 16, else (requested == 0) the
+ * library's choice; -1 if `requested` or `dtype` is invalid.  Each sequence
+ * of L tokens is cut into ceil(L / P) partitions of equal whole-block length,
+ * each at most P tokens. */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                  int32_t max_context_len, int32_t requested);
+                                  int32_t max_context_len, int32_t dtype, int32_t requested);
 
-/* Workspace bytes pkv_paged_attention_decode needs for this shape and
- * partition request (same rules as pkv_decode_partition_size); 0 if the
- * arguments are invalid. */
+/* Workspace bytes pkv_paged_attention_decode needs for this shape, cache
+ * dtype and partition request (same rules as pkv_decode_partition_size); 0
+ * if no merge is needed (every sequence fits one partition) or the arguments
+ * are invalid. */
 uint64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t max_context_len,
-                                    int32_t partition_size);
+                                    int32_t dtype, int32_t partition_size);
 
 /* ------------------------------------------------------------ device calls */
 
@@ -160,8 +163,10 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_poo
  *   max_context_len  host upper bound on every L_b (sizes the workspace).
  *   num_q_heads must be a multiple of layout->num_kv_heads with a group of at
  *   most 16.
- *   partition_size   tokens per split-KV partition: 0 = library choice, else
- *                 a positive multiple of 16.  Each partition yields a partial
+ *   partition_size   longest split-KV partition in tokens: 0 = library
+ *                 choice, else a positive multiple of 16.  A sequence of L
+ *                 tokens is cut into ceil(L / partition_size) partitions of
+ *                 equal whole-block length.  Each partition yields a partial
  *                 (max, sum, unnormalised output) and a second kernel merges
  *                 them with the log-sum-exp rule.
  *   workspace     device scratch of at least pkv_decode_workspace_bytes(...)

@@ -76,8 +76,8 @@ def load_library():
         "pkv_status_string": ([i32], ctypes.c_char_p),
         "pkv_bytes_per_token": ([i32, i32, i32, i32], u64),
         "pkv_pool_bytes": ([LP], u64),
-        "pkv_decode_partition_size": ([i32, i32, i32, i32], i32),
-        "pkv_decode_workspace_bytes": ([i32, i32, i32, i32, i32], u64),
+        "pkv_decode_partition_size": ([i32, i32, i32, i32, i32], i32),
+        "pkv_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], u64),
         "pkv_reshape_and_cache": ([P, P, P, P, P, i32, LP, f32, f32, P], i32),
         "pkv_paged_attention_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, LP, f32, f32, f32,
                                         i32, P, u64, P], i32),
@@ -153,15 +153,16 @@ def pkv_pool_bytes(layout: CacheLayout) -> int:
     return load_library().pkv_pool_bytes(ctypes.byref(layout))
 
 
-def pkv_decode_partition_size(num_seqs, num_kv_heads, max_context_len, requested=0) -> int:
+def pkv_decode_partition_size(num_seqs, num_kv_heads, max_context_len, dtype=PKV_FP8_E4M3FN,
+                              requested=0) -> int:
     return load_library().pkv_decode_partition_size(num_seqs, num_kv_heads, max_context_len,
-                                                    requested)
+                                                    dtype, requested)
 
 
 def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_context_len,
-                               partition_size=0) -> int:
+                               dtype=PKV_FP8_E4M3FN, partition_size=0) -> int:
     return load_library().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
-                                                     max_context_len, partition_size)
+                                                     max_context_len, dtype, partition_size)
 
 
 # --------------------------------------------------------- device calls
@@ -199,7 +200,7 @@ def _decode_args(out, q, block_tables, context_lens):
 
 def _workspace(workspace, B, Hq, layout, max_context_len, partition_size):
     need = pkv_decode_workspace_bytes(B, Hq, layout.num_kv_heads, max_context_len,
-                                      partition_size)
+                                      layout.dtype, partition_size)
     if workspace is None and need > 0:
         import torch
         workspace = torch.empty(need, dtype=torch.uint8, device="cuda")

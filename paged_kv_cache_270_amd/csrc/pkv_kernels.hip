@@ -27,6 +27,7 @@
 //     LDS; partitions are merged by a second kernel with the log-sum-exp rule.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -38,7 +39,7 @@ namespace {
 
 constexpr int kBS = 16;      // tokens per block
 constexpr int kD = 128;      // head dim
-constexpr int kNW = 4;       // waves per decode workgroup
+constexpr int kRW = 4;       // waves per merge workgroup
 constexpr int kWave = 64;
 constexpr int kMaxG = 16;    // MFMA N dimension: query heads per KV head
 
@@ -167,7 +168,7 @@ struct DecodeArgs {
   int32_t num_blocks;
   int32_t hq, hkv, g;
   int32_t max_ctx;             // clamp for context lengths
-  int32_t part;                // partition tokens (multiple of 16)
+  int32_t part_blocks;         // most blocks per partition (partition_size / 16)
   int32_t n_p_max;
   float qk_scale;              // sm_scale * k_scale * log2(e) [* 256 for FP8]
   float out_scale;             // v_scale [* 256 for FP8]
@@ -177,6 +178,21 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
   int L = a.context_lens[b];
   const int cap = min(a.max_ctx, a.max_blocks * kBS);
   return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+// Split-KV plan of one sequence: its nblk blocks are cut into
+// n_p = ceil(nblk / part_blocks) partitions of equal size (the first ones one
+// block longer when it does not divide), so no partition is nearly empty.
+struct SeqSplit {
+  int nblk, n_p, per;
+};
+
+__device__ __forceinline__ SeqSplit seq_split(const DecodeArgs& a, int L) {
+  SeqSplit s;
+  s.nblk = (L + kBS - 1) / kBS;
+  s.n_p = (s.nblk + a.part_blocks - 1) / a.part_blocks;
+  s.per = s.n_p > 0 ? (s.nblk + s.n_p - 1) / s.n_p : 0;
+  return s;
 }
 
 __device__ __forceinline__ float wave_shfl_xor(float v, int m) {
@@ -212,12 +228,115 @@ __device__ __forceinline__ void load_tile(TileRegs<kFP8>& r, const DecodeArgs& a
   }
 }
 
+// FP8 dequantisation of four codes (one dword) to fp16.  Two exact ways:
+//  * kHwCvt: the gfx950 conversion v_cvt_scalef32_pk_f16_fp8 (scale 1.0)
+//    gives the code values themselves;
+//  * otherwise integer bit operations give code_value / 256 (see
+//    e4m3x4_to_f16_div256); the factor 256 is folded into the scales.
+template <bool kHwCvt>
+__device__ __forceinline__ f16x4 dequant4(uint32_t x) {
+  if constexpr (kHwCvt) {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x, 1.0f, false);
+    const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x, 1.0f, true);
+    return f16x4{lo[0], lo[1], hi[0], hi[1]};
+  } else {
+    return e4m3x4_to_f16_div256(x);
+  }
+}
+
+// Online-softmax state of one lane: head j, tokens 4qg .. 4qg+3 of each tile.
+struct SoftmaxState {
+  float m_ref;   // reference max of the head (log2 units), equal on the 4 rows
+  float l;       // sum of this lane's probabilities, relative to m_ref
+  f32x4 acc[8];  // O^T rows 16n + 4qg .. +3 for head j, relative to m_ref
+};
+
+// Logits may exceed the reference max by up to 2^8 before the max is
+// re-reduced across the wave and the accumulators rescaled: p <= 256 stays
+// exact enough in fp16 and far from fp32 overflow.  On random data the
+// reference settles after a few tiles, so the steady state runs no
+// cross-lane reduction and no rescaling.
+constexpr float kLazyMaxSlack = 8.0f;
+
+template <bool kFP8, bool kHwCvt, bool kSplitP>
+__device__ __forceinline__ void process_tile(const TileRegs<kFP8>& t, const f16x8 (&qop)[4],
+                                             SoftmaxState& st, int tb, int qg, int L,
+                                             float qk_scale) {
+  // S^T[t][g] = sum_d K[t][d] Q[g][d]: 4 MFMAs over the 128 channels
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    f16x8 ka;
+    if constexpr (kFP8) {
+      const u32x4 raw = t.k[m >> 1];
+      const f16x4 lo = dequant4<kHwCvt>((m & 1) ? raw.z : raw.x);
+      const f16x4 hi = dequant4<kHwCvt>((m & 1) ? raw.w : raw.y);
+      ka = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      ka = __builtin_bit_cast(f16x8, t.k[m]);
+    }
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[m], s, 0, 0, 0);
+  }
+  float sv[4];
+  bool over = false;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sv[r] = (tb + qg * 4 + r < L) ? s[r] * qk_scale : -INFINITY;
+    over |= sv[r] - st.m_ref > kLazyMaxSlack;
+  }
+  if (__any(over)) {  // wave-uniform: re-reduce the max and rescale
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+    const float m_new = fmaxf(st.m_ref, bm);
+    const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.acc[n] *= alpha;
+    st.m_ref = m_new;
+  }
+  float pr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - st.m_ref);
+  f16x4 ph, pl;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ph[r] = (_Float16)pr[r];
+  if constexpr (kSplitP) {
+    // probabilities as fp16 hi + lo: the PV product keeps about 22 bits
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pl[r] = (_Float16)(pr[r] - (float)ph[r]);
+    st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  } else {
+    // the normaliser sums exactly the fp16 weights the PV product uses
+    st.l += ((float)ph[0] + (float)ph[1]) + ((float)ph[2] + (float)ph[3]);
+  }
+  // O^T[d][g] += sum_t V^T[d][t] P^T[t][g]: 8 MFMAs of 16 channels
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    f16x4 va;
+    if constexpr (kFP8) {
+      va = dequant4<kHwCvt>(t.v[n >> 2][n & 3]);
+    } else {
+      const u32x4 raw = t.v[n >> 1];
+      u32x2 two;
+      two.x = raw[(n & 1) * 2];
+      two.y = raw[(n & 1) * 2 + 1];
+      va = __builtin_bit_cast(f16x4, two);
+    }
+    st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, st.acc[n], 0, 0, 0);
+    if constexpr (kSplitP)
+      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, st.acc[n], 0, 0, 0);
+  }
+}
+
 // Decode partition kernel.  Grid (n_p_max, Hkv, B); kNW waves per workgroup.
 // Workgroup (p, kvh, b) covers tokens [p*P, min(L, (p+1)*P)) of sequence b
 // for the G query heads of KV head kvh.  Wave w takes the partition's blocks
 // w, w + kNW, ...  Lane (j = lane % 16, qg = lane / 16) serves query head
-// kvh*G + j and, in each tile, tokens 4qg .. 4qg+3.
-template <bool kFP8>
+// kvh*G + j and, in each tile, tokens 4qg .. 4qg+3.  Each wave keeps kPD
+// tiles in flight while it computes on another.
+template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW>
 __global__ void __launch_bounds__(kNW * kWave)
 decode_partition_kernel(DecodeArgs a) {
   extern __shared__ float smem[];  // [kNW][G][D] outputs, then [kNW][16] max and sum
@@ -229,18 +348,17 @@ decode_partition_kernel(DecodeArgs a) {
   const int G = a.g;
 
   const int L = clamp_len(a, b);
-  const int n_p = (L + a.part - 1) / a.part;
-  const int tok0 = p * a.part;
+  const SeqSplit sp = seq_split(a, L);
+  const int n_p = sp.n_p;
   const int64_t head0 = (int64_t)b * a.hq + (int64_t)kvh * G;  // first query head of the group
-  if (tok0 >= L) {
+  if (p >= n_p) {
     if (p == 0) {  // empty sequence: attention over nothing is defined as zeros
       for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) a.out[head0 * kD + i] = 0.0f;
     }
     return;
   }
-  const int tok1 = min(L, tok0 + a.part);
-  const int blk0 = tok0 / kBS;
-  const int nblk = (tok1 - tok0 + kBS - 1) / kBS;
+  const int blk0 = p * sp.per;
+  const int nblk = min(sp.nblk, blk0 + sp.per) - blk0;
 
   // Query heads of the group as the MFMA B operand, in the channel order the
   // K tile registers hold (FP8: runs of 16 channels; fp16: runs of 8).
@@ -255,11 +373,11 @@ decode_partition_kernel(DecodeArgs a) {
     }
   }
 
-  float m_run = -INFINITY;  // running max of this lane's head (log2 units)
-  float l_run = 0.0f;       // running sum over this lane's tokens
-  f32x4 acc[8];
+  SoftmaxState st;
+  st.m_ref = -INFINITY;
+  st.l = 0.0f;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 8; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int my_n = w < nblk ? (nblk - w + kNW - 1) / kNW : 0;
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk0 + w;
@@ -268,77 +386,29 @@ decode_partition_kernel(DecodeArgs a) {
     const int cnt = min(kWave, my_n - c0);
     // lane i holds the physical id of this wave's block c0 + i
     const int tbl = lane < cnt ? trow[(int64_t)(c0 + lane) * kNW] : 0;
-    TileRegs<kFP8> cur, nxt;
-    load_tile<kFP8>(cur, a, __builtin_amdgcn_readfirstlane(tbl), kvh, lane);
-    for (int ii = 0; ii < cnt; ++ii) {
-      if (ii + 1 < cnt) load_tile<kFP8>(nxt, a, __builtin_amdgcn_readlane(tbl, ii + 1), kvh, lane);
-      const int tb = (blk0 + w + (c0 + ii) * kNW) * kBS;  // first token of the block
-
-      // S^T[t][g] = sum_d K[t][d] Q[g][d]: 4 MFMAs over the 128 channels
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    TileRegs<kFP8> buf[kPD + 1];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        f16x8 ka;
-        if (kFP8) {
-          const u32x4 raw = cur.k[m >> 1];
-          const f16x4 lo = e4m3x4_to_f16_div256((m & 1) ? raw.z : raw.x);
-          const f16x4 hi = e4m3x4_to_f16_div256((m & 1) ? raw.w : raw.y);
-          ka = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-          ka = __builtin_bit_cast(f16x8, cur.k[m]);
+    for (int r = 0; r < kPD; ++r)
+      if (r < cnt) load_tile<kFP8>(buf[r], a, __builtin_amdgcn_readlane(tbl, r), kvh, lane);
+    for (int base = 0; base < cnt; base += kPD + 1) {
+#pragma unroll
+      for (int r = 0; r <= kPD; ++r) {
+        const int ii = base + r;
+        if (ii < cnt) {
+          if (ii + kPD < cnt)
+            load_tile<kFP8>(buf[(r + kPD) % (kPD + 1)], a,
+                            __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane);
+          const int tb = (blk0 + w + (c0 + ii) * kNW) * kBS;  // first token of the tile
+          process_tile<kFP8, kHwCvt, kSplitP>(buf[r], qop, st, tb, qg, L, a.qk_scale);
         }
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[m], s, 0, 0, 0);
       }
-
-      // online softmax over this block's 16 tokens (lane: 4 tokens, one head)
-      float sv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = (tb + qg * 4 + r < L) ? s[r] * a.qk_scale : -INFINITY;
-      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      bm = fmaxf(bm, wave_shfl_xor(bm, 16));
-      bm = fmaxf(bm, wave_shfl_xor(bm, 32));
-      const float m_new = fmaxf(m_run, bm);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float pr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - m_new);
-      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m_run = m_new;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] *= alpha;
-      }
-      // probabilities as fp16 hi + lo so the PV product keeps ~22 bits
-      f16x4 ph, pl;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ph[r] = (_Float16)pr[r];
-        pl[r] = (_Float16)(pr[r] - (float)ph[r]);
-      }
-      // O^T[d][g] += sum_t V^T[d][t] P^T[t][g]: 8 MFMAs of 16 channels
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        f16x4 va;
-        if (kFP8) {
-          const u32x4 raw = cur.v[n >> 2];
-          va = e4m3x4_to_f16_div256(raw[n & 3]);
-        } else {
-          const u32x4 raw = cur.v[n >> 1];
-          u32x2 two;
-          two.x = raw[(n & 1) * 2];
-          two.y = raw[(n & 1) * 2 + 1];
-          va = __builtin_bit_cast(f16x4, two);
-        }
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, acc[n], 0, 0, 0);
-      }
-      cur = nxt;
     }
   }
 
-  // sum of the four token rows of each head
-  l_run += wave_shfl_xor(l_run, 16);
-  l_run += wave_shfl_xor(l_run, 32);
+  // each head's sum over its four token rows
+  float l_run = st.l;
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
 
   // merge the kNW waves through LDS
   float* so = smem;                        // [kNW][G][D]
@@ -347,9 +417,9 @@ decode_partition_kernel(DecodeArgs a) {
   if (j < G) {
 #pragma unroll
     for (int n = 0; n < 8; ++n)
-      *reinterpret_cast<f32x4*>(so + (w * G + j) * kD + n * 16 + qg * 4) = acc[n];
+      *reinterpret_cast<f32x4*>(so + (w * G + j) * kD + n * 16 + qg * 4) = st.acc[n];
     if (qg == 0) {
-      sm[w * 16 + j] = m_run;
+      sm[w * 16 + j] = st.m_ref;
       sl[w * 16 + j] = l_run;
     }
   }
@@ -381,63 +451,124 @@ decode_partition_kernel(DecodeArgs a) {
   }
 }
 
-// Merge kernel.  Grid (Hq, B), 256 threads.  For sequences spanning n_p > 1
-// partitions: M = max m_p, out = out_scale * sum_p o_p 2^(m_p - M) /
-// sum_p l_p 2^(m_p - M).  Fixed summation order: results do not depend on
-// timing.
-__global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a) {
-  __shared__ float w_s[256];
-  __shared__ float red[256];
-  __shared__ f32x4 part[8][32];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int L = clamp_len(a, b);
-  const int n_p = (L + a.part - 1) / a.part;
-  if (n_p <= 1) return;  // written by the partition kernel
-  const int64_t row0 = ((int64_t)b * a.hq + h) * a.n_p_max;
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Merge kernel: for each (sequence, query head) whose sequence spans n_p > 1
+// partitions, M = max_p m_p and
+//   out = out_scale * sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+// kSplit = false: each of the 4 waves of a workgroup merges its own (b, h);
+// kSplit = true: the 4 waves share one (b, h), wave w taking partitions
+// w, w + 4, ..., and combine through LDS (for many partitions).
+// Lane i owns channels 2i, 2i+1; partition weights live one per lane and are
+// broadcast with readlane.  The summation order is fixed, so results do not
+// depend on timing.
+constexpr int kFewPartitions = 8;
+
+template <bool kSplit>
+__global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a, int64_t rows) {
+  __shared__ float2 part[kRW][kWave];
+  __shared__ float dens[kRW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t bh = kSplit ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kRW + w;
+  if (bh >= rows) return;                    // only when !kSplit: whole waves leave
+  const int b = (int)(bh / a.hq);
+  const int n_p = seq_split(a, clamp_len(a, b)).n_p;
+  if (n_p <= 1) return;                      // written by the partition kernel
+  const int64_t row0 = bh * a.n_p_max;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+
+  if (!kSplit && n_p <= kFewPartitions) {
+    // few partitions: issue every load before the max reduction
+    const float2 mine = lane < n_p ? ml[row0 + lane] : make_float2(-INFINITY, 0.0f);
+    const float2* orow = reinterpret_cast<const float2*>(a.ws_o + row0 * kD) + lane;
+    float2 o[kFewPartitions];
+#pragma unroll
+    for (int k = 0; k < kFewPartitions; ++k)
+      o[k] = k < n_p ? orow[k * (kD / 2)] : make_float2(0.f, 0.f);
+    const float mx = wave_max(mine.x);
+    const float wgt = lane < n_p ? __builtin_amdgcn_exp2f(mine.x - mx) : 0.0f;
+    const float den = wave_sum(mine.y * wgt);
+    float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kFewPartitions; ++k) {
+      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
+      acc.x += o[k].x * g;
+      acc.y += o[k].y * g;
+    }
+    const float scale = a.out_scale / den;
+    reinterpret_cast<float2*>(a.out + bh * kD)[lane] = make_float2(acc.x * scale, acc.y * scale);
+    return;
+  }
 
   float mx = -INFINITY;
-  for (int pp = tid; pp < n_p; pp += 256) mx = fmaxf(mx, a.ws_ml[(row0 + pp) * 2]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
-  }
-  mx = red[0];
-  __syncthreads();
+  for (int pp = lane; pp < n_p; pp += kWave) mx = fmaxf(mx, ml[row0 + pp].x);
+  mx = wave_max(mx);
 
-  const int rg = tid >> 5, c4 = tid & 31;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int p0 = kSplit ? w : 0, ps = kSplit ? kRW : 1;
+  float2 acc = make_float2(0.f, 0.f);
   float den = 0.0f;
-  for (int cb = 0; cb < n_p; cb += 256) {
-    const int pp = cb + tid;
+  for (int c = p0; c < n_p; c += kWave * ps) {
+    const int mine = c + lane * ps;          // this lane's partition of the chunk
     float wgt = 0.0f;
-    if (pp < n_p) {
-      wgt = __builtin_amdgcn_exp2f(a.ws_ml[(row0 + pp) * 2] - mx);
-      den += a.ws_ml[(row0 + pp) * 2 + 1] * wgt;
+    if (mine < n_p) {
+      const float2 v = ml[row0 + mine];
+      wgt = __builtin_amdgcn_exp2f(v.x - mx);
+      den += v.y * wgt;
     }
-    w_s[tid] = wgt;
-    __syncthreads();
-    const int rows = min(256, n_p - cb);
-    for (int r = rg; r < rows; r += 8) {
-      const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + (row0 + cb + r) * kD + c4 * 4);
-      acc += o * w_s[r];
+    const int cnt = min(kWave, (n_p - c + ps - 1) / ps);
+    const float2* orow = reinterpret_cast<const float2*>(a.ws_o + (row0 + c) * kD) + lane;
+    int k = 0;
+    for (; k + 4 <= cnt; k += 4) {
+      const float2 o0 = orow[(int64_t)(k + 0) * ps * (kD / 2)];
+      const float2 o1 = orow[(int64_t)(k + 1) * ps * (kD / 2)];
+      const float2 o2 = orow[(int64_t)(k + 2) * ps * (kD / 2)];
+      const float2 o3 = orow[(int64_t)(k + 3) * ps * (kD / 2)];
+      const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + 0));
+      const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + 1));
+      const float g2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + 2));
+      const float g3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + 3));
+      acc.x += o0.x * g0; acc.y += o0.y * g0;
+      acc.x += o1.x * g1; acc.y += o1.y * g1;
+      acc.x += o2.x * g2; acc.y += o2.y * g2;
+      acc.x += o3.x * g3; acc.y += o3.y * g3;
     }
-    __syncthreads();
+    for (; k < cnt; ++k) {
+      const float2 o = orow[(int64_t)k * ps * (kD / 2)];
+      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
+      acc.x += o.x * g; acc.y += o.y * g;
+    }
   }
-  red[tid] = den;
-  part[rg][c4] = acc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
+  den = wave_sum(den);
+  float2* dst = reinterpret_cast<float2*>(a.out + bh * kD) + lane;
+  if constexpr (!kSplit) {
+    const float scale = a.out_scale / den;
+    *dst = make_float2(acc.x * scale, acc.y * scale);
+  } else {
+    part[w][lane] = acc;
+    if (lane == 0) dens[w] = den;
     __syncthreads();
-  }
-  if (tid < 32) {
-    f32x4 sum = part[0][tid];
+    if (w == 0) {
+      float2 t = part[0][lane];
+      float dd = dens[0];
 #pragma unroll
-    for (int r = 1; r < 8; ++r) sum += part[r][tid];
-    const float scale = a.out_scale / red[0];
-    *reinterpret_cast<f32x4*>(a.out + ((int64_t)b * a.hq + h) * kD + tid * 4) = sum * scale;
+      for (int ww = 1; ww < kRW; ++ww) {
+        t.x += part[ww][lane].x;
+        t.y += part[ww][lane].y;
+        dd += dens[ww];
+      }
+      const float scale = a.out_scale / dd;
+      *dst = make_float2(t.x * scale, t.y * scale);
+    }
   }
 }
 
@@ -462,14 +593,27 @@ pkv_status launch_status() {
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+// Automatic partition length (measured on MI355X at the five reference
+// shapes): fewer, longer partitions are faster as long as enough tiles are in
+// flight to cover HBM latency -- about 2048 waves of FP8 tiles (4 KiB per
+// block and head) or 1024 waves of fp16 tiles (8 KiB).  So: the fewest
+// partitions per sequence that give that many waves (4 per workgroup), cut
+// into equal runs of whole blocks, at least 8 blocks each.  Batches with 1024
+// or more (sequence, KV head) pairs -- where lengths may be ragged -- cap a
+// partition at 512 blocks (8192 tokens) so that long sequences leave no tail;
+// otherwise the cap is 1024 blocks.
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
-                          int32_t requested) {
+                          int32_t dtype, int32_t requested) {
   if (requested < 0 || requested % kBS != 0) return -1;
   if (requested > 0) return requested;
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)max_ctx;
-  return 512;
+  const int64_t nblk = max_ctx > 0 ? ((int64_t)max_ctx + kBS - 1) / kBS : 1;
+  const int64_t pairs = std::max<int64_t>(1, (int64_t)num_seqs * std::max(1, num_kv_heads));
+  const int64_t target_waves = dtype == PKV_F16 ? 1024 : 2048;
+  int64_t n_p = (target_waves + 4 * pairs - 1) / (4 * pairs);
+  n_p = std::max<int64_t>(1, std::min<int64_t>(n_p, nblk / 8));
+  int64_t per = (nblk + n_p - 1) / n_p;
+  per = std::min<int64_t>(per, pairs >= 1024 ? 512 : 1024);
+  return (int32_t)(per * kBS);
 }
 
 struct WsLayout {
@@ -479,7 +623,10 @@ struct WsLayout {
 
 WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32_t part) {
   WsLayout w{0, 0, 0, 0};
-  w.n_p_max = max_ctx <= 0 ? 1 : (int32_t)(((int64_t)max_ctx + part - 1) / part);
+  // partitions of the longest sequence: ceil(blocks / (part / 16))
+  const int64_t nblk = ((int64_t)std::max(max_ctx, 0) + kBS - 1) / kBS;
+  const int64_t pb = part / kBS;
+  w.n_p_max = nblk == 0 ? 1 : (int32_t)((nblk + pb - 1) / pb);
   if (w.n_p_max <= 1) return w;
   const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)w.n_p_max;
   w.ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
@@ -488,10 +635,46 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32
   return w;
 }
 
+// Kernel variants, chosen once per process.  Environment overrides exist for
+// measurement (A/B runs of the same build); the defaults are the measured
+// best.
+//   PKV_FP8_DEQUANT = hw | bits   FP8 -> fp16 by the gfx950 conversion or by
+//                                 integer bit operations
+//   PKV_FP8_SPLIT_P = 0 | 1       probabilities as one fp16 or fp16 hi + lo
+//                                 (fp16 caches always use hi + lo)
+//   PKV_DECODE_PREFETCH = 1 | 2   tiles in flight per wave besides the one
+//                                 being computed
+//   PKV_DECODE_WAVES = 4 | 8      waves per partition workgroup
+struct KernelConfig {
+  bool hw_cvt;
+  bool split_p_fp8;
+  int prefetch;
+  int waves;
+};
+
+KernelConfig kernel_config() {
+  static const KernelConfig cfg = [] {
+    KernelConfig k{true, true, 1, 4};
+    if (const char* e = std::getenv("PKV_FP8_DEQUANT")) k.hw_cvt = std::strcmp(e, "hw") == 0;
+    if (const char* e = std::getenv("PKV_FP8_SPLIT_P")) k.split_p_fp8 = std::atoi(e) != 0;
+    if (const char* e = std::getenv("PKV_DECODE_PREFETCH")) {
+      const int v = std::atoi(e);
+      if (v >= 1 && v <= 2) k.prefetch = v;
+    }
+    if (const char* e = std::getenv("PKV_DECODE_WAVES")) {
+      const int v = std::atoi(e);
+      if (v == 4 || v == 8) k.waves = v;
+    }
+    return k;
+  }();
+  return cfg;
+}
+
 struct DecodePlan {
   DecodeArgs a;
   bool fp8;
   bool need_reduce;
+  KernelConfig cfg;
 };
 
 pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
@@ -522,7 +705,7 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
                v_scale > 0.0f))
     return PKV_ERR_INVALID_ARG;
   const int32_t part = resolve_partition(num_seqs, layout->num_kv_heads, max_context_len,
-                                         partition_size);
+                                         layout->dtype, partition_size);
   if (part <= 0) return PKV_ERR_INVALID_ARG;
   const WsLayout wl = ws_layout(num_seqs, num_q_heads, max_context_len, part);
   if (wl.total > 0) {
@@ -545,11 +728,14 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   a.hkv = layout->num_kv_heads;
   a.g = G;
   a.max_ctx = max_context_len;
-  a.part = part;
+  a.part_blocks = part / kBS;
   a.n_p_max = wl.n_p_max;
+  plan->cfg = kernel_config();
+  // FP8 tiles decoded by bit operations hold code / 256: fold the 256 back in
+  const float deq = (fp8 && !plan->cfg.hw_cvt) ? 256.0f : 1.0f;
   const float log2e = 1.4426950408889634f;
-  a.qk_scale = sm_scale * (fp8 ? k_scale * 256.0f : 1.0f) * log2e;
-  a.out_scale = fp8 ? v_scale * 256.0f : 1.0f;
+  a.qk_scale = sm_scale * (fp8 ? k_scale * deq : 1.0f) * log2e;
+  a.out_scale = fp8 ? v_scale * deq : 1.0f;
   plan->fp8 = fp8;
   plan->need_reduce = wl.n_p_max > 1;
   return PKV_OK;
@@ -560,15 +746,19 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
 // ------------------------------------------------------------------ C ABI
 
 extern "C" int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                             int32_t max_context_len, int32_t requested) {
-  return resolve_partition(num_seqs, num_kv_heads, max_context_len, requested);
+                                             int32_t max_context_len, int32_t dtype,
+                                             int32_t requested) {
+  if (dtype != PKV_F16 && dtype != PKV_FP8_E4M3FN) return -1;
+  return resolve_partition(num_seqs, num_kv_heads, max_context_len, dtype, requested);
 }
 
 extern "C" uint64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                int32_t num_kv_heads, int32_t max_context_len,
-                                               int32_t partition_size) {
+                                               int32_t dtype, int32_t partition_size) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
-  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+  if (dtype != PKV_F16 && dtype != PKV_FP8_E4M3FN) return 0;
+  const int32_t part =
+      resolve_partition(num_seqs, num_kv_heads, max_context_len, dtype, partition_size);
   if (part <= 0) return 0;
   return ws_layout(num_seqs, num_q_heads, max_context_len, part).total;
 }
@@ -608,22 +798,51 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
   return launch_status();
 }
 
+template <bool kFP8, bool kHw, bool kSplit, int kNW>
+static void launch_partition_v(int pd, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  const dim3 block(kNW * kWave);
+  const size_t lds = (size_t)(kNW * a.g * kD + 2 * kNW * 16) * sizeof(float);
+  if (pd == 2)
+    decode_partition_kernel<kFP8, kHw, kSplit, 2, kNW><<<grid, block, lds, s>>>(a);
+  else
+    decode_partition_kernel<kFP8, kHw, kSplit, 1, kNW><<<grid, block, lds, s>>>(a);
+}
+
+template <bool kFP8, bool kHw, bool kSplit>
+static void launch_partition(const KernelConfig& c, dim3 grid, hipStream_t s,
+                             const DecodeArgs& a) {
+  if (c.waves == 8)
+    launch_partition_v<kFP8, kHw, kSplit, 8>(c.prefetch, grid, s, a);
+  else
+    launch_partition_v<kFP8, kHw, kSplit, 4>(c.prefetch, grid, s, a);
+}
+
 static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStream_t s) {
   if (num_seqs == 0) return PKV_OK;
   const dim3 grid((unsigned)pl.a.n_p_max, (unsigned)pl.a.hkv, (unsigned)num_seqs);
-  const size_t lds = (size_t)(kNW * pl.a.g * kD + 2 * kNW * 16) * sizeof(float);
   (void)hipGetLastError();
-  if (pl.fp8)
-    decode_partition_kernel<true><<<grid, dim3(kNW * kWave), lds, s>>>(pl.a);
+  const KernelConfig& c = pl.cfg;
+  if (!pl.fp8)
+    launch_partition<false, false, true>(c, grid, s, pl.a);
+  else if (c.hw_cvt)
+    c.split_p_fp8 ? launch_partition<true, true, true>(c, grid, s, pl.a)
+                  : launch_partition<true, true, false>(c, grid, s, pl.a);
   else
-    decode_partition_kernel<false><<<grid, dim3(kNW * kWave), lds, s>>>(pl.a);
+    c.split_p_fp8 ? launch_partition<true, false, true>(c, grid, s, pl.a)
+                  : launch_partition<true, false, false>(c, grid, s, pl.a);
   return launch_status();
 }
 
 static pkv_status run_reduce(const DecodePlan& pl, int32_t num_seqs, hipStream_t s) {
   if (num_seqs == 0 || !pl.need_reduce) return PKV_OK;
   (void)hipGetLastError();
-  decode_reduce_kernel<<<dim3((unsigned)pl.a.hq, (unsigned)num_seqs), dim3(256), 0, s>>>(pl.a);
+  const int64_t rows = (int64_t)num_seqs * pl.a.hq;
+  if (pl.a.n_p_max > 32) {
+    decode_reduce_kernel<true><<<dim3((unsigned)rows), dim3(256), 0, s>>>(pl.a, rows);
+  } else {
+    const int64_t grid = (rows + kRW - 1) / kRW;
+    decode_reduce_kernel<false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(pl.a, rows);
+  }
   return launch_status();
 }
 

@@ -50,16 +50,27 @@ def test_pool_bytes():
 
 
 def test_partition_size_and_workspace():
-    assert pkv.pkv_decode_partition_size(4, 8, 131072, 512) == 512
-    assert pkv.pkv_decode_partition_size(4, 8, 131072, 500) == -1
-    assert pkv.pkv_decode_partition_size(4, 8, 131072, -16) == -1
-    auto = pkv.pkv_decode_partition_size(64, 8, 8193, 0)
-    assert auto > 0 and auto % 16 == 0
+    F8, F16 = pkv.PKV_FP8_E4M3FN, pkv.PKV_F16
+    assert pkv.pkv_decode_partition_size(4, 8, 131072, F8, 512) == 512
+    assert pkv.pkv_decode_partition_size(4, 8, 131072, F8, 500) == -1
+    assert pkv.pkv_decode_partition_size(4, 8, 131072, F8, -16) == -1
+    assert pkv.pkv_decode_partition_size(4, 8, 131072, 9, 0) == -1
+    for args in [(64, 8, 8193, F8), (32, 8, 4096, F16), (4, 8, 131072, F8), (4, 2, 244, F8),
+                 (256, 8, 18401, F8), (1, 1, 1, F16)]:
+        auto = pkv.pkv_decode_partition_size(*args, 0)
+        assert auto > 0 and auto % 16 == 0, args
+    # one partition per sequence when the pairs alone give enough waves
+    assert pkv.pkv_decode_partition_size(64, 8, 8193, F8, 0) >= 8193
+    # partitions are capped for big, possibly ragged batches
+    assert pkv.pkv_decode_partition_size(256, 8, 18401, F8, 0) <= 8192
     # 4 x 64 heads x 256 partitions x (2 + 128) floats, the max/sum block 256-aligned
-    ws = pkv.pkv_decode_workspace_bytes(4, 64, 8, 131072, 512)
+    ws = pkv.pkv_decode_workspace_bytes(4, 64, 8, 131072, F8, 512)
     rows = 4 * 64 * 256
     assert ws == (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
-    assert pkv.pkv_decode_workspace_bytes(4, 64, 8, 512, 512) == 0   # one partition: no merge
+    assert pkv.pkv_decode_workspace_bytes(4, 64, 8, 512, F8, 512) == 0   # one partition: no merge
+    # balanced split: 8193 tokens in partitions of at most 2048 -> 5 partitions
+    ws5 = pkv.pkv_decode_workspace_bytes(1, 1, 1, 8193, F8, 2048)
+    assert ws5 == (5 * 8 + 255) // 256 * 256 + 5 * 128 * 4
 
 
 def test_status_strings():

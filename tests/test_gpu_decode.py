@@ -210,7 +210,7 @@ def test_split_halves_equal_combined_call():
     whole = prep.gpu_decode()
     out = torch.empty_like(prep.q, dtype=torch.float32)
     need = pkv.pkv_decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
-                                          wl.max_context_len, 48)
+                                          wl.max_context_len, prep.layout.dtype, 48)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     pkv.pkv_decode_partitions(out, prep.q, prep.k_pool, prep.v_pool, prep.tables, prep.lens,
                               wl.max_context_len, prep.layout, prep.sm_scale, prep.k_scale,
