@@ -71,6 +71,27 @@ def _load():
     return lib
 
 
+def _swap_library(path: str):
+    """Load the oracle from another build of pkv_oracle.c (used by the tests
+    that plant mistakes in copies of the oracle to show its pins catch them);
+    returns the previously loaded library so it can be restored."""
+    global _lib
+    prev = _load()
+    _lib = None
+    global _LIB_PATH
+    saved, _LIB_PATH = _LIB_PATH, path
+    try:
+        _load()
+    finally:
+        _LIB_PATH = saved
+    return prev
+
+
+def _restore_library(lib) -> None:
+    global _lib
+    _lib = lib
+
+
 def _ptr(a: np.ndarray):
     assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
     return ctypes.c_void_p(a.ctypes.data)

@@ -169,11 +169,25 @@ int64_t oracle_slot(const int32_t* table_row, int64_t pos) {
 /* Store T new K/V rows ([T][Hkv][D] fp16 bits) into their slots.  fp16 pools
  * get the bits as they are; FP8 pools get E4M3(x / scale) ([FP8-128K] §4:
  * the new rows are turned into 8-bit values as they are written).  A negative
- * slot, or one past the pool, is skipped. */
+ * slot, or one past the pool, is skipped.  The code of an element depends only
+ * on its 16 input bits and the scale, so each of the 65536 inputs is encoded
+ * once per scale by the brute-force search and then looked up. */
 void oracle_reshape_and_cache(const uint16_t* key, const uint16_t* value, uint8_t* k_pool,
                               uint8_t* v_pool, const int64_t* slots, int T, int Hkv, int D,
                               int num_blocks, int fp8, float k_scale, float v_scale) {
   int e = fp8 ? 1 : 2;
+  uint8_t *klut = NULL, *vlut = NULL;
+  if (fp8) {
+    klut = (uint8_t*)malloc(65536);
+    vlut = (uint8_t*)malloc(65536);
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < 65536; ++h) {
+      double x = oracle_f16_to_double((uint16_t)h);
+      klut[h] = oracle_e4m3_encode(oracle_quotient(x, k_scale));
+      vlut[h] = oracle_e4m3_encode(oracle_quotient(x, v_scale));
+    }
+  }
+#pragma omp parallel for schedule(static)
   for (int i = 0; i < T; ++i) {
     int64_t s = slots[i];
     if (s < 0 || s >= (int64_t)num_blocks * ORC_BS)
@@ -186,14 +200,16 @@ void oracle_reshape_and_cache(const uint16_t* key, const uint16_t* value, uint8_
         int64_t ka = orc_addr(0, block, h, t, d, Hkv, D, e);
         int64_t va = orc_addr(1, block, h, t, d, Hkv, D, e);
         if (fp8) {
-          k_pool[ka] = oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double(key[src]), k_scale));
-          v_pool[va] = oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double(value[src]), v_scale));
+          k_pool[ka] = klut[key[src]];
+          v_pool[va] = vlut[value[src]];
         } else {
           memcpy(k_pool + ka, key + src, 2);
           memcpy(v_pool + va, value + src, 2);
         }
       }
   }
+  free(klut);
+  free(vlut);
 }
 
 /* ------------------------------------------------------------------- decode */

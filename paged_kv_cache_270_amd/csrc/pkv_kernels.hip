@@ -84,30 +84,18 @@ __device__ __forceinline__ f16x4 e4m3x4_to_f16_div256(uint32_t x) {
 
 // ------------------------------------------------------ reshape_and_cache
 
-// One thread per (token, kv head, run of 8 channels): 16 bytes of fp16 in.
+// Store channels 8c .. 8c+7 of one token's K and V rows (16 bytes of fp16
+// each) at position t of tile `tile` (= block * hkv + head).
 template <bool kFP8>
-__global__ void __launch_bounds__(256)
-reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
-                         uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-                         const int64_t* __restrict__ slots, int64_t total, int hkv,
-                         int64_t num_slots, float k_scale, float v_scale) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;
-  const int c = (int)(gid & 15);          // channels 8c .. 8c+7
-  const int64_t th = gid >> 4;            // token * hkv + head
-  const int64_t tok = th / hkv;
-  const int h = (int)(th - tok * hkv);
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot >> 4;
-  const int t = (int)(slot & 15);
-  const u32x4 kin = key[th * 16 + c];
-  const u32x4 vin = value[th * 16 + c];
+__device__ __forceinline__ void store_rows8(uint8_t* __restrict__ k_pool,
+                                            uint8_t* __restrict__ v_pool, int64_t tile, int t,
+                                            int c, u32x4 kin, u32x4 vin, float k_scale,
+                                            float v_scale) {
   const int n = c >> 1;                   // 16-channel group of these channels
   const int j0 = (c & 1) * 8;             // channel within the group
-  if (!kFP8) {
-    uint16_t* kp = reinterpret_cast<uint16_t*>(k_pool) + (blk * hkv + h) * (kBS * kD);
-    uint16_t* vp = reinterpret_cast<uint16_t*>(v_pool) + (blk * hkv + h) * (kBS * kD);
+  if constexpr (!kFP8) {
+    uint16_t* kp = reinterpret_cast<uint16_t*>(k_pool) + tile * (kBS * kD);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(v_pool) + tile * (kBS * kD);
     // K, x = 8: (d/8)*128 + t*8 + d%8 -> the 8 channels are contiguous
     *reinterpret_cast<u32x4*>(kp + c * 128 + t * 8) = kin;
     // V, x = 8: (n/2)*512 + ((t/4)*16 + d%16)*8 + (n%2)*4 + t%4
@@ -116,8 +104,8 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
 #pragma unroll
     for (int i = 0; i < 8; ++i) vb[i * 8] = vh[i];
   } else {
-    uint8_t* kp = k_pool + (blk * hkv + h) * (kBS * kD);
-    uint8_t* vp = v_pool + (blk * hkv + h) * (kBS * kD);
+    uint8_t* kp = k_pool + tile * (kBS * kD);
+    uint8_t* vp = v_pool + tile * (kBS * kD);
     const _Float16* kh = reinterpret_cast<const _Float16*>(&kin);
     const _Float16* vh = reinterpret_cast<const _Float16*>(&vin);
     uint32_t kc[8], vc[8];
@@ -136,6 +124,25 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
 #pragma unroll
     for (int i = 0; i < 8; ++i) vb[i * 16] = (uint8_t)vc[i];
   }
+}
+
+// One thread per (token, kv head, run of 8 channels): 16 bytes of fp16 in.
+template <bool kFP8>
+__global__ void __launch_bounds__(256)
+reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                         uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                         const int64_t* __restrict__ slots, int64_t total, int hkv,
+                         int64_t num_slots, float k_scale, float v_scale) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int c = (int)(gid & 15);          // channels 8c .. 8c+7
+  const int64_t th = gid >> 4;            // token * hkv + head
+  const int64_t tok = th / hkv;
+  const int h = (int)(th - tok * hkv);
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  store_rows8<kFP8>(k_pool, v_pool, (slot >> 4) * hkv + h, (int)(slot & 15), c,
+                    key[th * 16 + c], value[th * 16 + c], k_scale, v_scale);
 }
 
 // ------------------------------------------------------------ copy_blocks
@@ -644,7 +651,8 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32
 //                                 (fp16 caches always use hi + lo)
 //   PKV_DECODE_PREFETCH = 1 | 2   tiles in flight per wave besides the one
 //                                 being computed
-//   PKV_DECODE_WAVES = 4 | 8      waves per partition workgroup
+//   PKV_DECODE_WAVES = 1|2|4|8    waves per partition workgroup (default:
+//                                 from the partition length)
 struct KernelConfig {
   bool hw_cvt;
   bool split_p_fp8;
@@ -654,7 +662,7 @@ struct KernelConfig {
 
 KernelConfig kernel_config() {
   static const KernelConfig cfg = [] {
-    KernelConfig k{true, true, 1, 4};
+    KernelConfig k{true, true, 1, 0};
     if (const char* e = std::getenv("PKV_FP8_DEQUANT")) k.hw_cvt = std::strcmp(e, "hw") == 0;
     if (const char* e = std::getenv("PKV_FP8_SPLIT_P")) k.split_p_fp8 = std::atoi(e) != 0;
     if (const char* e = std::getenv("PKV_DECODE_PREFETCH")) {
@@ -663,7 +671,7 @@ KernelConfig kernel_config() {
     }
     if (const char* e = std::getenv("PKV_DECODE_WAVES")) {
       const int v = std::atoi(e);
-      if (v == 4 || v == 8) k.waves = v;
+      if (v == 1 || v == 2 || v == 4 || v == 8) k.waves = v;
     }
     return k;
   }();
@@ -690,6 +698,10 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   if (num_q_heads % layout->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   const int32_t G = num_q_heads / layout->num_kv_heads;
   if (G > kMaxG) return PKV_ERR_UNSUPPORTED;
+  plan->cfg = kernel_config();
+  plan->fp8 = layout->dtype == PKV_FP8_E4M3FN;
+  plan->need_reduce = false;
+  if (num_seqs == 0) return PKV_OK;  // nothing to compute; no pointer is touched
   if (!out || !context_lens || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
   if (need_pools) {
     if (!q || !k_pool || !v_pool || !block_tables) return PKV_ERR_INVALID_ARG;
@@ -798,23 +810,51 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
   return launch_status();
 }
 
-template <bool kFP8, bool kHw, bool kSplit, int kNW>
-static void launch_partition_v(int pd, dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  const dim3 block(kNW * kWave);
+template <bool kFP8, bool kHw, bool kSplit, int kPD, int kNW>
+static void launch_partition_v(dim3 grid, hipStream_t s, const DecodeArgs& a) {
   const size_t lds = (size_t)(kNW * a.g * kD + 2 * kNW * 16) * sizeof(float);
-  if (pd == 2)
-    decode_partition_kernel<kFP8, kHw, kSplit, 2, kNW><<<grid, block, lds, s>>>(a);
-  else
-    decode_partition_kernel<kFP8, kHw, kSplit, 1, kNW><<<grid, block, lds, s>>>(a);
+  decode_partition_kernel<kFP8, kHw, kSplit, kPD, kNW><<<grid, dim3(kNW * kWave), lds, s>>>(a);
 }
 
+// The measured default family (hardware convert, split P) exists for every
+// prefetch depth and wave count; the A/B variants only at the default shape.
 template <bool kFP8, bool kHw, bool kSplit>
-static void launch_partition(const KernelConfig& c, dim3 grid, hipStream_t s,
-                             const DecodeArgs& a) {
-  if (c.waves == 8)
-    launch_partition_v<kFP8, kHw, kSplit, 8>(c.prefetch, grid, s, a);
-  else
-    launch_partition_v<kFP8, kHw, kSplit, 4>(c.prefetch, grid, s, a);
+static void launch_partition(int pd, int nw, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  constexpr bool kFull = !kFP8 || (kHw && kSplit);
+  if constexpr (kFull) {
+    if (pd == 2) {
+      switch (nw) {
+        case 1: return launch_partition_v<kFP8, kHw, kSplit, 2, 1>(grid, s, a);
+        case 2: return launch_partition_v<kFP8, kHw, kSplit, 2, 2>(grid, s, a);
+        case 8: return launch_partition_v<kFP8, kHw, kSplit, 2, 8>(grid, s, a);
+        default: return launch_partition_v<kFP8, kHw, kSplit, 2, 4>(grid, s, a);
+      }
+    }
+    switch (nw) {
+      case 1: return launch_partition_v<kFP8, kHw, kSplit, 1, 1>(grid, s, a);
+      case 2: return launch_partition_v<kFP8, kHw, kSplit, 1, 2>(grid, s, a);
+      case 8: return launch_partition_v<kFP8, kHw, kSplit, 1, 8>(grid, s, a);
+      default: return launch_partition_v<kFP8, kHw, kSplit, 1, 4>(grid, s, a);
+    }
+  } else {
+    (void)pd;
+    (void)nw;
+    launch_partition_v<kFP8, kHw, kSplit, 1, 4>(grid, s, a);
+  }
+}
+
+// Waves per partition workgroup: each wave should stream at least 16 tiles,
+// so short partitions get fewer waves (and skip most of the LDS merge).
+static int waves_for(const DecodePlan& pl) {
+  int nw = pl.cfg.waves;
+  if (nw <= 0) {
+    const int per_wave_tiles = 16;
+    const int want = pl.a.part_blocks / per_wave_tiles;
+    nw = want >= 4 ? 4 : (want >= 2 ? 2 : 1);
+  }
+  // the LDS merge buffer must fit one workgroup's 64 KiB
+  while (nw > 1 && (size_t)(nw * pl.a.g * kD + 2 * nw * 16) * sizeof(float) > 65536) nw /= 2;
+  return nw;
 }
 
 static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStream_t s) {
@@ -822,14 +862,15 @@ static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStre
   const dim3 grid((unsigned)pl.a.n_p_max, (unsigned)pl.a.hkv, (unsigned)num_seqs);
   (void)hipGetLastError();
   const KernelConfig& c = pl.cfg;
+  const int nw = waves_for(pl);
   if (!pl.fp8)
-    launch_partition<false, false, true>(c, grid, s, pl.a);
+    launch_partition<false, false, true>(c.prefetch, nw, grid, s, pl.a);
   else if (c.hw_cvt)
-    c.split_p_fp8 ? launch_partition<true, true, true>(c, grid, s, pl.a)
-                  : launch_partition<true, true, false>(c, grid, s, pl.a);
+    c.split_p_fp8 ? launch_partition<true, true, true>(c.prefetch, nw, grid, s, pl.a)
+                  : launch_partition<true, true, false>(c.prefetch, nw, grid, s, pl.a);
   else
-    c.split_p_fp8 ? launch_partition<true, false, true>(c, grid, s, pl.a)
-                  : launch_partition<true, false, false>(c, grid, s, pl.a);
+    c.split_p_fp8 ? launch_partition<true, false, true>(c.prefetch, nw, grid, s, pl.a)
+                  : launch_partition<true, false, false>(c.prefetch, nw, grid, s, pl.a);
   return launch_status();
 }
 

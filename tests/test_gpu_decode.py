@@ -219,3 +219,72 @@ def test_split_halves_equal_combined_call():
                           prep.layout, prep.v_scale, 48, ws)
     torch.cuda.synchronize()
     assert np.array_equal(whole.view(np.uint32), out.cpu().numpy().view(np.uint32))
+
+
+def _small_workload(lens, hq=8, hkv=2, fp8=True, extra_blocks=4, seed=50):
+    rng = np.random.default_rng(seed)
+    need = [-(-int(L) // 16) for L in lens]
+    nb = sum(need) + extra_blocks
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.zeros((len(lens), max(1, max(need))), dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[pos:pos + n]
+        pos += n
+    return workloads.Workload("small", seed, hq, hkv, fp8, nb, np.asarray(lens, dtype=np.int32), bt)
+
+
+def test_out_of_range_block_ids_are_skipped():
+    """Ids outside the pool are never read; the other sequences are intact."""
+    wl = _small_workload([40, 70, 33])
+    prep = Prepared(wl)
+    ref = prep.oracle_decode()
+    bad = wl.block_tables.copy()
+    bad[1, 2] = wl.num_blocks + 1000
+    bad[1, 3] = -7
+    got = prep.gpu_decode(tables=torch.from_numpy(bad).cuda())
+    for b in (0, 2):
+        assert max_err(got[b], ref[b]) <= TOL[True]
+
+
+def test_lengths_are_clamped_to_the_table_and_max_context():
+    wl = _small_workload([40, 70, 33])
+    prep = Prepared(wl)
+    mb = wl.block_tables.shape[1]                    # 5 blocks = 80 tokens
+    full = prep.gpu_decode(lens=torch.tensor([80, 80, 80], dtype=torch.int32, device="cuda"),
+                           max_context_len=80)
+    over = prep.gpu_decode(lens=torch.tensor([80 + 9, 1000, 80], dtype=torch.int32, device="cuda"),
+                           max_context_len=80)
+    assert mb * 16 == 80
+    assert np.array_equal(full.view(np.uint32), over.view(np.uint32))
+    # max_context_len below some lengths: those are attended over max_context_len tokens
+    short = prep.gpu_decode(lens=torch.tensor([48, 48, 33], dtype=torch.int32, device="cuda"),
+                            max_context_len=48)
+    capped = prep.gpu_decode(lens=torch.tensor([70, 48, 33], dtype=torch.int32, device="cuda"),
+                             max_context_len=48)
+    assert np.array_equal(short.view(np.uint32), capped.view(np.uint32))
+
+
+def test_negative_length_gives_zeros_and_empty_batch_is_a_no_op():
+    wl = _small_workload([40, 70])
+    prep = Prepared(wl)
+    got = prep.gpu_decode(lens=torch.tensor([-5, 70], dtype=torch.int32, device="cuda"))
+    assert np.all(got[0] == 0)
+    out = torch.full((0, 8, 128), 7.0, dtype=torch.float32, device="cuda")
+    pkv.pkv_paged_attention_decode(out, prep.q[:0], prep.k_pool, prep.v_pool, prep.tables[:0],
+                                   prep.lens[:0], 0, prep.layout, prep.sm_scale, prep.k_scale,
+                                   prep.v_scale)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4])
+def test_each_wave_count_matches_the_oracle(waves, monkeypatch):
+    """Short and long partitions select 1, 2 or 4 waves per workgroup; check a
+    partition length that lands on each choice."""
+    ps = {1: 256, 2: 512, 4: 1024}[waves]
+    wl = _small_workload([1, 300, 1100, 2100], hq=16, hkv=2, seed=60 + waves)
+    wl.partition_size = ps
+    prep = Prepared(wl)
+    err = max_err(prep.gpu_decode(), prep.oracle_decode())
+    _report(f"partition {ps} (waves {waves})", err, TOL[True])
+    assert err <= TOL[True]
