@@ -1,21 +1,25 @@
 #!/usr/bin/env python3
-"""Benchmark: one decode step of PagedAttention at the Llama-3.1-70B layer
-shape with an FP8 E4M3 KV cache, on one MI355X.
+"""Benchmark: one decode step of PagedAttention over a paged FP8 KV cache on one
+MI355X.
 
-Workload (the shape of "Optimización de KV Cache con PagedAttention y
-Cuantización FP8 ...", §2, at one layer): 64 sequences, 8192 cached tokens
-each plus one new token, 64 query / 8 KV heads, head dim 128, 16-token blocks
-scattered over a shuffled pool of 36864 blocks, per-tensor scales amax/448.
+Default workload (the metric's): the Llama-3.1-70B layer shape of "Optimización
+de KV Cache con PagedAttention y Cuantización FP8 ...", §2 -- 64 sequences,
+8192 cached tokens each plus one new token, 64 query / 8 KV heads, head dim
+128, 16-token blocks scattered over a shuffled pool of 36864 blocks, FP8 E4M3
+cache with per-tensor scales amax/448.  `--workload` selects the other
+reference shapes (tiny, fp16 batch, 128K contexts, ragged shared prefixes).
 
-A step is the whole hot path on one batch: the host assigns the new tokens'
-slots (block pool, done once in set-up since it changes the state), then on
-the device pkv_reshape_and_cache stores the 64 new K/V rows into their FP8
-slots, then the partition kernel attends over L = 8193 tokens per sequence
-(split-KV partitions, merged by a second kernel when a sequence spans
-several).
+Every workload is built through the library's host block pool: sequences are
+created and grown block by block (forked from a group leader where they share
+a prefix), cached tokens are written by pkv_reshape_and_cache, and the pool
+hands out each sequence's slot for the new token (timed: host_slot_assignment).
 
-Prints one JSON line.  `value` = KV bytes the step must read (every cached
-token once, K and V, all KV heads: 1,073,872,896 B) / step time, in GB/s.
+A step is the whole hot path on one batch: pkv_reshape_and_cache stores each
+sequence's new K/V row into its slot, then the partition kernel attends over
+L tokens per sequence and, when some sequence spans several partitions, the
+merge kernel combines them.  Prints one JSON line; `value` = KV bytes the step
+must read from HBM (each stored token once, K and V, all KV heads) / step
+time, in GB/s.
 """
 import argparse
 import hashlib
@@ -28,8 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+METRIC = "KV GB/s read (% of HBM peak) + decode seqs·tok/s, 70B-layer shape, FP8 KV"
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_270_amd", "csrc", "pkv_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_partition_llama70b_fp8.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_sha() -> str:
@@ -37,11 +42,11 @@ def kernel_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the partition kernel from the committed
-    rocprofv3 counter runs, if they were taken on the current kernel source."""
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the partition kernel from committed rocprofv3
+    counter runs for this workload, if taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(TRAFFIC_DIR, f"traffic_decode_partition_{workload}.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -63,12 +68,55 @@ def copy_probe(mib: int) -> int:
     return 0
 
 
+def build_sequences(pkv, wl):
+    """Grow the workload's sequences in the library's block pool.
+
+    Returns (pool, seq ids, cached-token slots per sequence (a shared prefix
+    listed under every member), slots written once (the bulk fill), new-token
+    slots, host microseconds spent assigning the new tokens' slots)."""
+    import numpy as np
+    pool = pkv.BlockPool(wl.num_blocks, shuffle_seed=wl.seed)
+    lens = [int(x) for x in wl.context_lens]
+    seqs, per_seq, written = [], [], []
+    if wl.groups:
+        for members in wl.groups:
+            leader = pool.create()
+            prefix = pool.append(leader, wl.prefix_blocks * 16)[0]
+            written.extend(prefix)
+            ids = [leader] + [pool.fork(leader) for _ in members[1:]]
+            for sid, b in zip(ids, members):
+                tail = pool.append(sid, lens[b] - len(prefix) - 1)[0]
+                written.extend(tail)
+                seqs.append(sid)
+                per_seq.append(list(prefix) + tail)
+    else:
+        for L in lens:
+            sid = pool.create()
+            got = pool.append(sid, max(L - 1, 0))[0]
+            written.extend(got)
+            seqs.append(sid)
+            per_seq.append(got)
+    import gc
+    gc.disable()                      # time the appends, not a collection of set-up lists
+    t0 = time.perf_counter()
+    step_slots = [pool.append(sid, 1)[0][0] for sid in seqs]
+    host_us = (time.perf_counter() - t0) * 1e6
+    gc.enable()
+    return (pool, seqs, per_seq, np.asarray(written, dtype=np.int64),
+            np.asarray(step_slots, dtype=np.int64), host_us)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--workload", default="llama70b_fp8",
+                    help="llama70b_fp8 (default) | llama70b_fp16 | long_context | "
+                         "shared_prefix | tiny")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="longest split-KV partition in tokens (default: the workload's "
+                         "own, else the library's choice)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8,
                     help="sequences of the workload the CPU oracle baseline decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -92,43 +140,52 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     dev = "cuda"
-    B, cached, Hq, Hkv, D, NB = 64, 8192, 64, 8, 128, 36864
-    L = cached + 1
-    layout = pkv.CacheLayout(NB, Hkv, pkv.PKV_FP8_E4M3FN)
+    wl = workloads.CONFIGS[args.workload]()
+    B, Hq, Hkv, D, NB = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, workloads.D, wl.num_blocks
+    Lmax = wl.max_context_len
+    e = wl.elem_bytes
+    layout = pkv.CacheLayout(NB, Hkv, pkv.PKV_FP8_E4M3FN if wl.fp8 else pkv.PKV_F16)
 
-    # ---- a1 on the host: block pool, on-demand allocation, shuffled placement
-    pool = pkv.BlockPool(NB, shuffle_seed=3)
-    seqs = [pool.create() for _ in range(B)]
-    bulk_slots = np.concatenate([np.asarray(pool.append(s, cached)[0]) for s in seqs])
-    t0 = time.perf_counter()
-    step_slots = np.array([pool.append(s, 1)[0][0] for s in seqs], dtype=np.int64)
-    host_slot_us = (time.perf_counter() - t0) * 1e6
-    tables = np.stack([np.asarray(pool.block_table(s), dtype=np.int32) for s in seqs])
-    assert tables.shape == (B, L // 16 + 1)
+    # ---- a1 on the host: block pool, on-demand allocation, forks, shuffled placement
+    pool, seqs, per_seq, bulk_slots, step_slots, host_slot_us = build_sequences(pkv, wl)
+    lens = np.array([pool.seq_len(s) for s in seqs], dtype=np.int32)
+    assert np.array_equal(lens, wl.context_lens)
+    rows = [pool.block_table(s) for s in seqs]
+    # cache hint: leading blocks each sequence shares with others (refcount > 1)
+    shared = np.array([pool.shared_prefix_blocks(s) for s in seqs], dtype=np.int32)
+    tables = np.zeros((B, max(len(r) for r in rows)), dtype=np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = r
 
     # ---- inputs resident in HBM
-    key_src = workloads.randn_f16((B * cached, Hkv, D), 301, dev)
-    val_src = workloads.randn_f16((B * cached, Hkv, D), 302, dev)
+    T = int(bulk_slots.size)
+    key_src = workloads.randn_f16((T, Hkv, D), 301, dev)
+    val_src = workloads.randn_f16((T, Hkv, D), 302, dev)
     new_k = workloads.randn_f16((B, Hkv, D), 303, dev)
     new_v = workloads.randn_f16((B, Hkv, D), 304, dev)
     q = workloads.randn_f16((B, Hq, D), 305, dev)
-    k_scale = float(np.float32(max(key_src.abs().max().item(), new_k.abs().max().item())) /
-                    np.float32(448))
-    v_scale = float(np.float32(max(val_src.abs().max().item(), new_v.abs().max().item())) /
-                    np.float32(448))
+    if wl.fp8:
+        k_scale = float(np.float32(max(key_src.abs().max().item(), new_k.abs().max().item())) /
+                        np.float32(448))
+        v_scale = float(np.float32(max(val_src.abs().max().item(), new_v.abs().max().item())) /
+                        np.float32(448))
+    else:
+        k_scale = v_scale = 1.0
     k_pool = torch.zeros(pkv.pkv_pool_bytes(layout), dtype=torch.uint8, device=dev)
     v_pool = torch.zeros_like(k_pool)
-    d_bulk_slots = torch.from_numpy(bulk_slots.astype(np.int64)).to(dev)
+    d_bulk_slots = torch.from_numpy(bulk_slots).to(dev)
     d_step_slots = torch.from_numpy(step_slots).to(dev)
     d_tables = torch.from_numpy(tables).to(dev)
-    d_lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    d_lens = torch.from_numpy(lens).to(dev)
+    d_shared = torch.from_numpy(shared).to(dev) if shared.any() else None
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     sm_scale = float(np.float32(1 / np.sqrt(D)))
-    P = pkv.pkv_decode_partition_size(B, Hkv, L, layout.dtype, args.partition_size)
-    ws = torch.empty(max(1, pkv.pkv_decode_workspace_bytes(B, Hq, Hkv, L, layout.dtype, P)),
+    req = wl.partition_size if args.partition_size is None else args.partition_size
+    P = pkv.pkv_decode_partition_size(B, Hkv, Lmax, layout.dtype, req)
+    ws = torch.empty(max(1, pkv.pkv_decode_workspace_bytes(B, Hq, Hkv, Lmax, layout.dtype, P)),
                      dtype=torch.uint8, device=dev)
 
-    # ---- bulk fill (prefill-sized write of 524288 tokens), timed on its own
+    # ---- bulk fill (a prefill-sized write of every cached token), timed on its own
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -137,7 +194,7 @@ def main() -> int:
     e1.record()
     torch.cuda.synchronize()
     bulk_ms = e0.elapsed_time(e1)
-    bulk_bytes = B * cached * Hkv * D * 2 * (2 + 1) + B * cached * 8   # fp16 in, FP8 out, slots
+    bulk_bytes = T * Hkv * D * 2 * (2 + e) + T * 8   # fp16 rows in, cache rows out, slots
     del key_src, val_src
 
     def step(ev=None):
@@ -145,11 +202,12 @@ def main() -> int:
                                   v_scale)
         if ev is not None:
             ev[0].record()
-        pkv.pkv_decode_partitions(out, q, k_pool, v_pool, d_tables, d_lens, L, layout,
-                                  sm_scale, k_scale, v_scale, P, ws)
+        pkv.pkv_decode_partitions(out, q, k_pool, v_pool, d_tables, d_lens, Lmax, layout,
+                                  sm_scale, k_scale, v_scale, P, ws,
+                                  shared_prefix_blocks=d_shared)
         if ev is not None:
             ev[1].record()
-        pkv.pkv_decode_reduce(out, d_lens, L, tables.shape[1], layout, v_scale, P, ws)
+        pkv.pkv_decode_reduce(out, d_lens, Lmax, tables.shape[1], layout, v_scale, P, ws)
 
     def timed(fn):
         torch.cuda.synchronize()
@@ -174,17 +232,18 @@ def main() -> int:
     for i in range(args.steps):
         step(kev[i])
     torch.cuda.synchronize()
-    kern_ms = sorted(a.elapsed_time(b) for a, b in kev)
-    part_ms = sum(kern_ms) / len(kern_ms)
+    part_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
 
-    kv_bytes = B * L * Hkv * D * 2 * 1
-    value = kv_bytes / (step_ms * 1e-3) / 1e9
-    achieved = kv_bytes / (part_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    tokens = int(lens.astype(np.int64).sum())
+    logical = tokens * Hkv * D * 2 * e                  # every token of every sequence
+    unique = (T + B) * Hkv * D * 2 * e                  # each stored token once
+    value = unique / (step_ms * 1e-3) / 1e9
+    achieved = unique / (part_ms * 1e-3) / 1e9
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload.
     # Its inputs are built on the host by the oracle itself (its own write of
-    # freshly drawn rows into the same slots), never copied from the device.
+    # freshly drawn rows into the sampled sequences' slots), never copied from
+    # the device.
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -192,24 +251,25 @@ def main() -> int:
         threads = min(os.cpu_count() or 1, 16)
         kh = np.zeros(pkv.pkv_pool_bytes(layout), dtype=np.uint8)
         vh = np.zeros_like(kh)
-        n_tok = S * cached
+        slots = np.unique(np.concatenate([np.asarray(per_seq[b], dtype=np.int64)
+                                          for b in range(S)] + [step_slots[:S]]))
         rng = np.random.default_rng(306)
-        src_k = rng.standard_normal((n_tok + S, Hkv, D), dtype=np.float32).astype(np.float16)
-        src_v = rng.standard_normal((n_tok + S, Hkv, D), dtype=np.float32).astype(np.float16)
-        host_slots = np.concatenate([bulk_slots[:n_tok], step_slots[:S]]).astype(np.int64)
-        oracle.reshape_and_cache(src_k, src_v, kh, vh, host_slots, Hkv, True, k_scale, v_scale)
+        src_k = rng.standard_normal((slots.size, Hkv, D), dtype=np.float32).astype(np.float16)
+        src_v = rng.standard_normal((slots.size, Hkv, D), dtype=np.float32).astype(np.float16)
+        oracle.reshape_and_cache(src_k, src_v, kh, vh, slots, Hkv, wl.fp8, k_scale, v_scale)
         qh = rng.standard_normal((S, Hq, D), dtype=np.float32).astype(np.float16)
         t0 = time.perf_counter()
-        oracle.paged_attention_decode(qh, kh, vh, tables[:S], np.full(S, L, np.int32), Hkv,
-                                      True, sm_scale, k_scale, v_scale, threads)
+        oracle.paged_attention_decode(qh, kh, vh, tables[:S], lens[:S], Hkv, wl.fp8, sm_scale,
+                                      k_scale, v_scale, threads)
         cpu_s = time.perf_counter() - t0
-        cpu = {"value": round(S * L * Hkv * D * 2 / cpu_s / 1e9, 4), "unit": "GB/s",
+        sample_bytes = int(lens[:S].astype(np.int64).sum()) * Hkv * D * 2 * e
+        cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
                "cores": threads, "kind": "oracle",
-               "sample": f"{S} of {B} sequences (all 64 query heads, L={L}): "
-                         f"{cpu_s:.2f} s fp64 decode on the host"}
+               "sample": f"{S} of {B} sequences (all {Hq} query heads, "
+                         f"{int(lens[:S].sum())} tokens): {cpu_s:.2f} s fp64 decode on the host"}
 
     res = {
-        "metric": "KV GB/s read (% of HBM peak) + decode seqs·tok/s, 70B-layer shape, FP8 KV",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -221,20 +281,23 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "llama-3.1-70b layer decode, FP8 E4M3 KV cache",
-                   "global_batch": B, "seq_len": L, "q_heads": Hq, "kv_heads": Hkv,
-                   "head_dim": D, "block_size": 16, "pool_blocks": NB, "partition_size": P,
-                   "kv_dtype": "fp8_e4m3fn", "arith": "f16 MFMA inputs, f32 accumulate",
-                   "parallelism": "single GPU"},
+        "config": {"workload": wl.name, "global_batch": B, "seq_len": Lmax,
+                   "total_tokens": tokens, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "block_size": 16, "pool_blocks": NB, "partition_size": P,
+                   "kv_dtype": "fp8_e4m3fn" if wl.fp8 else "f16",
+                   "arith": "f16 MFMA inputs, f32 accumulate", "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "seq_tok_per_s": round(B * L / (step_ms * 1e-3), 1),
-        "kv_bytes_per_step": kv_bytes,
+        "seq_tok_per_s": round(tokens / (step_ms * 1e-3), 1),
+        "kv_bytes_per_step": unique,
+        "kv_bytes_per_step_logical": logical,
+        "kv_gbs_logical": round(logical / (step_ms * 1e-3) / 1e9, 2),
         "decode_partition_us": round(part_ms * 1e3, 2),
+        "shared_prefix_blocks_hint": int(shared.max()) if B else 0,
         "host_slot_assignment_us": round(host_slot_us, 1),
         "bulk_fill_gbs": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": measured_traffic(args.workload)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

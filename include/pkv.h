@@ -160,6 +160,13 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_poo
  *   context_lens  device int32 [num_seqs]; L_b includes the token being
  *                 decoded; values are clamped to [0, min(max_context_len,
  *                 16 * max_blocks_per_seq)].
+ *   shared_prefix_blocks  optional device int32 [num_seqs] (NULL = none): the
+ *                 number of leading blocks of each sequence that other
+ *                 sequences of the batch also read (a shared prompt, a fork's
+ *                 parent; pkv_seq_shared_prefix_blocks reports it).  A cache
+ *                 hint only: those tiles are loaded through the caches so the
+ *                 sibling sequences can hit, all others are streamed past
+ *                 them.  The result does not depend on it.
  *   max_context_len  host upper bound on every L_b (sizes the workspace).
  *   num_q_heads must be a multiple of layout->num_kv_heads with a group of at
  *   most 16.
@@ -176,7 +183,8 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_poo
 pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_pool,
                                       const void* v_pool, const int32_t* block_tables,
                                       int32_t max_blocks_per_seq,
-                                      const int32_t* context_lens, int32_t num_seqs,
+                                      const int32_t* context_lens,
+                                      const int32_t* shared_prefix_blocks, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_context_len,
                                       const pkv_cache_layout* layout, float sm_scale,
                                       float k_scale, float v_scale,
@@ -192,7 +200,8 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_p
 pkv_status pkv_decode_partitions(float* out, const void* q, const void* k_pool,
                                  const void* v_pool, const int32_t* block_tables,
                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                 int32_t num_seqs, int32_t num_q_heads,
+                                 const int32_t* shared_prefix_blocks, int32_t num_seqs,
+                                 int32_t num_q_heads,
                                  int32_t max_context_len, const pkv_cache_layout* layout,
                                  float sm_scale, float k_scale, float v_scale,
                                  int32_t partition_size, void* workspace,
@@ -263,6 +272,10 @@ pkv_status pkv_seq_block_table(const pkv_pool* pool, int32_t seq, int32_t* out, 
 int64_t pkv_seq_len(const pkv_pool* pool, int32_t seq);
 /* Number of live sequences. */
 int32_t pkv_pool_num_seqs(const pkv_pool* pool);
+/* Leading blocks of a sequence that are shared with another sequence
+ * (reference count > 1) -- the shared_prefix_blocks hint of the decode;
+ * -1 for an unknown id. */
+int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* pool, int32_t seq);
 
 #ifdef __cplusplus
 }

@@ -79,10 +79,10 @@ def load_library():
         "pkv_decode_partition_size": ([i32, i32, i32, i32, i32], i32),
         "pkv_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], u64),
         "pkv_reshape_and_cache": ([P, P, P, P, P, i32, LP, f32, f32, P], i32),
-        "pkv_paged_attention_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, LP, f32, f32, f32,
-                                        i32, P, u64, P], i32),
-        "pkv_decode_partitions": ([P, P, P, P, P, i32, P, i32, i32, i32, LP, f32, f32, f32, i32,
-                                   P, u64, P], i32),
+        "pkv_paged_attention_decode": ([P, P, P, P, P, i32, P, P, i32, i32, i32, LP, f32, f32,
+                                        f32, i32, P, u64, P], i32),
+        "pkv_decode_partitions": ([P, P, P, P, P, i32, P, P, i32, i32, i32, LP, f32, f32, f32,
+                                   i32, P, u64, P], i32),
         "pkv_decode_reduce": ([P, P, i32, i32, i32, i32, LP, f32, i32, P, u64, P], i32),
         "pkv_copy_blocks": ([P, P, LP, P, i32, P], i32),
         "pkv_pool_create": ([i32, i32, u64, ctypes.POINTER(P)], i32),
@@ -98,6 +98,7 @@ def load_library():
         "pkv_seq_free": ([P, i32], i32),
         "pkv_seq_block_table": ([P, i32, P, i32, ctypes.POINTER(i32)], i32),
         "pkv_seq_len": ([P, i32], i64),
+        "pkv_seq_shared_prefix_blocks": ([P, i32], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -208,30 +209,41 @@ def _workspace(workspace, B, Hq, layout, max_context_len, partition_size):
     return workspace, nbytes
 
 
+def _hint(shared_prefix_blocks, B):
+    if shared_prefix_blocks is None:
+        return None
+    import torch
+    _require(shared_prefix_blocks, torch.int32, "shared_prefix_blocks")
+    if shared_prefix_blocks.numel() != B:
+        raise ValueError("shared_prefix_blocks must hold one count per sequence")
+    return _ptr(shared_prefix_blocks)
+
+
 def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
                                max_context_len: int, layout: CacheLayout, sm_scale: float,
                                k_scale: float = 1.0, v_scale: float = 1.0,
-                               partition_size: int = 0, workspace=None, stream=None) -> None:
+                               partition_size: int = 0, workspace=None, stream=None,
+                               shared_prefix_blocks=None) -> None:
     B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
     workspace, nbytes = _workspace(workspace, B, Hq, layout, max_context_len, partition_size)
     _check(load_library().pkv_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
-        _ptr(context_lens), B, Hq, max_context_len, ctypes.byref(layout), sm_scale, k_scale,
-        v_scale, partition_size, _ptr(workspace), nbytes, _stream(stream)),
-        "pkv_paged_attention_decode")
+        _ptr(context_lens), _hint(shared_prefix_blocks, B), B, Hq, max_context_len,
+        ctypes.byref(layout), sm_scale, k_scale, v_scale, partition_size, _ptr(workspace),
+        nbytes, _stream(stream)), "pkv_paged_attention_decode")
 
 
 def pkv_decode_partitions(out, q, k_pool, v_pool, block_tables, context_lens,
                           max_context_len: int, layout: CacheLayout, sm_scale: float,
                           k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
-                          workspace=None, stream=None) -> None:
+                          workspace=None, stream=None, shared_prefix_blocks=None) -> None:
     B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().pkv_decode_partitions(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
-        _ptr(context_lens), B, Hq, max_context_len, ctypes.byref(layout), sm_scale, k_scale,
-        v_scale, partition_size, _ptr(workspace), nbytes, _stream(stream)),
-        "pkv_decode_partitions")
+        _ptr(context_lens), _hint(shared_prefix_blocks, B), B, Hq, max_context_len,
+        ctypes.byref(layout), sm_scale, k_scale, v_scale, partition_size, _ptr(workspace),
+        nbytes, _stream(stream)), "pkv_decode_partitions")
 
 
 def pkv_decode_reduce(out, context_lens, max_context_len: int, max_blocks_per_seq: int,
@@ -329,3 +341,6 @@ class BlockPool:
 
     def seq_len(self, seq: int) -> int:
         return self._L.pkv_seq_len(self._h, seq)
+
+    def shared_prefix_blocks(self, seq: int) -> int:
+        return self._L.pkv_seq_shared_prefix_blocks(self._h, seq)

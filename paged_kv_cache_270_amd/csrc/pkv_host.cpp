@@ -224,3 +224,15 @@ extern "C" int64_t pkv_seq_len(const pkv_pool* p, int32_t seq) {
   auto it = p->seqs.find(seq);
   return it == p->seqs.end() ? -1 : it->second.len;
 }
+
+extern "C" int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* p, int32_t seq) {
+  if (!p) return -1;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return -1;
+  int32_t n = 0;
+  for (int32_t b : it->second.blocks) {
+    if (p->ref[(size_t)b] <= 1) break;
+    ++n;
+  }
+  return n;
+}

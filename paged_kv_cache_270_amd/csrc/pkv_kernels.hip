@@ -169,6 +169,7 @@ struct DecodeArgs {
   const uint8_t* v_pool;
   const int32_t* block_tables; // [B][max_blocks]
   const int32_t* context_lens; // [B]
+  const int32_t* shared_prefix;// [B] or null: leading blocks shared with other sequences
   float* ws_ml;                // [B][Hq][n_p_max][2]: running max (log2 units), sum
   float* ws_o;                 // [B][Hq][n_p_max][D]: unnormalised output
   int32_t max_blocks;
@@ -213,18 +214,30 @@ struct TileRegs {
   u32x4 v[kVecs];
 };
 
+// Load one (block, kv head) tile: each lane reads 16 bytes at i * 1 KiB +
+// 16 * lane.  Tiles only this sequence reads are streamed past the caches
+// (non-temporal); tiles of a shared prefix go through them, so the sibling
+// sequences that read the same tile shortly after can hit.
 template <bool kFP8>
 __device__ __forceinline__ void load_tile(TileRegs<kFP8>& r, const DecodeArgs& a, int phys,
-                                          int kvh, int lane) {
+                                          int kvh, int lane, bool cached) {
   constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
   if ((unsigned)phys < (unsigned)a.num_blocks) {
     const int64_t off = ((int64_t)phys * a.hkv + kvh) * kTileBytes;
     const u32x4* kt = reinterpret_cast<const u32x4*>(a.k_pool + off);
     const u32x4* vt = reinterpret_cast<const u32x4*>(a.v_pool + off);
+    if (cached) {
 #pragma unroll
-    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
-      r.k[i] = __builtin_nontemporal_load(kt + i * kWave + lane);
-      r.v[i] = __builtin_nontemporal_load(vt + i * kWave + lane);
+      for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+        r.k[i] = kt[i * kWave + lane];
+        r.v[i] = vt[i * kWave + lane];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+        r.k[i] = __builtin_nontemporal_load(kt + i * kWave + lane);
+        r.v[i] = __builtin_nontemporal_load(vt + i * kWave + lane);
+      }
     }
   } else {
 #pragma unroll
@@ -389,14 +402,19 @@ decode_partition_kernel(DecodeArgs a) {
   const int my_n = w < nblk ? (nblk - w + kNW - 1) / kNW : 0;
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk0 + w;
 
+  // logical blocks below this are shared with other sequences (cache hint)
+  const int shared_blocks = a.shared_prefix != nullptr ? a.shared_prefix[b] : 0;
   for (int c0 = 0; c0 < my_n; c0 += kWave) {
     const int cnt = min(kWave, my_n - c0);
     // lane i holds the physical id of this wave's block c0 + i
     const int tbl = lane < cnt ? trow[(int64_t)(c0 + lane) * kNW] : 0;
+    const int lb0 = blk0 + w + c0 * kNW;  // logical block of this chunk's tile 0
     TileRegs<kFP8> buf[kPD + 1];
 #pragma unroll
     for (int r = 0; r < kPD; ++r)
-      if (r < cnt) load_tile<kFP8>(buf[r], a, __builtin_amdgcn_readlane(tbl, r), kvh, lane);
+      if (r < cnt)
+        load_tile<kFP8>(buf[r], a, __builtin_amdgcn_readlane(tbl, r), kvh, lane,
+                        lb0 + r * kNW < shared_blocks);
     for (int base = 0; base < cnt; base += kPD + 1) {
 #pragma unroll
       for (int r = 0; r <= kPD; ++r) {
@@ -404,7 +422,8 @@ decode_partition_kernel(DecodeArgs a) {
         if (ii < cnt) {
           if (ii + kPD < cnt)
             load_tile<kFP8>(buf[(r + kPD) % (kPD + 1)], a,
-                            __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane);
+                            __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane,
+                            lb0 + (ii + kPD) * kNW < shared_blocks);
           const int tb = (blk0 + w + (c0 + ii) * kNW) * kBS;  // first token of the tile
           process_tile<kFP8, kHwCvt, kSplitP>(buf[r], qop, st, tb, qg, L, a.qk_scale);
         }
@@ -606,9 +625,9 @@ pkv_status launch_status() {
 // block and head) or 1024 waves of fp16 tiles (8 KiB).  So: the fewest
 // partitions per sequence that give that many waves (4 per workgroup), cut
 // into equal runs of whole blocks, at least 8 blocks each.  Batches with 1024
-// or more (sequence, KV head) pairs -- where lengths may be ragged -- cap a
-// partition at 512 blocks (8192 tokens) so that long sequences leave no tail;
-// otherwise the cap is 1024 blocks.
+// or more (sequence, KV head) pairs -- where lengths may be ragged and
+// prefixes shared -- cap a partition at 256 blocks (4096 tokens) so that long
+// sequences leave no tail; otherwise the cap is 1024 blocks.
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
                           int32_t dtype, int32_t requested) {
   if (requested < 0 || requested % kBS != 0) return -1;
@@ -619,7 +638,7 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ct
   int64_t n_p = (target_waves + 4 * pairs - 1) / (4 * pairs);
   n_p = std::max<int64_t>(1, std::min<int64_t>(n_p, nblk / 8));
   int64_t per = (nblk + n_p - 1) / n_p;
-  per = std::min<int64_t>(per, pairs >= 1024 ? 512 : 1024);
+  per = std::min<int64_t>(per, pairs >= 1024 ? 256 : 1024);
   return (int32_t)(per * kBS);
 }
 
@@ -687,7 +706,8 @@ struct DecodePlan {
 
 pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
-                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                       int32_t num_seqs, int32_t num_q_heads,
                        int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale,
                        float k_scale, float v_scale, int32_t partition_size, void* workspace,
                        uint64_t workspace_bytes, bool need_pools, DecodePlan* plan) {
@@ -731,6 +751,7 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   a.v_pool = static_cast<const uint8_t*>(v_pool);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.shared_prefix = shared_prefix_blocks;
   a.ws_ml = wl.total ? static_cast<float*>(workspace) : nullptr;
   a.ws_o = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_bytes)
                     : nullptr;
@@ -890,7 +911,8 @@ static pkv_status run_reduce(const DecodePlan& pl, int32_t num_seqs, hipStream_t
 extern "C" pkv_status pkv_decode_partitions(float* out, const void* q, const void* k_pool,
                                             const void* v_pool, const int32_t* block_tables,
                                             int32_t max_blocks_per_seq,
-                                            const int32_t* context_lens, int32_t num_seqs,
+                                            const int32_t* context_lens,
+                                            const int32_t* shared_prefix_blocks, int32_t num_seqs,
                                             int32_t num_q_heads, int32_t max_context_len,
                                             const pkv_cache_layout* layout, float sm_scale,
                                             float k_scale, float v_scale,
@@ -898,9 +920,9 @@ extern "C" pkv_status pkv_decode_partitions(float* out, const void* q, const voi
                                             uint64_t workspace_bytes, void* stream) {
   DecodePlan pl;
   pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
-                              context_lens, num_seqs, num_q_heads, max_context_len, layout,
-                              sm_scale, k_scale, v_scale, partition_size, workspace,
-                              workspace_bytes, true, &pl);
+                              context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
+                              max_context_len, layout, sm_scale, k_scale, v_scale,
+                              partition_size, workspace, workspace_bytes, true, &pl);
   if (st != PKV_OK) return st;
   return run_partitions(pl, num_seqs, static_cast<hipStream_t>(stream));
 }
@@ -913,9 +935,9 @@ extern "C" pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens,
                                         uint64_t workspace_bytes, void* stream) {
   DecodePlan pl;
   pkv_status st = plan_decode(out, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq,
-                              context_lens, num_seqs, num_q_heads, max_context_len, layout,
-                              1.0f, 1.0f, v_scale, partition_size, workspace, workspace_bytes,
-                              false, &pl);
+                              context_lens, nullptr, num_seqs, num_q_heads, max_context_len,
+                              layout, 1.0f, 1.0f, v_scale, partition_size, workspace,
+                              workspace_bytes, false, &pl);
   if (st != PKV_OK) return st;
   return run_reduce(pl, num_seqs, static_cast<hipStream_t>(stream));
 }
@@ -923,14 +945,15 @@ extern "C" pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens,
 extern "C" pkv_status pkv_paged_attention_decode(
     float* out, const void* q, const void* k_pool, const void* v_pool,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const int32_t* shared_prefix_blocks, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len,
     const pkv_cache_layout* layout, float sm_scale, float k_scale, float v_scale,
     int32_t partition_size, void* workspace, uint64_t workspace_bytes, void* stream) {
   DecodePlan pl;
   pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
-                              context_lens, num_seqs, num_q_heads, max_context_len, layout,
-                              sm_scale, k_scale, v_scale, partition_size, workspace,
-                              workspace_bytes, true, &pl);
+                              context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
+                              max_context_len, layout, sm_scale, k_scale, v_scale,
+                              partition_size, workspace, workspace_bytes, true, &pl);
   if (st != PKV_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_partitions(pl, num_seqs, s);

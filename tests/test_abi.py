@@ -62,7 +62,7 @@ def test_partition_size_and_workspace():
     # one partition per sequence when the pairs alone give enough waves
     assert pkv.pkv_decode_partition_size(64, 8, 8193, F8, 0) >= 8193
     # partitions are capped for big, possibly ragged batches
-    assert pkv.pkv_decode_partition_size(256, 8, 18401, F8, 0) <= 8192
+    assert pkv.pkv_decode_partition_size(256, 8, 18401, F8, 0) <= 4096
     # 4 x 64 heads x 256 partitions x (2 + 128) floats, the max/sum block 256-aligned
     ws = pkv.pkv_decode_workspace_bytes(4, 64, 8, 131072, F8, 512)
     rows = 4 * 64 * 256
@@ -102,19 +102,19 @@ def test_host_validation_rejects_before_launch():
                                    None) == pkv.PKV_OK   # nothing to do
     dec = L.pkv_paged_attention_decode
     # group of 32 query heads per KV head: more than the 16 an MFMA tile holds
-    assert dec(16, 16, 16, 16, 16, 4, 16, 2, 64, 64, ctypes.byref(ok), 0.1, 1.0, 1.0, 0, 256,
+    assert dec(16, 16, 16, 16, 16, 4, 16, None, 2, 64, 64, ctypes.byref(ok), 0.1, 1.0, 1.0, 0, 256,
                1 << 20, None) == pkv.PKV_ERR_UNSUPPORTED
     # query heads not a multiple of KV heads
-    assert dec(16, 16, 16, 16, 16, 4, 16, 2, 3, 64, ctypes.byref(ok), 0.1, 1.0, 1.0, 0, 256,
+    assert dec(16, 16, 16, 16, 16, 4, 16, None, 2, 3, 64, ctypes.byref(ok), 0.1, 1.0, 1.0, 0, 256,
                1 << 20, None) == pkv.PKV_ERR_INVALID_ARG
     # workspace too small for 2 partitions
-    assert dec(16, 16, 16, 16, 16, 4, 16, 2, 4, 64, ctypes.byref(ok), 0.1, 1.0, 1.0, 32, 256,
+    assert dec(16, 16, 16, 16, 16, 4, 16, None, 2, 4, 64, ctypes.byref(ok), 0.1, 1.0, 1.0, 32, 256,
                16, None) == pkv.PKV_ERR_WORKSPACE
     # partition size not a multiple of 16
-    assert dec(16, 16, 16, 16, 16, 4, 16, 2, 4, 64, ctypes.byref(ok), 0.1, 1.0, 1.0, 24, 256,
+    assert dec(16, 16, 16, 16, 16, 4, 16, None, 2, 4, 64, ctypes.byref(ok), 0.1, 1.0, 1.0, 24, 256,
                1 << 20, None) == pkv.PKV_ERR_INVALID_ARG
     # FP8 needs positive finite scales
-    assert dec(16, 16, 16, 16, 16, 4, 16, 2, 4, 64, ctypes.byref(ok), 0.1, float("nan"), 1.0,
+    assert dec(16, 16, 16, 16, 16, 4, 16, None, 2, 4, 64, ctypes.byref(ok), 0.1, float("nan"), 1.0,
                0, 256, 1 << 20, None) == pkv.PKV_ERR_INVALID_ARG
     assert L.pkv_copy_blocks(16, 16, ctypes.byref(ok), 16, -1, None) == pkv.PKV_ERR_INVALID_ARG
     assert L.pkv_copy_blocks(None, None, ctypes.byref(ok), None, 0, None) == pkv.PKV_OK

@@ -75,6 +75,12 @@ def test_matches_oracle_model_on_random_operations(orc, seed):
         for sp, sm in zip(live_p, live_m):
             assert pool.block_table(sp) == model.table(sm)
             assert pool.seq_len(sp) == model.length(sm)
+            shared = 0
+            for blk in model.table(sm):
+                if model.ref[blk] <= 1:
+                    break
+                shared += 1
+            assert pool.shared_prefix_blocks(sp) == shared
         for b in range(NB):
             assert pool.refcount(b) == model.ref[b]
     for sp in live_p:
@@ -156,3 +162,17 @@ def test_usage_gauge():
     assert pool.usage() == 1.0
     pool.free(s)
     assert pool.usage() == 0.0
+
+
+def test_shared_prefix_blocks_after_forks():
+    pool = pkv.BlockPool(64)
+    a = pool.create()
+    pool.append(a, 40)                  # 3 blocks, the last partly filled
+    assert pool.shared_prefix_blocks(a) == 0
+    b = pool.fork(a)
+    assert pool.shared_prefix_blocks(a) == 3 and pool.shared_prefix_blocks(b) == 3
+    pool.append(b, 1)                   # copy-on-write of the shared tail
+    assert pool.shared_prefix_blocks(b) == 2 and pool.shared_prefix_blocks(a) == 2
+    pool.free(a)
+    assert pool.shared_prefix_blocks(b) == 0
+    assert pool.shared_prefix_blocks(999) == -1

@@ -288,3 +288,21 @@ def test_each_wave_count_matches_the_oracle(waves, monkeypatch):
     err = max_err(prep.gpu_decode(), prep.oracle_decode())
     _report(f"partition {ps} (waves {waves})", err, TOL[True])
     assert err <= TOL[True]
+
+
+def test_shared_prefix_cache_hint_changes_nothing():
+    """The shared-prefix hint only picks a cache policy: bit-identical output
+    with the hint, without it, and with a wrong one."""
+    wl = workloads.shared_prefix(groups=4, per_group=8, max_len=6000)
+    prep = Prepared(wl)
+    base = prep.gpu_decode()
+    for hint in (np.full(wl.num_seqs, wl.prefix_blocks, dtype=np.int32),
+                 np.full(wl.num_seqs, 10 ** 6, dtype=np.int32),
+                 np.zeros(wl.num_seqs, dtype=np.int32)):
+        out = torch.empty(prep.q.shape, dtype=torch.float32, device="cuda")
+        pkv.pkv_paged_attention_decode(out, prep.q, prep.k_pool, prep.v_pool, prep.tables,
+                                       prep.lens, wl.max_context_len, prep.layout,
+                                       prep.sm_scale, prep.k_scale, prep.v_scale,
+                                       shared_prefix_blocks=torch.from_numpy(hint).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(base.view(np.uint32), out.cpu().numpy().view(np.uint32))
