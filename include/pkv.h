@@ -237,9 +237,11 @@ pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, uint64_t shuf
                            pkv_pool** out);
 void pkv_pool_destroy(pkv_pool* pool);
 int32_t pkv_pool_num_blocks(const pkv_pool* pool);
+/* Blocks on the free list (held by no sequence and not in the prefix cache). */
 int32_t pkv_pool_num_free(const pkv_pool* pool);
-/* Fraction of blocks in use, (num_blocks - num_free) / num_blocks: the cache
- * usage gauge that [FP8-128K] §7 says to watch (alert above 0.90). */
+/* Fraction of blocks in use, (num_blocks - available) / num_blocks, where
+ * available = free blocks + evictable prefix-cache blocks: the cache usage
+ * gauge that [FP8-128K] §7 says to watch (alert above 0.90). */
 double pkv_pool_usage(const pkv_pool* pool);
 /* Reference count of a block (number of sequences whose table holds it);
  * -1 for an id out of range. */
@@ -260,9 +262,10 @@ pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* child_out);
  * All or nothing: PKV_ERR_NO_FREE_BLOCKS leaves every state unchanged. */
 pkv_status pkv_seq_append(pkv_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_out,
                           int32_t* cow_pairs_out, int32_t* n_cow_out);
-/* Release a sequence: each of its blocks loses one reference and returns to
- * the free list at zero ([GLOSSARY] §4.02: pages of a cancelled request go
- * back to the pool at once, else memory leaks). */
+/* Release a sequence: each of its blocks loses one reference; at zero it
+ * returns to the free list, or becomes evictable if the prefix cache holds it
+ * ([GLOSSARY] §4.02: pages of a cancelled request go back to the pool at once,
+ * else memory leaks). */
 pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
 /* Copy a sequence's block table into out[0..n) with n = number of blocks;
  * *n_out = n always; PKV_ERR_INVALID_ARG if cap < n (nothing copied). */
@@ -276,6 +279,46 @@ int32_t pkv_pool_num_seqs(const pkv_pool* pool);
  * (reference count > 1) -- the shared_prefix_blocks hint of the decode;
  * -1 for an unknown id. */
 int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* pool, int32_t seq);
+
+/* ------------------------------------------------------------- prefix cache
+ *
+ * A map from prompt chunks to filled blocks ([PRIMER-8] §8.3: the prompt is
+ * hashed in block-sized chunks; on a hit the new request's table points at
+ * the cached block and that prefill is skipped; on a miss the chunk is
+ * prefilled and its block registered; [GLOSSARY] §3.01: requests with one
+ * system prompt read the same physical pages).  A chunk's key is a 64-bit hash
+ * of its block_size token ids chained onto the previous chunk's key, so a key
+ * names a whole prefix; an entry also keeps its chunk's tokens and its
+ * parent's key and a lookup matches only when both agree, so a hash collision
+ * can never alias another prefix's keys and values.  Only full blocks are
+ * cached.  The cache's hold on a block is not a reference: a cached block no
+ * sequence holds is "evictable"; it counts as available, and when the free
+ * list is empty a new block is taken from the least recently hit or
+ * registered evictable block, whose entry is dropped.  A cached block is never
+ * written again: appends write only into a sequence's partially filled last
+ * block. */
+
+/* New sequence for a prompt of n_tokens token ids: its leading full chunks
+ * that are cached are mapped onto the cached blocks (each gains a reference),
+ * up to the first chunk that misses.  *n_cached_out = tokens covered (a
+ * multiple of block_size, possibly n_tokens); the sequence's length is that
+ * count, and the caller appends and prefills the rest.  Takes no free block. */
+pkv_status pkv_seq_create_cached(pkv_pool* pool, const int32_t* tokens, int32_t n_tokens,
+                                 int32_t* seq_out, int32_t* n_cached_out);
+/* Register the filled full blocks of a sequence whose first n_tokens token
+ * ids are `tokens` (call after their keys and values are written).  Chunks
+ * already cached for the same prefix are kept; registration stops at a chunk
+ * whose key is owned by a different prefix or whose block is already cached
+ * for a different chunk.  Chunks beyond the sequence's length are ignored. */
+pkv_status pkv_seq_cache_prefix(pkv_pool* pool, int32_t seq, const int32_t* tokens,
+                                int32_t n_tokens);
+/* Counters: chunks that hit and missed in pkv_seq_create_cached so far, and
+ * the cached and evictable blocks now.  Any output pointer may be NULL. */
+pkv_status pkv_prefix_cache_stats(const pkv_pool* pool, int64_t* hit_blocks,
+                                  int64_t* miss_blocks, int32_t* cached_blocks,
+                                  int32_t* evictable_blocks);
+/* Drop every entry; evictable blocks go to the free list in LRU order. */
+void pkv_prefix_cache_clear(pkv_pool* pool);
 
 #ifdef __cplusplus
 }

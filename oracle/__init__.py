@@ -237,6 +237,20 @@ class BlockPoolModel:
     * freeing a sequence drops one reference per block; a block returns to the
       free list when its count reaches zero (no leak on cancel);
     * an append that cannot get all the blocks it needs changes nothing.
+
+    Prefix cache ("LLM Primer VI, Capítulo 8", §8.3: a prompt is cut into
+    block-sized chunks; a chunk already filled for the same preceding text is
+    reused by pointing the new table at its block; otherwise it is prefilled and
+    its block registered).  The model keys an entry by the exact token prefix up
+    to the end of the chunk, so no hashing is involved:
+
+    * only full blocks are cached; the cache's hold on a block is not a
+      reference;
+    * a cached block that no sequence holds is evictable; it counts as
+      available, and when the free list is empty a new block comes from the
+      evictable block whose entry was hit or registered longest ago;
+    * registration keeps an entry that already exists for the same prefix and
+      stops at the first chunk whose block already serves another prefix.
     """
 
     def __init__(self, free_order, block_size: int = BLOCK_SIZE):
@@ -247,12 +261,43 @@ class BlockPoolModel:
         self.ref = [0] * self.num_blocks
         self.seqs = {}
         self._next = 0
+        self.cache = {}         # token prefix (tuple) -> block
+        self.prefix_of = {}     # block -> token prefix it is cached for
+        self.last_use = {}      # token prefix -> tick of last hit or registration
+        self._tick = 0
+        self.hit_blocks = 0
+        self.miss_blocks = 0
 
     def num_free(self) -> int:
         return len(self.free)
 
+    def evictable(self):
+        """Cached blocks no sequence holds, least recently used first."""
+        blocks = [b for b, pre in self.prefix_of.items() if self.ref[b] == 0]
+        return sorted(blocks, key=lambda b: self.last_use[self.prefix_of[b]])
+
+    def available(self) -> int:
+        return len(self.free) + len(self.evictable())
+
     def usage(self) -> float:
-        return (self.num_blocks - len(self.free)) / self.num_blocks
+        return (self.num_blocks - self.available()) / self.num_blocks
+
+    def _take(self) -> int:
+        if self.free:
+            b = self.free.pop(0)
+        else:
+            b = self.evictable()[0]
+            pre = self.prefix_of.pop(b)
+            del self.cache[pre]
+            del self.last_use[pre]
+        self.ref[b] += 1
+        return b
+
+    def _release(self, b: int) -> None:
+        self.ref[b] -= 1
+        assert self.ref[b] >= 0
+        if self.ref[b] == 0 and b not in self.prefix_of:
+            self.free.append(b)
 
     def create(self) -> int:
         sid = self._next
@@ -276,23 +321,20 @@ class BlockPoolModel:
         cow = n % bs != 0 and self.ref[blocks[-1]] > 1
         have = -(-n // bs)
         need = -(-(n + n_tokens) // bs) - have + (1 if cow else 0)
-        if need > len(self.free):
+        if need > self.available():
             raise NoFreeBlocks()
         blocks = list(blocks)
         pairs = []
         if cow:
-            new = self.free.pop(0)
+            new = self._take()
             old = blocks[-1]
-            self.ref[old] -= 1
-            self.ref[new] += 1
+            self._release(old)
             blocks[-1] = new
             pairs.append((old, new))
         slots = []
         for pos in range(n, n + n_tokens):
             if pos // bs >= len(blocks):
-                b = self.free.pop(0)
-                self.ref[b] += 1
-                blocks.append(b)
+                blocks.append(self._take())
             slots.append(blocks[pos // bs] * bs + pos % bs)
         self.seqs[sid] = (blocks, n + n_tokens)
         return slots, pairs
@@ -300,10 +342,54 @@ class BlockPoolModel:
     def free_seq(self, sid: int) -> None:
         blocks, _ = self.seqs.pop(sid)
         for b in blocks:
-            self.ref[b] -= 1
-            assert self.ref[b] >= 0
-            if self.ref[b] == 0:
-                self.free.append(b)
+            self._release(b)
+
+    def create_cached(self, tokens):
+        """New sequence mapped onto the cached blocks of the leading chunks of
+        `tokens`, up to the first chunk not cached; returns (sid, n_cached)."""
+        bs = self.block_size
+        chunks = len(tokens) // bs
+        blocks = []
+        for i in range(chunks):
+            pre = tuple(tokens[:bs * (i + 1)])
+            if pre not in self.cache:
+                break
+            b = self.cache[pre]
+            self.ref[b] += 1
+            self._tick += 1
+            self.last_use[pre] = self._tick
+            blocks.append(b)
+        self.hit_blocks += len(blocks)
+        self.miss_blocks += chunks - len(blocks)
+        sid = self.create()
+        self.seqs[sid] = (blocks, len(blocks) * bs)
+        return sid, len(blocks) * bs
+
+    def cache_prefix(self, sid: int, tokens) -> None:
+        """Register the full, filled blocks of `sid` under the prefixes of `tokens`."""
+        blocks, n = self.seqs[sid]
+        bs = self.block_size
+        for i in range(min(len(tokens), n) // bs):
+            pre = tuple(tokens[:bs * (i + 1)])
+            if pre in self.cache:
+                continue
+            b = blocks[i]
+            if b in self.prefix_of:
+                break
+            self.cache[pre] = b
+            self.prefix_of[b] = pre
+            self._tick += 1
+            self.last_use[pre] = self._tick
+
+    def prefix_cache_stats(self) -> dict:
+        return {"hit_blocks": self.hit_blocks, "miss_blocks": self.miss_blocks,
+                "cached_blocks": len(self.cache), "evictable_blocks": len(self.evictable())}
+
+    def clear_prefix_cache(self) -> None:
+        self.free.extend(self.evictable())
+        self.cache.clear()
+        self.prefix_of.clear()
+        self.last_use.clear()
 
     def table(self, sid: int):
         return list(self.seqs[sid][0])

@@ -99,6 +99,11 @@ def load_library():
         "pkv_seq_block_table": ([P, i32, P, i32, ctypes.POINTER(i32)], i32),
         "pkv_seq_len": ([P, i32], i64),
         "pkv_seq_shared_prefix_blocks": ([P, i32], i32),
+        "pkv_seq_create_cached": ([P, P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
+        "pkv_seq_cache_prefix": ([P, i32, P, i32], i32),
+        "pkv_prefix_cache_stats": ([P, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                    ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
+        "pkv_prefix_cache_clear": ([P], None),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -344,3 +349,34 @@ class BlockPool:
 
     def shared_prefix_blocks(self, seq: int) -> int:
         return self._L.pkv_seq_shared_prefix_blocks(self._h, seq)
+
+    def create_cached(self, tokens):
+        """New sequence whose leading cached chunks of `tokens` are mapped onto
+        the cached blocks; returns (seq, n_cached_tokens)."""
+        toks = _i32_array(tokens)
+        seq, n_cached = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._L.pkv_seq_create_cached(self._h, toks, len(tokens), ctypes.byref(seq),
+                                             ctypes.byref(n_cached)), "pkv_seq_create_cached")
+        return seq.value, n_cached.value
+
+    def cache_prefix(self, seq: int, tokens) -> None:
+        """Register the filled full blocks of `seq`, whose token ids are `tokens`."""
+        _check(self._L.pkv_seq_cache_prefix(self._h, seq, _i32_array(tokens), len(tokens)),
+               "pkv_seq_cache_prefix")
+
+    def prefix_cache_stats(self) -> dict:
+        hit, miss = ctypes.c_int64(), ctypes.c_int64()
+        cached, evictable = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._L.pkv_prefix_cache_stats(self._h, ctypes.byref(hit), ctypes.byref(miss),
+                                              ctypes.byref(cached), ctypes.byref(evictable)),
+               "pkv_prefix_cache_stats")
+        return {"hit_blocks": hit.value, "miss_blocks": miss.value,
+                "cached_blocks": cached.value, "evictable_blocks": evictable.value}
+
+    def clear_prefix_cache(self) -> None:
+        self._L.pkv_prefix_cache_clear(self._h)
+
+
+def _i32_array(values):
+    vals = [int(v) for v in values]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals)

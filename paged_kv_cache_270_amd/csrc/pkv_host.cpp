@@ -11,7 +11,9 @@
 #include <cstdint>
 #include <cstring>
 #include <deque>
+#include <algorithm>
 #include <new>
+#include <set>
 #include <unordered_map>
 #include <vector>
 
@@ -58,12 +60,30 @@ extern "C" uint64_t pkv_pool_bytes(const pkv_cache_layout* l) {
 }
 
 // ------------------------------------------------------------- block pool
+//
+// Reference counts count the sequences whose table holds a block.  Besides
+// the sequences, the prefix cache ("LLM Primer VI ...", §8.3: prompts hashed in
+// block-sized chunks; a hit points the new table at the cached block and its
+// prefill is skipped; a miss is prefilled and then registered) can hold a full
+// block.  A block is
+//   free       when no sequence holds it and it is not cached,
+//   evictable  when no sequence holds it but it is cached,
+//   in use     otherwise.
+// A new block comes from the free list first, else the least recently used
+// evictable block is dropped from the cache and reused.
 
 namespace {
 
 struct Seq {
   std::vector<int32_t> blocks;
   int64_t len = 0;
+};
+
+struct CacheEntry {
+  int32_t block;
+  uint64_t parent;              // key of the previous chunk (0 for the first)
+  std::vector<int32_t> tokens;  // the chunk, to verify a key match
+  uint64_t tick;                // last hit or registration
 };
 
 uint64_t splitmix64(uint64_t& s) {
@@ -73,15 +93,64 @@ uint64_t splitmix64(uint64_t& s) {
   return z ^ (z >> 31);
 }
 
+// Key of a chunk of block_size token ids chained onto its parent's key.
+uint64_t chunk_key(uint64_t parent, const int32_t* tokens, int32_t n) {
+  uint64_t h = parent ^ 0x243F6A8885A308D3ull;
+  for (int32_t i = 0; i < n; ++i) {
+    uint64_t x = h ^ (uint64_t)(uint32_t)tokens[i];
+    h = splitmix64(x);
+  }
+  return h == 0 ? 1 : h;  // 0 is reserved for "no parent"
+}
+
 }  // namespace
 
 struct pkv_pool {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
   std::deque<int32_t> free_list;  // popped at the front, returned at the back
-  std::vector<int32_t> ref;
+  std::vector<int32_t> ref;       // sequences holding each block
   std::unordered_map<int32_t, Seq> seqs;
   int32_t next_id = 0;
+  // prefix cache
+  std::unordered_map<uint64_t, CacheEntry> cache;
+  std::vector<uint64_t> cache_key;                  // per block, 0 = not cached
+  std::set<std::pair<uint64_t, int32_t>> evictable;  // (tick, block), LRU first
+  uint64_t tick = 0;
+  int64_t hit_blocks = 0, miss_blocks = 0;
+
+  int64_t available() const { return (int64_t)free_list.size() + (int64_t)evictable.size(); }
+
+  // A block for a sequence (the caller has checked available()).
+  int32_t take() {
+    int32_t b;
+    if (!free_list.empty()) {
+      b = free_list.front();
+      free_list.pop_front();
+    } else {
+      auto it = evictable.begin();
+      b = it->second;
+      evictable.erase(it);
+      cache.erase(cache_key[(size_t)b]);
+      cache_key[(size_t)b] = 0;
+    }
+    ref[(size_t)b] += 1;
+    return b;
+  }
+
+  void acquire(int32_t b) {  // one more sequence holds b
+    if (ref[(size_t)b] == 0 && cache_key[(size_t)b] != 0)
+      evictable.erase({cache.at(cache_key[(size_t)b]).tick, b});
+    ref[(size_t)b] += 1;
+  }
+
+  void release(int32_t b) {  // one sequence fewer holds b
+    if (--ref[(size_t)b] > 0) return;
+    if (cache_key[(size_t)b] != 0)
+      evictable.insert({cache.at(cache_key[(size_t)b]).tick, b});
+    else
+      free_list.push_back(b);
+  }
 };
 
 extern "C" pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
@@ -92,6 +161,7 @@ extern "C" pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
   p->num_blocks = num_blocks;
   p->block_size = block_size;
   p->ref.assign((size_t)num_blocks, 0);
+  p->cache_key.assign((size_t)num_blocks, 0);
   std::vector<int32_t> order((size_t)num_blocks);
   for (int32_t i = 0; i < num_blocks; ++i) order[(size_t)i] = i;
   if (shuffle_seed != 0) {  // Fisher-Yates with a splitmix64 stream
@@ -116,7 +186,7 @@ extern "C" int32_t pkv_pool_num_free(const pkv_pool* p) {
 
 extern "C" double pkv_pool_usage(const pkv_pool* p) {
   if (!p || p->num_blocks == 0) return 0.0;
-  return (double)(p->num_blocks - (int32_t)p->free_list.size()) / (double)p->num_blocks;
+  return (double)(p->num_blocks - p->available()) / (double)p->num_blocks;
 }
 
 extern "C" int32_t pkv_pool_refcount(const pkv_pool* p, int32_t block) {
@@ -143,7 +213,7 @@ extern "C" pkv_status pkv_seq_fork(pkv_pool* p, int32_t parent, int32_t* child_o
   auto it = p->seqs.find(parent);
   if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
   Seq child = it->second;  // same blocks, same length
-  for (int32_t b : child.blocks) p->ref[(size_t)b] += 1;
+  for (int32_t b : child.blocks) p->acquire(b);
   int32_t id = p->next_id++;
   p->seqs.emplace(id, std::move(child));
   *child_out = id;
@@ -168,13 +238,11 @@ extern "C" pkv_status pkv_seq_append(pkv_pool* p, int32_t seq, int32_t n_tokens,
   const int64_t have = (s.len + bs - 1) / bs;
   const int64_t want = (s.len + n_tokens + bs - 1) / bs;
   const int64_t need = want - have + (cow ? 1 : 0);
-  if (need > (int64_t)p->free_list.size()) return PKV_ERR_NO_FREE_BLOCKS;  // nothing changed
+  if (need > p->available()) return PKV_ERR_NO_FREE_BLOCKS;  // nothing changed
   if (cow) {
-    int32_t fresh = p->free_list.front();
-    p->free_list.pop_front();
-    int32_t old = s.blocks.back();
-    p->ref[(size_t)old] -= 1;
-    p->ref[(size_t)fresh] += 1;
+    const int32_t fresh = p->take();
+    const int32_t old = s.blocks.back();
+    p->release(old);
     s.blocks.back() = fresh;
     cow_pairs_out[0] = old;
     cow_pairs_out[1] = fresh;
@@ -182,12 +250,7 @@ extern "C" pkv_status pkv_seq_append(pkv_pool* p, int32_t seq, int32_t n_tokens,
   }
   for (int64_t i = 0; i < n_tokens; ++i) {
     const int64_t pos = s.len + i;
-    if (pos / bs >= (int64_t)s.blocks.size()) {  // the token opens a new block
-      int32_t b = p->free_list.front();
-      p->free_list.pop_front();
-      p->ref[(size_t)b] += 1;
-      s.blocks.push_back(b);
-    }
+    if (pos / bs >= (int64_t)s.blocks.size()) s.blocks.push_back(p->take());  // a new block
     slots_out[i] = (int64_t)s.blocks[(size_t)(pos / bs)] * bs + pos % bs;
   }
   s.len += n_tokens;
@@ -200,9 +263,7 @@ extern "C" pkv_status pkv_seq_free(pkv_pool* p, int32_t seq) {
   if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
   for (int32_t b : it->second.blocks)
     if (p->ref[(size_t)b] <= 0) return PKV_ERR_REFCOUNT;  // checked before any change
-  for (int32_t b : it->second.blocks) {
-    if (--p->ref[(size_t)b] == 0) p->free_list.push_back(b);
-  }
+  for (int32_t b : it->second.blocks) p->release(b);
   p->seqs.erase(it);
   return PKV_OK;
 }
@@ -235,4 +296,89 @@ extern "C" int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* p, int32_t seq) 
     ++n;
   }
   return n;
+}
+
+// ------------------------------------------------------------ prefix cache
+
+extern "C" pkv_status pkv_seq_create_cached(pkv_pool* p, const int32_t* tokens,
+                                            int32_t n_tokens, int32_t* seq_out,
+                                            int32_t* n_cached_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (!seq_out || n_tokens < 0 || (n_tokens > 0 && !tokens)) return PKV_ERR_INVALID_ARG;
+  const int32_t bs = p->block_size;
+  const int32_t chunks = n_tokens / bs;
+  Seq s;
+  uint64_t key = 0;
+  int32_t hits = 0;
+  for (int32_t i = 0; i < chunks; ++i) {
+    const int32_t* chunk = tokens + (int64_t)i * bs;
+    const uint64_t k = chunk_key(key, chunk, bs);
+    auto it = p->cache.find(k);
+    if (it == p->cache.end() || it->second.parent != key ||
+        !std::equal(it->second.tokens.begin(), it->second.tokens.end(), chunk))
+      break;  // miss: this chunk and every later one must be prefilled
+    const int32_t b = it->second.block;
+    p->acquire(b);  // leaves the evictable set if nobody held it
+    it->second.tick = ++p->tick;
+    s.blocks.push_back(b);
+    key = k;
+    ++hits;
+  }
+  s.len = (int64_t)hits * bs;
+  p->hit_blocks += hits;
+  p->miss_blocks += chunks - hits;
+  const int32_t id = p->next_id++;
+  p->seqs.emplace(id, std::move(s));
+  *seq_out = id;
+  if (n_cached_out) *n_cached_out = hits * bs;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_cache_prefix(pkv_pool* p, int32_t seq, const int32_t* tokens,
+                                           int32_t n_tokens) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return PKV_ERR_INVALID_ARG;
+  auto sit = p->seqs.find(seq);
+  if (sit == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+  const Seq& s = sit->second;
+  const int32_t bs = p->block_size;
+  const int64_t chunks = std::min<int64_t>(n_tokens, s.len) / bs;
+  uint64_t key = 0;
+  for (int64_t i = 0; i < chunks; ++i) {
+    const int32_t* chunk = tokens + i * bs;
+    const uint64_t k = chunk_key(key, chunk, bs);
+    auto it = p->cache.find(k);
+    if (it != p->cache.end()) {
+      if (it->second.parent != key ||
+          !std::equal(it->second.tokens.begin(), it->second.tokens.end(), chunk))
+        break;  // a different prefix owns this key: stop registering
+    } else {
+      const int32_t b = s.blocks[(size_t)i];
+      if (p->cache_key[(size_t)b] != 0) break;  // the block is cached for another chunk
+      CacheEntry e{b, key, std::vector<int32_t>(chunk, chunk + bs), ++p->tick};
+      p->cache.emplace(k, std::move(e));
+      p->cache_key[(size_t)b] = k;
+    }
+    key = k;
+  }
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_prefix_cache_stats(const pkv_pool* p, int64_t* hit_blocks,
+                                             int64_t* miss_blocks, int32_t* cached_blocks,
+                                             int32_t* evictable_blocks) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (hit_blocks) *hit_blocks = p->hit_blocks;
+  if (miss_blocks) *miss_blocks = p->miss_blocks;
+  if (cached_blocks) *cached_blocks = (int32_t)p->cache.size();
+  if (evictable_blocks) *evictable_blocks = (int32_t)p->evictable.size();
+  return PKV_OK;
+}
+
+extern "C" void pkv_prefix_cache_clear(pkv_pool* p) {
+  if (!p) return;
+  for (const auto& e : p->evictable) p->free_list.push_back(e.second);  // LRU first
+  p->evictable.clear();
+  for (const auto& kv : p->cache) p->cache_key[(size_t)kv.second.block] = 0;
+  p->cache.clear();
 }

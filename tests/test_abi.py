@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_covers_every_device_entry_point():
     for n in _declared_functions():
-        if n.startswith(("pkv_pool", "pkv_seq")):
+        if n.startswith(("pkv_pool", "pkv_seq", "pkv_prefix_cache")):
             continue   # wrapped by BlockPool
         assert hasattr(pkv, n), n
 
