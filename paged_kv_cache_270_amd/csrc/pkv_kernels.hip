@@ -279,10 +279,41 @@ struct SoftmaxState {
 // cross-lane reduction and no rescaling.
 constexpr float kLazyMaxSlack = 8.0f;
 
+// Zero the value elements of tokens >= L in a sequence's last, partly filled
+// tile.  Their probabilities are zero, but the slots may hold anything (a
+// pool allocated without clearing, an earlier sequence's data): a NaN or
+// infinity there would turn 0 * v into NaN inside the PV product.  Lane qg
+// holds tokens 4qg .. 4qg+3 of each value register (the innermost index).
+template <bool kFP8>
+__device__ __forceinline__ void mask_tail_values(TileRegs<kFP8>& t, int tb, int qg, int L) {
+  const int nv = min(max(L - (tb + qg * 4), 0), 4);  // valid tokens among this lane's four
+  if constexpr (kFP8) {  // one byte per token
+    const uint32_t m = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+#pragma unroll
+    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+      t.v[i].x &= m;
+      t.v[i].y &= m;
+      t.v[i].z &= m;
+      t.v[i].w &= m;
+    }
+  } else {  // two tokens per 32-bit word: x, z hold tokens 0-1, y, w tokens 2-3
+    const uint32_t m01 = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0xFFFFu : 0u);
+    const uint32_t m23 = nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0xFFFFu : 0u);
+#pragma unroll
+    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+      t.v[i].x &= m01;
+      t.v[i].y &= m23;
+      t.v[i].z &= m01;
+      t.v[i].w &= m23;
+    }
+  }
+}
+
 template <bool kFP8, bool kHwCvt, bool kSplitP>
-__device__ __forceinline__ void process_tile(const TileRegs<kFP8>& t, const f16x8 (&qop)[4],
+__device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qop)[4],
                                              SoftmaxState& st, int tb, int qg, int L,
                                              float qk_scale) {
+  if (tb + kBS > L) mask_tail_values<kFP8>(t, tb, qg, L);  // wave-uniform: last tile only
   // S^T[t][g] = sum_d K[t][d] Q[g][d]: 4 MFMAs over the 128 channels
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -196,6 +196,37 @@ def test_shared_prefix_equals_copied_prefix_bit_identical():
     assert np.array_equal(shared.view(np.uint32), copied.view(np.uint32))
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_nan_and_inf_past_the_context_are_ignored(fp8):
+    """Slots past L in a sequence's last block may hold anything (a pool
+    allocated without clearing): NaN and infinities there change nothing."""
+    prep = Prepared(workloads.tiny(seed=6, fp8=fp8, partition_size=32))
+    wl = prep.wl
+    clean = prep.gpu_decode()
+    slots = []
+    for b in range(wl.num_seqs):
+        L = int(wl.context_lens[b])
+        if L % 16:
+            slots += [oracle.slot(wl.block_tables[b], p) for p in range(L, (L // 16 + 1) * 16)]
+    assert slots
+    bad = np.full((len(slots), wl.num_kv_heads, D), np.nan, np.float16)
+    bad[0::3] = np.inf
+    bad[1::3] = -np.inf
+    kh, vh = prep.k_host.copy(), prep.v_host.copy()
+    oracle.reshape_and_cache(bad, bad, kh, vh, np.array(slots, np.int64), wl.num_kv_heads, fp8,
+                             prep.k_scale, prep.v_scale)
+    assert not np.array_equal(kh, prep.k_host)
+    got = prep.gpu_decode(k_pool=torch.from_numpy(kh).cuda(), v_pool=torch.from_numpy(vh).cuda())
+    assert np.isfinite(got).all()
+    assert np.array_equal(got.view(np.uint32), clean.view(np.uint32))
+    ref = oracle.paged_attention_decode(prep.q_host, kh, vh, wl.block_tables, wl.context_lens,
+                                        wl.num_kv_heads, fp8, prep.sm_scale, prep.k_scale,
+                                        prep.v_scale)
+    err = max_err(got, ref)
+    _report(f"poisoned tail slots fp8={fp8}", err, TOL[fp8])
+    assert err <= TOL[fp8]
+
+
 def test_reruns_are_bit_identical():
     prep = Prepared(workloads.tiny(seed=4, fp8=True, partition_size=32))
     a = prep.gpu_decode()
