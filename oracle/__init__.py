@@ -65,6 +65,11 @@ def _load():
     lib.oracle_paged_attention_decode.argtypes = [P, P, P, P, P, ctypes.c_int, P] + \
         [ctypes.c_int] * 5 + [f32, f32, f32, ctypes.c_int]
     lib.oracle_paged_attention_decode.restype = None
+    lib.oracle_reshape_and_cache_dynamic.argtypes = [P] * 7 + [ctypes.c_int] * 4
+    lib.oracle_reshape_and_cache_dynamic.restype = None
+    lib.oracle_paged_attention_decode_dynamic.argtypes = [P] * 7 + [ctypes.c_int, P] + \
+        [ctypes.c_int] * 4 + [f32, ctypes.c_int]
+    lib.oracle_paged_attention_decode_dynamic.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -212,6 +217,50 @@ def paged_attention_decode(q, k_pool: np.ndarray, v_pool: np.ndarray, block_tabl
         _ptr(bt), bt.shape[1], _ptr(cl), B, Hq, num_kv_heads, D, int(bool(fp8)),
         float(np.float32(sm_scale)), float(np.float32(k_scale)), float(np.float32(v_scale)),
         int(threads))
+    return out
+
+
+def reshape_and_cache_dynamic(key, value, k_pool: np.ndarray, v_pool: np.ndarray,
+                              k_scales: np.ndarray, v_scales: np.ndarray, slots,
+                              num_kv_heads: int) -> None:
+    """Write [T][Hkv][D] fp16 rows into FP8 byte pools whose (block, head)
+    tiles carry their own fp32 scale ([NB][Hkv] arrays, updated in place):
+    dynamic per-block scaling, "Optimización de KV Cache ... (128K)", §8."""
+    kb, vb = _f16_bits(key), _f16_bits(value)
+    T = kb.shape[0] if kb.ndim else 0
+    D = kb.shape[-1]
+    assert kb.shape == vb.shape and kb.shape[1] == num_kv_heads
+    sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int64))
+    assert sl.shape == (T,)
+    tile = BLOCK_SIZE * D * num_kv_heads
+    assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
+    assert k_pool.size % tile == 0 and v_pool.size == k_pool.size
+    nb = k_pool.size // tile
+    for a in (k_scales, v_scales):
+        assert a.dtype == np.float32 and a.shape == (nb, num_kv_heads) and a.flags["C_CONTIGUOUS"]
+    _load().oracle_reshape_and_cache_dynamic(_ptr(kb), _ptr(vb), _ptr(k_pool), _ptr(v_pool),
+                                             _ptr(k_scales), _ptr(v_scales), _ptr(sl), T,
+                                             num_kv_heads, D, nb)
+
+
+def paged_attention_decode_dynamic(q, k_pool: np.ndarray, v_pool: np.ndarray,
+                                   k_scales: np.ndarray, v_scales: np.ndarray, block_tables,
+                                   context_lens, num_kv_heads: int, sm_scale: float,
+                                   threads: int = 0) -> np.ndarray:
+    """fp64 decode attention over an FP8 pool with per-(block, head) scales."""
+    qb = _f16_bits(q)
+    B, Hq, D = qb.shape
+    assert Hq % num_kv_heads == 0
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    assert bt.ndim == 2 and bt.shape[0] == B and cl.shape == (B,)
+    ks = np.ascontiguousarray(k_scales, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scales, dtype=np.float32)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    _load().oracle_paged_attention_decode_dynamic(
+        _ptr(out), _ptr(qb), _ptr(np.ascontiguousarray(k_pool)), _ptr(np.ascontiguousarray(v_pool)),
+        _ptr(ks), _ptr(vs), _ptr(bt), bt.shape[1], _ptr(cl), B, Hq, num_kv_heads, D,
+        float(np.float32(sm_scale)), int(threads))
     return out
 
 

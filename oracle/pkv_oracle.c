@@ -26,7 +26,12 @@
  *   - decode attention: a library scaled-dot-product attention on the
  *     logically ordered rows, closed forms (one token, equal keys, zero
  *     query, two tokens), and invariances (block permutation, shared vs
- *     copied prefix, grouped-query vs repeated heads).
+ *     copied prefix, grouped-query vs repeated heads);
+ *   - per-block dynamic scales: one-call fills against a library cast,
+ *     growth by a power of two (old codes drop one binade exactly), the
+ *     fresh-block reset, the floor and non-finite inputs, error bounds after
+ *     repeated growth, and decode against library attention on rows rebuilt
+ *     with their own block's scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -223,11 +228,11 @@ void oracle_reshape_and_cache(const uint16_t* key, const uint16_t* value, uint8_
  *   out      = sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s).
  * L_b = 0 gives zeros.  out is fp64 [B][Hq][D].  The (b, h) pairs are
  * independent and are spread over `threads` OpenMP threads (0 = default). */
-void oracle_paged_attention_decode(double* out, const uint16_t* q, const uint8_t* k_pool,
-                                   const uint8_t* v_pool, const int32_t* block_tables,
-                                   int max_blocks, const int32_t* context_lens, int B, int Hq,
-                                   int Hkv, int D, int fp8, float sm_scale, float k_scale,
-                                   float v_scale, int threads) {
+static void orc_decode(double* out, const uint16_t* q, const uint8_t* k_pool,
+                       const uint8_t* v_pool, const int32_t* block_tables, int max_blocks,
+                       const int32_t* context_lens, int B, int Hq, int Hkv, int D, int fp8,
+                       float sm_scale, float k_scale, float v_scale, const float* k_bscales,
+                       const float* v_bscales, int threads) {
   int G = Hq / Hkv;
   double ks = fp8 ? (double)k_scale : 1.0, vs = fp8 ? (double)v_scale : 1.0;
 #ifdef _OPENMP
@@ -253,9 +258,10 @@ void oracle_paged_attention_decode(double* out, const uint16_t* q, const uint8_t
     double m = -INFINITY;
     for (int t = 0; t < L; ++t) {
       int64_t block = row[t / ORC_BS];
+      double kst = k_bscales ? (double)k_bscales[block * Hkv + kv] : ks;
       double dot = 0.0;
       for (int d = 0; d < D; ++d)
-        dot += qd[d] * orc_load(k_pool, 0, block, kv, t % ORC_BS, d, Hkv, D, fp8, ks);
+        dot += qd[d] * orc_load(k_pool, 0, block, kv, t % ORC_BS, d, Hkv, D, fp8, kst);
       s[t] = (double)sm_scale * dot;
       if (s[t] > m)
         m = s[t];
@@ -264,9 +270,10 @@ void oracle_paged_attention_decode(double* out, const uint16_t* q, const uint8_t
     for (int t = 0; t < L; ++t) {
       int64_t block = row[t / ORC_BS];
       double w = exp(s[t] - m);
+      double vst = v_bscales ? (double)v_bscales[block * Hkv + kv] : vs;
       den += w;
       for (int d = 0; d < D; ++d)
-        o[d] += w * orc_load(v_pool, 1, block, kv, t % ORC_BS, d, Hkv, D, fp8, vs);
+        o[d] += w * orc_load(v_pool, 1, block, kv, t % ORC_BS, d, Hkv, D, fp8, vst);
     }
     for (int d = 0; d < D; ++d)
       o[d] /= den;
@@ -276,6 +283,135 @@ void oracle_paged_attention_decode(double* out, const uint16_t* q, const uint8_t
 }
 
 /* Number of OpenMP threads a parallel region would use (for reports). */
+void oracle_paged_attention_decode(double* out, const uint16_t* q, const uint8_t* k_pool,
+                                   const uint8_t* v_pool, const int32_t* block_tables,
+                                   int max_blocks, const int32_t* context_lens, int B, int Hq,
+                                   int Hkv, int D, int fp8, float sm_scale, float k_scale,
+                                   float v_scale, int threads) {
+  orc_decode(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, B, Hq, Hkv, D, fp8,
+             sm_scale, k_scale, v_scale, NULL, NULL, threads);
+}
+
+/* Decode over an FP8 pool whose blocks carry their own scales: the element
+ * (block, kv head, t, d) stands for E4M3(code) * scales[block][kv head]
+ * ([FP8-128K] §8, dynamic scaling: one scale per cache block). */
+void oracle_paged_attention_decode_dynamic(double* out, const uint16_t* q, const uint8_t* k_pool,
+                                           const uint8_t* v_pool, const float* k_bscales,
+                                           const float* v_bscales, const int32_t* block_tables,
+                                           int max_blocks, const int32_t* context_lens, int B,
+                                           int Hq, int Hkv, int D, float sm_scale, int threads) {
+  orc_decode(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, B, Hq, Hkv, D, 1,
+             sm_scale, 1.0f, 1.0f, k_bscales, v_bscales, threads);
+}
+
+/* ------------------------------------------------- write with block scales */
+
+/* Store T new K/V rows into an FP8 pool whose (block, kv head) tiles carry
+ * their own scale ([FP8-128K] §8, dynamic scaling: the MaxAbs of each block is
+ * measured as the cache is written and the scale follows it).  The pages fix
+ * neither the floor nor what happens to a block filled over several calls;
+ * the reading implemented here, per call and per (block b, head h), for K
+ * and V separately, with W the offsets of b this call writes:
+ *   1. a = largest |x| over the finite elements of the new rows in W;
+ *   2. the block is fresh when offset 0 is in W (its first token arrives
+ *      now): its old scale and its other slots are disregarded;
+ *   3. s_old = 0 if fresh, else the stored scale;
+ *      s_new = max(s_old, fp32(a / 448), 2^-126), so the largest element maps
+ *      to 448 and a scale is never zero;
+ *   4. if not fresh and s_new > s_old, every slot of b outside W is
+ *      re-encoded: code' = E4M3(fp32(E4M3value(code) * fp32(s_old / s_new)))
+ *      (a NaN code stays NaN) -- the old rows are only held as codes;
+ *   5. each new element becomes E4M3(fp32(x / s_new)); the stored scale
+ *      becomes s_new.
+ * Slots must be distinct within a call; negative or out-of-pool slots are
+ * skipped. */
+static double orc_abs_finite(uint16_t bits) {
+  double x = oracle_f16_to_double(bits);
+  return isfinite(x) ? fabs(x) : 0.0;
+}
+
+void oracle_reshape_and_cache_dynamic(const uint16_t* key, const uint16_t* value,
+                                      uint8_t* k_pool, uint8_t* v_pool, float* k_bscales,
+                                      float* v_bscales, const int64_t* slots, int T, int Hkv,
+                                      int D, int num_blocks) {
+  const float floor_scale = (float)ldexp(1.0, -126);
+  uint32_t* written = (uint32_t*)calloc((size_t)num_blocks, sizeof(uint32_t));
+  double* amax = (double*)calloc((size_t)num_blocks * Hkv * 2, sizeof(double));
+  float* s_new = (float*)calloc((size_t)num_blocks * Hkv * 2, sizeof(float));
+  /* 1. offsets written and MaxAbs of the new rows, per (block, head, K/V) */
+  for (int i = 0; i < T; ++i) {
+    int64_t sl = slots[i];
+    if (sl < 0 || sl >= (int64_t)num_blocks * ORC_BS)
+      continue;
+    int64_t b = sl / ORC_BS;
+    written[b] |= 1u << (sl % ORC_BS);
+    for (int h = 0; h < Hkv; ++h)
+      for (int d = 0; d < D; ++d) {
+        int64_t src = ((int64_t)i * Hkv + h) * D + d;
+        double* ak = &amax[(b * Hkv + h) * 2];
+        double xk = orc_abs_finite(key[src]), xv = orc_abs_finite(value[src]);
+        if (xk > ak[0])
+          ak[0] = xk;
+        if (xv > ak[1])
+          ak[1] = xv;
+      }
+  }
+  /* 2-4. new scales, and old slots re-encoded where a scale grew */
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t b = 0; b < num_blocks; ++b) {
+    if (!written[b])
+      continue;
+    int fresh = (written[b] & 1u) != 0;
+    for (int h = 0; h < Hkv; ++h)
+      for (int is_v = 0; is_v < 2; ++is_v) {
+        float* stored = is_v ? &v_bscales[b * Hkv + h] : &k_bscales[b * Hkv + h];
+        uint8_t* pool = is_v ? v_pool : k_pool;
+        float s_old = fresh ? 0.0f : *stored;
+        float s = oracle_quotient(amax[(b * Hkv + h) * 2 + is_v], 448.0f);
+        if (s < s_old)
+          s = s_old;
+        if (s < floor_scale)
+          s = floor_scale;
+        s_new[(b * Hkv + h) * 2 + is_v] = s;
+        if (!fresh && s > s_old) {
+          float r = oracle_quotient((double)s_old, s);
+          for (int t = 0; t < ORC_BS; ++t) {
+            if (written[b] & (1u << t))
+              continue;
+            for (int d = 0; d < D; ++d) {
+              uint8_t* c = &pool[orc_addr(is_v, b, h, t, d, Hkv, D, 1)];
+              if ((*c & 0x7F) == 0x7F)
+                continue; /* NaN stays NaN */
+              *c = oracle_e4m3_encode((float)(oracle_e4m3_decode(*c) * (double)r));
+            }
+          }
+        }
+        *stored = s;
+      }
+  }
+  /* 5. the new rows, encoded with their block's new scale */
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < T; ++i) {
+    int64_t sl = slots[i];
+    if (sl < 0 || sl >= (int64_t)num_blocks * ORC_BS)
+      continue;
+    int64_t b = sl / ORC_BS;
+    int t = (int)(sl % ORC_BS);
+    for (int h = 0; h < Hkv; ++h)
+      for (int d = 0; d < D; ++d) {
+        int64_t src = ((int64_t)i * Hkv + h) * D + d;
+        float sk = s_new[(b * Hkv + h) * 2], sv = s_new[(b * Hkv + h) * 2 + 1];
+        k_pool[orc_addr(0, b, h, t, d, Hkv, D, 1)] =
+            oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double(key[src]), sk));
+        v_pool[orc_addr(1, b, h, t, d, Hkv, D, 1)] =
+            oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double(value[src]), sv));
+      }
+  }
+  free(written);
+  free(amax);
+  free(s_new);
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

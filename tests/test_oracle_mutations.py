@@ -1,7 +1,7 @@
 """The oracle's pins are strong enough: plant a plausible mistake in a copy of
 the oracle source (on the CPU), rebuild it, and check that at least one pin
 fails for every mistake.  The pins run here are the ones in
-test_oracle_fp8.py, test_oracle_attention.py and test_oracle_pool_model.py."""
+test_oracle_fp8.py, test_oracle_attention.py and test_oracle_dynamic.py."""
 import os
 import subprocess
 import sys
@@ -11,6 +11,7 @@ import pytest
 import oracle
 from conftest import ROOT
 import test_oracle_attention as ta
+import test_oracle_dynamic as tdy
 import test_oracle_fp8 as tf
 
 SRC = os.path.join(ROOT, "oracle", "pkv_oracle.c")
@@ -38,6 +39,23 @@ MUTATIONS = [
      "return (int64_t)table_row[pos / ORC_BS] * ORC_BS;"),
     ("stale table entry read", "int64_t block = row[t / ORC_BS];\n      double w",
      "int64_t block = row[t / ORC_BS + (t >= 16 ? 1 : 0)];\n      double w"),
+    # per-block dynamic scales
+    ("no requantization when a scale grows", "if (!fresh && s > s_old) {", "if (0) {"),
+    ("fresh block keeps its stale scale", "float s_old = fresh ? 0.0f : *stored;",
+     "float s_old = *stored;"),
+    ("requantization ratio inverted", "float r = oracle_quotient((double)s_old, s);",
+     "float r = oracle_quotient((double)s, s_old);"),
+    ("block scale ignores the head", "(double)k_bscales[block * Hkv + kv]",
+     "(double)k_bscales[block * Hkv]"),
+    ("V read with the K block scale", "(double)v_bscales[block * Hkv + kv]",
+     "(double)k_bscales[block * Hkv + kv]"),
+    ("scale floor dropped", "if (s < floor_scale)\n          s = floor_scale;", ""),
+    ("MaxAbs not divided by 448", "oracle_quotient(amax[(b * Hkv + h) * 2 + is_v], 448.0f)",
+     "(float)amax[(b * Hkv + h) * 2 + is_v]"),
+    ("non-finite inputs measured", "return isfinite(x) ? fabs(x) : 0.0;", "return fabs(x);"),
+    ("K MaxAbs taken from V", "if (xk > ak[0])\n          ak[0] = xk;",
+     "if (xv > ak[0])\n          ak[0] = xv;"),
+    ("new scale not stored", "        *stored = s;\n", ""),
 ]
 
 
@@ -57,6 +75,11 @@ def _pins(orc):
         ("sdpa fp8 G2", lambda: ta.test_decode_matches_library_sdpa(orc, True, 6, 3)),
         ("single token fp8", lambda: ta.test_decode_single_token_returns_its_value_row(orc, True)),
         ("zero query", lambda: ta.test_decode_zero_query_is_mean_of_values(orc)),
+        ("dyn one call", lambda: tdy.test_one_call_fill_matches_library_cast(orc)),
+        ("dyn growth 2x", lambda: tdy.test_growth_by_a_power_of_two_requantizes_old_rows_exactly(orc)),
+        ("dyn fresh", lambda: tdy.test_offset_zero_starts_a_fresh_block(orc)),
+        ("dyn floor", lambda: tdy.test_zero_rows_get_the_floor_scale_and_non_finite_values_are_not_measured(orc)),
+        ("dyn sdpa", lambda: tdy.test_decode_with_block_scales_matches_library_sdpa(orc, 8, 2)),
     ]
     for name, fn in checks:
         try:
