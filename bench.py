@@ -7,7 +7,9 @@ de KV Cache con PagedAttention y Cuantización FP8 ...", §2 -- 64 sequences,
 8192 cached tokens each plus one new token, 64 query / 8 KV heads, head dim
 128, 16-token blocks scattered over a shuffled pool of 36864 blocks, FP8 E4M3
 cache with per-tensor scales amax/448.  `--workload` selects the other
-reference shapes (tiny, fp16 batch, 128K contexts, ragged shared prefixes).
+reference shapes (tiny, fp16 batch, 128K contexts, ragged shared prefixes);
+`--kv-scales block` switches an FP8 workload to per-(block, KV head) scales
+measured as the cache is written (same page, §8, dynamic scaling).
 
 Every workload is built through the library's host block pool: sequences are
 created and grown block by block (forked from a group leader where they share
@@ -117,6 +119,9 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=None,
                     help="longest split-KV partition in tokens (default: the workload's "
                          "own, else the library's choice)")
+    ap.add_argument("--kv-scales", choices=("tensor", "block"), default="tensor",
+                    help="FP8 scales: one per tensor (amax/448, default) or one per "
+                         "(block, KV head) measured as the cache is written")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8,
                     help="sequences of the workload the CPU oracle baseline decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -145,6 +150,10 @@ def main() -> int:
     Lmax = wl.max_context_len
     e = wl.elem_bytes
     layout = pkv.CacheLayout(NB, Hkv, pkv.PKV_FP8_E4M3FN if wl.fp8 else pkv.PKV_F16)
+    dyn = args.kv_scales == "block"
+    if dyn and not wl.fp8:
+        print("bench.py: per-block scales apply to FP8 caches only", file=sys.stderr)
+        return 2
 
     # ---- a1 on the host: block pool, on-demand allocation, forks, shuffled placement
     pool, seqs, per_seq, bulk_slots, step_slots, host_slot_us = build_sequences(pkv, wl)
@@ -184,13 +193,24 @@ def main() -> int:
     P = pkv.pkv_decode_partition_size(B, Hkv, Lmax, layout.dtype, req)
     ws = torch.empty(max(1, pkv.pkv_decode_workspace_bytes(B, Hq, Hkv, Lmax, layout.dtype, P)),
                      dtype=torch.uint8, device=dev)
+    if dyn:
+        k_bs = torch.zeros((NB, Hkv), dtype=torch.float32, device=dev)
+        v_bs = torch.zeros_like(k_bs)
+        wws = torch.empty(pkv.pkv_reshape_dynamic_workspace_bytes(layout), dtype=torch.uint8,
+                          device=dev)
+
+    def write(k, v, slots):
+        if dyn:
+            pkv.pkv_reshape_and_cache_dynamic(k, v, k_pool, v_pool, k_bs, v_bs, slots, layout,
+                                              wws)
+        else:
+            pkv.pkv_reshape_and_cache(k, v, k_pool, v_pool, slots, layout, k_scale, v_scale)
 
     # ---- bulk fill (a prefill-sized write of every cached token), timed on its own
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    pkv.pkv_reshape_and_cache(key_src, val_src, k_pool, v_pool, d_bulk_slots, layout, k_scale,
-                              v_scale)
+    write(key_src, val_src, d_bulk_slots)
     e1.record()
     torch.cuda.synchronize()
     bulk_ms = e0.elapsed_time(e1)
@@ -198,10 +218,18 @@ def main() -> int:
     del key_src, val_src
 
     def step(ev=None):
-        pkv.pkv_reshape_and_cache(new_k, new_v, k_pool, v_pool, d_step_slots, layout, k_scale,
-                                  v_scale)
+        write(new_k, new_v, d_step_slots)
         if ev is not None:
             ev[0].record()
+        if dyn:
+            # one call: the partition kernel, then the merge when a sequence
+            # spans several partitions (none at the default workload)
+            pkv.pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_bs, v_bs, d_tables,
+                                                   d_lens, Lmax, layout, sm_scale, P, ws,
+                                                   shared_prefix_blocks=d_shared)
+            if ev is not None:
+                ev[1].record()
+            return
         pkv.pkv_decode_partitions(out, q, k_pool, v_pool, d_tables, d_lens, Lmax, layout,
                                   sm_scale, k_scale, v_scale, P, ws,
                                   shared_prefix_blocks=d_shared)
@@ -237,6 +265,11 @@ def main() -> int:
     tokens = int(lens.astype(np.int64).sum())
     logical = tokens * Hkv * D * 2 * e                  # every token of every sequence
     unique = (T + B) * Hkv * D * 2 * e                  # each stored token once
+    if dyn:  # plus one K and one V fp32 scale per (block, KV head) tile read
+        nblk = -(-lens.astype(np.int64) // 16)
+        used = np.unique(np.concatenate([tables[i, :nblk[i]] for i in range(B)]))
+        logical += int(nblk.sum()) * Hkv * 8
+        unique += int(used.size) * Hkv * 8
     value = unique / (step_ms * 1e-3) / 1e9
     achieved = unique / (part_ms * 1e-3) / 1e9
 
@@ -256,11 +289,20 @@ def main() -> int:
         rng = np.random.default_rng(306)
         src_k = rng.standard_normal((slots.size, Hkv, D), dtype=np.float32).astype(np.float16)
         src_v = rng.standard_normal((slots.size, Hkv, D), dtype=np.float32).astype(np.float16)
-        oracle.reshape_and_cache(src_k, src_v, kh, vh, slots, Hkv, wl.fp8, k_scale, v_scale)
+        if not dyn:
+            oracle.reshape_and_cache(src_k, src_v, kh, vh, slots, Hkv, wl.fp8, k_scale, v_scale)
         qh = rng.standard_normal((S, Hq, D), dtype=np.float32).astype(np.float16)
-        t0 = time.perf_counter()
-        oracle.paged_attention_decode(qh, kh, vh, tables[:S], lens[:S], Hkv, wl.fp8, sm_scale,
-                                      k_scale, v_scale, threads)
+        if dyn:
+            ksh = np.zeros((NB, Hkv), dtype=np.float32)
+            vsh = np.zeros_like(ksh)
+            oracle.reshape_and_cache_dynamic(src_k, src_v, kh, vh, ksh, vsh, slots, Hkv)
+            t0 = time.perf_counter()
+            oracle.paged_attention_decode_dynamic(qh, kh, vh, ksh, vsh, tables[:S], lens[:S],
+                                                  Hkv, sm_scale, threads)
+        else:
+            t0 = time.perf_counter()
+            oracle.paged_attention_decode(qh, kh, vh, tables[:S], lens[:S], Hkv, wl.fp8,
+                                          sm_scale, k_scale, v_scale, threads)
         cpu_s = time.perf_counter() - t0
         sample_bytes = int(lens[:S].astype(np.int64).sum()) * Hkv * D * 2 * e
         cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
@@ -281,10 +323,13 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "global_batch": B, "seq_len": Lmax,
+        "config": {"workload": wl.name + ("-block-scales" if dyn else ""),
+                   "global_batch": B, "seq_len": Lmax,
                    "total_tokens": tokens, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
                    "block_size": 16, "pool_blocks": NB, "partition_size": P,
                    "kv_dtype": "fp8_e4m3fn" if wl.fp8 else "f16",
+                   "kv_scales": ("per (block, kv head)" if dyn else "per tensor")
+                   if wl.fp8 else None,
                    "arith": "f16 MFMA inputs, f32 accumulate", "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tok_per_s": round(tokens / (step_ms * 1e-3), 1),
@@ -297,7 +342,8 @@ def main() -> int:
         "bulk_fill_gbs": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload)},
+                     "traffic": measured_traffic(args.workload + ("_block_scales" if dyn
+                                                                 else ""))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

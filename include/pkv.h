@@ -221,6 +221,67 @@ pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens, int32_t nu
 pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const pkv_cache_layout* layout,
                            const int32_t* src_dst_pairs, int32_t num_pairs, void* stream);
 
+/* --------------------------------------------- per-block dynamic FP8 scales
+ *
+ * [FP8-128K] §8, dynamic scaling: instead of one scale per tensor, each
+ * (block, KV head) tile of K and of V carries its own fp32 scale, measured
+ * from the MaxAbs of the values written into it as the cache is written.
+ * FP8 pools only (PKV_ERR_UNSUPPORTED otherwise).
+ *   k_block_scales, v_block_scales  device fp32 [num_blocks][num_kv_heads],
+ *                 caller-owned, updated in place by the write; an element of
+ *                 tile (b, h) stands for E4M3value(code) * scales[b][h].
+ *
+ * Write rule, per call and per tile (K and V apart), with W the offsets of
+ * the block this call writes (the pages leave open how a block filled over
+ * several calls is scaled; this is the library's reading):
+ *   - the block is fresh when offset 0 is in W: its first token arrives now,
+ *     so its stored scale and its other slots are disregarded;
+ *   - s_new = max(s_old (0 if fresh), fp32(m / 448), 2^-126) with m the
+ *     largest magnitude among the finite new values: the block's MaxAbs maps
+ *     to 448 and a scale is never zero;
+ *   - if a non-fresh tile's scale grows, its slots outside W are re-encoded,
+ *     code' = E4M3(fp32(E4M3value(code) * fp32(s_old / s_new))), NaN codes
+ *     kept (the earlier rows exist only as codes);
+ *   - new elements become E4M3(fp32(x / s_new)) (RNE, saturating, NaN kept).
+ * Slots must be distinct within a call; calls are ordered by the stream. */
+
+/* Scratch bytes pkv_reshape_and_cache_dynamic needs for this layout:
+ * num_blocks * (2 * num_kv_heads + 1) 32-bit words, rounded up to 256; 0 for
+ * a non-FP8 or invalid layout. */
+uint64_t pkv_reshape_dynamic_workspace_bytes(const pkv_cache_layout* layout);
+
+/* Write T new K/V rows with per-block scales (rule above).  Arguments as in
+ * pkv_reshape_and_cache, plus the two scale arrays and a device workspace of
+ * at least pkv_reshape_dynamic_workspace_bytes(layout) bytes, 256-byte
+ * aligned, whose contents are internal (no clearing needed).  Three kernel
+ * launches on `stream`. */
+pkv_status pkv_reshape_and_cache_dynamic(const void* key, const void* value, void* k_pool,
+                                         void* v_pool, float* k_block_scales,
+                                         float* v_block_scales, const int64_t* slot_mapping,
+                                         int32_t num_tokens, const pkv_cache_layout* layout,
+                                         void* workspace, uint64_t workspace_bytes,
+                                         void* stream);
+
+/* Decode attention over an FP8 pool with per-block scales: as
+ * pkv_paged_attention_decode, with each tile's K and V scale read from the
+ * arrays in place of the per-tensor k_scale and v_scale (so there are none).
+ * The workspace is sized by pkv_decode_workspace_bytes for the FP8 dtype.
+ * Table entries outside [0, num_blocks) read as zeros, as in the plain call. */
+pkv_status pkv_paged_attention_decode_dynamic(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const float* k_block_scales, const float* v_block_scales, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale,
+    int32_t partition_size, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* pkv_copy_blocks for a pool with per-block scales: the destination also
+ * takes the source's scale rows (copy-on-write of a partly filled block). */
+pkv_status pkv_copy_blocks_dynamic(void* k_pool, void* v_pool, float* k_block_scales,
+                                   float* v_block_scales, const pkv_cache_layout* layout,
+                                   const int32_t* src_dst_pairs, int32_t num_pairs,
+                                   void* stream);
+
 /* ------------------------------------------------ host block pool and tables */
 
 /* A pool of physical block ids with reference counts, and the sequences that

@@ -17,7 +17,8 @@ __all__ = [
     "load_library", "pkv_status_string", "pkv_bytes_per_token", "pkv_pool_bytes",
     "pkv_decode_partition_size", "pkv_decode_workspace_bytes", "pkv_reshape_and_cache",
     "pkv_paged_attention_decode", "pkv_decode_partitions", "pkv_decode_reduce",
-    "pkv_copy_blocks",
+    "pkv_copy_blocks", "pkv_reshape_dynamic_workspace_bytes", "pkv_reshape_and_cache_dynamic",
+    "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +86,11 @@ def load_library():
                                    i32, P, u64, P], i32),
         "pkv_decode_reduce": ([P, P, i32, i32, i32, i32, LP, f32, i32, P, u64, P], i32),
         "pkv_copy_blocks": ([P, P, LP, P, i32, P], i32),
+        "pkv_reshape_dynamic_workspace_bytes": ([LP], u64),
+        "pkv_reshape_and_cache_dynamic": ([P, P, P, P, P, P, P, i32, LP, P, u64, P], i32),
+        "pkv_paged_attention_decode_dynamic": ([P, P, P, P, P, P, P, i32, P, P, i32, i32, i32,
+                                                LP, f32, i32, P, u64, P], i32),
+        "pkv_copy_blocks_dynamic": ([P, P, P, P, LP, P, i32, P], i32),
         "pkv_pool_create": ([i32, i32, u64, ctypes.POINTER(P)], i32),
         "pkv_pool_destroy": ([P], None),
         "pkv_pool_num_blocks": ([P], i32),
@@ -270,6 +276,72 @@ def pkv_copy_blocks(k_pool, v_pool, layout: CacheLayout, src_dst_pairs, stream=N
     _check(load_library().pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), ctypes.byref(layout),
                                           _ptr(src_dst_pairs), n, _stream(stream)),
            "pkv_copy_blocks")
+
+
+# ------------------------------------------- per-block dynamic FP8 scales
+
+def pkv_reshape_dynamic_workspace_bytes(layout: CacheLayout) -> int:
+    return load_library().pkv_reshape_dynamic_workspace_bytes(ctypes.byref(layout))
+
+
+def _block_scales(k_block_scales, v_block_scales, layout):
+    import torch
+    for t, name in ((k_block_scales, "k_block_scales"), (v_block_scales, "v_block_scales")):
+        _require(t, torch.float32, name)
+        if t.numel() != layout.num_blocks * layout.num_kv_heads:
+            raise ValueError(f"{name} must be [num_blocks][num_kv_heads]")
+
+
+def pkv_reshape_and_cache_dynamic(key, value, k_pool, v_pool, k_block_scales, v_block_scales,
+                                  slot_mapping, layout: CacheLayout, workspace=None,
+                                  stream=None) -> None:
+    """FP8 write with per-(block, KV head) scales, updated in place."""
+    import torch
+    _require(key, torch.float16, "key")
+    _require(value, torch.float16, "value")
+    _require(slot_mapping, torch.int64, "slot_mapping")
+    _block_scales(k_block_scales, v_block_scales, layout)
+    T = key.shape[0]
+    if key.shape != value.shape or tuple(key.shape[1:]) != (layout.num_kv_heads, layout.head_dim):
+        raise ValueError("key/value must be [T][num_kv_heads][head_dim]")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must hold one slot per token")
+    if workspace is None:
+        need = pkv_reshape_dynamic_workspace_bytes(layout)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().pkv_reshape_and_cache_dynamic(
+        _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(k_block_scales),
+        _ptr(v_block_scales), _ptr(slot_mapping), T, ctypes.byref(layout), _ptr(workspace),
+        nbytes, _stream(stream)), "pkv_reshape_and_cache_dynamic")
+
+
+def pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_block_scales, v_block_scales,
+                                       block_tables, context_lens, max_context_len: int,
+                                       layout: CacheLayout, sm_scale: float,
+                                       partition_size: int = 0, workspace=None, stream=None,
+                                       shared_prefix_blocks=None) -> None:
+    B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
+    _block_scales(k_block_scales, v_block_scales, layout)
+    workspace, nbytes = _workspace(workspace, B, Hq, layout, max_context_len, partition_size)
+    _check(load_library().pkv_paged_attention_decode_dynamic(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_block_scales),
+        _ptr(v_block_scales), _ptr(block_tables), mb, _ptr(context_lens),
+        _hint(shared_prefix_blocks, B), B, Hq, max_context_len, ctypes.byref(layout), sm_scale,
+        partition_size, _ptr(workspace), nbytes, _stream(stream)),
+        "pkv_paged_attention_decode_dynamic")
+
+
+def pkv_copy_blocks_dynamic(k_pool, v_pool, k_block_scales, v_block_scales, layout: CacheLayout,
+                            src_dst_pairs, stream=None) -> None:
+    import torch
+    _require(src_dst_pairs, torch.int32, "src_dst_pairs")
+    _block_scales(k_block_scales, v_block_scales, layout)
+    n = src_dst_pairs.numel() // 2
+    _check(load_library().pkv_copy_blocks_dynamic(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_block_scales), _ptr(v_block_scales),
+        ctypes.byref(layout), _ptr(src_dst_pairs), n, _stream(stream)),
+        "pkv_copy_blocks_dynamic")
 
 
 # ---------------------------------------------------------- block pool

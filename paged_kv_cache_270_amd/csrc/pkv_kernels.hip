@@ -1,6 +1,7 @@
 // pkv_kernels.hip — gfx950 (MI355X) kernels and the device half of libpkv's
-// C ABI: the cache write, split-KV decode PagedAttention with its
-// log-sum-exp merge, and the block copy used for copy-on-write.
+// C ABI: the cache write (per-tensor or per-block dynamic FP8 scales),
+// split-KV decode PagedAttention with its log-sum-exp merge, and the block
+// copy used for copy-on-write.
 //
 // Pages the kernels follow (cited by title and section):
 //   [FP8-128K] "Optimización de KV Cache con PagedAttention y Cuantización FP8
@@ -16,15 +17,17 @@
 //   * tiles are stored in the order the MFMA operands consume them (see the
 //     layout in pkv.h), so a wave reads a 2 KiB FP8 tile with two 16-byte
 //     loads per lane, each instruction covering 1 KiB of contiguous memory;
-//   * FP8 codes become fp16 with integer bit operations (exact: every E4M3
-//     value is an fp16 value); the scales are folded into the logit scale
-//     and into the final output, never applied per element;
+//   * FP8 codes become fp16 exactly (every E4M3 value is an fp16 value) with
+//     the gfx950 conversion instruction; per-tensor scales are folded into
+//     the logit scale and the final output, per-block scales into the tile's
+//     logits and probabilities, never applied per element;
 //   * QK^T gives S^T (tokens x heads) in the accumulator layout that is
 //     exactly the B operand of the PV MFMA, so the online softmax runs on
-//     registers with two cross-row max reductions per block and no shuffles
-//     of the probabilities;
-//   * split-KV: four waves per workgroup share a partition and merge through
-//     LDS; partitions are merged by a second kernel with the log-sum-exp rule.
+//     registers; its reference max is re-reduced only when a logit exceeds
+//     it by a fixed slack;
+//   * split-KV: up to eight waves per workgroup share a partition and merge
+//     through LDS; partitions are merged by a second kernel with the
+//     log-sum-exp rule.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -145,10 +148,176 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
                     key[th * 16 + c], value[th * 16 + c], k_scale, v_scale);
 }
 
-// ------------------------------------------------------------ copy_blocks
+// ------------------------------------------ write with per-block FP8 scales
+//
+// [FP8-128K] §8, dynamic scaling: each (block, KV head) tile of K and of V
+// carries its own fp32 scale, following the MaxAbs of the values written
+// into it.  Per call and per tile, with W the block's offsets this call
+// writes: the block is fresh when offset 0 is in W (its old scale and other
+// slots are disregarded); s_new = max(s_old or 0 if fresh, fp32(MaxAbs of
+// the new finite values / 448), 2^-126); if a non-fresh tile's scale grows,
+// its slots outside W are re-encoded as E4M3(fp32(value * fp32(s_old /
+// s_new))); new rows are E4M3(fp32(x / s_new)).
+//
+// Three launches, because the new scale of a block depends on every token
+// the call writes into it:
+//   1. clear the scratch entries of the touched blocks;
+//   2. MaxAbs of each new row into the scratch (integer atomic max of the
+//      non-negative float bits) and the written offsets (atomic or);
+//   3. every row is encoded with its tile's new scale; the call's token with
+//      the lowest offset in a block re-encodes the other slots and stores the
+//      new scales.  Any thread may read a tile's scale while that token
+//      replaces it: both values give the same s_new, since s_new is the max.
+
+// Value of an E4M3FN code (not NaN) as fp32, from the format definition.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ uint32_t requant_code(uint32_t c, float r) {
+  if ((c & 0x7Fu) == 0x7Fu) return c;  // NaN stays NaN
+  return e4m3_from_f32(e4m3_value(c) * r);
+}
+
+// Largest finite magnitude among 8 fp16 values, as fp16 bits (integer order
+// of non-negative fp16 bit patterns is their numeric order).
+__device__ __forceinline__ uint32_t max_abs_bits8(u32x4 x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = x[i];
+    const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+    if (lo < 0x7C00u) m = max(m, lo);
+    if (hi < 0x7C00u) m = max(m, hi);
+  }
+  return m;
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
 
 __global__ void __launch_bounds__(256)
+dyn_clear_kernel(const int64_t* __restrict__ slots, int64_t total, int per_block,
+                 int64_t num_slots, uint32_t* __restrict__ amax, uint32_t* __restrict__ written) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int64_t tok = gid / (per_block + 1);
+  const int j = (int)(gid - tok * (per_block + 1));
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  if (j < per_block)
+    amax[blk * per_block + j] = 0u;
+  else
+    written[blk] = 0u;
+}
+
+// One thread per (token, kv head, run of 8 channels), as the plain write;
+// the 16 threads of a row are 16 consecutive lanes.
+__global__ void __launch_bounds__(256)
+dyn_amax_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                const int64_t* __restrict__ slots, int64_t total, int hkv, int64_t num_slots,
+                uint32_t* __restrict__ amax, uint32_t* __restrict__ written) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;                  // total is a multiple of 16: whole rows leave
+  const int c = (int)(gid & 15);
+  const int64_t th = gid >> 4;
+  const int64_t tok = th / hkv;
+  const int h = (int)(th - tok * hkv);
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;  // the same for all 16 lanes of the row
+  uint32_t km = max_abs_bits8(key[th * 16 + c]);
+  uint32_t vm = max_abs_bits8(value[th * 16 + c]);
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) {
+    km = max(km, (uint32_t)__shfl_xor((int)km, m, kWave));
+    vm = max(vm, (uint32_t)__shfl_xor((int)vm, m, kWave));
+  }
+  if (c == 0) {
+    const int64_t blk = slot >> 4;
+    uint32_t* a = amax + (blk * hkv + h) * 2;
+    atomicMax(a, __float_as_uint(f16_bits_to_float(km)));
+    atomicMax(a + 1, __float_as_uint(f16_bits_to_float(vm)));
+    if (h == 0) atomicOr(written + blk, 1u << (slot & 15));
+  }
+}
+
+// Re-encode channels 8c .. 8c+7 of every slot of one FP8 tile outside `keep`.
+__device__ __forceinline__ void requant_k_rows(uint8_t* kp, int c, uint32_t keep, float r) {
+  const int n = c >> 1, j0 = (c & 1) * 8;
+  for (int t = 0; t < kBS; ++t) {
+    if (keep & (1u << t)) continue;
+    u32x2* p = reinterpret_cast<u32x2*>(kp + n * 256 + t * 16 + j0);  // K: 8 contiguous bytes
+    u32x2 w = *p;
+    uint32_t o[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t x = w[i];
+      o[i] = requant_code(x & 0xFFu, r) | (requant_code((x >> 8) & 0xFFu, r) << 8) |
+             (requant_code((x >> 16) & 0xFFu, r) << 16) | (requant_code(x >> 24, r) << 24);
+    }
+    w.x = o[0];
+    w.y = o[1];
+    *p = w;
+  }
+}
+
+__device__ __forceinline__ void requant_v_rows(uint8_t* vp, int c, uint32_t keep, float r) {
+  const int n = c >> 1, j0 = (c & 1) * 8;
+  for (int t = 0; t < kBS; ++t) {
+    if (keep & (1u << t)) continue;
+    uint8_t* vb = vp + (n >> 2) * 1024 + ((t >> 2) * 16 + j0) * 16 + (n & 3) * 4 + (t & 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vb[i * 16] = (uint8_t)requant_code(vb[i * 16], r);
+  }
+}
+
+__global__ void __launch_bounds__(256)
+dyn_write_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                 uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                 float* __restrict__ k_bscale, float* __restrict__ v_bscale,
+                 const int64_t* __restrict__ slots, int64_t total, int hkv, int64_t num_slots,
+                 const uint32_t* __restrict__ amax, const uint32_t* __restrict__ written) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int c = (int)(gid & 15);
+  const int64_t th = gid >> 4;
+  const int64_t tok = th / hkv;
+  const int h = (int)(th - tok * hkv);
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int off = (int)(slot & 15);
+  const int64_t tile = blk * hkv + h;
+  const uint32_t mask = written[blk];
+  const bool fresh = (mask & 1u) != 0;
+  const float min_scale = 0x1p-126f;
+  const float sk_old = fresh ? 0.0f : k_bscale[tile];
+  const float sv_old = fresh ? 0.0f : v_bscale[tile];
+  const float sk = fmaxf(fmaxf(sk_old, __uint_as_float(amax[tile * 2]) / 448.0f), min_scale);
+  const float sv = fmaxf(fmaxf(sv_old, __uint_as_float(amax[tile * 2 + 1]) / 448.0f), min_scale);
+  store_rows8<true>(k_pool, v_pool, tile, off, c, key[th * 16 + c], value[th * 16 + c], sk, sv);
+  if (off != __builtin_ctz(mask)) return;    // not this block's lowest new offset
+  uint8_t* kp = k_pool + tile * (kBS * kD);
+  uint8_t* vp = v_pool + tile * (kBS * kD);
+  if (!fresh && sk > sk_old) requant_k_rows(kp, c, mask, sk_old / sk);
+  if (!fresh && sv > sv_old) requant_v_rows(vp, c, mask, sv_old / sv);
+  if (c == 0) {
+    k_bscale[tile] = sk;
+    v_bscale[tile] = sv;
+  }
+}
+
+// ------------------------------------------------------------ copy_blocks
+
+// One workgroup per (source, destination) pair; with per-block scales the
+// destination's scale rows are copied too.
+__global__ void __launch_bounds__(256)
 copy_blocks_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
+                   float* __restrict__ k_bscale, float* __restrict__ v_bscale, int hkv,
                    const int32_t* __restrict__ pairs, int64_t vecs_per_block, int num_blocks) {
   const int i = blockIdx.x;
   const int src = pairs[2 * i], dst = pairs[2 * i + 1];
@@ -157,6 +326,12 @@ copy_blocks_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
   for (int64_t v = threadIdx.x; v < vecs_per_block; v += 256) {
     k_pool[d0 + v] = k_pool[s0 + v];
     v_pool[d0 + v] = v_pool[s0 + v];
+  }
+  if (k_bscale != nullptr) {
+    for (int h = threadIdx.x; h < hkv; h += 256) {
+      k_bscale[(int64_t)dst * hkv + h] = k_bscale[(int64_t)src * hkv + h];
+      v_bscale[(int64_t)dst * hkv + h] = v_bscale[(int64_t)src * hkv + h];
+    }
   }
 }
 
@@ -178,8 +353,10 @@ struct DecodeArgs {
   int32_t max_ctx;             // clamp for context lengths
   int32_t part_blocks;         // most blocks per partition (partition_size / 16)
   int32_t n_p_max;
-  float qk_scale;              // sm_scale * k_scale * log2(e) [* 256 for FP8]
-  float out_scale;             // v_scale [* 256 for FP8]
+  float qk_scale;              // sm_scale * k_scale * log2(e) [* 256 for FP8 bit dequant]
+  float out_scale;             // v_scale [* 256 for FP8 bit dequant]
+  const float* k_bscale;       // [num_blocks][hkv] per-block K scales, or null
+  const float* v_bscale;       // [num_blocks][hkv] per-block V scales, or null
 };
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
@@ -203,8 +380,16 @@ __device__ __forceinline__ SeqSplit seq_split(const DecodeArgs& a, int L) {
   return s;
 }
 
-__device__ __forceinline__ float wave_shfl_xor(float v, int m) {
-  return __shfl_xor(v, m, kWave);
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
 }
 
 template <bool kFP8>
@@ -270,6 +455,8 @@ struct SoftmaxState {
   float m_ref;   // reference max of the head (log2 units), equal on the 4 rows
   float l;       // sum of this lane's probabilities, relative to m_ref
   f32x4 acc[8];  // O^T rows 16n + 4qg .. +3 for head j, relative to m_ref
+                 // (and, with per-block scales, in units of vref)
+  float vref;    // per-block scales: the largest V scale seen by the wave
 };
 
 // Logits may exceed the reference max by up to 2^8 before the max is
@@ -309,10 +496,15 @@ __device__ __forceinline__ void mask_tail_values(TileRegs<kFP8>& t, int tb, int 
   }
 }
 
-template <bool kFP8, bool kHwCvt, bool kSplitP>
+// One tile: logits, online softmax, PV.  With per-block scales (kDyn) the
+// tile's K scale multiplies its logits (k_mul) and its V scale, relative to
+// the wave's reference vref, its probabilities (v_mul); the normaliser sums
+// the unscaled probabilities.
+template <bool kFP8, bool kHwCvt, bool kSplitP, bool kDyn = false>
 __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qop)[4],
                                              SoftmaxState& st, int tb, int qg, int L,
-                                             float qk_scale) {
+                                             float qk_scale, float k_mul = 1.0f,
+                                             float v_mul = 1.0f) {
   if (tb + kBS > L) mask_tail_values<kFP8>(t, tb, qg, L);  // wave-uniform: last tile only
   // S^T[t][g] = sum_d K[t][d] Q[g][d]: 4 MFMAs over the 128 channels
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -331,9 +523,10 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
   }
   float sv[4];
   bool over = false;
+  const float qk = kDyn ? qk_scale * k_mul : qk_scale;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sv[r] = (tb + qg * 4 + r < L) ? s[r] * qk_scale : -INFINITY;
+    sv[r] = (tb + qg * 4 + r < L) ? s[r] * qk : -INFINITY;
     over |= sv[r] - st.m_ref > kLazyMaxSlack;
   }
   if (__any(over)) {  // wave-uniform: re-reduce the max and rescale
@@ -351,6 +544,17 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
 #pragma unroll
   for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - st.m_ref);
   f16x4 ph, pl;
+  if constexpr (kDyn) {
+    static_assert(kSplitP, "per-block scales use the split probabilities");
+    st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = pr[r] * v_mul;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ph[r] = (_Float16)pw[r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pl[r] = (_Float16)(pw[r] - (float)ph[r]);
+  } else {
 #pragma unroll
   for (int r = 0; r < 4; ++r) ph[r] = (_Float16)pr[r];
   if constexpr (kSplitP) {
@@ -361,6 +565,7 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
   } else {
     // the normaliser sums exactly the fp16 weights the PV product uses
     st.l += ((float)ph[0] + (float)ph[1]) + ((float)ph[2] + (float)ph[3]);
+  }
   }
   // O^T[d][g] += sum_t V^T[d][t] P^T[t][g]: 8 MFMAs of 16 channels
 #pragma unroll
@@ -387,8 +592,10 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
 // w, w + kNW, ...  Lane (j = lane % 16, qg = lane / 16) serves query head
 // kvh*G + j and, in each tile, tokens 4qg .. 4qg+3.  Each wave keeps kPD
 // tiles in flight while it computes on another.
-template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW>
-__global__ void __launch_bounds__(kNW * kWave)
+// With per-block scales the kernel is held to 128 VGPRs (4 waves per SIMD);
+// the compiler fits it without spilling.
+template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false>
+__global__ void __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kDyn ? 4 : 1)))
 decode_partition_kernel(DecodeArgs a) {
   extern __shared__ float smem[];  // [kNW][G][D] outputs, then [kNW][16] max and sum
   const int lane = threadIdx.x & 63;
@@ -427,6 +634,7 @@ decode_partition_kernel(DecodeArgs a) {
   SoftmaxState st;
   st.m_ref = -INFINITY;
   st.l = 0.0f;
+  st.vref = 0.0f;
 #pragma unroll
   for (int n = 0; n < 8; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -440,6 +648,25 @@ decode_partition_kernel(DecodeArgs a) {
     // lane i holds the physical id of this wave's block c0 + i
     const int tbl = lane < cnt ? trow[(int64_t)(c0 + lane) * kNW] : 0;
     const int lb0 = blk0 + w + c0 * kNW;  // logical block of this chunk's tile 0
+    // per-block scales: lane i holds block i's K scale and its V scale
+    // relative to the wave's reference (the largest V scale so far)
+    float k_mul = 1.0f, v_mul = 1.0f;
+    if constexpr (kDyn) {
+      float ks = 0.0f, vs = 0.0f;
+      if (lane < cnt && (unsigned)tbl < (unsigned)a.num_blocks) {
+        ks = a.k_bscale[(int64_t)tbl * a.hkv + kvh];
+        vs = a.v_bscale[(int64_t)tbl * a.hkv + kvh];
+      }
+      const float ref = fmaxf(fmaxf(st.vref, wave_max(vs)), 0x1p-126f);
+      if (ref > st.vref && st.vref > 0.0f) {  // wave-uniform: rescale what is accumulated
+        const float f = st.vref / ref;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) st.acc[n] *= f;
+      }
+      st.vref = ref;
+      k_mul = ks;
+      v_mul = vs / ref;
+    }
     TileRegs<kFP8> buf[kPD + 1];
 #pragma unroll
     for (int r = 0; r < kPD; ++r)
@@ -456,7 +683,13 @@ decode_partition_kernel(DecodeArgs a) {
                             __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane,
                             lb0 + (ii + kPD) * kNW < shared_blocks);
           const int tb = (blk0 + w + (c0 + ii) * kNW) * kBS;  // first token of the tile
-          process_tile<kFP8, kHwCvt, kSplitP>(buf[r], qop, st, tb, qg, L, a.qk_scale);
+          if constexpr (kDyn)
+            process_tile<kFP8, kHwCvt, kSplitP, true>(
+                buf[r], qop, st, tb, qg, L, a.qk_scale,
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k_mul), ii)),
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_mul), ii)));
+          else
+            process_tile<kFP8, kHwCvt, kSplitP>(buf[r], qop, st, tb, qg, L, a.qk_scale);
         }
       }
     }
@@ -466,6 +699,11 @@ decode_partition_kernel(DecodeArgs a) {
   float l_run = st.l;
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
+
+  if constexpr (kDyn) {  // back from units of the wave's V reference
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.acc[n] *= st.vref;
+  }
 
   // merge the kNW waves through LDS
   float* so = smem;                        // [kNW][G][D]
@@ -508,17 +746,6 @@ decode_partition_kernel(DecodeArgs a) {
   }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
 
 // Merge kernel: for each (sequence, query head) whose sequence spans n_p > 1
 // partitions, M = max_p m_p and
@@ -731,6 +958,7 @@ KernelConfig kernel_config() {
 struct DecodePlan {
   DecodeArgs a;
   bool fp8;
+  bool dyn;  // per-block scales
   bool need_reduce;
   KernelConfig cfg;
 };
@@ -740,7 +968,8 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
                        const int32_t* context_lens, const int32_t* shared_prefix_blocks,
                        int32_t num_seqs, int32_t num_q_heads,
                        int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale,
-                       float k_scale, float v_scale, int32_t partition_size, void* workspace,
+                       float k_scale, float v_scale, const float* k_bscale,
+                       const float* v_bscale, int32_t partition_size, void* workspace,
                        uint64_t workspace_bytes, bool need_pools, DecodePlan* plan) {
   pkv_status st = check_layout(layout);
   if (st != PKV_OK) return st;
@@ -751,7 +980,9 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   if (G > kMaxG) return PKV_ERR_UNSUPPORTED;
   plan->cfg = kernel_config();
   plan->fp8 = layout->dtype == PKV_FP8_E4M3FN;
+  plan->dyn = k_bscale != nullptr || v_bscale != nullptr;
   plan->need_reduce = false;
+  if (plan->dyn && !plan->fp8) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;  // nothing to compute; no pointer is touched
   if (!out || !context_lens || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
   if (need_pools) {
@@ -760,6 +991,8 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
       return PKV_ERR_INVALID_ARG;
     if (max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
     if (!std::isfinite(sm_scale)) return PKV_ERR_INVALID_ARG;
+    if (plan->dyn && (!k_bscale || !v_bscale || !aligned(k_bscale, 4) || !aligned(v_bscale, 4)))
+      return PKV_ERR_INVALID_ARG;
   } else if (max_blocks_per_seq <= 0) {
     return PKV_ERR_INVALID_ARG;
   }
@@ -794,9 +1027,11 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   a.max_ctx = max_context_len;
   a.part_blocks = part / kBS;
   a.n_p_max = wl.n_p_max;
-  plan->cfg = kernel_config();
-  // FP8 tiles decoded by bit operations hold code / 256: fold the 256 back in
-  const float deq = (fp8 && !plan->cfg.hw_cvt) ? 256.0f : 1.0f;
+  a.k_bscale = plan->dyn ? k_bscale : nullptr;
+  a.v_bscale = plan->dyn ? v_bscale : nullptr;
+  // FP8 tiles decoded by bit operations hold code / 256: fold the 256 back
+  // in (per-block scales always use the hardware conversion)
+  const float deq = (fp8 && !plan->cfg.hw_cvt && !plan->dyn) ? 256.0f : 1.0f;
   const float log2e = 1.4426950408889634f;
   a.qk_scale = sm_scale * (fp8 ? k_scale * deq : 1.0f) * log2e;
   a.out_scale = fp8 ? v_scale * deq : 1.0f;
@@ -862,10 +1097,22 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
   return launch_status();
 }
 
-template <bool kFP8, bool kHw, bool kSplit, int kPD, int kNW>
+template <bool kFP8, bool kHw, bool kSplit, int kPD, int kNW, bool kDyn = false>
 static void launch_partition_v(dim3 grid, hipStream_t s, const DecodeArgs& a) {
   const size_t lds = (size_t)(kNW * a.g * kD + 2 * kNW * 16) * sizeof(float);
-  decode_partition_kernel<kFP8, kHw, kSplit, kPD, kNW><<<grid, dim3(kNW * kWave), lds, s>>>(a);
+  decode_partition_kernel<kFP8, kHw, kSplit, kPD, kNW, kDyn>
+      <<<grid, dim3(kNW * kWave), lds, s>>>(a);
+}
+
+// Per-block scales: the default family (hardware convert, split P, one tile
+// in flight besides the current one) at every wave count.
+static void launch_partition_dyn(int nw, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  switch (nw) {
+    case 1: return launch_partition_v<true, true, true, 1, 1, true>(grid, s, a);
+    case 2: return launch_partition_v<true, true, true, 1, 2, true>(grid, s, a);
+    case 8: return launch_partition_v<true, true, true, 1, 8, true>(grid, s, a);
+    default: return launch_partition_v<true, true, true, 1, 4, true>(grid, s, a);
+  }
 }
 
 // The measured default family (hardware convert, split P) exists for every
@@ -915,7 +1162,9 @@ static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStre
   (void)hipGetLastError();
   const KernelConfig& c = pl.cfg;
   const int nw = waves_for(pl);
-  if (!pl.fp8)
+  if (pl.dyn)
+    launch_partition_dyn(nw, grid, s, pl.a);
+  else if (!pl.fp8)
     launch_partition<false, false, true>(c.prefetch, nw, grid, s, pl.a);
   else if (c.hw_cvt)
     c.split_p_fp8 ? launch_partition<true, true, true>(c.prefetch, nw, grid, s, pl.a)
@@ -952,8 +1201,8 @@ extern "C" pkv_status pkv_decode_partitions(float* out, const void* q, const voi
   DecodePlan pl;
   pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                               context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
-                              max_context_len, layout, sm_scale, k_scale, v_scale,
-                              partition_size, workspace, workspace_bytes, true, &pl);
+                              max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
   if (st != PKV_OK) return st;
   return run_partitions(pl, num_seqs, static_cast<hipStream_t>(stream));
 }
@@ -967,8 +1216,8 @@ extern "C" pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens,
   DecodePlan pl;
   pkv_status st = plan_decode(out, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq,
                               context_lens, nullptr, num_seqs, num_q_heads, max_context_len,
-                              layout, 1.0f, 1.0f, v_scale, partition_size, workspace,
-                              workspace_bytes, false, &pl);
+                              layout, 1.0f, 1.0f, v_scale, nullptr, nullptr, partition_size,
+                              workspace, workspace_bytes, false, &pl);
   if (st != PKV_OK) return st;
   return run_reduce(pl, num_seqs, static_cast<hipStream_t>(stream));
 }
@@ -983,8 +1232,8 @@ extern "C" pkv_status pkv_paged_attention_decode(
   DecodePlan pl;
   pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                               context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
-                              max_context_len, layout, sm_scale, k_scale, v_scale,
-                              partition_size, workspace, workspace_bytes, true, &pl);
+                              max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
   if (st != PKV_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_partitions(pl, num_seqs, s);
@@ -1006,7 +1255,100 @@ extern "C" pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const pkv_cach
   (void)hipGetLastError();
   copy_blocks_kernel<<<dim3((unsigned)num_pairs), dim3(256), 0,
                        static_cast<hipStream_t>(stream)>>>(
-      static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), src_dst_pairs, bytes / 16,
-      layout->num_blocks);
+      static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), nullptr, nullptr,
+      layout->num_kv_heads, src_dst_pairs, bytes / 16, layout->num_blocks);
+  return launch_status();
+}
+
+// ------------------------------------------------ per-block dynamic scales
+
+extern "C" uint64_t pkv_reshape_dynamic_workspace_bytes(const pkv_cache_layout* layout) {
+  if (check_layout(layout) != PKV_OK || layout->dtype != PKV_FP8_E4M3FN) return 0;
+  const uint64_t words = (uint64_t)layout->num_blocks * (2 * (uint64_t)layout->num_kv_heads + 1);
+  return (words * 4 + 255) / 256 * 256;
+}
+
+extern "C" pkv_status pkv_reshape_and_cache_dynamic(
+    const void* key, const void* value, void* k_pool, void* v_pool, float* k_block_scales,
+    float* v_block_scales, const int64_t* slot_mapping, int32_t num_tokens,
+    const pkv_cache_layout* layout, void* workspace, uint64_t workspace_bytes, void* stream) {
+  pkv_status st = check_layout(layout);
+  if (st != PKV_OK) return st;
+  if (layout->dtype != PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping || !k_block_scales ||
+      !v_block_scales)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 8) || !aligned(k_block_scales, 4) || !aligned(v_block_scales, 4))
+    return PKV_ERR_INVALID_ARG;
+  const uint64_t need = pkv_reshape_dynamic_workspace_bytes(layout);
+  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return PKV_ERR_INVALID_ARG;
+  const int hkv = layout->num_kv_heads;
+  const int64_t total = (int64_t)num_tokens * hkv * 16;
+  const int64_t blocks = (total + 255) / 256;
+  const int64_t clear_total = (int64_t)num_tokens * (2 * hkv + 1);
+  const int64_t clear_blocks = (clear_total + 255) / 256;
+  if (blocks > 0x7FFFFFFF || clear_blocks > 0x7FFFFFFF) return PKV_ERR_INVALID_ARG;
+  const int64_t num_slots = (int64_t)layout->num_blocks * kBS;
+  uint32_t* amax = static_cast<uint32_t*>(workspace);
+  uint32_t* written = amax + (int64_t)layout->num_blocks * 2 * hkv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  dyn_clear_kernel<<<dim3((unsigned)clear_blocks), dim3(256), 0, s>>>(
+      slot_mapping, clear_total, 2 * hkv, num_slots, amax, written);
+  dyn_amax_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+      static_cast<const u32x4*>(key), static_cast<const u32x4*>(value), slot_mapping, total, hkv,
+      num_slots, amax, written);
+  dyn_write_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+      static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
+      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_block_scales,
+      v_block_scales, slot_mapping, total, hkv, num_slots, amax, written);
+  return launch_status();
+}
+
+extern "C" pkv_status pkv_paged_attention_decode_dynamic(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const float* k_block_scales, const float* v_block_scales, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+    int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const pkv_cache_layout* layout, float sm_scale, int32_t partition_size, void* workspace,
+    uint64_t workspace_bytes, void* stream) {
+  if (!k_block_scales || !v_block_scales) return PKV_ERR_INVALID_ARG;
+  DecodePlan pl;
+  pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                              context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
+                              max_context_len, layout, sm_scale, 1.0f, 1.0f, k_block_scales,
+                              v_block_scales, partition_size, workspace, workspace_bytes, true,
+                              &pl);
+  if (st != PKV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_partitions(pl, num_seqs, s);
+  if (st != PKV_OK) return st;
+  return run_reduce(pl, num_seqs, s);
+}
+
+extern "C" pkv_status pkv_copy_blocks_dynamic(void* k_pool, void* v_pool, float* k_block_scales,
+                                              float* v_block_scales,
+                                              const pkv_cache_layout* layout,
+                                              const int32_t* src_dst_pairs, int32_t num_pairs,
+                                              void* stream) {
+  pkv_status st = check_layout(layout);
+  if (st != PKV_OK) return st;
+  if (layout->dtype != PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs < 0) return PKV_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src_dst_pairs || !k_block_scales || !v_block_scales ||
+      !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(src_dst_pairs, 4) ||
+      !aligned(k_block_scales, 4) || !aligned(v_block_scales, 4))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t bytes = (int64_t)layout->num_kv_heads * kBS * kD;
+  (void)hipGetLastError();
+  copy_blocks_kernel<<<dim3((unsigned)num_pairs), dim3(256), 0,
+                       static_cast<hipStream_t>(stream)>>>(
+      static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), k_block_scales, v_block_scales,
+      layout->num_kv_heads, src_dst_pairs, bytes / 16, layout->num_blocks);
   return launch_status();
 }

@@ -118,3 +118,35 @@ def test_host_validation_rejects_before_launch():
                0, 256, 1 << 20, None) == pkv.PKV_ERR_INVALID_ARG
     assert L.pkv_copy_blocks(16, 16, ctypes.byref(ok), 16, -1, None) == pkv.PKV_ERR_INVALID_ARG
     assert L.pkv_copy_blocks(None, None, ctypes.byref(ok), None, 0, None) == pkv.PKV_OK
+
+
+def test_dynamic_scale_entry_points_validate_before_launch():
+    L = pkv.load_library()
+    f8 = pkv.CacheLayout(36864, 8, pkv.PKV_FP8_E4M3FN)
+    f16 = pkv.CacheLayout(16, 2, pkv.PKV_F16)
+    # num_blocks * (2 * Hkv + 1) words, rounded up to 256 bytes
+    assert pkv.pkv_reshape_dynamic_workspace_bytes(f8) == (36864 * 17 * 4 + 255) // 256 * 256
+    assert pkv.pkv_reshape_dynamic_workspace_bytes(f16) == 0
+    w = L.pkv_reshape_and_cache_dynamic
+    assert w(16, 16, 16, 16, 16, 16, 16, 1, ctypes.byref(f16), 256, 1 << 30,
+             None) == pkv.PKV_ERR_UNSUPPORTED
+    assert w(None, None, None, None, None, None, None, 0, ctypes.byref(f8), None, 0,
+             None) == pkv.PKV_OK
+    assert w(16, 16, 16, 16, None, 16, 16, 1, ctypes.byref(f8), 256, 1 << 30,
+             None) == pkv.PKV_ERR_INVALID_ARG
+    assert w(16, 16, 16, 16, 16, 16, 16, 1, ctypes.byref(f8), 256, 1024,
+             None) == pkv.PKV_ERR_WORKSPACE
+    assert w(16, 16, 16, 16, 16, 16, 16, 1, ctypes.byref(f8), 128, 1 << 30,
+             None) == pkv.PKV_ERR_INVALID_ARG          # workspace not 256-byte aligned
+    d = L.pkv_paged_attention_decode_dynamic
+    small8 = pkv.CacheLayout(16, 2, pkv.PKV_FP8_E4M3FN)
+    assert d(16, 16, 16, 16, 16, 16, 16, 4, 16, None, 2, 4, 64, ctypes.byref(f16), 0.1, 0, 256,
+             1 << 20, None) == pkv.PKV_ERR_UNSUPPORTED
+    assert d(16, 16, 16, 16, None, 16, 16, 4, 16, None, 2, 4, 64, ctypes.byref(small8), 0.1, 0,
+             256, 1 << 20, None) == pkv.PKV_ERR_INVALID_ARG
+    assert d(16, 16, 16, 16, 16, 16, 16, 4, 16, None, 2, 4, 64, ctypes.byref(small8), 0.1, 32,
+             256, 16, None) == pkv.PKV_ERR_WORKSPACE
+    c = L.pkv_copy_blocks_dynamic
+    assert c(16, 16, 16, 16, ctypes.byref(f16), 16, 1, None) == pkv.PKV_ERR_UNSUPPORTED
+    assert c(16, 16, None, 16, ctypes.byref(small8), 16, 1, None) == pkv.PKV_ERR_INVALID_ARG
+    assert c(None, None, None, None, ctypes.byref(small8), None, 0, None) == pkv.PKV_OK
