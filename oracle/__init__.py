@@ -70,6 +70,9 @@ def _load():
     lib.oracle_paged_attention_decode_dynamic.argtypes = [P] * 7 + [ctypes.c_int, P] + \
         [ctypes.c_int] * 4 + [f32, ctypes.c_int]
     lib.oracle_paged_attention_decode_dynamic.restype = None
+    lib.oracle_paged_prefill_attention.argtypes = [P] * 5 + [ctypes.c_int, P, P] + \
+        [ctypes.c_int] * 5 + [f32, f32, f32, ctypes.c_int]
+    lib.oracle_paged_prefill_attention.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -215,6 +218,30 @@ def paged_attention_decode(q, k_pool: np.ndarray, v_pool: np.ndarray, block_tabl
     _load().oracle_paged_attention_decode(
         _ptr(out), _ptr(qb), _ptr(np.ascontiguousarray(k_pool)), _ptr(np.ascontiguousarray(v_pool)),
         _ptr(bt), bt.shape[1], _ptr(cl), B, Hq, num_kv_heads, D, int(bool(fp8)),
+        float(np.float32(sm_scale)), float(np.float32(k_scale)), float(np.float32(v_scale)),
+        int(threads))
+    return out
+
+
+def paged_prefill_attention(q, k_pool: np.ndarray, v_pool: np.ndarray, block_tables,
+                            context_lens, query_start, num_kv_heads: int, fp8: bool,
+                            sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                            threads: int = 0) -> np.ndarray:
+    """fp64 causal attention of each sequence's last chunk of tokens over the
+    paged cache; q is fp16 [rows][Hq][D] with sequence b's chunk at rows
+    query_start[b] .. query_start[b+1]-1; returns fp64 [rows][Hq][D]."""
+    qb = _f16_bits(q)
+    R, Hq, D = qb.shape
+    assert Hq % num_kv_heads == 0
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    qs = np.ascontiguousarray(np.asarray(query_start, dtype=np.int32))
+    B = cl.shape[0]
+    assert bt.ndim == 2 and bt.shape[0] == B and qs.shape == (B + 1,) and qs[-1] == R
+    out = np.empty((R, Hq, D), dtype=np.float64)
+    _load().oracle_paged_prefill_attention(
+        _ptr(out), _ptr(qb), _ptr(np.ascontiguousarray(k_pool)), _ptr(np.ascontiguousarray(v_pool)),
+        _ptr(bt), bt.shape[1], _ptr(cl), _ptr(qs), B, Hq, num_kv_heads, D, int(bool(fp8)),
         float(np.float32(sm_scale)), float(np.float32(k_scale)), float(np.float32(v_scale)),
         int(threads))
     return out

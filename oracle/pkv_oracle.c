@@ -304,6 +304,78 @@ void oracle_paged_attention_decode_dynamic(double* out, const uint16_t* q, const
              sm_scale, 1.0f, 1.0f, k_bscales, v_bscales, threads);
 }
 
+/* ------------------------------------------------------ chunked prefill */
+
+/* Attention for a chunk of prompt tokens over the paged cache ([FP8-128K]
+ * §5: with chunked prefill a long prompt is cut into packets of tokens that
+ * run between decode steps).  Sequence b's chunk is its last n_b tokens:
+ * rows query_start[b] .. query_start[b+1]-1 of q, whose keys and values are
+ * already in the cache, so the sequence holds L_b = context_lens[b] tokens.
+ * Row i of the chunk sits at position p = L_b - n_b + i and attends, causally,
+ * to the tokens 0..p of its sequence, with each KV head serving G = Hq / Hkv
+ * query heads.  Plain softmax(sm_scale * q.k) v in fp64, tokens in order. */
+void oracle_paged_prefill_attention(double* out, const uint16_t* q, const uint8_t* k_pool,
+                                    const uint8_t* v_pool, const int32_t* block_tables,
+                                    int max_blocks, const int32_t* context_lens,
+                                    const int32_t* query_start, int B, int Hq, int Hkv, int D,
+                                    int fp8, float sm_scale, float k_scale, float v_scale,
+                                    int threads) {
+  int G = Hq / Hkv;
+  double kfac = fp8 ? (double)k_scale : 1.0;
+  double vfac = fp8 ? (double)v_scale : 1.0;
+  int64_t rows = query_start[B];
+#ifdef _OPENMP
+  if (threads > 0)
+    omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t rh = 0; rh < rows * Hq; ++rh) {
+    int64_t r = rh / Hq;
+    int h = (int)(rh % Hq), kvh = h / G;
+    int b = 0;
+    while (query_start[b + 1] <= r)
+      ++b;
+    int n = query_start[b + 1] - query_start[b];
+    int L = context_lens[b];
+    int64_t pos = (int64_t)L - n + (r - query_start[b]);
+    double* o = out + rh * D;
+    for (int d = 0; d < D; ++d)
+      o[d] = 0.0;
+    if (pos < 0)
+      continue; /* a chunk longer than its sequence: such rows see nothing */
+    const int32_t* row = block_tables + (int64_t)b * max_blocks;
+    int64_t cnt = pos + 1;
+    double* qd = (double*)malloc(sizeof(double) * D);
+    double* sc = (double*)malloc(sizeof(double) * cnt);
+    for (int d = 0; d < D; ++d)
+      qd[d] = oracle_f16_to_double(q[rh * D + d]);
+    double m = -INFINITY;
+    for (int64_t t = 0; t < cnt; ++t) {
+      int64_t block = row[t / ORC_BS];
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d)
+        dot += qd[d] * orc_load(k_pool, 0, block, kvh, (int)(t % ORC_BS), d, Hkv, D, fp8, kfac);
+      sc[t] = (double)sm_scale * dot;
+      if (sc[t] > m)
+        m = sc[t];
+    }
+    double wsum = 0.0;
+    for (int64_t t = 0; t < cnt; ++t) {
+      int64_t blk = row[t / ORC_BS];
+      double w = exp(sc[t] - m);
+      wsum += w;
+      for (int d = 0; d < D; ++d)
+        o[d] += w * orc_load(v_pool, 1, blk, kvh, (int)(t % ORC_BS), d, Hkv, D, fp8, vfac);
+    }
+    for (int d = 0; d < D; ++d)
+      o[d] /= wsum;
+    free(qd);
+    free(sc);
+  }
+}
+
 /* ------------------------------------------------- write with block scales */
 
 /* Store T new K/V rows into an FP8 pool whose (block, kv head) tiles carry

@@ -1,7 +1,8 @@
 """The oracle's pins are strong enough: plant a plausible mistake in a copy of
 the oracle source (on the CPU), rebuild it, and check that at least one pin
 fails for every mistake.  The pins run here are the ones in
-test_oracle_fp8.py, test_oracle_attention.py and test_oracle_dynamic.py."""
+test_oracle_fp8.py, test_oracle_attention.py, test_oracle_dynamic.py and
+test_oracle_prefill.py."""
 import os
 import subprocess
 import sys
@@ -12,6 +13,7 @@ import oracle
 from conftest import ROOT
 import test_oracle_attention as ta
 import test_oracle_dynamic as tdy
+import test_oracle_prefill as tpf
 import test_oracle_fp8 as tf
 
 SRC = os.path.join(ROOT, "oracle", "pkv_oracle.c")
@@ -56,6 +58,13 @@ MUTATIONS = [
     ("K MaxAbs taken from V", "if (xk > ak[0])\n          ak[0] = xk;",
      "if (xv > ak[0])\n          ak[0] = xv;"),
     ("new scale not stored", "        *stored = s;\n", ""),
+    # chunked prefill
+    ("prefill row does not see itself", "int64_t cnt = pos + 1;", "int64_t cnt = pos;"),
+    ("prefill position off by one", "int64_t pos = (int64_t)L - n + (r - query_start[b]);",
+     "int64_t pos = (int64_t)L - n + (r - query_start[b]) - 1;"),
+    ("prefill GQA mapping", "kvh = h / G;", "kvh = h % Hkv;"),
+    ("prefill drops the V scale", "double vfac = fp8 ? (double)v_scale : 1.0;", "double vfac = 1.0;"),
+    ("prefill normaliser squared", "wsum += w;", "wsum += w * w;"),
 ]
 
 
@@ -80,6 +89,8 @@ def _pins(orc):
         ("dyn fresh", lambda: tdy.test_offset_zero_starts_a_fresh_block(orc)),
         ("dyn floor", lambda: tdy.test_zero_rows_get_the_floor_scale_and_non_finite_values_are_not_measured(orc)),
         ("dyn sdpa", lambda: tdy.test_decode_with_block_scales_matches_library_sdpa(orc, 8, 2)),
+        ("prefill sdpa fp8", lambda: tpf.test_prefill_matches_library_sdpa_with_causal_mask(orc, True, 8, 2)),
+        ("prefill causality", lambda: tpf.test_future_tokens_do_not_leak(orc)),
     ]
     for name, fn in checks:
         try:
