@@ -108,6 +108,146 @@ def build_sequences(pkv, wl):
             np.asarray(step_slots, dtype=np.int64), host_us)
 
 
+MFMA_F16_PEAK_TFS = 2500.0    # MI355X dense fp16 matrix peak
+
+
+def run_prefill(args) -> int:
+    """One chunked-prefill step: write the chunk's new K/V rows, then causal
+    attention of the chunk's queries over the whole paged cache.  `value` is
+    algorithmic TFLOP/s (QK^T and PV over every visible token, 4 * D flop per
+    token, query row and head) for the attention plus its write."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_270_amd as pkv
+    from paged_kv_cache_270_amd import workloads
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = workloads.PREFILL_CONFIGS[args.workload]()
+    B, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, workloads.D
+    layout = pkv.CacheLayout(wl.num_blocks, Hkv, pkv.PKV_FP8_E4M3FN if wl.fp8 else pkv.PKV_F16)
+    # the block pool hands out every block: the earlier tokens, then the chunk
+    pool = pkv.BlockPool(wl.num_blocks, shuffle_seed=wl.seed)
+    seqs, early, chunk = [], [], []
+    for L, n in zip(wl.context_lens.tolist(), wl.chunk_lens.tolist()):
+        sid = pool.create()
+        early.extend(pool.append(sid, L - n)[0])
+        chunk.extend(pool.append(sid, n)[0])
+        seqs.append(sid)
+    rows = [pool.block_table(s) for s in seqs]
+    tables = np.zeros((B, max(len(r) for r in rows)), dtype=np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = r
+    Te, Tc = len(early), len(chunk)
+    ks, vs = (0.011, 0.013) if wl.fp8 else (1.0, 1.0)   # N(0,1) rows stay far below 448 * scale
+    k_pool = torch.zeros(pkv.pkv_pool_bytes(layout), dtype=torch.uint8, device=dev)
+    v_pool = torch.zeros_like(k_pool)
+    if Te:
+        pkv.pkv_reshape_and_cache(workloads.randn_f16((Te, Hkv, D), 401, dev),
+                                  workloads.randn_f16((Te, Hkv, D), 402, dev), k_pool, v_pool,
+                                  torch.from_numpy(np.asarray(early, np.int64)).to(dev), layout,
+                                  ks, vs)
+    new_k = workloads.randn_f16((Tc, Hkv, D), 403, dev)
+    new_v = workloads.randn_f16((Tc, Hkv, D), 404, dev)
+    q = workloads.randn_f16((Tc, Hq, D), 405, dev)
+    d_chunk = torch.from_numpy(np.asarray(chunk, np.int64)).to(dev)
+    d_tables = torch.from_numpy(tables).to(dev)
+    d_lens = torch.from_numpy(wl.context_lens).to(dev)
+    d_qs = torch.from_numpy(wl.query_start).to(dev)
+    out = torch.empty((Tc, Hq, D), dtype=torch.float32, device=dev)
+    sm = float(np.float32(1 / np.sqrt(D)))
+    maxq, maxl = int(wl.chunk_lens.max()), int(wl.context_lens.max())
+
+    def step(ev=None):
+        pkv.pkv_reshape_and_cache(new_k, new_v, k_pool, v_pool, d_chunk, layout, ks, vs)
+        if ev is not None:
+            ev[0].record()
+        pkv.pkv_paged_prefill_attention(out, q, k_pool, v_pool, d_tables, d_lens, d_qs, maxq,
+                                        maxl, layout, sm, ks, vs)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(kev[i])
+    torch.cuda.synchronize()
+    attn_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+    flops = wl.flops()
+    value = flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on a bounded sample: a few chunk rows, each as a one-token
+        # chunk over its prefix, on inputs the oracle writes itself
+        import oracle
+        rng = np.random.default_rng(406)
+        S = max(1, args.cpu_sample_seqs // 2)
+        b = B - 1
+        L, n = int(wl.context_lens[b]), int(wl.chunk_lens[b])
+        kh = np.zeros(pkv.pkv_pool_bytes(layout), dtype=np.uint8)
+        vh = np.zeros_like(kh)
+        sl = np.asarray(pool.block_table(seqs[b]), np.int64)
+        pos = np.arange(L)
+        slots = sl[pos // 16] * 16 + pos % 16
+        src = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
+        oracle.reshape_and_cache(src, src, kh, vh, slots, Hkv, wl.fp8, ks, vs)
+        qh = rng.standard_normal((S, Hq, D), dtype=np.float32).astype(np.float16)
+        threads = min(os.cpu_count() or 1, 16)
+        ps = [L - 1 - 97 * i for i in range(S)]
+        t = time.perf_counter()
+        for i, p in enumerate(ps):
+            oracle.paged_prefill_attention(qh[i:i + 1], kh, vh, tables[b:b + 1], [p + 1], [0, 1],
+                                           Hkv, wl.fp8, sm, ks, vs, threads)
+        cpu_s = time.perf_counter() - t
+        sample_flops = sum(p + 1 for p in ps) * Hq * 4 * D
+        cpu = {"value": round(sample_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{S} chunk rows near position {L - 1} of the deepest sequence (all "
+                         f"{Hq} query heads): {cpu_s:.2f} s fp64 on the host"}
+
+    res = {
+        "metric": "chunked-prefill attention TFLOP/s (algorithmic), 70B-layer shape",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "global_batch": B, "chunk_tokens": int(Tc),
+                   "seq_len": maxl, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "block_size": 16, "pool_blocks": wl.num_blocks,
+                   "kv_dtype": "fp8_e4m3fn" if wl.fp8 else "f16",
+                   "arith": "f16 MFMA inputs, f32 accumulate, f16 probabilities",
+                   "parallelism": "single GPU"},
+        "flops_per_step": flops,
+        "prefill_attention_ms": round(attn_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,7 +255,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama70b_fp8",
                     help="llama70b_fp8 (default) | llama70b_fp16 | long_context | "
-                         "shared_prefix | tiny")
+                         "shared_prefix | tiny | prefill_128k | prefill_mixed")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="longest split-KV partition in tokens (default: the workload's "
                          "own, else the library's choice)")
@@ -136,6 +276,10 @@ def main() -> int:
               "(the path shards by sequence or KV head with no exchange; see DESIGN.md)",
               file=sys.stderr)
         return 2
+
+    from paged_kv_cache_270_amd import workloads as _wls
+    if args.workload in _wls.PREFILL_CONFIGS:
+        return run_prefill(args)
 
     import numpy as np
     import torch

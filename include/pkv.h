@@ -221,6 +221,37 @@ pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens, int32_t nu
 pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const pkv_cache_layout* layout,
                            const int32_t* src_dst_pairs, int32_t num_pairs, void* stream);
 
+/* ------------------------------------------------------- chunked prefill
+ *
+ * [FP8-128K] §5: with chunked prefill a long prompt is processed in packets of
+ * tokens between decode steps.  This call is the attention of one packet:
+ * sequence b's chunk is its last n_b = query_start[b+1] - query_start[b]
+ * tokens, whose keys and values the caller has already written into the
+ * cache (pkv_reshape_and_cache), so the sequence holds L_b = context_lens[b]
+ * tokens.  Chunk row i sits at position p = L_b - n_b + i and attends
+ * causally to tokens 0..p:
+ *   out[r][h][:] = softmax_t(sm_scale * q[r][h] . k_t) v_t over t = 0..p,
+ * with k_t, v_t read through block_tables[b] for KV head h / G as in decode.
+ *   out          device fp32 [rows][num_q_heads][128], rows = query_start[B];
+ *   q            device fp16 [rows][num_q_heads][128];
+ *   query_start  device int32 [num_seqs + 1], non-decreasing, query_start[0] =
+ *                0 (empty chunks allowed);
+ *   max_query_len  host upper bound on every n_b (sizes the grid);
+ *   max_context_len  host clamp on every L_b, as in decode;
+ *   other arguments as in pkv_paged_attention_decode (group of at most 16).
+ * Rows whose position is negative (a chunk longer than its sequence) are
+ * written as zeros.  Value slots past L_b may hold anything.  Arithmetic: FP8
+ * codes are converted to fp16 exactly, products on fp16 MFMA with fp32
+ * accumulation, probabilities rounded to fp16.  No workspace. */
+pkv_status pkv_paged_prefill_attention(float* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       const int32_t* query_start, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_query_len,
+                                       int32_t max_context_len, const pkv_cache_layout* layout,
+                                       float sm_scale, float k_scale, float v_scale,
+                                       void* stream);
+
 /* --------------------------------------------- per-block dynamic FP8 scales
  *
  * [FP8-128K] §8, dynamic scaling: instead of one scale per tensor, each

@@ -18,7 +18,7 @@ __all__ = [
     "pkv_decode_partition_size", "pkv_decode_workspace_bytes", "pkv_reshape_and_cache",
     "pkv_paged_attention_decode", "pkv_decode_partitions", "pkv_decode_reduce",
     "pkv_copy_blocks", "pkv_reshape_dynamic_workspace_bytes", "pkv_reshape_and_cache_dynamic",
-    "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic",
+    "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic", "pkv_paged_prefill_attention",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +91,8 @@ def load_library():
         "pkv_paged_attention_decode_dynamic": ([P, P, P, P, P, P, P, i32, P, P, i32, i32, i32,
                                                 LP, f32, i32, P, u64, P], i32),
         "pkv_copy_blocks_dynamic": ([P, P, P, P, LP, P, i32, P], i32),
+        "pkv_paged_prefill_attention": ([P, P, P, P, P, i32, P, P, i32, i32, i32, i32, LP, f32,
+                                         f32, f32, P], i32),
         "pkv_pool_create": ([i32, i32, u64, ctypes.POINTER(P)], i32),
         "pkv_pool_destroy": ([P], None),
         "pkv_pool_num_blocks": ([P], i32),
@@ -276,6 +278,32 @@ def pkv_copy_blocks(k_pool, v_pool, layout: CacheLayout, src_dst_pairs, stream=N
     _check(load_library().pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), ctypes.byref(layout),
                                           _ptr(src_dst_pairs), n, _stream(stream)),
            "pkv_copy_blocks")
+
+
+# ------------------------------------------------------ chunked prefill
+
+def pkv_paged_prefill_attention(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                                max_query_len: int, max_context_len: int, layout: CacheLayout,
+                                sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                                stream=None) -> None:
+    """Causal attention of each sequence's last chunk of tokens (rows
+    query_start[b] .. query_start[b+1]-1 of q) over the paged cache."""
+    import torch
+    _require(out, torch.float32, "out")
+    _require(q, torch.float16, "q")
+    _require(block_tables, torch.int32, "block_tables")
+    _require(context_lens, torch.int32, "context_lens")
+    _require(query_start, torch.int32, "query_start")
+    B = context_lens.numel()
+    if tuple(out.shape) != tuple(q.shape) or q.dim() != 3:
+        raise ValueError("q and out must be [rows][num_q_heads][head_dim]")
+    if query_start.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("query_start must be [B + 1], block_tables [B][max_blocks]")
+    _check(load_library().pkv_paged_prefill_attention(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), _ptr(query_start), B, q.shape[1],
+        max_query_len, max_context_len, ctypes.byref(layout), sm_scale, k_scale, v_scale,
+        _stream(stream)), "pkv_paged_prefill_attention")
 
 
 # ------------------------------------------- per-block dynamic FP8 scales

@@ -1,0 +1,310 @@
+// pkv_prefill.hip — gfx950 kernel for chunked prefill over the paged cache:
+// the queries of a prompt chunk attend causally to every token of their
+// sequence already in the cache ([FP8-128K] "Optimización de KV Cache con
+// PagedAttention y Cuantización FP8 para Contextos Largos (128K)", §5:
+// chunked prefill cuts a long prompt into packets of tokens).
+//
+// Sequence b's chunk is its last n_b tokens (their keys and values are in the
+// cache), so chunk row i sits at position p = L_b - n_b + i and attends to
+// tokens 0..p.
+//
+// Unlike decode this is a dense contraction: each K/V tile meets 16 query
+// tokens x G heads, so the work is bound by the matrix cores, not by HBM.
+// Design for CDNA4:
+//   * a workgroup owns 16 consecutive chunk tokens and one KV head; its
+//     ceil(G/2) waves take two query heads each, so a K/V tile loaded once
+//     per wave (the waves of a workgroup share it through L1) feeds 32 query
+//     rows per wave and 16 x G per workgroup;
+//   * tiles go in pairs (32 tokens): S^T = K Q^T by four 16x16x32 fp16 MFMAs
+//     per tile and head, and O^T += V^T P^T by eight 16x16x32 MFMAs per pair
+//     and head -- the S^T accumulators of the two tiles, taken as fp16, are
+//     exactly the B operand of the second product (contraction order: this
+//     lane's four tokens of the first tile, then its four of the second);
+//   * FP8 tiles are converted to fp16 in registers (exact), probabilities are
+//     fp16, accumulation fp32; the online softmax keeps a lazy reference max
+//     per query row, as the decode kernel does;
+//   * only the pairs that reach past the workgroup's first position apply
+//     the causal mask; value slots past the sequence's end are zeroed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "pkv.h"
+#include "pkv_tile.h"
+
+namespace {
+
+using namespace pkv_dev;
+
+constexpr int kQT = 16;       // chunk tokens per workgroup
+constexpr int kHeadsPerWave = 2;
+
+struct PrefillArgs {
+  float* out;                   // [rows][Hq][D]
+  const _Float16* q;            // [rows][Hq][D]
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* context_lens;  // [B]
+  const int32_t* query_start;   // [B + 1]
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t hq, hkv, g;
+  int32_t max_ctx;
+  float qk_scale;               // sm_scale * k_scale * log2(e)
+  float out_scale;              // v_scale
+};
+
+struct RowState {
+  float m_ref;   // reference max of the row (log2 units), equal on its 4 lanes
+  float l;       // this lane's share of the normaliser
+  f32x4 acc[8];  // O^T rows 16n + 4qg .. +3
+};
+
+template <bool kFP8>
+__device__ __forceinline__ f16x8 k_operand(const TileRegs<kFP8>& t, int m) {
+  if constexpr (kFP8) {
+    const u32x4 raw = t.k[m >> 1];
+    const f16x4 lo = dequant4<true>((m & 1) ? raw.z : raw.x);
+    const f16x4 hi = dequant4<true>((m & 1) ? raw.w : raw.y);
+    return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    return __builtin_bit_cast(f16x8, t.k[m]);
+  }
+}
+
+// The four tokens 4qg..4qg+3 of channel 16n + (lane % 16) in one tile.
+template <bool kFP8>
+__device__ __forceinline__ f16x4 v_quad(const TileRegs<kFP8>& t, int n) {
+  if constexpr (kFP8) {
+    return dequant4<true>(t.v[n >> 2][n & 3]);
+  } else {
+    const u32x4 raw = t.v[n >> 1];
+    u32x2 two;
+    two.x = raw[(n & 1) * 2];
+    two.y = raw[(n & 1) * 2 + 1];
+    return __builtin_bit_cast(f16x4, two);
+  }
+}
+
+// One pair of tiles (tokens tb .. tb+31) for the wave's query heads.
+// pos_j: position of this lane's query row; masked: the pair reaches past
+// the workgroup's first position, so tokens after pos_j are dropped.
+template <bool kFP8>
+__device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb_,
+                                             const f16x8 (&qop)[kHeadsPerWave][4],
+                                             RowState (&st)[kHeadsPerWave], int tb, int qg,
+                                             int pos_j, int L, bool masked, float qk_scale) {
+  if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
+    mask_tail_values<kFP8>(ta, tb, qg, L);
+    mask_tail_values<kFP8>(tb_, tb + kBS, qg, L);
+  }
+  f32x4 s[kHeadsPerWave][2];
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) s[h][0] = s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const f16x8 ka = k_operand<kFP8>(ta, m);
+    const f16x8 kb = k_operand<kFP8>(tb_, m);
+#pragma unroll
+    for (int h = 0; h < kHeadsPerWave; ++h) {
+      s[h][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[h][m], s[h][0], 0, 0, 0);
+      s[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qop[h][m], s[h][1], 0, 0, 0);
+    }
+  }
+  f16x8 p[kHeadsPerWave];
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    float sv[8];
+    bool over = false;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int tok = tb + (r >> 2) * kBS + qg * 4 + (r & 3);
+      const float x = s[h][r >> 2][r & 3] * qk_scale;
+      sv[r] = (!masked || tok <= pos_j) ? x : -INFINITY;
+      over |= sv[r] - st[h].m_ref > kLazyMaxSlack;
+    }
+    if (__any(over)) {  // wave-uniform: re-reduce the row maxima and rescale
+      float bm = sv[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) bm = fmaxf(bm, sv[r]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+      const float m_new = fmaxf(st[h].m_ref, bm);
+      const float alpha = __builtin_amdgcn_exp2f(st[h].m_ref - m_new);
+      st[h].l *= alpha;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st[h].acc[n] *= alpha;
+      st[h].m_ref = m_new;
+    }
+    float lsum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      p[h][r] = (_Float16)__builtin_amdgcn_exp2f(sv[r] - st[h].m_ref);
+      lsum += (float)p[h][r];  // the normaliser sums the fp16 weights the product uses
+    }
+    st[h].l += lsum;
+  }
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const f16x4 va = v_quad<kFP8>(ta, n);
+    const f16x4 vb = v_quad<kFP8>(tb_, n);
+    const f16x8 v = f16x8{va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+#pragma unroll
+    for (int h = 0; h < kHeadsPerWave; ++h)
+      st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
+  }
+}
+
+template <bool kFP8>
+__device__ __forceinline__ void zero_tile(TileRegs<kFP8>& t) {
+#pragma unroll
+  for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+    t.k[i] = u32x4{0, 0, 0, 0};
+    t.v[i] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// Grid (ceil(max chunk / 16), Hkv, B); ceil(G / 2) waves per workgroup.
+// Lane (j = lane % 16, qg = lane / 16) serves chunk row 16 * blockIdx.x + j of
+// the wave's two query heads.
+template <bool kFP8>
+__global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int j = lane & 15, qg = lane >> 4;
+  const int qt = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int q0 = a.query_start[b];
+  const int n = a.query_start[b + 1] - q0;
+  if (qt * kQT >= n) return;
+  int L = a.context_lens[b];
+  const int cap = min(a.max_ctx, a.max_blocks * kBS);
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int i = qt * kQT + j;             // this lane's chunk row
+  const bool row_ok = i < n;
+  const int pos = L - n + i;              // its position; < 0 sees nothing
+  const int first = L - n + qt * kQT;     // the workgroup's first position
+  const int last = L - n + min(qt * kQT + kQT - 1, n - 1);
+  const int h0 = kvh * a.g + w * kHeadsPerWave;
+
+  f16x8 qop[kHeadsPerWave][4];
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    const bool ok = row_ok && pos >= 0 && w * kHeadsPerWave + h < a.g;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int d0 = kFP8 ? (m >> 1) * 64 + qg * 16 + (m & 1) * 8 : m * 32 + qg * 8;
+      qop[h][m] = ok ? *reinterpret_cast<const f16x8*>(
+                           a.q + ((int64_t)(q0 + i) * a.hq + h0 + h) * kD + d0)
+                     : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  RowState st[kHeadsPerWave];
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    st[h].m_ref = -INFINITY;
+    st[h].l = 0.0f;
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) st[h].acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // rows before the sequence (a chunk longer than it) attend to nothing and
+  // rows past the chunk are not written; every row computed sees token 0, so
+  // its max is finite
+  const int pos_c = pos < 0 ? 0 : (pos > L - 1 ? L - 1 : pos);
+  const int ntiles = last >= 0 ? last / kBS + 1 : 0;
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
+  for (int c0 = 0; c0 < ntiles; c0 += kWave) {
+    const int cnt = min(kWave, ntiles - c0);
+    const int tbl = lane < cnt ? trow[c0 + lane] : -1;  // lane i: tile c0 + i
+    for (int t = 0; t < cnt; t += 2) {
+      TileRegs<kFP8> ta, tb;
+      load_tile<kFP8>(ta, a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                      __builtin_amdgcn_readlane(tbl, t), kvh, lane, true);
+      if (t + 1 < cnt)
+        load_tile<kFP8>(tb, a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                        __builtin_amdgcn_readlane(tbl, t + 1), kvh, lane, true);
+      else
+        zero_tile<kFP8>(tb);                // past the last tile: all masked below
+      const int tok0 = (c0 + t) * kBS;
+      process_pair<kFP8>(ta, tb, qop, st, tok0, qg, pos_c, L, tok0 + 2 * kBS - 1 > first,
+                         a.qk_scale);
+    }
+  }
+
+  if (!row_ok) return;
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    if (w * kHeadsPerWave + h >= a.g) break;
+    float l = st[h].l;
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const float f = pos < 0 ? 0.0f : a.out_scale / l;
+    float* o = a.out + ((int64_t)(q0 + i) * a.hq + h0 + h) * kD;
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn)
+      *reinterpret_cast<f32x4*>(o + nn * 16 + qg * 4) = st[h].acc[nn] * f;
+  }
+}
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_prefill_attention(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* query_start, int32_t num_seqs, int32_t num_q_heads, int32_t max_query_len,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, void* stream) {
+  if (!layout) return PKV_ERR_INVALID_ARG;
+  if (layout->block_size != kBS || layout->head_dim != kD ||
+      (layout->dtype != PKV_F16 && layout->dtype != PKV_FP8_E4M3FN))
+    return PKV_ERR_UNSUPPORTED;
+  if (layout->num_blocks <= 0 || layout->num_kv_heads <= 0 || layout->num_kv_heads > 65535)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_seqs > 65535 || num_q_heads <= 0 || max_query_len < 0 ||
+      max_context_len < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % layout->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  const int32_t G = num_q_heads / layout->num_kv_heads;
+  if (G > kMaxG) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return PKV_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0 || !std::isfinite(sm_scale)) return PKV_ERR_INVALID_ARG;
+  const bool fp8 = layout->dtype == PKV_FP8_E4M3FN;
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
+               v_scale > 0.0f))
+    return PKV_ERR_INVALID_ARG;
+  PrefillArgs a;
+  a.out = out;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = layout->num_blocks;
+  a.hq = num_q_heads;
+  a.hkv = layout->num_kv_heads;
+  a.g = G;
+  a.max_ctx = max_context_len;
+  a.qk_scale = sm_scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
+  a.out_scale = fp8 ? v_scale : 1.0f;
+  const int waves = (G + kHeadsPerWave - 1) / kHeadsPerWave;
+  const dim3 grid((unsigned)((max_query_len + kQT - 1) / kQT), (unsigned)layout->num_kv_heads,
+                  (unsigned)num_seqs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (fp8)
+    prefill_kernel<true><<<grid, dim3(waves * kWave), 0, s>>>(a);
+  else
+    prefill_kernel<false><<<grid, dim3(waves * kWave), 0, s>>>(a);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

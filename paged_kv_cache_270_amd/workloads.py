@@ -166,12 +166,81 @@ def shared_prefix(seed: int = 5, groups: int = 32, per_group: int = 8,
                     groups=grp, prefix_blocks=pblocks)
 
 
+@dataclass
+class PrefillWorkload:
+    """A batch of prompt chunks: sequence b holds context_lens[b] tokens in
+    the cache, the last chunk_lens[b] of which are the chunk's queries."""
+    name: str
+    seed: int
+    num_q_heads: int
+    num_kv_heads: int
+    fp8: bool
+    num_blocks: int
+    context_lens: np.ndarray            # int32 [B]
+    chunk_lens: np.ndarray              # int32 [B]
+    block_tables: np.ndarray            # int32 [B][max_blocks]
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def query_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.chunk_lens)]).astype(np.int32)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 1 if self.fp8 else 2
+
+    def flops(self) -> int:
+        """Algorithmic flops: for every chunk row at position p and query head,
+        QK^T and PV over its p + 1 visible tokens, 2 * D flops each."""
+        total = 0
+        for L, n in zip(self.context_lens.astype(np.int64), self.chunk_lens.astype(np.int64)):
+            first = L - n
+            total += n * first + n * (n + 1) // 2     # sum over rows of (p + 1)
+        return int(total) * self.num_q_heads * 4 * D
+
+
+def _prefill(name, seed, lens, chunks, fp8=True):
+    rng = np.random.default_rng(seed)
+    nblk = [-(-int(L) // BS) for L in lens]
+    nb = int(sum(nblk))
+    perm = rng.permutation(nb).astype(np.int32)
+    rows, pos = [], 0
+    for n in nblk:
+        rows.append(perm[pos:pos + n])
+        pos += n
+    return PrefillWorkload(name, seed, 64, 8, fp8, nb, np.asarray(lens, np.int32),
+                           np.asarray(chunks, np.int32), _pad_tables(rows))
+
+
+def prefill_128k(seed: int = 6) -> PrefillWorkload:
+    """The last 8192-token chunk (the page's batched-token budget) of one
+    131072-token prompt: 8192 query rows over 122880 earlier tokens plus the
+    causal triangle; 70B layer shape, FP8 KV, shuffled pool."""
+    return _prefill("prefill-fp8-b1-chunk8192-l131072", seed, [131072], [8192])
+
+
+def prefill_mixed(seed: int = 7) -> PrefillWorkload:
+    """Four prompts' chunks sharing an 8192-token budget (2048 each), at
+    different depths: a first chunk, and chunks ending at 16K, 64K and 128K
+    tokens; FP8 KV."""
+    return _prefill("prefill-fp8-b4-chunk2048-mixed", seed, [2048, 16384, 65536, 131072],
+                    [2048] * 4)
+
+
 CONFIGS = {
     "tiny": tiny,
     "llama70b_fp16": llama70b_fp16,
     "llama70b_fp8": llama70b_fp8,
     "long_context": long_context,
     "shared_prefix": shared_prefix,
+}
+
+PREFILL_CONFIGS = {
+    "prefill_128k": prefill_128k,
+    "prefill_mixed": prefill_mixed,
 }
 
 
