@@ -21,8 +21,9 @@
 //     exactly the B operand of the second product (contraction order: this
 //     lane's four tokens of the first tile, then its four of the second);
 //   * FP8 tiles are converted to fp16 in registers (exact), probabilities are
-//     fp16, accumulation fp32; the online softmax keeps a lazy reference max
-//     per query row, as the decode kernel does;
+//     fp16 (the normaliser sums them in fp32 before rounding), accumulation
+//     fp32; the online softmax keeps a lazy reference max per query row, as
+//     the decode kernel does, tested on each lane's largest logit;
 //   * only the pairs that reach past the workgroup's first position apply
 //     the causal mask; value slots past the sequence's end are zeroed.
 #include <hip/hip_runtime.h>
@@ -63,41 +64,57 @@ struct RowState {
   f32x4 acc[8];  // O^T rows 16n + 4qg .. +3
 };
 
+// Two FP8 codes (the low or high half of a dword) -> two fp16 values, as the
+// 32-bit word an MFMA operand register holds (exact).
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t x) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x, 1.0f, kHi);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 template <bool kFP8>
 __device__ __forceinline__ f16x8 k_operand(const TileRegs<kFP8>& t, int m) {
   if constexpr (kFP8) {
     const u32x4 raw = t.k[m >> 1];
-    const f16x4 lo = dequant4<true>((m & 1) ? raw.z : raw.x);
-    const f16x4 hi = dequant4<true>((m & 1) ? raw.w : raw.y);
-    return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const uint32_t a = (m & 1) ? raw.z : raw.x, b = (m & 1) ? raw.w : raw.y;
+    const u32x4 w = u32x4{fp8x2_to_f16x2<false>(a), fp8x2_to_f16x2<true>(a),
+                          fp8x2_to_f16x2<false>(b), fp8x2_to_f16x2<true>(b)};
+    return __builtin_bit_cast(f16x8, w);
   } else {
     return __builtin_bit_cast(f16x8, t.k[m]);
   }
 }
 
-// The four tokens 4qg..4qg+3 of channel 16n + (lane % 16) in one tile.
+// Channel 16n + (lane % 16), tokens 4qg..4qg+3 of tile a then of tile b: the
+// A operand of the PV product for one pair.
 template <bool kFP8>
-__device__ __forceinline__ f16x4 v_quad(const TileRegs<kFP8>& t, int n) {
+__device__ __forceinline__ f16x8 v_operand(const TileRegs<kFP8>& ta, const TileRegs<kFP8>& tb,
+                                           int n) {
   if constexpr (kFP8) {
-    return dequant4<true>(t.v[n >> 2][n & 3]);
+    const uint32_t a = ta.v[n >> 2][n & 3], b = tb.v[n >> 2][n & 3];
+    const u32x4 w = u32x4{fp8x2_to_f16x2<false>(a), fp8x2_to_f16x2<true>(a),
+                          fp8x2_to_f16x2<false>(b), fp8x2_to_f16x2<true>(b)};
+    return __builtin_bit_cast(f16x8, w);
   } else {
-    const u32x4 raw = t.v[n >> 1];
-    u32x2 two;
-    two.x = raw[(n & 1) * 2];
-    two.y = raw[(n & 1) * 2 + 1];
-    return __builtin_bit_cast(f16x4, two);
+    const u32x4 ra = ta.v[n >> 1], rb = tb.v[n >> 1];
+    const int o = (n & 1) * 2;
+    return __builtin_bit_cast(f16x8, u32x4{ra[o], ra[o + 1], rb[o], rb[o + 1]});
   }
 }
 
 // One pair of tiles (tokens tb .. tb+31) for the wave's query heads.
-// pos_j: position of this lane's query row; masked: the pair reaches past
-// the workgroup's first position, so tokens after pos_j are dropped.
+// pos_j: position of this lane's query row.  masked: the pair reaches past
+// the workgroup's first position, so tokens after pos_j are dropped.  The
+// logit scale qk_scale is positive, so a row's largest logit is qk_scale
+// times its largest dot product.
 template <bool kFP8>
 __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb_,
                                              const f16x8 (&qop)[kHeadsPerWave][4],
                                              RowState (&st)[kHeadsPerWave], int tb, int qg,
                                              int pos_j, int L, bool masked, float qk_scale) {
   if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
+    __asm__ volatile("" ::: "memory");  // keep this rare path a branch
     mask_tail_values<kFP8>(ta, tb, qg, L);
     mask_tail_values<kFP8>(tb_, tb + kBS, qg, L);
   }
@@ -114,44 +131,55 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
       s[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qop[h][m], s[h][1], 0, 0, 0);
     }
   }
-  f16x8 p[kHeadsPerWave];
-#pragma unroll
-  for (int h = 0; h < kHeadsPerWave; ++h) {
-    float sv[8];
-    bool over = false;
+  if (masked) {  // wave-uniform; only the pairs that reach past the first position
+    __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int tok = tb + (r >> 2) * kBS + qg * 4 + (r & 3);
-      const float x = s[h][r >> 2][r & 3] * qk_scale;
-      sv[r] = (!masked || tok <= pos_j) ? x : -INFINITY;
-      over |= sv[r] - st[h].m_ref > kLazyMaxSlack;
-    }
-    if (__any(over)) {  // wave-uniform: re-reduce the row maxima and rescale
-      float bm = sv[0];
+      if (tok > pos_j) {
 #pragma unroll
-      for (int r = 1; r < 8; ++r) bm = fmaxf(bm, sv[r]);
-      bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-      const float m_new = fmaxf(st[h].m_ref, bm);
-      const float alpha = __builtin_amdgcn_exp2f(st[h].m_ref - m_new);
+        for (int h = 0; h < kHeadsPerWave; ++h) s[h][r >> 2][r & 3] = -INFINITY;
+      }
+    }
+  }
+  f16x8 p[kHeadsPerWave];
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    // exponent of each weight relative to the reference max (log2 units)
+    float y[8];
+    const float neg_m = -st[h].m_ref;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk_scale, neg_m);
+    float ymax = y[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) ymax = fmaxf(ymax, y[r]);
+    if (__any(ymax > kLazyMaxSlack)) {
+      __asm__ volatile("" ::: "memory");  // rare: keep the rescale a branch
+      // the row's new reference: its largest logit so far
+      float top = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) top = fmaxf(top, s[h][r >> 2][r & 3] * qk_scale);
+      top = fmaxf(top, __shfl_xor(top, 16, kWave));
+      top = fmaxf(top, __shfl_xor(top, 32, kWave));
+      const float m_upd = fmaxf(st[h].m_ref, top);
+      const float alpha = __builtin_amdgcn_exp2f(st[h].m_ref - m_upd);
       st[h].l *= alpha;
 #pragma unroll
       for (int n = 0; n < 8; ++n) st[h].acc[n] *= alpha;
-      st[h].m_ref = m_new;
-    }
-    float lsum = 0.0f;
+      st[h].m_ref = m_upd;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      p[h][r] = (_Float16)__builtin_amdgcn_exp2f(sv[r] - st[h].m_ref);
-      lsum += (float)p[h][r];  // the normaliser sums the fp16 weights the product uses
+      for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk_scale, -m_upd);
     }
-    st[h].l += lsum;
+    float e[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(y[r]);
+    st[h].l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
   }
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    const f16x4 va = v_quad<kFP8>(ta, n);
-    const f16x4 vb = v_quad<kFP8>(tb_, n);
-    const f16x8 v = f16x8{va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+    const f16x8 v = v_operand<kFP8>(ta, tb_, n);
 #pragma unroll
     for (int h = 0; h < kHeadsPerWave; ++h)
       st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
@@ -164,6 +192,35 @@ __device__ __forceinline__ void zero_tile(TileRegs<kFP8>& t) {
   for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
     t.k[i] = u32x4{0, 0, 0, 0};
     t.v[i] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// Both tiles of a pair.  Table entries outside the pool read as zeros (the
+// uncommon case takes a branch, so the common path has no zeroing moves).
+template <bool kFP8>
+__device__ __forceinline__ void load_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb,
+                                          const PrefillArgs& a, int pa, int pb, int kvh,
+                                          int lane) {
+  constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
+  const bool oka = (unsigned)pa < (unsigned)a.num_blocks;
+  const bool okb = (unsigned)pb < (unsigned)a.num_blocks;
+  const int64_t oa = ((int64_t)(oka ? pa : 0) * a.hkv + kvh) * kTileBytes;
+  const int64_t ob = ((int64_t)(okb ? pb : 0) * a.hkv + kvh) * kTileBytes;
+  const u32x4* ka = reinterpret_cast<const u32x4*>(a.k_pool + oa) + lane;
+  const u32x4* va = reinterpret_cast<const u32x4*>(a.v_pool + oa) + lane;
+  const u32x4* kb = reinterpret_cast<const u32x4*>(a.k_pool + ob) + lane;
+  const u32x4* vb = reinterpret_cast<const u32x4*>(a.v_pool + ob) + lane;
+#pragma unroll
+  for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+    ta.k[i] = ka[i * kWave];
+    ta.v[i] = va[i * kWave];
+    tb.k[i] = kb[i * kWave];
+    tb.v[i] = vb[i * kWave];
+  }
+  if (!oka || !okb) {
+    __asm__ volatile("" ::: "memory");
+    if (!oka) zero_tile<kFP8>(ta);
+    if (!okb) zero_tile<kFP8>(tb);
   }
 }
 
@@ -219,18 +276,49 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
   for (int c0 = 0; c0 < ntiles; c0 += kWave) {
     const int cnt = min(kWave, ntiles - c0);
     const int tbl = lane < cnt ? trow[c0 + lane] : -1;  // lane i: tile c0 + i
-    for (int t = 0; t < cnt; t += 2) {
-      TileRegs<kFP8> ta, tb;
-      load_tile<kFP8>(ta, a.k_pool, a.v_pool, a.num_blocks, a.hkv,
-                      __builtin_amdgcn_readlane(tbl, t), kvh, lane, true);
-      if (t + 1 < cnt)
-        load_tile<kFP8>(tb, a.k_pool, a.v_pool, a.num_blocks, a.hkv,
-                        __builtin_amdgcn_readlane(tbl, t + 1), kvh, lane, true);
-      else
-        zero_tile<kFP8>(tb);                // past the last tile: all masked below
-      const int tok0 = (c0 + t) * kBS;
-      process_pair<kFP8>(ta, tb, qop, st, tok0, qg, pos_c, L, tok0 + 2 * kBS - 1 > first,
-                         a.qk_scale);
+    if constexpr (!kFP8) {  // fp16 tiles are twice the registers: one pair at a time
+      for (int t = 0; t < cnt; t += 2) {
+        TileRegs<kFP8> ta, tb;
+        const int pa = __builtin_amdgcn_readlane(tbl, t);
+        const int pb = t + 1 < cnt ? __builtin_amdgcn_readlane(tbl, t + 1) : pa;
+        load_pair<kFP8>(ta, tb, a, pa, pb, kvh, lane);
+        if (t + 1 >= cnt) {                 // past the last tile: all masked below
+          __asm__ volatile("" ::: "memory");
+          zero_tile<kFP8>(tb);
+        }
+        const int tok0 = (c0 + t) * kBS;
+        process_pair<kFP8>(ta, tb, qop, st, tok0, qg, pos_c, L, tok0 + 2 * kBS - 1 > first,
+                           a.qk_scale);
+      }
+      continue;
+    }
+    // FP8: two pairs in flight, the next pair's loads issued before the
+    // current pair is computed
+    TileRegs<kFP8> buf[2][2];
+    {
+      const int pa = __builtin_amdgcn_readlane(tbl, 0);
+      const int pb = cnt > 1 ? __builtin_amdgcn_readlane(tbl, 1) : pa;
+      load_pair<kFP8>(buf[0][0], buf[0][1], a, pa, pb, kvh, lane);
+    }
+    for (int t = 0; t < cnt; t += 4) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tt = t + 2 * u;
+        if (tt < cnt) {
+          if (tt + 2 < cnt) {
+            const int pa = __builtin_amdgcn_readlane(tbl, tt + 2);
+            const int pb = tt + 3 < cnt ? __builtin_amdgcn_readlane(tbl, tt + 3) : pa;
+            load_pair<kFP8>(buf[u ^ 1][0], buf[u ^ 1][1], a, pa, pb, kvh, lane);
+          }
+          if (tt + 1 >= cnt) {              // past the last tile: all masked below
+            __asm__ volatile("" ::: "memory");
+            zero_tile<kFP8>(buf[u][1]);
+          }
+          const int tok0 = (c0 + tt) * kBS;
+          process_pair<kFP8>(buf[u][0], buf[u][1], qop, st, tok0, qg, pos_c, L,
+                             tok0 + 2 * kBS - 1 > first, a.qk_scale);
+        }
+      }
     }
   }
 
@@ -276,7 +364,8 @@ extern "C" pkv_status pkv_paged_prefill_attention(
     return PKV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
     return PKV_ERR_INVALID_ARG;
-  if (max_blocks_per_seq <= 0 || !std::isfinite(sm_scale)) return PKV_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return PKV_ERR_INVALID_ARG;
   const bool fp8 = layout->dtype == PKV_FP8_E4M3FN;
   if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
                v_scale > 0.0f))
