@@ -25,7 +25,9 @@
 //     fp32; the online softmax keeps a lazy reference max per query row, as
 //     the decode kernel does, tested on each lane's largest logit;
 //   * only the pairs that reach past the workgroup's first position apply
-//     the causal mask; value slots past the sequence's end are zeroed.
+//     the causal mask; value slots past the sequence's end are zeroed;
+//   * the matrix bursts of a wave run at raised priority (s_setprio), so the
+//     two waves of a SIMD tend to alternate matrix and vector phases.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -119,6 +121,9 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
     mask_tail_values<kFP8>(tb_, tb + kBS, qg, L);
   }
   f32x4 s[kHeadsPerWave][2];
+  // matrix bursts run at raised priority, so the SIMD's other wave does its
+  // vector work meanwhile instead of both reaching their softmax together
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int h = 0; h < kHeadsPerWave; ++h) s[h][0] = s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -131,6 +136,7 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
       s[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qop[h][m], s[h][1], 0, 0, 0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   if (masked) {  // wave-uniform; only the pairs that reach past the first position
     __asm__ volatile("" ::: "memory");
 #pragma unroll
@@ -177,6 +183,7 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
 #pragma unroll
     for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
   }
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const f16x8 v = v_operand<kFP8>(ta, tb_, n);
@@ -184,6 +191,7 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
     for (int h = 0; h < kHeadsPerWave; ++h)
       st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <bool kFP8>
