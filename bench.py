@@ -35,24 +35,31 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "KV GB/s read (% of HBM peak) + decode seqs·tok/s, 70B-layer shape, FP8 KV"
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_270_amd", "csrc", "pkv_kernels.hip")
+CSRC = os.path.join(ROOT, "paged_kv_cache_270_amd", "csrc")
+# the sources each measured kernel is built from
+DECODE_SRCS = ("pkv_kernels.hip", "pkv_tile.h")
+PREFILL_SRCS = ("pkv_prefill.hip", "pkv_tile.h")
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_sha(sources=DECODE_SRCS) -> str:
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the partition kernel from committed rocprofv3
-    counter runs for this workload, if taken on the current kernel source."""
+def measured_traffic(key: str, sources=DECODE_SRCS):
+    """HBM bytes per launch of the measured kernel from committed rocprofv3
+    counter runs (profiles/traffic_<key>.json), if taken on the current
+    kernel sources."""
     try:
-        with open(os.path.join(TRAFFIC_DIR, f"traffic_decode_partition_{workload}.json")) as f:
+        with open(os.path.join(TRAFFIC_DIR, f"traffic_{key}.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_sha():
+    if t.get("kernel_source_sha256") != kernel_source_sha(sources):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -241,7 +248,7 @@ def run_prefill(args) -> int:
         "prefill_attention_ms": round(attn_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("prefill_" + args.workload, PREFILL_SRCS)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -486,8 +493,8 @@ def main() -> int:
         "bulk_fill_gbs": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload + ("_block_scales" if dyn
-                                                                 else ""))},
+                     "traffic": measured_traffic("decode_partition_" + args.workload +
+                                                 ("_block_scales" if dyn else ""))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
