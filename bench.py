@@ -255,6 +255,99 @@ def run_prefill(args) -> int:
     return 0
 
 
+def run_swap(args) -> int:
+    """Page-granular eviction: a quarter of the 70B-layer FP8 batch's pages
+    (16 sequences x 513 blocks, all KV heads, K and V) go to pinned host
+    memory and come back.  `value` = bytes moved per direction / copy time
+    (GB/s), the mean of the two directions; the pool bookkeeping is timed on
+    the host separately.  A plain DMA copy of the same bytes between pinned
+    host and device memory is timed as the link's ceiling."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_270_amd as pkv
+    from paged_kv_cache_270_amd import workloads
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = workloads.llama70b_fp8()
+    B, Hkv, D, NB = wl.num_seqs, wl.num_kv_heads, workloads.D, wl.num_blocks
+    layout = pkv.CacheLayout(NB, Hkv, pkv.PKV_FP8_E4M3FN)
+    pool, seqs, per_seq, bulk_slots, step_slots, _ = build_sequences(pkv, wl)
+    k_pool = torch.zeros(pkv.pkv_pool_bytes(layout), dtype=torch.uint8, device=dev)
+    v_pool = torch.zeros_like(k_pool)
+    T = int(bulk_slots.size)
+    pkv.pkv_reshape_and_cache(workloads.randn_f16((T, Hkv, D), 301, dev),
+                              workloads.randn_f16((T, Hkv, D), 302, dev), k_pool, v_pool,
+                              torch.from_numpy(bulk_slots).to(dev), layout, 0.011, 0.013)
+    victims = seqs[:16]
+    per_block = Hkv * 16 * D            # bytes of one block per pool (FP8)
+    H = sum(len(pool.block_table(s)) for s in victims)
+    pool.set_swap_space(H)
+    host_k = torch.empty(H * per_block, dtype=torch.uint8, pin_memory=True)
+    host_v = torch.empty(H * per_block, dtype=torch.uint8, pin_memory=True)
+    for s in victims:                    # one untimed round trip warms the pool's lists
+        pool.swap_out(s, 0, len(pool.block_table(s)))
+    for s in victims:
+        pool.swap_in(s)
+    import gc
+    gc.disable()
+    t0 = time.perf_counter()
+    out_pairs = [p for s in victims for p in pool.swap_out(s, 0, len(pool.block_table(s)))]
+    host_out_us = (time.perf_counter() - t0) * 1e6
+    t0 = time.perf_counter()
+    in_pairs = [p for s in victims for p in pool.swap_in(s)]
+    host_in_us = (time.perf_counter() - t0) * 1e6
+    gc.enable()
+    assert len(in_pairs) == len(out_pairs) == H
+    d_out = torch.tensor(out_pairs, dtype=torch.int32, device=dev)
+    # the copies move the same blocks back into the blocks they left (the
+    # pool may choose others; the bytes moved are the same)
+    d_in = torch.tensor([(h, d) for d, h in out_pairs], dtype=torch.int32, device=dev)
+    moved = 2 * H * per_block            # K and V
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    d2h_ms = timed(lambda: pkv.pkv_swap_blocks(k_pool, v_pool, host_k, host_v, H, layout, d_out,
+                                               to_host=True))
+    h2d_ms = timed(lambda: pkv.pkv_swap_blocks(k_pool, v_pool, host_k, host_v, H, layout, d_in,
+                                               to_host=False))
+    dma_src = torch.empty(moved, dtype=torch.uint8, device=dev)
+    dma_host = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+    dma_d2h = timed(lambda: dma_host.copy_(dma_src, non_blocking=True))
+    dma_h2d = timed(lambda: dma_src.copy_(dma_host, non_blocking=True))
+    d2h, h2d = moved / (d2h_ms * 1e-3) / 1e9, moved / (h2d_ms * 1e-3) / 1e9
+    ceiling = max(moved / (dma_d2h * 1e-3) / 1e9, moved / (dma_h2d * 1e-3) / 1e9)
+    value = (d2h + h2d) / 2
+    res = {
+        "metric": "KV page swap GB/s per direction (device <-> pinned host), 70B-layer FP8 pages",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(d2h_ms + h2d_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": "swap-fp8-16x513-blocks", "blocks": H, "bytes_per_direction": moved,
+                   "kv_dtype": "fp8_e4m3fn", "parallelism": "single GPU"},
+        "device_to_host_gbs": round(d2h, 2), "host_to_device_gbs": round(h2d, 2),
+        "dma_copy_ceiling_gbs": round(ceiling, 2),
+        "host_bookkeeping_us": {"swap_out": round(host_out_us, 1), "swap_in": round(host_in_us, 1)},
+        "roofline": {"bound": "host-link", "achieved": round(value, 2), "peak": round(ceiling, 2),
+                     "unit": "GB/s", "frac": round(value / ceiling, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,7 +355,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama70b_fp8",
                     help="llama70b_fp8 (default) | llama70b_fp16 | long_context | "
-                         "shared_prefix | tiny | prefill_128k | prefill_mixed")
+                         "shared_prefix | tiny | prefill_128k | prefill_mixed | swap")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="longest split-KV partition in tokens (default: the workload's "
                          "own, else the library's choice)")
@@ -287,6 +380,8 @@ def main() -> int:
     from paged_kv_cache_270_amd import workloads as _wls
     if args.workload in _wls.PREFILL_CONFIGS:
         return run_prefill(args)
+    if args.workload == "swap":
+        return run_swap(args)
 
     import numpy as np
     import torch

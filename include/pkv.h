@@ -412,6 +412,61 @@ pkv_status pkv_prefix_cache_stats(const pkv_pool* pool, int64_t* hit_blocks,
 /* Drop every entry; evictable blocks go to the free list in LRU order. */
 void pkv_prefix_cache_clear(pkv_pool* pool);
 
+/* ------------------------------------------------------------------- swap
+ *
+ * Page-granular eviction ([KV-SLOW] "Cómo PagedAttention soluciona esto":
+ * when the cache is full, small pages move to CPU memory rather than whole
+ * sequences; [GLOSSARY] glossary entry on KV-cache offloading: the cache is
+ * moved temporarily from GPU memory to system RAM).  The pool keeps a swap
+ * space of host slots, each holding one block (every KV head, K and V, in the
+ * pool's tile layout).  A sequence's blocks can be swapped out a run at a
+ * time; a sequence with swapped blocks cannot be decoded, appended to,
+ * forked or registered in the prefix cache until pkv_seq_swap_in brings them
+ * all back (into whatever device blocks are free).  Its block table shows -1
+ * for a swapped block. */
+
+/* Size the swap space: num_host_blocks host slots, handed out in ascending
+ * order.  PKV_ERR_INVALID_ARG while any slot is in use. */
+pkv_status pkv_pool_set_swap_space(pkv_pool* pool, int32_t num_host_blocks);
+/* Free host slots; -1 for a bad handle. */
+int32_t pkv_pool_num_free_host(const pkv_pool* pool);
+/* Blocks of a sequence now in host slots; -1 for an unknown id. */
+int32_t pkv_seq_num_swapped(const pkv_pool* pool, int32_t seq);
+/* Move logical blocks [first_block, first_block + n_blocks) of a sequence to
+ * host slots.  Each must be on the device and held by this sequence alone
+ * (PKV_ERR_REFCOUNT otherwise: a shared page stays for its other holders); a
+ * block's prefix-cache entry is dropped.  The device blocks return to the
+ * free list.  pairs_out: host int32 [n_blocks][2] (device block, host slot),
+ * in logical order, for pkv_swap_blocks(to_host = 1) -- which must run
+ * before the freed blocks are written again.  All or nothing:
+ * PKV_ERR_NO_FREE_BLOCKS when the swap space is short, nothing changed. */
+pkv_status pkv_seq_swap_out(pkv_pool* pool, int32_t seq, int32_t first_block, int32_t n_blocks,
+                            int32_t* pairs_out);
+/* Bring every swapped block of a sequence back into device blocks taken as
+ * an append takes them (free list, then least recently used cache-only
+ * blocks).  *n_out = number of such blocks always; pairs_out: host int32
+ * [cap][2] (host slot, device block), for pkv_swap_blocks(to_host = 0).
+ * PKV_ERR_INVALID_ARG if cap is short, PKV_ERR_NO_FREE_BLOCKS if the device
+ * is: nothing changed in either case. */
+pkv_status pkv_seq_swap_in(pkv_pool* pool, int32_t seq, int32_t* pairs_out, int32_t cap,
+                           int32_t* n_out);
+
+/* Copy blocks between the device pools and the host swap space.
+ *   host_k, host_v  pinned host memory the device can address (hipHostMalloc,
+ *                 or a pinned torch tensor), [num_host_blocks][num_kv_heads]
+ *                 [16 * 128] elements each, the pool's tile layout;
+ *   pairs         device int32 [num_pairs][2]: (device block, host slot) when
+ *                 to_host = 1, (host slot, device block) when to_host = 0;
+ *                 pairs with an id out of range are skipped.
+ * Host buffers the runtime does not know as pinned, device-reachable memory
+ * (hipHostGetDevicePointer fails) give PKV_ERR_INVALID_ARG before any launch.
+ * Bound by the host link, not HBM.  Asynchronous on `stream`: the host copy
+ * is complete once the stream is. */
+pkv_status pkv_swap_blocks(void* k_pool, void* v_pool, void* host_k, void* host_v,
+                           int32_t num_host_blocks, const pkv_cache_layout* layout,
+                           const int32_t* pairs, int32_t num_pairs, int32_t to_host,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

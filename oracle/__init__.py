@@ -301,6 +301,14 @@ class NoFreeBlocks(Exception):
     pass
 
 
+class InvalidArg(Exception):
+    pass
+
+
+class SharedBlock(Exception):
+    """A block other sequences also hold cannot leave the device."""
+
+
 class BlockPoolModel:
     """Plain model of a refcounted block pool (host bookkeeping only).
 
@@ -327,6 +335,18 @@ class BlockPoolModel:
       evictable block whose entry was hit or registered longest ago;
     * registration keeps an entry that already exists for the same prefix and
       stops at the first chunk whose block already serves another prefix.
+
+    Swap space ("KV Cache y PagedAttention: por qué se reduce la velocidad de
+    tu servidor LLM": when memory runs out, single pages go to CPU memory
+    instead of whole sequences):
+
+    * host slots are handed out in ascending order and returned at the back;
+    * a run of a sequence's blocks moves to host slots only if every block is
+      on the device and held by that sequence alone; the device blocks are
+      released (a cached one loses its cache entry);
+    * swapping in takes device blocks as an append would, in logical order;
+    * a sequence with swapped blocks cannot be appended to, forked or
+      registered; its table shows -1 for them.
     """
 
     def __init__(self, free_order, block_size: int = BLOCK_SIZE):
@@ -343,6 +363,8 @@ class BlockPoolModel:
         self._tick = 0
         self.hit_blocks = 0
         self.miss_blocks = 0
+        self.num_host = 0
+        self.host_free = []
 
     def num_free(self) -> int:
         return len(self.free)
@@ -381,8 +403,13 @@ class BlockPoolModel:
         self.seqs[sid] = ([], 0)
         return sid
 
+    def _swapped(self, sid) -> int:
+        return sum(1 for b in self.seqs[sid][0] if isinstance(b, tuple))
+
     def fork(self, parent: int) -> int:
         blocks, n = self.seqs[parent]
+        if self._swapped(parent):
+            raise InvalidArg()
         for b in blocks:
             self.ref[b] += 1
         sid = self.create()
@@ -394,6 +421,8 @@ class BlockPoolModel:
         bs = self.block_size
         if n_tokens == 0:      # nothing is written, so nothing needs copying
             return [], []
+        if self._swapped(sid):
+            raise InvalidArg()
         cow = n % bs != 0 and self.ref[blocks[-1]] > 1
         have = -(-n // bs)
         need = -(-(n + n_tokens) // bs) - have + (1 if cow else 0)
@@ -418,7 +447,10 @@ class BlockPoolModel:
     def free_seq(self, sid: int) -> None:
         blocks, _ = self.seqs.pop(sid)
         for b in blocks:
-            self._release(b)
+            if isinstance(b, tuple):
+                self.host_free.append(b[1])
+            else:
+                self._release(b)
 
     def create_cached(self, tokens):
         """New sequence mapped onto the cached blocks of the leading chunks of
@@ -444,6 +476,8 @@ class BlockPoolModel:
     def cache_prefix(self, sid: int, tokens) -> None:
         """Register the full, filled blocks of `sid` under the prefixes of `tokens`."""
         blocks, n = self.seqs[sid]
+        if self._swapped(sid):
+            raise InvalidArg()
         bs = self.block_size
         for i in range(min(len(tokens), n) // bs):
             pre = tuple(tokens[:bs * (i + 1)])
@@ -468,7 +502,63 @@ class BlockPoolModel:
         self.last_use.clear()
 
     def table(self, sid: int):
-        return list(self.seqs[sid][0])
+        return [-1 if isinstance(b, tuple) else b for b in self.seqs[sid][0]]
+
+    def num_free_host(self) -> int:
+        return len(self.host_free)
+
+    def num_swapped(self, sid: int) -> int:
+        return self._swapped(sid)
+
+    def set_swap_space(self, num_host_blocks: int) -> None:
+        if len(self.host_free) != self.num_host:
+            raise InvalidArg()
+        self.num_host = num_host_blocks
+        self.host_free = list(range(num_host_blocks))
+
+    def swap_out(self, sid: int, first: int, n_blocks: int):
+        blocks, n = self.seqs[sid]
+        if first < 0 or n_blocks < 0 or first + n_blocks > len(blocks):
+            raise InvalidArg()
+        for b in blocks[first:first + n_blocks]:
+            if isinstance(b, tuple):
+                raise InvalidArg()
+            if self.ref[b] != 1:
+                raise SharedBlock()
+        if n_blocks > len(self.host_free):
+            raise NoFreeBlocks()
+        blocks = list(blocks)
+        pairs = []
+        for i in range(first, first + n_blocks):
+            b = blocks[i]
+            slot = self.host_free.pop(0)
+            if b in self.prefix_of:
+                pre = self.prefix_of.pop(b)
+                del self.cache[pre]
+                del self.last_use[pre]
+            self._release(b)
+            blocks[i] = ("h", slot)
+            pairs.append((b, slot))
+        self.seqs[sid] = (blocks, n)
+        return pairs
+
+    def swap_in(self, sid: int):
+        blocks, n = self.seqs[sid]
+        k = self._swapped(sid)
+        if k == 0:
+            return []
+        if k > self.available():
+            raise NoFreeBlocks()
+        blocks = list(blocks)
+        pairs = []
+        for i, b in enumerate(blocks):
+            if isinstance(b, tuple):
+                d = self._take()
+                self.host_free.append(b[1])
+                blocks[i] = d
+                pairs.append((b[1], d))
+        self.seqs[sid] = (blocks, n)
+        return pairs
 
     def length(self, sid: int) -> int:
         return self.seqs[sid][1]

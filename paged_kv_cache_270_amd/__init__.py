@@ -19,6 +19,7 @@ __all__ = [
     "pkv_paged_attention_decode", "pkv_decode_partitions", "pkv_decode_reduce",
     "pkv_copy_blocks", "pkv_reshape_dynamic_workspace_bytes", "pkv_reshape_and_cache_dynamic",
     "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic", "pkv_paged_prefill_attention",
+    "pkv_swap_blocks",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,12 @@ def load_library():
         "pkv_copy_blocks_dynamic": ([P, P, P, P, LP, P, i32, P], i32),
         "pkv_paged_prefill_attention": ([P, P, P, P, P, i32, P, P, i32, i32, i32, i32, LP, f32,
                                          f32, f32, P], i32),
+        "pkv_swap_blocks": ([P, P, P, P, i32, LP, P, i32, i32, P], i32),
+        "pkv_pool_set_swap_space": ([P, i32], i32),
+        "pkv_pool_num_free_host": ([P], i32),
+        "pkv_seq_num_swapped": ([P, i32], i32),
+        "pkv_seq_swap_out": ([P, i32, i32, i32, P], i32),
+        "pkv_seq_swap_in": ([P, i32, P, i32, ctypes.POINTER(i32)], i32),
         "pkv_pool_create": ([i32, i32, u64, ctypes.POINTER(P)], i32),
         "pkv_pool_destroy": ([P], None),
         "pkv_pool_num_blocks": ([P], i32),
@@ -280,6 +287,22 @@ def pkv_copy_blocks(k_pool, v_pool, layout: CacheLayout, src_dst_pairs, stream=N
            "pkv_copy_blocks")
 
 
+# ------------------------------------------------------------------ swap
+
+def pkv_swap_blocks(k_pool, v_pool, host_k, host_v, num_host_blocks: int, layout: CacheLayout,
+                    pairs, to_host: bool, stream=None) -> None:
+    """Copy blocks between the device pools and pinned host buffers."""
+    import torch
+    _require(pairs, torch.int32, "pairs")
+    for t, name in ((host_k, "host_k"), (host_v, "host_v")):
+        if t.is_cuda or not t.is_pinned():
+            raise ValueError(f"{name} must be pinned host memory")
+    _check(load_library().pkv_swap_blocks(
+        _ptr(k_pool), _ptr(v_pool), _ptr(host_k), _ptr(host_v), num_host_blocks,
+        ctypes.byref(layout), _ptr(pairs), pairs.numel() // 2, int(bool(to_host)),
+        _stream(stream)), "pkv_swap_blocks")
+
+
 # ------------------------------------------------------ chunked prefill
 
 def pkv_paged_prefill_attention(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
@@ -450,6 +473,38 @@ class BlockPool:
     def shared_prefix_blocks(self, seq: int) -> int:
         return self._L.pkv_seq_shared_prefix_blocks(self._h, seq)
 
+    # ---- swap space (page-granular eviction to host memory)
+
+    def set_swap_space(self, num_host_blocks: int) -> None:
+        _check(self._L.pkv_pool_set_swap_space(self._h, num_host_blocks),
+               "pkv_pool_set_swap_space")
+
+    def num_free_host(self) -> int:
+        return self._L.pkv_pool_num_free_host(self._h)
+
+    def num_swapped(self, seq: int) -> int:
+        return self._L.pkv_seq_num_swapped(self._h, seq)
+
+    def swap_out(self, seq: int, first_block: int, n_blocks: int):
+        """Returns [(device block, host slot)] in logical order."""
+        buf = (ctypes.c_int32 * max(2, 2 * n_blocks))()
+        _check(self._L.pkv_seq_swap_out(self._h, seq, first_block, n_blocks, buf),
+               "pkv_seq_swap_out")
+        return [(buf[2 * i], buf[2 * i + 1]) for i in range(n_blocks)]
+
+    def swap_in(self, seq: int):
+        """Returns [(host slot, device block)] in logical order."""
+        n = ctypes.c_int32()
+        st = self._L.pkv_seq_swap_in(self._h, seq, None, 0, ctypes.byref(n))
+        if st not in (PKV_OK, PKV_ERR_INVALID_ARG):
+            _check(st, "pkv_seq_swap_in")
+        if n.value == 0:
+            return []
+        buf = (ctypes.c_int32 * (2 * n.value))()
+        _check(self._L.pkv_seq_swap_in(self._h, seq, buf, n.value, ctypes.byref(n)),
+               "pkv_seq_swap_in")
+        return [(buf[2 * i], buf[2 * i + 1]) for i in range(n.value)]
+
     def create_cached(self, tokens):
         """New sequence whose leading cached chunks of `tokens` are mapped onto
         the cached blocks; returns (seq, n_cached_tokens)."""
@@ -480,3 +535,4 @@ class BlockPool:
 def _i32_array(values):
     vals = [int(v) for v in values]
     return (ctypes.c_int32 * max(1, len(vals)))(*vals)
+

@@ -2,7 +2,7 @@
 
     python -m paged_kv_cache_270_amd.build
 
-Compiles csrc/pkv_host.cpp, csrc/pkv_kernels.hip and csrc/pkv_prefill.hip into
+Compiles csrc/pkv_host.cpp and the kernels in csrc/*.hip into
 paged_kv_cache_270_amd/libpkv.so.  Device code is built for gfx950 only, at -O3,
 with packed fp32 instructions disabled (-packed-fp32-ops) and the default
 correctly rounded fp32 division (no fast-math).
@@ -28,7 +28,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", I
 def build(verbose: bool = False) -> str:
     objs = []
     for src, dev in (("pkv_host.cpp", False), ("pkv_kernels.hip", True),
-                     ("pkv_prefill.hip", True)):
+                     ("pkv_prefill.hip", True), ("pkv_swap.hip", True)):
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC] + COMMON + (DEVICE_FLAGS + ["-x", "hip"] if dev else []) + \
               ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -74,10 +74,16 @@ extern "C" uint64_t pkv_pool_bytes(const pkv_cache_layout* l) {
 
 namespace {
 
+// A sequence's logical blocks: a device block id (>= 0), or a block swapped
+// out to host slot k, stored as -(k + 2).
 struct Seq {
   std::vector<int32_t> blocks;
   int64_t len = 0;
+  int32_t swapped = 0;  // blocks now in host slots
 };
+
+inline int32_t host_code(int32_t slot) { return -slot - 2; }
+inline int32_t host_slot(int32_t code) { return -code - 2; }
 
 struct CacheEntry {
   int32_t block;
@@ -118,6 +124,9 @@ struct pkv_pool {
   std::set<std::pair<uint64_t, int32_t>> evictable;  // (tick, block), LRU first
   uint64_t tick = 0;
   int64_t hit_blocks = 0, miss_blocks = 0;
+  // swap space: host slots for swapped-out blocks
+  int32_t num_host = 0;
+  std::deque<int32_t> host_free;
 
   int64_t available() const { return (int64_t)free_list.size() + (int64_t)evictable.size(); }
 
@@ -212,6 +221,7 @@ extern "C" pkv_status pkv_seq_fork(pkv_pool* p, int32_t parent, int32_t* child_o
   if (!child_out) return PKV_ERR_INVALID_ARG;
   auto it = p->seqs.find(parent);
   if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+  if (it->second.swapped) return PKV_ERR_INVALID_ARG;  // swap it in first
   Seq child = it->second;  // same blocks, same length
   for (int32_t b : child.blocks) p->acquire(b);
   int32_t id = p->next_id++;
@@ -231,6 +241,7 @@ extern "C" pkv_status pkv_seq_append(pkv_pool* p, int32_t seq, int32_t n_tokens,
   const int64_t bs = p->block_size;
   if (n_cow_out) *n_cow_out = 0;
   if (n_tokens == 0) return PKV_OK;
+  if (s.swapped) return PKV_ERR_INVALID_ARG;  // swap it in first
   // Writing into a partially filled last block that another sequence also
   // holds would change that sequence's tokens: copy the block first.
   const bool cow = (s.len % bs) != 0 && p->ref[(size_t)s.blocks.back()] > 1;
@@ -262,8 +273,13 @@ extern "C" pkv_status pkv_seq_free(pkv_pool* p, int32_t seq) {
   auto it = p->seqs.find(seq);
   if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
   for (int32_t b : it->second.blocks)
-    if (p->ref[(size_t)b] <= 0) return PKV_ERR_REFCOUNT;  // checked before any change
-  for (int32_t b : it->second.blocks) p->release(b);
+    if (b >= 0 && p->ref[(size_t)b] <= 0) return PKV_ERR_REFCOUNT;  // checked before any change
+  for (int32_t b : it->second.blocks) {
+    if (b >= 0)
+      p->release(b);
+    else
+      p->host_free.push_back(host_slot(b));
+  }
   p->seqs.erase(it);
   return PKV_OK;
 }
@@ -276,7 +292,10 @@ extern "C" pkv_status pkv_seq_block_table(const pkv_pool* p, int32_t seq, int32_
   const int32_t n = (int32_t)it->second.blocks.size();
   if (n_out) *n_out = n;
   if (cap < n || (n > 0 && !out)) return PKV_ERR_INVALID_ARG;
-  if (n > 0) std::memcpy(out, it->second.blocks.data(), sizeof(int32_t) * (size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = it->second.blocks[(size_t)i];
+    out[i] = b >= 0 ? b : -1;  // swapped out: no device block
+  }
   return PKV_OK;
 }
 
@@ -292,7 +311,7 @@ extern "C" int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* p, int32_t seq) 
   if (it == p->seqs.end()) return -1;
   int32_t n = 0;
   for (int32_t b : it->second.blocks) {
-    if (p->ref[(size_t)b] <= 1) break;
+    if (b < 0 || p->ref[(size_t)b] <= 1) break;
     ++n;
   }
   return n;
@@ -341,6 +360,7 @@ extern "C" pkv_status pkv_seq_cache_prefix(pkv_pool* p, int32_t seq, const int32
   auto sit = p->seqs.find(seq);
   if (sit == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
   const Seq& s = sit->second;
+  if (s.swapped) return PKV_ERR_INVALID_ARG;
   const int32_t bs = p->block_size;
   const int64_t chunks = std::min<int64_t>(n_tokens, s.len) / bs;
   uint64_t key = 0;
@@ -381,4 +401,84 @@ extern "C" void pkv_prefix_cache_clear(pkv_pool* p) {
   p->evictable.clear();
   for (const auto& kv : p->cache) p->cache_key[(size_t)kv.second.block] = 0;
   p->cache.clear();
+}
+
+// ------------------------------------------------------------------- swap
+
+extern "C" pkv_status pkv_pool_set_swap_space(pkv_pool* p, int32_t num_host_blocks) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (num_host_blocks < 0) return PKV_ERR_INVALID_ARG;
+  if ((int32_t)p->host_free.size() != p->num_host) return PKV_ERR_INVALID_ARG;  // slots in use
+  p->num_host = num_host_blocks;
+  p->host_free.clear();
+  for (int32_t i = 0; i < num_host_blocks; ++i) p->host_free.push_back(i);
+  return PKV_OK;
+}
+
+extern "C" int32_t pkv_pool_num_free_host(const pkv_pool* p) {
+  return p ? (int32_t)p->host_free.size() : -1;
+}
+
+extern "C" int32_t pkv_seq_num_swapped(const pkv_pool* p, int32_t seq) {
+  if (!p) return -1;
+  auto it = p->seqs.find(seq);
+  return it == p->seqs.end() ? -1 : it->second.swapped;
+}
+
+extern "C" pkv_status pkv_seq_swap_out(pkv_pool* p, int32_t seq, int32_t first_block,
+                                       int32_t n_blocks, int32_t* pairs_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+  Seq& s = it->second;
+  if (n_blocks < 0 || first_block < 0 || (n_blocks > 0 && !pairs_out) ||
+      (int64_t)first_block + n_blocks > (int64_t)s.blocks.size())
+    return PKV_ERR_INVALID_ARG;
+  for (int32_t i = first_block; i < first_block + n_blocks; ++i) {  // all checked first
+    const int32_t b = s.blocks[(size_t)i];
+    if (b < 0) return PKV_ERR_INVALID_ARG;             // already swapped out
+    if (p->ref[(size_t)b] != 1) return PKV_ERR_REFCOUNT;  // shared: not this sequence's alone
+  }
+  if (n_blocks > (int32_t)p->host_free.size()) return PKV_ERR_NO_FREE_BLOCKS;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    int32_t& e = s.blocks[(size_t)(first_block + i)];
+    const int32_t b = e;
+    const int32_t slot = p->host_free.front();
+    p->host_free.pop_front();
+    if (p->cache_key[(size_t)b] != 0) {  // its prefix-cache entry leaves with it
+      p->cache.erase(p->cache_key[(size_t)b]);
+      p->cache_key[(size_t)b] = 0;
+    }
+    p->release(b);
+    e = host_code(slot);
+    pairs_out[2 * i] = b;
+    pairs_out[2 * i + 1] = slot;
+  }
+  s.swapped += n_blocks;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_swap_in(pkv_pool* p, int32_t seq, int32_t* pairs_out, int32_t cap,
+                                      int32_t* n_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+  Seq& s = it->second;
+  if (n_out) *n_out = s.swapped;
+  if (s.swapped == 0) return PKV_OK;
+  if (cap < s.swapped || !pairs_out) return PKV_ERR_INVALID_ARG;
+  if (s.swapped > p->available()) return PKV_ERR_NO_FREE_BLOCKS;  // nothing changed
+  int32_t k = 0;
+  for (int32_t& e : s.blocks) {
+    if (e >= 0) continue;
+    const int32_t slot = host_slot(e);
+    const int32_t b = p->take();
+    p->host_free.push_back(slot);
+    e = b;
+    pairs_out[2 * k] = slot;
+    pairs_out[2 * k + 1] = b;
+    ++k;
+  }
+  s.swapped = 0;
+  return PKV_OK;
 }
