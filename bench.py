@@ -365,6 +365,9 @@ def main() -> int:
     ap.add_argument("--cpu-sample-seqs", type=int, default=8,
                     help="sequences of the workload the CPU oracle baseline decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the decode step as one captured HIP graph instead of "
+                         "launching its kernels one by one")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
@@ -495,8 +498,17 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
+    # optionally the step as one HIP graph (write, partitions, merge),
+    # replayed; measured slower than launching the three kernels here
+    run = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        run = graph.replay
     # the timed region: K whole steps back to back, nothing else on the stream
-    step_ms = timed(step)
+    step_ms = timed(run)
     # a second timed region of K steps with events around the partition kernel
     # (same stream) for its own duration; events add a few microseconds per
     # step, so the step time above is taken without them
@@ -576,7 +588,8 @@ def main() -> int:
                    "kv_dtype": "fp8_e4m3fn" if wl.fp8 else "f16",
                    "kv_scales": ("per (block, kv head)" if dyn else "per tensor")
                    if wl.fp8 else None,
-                   "arith": "f16 MFMA inputs, f32 accumulate", "parallelism": "single GPU"},
+                   "arith": "f16 MFMA inputs, f32 accumulate", "parallelism": "single GPU",
+                   "launch": "hip graph" if args.graph else "eager"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tok_per_s": round(tokens / (step_ms * 1e-3), 1),
         "kv_bytes_per_step": unique,

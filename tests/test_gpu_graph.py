@@ -1,0 +1,55 @@
+"""The decode step (cache write, partitions, merge) captured as one HIP graph
+and replayed: every replay, with eager work and synchronisations between
+replays, equals the eager step bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import paged_kv_cache_270_amd as pkv  # noqa: E402
+from paged_kv_cache_270_amd import workloads  # noqa: E402
+
+from gpu_common import Prepared  # noqa: E402
+
+
+@pytest.mark.parametrize("fp8,ps", [(True, 0), (True, 64), (False, 32)])
+def test_graph_replays_equal_the_eager_step(fp8, ps):
+    wl = workloads.tiny(seed=12, fp8=fp8, partition_size=ps)
+    prep = Prepared(wl)
+    B, Hq, D = wl.num_seqs, wl.num_q_heads, workloads.D
+    P = pkv.pkv_decode_partition_size(B, wl.num_kv_heads, wl.max_context_len, prep.layout.dtype,
+                                      ps)
+    ws = torch.empty(max(1, pkv.pkv_decode_workspace_bytes(B, Hq, wl.num_kv_heads,
+                                                           wl.max_context_len,
+                                                           prep.layout.dtype, P)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    k0, v0 = prep.k_pool.clone(), prep.v_pool.clone()
+
+    def step():
+        if wl.new_tokens:
+            pkv.pkv_reshape_and_cache(prep.new_k, prep.new_v, prep.k_pool, prep.v_pool,
+                                      prep.new_slots, prep.layout, prep.k_scale, prep.v_scale)
+        pkv.pkv_decode_partitions(out, prep.q, prep.k_pool, prep.v_pool, prep.tables, prep.lens,
+                                  wl.max_context_len, prep.layout, prep.sm_scale, prep.k_scale,
+                                  prep.v_scale, P, ws)
+        pkv.pkv_decode_reduce(out, prep.lens, wl.max_context_len, prep.tables.shape[1],
+                              prep.layout, prep.v_scale, P, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy().copy()
+    eager_k = prep.k_pool.cpu().numpy().copy()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(4):
+        out.fill_(float("nan"))                    # eager work between replays
+        prep.k_pool.copy_(k0)
+        prep.v_pool.copy_(v0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.view(np.uint32)), r
+        assert np.array_equal(prep.k_pool.cpu().numpy(), eager_k), r
