@@ -122,6 +122,17 @@ def llama70b_fp8(seed: int = 3, batch: int = 64, cached: int = 8192) -> Workload
                     _pad_tables(rows), new_tokens=new)
 
 
+def llama70b_fp8_tp4(seed: int = 3) -> Workload:
+    """One GPU's share of the 70B FP8 batch under 4-way tensor parallelism
+    over KV heads ("Optimización de KV Cache ...", §5 serves the model on 4
+    GPUs): the same 64 sequences and tables, 2 of the 8 KV heads and their 16
+    query heads."""
+    wl = llama70b_fp8(seed)
+    wl.name = wl.name.replace("llama70b-fp8", "llama70b-fp8-tp4-share")
+    wl.num_q_heads, wl.num_kv_heads = 16, 2
+    return wl
+
+
 def long_context(seed: int = 4, batch: int = 4, length: int = 131072,
                  partition_size: int = 512) -> Workload:
     """Batch 4 x 131072 tokens, FP8, split-KV into 512-token partitions; the
@@ -234,6 +245,7 @@ CONFIGS = {
     "tiny": tiny,
     "llama70b_fp16": llama70b_fp16,
     "llama70b_fp8": llama70b_fp8,
+    "llama70b_fp8_tp4": llama70b_fp8_tp4,
     "long_context": long_context,
     "shared_prefix": shared_prefix,
 }

@@ -59,6 +59,18 @@ def test_llama70b_fp8_step_full():
     assert err <= TOL[True]
 
 
+def test_tensor_parallel_share_full():
+    """One GPU's share of the 70B FP8 step under 4-way tensor parallelism over
+    KV heads: 2 KV heads, 16 query heads, the same 64 x 8193 tokens."""
+    prep = Prepared(workloads.llama70b_fp8_tp4())
+    prep.write_new_tokens()
+    got = prep.gpu_decode()
+    ref = prep.oracle_decode()
+    err = max_err(got, ref)
+    _report("llama70b fp8 TP=4 share (Hq=16, Hkv=2)", err, TOL[True])
+    assert err <= TOL[True]
+
+
 def test_long_context_full():
     prep = Prepared(workloads.long_context())
     got = prep.gpu_decode()
