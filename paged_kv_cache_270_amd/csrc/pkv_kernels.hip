@@ -1,7 +1,7 @@
-// pkv_kernels.hip — gfx950 (MI355X) kernels and the device half of libpkv's
-// C ABI: the cache write (per-tensor or per-block dynamic FP8 scales),
-// split-KV decode PagedAttention with its log-sum-exp merge, and the block
-// copy used for copy-on-write.
+// pkv_kernels.hip — gfx950 (MI355X) decode kernels and their part of libpkv's
+// C ABI: split-KV decode PagedAttention (per-tensor or per-block FP8 scales)
+// with its log-sum-exp merge.  The cache writes and block copies are in
+// pkv_write.hip, chunked prefill in pkv_prefill.hip, swap in pkv_swap.hip.
 //
 // Pages the kernels follow (cited by title and section):
 //   [FP8-128K] "Optimización de KV Cache con PagedAttention y Cuantización FP8
@@ -37,284 +37,15 @@
 #include <cstring>
 
 #include "pkv.h"
+#include "pkv_check.h"
 #include "pkv_tile.h"
 
 namespace {
 
 using namespace pkv_dev;
+using namespace pkv_check;
 
 constexpr int kRW = 4;       // waves per merge workgroup
-
-// ------------------------------------------------------------- FP8 codec
-
-// fp32 -> OCP E4M3FN code: round to nearest, ties to even, finite values
-// at or above 448 (and infinities) saturate to +-448, NaN -> 0x7F | sign.
-// Written from the format definition: below 2^-6 the codes are a uniform
-// grid of 2^-9 (subnormals), above it 3 mantissa bits are kept.
-__device__ __forceinline__ uint32_t e4m3_from_f32(float u) {
-  const uint32_t bits = __float_as_uint(u);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t abits = bits & 0x7FFFFFFFu;
-  if (abits > 0x7F800000u) return sign | 0x7Fu;              // NaN
-  const float a = __uint_as_float(abits);
-  if (a >= 448.0f) return sign | 0x7Eu;                      // saturate
-  if (a < 0.015625f)                                         // < 2^-6
-    return sign | (uint32_t)__builtin_rintf(a * 512.0f);     // 0..8, exact scaling
-  // keep the top 3 mantissa bits, round the 20 dropped bits half-to-even;
-  // a carry moves into the exponent, which is what the code needs
-  const uint32_t r = abits + 0x7FFFFu + ((abits >> 20) & 1u);
-  return sign | ((r >> 20) - (120u << 3));                   // rebias 127 -> 7
-}
-
-// ------------------------------------------------------ reshape_and_cache
-
-// Store channels 8c .. 8c+7 of one token's K and V rows (16 bytes of fp16
-// each) at position t of tile `tile` (= block * hkv + head).
-template <bool kFP8>
-__device__ __forceinline__ void store_rows8(uint8_t* __restrict__ k_pool,
-                                            uint8_t* __restrict__ v_pool, int64_t tile, int t,
-                                            int c, u32x4 kin, u32x4 vin, float k_scale,
-                                            float v_scale) {
-  const int n = c >> 1;                   // 16-channel group of these channels
-  const int j0 = (c & 1) * 8;             // channel within the group
-  if constexpr (!kFP8) {
-    uint16_t* kp = reinterpret_cast<uint16_t*>(k_pool) + tile * (kBS * kD);
-    uint16_t* vp = reinterpret_cast<uint16_t*>(v_pool) + tile * (kBS * kD);
-    // K, x = 8: (d/8)*128 + t*8 + d%8 -> the 8 channels are contiguous
-    *reinterpret_cast<u32x4*>(kp + c * 128 + t * 8) = kin;
-    // V, x = 8: (n/2)*512 + ((t/4)*16 + d%16)*8 + (n%2)*4 + t%4
-    const uint16_t* vh = reinterpret_cast<const uint16_t*>(&vin);
-    uint16_t* vb = vp + (n >> 1) * 512 + ((t >> 2) * 16 + j0) * 8 + (n & 1) * 4 + (t & 3);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vb[i * 8] = vh[i];
-  } else {
-    uint8_t* kp = k_pool + tile * (kBS * kD);
-    uint8_t* vp = v_pool + tile * (kBS * kD);
-    const _Float16* kh = reinterpret_cast<const _Float16*>(&kin);
-    const _Float16* vh = reinterpret_cast<const _Float16*>(&vin);
-    uint32_t kc[8], vc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      kc[i] = e4m3_from_f32((float)kh[i] / k_scale);  // correctly rounded fp32 division
-      vc[i] = e4m3_from_f32((float)vh[i] / v_scale);
-    }
-    // K, x = 16: (d/16)*256 + t*16 + d%16 -> 8 contiguous bytes
-    u32x2 kw;
-    kw.x = kc[0] | (kc[1] << 8) | (kc[2] << 16) | (kc[3] << 24);
-    kw.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
-    *reinterpret_cast<u32x2*>(kp + n * 256 + t * 16 + j0) = kw;
-    // V, x = 16: (n/4)*1024 + ((t/4)*16 + d%16)*16 + (n%4)*4 + t%4
-    uint8_t* vb = vp + (n >> 2) * 1024 + ((t >> 2) * 16 + j0) * 16 + (n & 3) * 4 + (t & 3);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vb[i * 16] = (uint8_t)vc[i];
-  }
-}
-
-// One thread per (token, kv head, run of 8 channels): 16 bytes of fp16 in.
-template <bool kFP8>
-__global__ void __launch_bounds__(256)
-reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
-                         uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-                         const int64_t* __restrict__ slots, int64_t total, int hkv,
-                         int64_t num_slots, float k_scale, float v_scale) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;
-  const int c = (int)(gid & 15);          // channels 8c .. 8c+7
-  const int64_t th = gid >> 4;            // token * hkv + head
-  const int64_t tok = th / hkv;
-  const int h = (int)(th - tok * hkv);
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;
-  store_rows8<kFP8>(k_pool, v_pool, (slot >> 4) * hkv + h, (int)(slot & 15), c,
-                    key[th * 16 + c], value[th * 16 + c], k_scale, v_scale);
-}
-
-// ------------------------------------------ write with per-block FP8 scales
-//
-// [FP8-128K] §8, dynamic scaling: each (block, KV head) tile of K and of V
-// carries its own fp32 scale, following the MaxAbs of the values written
-// into it.  Per call and per tile, with W the block's offsets this call
-// writes: the block is fresh when offset 0 is in W (its old scale and other
-// slots are disregarded); s_new = max(s_old or 0 if fresh, fp32(MaxAbs of
-// the new finite values / 448), 2^-126); if a non-fresh tile's scale grows,
-// its slots outside W are re-encoded as E4M3(fp32(value * fp32(s_old /
-// s_new))); new rows are E4M3(fp32(x / s_new)).
-//
-// Three launches, because the new scale of a block depends on every token
-// the call writes into it:
-//   1. clear the scratch entries of the touched blocks;
-//   2. MaxAbs of each new row into the scratch (integer atomic max of the
-//      non-negative float bits) and the written offsets (atomic or);
-//   3. every row is encoded with its tile's new scale; the call's token with
-//      the lowest offset in a block re-encodes the other slots and stores the
-//      new scales.  Any thread may read a tile's scale while that token
-//      replaces it: both values give the same s_new, since s_new is the max.
-
-// Value of an E4M3FN code (not NaN) as fp32, from the format definition.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -v : v;
-}
-
-__device__ __forceinline__ uint32_t requant_code(uint32_t c, float r) {
-  if ((c & 0x7Fu) == 0x7Fu) return c;  // NaN stays NaN
-  return e4m3_from_f32(e4m3_value(c) * r);
-}
-
-// Largest finite magnitude among 8 fp16 values, as fp16 bits (integer order
-// of non-negative fp16 bit patterns is their numeric order).
-__device__ __forceinline__ uint32_t max_abs_bits8(u32x4 x) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = x[i];
-    const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
-    if (lo < 0x7C00u) m = max(m, lo);
-    if (hi < 0x7C00u) m = max(m, hi);
-  }
-  return m;
-}
-
-__device__ __forceinline__ float f16_bits_to_float(uint32_t b) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-}
-
-__global__ void __launch_bounds__(256)
-dyn_clear_kernel(const int64_t* __restrict__ slots, int64_t total, int per_block,
-                 int64_t num_slots, uint32_t* __restrict__ amax, uint32_t* __restrict__ written) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;
-  const int64_t tok = gid / (per_block + 1);
-  const int j = (int)(gid - tok * (per_block + 1));
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot >> 4;
-  if (j < per_block)
-    amax[blk * per_block + j] = 0u;
-  else
-    written[blk] = 0u;
-}
-
-// One thread per (token, kv head, run of 8 channels), as the plain write;
-// the 16 threads of a row are 16 consecutive lanes.
-__global__ void __launch_bounds__(256)
-dyn_amax_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
-                const int64_t* __restrict__ slots, int64_t total, int hkv, int64_t num_slots,
-                uint32_t* __restrict__ amax, uint32_t* __restrict__ written) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;                  // total is a multiple of 16: whole rows leave
-  const int c = (int)(gid & 15);
-  const int64_t th = gid >> 4;
-  const int64_t tok = th / hkv;
-  const int h = (int)(th - tok * hkv);
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;  // the same for all 16 lanes of the row
-  uint32_t km = max_abs_bits8(key[th * 16 + c]);
-  uint32_t vm = max_abs_bits8(value[th * 16 + c]);
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) {
-    km = max(km, (uint32_t)__shfl_xor((int)km, m, kWave));
-    vm = max(vm, (uint32_t)__shfl_xor((int)vm, m, kWave));
-  }
-  if (c == 0) {
-    const int64_t blk = slot >> 4;
-    uint32_t* a = amax + (blk * hkv + h) * 2;
-    atomicMax(a, __float_as_uint(f16_bits_to_float(km)));
-    atomicMax(a + 1, __float_as_uint(f16_bits_to_float(vm)));
-    if (h == 0) atomicOr(written + blk, 1u << (slot & 15));
-  }
-}
-
-// Re-encode channels 8c .. 8c+7 of every slot of one FP8 tile outside `keep`.
-__device__ __forceinline__ void requant_k_rows(uint8_t* kp, int c, uint32_t keep, float r) {
-  const int n = c >> 1, j0 = (c & 1) * 8;
-  for (int t = 0; t < kBS; ++t) {
-    if (keep & (1u << t)) continue;
-    u32x2* p = reinterpret_cast<u32x2*>(kp + n * 256 + t * 16 + j0);  // K: 8 contiguous bytes
-    u32x2 w = *p;
-    uint32_t o[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t x = w[i];
-      o[i] = requant_code(x & 0xFFu, r) | (requant_code((x >> 8) & 0xFFu, r) << 8) |
-             (requant_code((x >> 16) & 0xFFu, r) << 16) | (requant_code(x >> 24, r) << 24);
-    }
-    w.x = o[0];
-    w.y = o[1];
-    *p = w;
-  }
-}
-
-__device__ __forceinline__ void requant_v_rows(uint8_t* vp, int c, uint32_t keep, float r) {
-  const int n = c >> 1, j0 = (c & 1) * 8;
-  for (int t = 0; t < kBS; ++t) {
-    if (keep & (1u << t)) continue;
-    uint8_t* vb = vp + (n >> 2) * 1024 + ((t >> 2) * 16 + j0) * 16 + (n & 3) * 4 + (t & 3);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vb[i * 16] = (uint8_t)requant_code(vb[i * 16], r);
-  }
-}
-
-__global__ void __launch_bounds__(256)
-dyn_write_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
-                 uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-                 float* __restrict__ k_bscale, float* __restrict__ v_bscale,
-                 const int64_t* __restrict__ slots, int64_t total, int hkv, int64_t num_slots,
-                 const uint32_t* __restrict__ amax, const uint32_t* __restrict__ written) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;
-  const int c = (int)(gid & 15);
-  const int64_t th = gid >> 4;
-  const int64_t tok = th / hkv;
-  const int h = (int)(th - tok * hkv);
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot >> 4;
-  const int off = (int)(slot & 15);
-  const int64_t tile = blk * hkv + h;
-  const uint32_t mask = written[blk];
-  const bool fresh = (mask & 1u) != 0;
-  const float min_scale = 0x1p-126f;
-  const float sk_old = fresh ? 0.0f : k_bscale[tile];
-  const float sv_old = fresh ? 0.0f : v_bscale[tile];
-  const float sk = fmaxf(fmaxf(sk_old, __uint_as_float(amax[tile * 2]) / 448.0f), min_scale);
-  const float sv = fmaxf(fmaxf(sv_old, __uint_as_float(amax[tile * 2 + 1]) / 448.0f), min_scale);
-  store_rows8<true>(k_pool, v_pool, tile, off, c, key[th * 16 + c], value[th * 16 + c], sk, sv);
-  if (off != __builtin_ctz(mask)) return;    // not this block's lowest new offset
-  uint8_t* kp = k_pool + tile * (kBS * kD);
-  uint8_t* vp = v_pool + tile * (kBS * kD);
-  if (!fresh && sk > sk_old) requant_k_rows(kp, c, mask, sk_old / sk);
-  if (!fresh && sv > sv_old) requant_v_rows(vp, c, mask, sv_old / sv);
-  if (c == 0) {
-    k_bscale[tile] = sk;
-    v_bscale[tile] = sv;
-  }
-}
-
-// ------------------------------------------------------------ copy_blocks
-
-// One workgroup per (source, destination) pair; with per-block scales the
-// destination's scale rows are copied too.
-__global__ void __launch_bounds__(256)
-copy_blocks_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
-                   float* __restrict__ k_bscale, float* __restrict__ v_bscale, int hkv,
-                   const int32_t* __restrict__ pairs, int64_t vecs_per_block, int num_blocks) {
-  const int i = blockIdx.x;
-  const int src = pairs[2 * i], dst = pairs[2 * i + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const int64_t s0 = (int64_t)src * vecs_per_block, d0 = (int64_t)dst * vecs_per_block;
-  for (int64_t v = threadIdx.x; v < vecs_per_block; v += 256) {
-    k_pool[d0 + v] = k_pool[s0 + v];
-    v_pool[d0 + v] = v_pool[s0 + v];
-  }
-  if (k_bscale != nullptr) {
-    for (int h = threadIdx.x; h < hkv; h += 256) {
-      k_bscale[(int64_t)dst * hkv + h] = k_bscale[(int64_t)src * hkv + h];
-      v_bscale[(int64_t)dst * hkv + h] = v_bscale[(int64_t)src * hkv + h];
-    }
-  }
-}
 
 // ----------------------------------------------------------------- decode
 
@@ -733,25 +464,6 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a, int64_
 
 // ------------------------------------------------------------- host side
 
-bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
-
-int elem_bytes(int32_t dtype) {
-  return dtype == PKV_F16 ? 2 : (dtype == PKV_FP8_E4M3FN ? 1 : 0);
-}
-
-pkv_status check_layout(const pkv_cache_layout* l) {
-  if (!l) return PKV_ERR_INVALID_ARG;
-  if (l->block_size != kBS || l->head_dim != kD || elem_bytes(l->dtype) == 0)
-    return PKV_ERR_UNSUPPORTED;
-  if (l->num_blocks <= 0 || l->num_kv_heads <= 0 || l->num_kv_heads > 65535)
-    return PKV_ERR_INVALID_ARG;
-  return PKV_OK;
-}
-
-pkv_status launch_status() {
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
-}
-
 // Automatic partition length (measured on MI355X at the five reference
 // shapes): fewer, longer partitions are faster as long as enough tiles are in
 // flight to cover HBM latency -- about 2048 waves of FP8 tiles (4 KiB per
@@ -937,40 +649,6 @@ extern "C" uint64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_h
   return ws_layout(num_seqs, num_q_heads, max_context_len, part).total;
 }
 
-extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
-                                            void* v_pool, const int64_t* slot_mapping,
-                                            int32_t num_tokens, const pkv_cache_layout* layout,
-                                            float k_scale, float v_scale, void* stream) {
-  pkv_status st = check_layout(layout);
-  if (st != PKV_OK) return st;
-  if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
-  if (num_tokens == 0) return PKV_OK;
-  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PKV_ERR_INVALID_ARG;
-  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-      !aligned(slot_mapping, 8))
-    return PKV_ERR_INVALID_ARG;
-  const bool fp8 = layout->dtype == PKV_FP8_E4M3FN;
-  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
-               v_scale > 0.0f))
-    return PKV_ERR_INVALID_ARG;
-  const int64_t total = (int64_t)num_tokens * layout->num_kv_heads * 16;
-  const int64_t blocks = (total + 255) / 256;
-  if (blocks > 0x7FFFFFFF) return PKV_ERR_INVALID_ARG;
-  const int64_t num_slots = (int64_t)layout->num_blocks * kBS;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  if (fp8)
-    reshape_and_cache_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
-        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping, total,
-        layout->num_kv_heads, num_slots, k_scale, v_scale);
-  else
-    reshape_and_cache_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
-        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping, total,
-        layout->num_kv_heads, num_slots, 1.0f, 1.0f);
-  return launch_status();
-}
 
 template <bool kFP8, bool kHw, bool kSplit, int kPD, int kNW, bool kDyn = false>
 static void launch_partition_v(dim3 grid, hipStream_t s, const DecodeArgs& a) {
@@ -1116,73 +794,9 @@ extern "C" pkv_status pkv_paged_attention_decode(
   return run_reduce(pl, num_seqs, s);
 }
 
-extern "C" pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const pkv_cache_layout* layout,
-                                      const int32_t* src_dst_pairs, int32_t num_pairs,
-                                      void* stream) {
-  pkv_status st = check_layout(layout);
-  if (st != PKV_OK) return st;
-  if (num_pairs < 0) return PKV_ERR_INVALID_ARG;
-  if (num_pairs == 0) return PKV_OK;
-  if (!k_pool || !v_pool || !src_dst_pairs || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-      !aligned(src_dst_pairs, 4))
-    return PKV_ERR_INVALID_ARG;
-  const int64_t bytes = (int64_t)layout->num_kv_heads * kBS * kD * elem_bytes(layout->dtype);
-  (void)hipGetLastError();
-  copy_blocks_kernel<<<dim3((unsigned)num_pairs), dim3(256), 0,
-                       static_cast<hipStream_t>(stream)>>>(
-      static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), nullptr, nullptr,
-      layout->num_kv_heads, src_dst_pairs, bytes / 16, layout->num_blocks);
-  return launch_status();
-}
 
-// ------------------------------------------------ per-block dynamic scales
 
-extern "C" uint64_t pkv_reshape_dynamic_workspace_bytes(const pkv_cache_layout* layout) {
-  if (check_layout(layout) != PKV_OK || layout->dtype != PKV_FP8_E4M3FN) return 0;
-  const uint64_t words = (uint64_t)layout->num_blocks * (2 * (uint64_t)layout->num_kv_heads + 1);
-  return (words * 4 + 255) / 256 * 256;
-}
 
-extern "C" pkv_status pkv_reshape_and_cache_dynamic(
-    const void* key, const void* value, void* k_pool, void* v_pool, float* k_block_scales,
-    float* v_block_scales, const int64_t* slot_mapping, int32_t num_tokens,
-    const pkv_cache_layout* layout, void* workspace, uint64_t workspace_bytes, void* stream) {
-  pkv_status st = check_layout(layout);
-  if (st != PKV_OK) return st;
-  if (layout->dtype != PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
-  if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
-  if (num_tokens == 0) return PKV_OK;
-  if (!key || !value || !k_pool || !v_pool || !slot_mapping || !k_block_scales ||
-      !v_block_scales)
-    return PKV_ERR_INVALID_ARG;
-  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-      !aligned(slot_mapping, 8) || !aligned(k_block_scales, 4) || !aligned(v_block_scales, 4))
-    return PKV_ERR_INVALID_ARG;
-  const uint64_t need = pkv_reshape_dynamic_workspace_bytes(layout);
-  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return PKV_ERR_INVALID_ARG;
-  const int hkv = layout->num_kv_heads;
-  const int64_t total = (int64_t)num_tokens * hkv * 16;
-  const int64_t blocks = (total + 255) / 256;
-  const int64_t clear_total = (int64_t)num_tokens * (2 * hkv + 1);
-  const int64_t clear_blocks = (clear_total + 255) / 256;
-  if (blocks > 0x7FFFFFFF || clear_blocks > 0x7FFFFFFF) return PKV_ERR_INVALID_ARG;
-  const int64_t num_slots = (int64_t)layout->num_blocks * kBS;
-  uint32_t* amax = static_cast<uint32_t*>(workspace);
-  uint32_t* written = amax + (int64_t)layout->num_blocks * 2 * hkv;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  dyn_clear_kernel<<<dim3((unsigned)clear_blocks), dim3(256), 0, s>>>(
-      slot_mapping, clear_total, 2 * hkv, num_slots, amax, written);
-  dyn_amax_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-      static_cast<const u32x4*>(key), static_cast<const u32x4*>(value), slot_mapping, total, hkv,
-      num_slots, amax, written);
-  dyn_write_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-      static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
-      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_block_scales,
-      v_block_scales, slot_mapping, total, hkv, num_slots, amax, written);
-  return launch_status();
-}
 
 extern "C" pkv_status pkv_paged_attention_decode_dynamic(
     float* out, const void* q, const void* k_pool, const void* v_pool,
@@ -1203,27 +817,4 @@ extern "C" pkv_status pkv_paged_attention_decode_dynamic(
   st = run_partitions(pl, num_seqs, s);
   if (st != PKV_OK) return st;
   return run_reduce(pl, num_seqs, s);
-}
-
-extern "C" pkv_status pkv_copy_blocks_dynamic(void* k_pool, void* v_pool, float* k_block_scales,
-                                              float* v_block_scales,
-                                              const pkv_cache_layout* layout,
-                                              const int32_t* src_dst_pairs, int32_t num_pairs,
-                                              void* stream) {
-  pkv_status st = check_layout(layout);
-  if (st != PKV_OK) return st;
-  if (layout->dtype != PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
-  if (num_pairs < 0) return PKV_ERR_INVALID_ARG;
-  if (num_pairs == 0) return PKV_OK;
-  if (!k_pool || !v_pool || !src_dst_pairs || !k_block_scales || !v_block_scales ||
-      !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(src_dst_pairs, 4) ||
-      !aligned(k_block_scales, 4) || !aligned(v_block_scales, 4))
-    return PKV_ERR_INVALID_ARG;
-  const int64_t bytes = (int64_t)layout->num_kv_heads * kBS * kD;
-  (void)hipGetLastError();
-  copy_blocks_kernel<<<dim3((unsigned)num_pairs), dim3(256), 0,
-                       static_cast<hipStream_t>(stream)>>>(
-      static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), k_block_scales, v_block_scales,
-      layout->num_kv_heads, src_dst_pairs, bytes / 16, layout->num_blocks);
-  return launch_status();
 }

@@ -35,11 +35,13 @@
 #include <cstdint>
 
 #include "pkv.h"
+#include "pkv_check.h"
 #include "pkv_tile.h"
 
 namespace {
 
 using namespace pkv_dev;
+using namespace pkv_check;
 
 constexpr int kQT = 16;       // chunk tokens per workgroup
 constexpr int kHeadsPerWave = 2;
@@ -345,8 +347,6 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
   }
 }
 
-bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
-
 }  // namespace
 
 extern "C" pkv_status pkv_paged_prefill_attention(
@@ -355,12 +355,8 @@ extern "C" pkv_status pkv_paged_prefill_attention(
     const int32_t* query_start, int32_t num_seqs, int32_t num_q_heads, int32_t max_query_len,
     int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
     float v_scale, void* stream) {
-  if (!layout) return PKV_ERR_INVALID_ARG;
-  if (layout->block_size != kBS || layout->head_dim != kD ||
-      (layout->dtype != PKV_F16 && layout->dtype != PKV_FP8_E4M3FN))
-    return PKV_ERR_UNSUPPORTED;
-  if (layout->num_blocks <= 0 || layout->num_kv_heads <= 0 || layout->num_kv_heads > 65535)
-    return PKV_ERR_INVALID_ARG;
+  const pkv_status st = check_layout(layout);
+  if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_seqs > 65535 || num_q_heads <= 0 || max_query_len < 0 ||
       max_context_len < 0)
     return PKV_ERR_INVALID_ARG;
@@ -403,5 +399,5 @@ extern "C" pkv_status pkv_paged_prefill_attention(
     prefill_kernel<true><<<grid, dim3(waves * kWave), 0, s>>>(a);
   else
     prefill_kernel<false><<<grid, dim3(waves * kWave), 0, s>>>(a);
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return launch_status();
 }

@@ -11,6 +11,7 @@
 #include <initializer_list>
 
 #include "pkv.h"
+#include "pkv_check.h"
 
 namespace {
 
@@ -45,7 +46,9 @@ swap_blocks_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
   }
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p % 16) == 0; }
+using namespace pkv_check;
+
+bool aligned16(const void* p) { return aligned(p, 16); }
 
 }  // namespace
 
@@ -53,12 +56,8 @@ extern "C" pkv_status pkv_swap_blocks(void* k_pool, void* v_pool, void* host_k, 
                                       int32_t num_host_blocks, const pkv_cache_layout* layout,
                                       const int32_t* pairs, int32_t num_pairs, int32_t to_host,
                                       void* stream) {
-  if (!layout) return PKV_ERR_INVALID_ARG;
-  if (layout->block_size != 16 || layout->head_dim != 128 ||
-      (layout->dtype != PKV_F16 && layout->dtype != PKV_FP8_E4M3FN))
-    return PKV_ERR_UNSUPPORTED;
-  if (layout->num_blocks <= 0 || layout->num_kv_heads <= 0 || layout->num_kv_heads > 65535)
-    return PKV_ERR_INVALID_ARG;
+  const pkv_status st = check_layout(layout);
+  if (st != PKV_OK) return st;
   if (num_pairs < 0 || num_host_blocks < 0 || (to_host != 0 && to_host != 1))
     return PKV_ERR_INVALID_ARG;
   if (num_pairs == 0) return PKV_OK;
@@ -66,8 +65,7 @@ extern "C" pkv_status pkv_swap_blocks(void* k_pool, void* v_pool, void* host_k, 
       !aligned16(v_pool) || !aligned16(host_k) || !aligned16(host_v) ||
       ((uintptr_t)pairs % 4) != 0)
     return PKV_ERR_INVALID_ARG;
-  const int64_t elem = layout->dtype == PKV_F16 ? 2 : 1;
-  const int64_t bytes = (int64_t)layout->num_kv_heads * 16 * 128 * elem;
+  const int64_t bytes = (int64_t)layout->num_kv_heads * 16 * 128 * elem_bytes(layout->dtype);
   // the device's address of each host buffer; memory that is not pinned host
   // memory the device can reach is refused here rather than faulted on
   (void)hipGetLastError();
@@ -90,5 +88,5 @@ extern "C" pkv_status pkv_swap_blocks(void* k_pool, void* v_pool, void* host_k, 
                        static_cast<hipStream_t>(stream)>>>(
       static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), static_cast<u32x4*>(dk),
       static_cast<u32x4*>(dv), pairs, bytes / 16, layout->num_blocks, num_host_blocks, to_host);
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return launch_status();
 }

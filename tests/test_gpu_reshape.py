@@ -46,15 +46,51 @@ def test_random_slots_bit_exact(fp8, hkv):
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.0110, 0.125, 0.37, 1e-3, 7.0, 3.0e-5])
-def test_fp8_encode_every_fp16_value(scale):
+@pytest.mark.parametrize("order", ["blocks", "rows"])
+def test_fp8_encode_every_fp16_value(scale, order):
     """All 65536 fp16 inputs (zeros, subnormals, infinities, NaNs) through
-    the device encoder, for several scales, against the oracle's encoder."""
+    the device encoder, for several scales, against the oracle's encoder --
+    written as whole blocks in order (the tile-building kernel: 1024 tokens)
+    and token by token (the row kernel: 512 tokens, reversed slots)."""
     bits = np.arange(65536, dtype=np.uint16)
     x = torch.from_numpy(bits.view(np.float16).reshape(512, 1, D).copy())
-    slots = np.arange(512, dtype=np.int64)
-    kd, vd, kh, vh = _write_both(x, x.flip(0).contiguous(), slots, 32, 1, True, scale, scale)
+    if order == "blocks":
+        x = torch.cat([x, x.flip(0)]).contiguous()
+        slots = np.arange(1024, dtype=np.int64)
+    else:
+        slots = np.arange(512, dtype=np.int64)[::-1].copy()
+    n = len(slots)
+    kd, vd, kh, vh = _write_both(x, x.flip(0).contiguous(), slots, n // 16, 1, True, scale,
+                                 scale)
     assert np.array_equal(kd, kh)
     assert np.array_equal(vd, vh)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("hkv", [1, 8])
+def test_whole_block_groups_and_row_by_row_groups_agree(fp8, hkv):
+    """Groups of 16 tokens that fill one block in order take the tile-building
+    path; every other group (misaligned, reversed, with a skipped slot, past
+    the pool, a short last group) is written row by row.  Both must leave
+    exactly the oracle's bytes."""
+    nb = 12 * 8
+    runs = []
+    for r in range(8):                              # > 512 tokens: the tile-building kernel
+        o = 12 * r
+        runs += [np.arange(16) + 16 * (o + 2),      # a block in order: whole
+                 np.arange(16) + 16 * (o + 5) + 3,  # misaligned: spans two blocks
+                 (np.arange(16) + 16 * (o + 7))[::-1],                      # reversed
+                 np.where(np.arange(16) == 9, -1, np.arange(16) + 16 * (o + 8)),  # a skip
+                 np.arange(16) + 16 * o]            # another whole block
+    runs += [np.arange(16) + 16 * (nb - 1) + 8,     # runs past the pool's end
+             np.arange(7) + 16 * 10]                # short last group
+    slots = np.concatenate(runs).astype(np.int64)
+    assert slots.size > 512
+    T = slots.size
+    key = workloads.randn_f16((T, hkv, D), 61 + hkv)
+    value = workloads.randn_f16((T, hkv, D), 62 + hkv)
+    kd, vd, kh, vh = _write_both(key, value, slots, nb, hkv, fp8, 0.0123, 0.031)
+    assert np.array_equal(kd, kh) and np.array_equal(vd, vh)
 
 
 def test_fp16_write_is_a_raw_copy():
