@@ -57,8 +57,10 @@ struct DecodeArgs {
   const int32_t* block_tables; // [B][max_blocks]
   const int32_t* context_lens; // [B]
   const int32_t* shared_prefix;// [B] or null: leading blocks shared with other sequences
-  float* ws_ml;                // [B][Hq][n_p_max][2]: running max (log2 units), sum
-  float* ws_o;                 // [B][Hq][n_p_max][D]: unnormalised output
+  // Partials, one row per (sequence, KV head, partition, head of the group):
+  // the G rows a workgroup or wave stores at a partition's end are adjacent.
+  float* ws_ml;                // [B][Hkv][n_p_max][G][2]: running max (log2 units), sum
+  float* ws_o;                 // [B][Hkv][n_p_max][G][D]: unnormalised output
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t hq, hkv, g;
@@ -70,6 +72,21 @@ struct DecodeArgs {
   const float* k_bscale;       // [num_blocks][hkv] per-block K scales, or null
   const float* v_bscale;       // [num_blocks][hkv] per-block V scales, or null
 };
+
+// Partials are stored write-through to memory (cache policy sc0 sc1, through
+// a buffer resource over the G rows of one partition): at 512-token
+// partitions this measured about 5% faster for the partition kernel than
+// ordinary write-back stores.
+constexpr int kWriteThrough = 1 | 16;  // sc0 | sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rows(float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+
+// Row of the partial of query head g of KV head kvh's group, partition p.
+__device__ __forceinline__ int64_t part_row(const DecodeArgs& a, int b, int kvh, int p, int g) {
+  return (((int64_t)b * a.hkv + kvh) * a.n_p_max + p) * a.g + g;
+}
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
   int L = a.context_lens[b];
@@ -326,6 +343,9 @@ decode_partition_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const bool single = n_p == 1;
+  // the G rows of this partition's partial output (not used when single)
+  const __amdgpu_buffer_rsrc_t orows =
+      partial_rows(single ? nullptr : a.ws_o + part_row(a, b, kvh, p, 0) * kD, G * kD * 4);
   for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) {
     const int gg = i / kD, d = i - gg * kD;
     float mx = -INFINITY;
@@ -342,8 +362,8 @@ decode_partition_kernel(DecodeArgs a) {
     if (single) {
       a.out[hrow * kD + d] = num / den * a.out_scale;
     } else {
-      const int64_t prow = hrow * a.n_p_max + p;
-      a.ws_o[prow * kD + d] = num;
+      const int64_t prow = part_row(a, b, kvh, p, gg);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(num), orows, i * 4, 0, kWriteThrough);
       if (d == 0) {
         a.ws_ml[prow * 2] = mx;
         a.ws_ml[prow * 2 + 1] = den;
@@ -352,6 +372,131 @@ decode_partition_kernel(DecodeArgs a) {
   }
 }
 
+// Short partitions (an explicit split-KV length of a few hundred tokens):
+// launching one workgroup per partition leaves each wave a stream of a few
+// tiles, and the stream drains at every partition end.  Here each wave owns
+// `chain` consecutive partitions of one (sequence, KV head) instead -- a
+// contiguous run of logical blocks -- and streams them back to back; at the
+// end of each partition it stores that partition's (max, sum, unnormalised
+// output) straight from registers, so there is no LDS merge and no barrier.
+// The partials, and the merge kernel that combines them, are the same as
+// with one workgroup per partition.  Per-tensor scales only: with per-block
+// scales the extra registers spill and one workgroup per partition is faster.
+// Grid (ceil(n_p_max / (kChainWaves * chain)), Hkv, B); kChainWaves waves per
+// workgroup, each independent of the others.
+constexpr int kChainWaves = 4;
+
+template <bool kFP8>
+__global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(DecodeArgs a,
+                                                                           int chain) {
+  constexpr int kPD = 1;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int qg = lane >> 4;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.g;
+
+  const int L = clamp_len(a, b);
+  const SeqSplit sp = seq_split(a, L);
+  const int64_t head0 = (int64_t)b * a.hq + (int64_t)kvh * G;
+  const int p_first = (blockIdx.x * kChainWaves + w) * chain;
+  if (p_first >= sp.n_p) {
+    if (p_first == 0) {  // empty sequence: attention over nothing is defined as zeros
+      for (int i = lane; i < G * kD; i += kWave) a.out[head0 * kD + i] = 0.0f;
+    }
+    return;
+  }
+  const int blk_begin = p_first * sp.per;
+  const int my_n = min(sp.nblk, (p_first + chain) * sp.per) - blk_begin;
+
+  f16x8 qop[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (j < G) {
+      const int d0 = kFP8 ? (m >> 1) * 64 + qg * 16 + (m & 1) * 8 : m * 32 + qg * 8;
+      qop[m] = *reinterpret_cast<const f16x8*>(a.q + (head0 + j) * kD + d0);
+    } else {
+      qop[m] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  SoftmaxState st;
+  st.m_ref = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bool single = sp.n_p == 1;
+  int part = p_first;                                   // partition being accumulated
+  int part_end = min(sp.nblk, (part + 1) * sp.per);     // its first block past the end
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk_begin;
+  const int shared_blocks = a.shared_prefix != nullptr ? a.shared_prefix[b] : 0;
+  for (int c0 = 0; c0 < my_n; c0 += kWave) {
+    const int cnt = min(kWave, my_n - c0);
+    const int tbl = lane < cnt ? trow[c0 + lane] : 0;
+    const int lb0 = blk_begin + c0;
+    TileRegs<kFP8> buf[kPD + 1];
+#pragma unroll
+    for (int r = 0; r < kPD; ++r)
+      if (r < cnt)
+        load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                        __builtin_amdgcn_readlane(tbl, r), kvh, lane, lb0 + r < shared_blocks);
+    for (int base = 0; base < cnt; base += kPD + 1) {
+#pragma unroll
+      for (int r = 0; r <= kPD; ++r) {
+        const int ii = base + r;
+        if (ii < cnt) {
+          if (ii + kPD < cnt)
+            load_tile<kFP8>(buf[(r + kPD) % (kPD + 1)], a.k_pool, a.v_pool, a.num_blocks,
+                            a.hkv, __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane,
+                            lb0 + ii + kPD < shared_blocks);
+          process_tile<kFP8, true, true>(buf[r], qop, st, (lb0 + ii) * kBS, qg, L, a.qk_scale);
+          if (lb0 + ii + 1 == part_end) {  // wave-uniform: partition `part` is complete
+            float l_run = st.l;
+            l_run += __shfl_xor(l_run, 16, kWave);
+            l_run += __shfl_xor(l_run, 32, kWave);
+            const int64_t hrow = head0 + j;
+            // the G rows of this partition's partial output (not used when single)
+            // (part is wave-uniform; readfirstlane lets the compiler know)
+            const int part_u = __builtin_amdgcn_readfirstlane(part);
+            const __amdgpu_buffer_rsrc_t orows = partial_rows(
+                single ? nullptr : a.ws_o + part_row(a, b, kvh, part_u, 0) * kD, G * kD * 4);
+            if (j < G) {
+              if (single) {
+                float* dst = a.out + hrow * kD + qg * 4;
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                  f32x4 o;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) o[e] = st.acc[n][e] / l_run * a.out_scale;
+                  *reinterpret_cast<f32x4*>(dst + n * 16) = o;
+                }
+              } else {
+                const int64_t prow = part_row(a, b, kvh, part, j);
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+                  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st.acc[n]),
+                                                         orows, (j * kD + n * 16 + qg * 4) * 4, 0,
+                                                         kWriteThrough);
+                if (qg == 0) {
+                  a.ws_ml[prow * 2] = st.m_ref;
+                  a.ws_ml[prow * 2 + 1] = l_run;
+                }
+              }
+            }
+            st.m_ref = -INFINITY;
+            st.l = 0.0f;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ++part;
+            part_end = min(sp.nblk, part_end + sp.per);
+          }
+        }
+      }
+    }
+  }
+}
 
 // Merge kernel: for each (sequence, query head) whose sequence spans n_p > 1
 // partitions, M = max_p m_p and
@@ -365,7 +510,7 @@ decode_partition_kernel(DecodeArgs a) {
 constexpr int kFewPartitions = 8;
 
 template <bool kSplit>
-__global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a, int64_t rows) {
+__global__ void __launch_bounds__(kRW * kWave) decode_reduce_kernel(DecodeArgs a, int64_t rows) {
   __shared__ float2 part[kRW][kWave];
   __shared__ float dens[kRW];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -374,17 +519,19 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a, int64_
   const int b = (int)(bh / a.hq);
   const int n_p = seq_split(a, clamp_len(a, b)).n_p;
   if (n_p <= 1) return;                      // written by the partition kernel
-  const int64_t row0 = bh * a.n_p_max;
+  const int h = (int)(bh - (int64_t)b * a.hq);
+  const int64_t row0 = part_row(a, b, h / a.g, 0, h % a.g);
+  const int64_t pst = a.g;                   // rows from one partition to the next
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
 
   if (!kSplit && n_p <= kFewPartitions) {
     // few partitions: issue every load before the max reduction
-    const float2 mine = lane < n_p ? ml[row0 + lane] : make_float2(-INFINITY, 0.0f);
+    const float2 mine = lane < n_p ? ml[row0 + lane * pst] : make_float2(-INFINITY, 0.0f);
     const float2* orow = reinterpret_cast<const float2*>(a.ws_o + row0 * kD) + lane;
     float2 o[kFewPartitions];
 #pragma unroll
     for (int k = 0; k < kFewPartitions; ++k)
-      o[k] = k < n_p ? orow[k * (kD / 2)] : make_float2(0.f, 0.f);
+      o[k] = k < n_p ? orow[k * pst * (kD / 2)] : make_float2(0.f, 0.f);
     const float mx = wave_max(mine.x);
     const float wgt = lane < n_p ? __builtin_amdgcn_exp2f(mine.x - mx) : 0.0f;
     const float den = wave_sum(mine.y * wgt);
@@ -401,7 +548,7 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a, int64_
   }
 
   float mx = -INFINITY;
-  for (int pp = lane; pp < n_p; pp += kWave) mx = fmaxf(mx, ml[row0 + pp].x);
+  for (int pp = lane; pp < n_p; pp += kWave) mx = fmaxf(mx, ml[row0 + pp * pst].x);
   mx = wave_max(mx);
 
   const int p0 = kSplit ? w : 0, ps = kSplit ? kRW : 1;
@@ -411,29 +558,29 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(DecodeArgs a, int64_
     const int mine = c + lane * ps;          // this lane's partition of the chunk
     float wgt = 0.0f;
     if (mine < n_p) {
-      const float2 v = ml[row0 + mine];
+      const float2 v = ml[row0 + mine * pst];
       wgt = __builtin_amdgcn_exp2f(v.x - mx);
       den += v.y * wgt;
     }
     const int cnt = min(kWave, (n_p - c + ps - 1) / ps);
-    const float2* orow = reinterpret_cast<const float2*>(a.ws_o + (row0 + c) * kD) + lane;
+    const float2* orow = reinterpret_cast<const float2*>(a.ws_o + (row0 + c * pst) * kD) + lane;
+    const int64_t ost = ps * pst * (kD / 2);  // float2 steps between this wave's partitions
+    // kBatch partial rows in flight per wave; summed in partition order
+    constexpr int kBatch = 16;
     int k = 0;
-    for (; k + 4 <= cnt; k += 4) {
-      const float2 o0 = orow[(int64_t)(k + 0) * ps * (kD / 2)];
-      const float2 o1 = orow[(int64_t)(k + 1) * ps * (kD / 2)];
-      const float2 o2 = orow[(int64_t)(k + 2) * ps * (kD / 2)];
-      const float2 o3 = orow[(int64_t)(k + 3) * ps * (kD / 2)];
-      const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + 0));
-      const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + 1));
-      const float g2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + 2));
-      const float g3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + 3));
-      acc.x += o0.x * g0; acc.y += o0.y * g0;
-      acc.x += o1.x * g1; acc.y += o1.y * g1;
-      acc.x += o2.x * g2; acc.y += o2.y * g2;
-      acc.x += o3.x * g3; acc.y += o3.y * g3;
+    for (; k + kBatch <= cnt; k += kBatch) {
+      float2 o[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) o[u] = orow[(int64_t)(k + u) * ost];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + u));
+        acc.x += o[u].x * g;
+        acc.y += o[u].y * g;
+      }
     }
     for (; k < cnt; ++k) {
-      const float2 o = orow[(int64_t)k * ps * (kD / 2)];
+      const float2 o = orow[(int64_t)k * ost];
       const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
       acc.x += o.x * g; acc.y += o.y * g;
     }
@@ -517,21 +664,29 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32
 //                                 being computed
 //   PKV_DECODE_WAVES = 1|2|4|8    waves per partition workgroup (default:
 //                                 from the partition length)
+//   PKV_DECODE_CHAIN = 0 | n      partitions per wave for short partitions:
+//                                 0 = one workgroup per partition, n = fixed
+//                                 (default: from the shape)
 struct KernelConfig {
   bool hw_cvt;
   bool split_p_fp8;
   int prefetch;
   int waves;
+  int chain;  // -1 = automatic
 };
 
 KernelConfig kernel_config() {
   static const KernelConfig cfg = [] {
-    KernelConfig k{true, true, 1, 0};
+    KernelConfig k{true, true, 1, 0, -1};
     if (const char* e = std::getenv("PKV_FP8_DEQUANT")) k.hw_cvt = std::strcmp(e, "hw") == 0;
     if (const char* e = std::getenv("PKV_FP8_SPLIT_P")) k.split_p_fp8 = std::atoi(e) != 0;
     if (const char* e = std::getenv("PKV_DECODE_PREFETCH")) {
       const int v = std::atoi(e);
       if (v >= 1 && v <= 2) k.prefetch = v;
+    }
+    if (const char* e = std::getenv("PKV_DECODE_CHAIN")) {
+      const int v = std::atoi(e);
+      if (v >= 0 && v <= 1024) k.chain = v;
     }
     if (const char* e = std::getenv("PKV_DECODE_WAVES")) {
       const int v = std::atoi(e);
@@ -709,13 +864,43 @@ static int waves_for(const DecodePlan& pl) {
   return nw;
 }
 
+// Partitions per wave for the chained kernel, or 0 for one workgroup per
+// partition.  Chaining applies to short partitions (at most 64 blocks) of the
+// default kernel family with per-tensor scales: each wave gets about 128
+// tiles, as with the automatic partition length, while the grid keeps about
+// 2048 waves.
+static int chain_for(const DecodePlan& pl, int32_t num_seqs) {
+  const KernelConfig& c = pl.cfg;
+  if (c.chain == 0 || pl.a.n_p_max <= 1 || pl.dyn) return 0;
+  if (pl.fp8 && !(c.hw_cvt && c.split_p_fp8)) return 0;
+  if (c.chain > 0) return c.chain;
+  if (c.prefetch != 1 || c.waves != 0 || pl.a.part_blocks > 64) return 0;
+  const int64_t pairs = (int64_t)num_seqs * pl.a.hkv;
+  int chain = std::max(1, 128 / pl.a.part_blocks);
+  while (chain > 1 && pairs * ((pl.a.n_p_max + chain - 1) / chain) < 2048) chain /= 2;
+  return chain;
+}
+
+template <bool kFP8>
+static void launch_chain(int chain, int32_t num_seqs, hipStream_t s, const DecodeArgs& a) {
+  const int per_wg = kChainWaves * chain;
+  const dim3 grid((unsigned)((a.n_p_max + per_wg - 1) / per_wg), (unsigned)a.hkv,
+                  (unsigned)num_seqs);
+  decode_chain_kernel<kFP8><<<grid, dim3(kChainWaves * kWave), 0, s>>>(a, chain);
+}
+
 static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStream_t s) {
   if (num_seqs == 0) return PKV_OK;
   const dim3 grid((unsigned)pl.a.n_p_max, (unsigned)pl.a.hkv, (unsigned)num_seqs);
   (void)hipGetLastError();
   const KernelConfig& c = pl.cfg;
   const int nw = waves_for(pl);
-  if (pl.dyn)
+  if (const int chain = chain_for(pl, num_seqs)) {
+    if (pl.fp8)
+      launch_chain<true>(chain, num_seqs, s, pl.a);
+    else
+      launch_chain<false>(chain, num_seqs, s, pl.a);
+  } else if (pl.dyn)
     launch_partition_dyn(nw, grid, s, pl.a);
   else if (!pl.fp8)
     launch_partition<false, false, true>(c.prefetch, nw, grid, s, pl.a);
@@ -733,7 +918,7 @@ static pkv_status run_reduce(const DecodePlan& pl, int32_t num_seqs, hipStream_t
   (void)hipGetLastError();
   const int64_t rows = (int64_t)num_seqs * pl.a.hq;
   if (pl.a.n_p_max > 32) {
-    decode_reduce_kernel<true><<<dim3((unsigned)rows), dim3(256), 0, s>>>(pl.a, rows);
+    decode_reduce_kernel<true><<<dim3((unsigned)rows), dim3(kRW * kWave), 0, s>>>(pl.a, rows);
   } else {
     const int64_t grid = (rows + kRW - 1) / kRW;
     decode_reduce_kernel<false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(pl.a, rows);

@@ -320,17 +320,37 @@ def test_negative_length_gives_zeros_and_empty_batch_is_a_no_op():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("waves", [1, 2, 4])
-def test_each_wave_count_matches_the_oracle(waves, monkeypatch):
-    """Short and long partitions select 1, 2 or 4 waves per workgroup; check a
-    partition length that lands on each choice."""
-    ps = {1: 256, 2: 512, 4: 1024}[waves]
-    wl = _small_workload([1, 300, 1100, 2100], hq=16, hkv=2, seed=60 + waves)
+# Ragged lengths around block and partition edges, up to 8192 tokens.
+_RAGGED = [1, 15, 16, 17, 127, 128, 129, 1000, 2049, 4095, 4096, 4097, 6000, 8000, 8191, 8192]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("ps", [64, 128, 256, 512])
+def test_chained_short_partitions_ragged_batch(fp8, ps):
+    """Short explicit partitions go to the kernel where each wave streams
+    several consecutive partitions and stores a partial at each partition's
+    end.  With 16 sequences x 8 KV heads the library chains 8, 4, 2 and 1
+    partitions per wave at P = 64, 128, 256 and 512; the ragged lengths give
+    single-partition sequences, waves with nothing to do and chains cut short
+    at a sequence's end."""
+    wl = _small_workload(_RAGGED, hq=64, hkv=8, fp8=fp8, seed=70 + ps)
     wl.partition_size = ps
     prep = Prepared(wl)
     err = max_err(prep.gpu_decode(), prep.oracle_decode())
-    _report(f"partition {ps} (waves {waves})", err, TOL[True])
-    assert err <= TOL[True]
+    _report(f"ragged 16 x <=8192, P={ps} fp8={fp8}", err, TOL[fp8])
+    assert err <= TOL[fp8]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_long_partitions_merged_across_waves(fp8):
+    """Partitions of 2048 tokens go to one workgroup per partition, whose four
+    waves merge through LDS before the partial is stored."""
+    wl = _small_workload([1, 2047, 2048, 2049, 5000, 8192], hq=16, hkv=2, fp8=fp8, seed=81)
+    wl.partition_size = 2048
+    prep = Prepared(wl)
+    err = max_err(prep.gpu_decode(), prep.oracle_decode())
+    _report(f"P=2048 across waves fp8={fp8}", err, TOL[fp8])
+    assert err <= TOL[fp8]
 
 
 def test_shared_prefix_cache_hint_changes_nothing():

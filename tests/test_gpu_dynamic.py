@@ -104,7 +104,7 @@ def test_write_is_bit_exact_through_growth_and_interleaved_calls(Hkv):
     print(f"[parity] dynamic write Hkv={Hkv}: pools and scales bit-exact", flush=True)
 
 
-@pytest.mark.parametrize("ps", [0, 16, 64])
+@pytest.mark.parametrize("ps", [0, 16, 64, 256, 512])
 def test_decode_with_block_scales_matches_oracle(ps):
     rng = np.random.default_rng(50 + ps)
     NB, Hkv, Hq = 128, 2, 16
