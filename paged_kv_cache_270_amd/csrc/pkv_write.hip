@@ -88,24 +88,28 @@ __device__ __forceinline__ void store_rows8(uint8_t* __restrict__ k_pool,
 }
 
 // One thread per (token, kv head, run of 8 channels): 16 bytes of fp16 in.
-// One thread per (token, kv head, run of 8 channels): 16 bytes of fp16 in.
-// For calls of few tokens (a decode step) -- the most parallel form.
+// For calls of few tokens (a decode step) -- the most parallel form.  The
+// row loads do not depend on the slot, so all three loads are in flight at
+// once (the call is latency-bound).
 template <bool kFP8>
 __global__ void __launch_bounds__(256)
 reshape_rows_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
                     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-                    const int64_t* __restrict__ slots, int64_t total, int hkv,
+                    const int64_t* __restrict__ slots, uint32_t total, uint32_t hkv,
                     int64_t num_slots, float k_scale, float v_scale) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;  // total < 2^31 (checked on the host)
   if (gid >= total) return;
   const int c = (int)(gid & 15);          // channels 8c .. 8c+7
-  const int64_t th = gid >> 4;            // token * hkv + head
-  const int64_t tok = th / hkv;
+  const uint32_t th = gid >> 4;           // token * hkv + head
+  const uint32_t tok = th / hkv;
   const int h = (int)(th - tok * hkv);
+  const u32x4 kin = key[th * 16 + c];
+  const u32x4 vin = value[th * 16 + c];
   const int64_t slot = slots[tok];
+  asm volatile("" ::"v"(kin), "v"(vin));  // keeps the row loads ahead of the slot test
   if (slot < 0 || slot >= num_slots) return;
-  store_rows8<kFP8>(k_pool, v_pool, (slot >> 4) * hkv + h, (int)(slot & 15), c,
-                    key[th * 16 + c], value[th * 16 + c], k_scale, v_scale);
+  store_rows8<kFP8>(k_pool, v_pool, (slot >> 4) * hkv + h, (int)(slot & 15), c, kin, vin,
+                    k_scale, v_scale);
 }
 
 // Calls of at most this many tokens use the row kernel; longer ones (bulk
@@ -404,19 +408,19 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
   const dim3 grid((unsigned)groups, (unsigned)layout->num_kv_heads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (num_tokens <= kRowWriteMaxTokens) {
-    const int64_t total = (int64_t)num_tokens * layout->num_kv_heads * 16;
+  const int64_t total = (int64_t)num_tokens * layout->num_kv_heads * 16;
+  if (num_tokens <= kRowWriteMaxTokens && total < ((int64_t)1 << 31)) {
     const unsigned blocks = (unsigned)((total + 255) / 256);
     if (fp8)
       reshape_rows_kernel<true><<<dim3(blocks), dim3(256), 0, s>>>(
           static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
-          static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping, total,
-          layout->num_kv_heads, num_slots, k_scale, v_scale);
+          static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping,
+          (uint32_t)total, (uint32_t)layout->num_kv_heads, num_slots, k_scale, v_scale);
     else
       reshape_rows_kernel<false><<<dim3(blocks), dim3(256), 0, s>>>(
           static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
-          static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping, total,
-          layout->num_kv_heads, num_slots, 1.0f, 1.0f);
+          static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping,
+          (uint32_t)total, (uint32_t)layout->num_kv_heads, num_slots, 1.0f, 1.0f);
     return launch_status();
   }
   if (fp8)
