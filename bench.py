@@ -356,7 +356,7 @@ def main() -> int:
     ap.add_argument("--workload", default="llama70b_fp8",
                     help="llama70b_fp8 (default) | llama70b_fp8_tp4 | llama70b_fp16 | "
                          "long_context | shared_prefix | tiny | prefill_128k | prefill_mixed | "
-                         "swap")
+                         "prefill_128k_fp16 | swap")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="longest split-KV partition in tokens (default: the workload's "
                          "own, else the library's choice)")

@@ -241,6 +241,11 @@ def prefill_mixed(seed: int = 7) -> PrefillWorkload:
                     [2048] * 4)
 
 
+def prefill_128k_fp16(seed: int = 6) -> PrefillWorkload:
+    """The 128K prompt's last 8192-token chunk with an fp16 cache."""
+    return _prefill("prefill-fp16-b1-chunk8192-l131072", seed, [131072], [8192], fp8=False)
+
+
 CONFIGS = {
     "tiny": tiny,
     "llama70b_fp16": llama70b_fp16,
@@ -253,6 +258,7 @@ CONFIGS = {
 PREFILL_CONFIGS = {
     "prefill_128k": prefill_128k,
     "prefill_mixed": prefill_mixed,
+    "prefill_128k_fp16": prefill_128k_fp16,
 }
 
 
