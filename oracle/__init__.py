@@ -73,6 +73,9 @@ def _load():
     lib.oracle_paged_prefill_attention.argtypes = [P] * 5 + [ctypes.c_int, P, P] + \
         [ctypes.c_int] * 5 + [f32, f32, f32, ctypes.c_int]
     lib.oracle_paged_prefill_attention.restype = None
+    lib.oracle_paged_prefill_attention_dynamic.argtypes = [P] * 7 + [ctypes.c_int, P, P] + \
+        [ctypes.c_int] * 4 + [f32, ctypes.c_int]
+    lib.oracle_paged_prefill_attention_dynamic.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -287,6 +290,30 @@ def paged_attention_decode_dynamic(q, k_pool: np.ndarray, v_pool: np.ndarray,
     _load().oracle_paged_attention_decode_dynamic(
         _ptr(out), _ptr(qb), _ptr(np.ascontiguousarray(k_pool)), _ptr(np.ascontiguousarray(v_pool)),
         _ptr(ks), _ptr(vs), _ptr(bt), bt.shape[1], _ptr(cl), B, Hq, num_kv_heads, D,
+        float(np.float32(sm_scale)), int(threads))
+    return out
+
+
+def paged_prefill_attention_dynamic(q, k_pool: np.ndarray, v_pool: np.ndarray,
+                                    k_scales: np.ndarray, v_scales: np.ndarray, block_tables,
+                                    context_lens, query_start, num_kv_heads: int,
+                                    sm_scale: float, threads: int = 0) -> np.ndarray:
+    """fp64 chunked-prefill attention over an FP8 pool with per-(block, head)
+    scales; arguments as paged_prefill_attention, scales [NB][Hkv] fp32."""
+    qb = _f16_bits(q)
+    R, Hq, D = qb.shape
+    assert Hq % num_kv_heads == 0
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    qs = np.ascontiguousarray(np.asarray(query_start, dtype=np.int32))
+    B = cl.shape[0]
+    assert bt.ndim == 2 and bt.shape[0] == B and qs.shape == (B + 1,) and qs[-1] == R
+    ks = np.ascontiguousarray(k_scales, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scales, dtype=np.float32)
+    out = np.empty((R, Hq, D), dtype=np.float64)
+    _load().oracle_paged_prefill_attention_dynamic(
+        _ptr(out), _ptr(qb), _ptr(np.ascontiguousarray(k_pool)), _ptr(np.ascontiguousarray(v_pool)),
+        _ptr(ks), _ptr(vs), _ptr(bt), bt.shape[1], _ptr(cl), _ptr(qs), B, Hq, num_kv_heads, D,
         float(np.float32(sm_scale)), int(threads))
     return out
 

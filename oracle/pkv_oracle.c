@@ -313,13 +313,14 @@ void oracle_paged_attention_decode_dynamic(double* out, const uint16_t* q, const
  * already in the cache, so the sequence holds L_b = context_lens[b] tokens.
  * Row i of the chunk sits at position p = L_b - n_b + i and attends, causally,
  * to the tokens 0..p of its sequence, with each KV head serving G = Hq / Hkv
- * query heads.  Plain softmax(sm_scale * q.k) v in fp64, tokens in order. */
-void oracle_paged_prefill_attention(double* out, const uint16_t* q, const uint8_t* k_pool,
-                                    const uint8_t* v_pool, const int32_t* block_tables,
-                                    int max_blocks, const int32_t* context_lens,
-                                    const int32_t* query_start, int B, int Hq, int Hkv, int D,
-                                    int fp8, float sm_scale, float k_scale, float v_scale,
-                                    int threads) {
+ * query heads.  Plain softmax(sm_scale * q.k) v in fp64, tokens in order.
+ * With k_bscales / v_bscales (FP8 only) each cached element stands for
+ * E4M3(code) * the scale of its own (block, kv head), as in decode. */
+static void orc_prefill(double* out, const uint16_t* q, const uint8_t* k_pool,
+                        const uint8_t* v_pool, const int32_t* block_tables, int max_blocks,
+                        const int32_t* context_lens, const int32_t* query_start, int B, int Hq,
+                        int Hkv, int D, int fp8, float sm_scale, float k_scale, float v_scale,
+                        const float* k_bscales, const float* v_bscales, int threads) {
   int G = Hq / Hkv;
   double kfac = fp8 ? (double)k_scale : 1.0;
   double vfac = fp8 ? (double)v_scale : 1.0;
@@ -354,9 +355,10 @@ void oracle_paged_prefill_attention(double* out, const uint16_t* q, const uint8_
     double m = -INFINITY;
     for (int64_t t = 0; t < cnt; ++t) {
       int64_t block = row[t / ORC_BS];
+      double kst = k_bscales ? (double)k_bscales[block * Hkv + kvh] : kfac;
       double dot = 0.0;
       for (int d = 0; d < D; ++d)
-        dot += qd[d] * orc_load(k_pool, 0, block, kvh, (int)(t % ORC_BS), d, Hkv, D, fp8, kfac);
+        dot += qd[d] * orc_load(k_pool, 0, block, kvh, (int)(t % ORC_BS), d, Hkv, D, fp8, kst);
       sc[t] = (double)sm_scale * dot;
       if (sc[t] > m)
         m = sc[t];
@@ -365,15 +367,40 @@ void oracle_paged_prefill_attention(double* out, const uint16_t* q, const uint8_
     for (int64_t t = 0; t < cnt; ++t) {
       int64_t blk = row[t / ORC_BS];
       double w = exp(sc[t] - m);
+      double vst = v_bscales ? (double)v_bscales[blk * Hkv + kvh] : vfac;
       wsum += w;
       for (int d = 0; d < D; ++d)
-        o[d] += w * orc_load(v_pool, 1, blk, kvh, (int)(t % ORC_BS), d, Hkv, D, fp8, vfac);
+        o[d] += w * orc_load(v_pool, 1, blk, kvh, (int)(t % ORC_BS), d, Hkv, D, fp8, vst);
     }
     for (int d = 0; d < D; ++d)
       o[d] /= wsum;
     free(qd);
     free(sc);
   }
+}
+
+void oracle_paged_prefill_attention(double* out, const uint16_t* q, const uint8_t* k_pool,
+                                    const uint8_t* v_pool, const int32_t* block_tables,
+                                    int max_blocks, const int32_t* context_lens,
+                                    const int32_t* query_start, int B, int Hq, int Hkv, int D,
+                                    int fp8, float sm_scale, float k_scale, float v_scale,
+                                    int threads) {
+  orc_prefill(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, query_start, B, Hq,
+              Hkv, D, fp8, sm_scale, k_scale, v_scale, NULL, NULL, threads);
+}
+
+/* Chunked prefill over an FP8 pool whose (block, kv head) tiles carry their
+ * own K and V scales ([FP8-128K] §5 chunked prefill over the cache of §8's
+ * dynamic scaling). */
+void oracle_paged_prefill_attention_dynamic(double* out, const uint16_t* q,
+                                            const uint8_t* k_pool, const uint8_t* v_pool,
+                                            const float* k_bscales, const float* v_bscales,
+                                            const int32_t* block_tables, int max_blocks,
+                                            const int32_t* context_lens,
+                                            const int32_t* query_start, int B, int Hq, int Hkv,
+                                            int D, float sm_scale, int threads) {
+  orc_prefill(out, q, k_pool, v_pool, block_tables, max_blocks, context_lens, query_start, B, Hq,
+              Hkv, D, 1, sm_scale, 1.0f, 1.0f, k_bscales, v_bscales, threads);
 }
 
 /* ------------------------------------------------- write with block scales */

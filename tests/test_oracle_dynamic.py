@@ -256,3 +256,79 @@ def test_uniform_block_scales_equal_the_per_tensor_decode(orc):
                                              bt, lens, Hkv, sm)
     ref = orc.paged_attention_decode(q, kp, vp, bt, lens, Hkv, True, sm, s, s)
     assert np.array_equal(got, ref)
+
+
+# ------------------------------------------- chunked prefill over block scales
+
+def _rebuilt_rows(orc, kp, vp, ks, vs, bt, b, L, Hkv):
+    """Sequence b's K and V [Hkv][L][D] from the pool bytes, through the layout
+    and the library's E4M3 view, each times its own (block, head) scale."""
+    koff, voff = _offsets(orc)
+    K = np.zeros((Hkv, L, D))
+    V = np.zeros((Hkv, L, D))
+    for t in range(L):
+        blk = int(bt[b, t // BS])
+        for h in range(Hkv):
+            K[h, t] = _value(_rows(kp, koff, blk, h, Hkv)[t % BS]) * float(ks[blk, h])
+            V[h, t] = _value(_rows(vp, voff, blk, h, Hkv)[t % BS]) * float(vs[blk, h])
+    return K, V
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (6, 3)])
+def test_prefill_with_block_scales_matches_library_sdpa(orc, Hq, Hkv):
+    """Each sequence's last chunk attends causally over rows rebuilt with their
+    own block's scales, in torch SDPA with an explicit causal mask."""
+    rng = np.random.default_rng(40 + Hq)
+    lens = [1, 16, 17, 40, 75]
+    n = [1, 5, 17, 0, 40]                       # whole sequences, ragged, empty
+    kp, vp, ks, vs, bt = _dynamic_sequences(orc, rng, lens, Hkv, 32)
+    assert len(np.unique(vs)) > 8
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = rng.standard_normal((int(qs[-1]), Hq, D)).astype(np.float16)
+    sm = np.float32(1 / math.sqrt(D))
+    got = orc.paged_prefill_attention_dynamic(q, kp, vp, ks, vs, bt, lens, qs, Hkv, sm)
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        if n[b] == 0:
+            continue
+        K, V = _rebuilt_rows(orc, kp, vp, ks, vs, bt, b, L, Hkv)
+        k = torch.from_numpy(K).repeat_interleave(G, dim=0)
+        v = torch.from_numpy(V).repeat_interleave(G, dim=0)
+        qq = torch.from_numpy(q[qs[b]:qs[b + 1]].astype(np.float64)).permute(1, 0, 2)
+        pos = L - n[b] + np.arange(n[b])
+        mask = torch.from_numpy(np.arange(L)[None, :] <= pos[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0), attn_mask=mask,
+            scale=float(sm))[0].permute(1, 0, 2).numpy()
+        assert np.max(np.abs(got[qs[b]:qs[b + 1]] - ref)) < 1e-12
+
+
+def test_prefill_with_block_scales_rows_are_the_dynamic_decode_of_their_prefix(orc):
+    rng = np.random.default_rng(41)
+    lens, Hkv, Hq = [37, 64], 2, 8
+    kp, vp, ks, vs, bt = _dynamic_sequences(orc, rng, lens, Hkv, 16)
+    n = [20, 64]
+    qs = np.array([0, 20, 84], np.int32)
+    q = rng.standard_normal((84, Hq, D)).astype(np.float16)
+    sm = np.float32(0.09)
+    got = orc.paged_prefill_attention_dynamic(q, kp, vp, ks, vs, bt, lens, qs, Hkv, sm)
+    for b, L in enumerate(lens):
+        for i in range(n[b]):
+            r, p = qs[b] + i, L - n[b] + i
+            dec = orc.paged_attention_decode_dynamic(q[r:r + 1], kp, vp, ks, vs, bt[b:b + 1],
+                                                     [p + 1], Hkv, sm)
+            assert np.array_equal(got[r], dec[0])
+
+
+def test_prefill_with_uniform_block_scales_equals_the_per_tensor_prefill(orc):
+    rng = np.random.default_rng(42)
+    Hkv, lens = 2, [5, 33, 64]
+    kp, vp, ks, vs, bt = _dynamic_sequences(orc, rng, lens, Hkv, 16)
+    qs = np.array([0, 5, 15, 79], np.int32)
+    q = rng.standard_normal((79, 8, D)).astype(np.float16)
+    sm = np.float32(1 / math.sqrt(D))
+    sk, sv = np.float32(0.0173), np.float32(0.031)
+    got = orc.paged_prefill_attention_dynamic(q, kp, vp, np.full_like(ks, sk),
+                                              np.full_like(vs, sv), bt, lens, qs, Hkv, sm)
+    ref = orc.paged_prefill_attention(q, kp, vp, bt, lens, qs, Hkv, True, sm, sk, sv)
+    assert np.array_equal(got, ref)

@@ -65,6 +65,11 @@ MUTATIONS = [
     ("prefill GQA mapping", "kvh = h / G;", "kvh = h % Hkv;"),
     ("prefill drops the V scale", "double vfac = fp8 ? (double)v_scale : 1.0;", "double vfac = 1.0;"),
     ("prefill normaliser squared", "wsum += w;", "wsum += w * w;"),
+    # chunked prefill over per-block scales
+    ("prefill block scale ignores the head", "(double)k_bscales[block * Hkv + kvh]",
+     "(double)k_bscales[block * Hkv]"),
+    ("prefill V read with the K block scale", "(double)v_bscales[blk * Hkv + kvh]",
+     "(double)k_bscales[blk * Hkv + kvh]"),
 ]
 
 
@@ -91,6 +96,7 @@ def _pins(orc):
         ("dyn sdpa", lambda: tdy.test_decode_with_block_scales_matches_library_sdpa(orc, 8, 2)),
         ("prefill sdpa fp8", lambda: tpf.test_prefill_matches_library_sdpa_with_causal_mask(orc, True, 8, 2)),
         ("prefill causality", lambda: tpf.test_future_tokens_do_not_leak(orc)),
+        ("prefill dyn sdpa", lambda: tdy.test_prefill_with_block_scales_matches_library_sdpa(orc, 8, 2)),
     ]
     for name, fn in checks:
         try:
