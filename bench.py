@@ -147,14 +147,29 @@ def run_prefill(args) -> int:
     for i, r in enumerate(rows):
         tables[i, :len(r)] = r
     Te, Tc = len(early), len(chunk)
+    dyn = args.kv_scales == "block"
+    if dyn and not wl.fp8:
+        print("bench.py: per-block scales apply to FP8 caches only", file=sys.stderr)
+        return 2
     ks, vs = (0.011, 0.013) if wl.fp8 else (1.0, 1.0)   # N(0,1) rows stay far below 448 * scale
     k_pool = torch.zeros(pkv.pkv_pool_bytes(layout), dtype=torch.uint8, device=dev)
     v_pool = torch.zeros_like(k_pool)
+    if dyn:   # per-(block, KV head) scales, measured as the cache is written
+        k_bs = torch.zeros((wl.num_blocks, Hkv), dtype=torch.float32, device=dev)
+        v_bs = torch.zeros_like(k_bs)
+        ws = torch.empty(pkv.pkv_reshape_dynamic_workspace_bytes(layout), dtype=torch.uint8,
+                         device=dev)
+
+    def write(k, v, slots):
+        if dyn:
+            pkv.pkv_reshape_and_cache_dynamic(k, v, k_pool, v_pool, k_bs, v_bs, slots, layout, ws)
+        else:
+            pkv.pkv_reshape_and_cache(k, v, k_pool, v_pool, slots, layout, ks, vs)
+
     if Te:
-        pkv.pkv_reshape_and_cache(workloads.randn_f16((Te, Hkv, D), 401, dev),
-                                  workloads.randn_f16((Te, Hkv, D), 402, dev), k_pool, v_pool,
-                                  torch.from_numpy(np.asarray(early, np.int64)).to(dev), layout,
-                                  ks, vs)
+        write(workloads.randn_f16((Te, Hkv, D), 401, dev),
+              workloads.randn_f16((Te, Hkv, D), 402, dev),
+              torch.from_numpy(np.asarray(early, np.int64)).to(dev))
     new_k = workloads.randn_f16((Tc, Hkv, D), 403, dev)
     new_v = workloads.randn_f16((Tc, Hkv, D), 404, dev)
     q = workloads.randn_f16((Tc, Hq, D), 405, dev)
@@ -167,11 +182,15 @@ def run_prefill(args) -> int:
     maxq, maxl = int(wl.chunk_lens.max()), int(wl.context_lens.max())
 
     def step(ev=None):
-        pkv.pkv_reshape_and_cache(new_k, new_v, k_pool, v_pool, d_chunk, layout, ks, vs)
+        write(new_k, new_v, d_chunk)
         if ev is not None:
             ev[0].record()
-        pkv.pkv_paged_prefill_attention(out, q, k_pool, v_pool, d_tables, d_lens, d_qs, maxq,
-                                        maxl, layout, sm, ks, vs)
+        if dyn:
+            pkv.pkv_paged_prefill_attention_dynamic(out, q, k_pool, v_pool, k_bs, v_bs, d_tables,
+                                                    d_lens, d_qs, maxq, maxl, layout, sm)
+        else:
+            pkv.pkv_paged_prefill_attention(out, q, k_pool, v_pool, d_tables, d_lens, d_qs, maxq,
+                                            maxl, layout, sm, ks, vs)
         if ev is not None:
             ev[1].record()
 
@@ -210,14 +229,24 @@ def run_prefill(args) -> int:
         pos = np.arange(L)
         slots = sl[pos // 16] * 16 + pos % 16
         src = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
-        oracle.reshape_and_cache(src, src, kh, vh, slots, Hkv, wl.fp8, ks, vs)
+        if dyn:
+            ksh = np.zeros((wl.num_blocks, Hkv), np.float32)
+            vsh = np.zeros_like(ksh)
+            oracle.reshape_and_cache_dynamic(src, src, kh, vh, ksh, vsh, slots, Hkv)
+        else:
+            oracle.reshape_and_cache(src, src, kh, vh, slots, Hkv, wl.fp8, ks, vs)
         qh = rng.standard_normal((S, Hq, D), dtype=np.float32).astype(np.float16)
         threads = min(os.cpu_count() or 1, 16)
         ps = [L - 1 - 97 * i for i in range(S)]
         t = time.perf_counter()
         for i, p in enumerate(ps):
-            oracle.paged_prefill_attention(qh[i:i + 1], kh, vh, tables[b:b + 1], [p + 1], [0, 1],
-                                           Hkv, wl.fp8, sm, ks, vs, threads)
+            if dyn:
+                oracle.paged_prefill_attention_dynamic(qh[i:i + 1], kh, vh, ksh, vsh,
+                                                       tables[b:b + 1], [p + 1], [0, 1], Hkv, sm,
+                                                       threads)
+            else:
+                oracle.paged_prefill_attention(qh[i:i + 1], kh, vh, tables[b:b + 1], [p + 1],
+                                               [0, 1], Hkv, wl.fp8, sm, ks, vs, threads)
         cpu_s = time.perf_counter() - t
         sample_flops = sum(p + 1 for p in ps) * Hq * 4 * D
         cpu = {"value": round(sample_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
@@ -242,13 +271,17 @@ def run_prefill(args) -> int:
                    "seq_len": maxl, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
                    "block_size": 16, "pool_blocks": wl.num_blocks,
                    "kv_dtype": "fp8_e4m3fn" if wl.fp8 else "f16",
+                   "kv_scales": ("per (block, kv head)" if dyn else "per tensor") if wl.fp8
+                   else None,
                    "arith": "f16 MFMA inputs, f32 accumulate, f16 probabilities",
                    "parallelism": "single GPU"},
         "flops_per_step": flops,
         "prefill_attention_ms": round(attn_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4),
-                     "traffic": measured_traffic("prefill_" + args.workload, PREFILL_SRCS)},
+                     "traffic": measured_traffic("prefill_" + args.workload +
+                                                 ("_block_scales" if dyn else ""),
+                                                 PREFILL_SRCS)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -306,6 +306,20 @@ pkv_status pkv_paged_attention_decode_dynamic(
     int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale,
     int32_t partition_size, void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* Chunked prefill over an FP8 pool with per-block scales ([FP8-128K] §5 over
+ * the cache of §8): as pkv_paged_prefill_attention, with each tile's K and V
+ * scale read from the arrays in place of the per-tensor scales.  Within a
+ * workgroup the probabilities of a tile are multiplied by its V scale over
+ * the largest V scale met so far before rounding to fp16.  No workspace;
+ * PKV_ERR_UNSUPPORTED for fp16 pools, PKV_ERR_INVALID_ARG for a null scale
+ * array. */
+pkv_status pkv_paged_prefill_attention_dynamic(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const float* k_block_scales, const float* v_block_scales, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* query_start,
+    int32_t num_seqs, int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
+    const pkv_cache_layout* layout, float sm_scale, void* stream);
+
 /* pkv_copy_blocks for a pool with per-block scales: the destination also
  * takes the source's scale rows (copy-on-write of a partly filled block). */
 pkv_status pkv_copy_blocks_dynamic(void* k_pool, void* v_pool, float* k_block_scales,

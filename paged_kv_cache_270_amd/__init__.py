@@ -19,7 +19,7 @@ __all__ = [
     "pkv_paged_attention_decode", "pkv_decode_partitions", "pkv_decode_reduce",
     "pkv_copy_blocks", "pkv_reshape_dynamic_workspace_bytes", "pkv_reshape_and_cache_dynamic",
     "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic", "pkv_paged_prefill_attention",
-    "pkv_swap_blocks",
+    "pkv_paged_prefill_attention_dynamic", "pkv_swap_blocks",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -94,6 +94,8 @@ def load_library():
         "pkv_copy_blocks_dynamic": ([P, P, P, P, LP, P, i32, P], i32),
         "pkv_paged_prefill_attention": ([P, P, P, P, P, i32, P, P, i32, i32, i32, i32, LP, f32,
                                          f32, f32, P], i32),
+        "pkv_paged_prefill_attention_dynamic": ([P, P, P, P, P, P, P, i32, P, P, i32, i32, i32,
+                                                 i32, LP, f32, P], i32),
         "pkv_swap_blocks": ([P, P, P, P, i32, LP, P, i32, i32, P], i32),
         "pkv_pool_set_swap_space": ([P, i32], i32),
         "pkv_pool_num_free_host": ([P], i32),
@@ -305,12 +307,7 @@ def pkv_swap_blocks(k_pool, v_pool, host_k, host_v, num_host_blocks: int, layout
 
 # ------------------------------------------------------ chunked prefill
 
-def pkv_paged_prefill_attention(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
-                                max_query_len: int, max_context_len: int, layout: CacheLayout,
-                                sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-                                stream=None) -> None:
-    """Causal attention of each sequence's last chunk of tokens (rows
-    query_start[b] .. query_start[b+1]-1 of q) over the paged cache."""
+def _prefill_args(out, q, block_tables, context_lens, query_start):
     import torch
     _require(out, torch.float32, "out")
     _require(q, torch.float16, "q")
@@ -322,6 +319,16 @@ def pkv_paged_prefill_attention(out, q, k_pool, v_pool, block_tables, context_le
         raise ValueError("q and out must be [rows][num_q_heads][head_dim]")
     if query_start.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("query_start must be [B + 1], block_tables [B][max_blocks]")
+    return B
+
+
+def pkv_paged_prefill_attention(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                                max_query_len: int, max_context_len: int, layout: CacheLayout,
+                                sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                                stream=None) -> None:
+    """Causal attention of each sequence's last chunk of tokens (rows
+    query_start[b] .. query_start[b+1]-1 of q) over the paged cache."""
+    B = _prefill_args(out, q, block_tables, context_lens, query_start)
     _check(load_library().pkv_paged_prefill_attention(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(query_start), B, q.shape[1],
@@ -381,6 +388,21 @@ def pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_block_scales, v
         _hint(shared_prefix_blocks, B), B, Hq, max_context_len, ctypes.byref(layout), sm_scale,
         partition_size, _ptr(workspace), nbytes, _stream(stream)),
         "pkv_paged_attention_decode_dynamic")
+
+
+def pkv_paged_prefill_attention_dynamic(out, q, k_pool, v_pool, k_block_scales, v_block_scales,
+                                        block_tables, context_lens, query_start,
+                                        max_query_len: int, max_context_len: int,
+                                        layout: CacheLayout, sm_scale: float,
+                                        stream=None) -> None:
+    """Chunked prefill over an FP8 pool with per-(block, head) scales."""
+    B = _prefill_args(out, q, block_tables, context_lens, query_start)
+    _block_scales(k_block_scales, v_block_scales, layout)
+    _check(load_library().pkv_paged_prefill_attention_dynamic(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_block_scales),
+        _ptr(v_block_scales), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        _ptr(query_start), B, q.shape[1], max_query_len, max_context_len, ctypes.byref(layout),
+        sm_scale, _stream(stream)), "pkv_paged_prefill_attention_dynamic")
 
 
 def pkv_copy_blocks_dynamic(k_pool, v_pool, k_block_scales, v_block_scales, layout: CacheLayout,

@@ -58,8 +58,10 @@ struct PrefillArgs {
   int32_t num_blocks;
   int32_t hq, hkv, g;
   int32_t max_ctx;
-  float qk_scale;               // sm_scale * k_scale * log2(e)
-  float out_scale;              // v_scale
+  float qk_scale;               // sm_scale * k_scale * log2(e) (per-block scales: no k_scale)
+  float out_scale;              // v_scale (per-block scales: unused)
+  const float* k_bscale;        // [num_blocks][hkv] per-block K scales, or null
+  const float* v_bscale;        // [num_blocks][hkv] per-block V scales, or null
 };
 
 struct RowState {
@@ -109,14 +111,20 @@ __device__ __forceinline__ f16x8 v_operand(const TileRegs<kFP8>& ta, const TileR
 
 // One pair of tiles (tokens tb .. tb+31) for the wave's query heads.
 // pos_j: position of this lane's query row.  masked: the pair reaches past
-// the workgroup's first position, so tokens after pos_j are dropped.  The
-// logit scale qk_scale is positive, so a row's largest logit is qk_scale
-// times its largest dot product.
-template <bool kFP8>
+// the workgroup's first position, so tokens after pos_j are dropped.  qk[t]
+// is tile t's logit scale (per-block scales: times the tile's K scale); it
+// is positive, so a row's largest logit is qk times its largest dot product.
+// With per-block scales (kDyn) tile t's probabilities are also multiplied by
+// vmul[t], its V scale relative to the wave's reference, and taken as fp16
+// hi + lo (two PV products, about 22 bits): dynamic scales are for values
+// with outliers, where one fp16 rounding of P is too coarse against the
+// absolute tolerance.  The normaliser sums the unscaled probabilities.
+template <bool kFP8, bool kDyn = false>
 __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb_,
                                              const f16x8 (&qop)[kHeadsPerWave][4],
                                              RowState (&st)[kHeadsPerWave], int tb, int qg,
-                                             int pos_j, int L, bool masked, float qk_scale) {
+                                             int pos_j, int L, bool masked, const float (&qk)[2],
+                                             const float (&vmul)[2]) {
   if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
     __asm__ volatile("" ::: "memory");  // keep this rare path a branch
     mask_tail_values<kFP8>(ta, tb, qg, L);
@@ -150,14 +158,14 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
       }
     }
   }
-  f16x8 p[kHeadsPerWave];
+  f16x8 p[kHeadsPerWave], plo[kHeadsPerWave];
 #pragma unroll
   for (int h = 0; h < kHeadsPerWave; ++h) {
     // exponent of each weight relative to the reference max (log2 units)
     float y[8];
     const float neg_m = -st[h].m_ref;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk_scale, neg_m);
+    for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk[r >> 2], neg_m);
     float ymax = y[0];
 #pragma unroll
     for (int r = 1; r < 8; ++r) ymax = fmaxf(ymax, y[r]);
@@ -166,7 +174,7 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
       // the row's new reference: its largest logit so far
       float top = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) top = fmaxf(top, s[h][r >> 2][r & 3] * qk_scale);
+      for (int r = 0; r < 8; ++r) top = fmaxf(top, s[h][r >> 2][r & 3] * qk[r >> 2]);
       top = fmaxf(top, __shfl_xor(top, 16, kWave));
       top = fmaxf(top, __shfl_xor(top, 32, kWave));
       const float m_upd = fmaxf(st[h].m_ref, top);
@@ -176,22 +184,34 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
       for (int n = 0; n < 8; ++n) st[h].acc[n] *= alpha;
       st[h].m_ref = m_upd;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk_scale, -m_upd);
+      for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk[r >> 2], -m_upd);
     }
     float e[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(y[r]);
     st[h].l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    if constexpr (kDyn) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
+      for (int r = 0; r < 8; ++r) {
+        const float w = e[r] * vmul[r >> 2];
+        p[h][r] = (_Float16)w;
+        plo[h][r] = (_Float16)(w - (float)p[h][r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
+    }
   }
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const f16x8 v = v_operand<kFP8>(ta, tb_, n);
 #pragma unroll
-    for (int h = 0; h < kHeadsPerWave; ++h)
+    for (int h = 0; h < kHeadsPerWave; ++h) {
       st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
+      if constexpr (kDyn)
+        st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, plo[h], st[h].acc[n], 0, 0, 0);
+    }
   }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -234,11 +254,24 @@ __device__ __forceinline__ void load_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb
   }
 }
 
+// The K and V scales of a pair's two (block, head) tiles; ids outside the
+// pool read as 0 (their tiles are zeros).
+__device__ __forceinline__ void pair_scales(const PrefillArgs& a, int pa, int pb, int kvh,
+                                            float (&sk)[2], float (&sv)[2]) {
+  const bool oka = (unsigned)pa < (unsigned)a.num_blocks;
+  const bool okb = (unsigned)pb < (unsigned)a.num_blocks;
+  sk[0] = oka ? a.k_bscale[(int64_t)pa * a.hkv + kvh] : 0.0f;
+  sv[0] = oka ? a.v_bscale[(int64_t)pa * a.hkv + kvh] : 0.0f;
+  sk[1] = okb ? a.k_bscale[(int64_t)pb * a.hkv + kvh] : 0.0f;
+  sv[1] = okb ? a.v_bscale[(int64_t)pb * a.hkv + kvh] : 0.0f;
+}
+
 // Grid (ceil(max chunk / 16), Hkv, B); ceil(G / 2) waves per workgroup.
 // Lane (j = lane % 16, qg = lane / 16) serves chunk row 16 * blockIdx.x + j of
-// the wave's two query heads.
-template <bool kFP8>
+// the wave's two query heads.  kDyn: FP8 pool with per-block scales.
+template <bool kFP8, bool kDyn = false>
 __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
+  static_assert(kFP8 || !kDyn, "per-block scales are for FP8 pools");
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int j = lane & 15, qg = lane >> 4;
@@ -282,6 +315,9 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
   // its max is finite
   const int pos_c = pos < 0 ? 0 : (pos > L - 1 ? L - 1 : pos);
   const int ntiles = last >= 0 ? last / kBS + 1 : 0;
+  const float qk_one[2] = {a.qk_scale, a.qk_scale}, v_one[2] = {1.0f, 1.0f};
+  float vref = 0.0f;  // per-block scales: the largest V scale seen so far
+  float inv_vref = 0.0f;
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
   for (int c0 = 0; c0 < ntiles; c0 += kWave) {
     const int cnt = min(kWave, ntiles - c0);
@@ -298,17 +334,19 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
         }
         const int tok0 = (c0 + t) * kBS;
         process_pair<kFP8>(ta, tb, qop, st, tok0, qg, pos_c, L, tok0 + 2 * kBS - 1 > first,
-                           a.qk_scale);
+                           qk_one, v_one);
       }
       continue;
     }
     // FP8: two pairs in flight, the next pair's loads issued before the
     // current pair is computed
     TileRegs<kFP8> buf[2][2];
+    float bsk[2][2], bsv[2][2];  // per-block scales of the pairs in buf (kDyn)
     {
       const int pa = __builtin_amdgcn_readlane(tbl, 0);
       const int pb = cnt > 1 ? __builtin_amdgcn_readlane(tbl, 1) : pa;
       load_pair<kFP8>(buf[0][0], buf[0][1], a, pa, pb, kvh, lane);
+      if constexpr (kDyn) pair_scales(a, pa, pb, kvh, bsk[0], bsv[0]);
     }
     for (int t = 0; t < cnt; t += 4) {
 #pragma unroll
@@ -319,14 +357,37 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
             const int pa = __builtin_amdgcn_readlane(tbl, tt + 2);
             const int pb = tt + 3 < cnt ? __builtin_amdgcn_readlane(tbl, tt + 3) : pa;
             load_pair<kFP8>(buf[u ^ 1][0], buf[u ^ 1][1], a, pa, pb, kvh, lane);
+            if constexpr (kDyn) pair_scales(a, pa, pb, kvh, bsk[u ^ 1], bsv[u ^ 1]);
           }
           if (tt + 1 >= cnt) {              // past the last tile: all masked below
             __asm__ volatile("" ::: "memory");
             zero_tile<kFP8>(buf[u][1]);
           }
           const int tok0 = (c0 + tt) * kBS;
-          process_pair<kFP8>(buf[u][0], buf[u][1], qop, st, tok0, qg, pos_c, L,
-                             tok0 + 2 * kBS - 1 > first, a.qk_scale);
+          if constexpr (kDyn) {
+            // the accumulators hold sum p * (V scale / vref) * code: when a
+            // tile's V scale exceeds the reference, rescale them to the new one
+            const float ref = fmaxf(fmaxf(vref, fmaxf(bsv[u][0], bsv[u][1])), 0x1p-126f);
+            if (ref > vref) {  // wave-uniform, rare
+              __asm__ volatile("" ::: "memory");
+              if (vref > 0.0f) {
+                const float f = vref / ref;
+#pragma unroll
+                for (int h = 0; h < kHeadsPerWave; ++h)
+#pragma unroll
+                  for (int nn = 0; nn < 8; ++nn) st[h].acc[nn] *= f;
+              }
+              vref = ref;
+              inv_vref = 1.0f / ref;
+            }
+            const float qk[2] = {a.qk_scale * bsk[u][0], a.qk_scale * bsk[u][1]};
+            const float vm[2] = {bsv[u][0] * inv_vref, bsv[u][1] * inv_vref};
+            process_pair<kFP8, true>(buf[u][0], buf[u][1], qop, st, tok0, qg, pos_c, L,
+                                     tok0 + 2 * kBS - 1 > first, qk, vm);
+          } else {
+            process_pair<kFP8>(buf[u][0], buf[u][1], qop, st, tok0, qg, pos_c, L,
+                               tok0 + 2 * kBS - 1 > first, qk_one, v_one);
+          }
         }
       }
     }
@@ -339,7 +400,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
     float l = st[h].l;
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
-    const float f = pos < 0 ? 0.0f : a.out_scale / l;
+    const float f = pos < 0 ? 0.0f : (kDyn ? vref : a.out_scale) / l;
     float* o = a.out + ((int64_t)(q0 + i) * a.hq + h0 + h) * kD;
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn)
@@ -347,14 +408,16 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
   }
 }
 
-}  // namespace
-
-extern "C" pkv_status pkv_paged_prefill_attention(
-    float* out, const void* q, const void* k_pool, const void* v_pool,
-    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* query_start, int32_t num_seqs, int32_t num_q_heads, int32_t max_query_len,
-    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
-    float v_scale, void* stream) {
+// Argument checks and kernel arguments shared by both entry points; with
+// per-block scales (k_bscale non-null) the per-tensor scales are not used.
+pkv_status plan_prefill(float* out, const void* q, const void* k_pool, const void* v_pool,
+                        const float* k_bscale, const float* v_bscale,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, const int32_t* query_start,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t max_query_len,
+                        int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale,
+                        float k_scale, float v_scale, PrefillArgs& a, bool& empty) {
+  empty = false;
   const pkv_status st = check_layout(layout);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_seqs > 65535 || num_q_heads <= 0 || max_query_len < 0 ||
@@ -363,18 +426,24 @@ extern "C" pkv_status pkv_paged_prefill_attention(
   if (num_q_heads % layout->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   const int32_t G = num_q_heads / layout->num_kv_heads;
   if (G > kMaxG) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+  const bool fp8 = layout->dtype == PKV_FP8_E4M3FN;
+  const bool dyn = k_bscale != nullptr;
+  if (dyn && !fp8) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_query_len == 0) {
+    empty = true;
+    return PKV_OK;
+  }
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return PKV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
     return PKV_ERR_INVALID_ARG;
+  if (dyn && (!v_bscale || !aligned(k_bscale, 4) || !aligned(v_bscale, 4)))
+    return PKV_ERR_INVALID_ARG;
   if (max_blocks_per_seq <= 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.0f))
     return PKV_ERR_INVALID_ARG;
-  const bool fp8 = layout->dtype == PKV_FP8_E4M3FN;
-  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
-               v_scale > 0.0f))
+  if (fp8 && !dyn &&
+      !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
     return PKV_ERR_INVALID_ARG;
-  PrefillArgs a;
   a.out = out;
   a.q = static_cast<const _Float16*>(q);
   a.k_pool = static_cast<const uint8_t*>(k_pool);
@@ -388,16 +457,58 @@ extern "C" pkv_status pkv_paged_prefill_attention(
   a.hkv = layout->num_kv_heads;
   a.g = G;
   a.max_ctx = max_context_len;
-  a.qk_scale = sm_scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
-  a.out_scale = fp8 ? v_scale : 1.0f;
-  const int waves = (G + kHeadsPerWave - 1) / kHeadsPerWave;
-  const dim3 grid((unsigned)((max_query_len + kQT - 1) / kQT), (unsigned)layout->num_kv_heads,
+  a.qk_scale = sm_scale * (fp8 && !dyn ? k_scale : 1.0f) * 1.4426950408889634f;
+  a.out_scale = fp8 && !dyn ? v_scale : 1.0f;
+  a.k_bscale = dyn ? k_bscale : nullptr;
+  a.v_bscale = dyn ? v_bscale : nullptr;
+  return PKV_OK;
+}
+
+template <bool kFP8, bool kDyn>
+pkv_status launch_prefill(const PrefillArgs& a, int32_t max_query_len, int32_t num_seqs,
+                          void* stream) {
+  const int waves = (a.g + kHeadsPerWave - 1) / kHeadsPerWave;
+  const dim3 grid((unsigned)((max_query_len + kQT - 1) / kQT), (unsigned)a.hkv,
                   (unsigned)num_seqs);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (fp8)
-    prefill_kernel<true><<<grid, dim3(waves * kWave), 0, s>>>(a);
-  else
-    prefill_kernel<false><<<grid, dim3(waves * kWave), 0, s>>>(a);
+  prefill_kernel<kFP8, kDyn>
+      <<<grid, dim3(waves * kWave), 0, static_cast<hipStream_t>(stream)>>>(a);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_prefill_attention(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* query_start, int32_t num_seqs, int32_t num_q_heads, int32_t max_query_len,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, void* stream) {
+  PrefillArgs a;
+  bool empty;
+  const pkv_status st = plan_prefill(out, q, k_pool, v_pool, nullptr, nullptr, block_tables,
+                                     max_blocks_per_seq, context_lens, query_start, num_seqs,
+                                     num_q_heads, max_query_len, max_context_len, layout,
+                                     sm_scale, k_scale, v_scale, a, empty);
+  if (st != PKV_OK || empty) return st;
+  return layout->dtype == PKV_FP8_E4M3FN
+             ? launch_prefill<true, false>(a, max_query_len, num_seqs, stream)
+             : launch_prefill<false, false>(a, max_query_len, num_seqs, stream);
+}
+
+extern "C" pkv_status pkv_paged_prefill_attention_dynamic(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const float* k_block_scales, const float* v_block_scales, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* query_start,
+    int32_t num_seqs, int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
+    const pkv_cache_layout* layout, float sm_scale, void* stream) {
+  if (!k_block_scales || !v_block_scales) return PKV_ERR_INVALID_ARG;
+  PrefillArgs a;
+  bool empty;
+  const pkv_status st = plan_prefill(out, q, k_pool, v_pool, k_block_scales, v_block_scales,
+                                     block_tables, max_blocks_per_seq, context_lens,
+                                     query_start, num_seqs, num_q_heads, max_query_len,
+                                     max_context_len, layout, sm_scale, 1.0f, 1.0f, a, empty);
+  if (st != PKV_OK || empty) return st;
+  return launch_prefill<true, true>(a, max_query_len, num_seqs, stream);
 }

@@ -150,3 +150,30 @@ def test_dynamic_scale_entry_points_validate_before_launch():
     assert c(16, 16, 16, 16, ctypes.byref(f16), 16, 1, None) == pkv.PKV_ERR_UNSUPPORTED
     assert c(16, 16, None, 16, ctypes.byref(small8), 16, 1, None) == pkv.PKV_ERR_INVALID_ARG
     assert c(None, None, None, None, ctypes.byref(small8), None, 0, None) == pkv.PKV_OK
+
+
+def test_prefill_entry_points_validate_before_launch():
+    """Every call here is rejected (or is a no-op) before any HIP call."""
+    L = pkv.load_library()
+    f8 = pkv.CacheLayout(16, 2, pkv.PKV_FP8_E4M3FN)
+    f16 = pkv.CacheLayout(16, 2, pkv.PKV_F16)
+    pre = L.pkv_paged_prefill_attention
+    # out, q, k, v, tables, max_blocks, lens, query_start, B, Hq, max_q, max_ctx, layout, sm, ks, vs
+    assert pre(16, 16, 16, 16, 16, 4, 16, 16, 2, 4, 32, 64, ctypes.byref(f8), 0.0, 1.0, 1.0,
+               None) == pkv.PKV_ERR_INVALID_ARG          # sm_scale must be > 0
+    assert pre(16, 16, 16, 16, 16, 4, 16, 16, 2, 4, 32, 64, ctypes.byref(f8), 0.1, -1.0, 1.0,
+               None) == pkv.PKV_ERR_INVALID_ARG          # FP8 scales must be > 0
+    assert pre(16, 16, 16, 16, 16, 4, 16, 16, 2, 64, 32, 64, ctypes.byref(f8), 0.1, 1.0, 1.0,
+               None) == pkv.PKV_ERR_UNSUPPORTED          # group of 32 query heads
+    assert pre(None, None, None, None, None, 4, None, None, 0, 4, 32, 64, ctypes.byref(f8), 0.1,
+               1.0, 1.0, None) == pkv.PKV_OK            # no sequences: nothing to do
+    dyn = L.pkv_paged_prefill_attention_dynamic
+    # out, q, k, v, ks, vs, tables, max_blocks, lens, query_start, B, Hq, max_q, max_ctx, layout, sm
+    assert dyn(16, 16, 16, 16, 16, 16, 16, 4, 16, 16, 2, 4, 32, 64, ctypes.byref(f16), 0.1,
+               None) == pkv.PKV_ERR_UNSUPPORTED          # fp16 pools carry no scales
+    assert dyn(16, 16, 16, 16, None, 16, 16, 4, 16, 16, 2, 4, 32, 64, ctypes.byref(f8), 0.1,
+               None) == pkv.PKV_ERR_INVALID_ARG
+    assert dyn(16, 16, 16, 16, 16, 6, 16, 4, 16, 16, 2, 4, 32, 64, ctypes.byref(f8), 0.1,
+               None) == pkv.PKV_ERR_INVALID_ARG          # misaligned V scales
+    assert dyn(None, None, None, None, 16, 16, None, 4, None, None, 0, 4, 32, 64,
+               ctypes.byref(f8), 0.1, None) == pkv.PKV_OK

@@ -225,3 +225,53 @@ def test_llama70b_shape_bulk_fill_then_growing_steps():
     err = max_err(out[sample].cpu().numpy(), ref)
     print(f"[parity] dynamic 70B shape (sampled): max abs err {err:.3e}", flush=True)
     assert err <= TOL[True]
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (6, 2), (16, 1), (4, 4)])
+def test_prefill_with_block_scales_matches_oracle(hq, hkv):
+    """Chunked prefill over a pool written by the dynamic write: ragged and
+    empty chunks, whole-sequence chunks, garbage (NaN codes, stale scales) in
+    unwritten slots and past each sequence, and one sequence whose values
+    grow along it, so the kernel's V reference grows many times."""
+    rng = np.random.default_rng(90 + hq + hkv)
+    NB = 160
+    pool = DynPool(NB, hkv, 5 + hq)
+    lens = np.array([1, 16, 17, 100, 250, 513, 700], np.int32)
+    chunks = np.array([1, 16, 0, 37, 250, 100, 333], np.int32)
+    perm = rng.permutation(NB)
+    tables, pos = np.zeros((len(lens), 48), np.int32), 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // BS)
+        tables[b, :n] = perm[pos:pos + n]
+        tables[b, n:] = perm[(pos + n) % NB]        # stale entries past the sequence
+        pos += n
+    seed = 500
+    for b, L in enumerate(lens):                  # each sequence in 1 to 4 calls
+        cuts = sorted(set([0, int(L)] + list(rng.integers(0, L + 1, 3))))
+        for c0, c1 in zip(cuts[:-1], cuts[1:]):
+            sl = oracle.slots_for(tables, [b] * (c1 - c0), range(c0, c1))
+            seed += 5
+            k, v = _rows(c1 - c0, hkv, seed, 1.0), _rows(c1 - c0, hkv, seed + 2, 1.0)
+            if b == 5:                            # magnitudes growing along the sequence
+                grow = torch.linspace(0.05 + c0 / 100, 0.05 + c1 / 100, c1 - c0,
+                                      device="cuda").to(torch.float16)[:, None, None]
+                k, v = k * grow, v * grow
+            pool.write(k, v, sl)
+    pool.check_equal()
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = workloads.randn_f16((int(qs[-1]), hq, D), 321 + hq, "cuda")
+    out = torch.empty((int(qs[-1]), hq, D), dtype=torch.float32, device="cuda")
+    sm = float(np.float32(1 / np.sqrt(D)))
+    pkv.pkv_paged_prefill_attention_dynamic(out, q, pool.kd, pool.vd, pool.ksd, pool.vsd,
+                                            torch.from_numpy(tables).cuda(),
+                                            torch.from_numpy(lens).cuda(),
+                                            torch.from_numpy(qs).cuda(), int(chunks.max()),
+                                            int(lens.max()), pool.layout, sm)
+    torch.cuda.synchronize()
+    ref = oracle.paged_prefill_attention_dynamic(q.cpu().numpy(), pool.kh, pool.vh, pool.ksh,
+                                                 pool.vsh, tables, lens, qs, hkv, sm, THREADS)
+    got = out.cpu().numpy()
+    err = max_err(got, ref)
+    print(f"[parity] dynamic prefill Hq={hq} Hkv={hkv}: max abs err {err:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL[True]
