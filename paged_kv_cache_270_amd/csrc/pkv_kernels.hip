@@ -868,14 +868,17 @@ static int waves_for(const DecodePlan& pl) {
 // partition.  Chaining applies to short partitions (at most 64 blocks) of the
 // default kernel family with per-tensor scales: each wave gets about 128
 // tiles, as with the automatic partition length, while the grid keeps about
-// 2048 waves.
+// 2048 waves.  Not for batches of 1024 or more (sequence, KV head) pairs,
+// where lengths may be ragged: there the longest sequence's chains would be
+// the tail (measured: 256 ragged sequences at 1024-token partitions, 286 us
+// chained against 234 us with a workgroup per partition).
 static int chain_for(const DecodePlan& pl, int32_t num_seqs) {
   const KernelConfig& c = pl.cfg;
   if (c.chain == 0 || pl.a.n_p_max <= 1 || pl.dyn) return 0;
   if (pl.fp8 && !(c.hw_cvt && c.split_p_fp8)) return 0;
   if (c.chain > 0) return c.chain;
-  if (c.prefetch != 1 || c.waves != 0 || pl.a.part_blocks > 64) return 0;
   const int64_t pairs = (int64_t)num_seqs * pl.a.hkv;
+  if (c.prefetch != 1 || c.waves != 0 || pl.a.part_blocks > 64 || pairs >= 1024) return 0;
   int chain = std::max(1, 128 / pl.a.part_blocks);
   while (chain > 1 && pairs * ((pl.a.n_p_max + chain - 1) / chain) < 2048) chain /= 2;
   return chain;

@@ -353,10 +353,13 @@ def test_long_partitions_merged_across_waves(fp8):
     assert err <= TOL[fp8]
 
 
-def test_shared_prefix_cache_hint_changes_nothing():
+@pytest.mark.parametrize("ps", [0, 256])
+def test_shared_prefix_cache_hint_changes_nothing(ps):
     """The shared-prefix hint only picks a cache policy: bit-identical output
-    with the hint, without it, and with a wrong one."""
+    with the hint, without it, and with a wrong one -- with the automatic
+    partitions and with short ones, which chain partitions per wave."""
     wl = workloads.shared_prefix(groups=4, per_group=8, max_len=6000)
+    wl.partition_size = ps
     prep = Prepared(wl)
     base = prep.gpu_decode()
     for hint in (np.full(wl.num_seqs, wl.prefix_blocks, dtype=np.int32),
@@ -366,6 +369,7 @@ def test_shared_prefix_cache_hint_changes_nothing():
         pkv.pkv_paged_attention_decode(out, prep.q, prep.k_pool, prep.v_pool, prep.tables,
                                        prep.lens, wl.max_context_len, prep.layout,
                                        prep.sm_scale, prep.k_scale, prep.v_scale,
+                                       partition_size=ps,
                                        shared_prefix_blocks=torch.from_numpy(hint).cuda())
         torch.cuda.synchronize()
         assert np.array_equal(base.view(np.uint32), out.cpu().numpy().view(np.uint32))
