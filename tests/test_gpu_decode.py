@@ -329,10 +329,10 @@ _RAGGED = [1, 15, 16, 17, 127, 128, 129, 1000, 2049, 4095, 4096, 4097, 6000, 800
 def test_chained_short_partitions_ragged_batch(fp8, ps):
     """Short explicit partitions go to the kernel where each wave streams
     several consecutive partitions and stores a partial at each partition's
-    end.  With 16 sequences x 8 KV heads the library chains 8, 4, 2 and 1
-    partitions per wave at P = 64, 128, 256 and 512; the ragged lengths give
-    single-partition sequences, waves with nothing to do and chains cut short
-    at a sequence's end."""
+    end.  With 16 sequences x 8 KV heads the library chains 8, 4 and 2
+    partitions per wave at P = 64, 128 and 256 (and keeps a workgroup per
+    partition at 512); the ragged lengths give single-partition sequences,
+    waves with nothing to do and chains cut short at a sequence's end."""
     wl = _small_workload(_RAGGED, hq=64, hkv=8, fp8=fp8, seed=70 + ps)
     wl.partition_size = ps
     prep = Prepared(wl)
