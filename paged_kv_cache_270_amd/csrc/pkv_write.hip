@@ -207,8 +207,9 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
 // its slots outside W are re-encoded as E4M3(fp32(value * fp32(s_old /
 // s_new))); new rows are E4M3(fp32(x / s_new)).
 //
-// Three launches, because the new scale of a block depends on every token
-// the call writes into it:
+// Three launches (one for calls of at most 64 tokens, dyn_write_small_kernel
+// below), because the new scale of a block depends on every token the call
+// writes into it:
 //   1. clear the scratch entries of the touched blocks;
 //   2. MaxAbs of each new row into the scratch (integer atomic max of the
 //      non-negative float bits) and the written offsets (atomic or);
@@ -359,6 +360,75 @@ dyn_write_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
   }
 }
 
+// Calls of at most one wave of tokens (a decode step) in one launch: each row
+// finds the call's tokens in its block by comparing the call's slots, which
+// one wave holds (lane l: token l), and computes the block's MaxAbs and
+// written offsets itself instead of through the scratch.  Then as
+// dyn_write_kernel: the same scale, codes and re-encoding.  Thread mapping
+// as the plain write: 16 lanes per (token, kv head) row, 4 rows per wave.
+constexpr int kDynSmallTokens = kWave;
+
+__global__ void __launch_bounds__(256)
+dyn_write_small_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                       uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                       float* __restrict__ k_bscale, float* __restrict__ v_bscale,
+                       const int64_t* __restrict__ slots, int num_tokens, int hkv,
+                       int64_t num_slots) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)num_tokens * hkv * 16;
+  const bool active = gid < total;          // inactive lanes still take part in the ballots
+  const int c = (int)(gid & 15);
+  const int64_t th = gid >> 4;
+  const int tok = active ? (int)(th / hkv) : 0;
+  const int h = active ? (int)(th - (int64_t)tok * hkv) : 0;
+  const int64_t my_slot = active ? slots[tok] : -1;
+  const bool valid = my_slot >= 0 && my_slot < num_slots;
+  const int blk = valid ? (int)(my_slot >> 4) : -1;   // block ids fit 31 bits
+  // lane l holds token l's block (or -1)
+  const int64_t sl = lane < num_tokens ? slots[lane] : -1;
+  const int lblk = sl >= 0 && sl < num_slots ? (int)(sl >> 4) : -1;
+  uint64_t same = 0;                        // the call's tokens in this row's block
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {             // every lane takes part: no lane has left yet
+    const int bg = __shfl(blk, g * 16, kWave);
+    const uint64_t m = __ballot(lblk == bg && bg >= 0);
+    if ((lane >> 4) == g) same = m;
+  }
+  if (!valid) return;                       // the same for all 16 lanes of the row
+  uint32_t km = 0, vm = 0, mask = 0;
+  for (uint64_t rest = same; rest != 0; rest &= rest - 1) {
+    const int t = __builtin_ctzll(rest);
+    const int64_t row = ((int64_t)t * hkv + h) * 16 + c;
+    km = max(km, max_abs_bits8(key[row]));
+    vm = max(vm, max_abs_bits8(value[row]));
+    mask |= 1u << (slots[t] & 15);
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) {
+    km = max(km, (uint32_t)__shfl_xor((int)km, m, kWave));
+    vm = max(vm, (uint32_t)__shfl_xor((int)vm, m, kWave));
+  }
+  const int off = (int)(my_slot & 15);
+  const int64_t tile = blk * hkv + h;
+  const bool fresh = (mask & 1u) != 0;
+  const float min_scale = 0x1p-126f;
+  const float sk_old = fresh ? 0.0f : k_bscale[tile];
+  const float sv_old = fresh ? 0.0f : v_bscale[tile];
+  const float sk = fmaxf(fmaxf(sk_old, f16_bits_to_float(km) / 448.0f), min_scale);
+  const float sv = fmaxf(fmaxf(sv_old, f16_bits_to_float(vm) / 448.0f), min_scale);
+  store_rows8<true>(k_pool, v_pool, tile, off, c, key[th * 16 + c], value[th * 16 + c], sk, sv);
+  if (off != __builtin_ctz(mask)) return;    // not this block's lowest new offset
+  uint8_t* kp = k_pool + tile * (kBS * kD);
+  uint8_t* vp = v_pool + tile * (kBS * kD);
+  if (!fresh && sk > sk_old) requant_k_rows(kp, c, mask, sk_old / sk);
+  if (!fresh && sv > sv_old) requant_v_rows(vp, c, mask, sv_old / sv);
+  if (c == 0) {
+    k_bscale[tile] = sk;
+    v_bscale[tile] = sv;
+  }
+}
+
 // ------------------------------------------------------------ copy_blocks
 
 // One workgroup per (source, destination) pair; with per-block scales the
@@ -490,6 +560,13 @@ extern "C" pkv_status pkv_reshape_and_cache_dynamic(
   uint32_t* written = amax + (int64_t)layout->num_blocks * 2 * hkv;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (num_tokens <= kDynSmallTokens) {  // a decode step: one launch, no scratch
+    dyn_write_small_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
+        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_block_scales,
+        v_block_scales, slot_mapping, num_tokens, hkv, num_slots);
+    return launch_status();
+  }
   dyn_clear_kernel<<<dim3((unsigned)clear_blocks), dim3(256), 0, s>>>(
       slot_mapping, clear_total, 2 * hkv, num_slots, amax, written);
   dyn_amax_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(

@@ -74,9 +74,13 @@ def _rows(T, Hkv, seed, spread=2.0):
     return (x * mag).clamp(-60000, 60000).half()
 
 
-@pytest.mark.parametrize("Hkv", [2, 8])
-def test_write_is_bit_exact_through_growth_and_interleaved_calls(Hkv):
-    rng = np.random.default_rng(40 + Hkv)
+@pytest.mark.parametrize("Hkv,chunk", [(2, 40), (8, 40), (2, 7), (8, 7)])
+def test_write_is_bit_exact_through_growth_and_interleaved_calls(Hkv, chunk):
+    """Calls of up to 8 x chunk tokens plus two skipped slots: with chunks of 7
+    every call has at most 58 tokens and takes the one-launch path, several
+    tokens of a call often landing in one block; with 40 most take the
+    three-launch path."""
+    rng = np.random.default_rng(40 + Hkv + chunk)
     NB = 96
     pool = DynPool(NB, Hkv, 7 + Hkv)
     lens = [1, 15, 16, 17, 40, 75, 200, 333]
@@ -93,7 +97,7 @@ def test_write_is_bit_exact_through_growth_and_interleaved_calls(Hkv):
         sl = []
         for b, L in enumerate(lens):
             if done[b] < L:
-                n = int(rng.integers(1, min(40, L - done[b]) + 1))
+                n = int(rng.integers(1, min(chunk, L - done[b]) + 1))
                 sl += [int(tables[b][p // BS]) * BS + p % BS for p in range(done[b], done[b] + n)]
                 done[b] += n
         sl += [-1, NB * BS + 3]                   # skipped slots
@@ -101,7 +105,8 @@ def test_write_is_bit_exact_through_growth_and_interleaved_calls(Hkv):
         seed += 7
         pool.write(_rows(len(sl), Hkv, seed), _rows(len(sl), Hkv, seed + 3), sl)
         pool.check_equal()
-    print(f"[parity] dynamic write Hkv={Hkv}: pools and scales bit-exact", flush=True)
+    print(f"[parity] dynamic write Hkv={Hkv} chunk={chunk}: pools and scales bit-exact",
+          flush=True)
 
 
 @pytest.mark.parametrize("ps", [0, 16, 64, 256, 512])
