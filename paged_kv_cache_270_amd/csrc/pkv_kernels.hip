@@ -26,8 +26,9 @@
 //     registers; its reference max is re-reduced only when a logit exceeds
 //     it by a fixed slack;
 //   * split-KV: up to eight waves per workgroup share a partition and merge
-//     through LDS; partitions are merged by a second kernel with the
-//     log-sum-exp rule.
+//     through LDS, or, for short partitions, each wave streams a chain of
+//     consecutive partitions and stores each partial from registers;
+//     partitions are merged by a second kernel with the log-sum-exp rule.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
