@@ -373,3 +373,26 @@ def test_shared_prefix_cache_hint_changes_nothing(ps):
                                        shared_prefix_blocks=torch.from_numpy(hint).cuda())
         torch.cuda.synchronize()
         assert np.array_equal(base.view(np.uint32), out.cpu().numpy().view(np.uint32))
+
+
+def test_largest_batch_the_grid_allows():
+    """65535 sequences (the most one launch takes) of 1 to 40 tokens, FP8,
+    2 query heads per KV head; sampled sequences, spread over the batch,
+    against the oracle.  One more sequence is rejected before any launch."""
+    rng = np.random.default_rng(65535)
+    lens = rng.integers(1, 41, 65535)
+    wl = _small_workload(lens, hq=2, hkv=1, fp8=True, seed=77)
+    prep = Prepared(wl)
+    got = prep.gpu_decode()
+    sample = np.unique(np.concatenate([[0, 1, 65534], rng.integers(0, 65535, 300)]))
+    ref = prep.oracle_decode(sample)
+    err = max_err(got[sample], ref)
+    _report("65535 sequences (sampled)", err, TOL[True])
+    assert err <= TOL[True]
+    q = torch.zeros((65536, 2, D), dtype=torch.float16, device="cuda")
+    out = torch.empty((65536, 2, D), dtype=torch.float32, device="cuda")
+    tables = torch.zeros((65536, 3), dtype=torch.int32, device="cuda")
+    lens1 = torch.ones(65536, dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_paged_attention_decode(out, q, prep.k_pool, prep.v_pool, tables, lens1, 40,
+                                       prep.layout, prep.sm_scale, prep.k_scale, prep.v_scale)
