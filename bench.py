@@ -16,12 +16,14 @@ created and grown block by block (forked from a group leader where they share
 a prefix), cached tokens are written by pkv_reshape_and_cache, and the pool
 hands out each sequence's slot for the new token (timed: host_slot_assignment).
 
-A step is the whole hot path on one batch: pkv_reshape_and_cache stores each
-sequence's new K/V row into its slot, then the partition kernel attends over
-L tokens per sequence and, when some sequence spans several partitions, the
-merge kernel combines them.  Prints one JSON line; `value` = KV bytes the step
-must read from HBM (each stored token once, K and V, all KV heads) / step
-time, in GB/s.
+A step is the whole hot path on one batch: each sequence's new K/V row is
+stored into its slot and the partition kernel attends over L tokens per
+sequence -- one launch, pkv_decode_partitions_append, whose kernel also
+writes the new rows -- and, when some sequence spans several partitions, the
+merge kernel combines them.  With `--kv-scales block` the write is
+pkv_reshape_and_cache_dynamic, launched first.  Prints one JSON line;
+`value` = KV bytes the step must read from HBM (each stored token once, K and
+V, all KV heads) / step time, in GB/s.
 """
 import argparse
 import hashlib
@@ -37,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "KV GB/s read (% of HBM peak) + decode seqs·tok/s, 70B-layer shape, FP8 KV"
 CSRC = os.path.join(ROOT, "paged_kv_cache_270_amd", "csrc")
 # the sources each measured kernel is built from
-DECODE_SRCS = ("pkv_kernels.hip", "pkv_tile.h")
+DECODE_SRCS = ("pkv_kernels.hip", "pkv_tile.h", "pkv_codec.h")
 PREFILL_SRCS = ("pkv_prefill.hip", "pkv_tile.h")
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
@@ -504,10 +506,10 @@ def main() -> int:
     del key_src, val_src
 
     def step(ev=None):
-        write(new_k, new_v, d_step_slots)
-        if ev is not None:
-            ev[0].record()
         if dyn:
+            write(new_k, new_v, d_step_slots)
+            if ev is not None:
+                ev[0].record()
             # one call: the partition kernel, then the merge when a sequence
             # spans several partitions (none at the default workload)
             pkv.pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_bs, v_bs, d_tables,
@@ -516,9 +518,13 @@ def main() -> int:
             if ev is not None:
                 ev[1].record()
             return
-        pkv.pkv_decode_partitions(out, q, k_pool, v_pool, d_tables, d_lens, Lmax, layout,
-                                  sm_scale, k_scale, v_scale, P, ws,
-                                  shared_prefix_blocks=d_shared)
+        # the newest token of each sequence (position L - 1, the slot
+        # pool.append gave it) is written by the partition kernel itself
+        if ev is not None:
+            ev[0].record()
+        pkv.pkv_decode_partitions_append(out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens,
+                                         Lmax, layout, sm_scale, k_scale, v_scale, P, ws,
+                                         shared_prefix_blocks=d_shared)
         if ev is not None:
             ev[1].record()
         pkv.pkv_decode_reduce(out, d_lens, Lmax, tables.shape[1], layout, v_scale, P, ws)
@@ -626,7 +632,8 @@ def main() -> int:
                    "kv_scales": ("per (block, kv head)" if dyn else "per tensor")
                    if wl.fp8 else None,
                    "arith": "f16 MFMA inputs, f32 accumulate", "parallelism": "single GPU",
-                   "launch": "hip graph" if args.graph else "eager"},
+                   "launch": "hip graph" if args.graph else "eager",
+                   "new_token_write": "separate launch" if dyn else "in the decode kernel"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tok_per_s": round(tokens / (step_ms * 1e-3), 1),
         "kv_bytes_per_step": unique,

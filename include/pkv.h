@@ -212,6 +212,44 @@ pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens, int32_t nu
                              float v_scale, int32_t partition_size, void* workspace,
                              uint64_t workspace_bytes, void* stream);
 
+/* A decode step in one call: write each sequence's newest token into the
+ * cache, then attend over its whole context, that token included -- the
+ * cache write of [FP8-128K] §6.2 followed by the decode attention above.
+ * Sequence b's newest token is at position L_b - 1 (L_b = context_lens[b]
+ * after the clamp described above); its slot is
+ *   block_tables[b][(L_b - 1) / 16] * 16 + (L_b - 1) % 16,
+ * so its block must already be in the table (pkv_seq_append assigns it) and
+ * must not be shared with another sequence (copy-on-write done first).
+ *   key, value    device fp16 [num_seqs][num_kv_heads][128], contiguous,
+ *                 16-byte aligned: the new token's K and V rows.
+ *   k_pool/v_pool the pools, read and written.
+ *   k_scale/v_scale  per-tensor scales (FP8): the new rows are stored as the
+ *                 codes pkv_reshape_and_cache would store, and all rows are
+ *                 decoded with them.
+ * Other arguments as in pkv_paged_attention_decode.  The pools and `out` end
+ * up exactly as after pkv_reshape_and_cache (slot_mapping as above) then
+ * pkv_paged_attention_decode with the same arguments; L_b = 0 writes nothing;
+ * a block id outside [0, num_blocks) is skipped, as that write skips it.
+ * The kernel that reads a sequence's last block also stores its newest rows
+ * and uses them from registers, so no separate write launch is made (with
+ * the PKV_DECODE_PREFETCH / PKV_FP8_* A/B variants a small write kernel
+ * runs first).  pkv_decode_partitions_append is its first half, completed by
+ * pkv_decode_reduce with the same arguments. */
+pkv_status pkv_paged_attention_decode_append(
+    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream);
+pkv_status pkv_decode_partitions_append(
+    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream);
+
 /* Copy whole blocks (every KV head, K and V) for copy-on-write: a shared
  * block is duplicated before a sequence writes into it ([KV-SLOW] "Cómo
  * PagedAttention soluciona esto"; [GLOSSARY] §3.01).

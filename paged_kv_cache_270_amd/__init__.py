@@ -17,6 +17,7 @@ __all__ = [
     "load_library", "pkv_status_string", "pkv_bytes_per_token", "pkv_pool_bytes",
     "pkv_decode_partition_size", "pkv_decode_workspace_bytes", "pkv_reshape_and_cache",
     "pkv_paged_attention_decode", "pkv_decode_partitions", "pkv_decode_reduce",
+    "pkv_paged_attention_decode_append", "pkv_decode_partitions_append",
     "pkv_copy_blocks", "pkv_reshape_dynamic_workspace_bytes", "pkv_reshape_and_cache_dynamic",
     "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic", "pkv_paged_prefill_attention",
     "pkv_paged_prefill_attention_dynamic", "pkv_swap_blocks",
@@ -86,6 +87,10 @@ def load_library():
         "pkv_decode_partitions": ([P, P, P, P, P, i32, P, P, i32, i32, i32, LP, f32, f32, f32,
                                    i32, P, u64, P], i32),
         "pkv_decode_reduce": ([P, P, i32, i32, i32, i32, LP, f32, i32, P, u64, P], i32),
+        "pkv_paged_attention_decode_append": ([P, P, P, P, P, P, P, i32, P, P, i32, i32, i32,
+                                               LP, f32, f32, f32, i32, P, u64, P], i32),
+        "pkv_decode_partitions_append": ([P, P, P, P, P, P, P, i32, P, P, i32, i32, i32, LP,
+                                          f32, f32, f32, i32, P, u64, P], i32),
         "pkv_copy_blocks": ([P, P, LP, P, i32, P], i32),
         "pkv_reshape_dynamic_workspace_bytes": ([LP], u64),
         "pkv_reshape_and_cache_dynamic": ([P, P, P, P, P, P, P, i32, LP, P, u64, P], i32),
@@ -277,6 +282,48 @@ def pkv_decode_reduce(out, context_lens, max_context_len: int, max_blocks_per_se
         _ptr(out), _ptr(context_lens), B, Hq, max_context_len, max_blocks_per_seq,
         ctypes.byref(layout), v_scale, partition_size, _ptr(workspace), nbytes,
         _stream(stream)), "pkv_decode_reduce")
+
+
+def _new_rows(key, value, B, layout):
+    import torch
+    _require(key, torch.float16, "key")
+    _require(value, torch.float16, "value")
+    if key.shape != value.shape or tuple(key.shape) != (B, layout.num_kv_heads, layout.head_dim):
+        raise ValueError("key/value must be [num_seqs][num_kv_heads][head_dim]")
+    return _ptr(key), _ptr(value)
+
+
+def pkv_paged_attention_decode_append(out, q, key, value, k_pool, v_pool, block_tables,
+                                      context_lens, max_context_len: int, layout: CacheLayout,
+                                      sm_scale: float, k_scale: float = 1.0,
+                                      v_scale: float = 1.0, partition_size: int = 0,
+                                      workspace=None, stream=None,
+                                      shared_prefix_blocks=None) -> None:
+    """One decode step: store each sequence's newest token (key/value fp16
+    [B][Hkv][128], at position context_lens[b] - 1) and attend over all."""
+    B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
+    kp, vp = _new_rows(key, value, B, layout)
+    workspace, nbytes = _workspace(workspace, B, Hq, layout, max_context_len, partition_size)
+    _check(load_library().pkv_paged_attention_decode_append(
+        _ptr(out), _ptr(q), kp, vp, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
+        _ptr(context_lens), _hint(shared_prefix_blocks, B), B, Hq, max_context_len,
+        ctypes.byref(layout), sm_scale, k_scale, v_scale, partition_size, _ptr(workspace),
+        nbytes, _stream(stream)), "pkv_paged_attention_decode_append")
+
+
+def pkv_decode_partitions_append(out, q, key, value, k_pool, v_pool, block_tables,
+                                 context_lens, max_context_len: int, layout: CacheLayout,
+                                 sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                                 partition_size: int = 0, workspace=None, stream=None,
+                                 shared_prefix_blocks=None) -> None:
+    B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
+    kp, vp = _new_rows(key, value, B, layout)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().pkv_decode_partitions_append(
+        _ptr(out), _ptr(q), kp, vp, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
+        _ptr(context_lens), _hint(shared_prefix_blocks, B), B, Hq, max_context_len,
+        ctypes.byref(layout), sm_scale, k_scale, v_scale, partition_size, _ptr(workspace),
+        nbytes, _stream(stream)), "pkv_decode_partitions_append")
 
 
 def pkv_copy_blocks(k_pool, v_pool, layout: CacheLayout, src_dst_pairs, stream=None) -> None:

@@ -39,6 +39,7 @@
 
 #include "pkv.h"
 #include "pkv_check.h"
+#include "pkv_codec.h"
 #include "pkv_tile.h"
 
 namespace {
@@ -72,6 +73,14 @@ struct DecodeArgs {
   float out_scale;             // v_scale [* 256 for FP8 bit dequant]
   const float* k_bscale;       // [num_blocks][hkv] per-block K scales, or null
   const float* v_bscale;       // [num_blocks][hkv] per-block V scales, or null
+  // Each sequence's newest token, when the decode call also writes it into
+  // the cache (null otherwise): rows [B][Hkv][D] fp16, stored at position
+  // L - 1 through the same pools, FP8 as E4M3(x / scale).
+  const _Float16* new_k;
+  const _Float16* new_v;
+  uint8_t* k_wr;
+  uint8_t* v_wr;
+  float k_enc_scale, v_enc_scale;
 };
 
 // Partials are stored write-through to memory (cache policy sc0 sc1, through
@@ -108,6 +117,134 @@ __device__ __forceinline__ SeqSplit seq_split(const DecodeArgs& a, int L) {
   s.n_p = (s.nblk + a.part_blocks - 1) / a.part_blocks;
   s.per = s.n_p > 0 ? (s.nblk + s.n_p - 1) / s.n_p : 0;
   return s;
+}
+
+// ------------------------------------------- newest token, written in place
+//
+// A decode step first stores the new token's K and V rows in its slot
+// ([FP8-128K] §6.2, the cache write) and then attends over the whole
+// context, that token included.  The decode kernels do both in one launch.
+// The wave that reads the sequence's last block
+//   1. loads the token's rows (one dword of K and one of V per lane) with
+//      its first block-table load, so they cost no wait of their own;
+//   2. once its first tiles are in flight, encodes them (fp16 as they are,
+//      FP8 as E4M3(x / scale): the arithmetic of the cache-write kernels)
+//      into LDS, in the order its lanes hold tile bytes;
+//   3. when the last tile arrives, patches the token's bytes into the tile
+//      registers (whatever the load returned for that slot) and stores them
+//      to the slot.
+// So the attention never depends on when the store lands, the stream does
+// not wait for the write, and no separate write launch is needed.
+//
+// Lane (j, qg) loads, of each tile, K bytes of token j only and V bytes of
+// tokens 4qg .. 4qg+3 only (the MFMA operand orders of the tile layout), so
+// the token at block offset `off` is K on the lanes j == off and V on the
+// lanes qg == off / 4.  Kept bytes in LDS: K at [qg][32 | 64 bytes] (FP8 |
+// fp16), V at 256 + [j][8 | 16 bytes].
+
+constexpr int kKeepBytes = 512;  // LDS per workgroup for the kept bytes
+
+// Step 1: lane l's K and V dwords of the new rows (channels 2l, 2l + 1).
+__device__ __forceinline__ u32x2 append_load(const DecodeArgs& a, int b, int kvh, int lane) {
+  const int64_t row = ((int64_t)b * a.hkv + kvh) * kD;
+  u32x2 r;
+  r.x = reinterpret_cast<const uint32_t*>(a.new_k + row)[lane];
+  r.y = reinterpret_cast<const uint32_t*>(a.new_v + row)[lane];
+  return r;
+}
+
+// Step 2: encode lane l's four values and place them where patch_tile reads.
+template <bool kFP8>
+__device__ __forceinline__ void append_keep(const DecodeArgs& a, u32x2 rows, int lane,
+                                            uint8_t* keep) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int c = 2 * lane + e;                       // channel
+    const uint32_t kh = (rows.x >> (16 * e)) & 0xFFFFu;
+    const uint32_t vh = (rows.y >> (16 * e)) & 0xFFFFu;
+    const int vpos = ((c & 15) * (kFP8 ? 8 : 16)) + (c >> 4) * (kFP8 ? 1 : 2);  // [j][n]
+    if constexpr (kFP8) {
+      const float kx = (float)__builtin_bit_cast(_Float16, (uint16_t)kh);
+      const float vx = (float)__builtin_bit_cast(_Float16, (uint16_t)vh);
+      // K channel c = 64i + 16qg + x -> [qg][i][x]
+      keep[((c >> 4) & 3) * 32 + (c >> 6) * 16 + (c & 15)] =
+          (uint8_t)e4m3_from_f32(kx / a.k_enc_scale);  // correctly rounded fp32 division
+      keep[256 + vpos] = (uint8_t)e4m3_from_f32(vx / a.v_enc_scale);
+    } else {
+      // K channel c = 32m + 8qg + x -> [qg][m][x]
+      *reinterpret_cast<uint16_t*>(keep + ((c >> 3) & 3) * 64 + (c >> 5) * 16 + (c & 7) * 2) =
+          (uint16_t)kh;
+      *reinterpret_cast<uint16_t*>(keep + 256 + vpos) = (uint16_t)vh;
+    }
+  }
+  // other lanes of this wave read these bytes (patch_tile): keep the LDS
+  // stores ahead of any later LDS access of the wave
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// Step 3: replace the newest token's bytes in the loaded tile registers by
+// the bytes append_keep placed in LDS (whatever the load returned for that
+// slot).
+template <bool kFP8>
+__device__ __forceinline__ void patch_tile(TileRegs<kFP8>& t, const uint8_t* keep, int lane,
+                                           int off) {
+  const int j = lane & 15, qg = lane >> 4;
+  if (j == off) {
+#pragma unroll
+    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i)
+      t.k[i] = *reinterpret_cast<const u32x4*>(keep + qg * (kFP8 ? 32 : 64) + i * 16);
+  }
+  if (qg == (off >> 2)) {
+    if constexpr (kFP8) {  // byte off % 4 of the dword of channel 16n + j
+      const u32x2 kept = *reinterpret_cast<const u32x2*>(keep + 256 + j * 8);
+      const uint32_t sh = (off & 3) * 8;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint32_t c = (kept[n >> 2] >> ((n & 3) * 8)) & 0xFFu;
+        t.v[n >> 2][n & 3] = (t.v[n >> 2][n & 3] & ~(0xFFu << sh)) | (c << sh);
+      }
+    } else {  // half off % 4 of the 4 tokens of channel 16n + j (two dwords)
+      const u32x4 kept = *reinterpret_cast<const u32x4*>(keep + 256 + j * 16);
+      const uint32_t sh = (off & 1) * 16;
+      const uint32_t m_lo = (off & 2) ? 0u : (0xFFFFu << sh);
+      const uint32_t m_hi = (off & 2) ? (0xFFFFu << sh) : 0u;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint32_t h = ((kept[n >> 1] >> ((n & 1) * 16)) & 0xFFFFu) << sh;
+        t.v[n >> 1][(n & 1) * 2] = (t.v[n >> 1][(n & 1) * 2] & ~m_lo) | (h & m_lo);
+        t.v[n >> 1][(n & 1) * 2 + 1] = (t.v[n >> 1][(n & 1) * 2 + 1] & ~m_hi) | (h & m_hi);
+      }
+    }
+  }
+}
+
+// Step 3's store: the newest token's bytes, from tile registers patched by
+// patch_tile, into tile `phys` (a block of the pool) of KV head kvh.
+template <bool kFP8>
+__device__ __forceinline__ void append_store(const DecodeArgs& a, const TileRegs<kFP8>& t,
+                                             int phys, int kvh, int lane, int off) {
+  constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
+  const int j = lane & 15, qg = lane >> 4;
+  const int64_t tile = ((int64_t)phys * a.hkv + kvh) * kTileBytes;
+  if (j == off) {
+#pragma unroll
+    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i)
+      *reinterpret_cast<u32x4*>(a.k_wr + tile + i * 1024 + 16 * lane) = t.k[i];
+  }
+  if (qg == (off >> 2)) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      if constexpr (kFP8) {
+        a.v_wr[tile + (n >> 2) * 1024 + 16 * lane + (n & 3) * 4 + (off & 3)] =
+            (uint8_t)(t.v[n >> 2][n & 3] >> ((off & 3) * 8));
+      } else {
+        const uint32_t w = (off & 2) ? t.v[n >> 1][(n & 1) * 2 + 1] : t.v[n >> 1][(n & 1) * 2];
+        *reinterpret_cast<uint16_t*>(a.v_wr + tile + (n >> 1) * 1024 + 16 * lane +
+                                     (n & 1) * 8 + (off & 3) * 2) =
+            (uint16_t)(w >> ((off & 1) * 16));
+      }
+    }
+  }
 }
 
 // Online-softmax state of one lane: head j, tokens 4qg .. 4qg+3 of each tile.
@@ -216,11 +353,15 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
 // kvh*G + j and, in each tile, tokens 4qg .. 4qg+3.  Each wave keeps kPD
 // tiles in flight while it computes on another.
 // With per-block scales the kernel is held to 128 VGPRs (4 waves per SIMD);
-// the compiler fits it without spilling.
-template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false>
+// the compiler fits it without spilling.  kAppend: the kernel also writes
+// each sequence's newest token (steps 1-3 above).
+template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false,
+          bool kAppend = false>
 __global__ void __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kDyn ? 4 : 1)))
 decode_partition_kernel(DecodeArgs a) {
-  extern __shared__ float smem[];  // [kNW][G][D] outputs, then [kNW][16] max and sum
+  // [kNW][G][D] outputs, then [kNW][16] max and sum, then (kAppend) the
+  // newest token's kept bytes
+  extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int j = lane & 15;
@@ -264,10 +405,25 @@ decode_partition_kernel(DecodeArgs a) {
   const int my_n = w < nblk ? (nblk - w + kNW - 1) / kNW : 0;
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk0 + w;
 
+  // The sequence's last block is the last tile of wave (nblk - 1) % kNW of
+  // the last partition: that wave writes the newest token and patches it
+  // into its tile my_n - 1.
+  uint8_t* keep = reinterpret_cast<uint8_t*>(smem + kNW * G * kD + 2 * kNW * 16);
+  int patch_at = -1;
+  if constexpr (kAppend) {
+    if (p == n_p - 1 && w == (nblk - 1) % kNW) patch_at = my_n - 1;
+    patch_at = __builtin_amdgcn_readfirstlane(patch_at);
+  }
+
   // logical blocks below this are shared with other sequences (cache hint)
   const int shared_blocks = a.shared_prefix != nullptr ? a.shared_prefix[b] : 0;
   for (int c0 = 0; c0 < my_n; c0 += kWave) {
     const int cnt = min(kWave, my_n - c0);
+    // the newest token's rows, issued ahead of the table load whose wait
+    // then covers them too
+    u32x2 rows = u32x2{0u, 0u};
+    if constexpr (kAppend)
+      if (c0 == 0 && patch_at >= 0) rows = append_load(a, b, kvh, lane);
     // lane i holds the physical id of this wave's block c0 + i
     const int tbl = lane < cnt ? trow[(int64_t)(c0 + lane) * kNW] : 0;
     const int lb0 = blk0 + w + c0 * kNW;  // logical block of this chunk's tile 0
@@ -297,6 +453,8 @@ decode_partition_kernel(DecodeArgs a) {
         load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
                         __builtin_amdgcn_readlane(tbl, r), kvh, lane,
                         lb0 + r * kNW < shared_blocks);
+    if constexpr (kAppend)
+      if (c0 == 0 && patch_at >= 0) append_keep<kFP8>(a, rows, lane, keep);
     for (int base = 0; base < cnt; base += kPD + 1) {
 #pragma unroll
       for (int r = 0; r <= kPD; ++r) {
@@ -307,6 +465,14 @@ decode_partition_kernel(DecodeArgs a) {
                             a.hkv, __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane,
                             lb0 + (ii + kPD) * kNW < shared_blocks);
           const int tb = (blk0 + w + (c0 + ii) * kNW) * kBS;  // first token of the tile
+          if constexpr (kAppend)
+            if (c0 + ii == patch_at) {
+              const int phys = __builtin_amdgcn_readlane(tbl, ii);
+              if ((unsigned)phys < (unsigned)a.num_blocks) {  // else nothing is written
+                patch_tile<kFP8>(buf[r], keep, lane, (L - 1) & 15);
+                append_store<kFP8>(a, buf[r], phys, kvh, lane, (L - 1) & 15);
+              }
+            }
           if constexpr (kDyn)
             process_tile<kFP8, kHwCvt, kSplitP, true>(
                 buf[r], qop, st, tb, qg, L, a.qk_scale,
@@ -384,13 +550,15 @@ decode_partition_kernel(DecodeArgs a) {
 // with one workgroup per partition.  Per-tensor scales only: with per-block
 // scales the extra registers spill and one workgroup per partition is faster.
 // Grid (ceil(n_p_max / (kChainWaves * chain)), Hkv, B); kChainWaves waves per
-// workgroup, each independent of the others.
+// workgroup, each independent of the others.  kAppend: the kernel also
+// writes each sequence's newest token (steps 1-3 above).
 constexpr int kChainWaves = 4;
 
-template <bool kFP8>
+template <bool kFP8, bool kAppend = false>
 __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(DecodeArgs a,
                                                                            int chain) {
   constexpr int kPD = 1;
+  __shared__ __align__(16) uint8_t keep[kAppend ? kKeepBytes : 16];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int j = lane & 15;
@@ -410,6 +578,15 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
   }
   const int blk_begin = p_first * sp.per;
   const int my_n = min(sp.nblk, (p_first + chain) * sp.per) - blk_begin;
+
+  // the wave whose run ends with the sequence's last block writes the
+  // newest token and patches it into its last tile (one such wave per
+  // sequence and KV head, so the workgroup's kept bytes are its own)
+  int patch_at = -1;
+  if constexpr (kAppend) {
+    if (blk_begin + my_n == sp.nblk) patch_at = my_n - 1;
+    patch_at = __builtin_amdgcn_readfirstlane(patch_at);
+  }
 
   f16x8 qop[4];
 #pragma unroll
@@ -435,6 +612,9 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
   const int shared_blocks = a.shared_prefix != nullptr ? a.shared_prefix[b] : 0;
   for (int c0 = 0; c0 < my_n; c0 += kWave) {
     const int cnt = min(kWave, my_n - c0);
+    u32x2 rows = u32x2{0u, 0u};  // the newest token's rows, ahead of the table load
+    if constexpr (kAppend)
+      if (c0 == 0 && patch_at >= 0) rows = append_load(a, b, kvh, lane);
     const int tbl = lane < cnt ? trow[c0 + lane] : 0;
     const int lb0 = blk_begin + c0;
     TileRegs<kFP8> buf[kPD + 1];
@@ -443,6 +623,8 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
       if (r < cnt)
         load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
                         __builtin_amdgcn_readlane(tbl, r), kvh, lane, lb0 + r < shared_blocks);
+    if constexpr (kAppend)
+      if (c0 == 0 && patch_at >= 0) append_keep<kFP8>(a, rows, lane, keep);
     for (int base = 0; base < cnt; base += kPD + 1) {
 #pragma unroll
       for (int r = 0; r <= kPD; ++r) {
@@ -452,6 +634,14 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
             load_tile<kFP8>(buf[(r + kPD) % (kPD + 1)], a.k_pool, a.v_pool, a.num_blocks,
                             a.hkv, __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane,
                             lb0 + ii + kPD < shared_blocks);
+          if constexpr (kAppend)
+            if (c0 + ii == patch_at) {
+              const int phys = __builtin_amdgcn_readlane(tbl, ii);
+              if ((unsigned)phys < (unsigned)a.num_blocks) {  // else nothing is written
+                patch_tile<kFP8>(buf[r], keep, lane, (L - 1) & 15);
+                append_store<kFP8>(a, buf[r], phys, kvh, lane, (L - 1) & 15);
+              }
+            }
           process_tile<kFP8, true, true>(buf[r], qop, st, (lb0 + ii) * kBS, qg, L, a.qk_scale);
           if (lb0 + ii + 1 == part_end) {  // wave-uniform: partition `part` is complete
             float l_run = st.l;
@@ -772,6 +962,10 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   a.n_p_max = wl.n_p_max;
   a.k_bscale = plan->dyn ? k_bscale : nullptr;
   a.v_bscale = plan->dyn ? v_bscale : nullptr;
+  a.new_k = a.new_v = nullptr;
+  a.k_wr = a.v_wr = nullptr;
+  a.k_enc_scale = k_scale;
+  a.v_enc_scale = v_scale;
   // FP8 tiles decoded by bit operations hold code / 256: fold the 256 back
   // in (per-block scales always use the hardware conversion)
   const float deq = (fp8 && !plan->cfg.hw_cvt && !plan->dyn) ? 256.0f : 1.0f;
@@ -806,11 +1000,25 @@ extern "C" uint64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_h
 }
 
 
-template <bool kFP8, bool kHw, bool kSplit, int kPD, int kNW, bool kDyn = false>
+template <bool kFP8, bool kHw, bool kSplit, int kPD, int kNW, bool kDyn = false,
+          bool kAppend = false>
 static void launch_partition_v(dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  const size_t lds = (size_t)(kNW * a.g * kD + 2 * kNW * 16) * sizeof(float);
-  decode_partition_kernel<kFP8, kHw, kSplit, kPD, kNW, kDyn>
+  const size_t lds = (size_t)(kNW * a.g * kD + 2 * kNW * 16) * sizeof(float) +
+                     (kAppend ? kKeepBytes : 0);
+  decode_partition_kernel<kFP8, kHw, kSplit, kPD, kNW, kDyn, kAppend>
       <<<grid, dim3(kNW * kWave), lds, s>>>(a);
+}
+
+// Writing the newest token too: the default family (FP8: hardware convert,
+// split probabilities; one tile in flight) at every wave count.
+template <bool kFP8>
+static void launch_partition_append(int nw, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  switch (nw) {
+    case 1: return launch_partition_v<kFP8, kFP8, true, 1, 1, false, true>(grid, s, a);
+    case 2: return launch_partition_v<kFP8, kFP8, true, 1, 2, false, true>(grid, s, a);
+    case 8: return launch_partition_v<kFP8, kFP8, true, 1, 8, false, true>(grid, s, a);
+    default: return launch_partition_v<kFP8, kFP8, true, 1, 4, false, true>(grid, s, a);
+  }
 }
 
 // Per-block scales: the default family (hardware convert, split P, one tile
@@ -853,7 +1061,7 @@ static void launch_partition(int pd, int nw, dim3 grid, hipStream_t s, const Dec
 
 // Waves per partition workgroup: each wave should stream at least 16 tiles,
 // so short partitions get fewer waves (and skip most of the LDS merge).
-static int waves_for(const DecodePlan& pl) {
+static int waves_for(const DecodePlan& pl, size_t extra_lds = 0) {
   int nw = pl.cfg.waves;
   if (nw <= 0) {
     const int per_wave_tiles = 16;
@@ -861,7 +1069,9 @@ static int waves_for(const DecodePlan& pl) {
     nw = want >= 4 ? 4 : (want >= 2 ? 2 : 1);
   }
   // the LDS merge buffer must fit one workgroup's 64 KiB
-  while (nw > 1 && (size_t)(nw * pl.a.g * kD + 2 * nw * 16) * sizeof(float) > 65536) nw /= 2;
+  while (nw > 1 &&
+         (size_t)(nw * pl.a.g * kD + 2 * nw * 16) * sizeof(float) + extra_lds > 65536)
+    nw /= 2;
   return nw;
 }
 
@@ -888,12 +1098,34 @@ static int chain_for(const DecodePlan& pl, int32_t num_seqs) {
   return chain >= 2 ? chain : 0;
 }
 
-template <bool kFP8>
+template <bool kFP8, bool kAppend = false>
 static void launch_chain(int chain, int32_t num_seqs, hipStream_t s, const DecodeArgs& a) {
   const int per_wg = kChainWaves * chain;
   const dim3 grid((unsigned)((a.n_p_max + per_wg - 1) / per_wg), (unsigned)a.hkv,
                   (unsigned)num_seqs);
-  decode_chain_kernel<kFP8><<<grid, dim3(kChainWaves * kWave), 0, s>>>(a, chain);
+  decode_chain_kernel<kFP8, kAppend><<<grid, dim3(kChainWaves * kWave), 0, s>>>(a, chain);
+}
+
+// The newest token alone, one wave per (KV head, sequence), for the kernel
+// variants that do not write it themselves (the A/B variants of
+// kernel_config); launched before them on the same stream.
+template <bool kFP8>
+__global__ void __launch_bounds__(kWave) append_kernel(DecodeArgs a) {
+  __shared__ __align__(16) uint8_t keep[kKeepBytes];
+  const int kvh = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int L = clamp_len(a, b);
+  if (L <= 0) return;
+  const int phys = a.block_tables[(int64_t)b * a.max_blocks + ((L - 1) >> 4)];
+  if ((unsigned)phys >= (unsigned)a.num_blocks) return;  // nothing is written
+  append_keep<kFP8>(a, append_load(a, b, kvh, lane), lane, keep);
+  TileRegs<kFP8> t;  // only the token's bytes are patched in and stored
+#pragma unroll
+  for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+    t.k[i] = u32x4{0u, 0u, 0u, 0u};
+    t.v[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  patch_tile<kFP8>(t, keep, lane, (L - 1) & 15);
+  append_store<kFP8>(a, t, phys, kvh, lane, (L - 1) & 15);
 }
 
 static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStream_t s) {
@@ -917,6 +1149,41 @@ static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStre
   else
     c.split_p_fp8 ? launch_partition<true, false, true>(c.prefetch, nw, grid, s, pl.a)
                   : launch_partition<true, false, false>(c.prefetch, nw, grid, s, pl.a);
+  return launch_status();
+}
+
+// The partition kernels that also write each sequence's newest token: the
+// chained kernel or the default family of the partition kernel; otherwise
+// append_kernel, then the partition kernels as without the write.
+static pkv_status run_partitions_append(const DecodePlan& pl, int32_t num_seqs,
+                                        hipStream_t s) {
+  if (num_seqs == 0) return PKV_OK;
+  (void)hipGetLastError();
+  const KernelConfig& c = pl.cfg;
+  if (const int chain = chain_for(pl, num_seqs)) {
+    if (pl.fp8)
+      launch_chain<true, true>(chain, num_seqs, s, pl.a);
+    else
+      launch_chain<false, true>(chain, num_seqs, s, pl.a);
+    return launch_status();
+  }
+  const bool default_family = c.prefetch == 1 && (!pl.fp8 || (c.hw_cvt && c.split_p_fp8));
+  if (!default_family) {
+    const dim3 grid((unsigned)pl.a.hkv, (unsigned)num_seqs);
+    if (pl.fp8)
+      append_kernel<true><<<grid, dim3(kWave), 0, s>>>(pl.a);
+    else
+      append_kernel<false><<<grid, dim3(kWave), 0, s>>>(pl.a);
+    const pkv_status st = launch_status();
+    if (st != PKV_OK) return st;
+    return run_partitions(pl, num_seqs, s);
+  }
+  const dim3 grid((unsigned)pl.a.n_p_max, (unsigned)pl.a.hkv, (unsigned)num_seqs);
+  const int nw = waves_for(pl, kKeepBytes);
+  if (pl.fp8)
+    launch_partition_append<true>(nw, grid, s, pl.a);
+  else
+    launch_partition_append<false>(nw, grid, s, pl.a);
   return launch_status();
 }
 
@@ -986,9 +1253,56 @@ extern "C" pkv_status pkv_paged_attention_decode(
   return run_reduce(pl, num_seqs, s);
 }
 
+// The newest-token arguments of the *_append entry points.
+static pkv_status set_append(DecodePlan* pl, int32_t num_seqs, const void* key,
+                             const void* value, void* k_pool, void* v_pool) {
+  if (num_seqs == 0) return PKV_OK;
+  if (!key || !value || !aligned(key, 16) || !aligned(value, 16)) return PKV_ERR_INVALID_ARG;
+  pl->a.new_k = static_cast<const _Float16*>(key);
+  pl->a.new_v = static_cast<const _Float16*>(value);
+  pl->a.k_wr = static_cast<uint8_t*>(k_pool);
+  pl->a.v_wr = static_cast<uint8_t*>(v_pool);
+  return PKV_OK;
+}
 
+extern "C" pkv_status pkv_decode_partitions_append(
+    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream) {
+  DecodePlan pl;
+  pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                              context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
+                              max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
+  if (st != PKV_OK) return st;
+  st = set_append(&pl, num_seqs, key, value, k_pool, v_pool);
+  if (st != PKV_OK) return st;
+  return run_partitions_append(pl, num_seqs, static_cast<hipStream_t>(stream));
+}
 
-
+extern "C" pkv_status pkv_paged_attention_decode_append(
+    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream) {
+  DecodePlan pl;
+  pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                              context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
+                              max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
+  if (st != PKV_OK) return st;
+  st = set_append(&pl, num_seqs, key, value, k_pool, v_pool);
+  if (st != PKV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_partitions_append(pl, num_seqs, s);
+  if (st != PKV_OK) return st;
+  return run_reduce(pl, num_seqs, s);
+}
 
 extern "C" pkv_status pkv_paged_attention_decode_dynamic(
     float* out, const void* q, const void* k_pool, const void* v_pool,

@@ -177,3 +177,24 @@ def test_prefill_entry_points_validate_before_launch():
                None) == pkv.PKV_ERR_INVALID_ARG          # misaligned V scales
     assert dyn(None, None, None, None, 16, 16, None, 4, None, None, 0, 4, 32, 64,
                ctypes.byref(f8), 0.1, None) == pkv.PKV_OK
+
+
+def test_append_entry_points_validate_before_launch():
+    """Every call here is rejected (or is a no-op) before any HIP call."""
+    L = pkv.load_library()
+    f8 = pkv.CacheLayout(16, 2, pkv.PKV_FP8_E4M3FN)
+    for fn in (L.pkv_paged_attention_decode_append, L.pkv_decode_partitions_append):
+        # out, q, key, value, k_pool, v_pool, tables, max_blocks, lens, hint, B, Hq, max_ctx,
+        # layout, sm_scale, k_scale, v_scale, partition, workspace, bytes, stream
+        def call(key=16, value=16, B=2, Hq=4, ks=1.0, ws_bytes=1 << 20, part=0):
+            return fn(16, 16, key, value, 16, 16, 16, 4, 16, None, B, Hq, 64, ctypes.byref(f8),
+                      0.1, ks, 1.0, part, 256, ws_bytes, None)
+        assert call(key=None) == pkv.PKV_ERR_INVALID_ARG
+        assert call(value=None) == pkv.PKV_ERR_INVALID_ARG
+        assert call(key=8) == pkv.PKV_ERR_INVALID_ARG         # rows not 16-byte aligned
+        assert call(value=24) == pkv.PKV_ERR_INVALID_ARG
+        assert call(ks=float("inf")) == pkv.PKV_ERR_INVALID_ARG
+        assert call(Hq=64) == pkv.PKV_ERR_UNSUPPORTED           # group of 32 query heads
+        assert call(part=32, ws_bytes=16) == pkv.PKV_ERR_WORKSPACE
+        assert fn(None, None, None, None, None, None, None, 4, None, None, 0, 4, 64,
+                  ctypes.byref(f8), 0.1, 1.0, 1.0, 0, None, 0, None) == pkv.PKV_OK
