@@ -645,8 +645,10 @@ def main() -> int:
         "bulk_fill_gbs": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     # counters were taken at the workload's own partition size
                      "traffic": measured_traffic("decode_partition_" + args.workload +
-                                                 ("_block_scales" if dyn else ""))},
+                                                 ("_block_scales" if dyn else ""))
+                     if args.partition_size is None else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
