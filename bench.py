@@ -401,6 +401,10 @@ def main() -> int:
     ap.add_argument("--cpu-sample-seqs", type=int, default=8,
                     help="sequences of the workload the CPU oracle baseline decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cascade", choices=("auto", "on", "off"), default="auto",
+                    help="decode each group's shared prefix once for the group "
+                         "(pkv_paged_attention_decode_cascade); auto = when the host pool "
+                         "finds prefix groups in the batch and the scales are per tensor")
     ap.add_argument("--graph", action="store_true",
                     help="replay the decode step as one captured HIP graph instead of "
                          "launching its kernels one by one")
@@ -476,8 +480,21 @@ def main() -> int:
     sm_scale = float(np.float32(1 / np.sqrt(D)))
     req = wl.partition_size if args.partition_size is None else args.partition_size
     P = pkv.pkv_decode_partition_size(B, Hkv, Lmax, layout.dtype, req)
-    ws = torch.empty(max(1, pkv.pkv_decode_workspace_bytes(B, Hq, Hkv, Lmax, layout.dtype, P)),
-                     dtype=torch.uint8, device=dev)
+    # prefix groups of the batch, found by the host pool from the forks
+    prefix, garr, max_pre, order = pool.prefix_groups(seqs, 8, with_order=True)
+    cascade = args.cascade == "on" or (args.cascade == "auto" and garr.shape[0] > 0 and not dyn)
+    if cascade and dyn:
+        print("bench.py: the cascade decode takes per-tensor scales", file=sys.stderr)
+        return 2
+    if cascade:
+        d_prefix = torch.from_numpy(prefix).to(dev)
+        d_groups = torch.from_numpy(garr).to(dev) if garr.shape[0] else None
+        d_order = torch.from_numpy(order).to(dev)   # longest tails first
+        ws_bytes = pkv.pkv_decode_cascade_workspace_bytes(B, Hq, Hkv, Lmax, max_pre,
+                                                          layout.dtype, P)
+    else:
+        ws_bytes = pkv.pkv_decode_workspace_bytes(B, Hq, Hkv, Lmax, layout.dtype, P)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     if dyn:
         k_bs = torch.zeros((NB, Hkv), dtype=torch.float32, device=dev)
         v_bs = torch.zeros_like(k_bs)
@@ -515,6 +532,18 @@ def main() -> int:
             pkv.pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_bs, v_bs, d_tables,
                                                    d_lens, Lmax, layout, sm_scale, P, ws,
                                                    shared_prefix_blocks=d_shared)
+            if ev is not None:
+                ev[1].record()
+            return
+        if cascade:
+            # one call: the partition kernel (prefix items and tails, writing
+            # the newest tokens), then the merge; events span both
+            if ev is not None:
+                ev[0].record()
+            pkv.pkv_paged_attention_decode_cascade(
+                out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens, Lmax, layout, sm_scale,
+                d_prefix, d_groups, max_pre, k_scale, v_scale, P, ws,
+                shared_prefix_blocks=d_shared, seq_order=d_order)
             if ev is not None:
                 ev[1].record()
             return
@@ -633,13 +662,18 @@ def main() -> int:
                    if wl.fp8 else None,
                    "arith": "f16 MFMA inputs, f32 accumulate", "parallelism": "single GPU",
                    "launch": "hip graph" if args.graph else "eager",
-                   "new_token_write": "separate launch" if dyn else "in the decode kernel"},
+                   "new_token_write": "separate launch" if dyn else "in the decode kernel",
+                   "decode": ("cascade: each shared prefix once per group "
+                              f"({garr.shape[0]} groups, {max_pre} prefix blocks)")
+                   if cascade else "per sequence"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tok_per_s": round(tokens / (step_ms * 1e-3), 1),
         "kv_bytes_per_step": unique,
         "kv_bytes_per_step_logical": logical,
         "kv_gbs_logical": round(logical / (step_ms * 1e-3) / 1e9, 2),
         "decode_partition_us": round(part_ms * 1e3, 2),
+        "decode_partition_us_covers": "partition + merge kernels" if cascade
+        else "partition kernel",
         "shared_prefix_blocks_hint": int(shared.max()) if B else 0,
         "host_slot_assignment_us": round(host_slot_us, 1),
         "bulk_fill_gbs": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),
@@ -647,7 +681,8 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      # counters were taken at the workload's own partition size
                      "traffic": measured_traffic("decode_partition_" + args.workload +
-                                                 ("_block_scales" if dyn else ""))
+                                                 ("_block_scales" if dyn else "") +
+                                                 ("_cascade" if cascade else ""))
                      if args.partition_size is None else None},
         "cpu_baseline": cpu,
     }

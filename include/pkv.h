@@ -250,6 +250,66 @@ pkv_status pkv_decode_partitions_append(
     float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
     void* stream);
 
+/* Decode over shared prefixes as a cascade.  Sequences that share their
+ * leading blocks (a common system prompt, or the branches of a parallel
+ * sample: [PRIMER-8] §8.1, [GLOSSARY] §3.02) hold the same physical blocks
+ * there.  Here those blocks are attended once per group: one wave serves up
+ * to 16 / G members of a group (G query heads each, one MFMA column per
+ * head) over every prefix tile, storing one split-KV partial per member;
+ * each sequence's tail (the blocks after its prefix) is split into
+ * partitions as in pkv_paged_attention_decode, and the log-sum-exp merge
+ * combines prefix and tail partials.  The result equals the plain decode
+ * over the same tables within rounding (the split-KV identity).
+ *   prefix_blocks  device int32 [num_seqs]: S_b, the leading blocks of
+ *                  sequence b attended by its group; 0 = none.  Used only
+ *                  if 0 < S_b <= max_prefix_blocks and 16 * S_b < L_b (the
+ *                  newest token stays in the tail); otherwise sequence b is
+ *                  decoded on its own, and groups must leave it out.
+ *   prefix_groups  device int32 [num_groups][group_cap]: the batch indices
+ *                  of each group's members, -1 for an empty slot.  The first
+ *                  slot of a group holds a member; all members of a group
+ *                  have the same S_b and the same first S_b table entries;
+ *                  every sequence with a used S_b > 0 is in exactly one
+ *                  group.  (pkv_pool_prefix_groups builds these.)  Results
+ *                  for sequences that break this are unspecified; no memory
+ *                  outside the arguments is touched.
+ *   max_prefix_blocks  host: the largest S_b; sizes the workspace
+ *                  (pkv_decode_cascade_workspace_bytes).
+ *   seq_order      optional device int32 [num_seqs] (NULL = batch order): a
+ *                  permutation of the batch; the sequences' tails are
+ *                  scheduled in this order after the prefix items.  Longest
+ *                  tails first (pkv_pool_prefix_groups gives that order)
+ *                  keeps the longest workgroups from starting last.  An
+ *                  entry outside [0, num_seqs) is skipped; a sequence not
+ *                  listed gets unspecified output (no memory outside the
+ *                  arguments is touched).
+ *   key, value     the newest tokens' rows as in
+ *                  pkv_paged_attention_decode_append, written in the same
+ *                  launch; both null = decode only.
+ * Other arguments as in pkv_paged_attention_decode_append.  The kernel
+ * variant is the default family whatever PKV_* variant switches say.
+ * Errors: INVALID_ARG for one of key/value null, negative counts, groups
+ * without arrays, or more than 65535 items plus sequences
+ * (num_groups * ceil(group_cap / (16 / G)) + num_seqs); WORKSPACE if the
+ * workspace is smaller than pkv_decode_cascade_workspace_bytes. */
+pkv_status pkv_paged_attention_decode_cascade(
+    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, const int32_t* prefix_blocks,
+    const int32_t* prefix_groups, int32_t num_groups, int32_t group_cap,
+    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream);
+
+/* Workspace of pkv_paged_attention_decode_cascade: room for each sequence's
+ * prefix partitions (ceil(16 * max_prefix_blocks / P)) and tail partitions;
+ * 0 when no sequence needs a merge or on invalid arguments. */
+uint64_t pkv_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t max_context_len,
+                                            int32_t max_prefix_blocks, int32_t dtype,
+                                            int32_t partition_size);
+
 /* Copy whole blocks (every KV head, K and V) for copy-on-write: a shared
  * block is duplicated before a sequence writes into it ([KV-SLOW] "Cómo
  * PagedAttention soluciona esto"; [GLOSSARY] §3.01).
@@ -423,6 +483,29 @@ int32_t pkv_pool_num_seqs(const pkv_pool* pool);
  * (reference count > 1) -- the shared_prefix_blocks hint of the decode;
  * -1 for an unknown id. */
 int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* pool, int32_t seq);
+/* Prefix groups of a decode batch for pkv_paged_attention_decode_cascade.
+ * seqs[0..n) are the batch's sequences in batch order.  Entries whose first
+ * block is the same shared block ([PRIMER-8] §8.1: forks of one prompt hold
+ * the same pages) form a group; its prefix is the longest run of leading
+ * table entries that all its members hold, shortened so that every member
+ * keeps at least one token after it.  A first block held by one entry, or a
+ * prefix of 0 blocks, gives no group.  A group of more than group_cap entries
+ * is split into groups of at most group_cap.
+ *   prefix_blocks_out  host int32 [n]: each entry's prefix blocks, 0 = none
+ *   groups_out         host int32 [cap_groups][group_cap]: batch indices of
+ *                      each group's members in batch order, -1 padded
+ *   *n_groups_out      groups found; *max_prefix_out their largest prefix
+ *   order_out          optional host int32 [n] (NULL = not wanted): batch
+ *                      indices by decreasing tail (tokens after the prefix),
+ *                      ties in batch order -- the cascade's seq_order
+ * BAD_HANDLE for an unknown sequence id; INVALID_ARG for bad sizes or if
+ * more than cap_groups groups are found (then only the two counts are set).
+ * Reads the pool only. */
+pkv_status pkv_pool_prefix_groups(const pkv_pool* pool, const int32_t* seqs, int32_t n,
+                                  int32_t group_cap, int32_t cap_groups,
+                                  int32_t* prefix_blocks_out, int32_t* groups_out,
+                                  int32_t* n_groups_out, int32_t* max_prefix_out,
+                                  int32_t* order_out);
 
 /* ------------------------------------------------------------- prefix cache
  *

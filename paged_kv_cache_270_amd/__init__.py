@@ -91,6 +91,12 @@ def load_library():
                                                LP, f32, f32, f32, i32, P, u64, P], i32),
         "pkv_decode_partitions_append": ([P, P, P, P, P, P, P, i32, P, P, i32, i32, i32, LP,
                                           f32, f32, f32, i32, P, u64, P], i32),
+        "pkv_paged_attention_decode_cascade": ([P, P, P, P, P, P, P, i32, P, P, P, P, i32, i32,
+                                                i32, P, i32, i32, i32, LP, f32, f32, f32, i32,
+                                                P, u64, P], i32),
+        "pkv_decode_cascade_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], u64),
+        "pkv_pool_prefix_groups": ([P, P, i32, i32, i32, P, P, ctypes.POINTER(i32),
+                                    ctypes.POINTER(i32), P], i32),
         "pkv_copy_blocks": ([P, P, LP, P, i32, P], i32),
         "pkv_reshape_dynamic_workspace_bytes": ([LP], u64),
         "pkv_reshape_and_cache_dynamic": ([P, P, P, P, P, P, P, i32, LP, P, u64, P], i32),
@@ -326,6 +332,60 @@ def pkv_decode_partitions_append(out, q, key, value, k_pool, v_pool, block_table
         nbytes, _stream(stream)), "pkv_decode_partitions_append")
 
 
+def pkv_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                                       max_prefix_blocks, dtype=PKV_FP8_E4M3FN,
+                                       partition_size=0) -> int:
+    return load_library().pkv_decode_cascade_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, max_context_len, max_prefix_blocks, dtype,
+        partition_size)
+
+
+def pkv_paged_attention_decode_cascade(out, q, key, value, k_pool, v_pool, block_tables,
+                                       context_lens, max_context_len: int, layout: CacheLayout,
+                                       sm_scale: float, prefix_blocks, prefix_groups,
+                                       max_prefix_blocks: int, k_scale: float = 1.0,
+                                       v_scale: float = 1.0, partition_size: int = 0,
+                                       workspace=None, stream=None,
+                                       shared_prefix_blocks=None, seq_order=None) -> None:
+    """Decode with each group's shared prefix attended once for the group.
+    prefix_blocks: device int32 [B]; prefix_groups: device int32
+    [n_groups][group_cap] (or None for no groups); key/value: the newest
+    tokens' rows to write in the same launch, or both None; seq_order:
+    optional device int32 [B], the order the tails are scheduled in."""
+    import torch
+    B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
+    if key is None and value is None:
+        kp = vp = None
+    else:
+        kp, vp = _new_rows(key, value, B, layout)
+    if prefix_groups is None or prefix_groups.numel() == 0:
+        n_groups, cap, gp, pp = 0, 1, None, None
+    else:
+        _require(prefix_groups, torch.int32, "prefix_groups")
+        _require(prefix_blocks, torch.int32, "prefix_blocks")
+        if prefix_groups.dim() != 2 or prefix_blocks.numel() != B:
+            raise ValueError("prefix_groups must be [n_groups][group_cap], prefix_blocks [B]")
+        n_groups, cap = prefix_groups.shape
+        gp, pp = _ptr(prefix_groups), _ptr(prefix_blocks)
+    if seq_order is not None:
+        _require(seq_order, torch.int32, "seq_order")
+        if seq_order.numel() != B:
+            raise ValueError("seq_order must hold one entry per sequence")
+    need = pkv_decode_cascade_workspace_bytes(B, Hq, layout.num_kv_heads, max_context_len,
+                                              max_prefix_blocks if n_groups else 0,
+                                              layout.dtype, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().pkv_paged_attention_decode_cascade(
+        _ptr(out), _ptr(q), kp, vp, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
+        _ptr(context_lens), _hint(shared_prefix_blocks, B), pp, gp, n_groups, cap,
+        max_prefix_blocks, _ptr(seq_order), B, Hq, max_context_len, ctypes.byref(layout),
+        sm_scale, k_scale,
+        v_scale, partition_size, _ptr(workspace), nbytes, _stream(stream)),
+        "pkv_paged_attention_decode_cascade")
+
+
 def pkv_copy_blocks(k_pool, v_pool, layout: CacheLayout, src_dst_pairs, stream=None) -> None:
     """src_dst_pairs: int32 [n][2] device tensor of (source, destination)."""
     import torch
@@ -541,6 +601,26 @@ class BlockPool:
 
     def shared_prefix_blocks(self, seq: int) -> int:
         return self._L.pkv_seq_shared_prefix_blocks(self._h, seq)
+
+    def prefix_groups(self, seqs, group_cap: int = 8, with_order: bool = False):
+        """Prefix groups of a batch for the cascade decode.  Returns
+        (prefix_blocks int32 [n], groups int32 [n_groups][group_cap] with -1
+        padding, max_prefix_blocks) as numpy arrays and an int, plus the batch
+        order by decreasing tail (int32 [n]) if with_order."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = seqs.size
+        prefix = np.zeros(max(1, n), dtype=np.int32)
+        cap_groups = max(1, n)
+        groups = np.full((cap_groups, group_cap), -1, dtype=np.int32)
+        order = np.zeros(max(1, n), dtype=np.int32)
+        ng, mx = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._L.pkv_pool_prefix_groups(
+            self._h, seqs.ctypes.data, n, group_cap, cap_groups, prefix.ctypes.data,
+            groups.ctypes.data, ctypes.byref(ng), ctypes.byref(mx), order.ctypes.data),
+            "pkv_pool_prefix_groups")
+        res = (prefix[:n].copy(), groups[:ng.value].copy(), mx.value)
+        return res + (order[:n].copy(),) if with_order else res
 
     # ---- swap space (page-granular eviction to host memory)
 

@@ -317,6 +317,81 @@ extern "C" int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* p, int32_t seq) 
   return n;
 }
 
+// Groups for the cascade decode: batch entries whose first block is one
+// shared physical block ([PRIMER-8] §8.1: forks of one prompt hold the same
+// pages), each group's prefix being the leading table entries all its members
+// hold, cut so that every member keeps at least one token after it.
+extern "C" pkv_status pkv_pool_prefix_groups(const pkv_pool* p, const int32_t* seqs, int32_t n,
+                                             int32_t group_cap, int32_t cap_groups,
+                                             int32_t* prefix_blocks_out, int32_t* groups_out,
+                                             int32_t* n_groups_out, int32_t* max_prefix_out,
+                                             int32_t* order_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (n < 0 || group_cap <= 0 || cap_groups < 0 || !n_groups_out || !max_prefix_out ||
+      (n > 0 && (!seqs || !prefix_blocks_out)) || (cap_groups > 0 && !groups_out))
+    return PKV_ERR_INVALID_ARG;
+  std::vector<const Seq*> sq((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+    sq[(size_t)i] = &it->second;
+  }
+  // batch entries by first block, groups in order of first appearance
+  std::unordered_map<int32_t, size_t> by_first;
+  std::vector<std::vector<int32_t>> cand;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = *sq[(size_t)i];
+    if (s.blocks.empty() || s.blocks[0] < 0 || p->ref[(size_t)s.blocks[0]] <= 1) continue;
+    auto ins = by_first.emplace(s.blocks[0], cand.size());
+    if (ins.second) cand.emplace_back();
+    cand[ins.first->second].push_back(i);
+  }
+  std::vector<int32_t> prefix((size_t)n, 0);
+  std::vector<std::vector<int32_t>> groups;
+  int32_t max_prefix = 0;
+  for (const auto& mem : cand) {
+    if (mem.size() < 2) continue;
+    // longest run of leading entries every member holds, on the device
+    const std::vector<int32_t>& lead = sq[(size_t)mem[0]]->blocks;
+    int64_t S = (int64_t)lead.size();
+    for (int32_t i : mem) {
+      const Seq& s = *sq[(size_t)i];
+      int64_t k = 0;
+      while (k < S && k < (int64_t)s.blocks.size() && s.blocks[(size_t)k] >= 0 &&
+             s.blocks[(size_t)k] == lead[(size_t)k])
+        ++k;
+      S = std::min<int64_t>(k, (s.len - 1) / p->block_size);  // a token after it
+    }
+    if (S <= 0) continue;
+    for (size_t c = 0; c < mem.size(); c += (size_t)group_cap) {
+      std::vector<int32_t> g(mem.begin() + (ptrdiff_t)c,
+                             mem.begin() + (ptrdiff_t)std::min(mem.size(), c + group_cap));
+      for (int32_t i : g) prefix[(size_t)i] = (int32_t)S;
+      groups.push_back(std::move(g));
+    }
+    max_prefix = std::max<int32_t>(max_prefix, (int32_t)S);
+  }
+  *n_groups_out = (int32_t)groups.size();
+  *max_prefix_out = max_prefix;
+  if ((int32_t)groups.size() > cap_groups) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) prefix_blocks_out[i] = prefix[(size_t)i];
+  if (order_out) {  // longest tail first, ties in batch order
+    std::vector<int32_t> ord((size_t)n);
+    for (int32_t i = 0; i < n; ++i) ord[(size_t)i] = i;
+    auto tail = [&](int32_t i) {
+      return sq[(size_t)i]->len - (int64_t)prefix[(size_t)i] * p->block_size;
+    };
+    std::stable_sort(ord.begin(), ord.end(),
+                     [&](int32_t x, int32_t y) { return tail(x) > tail(y); });
+    for (int32_t i = 0; i < n; ++i) order_out[i] = ord[(size_t)i];
+  }
+  for (size_t gi = 0; gi < groups.size(); ++gi)
+    for (int32_t k = 0; k < group_cap; ++k)
+      groups_out[gi * (size_t)group_cap + (size_t)k] =
+          k < (int32_t)groups[gi].size() ? groups[gi][(size_t)k] : -1;
+  return PKV_OK;
+}
+
 // ------------------------------------------------------------ prefix cache
 
 extern "C" pkv_status pkv_seq_create_cached(pkv_pool* p, const int32_t* tokens,

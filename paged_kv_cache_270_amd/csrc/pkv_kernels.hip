@@ -81,6 +81,19 @@ struct DecodeArgs {
   uint8_t* k_wr;
   uint8_t* v_wr;
   float k_enc_scale, v_enc_scale;
+  // Cascade over shared prefixes (null casc_prefix otherwise): sequence b's
+  // first casc_prefix[b] blocks are attended once for its whole group; the
+  // grid's first casc_items z-slices are (group, chunk of casc_m members)
+  // items over those blocks, the rest one slice per sequence for its tail.
+  const int32_t* casc_prefix;  // [B] prefix blocks of each sequence, 0 = none
+  const int32_t* casc_groups;  // [n_groups][casc_cap] member sequences, -1 = none
+  int32_t casc_items;          // n_groups * casc_chunks
+  int32_t casc_chunks;         // items per group: ceil(casc_cap / casc_m)
+  int32_t casc_cap;            // member slots per group
+  int32_t casc_m;              // members per item: 16 / G, one MFMA column each
+  int32_t casc_max;            // largest prefix (blocks) the workspace is sized for
+  const int32_t* seq_order;    // [B] or null: the sequence of each tail z-slice
+  int32_t nseq;                // B
 };
 
 // Partials are stored write-through to memory (cache policy sc0 sc1, through
@@ -117,6 +130,36 @@ __device__ __forceinline__ SeqSplit seq_split(const DecodeArgs& a, int L) {
   s.n_p = (s.nblk + a.part_blocks - 1) / a.part_blocks;
   s.per = s.n_p > 0 ? (s.nblk + s.n_p - 1) / s.n_p : 0;
   return s;
+}
+
+// Cascade: blocks of sequence b (length L) attended by its group's prefix
+// items.  0 unless the sequence has a prefix within what the workspace was
+// sized for and at least one token after it (so its newest token, and its
+// own partition, are in the tail).
+__device__ __forceinline__ int casc_blocks(const DecodeArgs& a, int b, int L) {
+  if (a.casc_prefix == nullptr) return 0;
+  const int S = a.casc_prefix[b];
+  return (S > 0 && S <= a.casc_max && S * kBS < L) ? S : 0;
+}
+
+// Prefix partitions of a prefix of S blocks: ceil(S / part_blocks), cut
+// into equal runs of whole blocks.
+__device__ __forceinline__ SeqSplit prefix_split(const DecodeArgs& a, int S) {
+  SeqSplit s;
+  s.nblk = S;
+  s.n_p = (S + a.part_blocks - 1) / a.part_blocks;
+  s.per = s.n_p > 0 ? (S + s.n_p - 1) / s.n_p : 0;
+  return s;
+}
+
+// Partitions whose partials the merge combines for sequence b: without the
+// cascade, seq_split's; with it, the prefix's partitions first, then the
+// tail's (the blocks after the prefix, split as seq_split splits a sequence).
+__device__ __forceinline__ int seq_parts(const DecodeArgs& a, int b, int L) {
+  const int S = casc_blocks(a, b, L);
+  if (S == 0) return seq_split(a, L).n_p;
+  const int tail = (L + kBS - 1) / kBS - S;
+  return prefix_split(a, S).n_p + (tail + a.part_blocks - 1) / a.part_blocks;
 }
 
 // ------------------------------------------- newest token, written in place
@@ -356,40 +399,95 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
 // the compiler fits it without spilling.  kAppend: the kernel also writes
 // each sequence's newest token (steps 1-3 above).
 template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false,
-          bool kAppend = false>
+          bool kAppend = false, bool kCasc = false>
 __global__ void __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kDyn ? 4 : 1)))
 decode_partition_kernel(DecodeArgs a) {
-  // [kNW][G][D] outputs, then [kNW][16] max and sum, then (kAppend) the
-  // newest token's kept bytes
+  // [kNW][CS][D] outputs, then [kNW][16] max and sum, then (kAppend) the
+  // newest token's kept bytes, then (kCasc) the item's member per column
   extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int j = lane & 15;
   const int qg = lane >> 4;
-  const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int p = blockIdx.x, kvh = blockIdx.y;
   const int G = a.g;
+  constexpr int kCS = kCasc ? kMaxG : 0;  // LDS column stride (0: G)
+  const int CS = kCasc ? kCS : G;
+  int* memb = reinterpret_cast<int*>(smem + kNW * CS * kD + 2 * kNW * 16 + kKeepBytes / 4);
 
-  const int L = clamp_len(a, b);
-  const SeqSplit sp = seq_split(a, L);
-  const int n_p = sp.n_p;
-  const int64_t head0 = (int64_t)b * a.hq + (int64_t)kvh * G;  // first query head of the group
-  if (p >= n_p) {
-    if (p == 0) {  // empty sequence: attention over nothing is defined as zeros
-      for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) a.out[head0 * kD + i] = 0.0f;
+  int b = blockIdx.z;  // the sequence (a prefix item: its group's first member)
+  int L, n_p, pidx, blk0, nblk, ncol = G, shared_blocks;
+  bool item = false;
+  int qrow = -1;       // this lane's query row [B*Hq], -1 = column unused
+  if constexpr (kCasc) {
+    if (b < a.casc_items) {
+      // A prefix item: up to casc_m members of one group, G columns each,
+      // over partition p of the group's prefix blocks (whole blocks, every
+      // token valid).  Members whose prefix differs are left out.
+      item = true;
+      const int gi = b / a.casc_chunks, ch = b - gi * a.casc_chunks;
+      const int32_t* grp = a.casc_groups + (int64_t)gi * a.casc_cap;
+      const int lead = grp[0];
+      if ((unsigned)lead >= (unsigned)a.nseq) return;
+      const int S = casc_blocks(a, lead, clamp_len(a, lead));
+      if (S == 0) return;
+      const SeqSplit ps = prefix_split(a, S);
+      if (p >= ps.n_p) return;
+      b = lead;
+      L = S * kBS;
+      n_p = 2;  // never the only partition: partials are always stored
+      pidx = p;
+      blk0 = p * ps.per;
+      nblk = min(S, blk0 + ps.per) - blk0;
+      ncol = a.casc_m * G;
+      shared_blocks = S;  // every item of the group reads these tiles
+      const int slot = ch * a.casc_m + j / G;
+      int m = -1;
+      if (j < ncol && slot < a.casc_cap) {
+        m = grp[slot];
+        if ((unsigned)m >= (unsigned)a.nseq || casc_blocks(a, m, clamp_len(a, m)) != S) m = -1;
+      }
+      if (m >= 0) qrow = m * a.hq + kvh * G + (j - (j / G) * G);
+      if (w == 0 && qg == 0) memb[j] = m;
+    } else {
+      b -= a.casc_items;
+      if (a.seq_order != nullptr) {  // tails in the caller's order (longest first)
+        b = a.seq_order[b];
+        if ((unsigned)b >= (unsigned)a.nseq) return;
+      }
     }
-    return;
   }
-  const int blk0 = p * sp.per;
-  const int nblk = min(sp.nblk, blk0 + sp.per) - blk0;
+  if (!item) {
+    L = clamp_len(a, b);
+    int S = 0;
+    if constexpr (kCasc) S = casc_blocks(a, b, L);
+    // the blocks after the prefix (all of them without one), split evenly
+    const SeqSplit sp = seq_split(a, L - S * kBS);
+    const int n_pp = S > 0 ? prefix_split(a, S).n_p : 0;
+    n_p = n_pp + sp.n_p;
+    if (p >= sp.n_p) {
+      if (p == 0) {  // empty sequence: attention over nothing is defined as zeros
+        const int64_t head0 = (int64_t)b * a.hq + (int64_t)kvh * G;
+        for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) a.out[head0 * kD + i] = 0.0f;
+      }
+      return;
+    }
+    pidx = n_pp + p;
+    blk0 = S + p * sp.per;
+    nblk = min(S + sp.nblk, blk0 + sp.per) - blk0;
+    shared_blocks = a.shared_prefix != nullptr ? a.shared_prefix[b] : 0;
+    if (j < G) qrow = b * a.hq + kvh * G + j;
+  }
+  const int64_t head0 = (int64_t)b * a.hq + (int64_t)kvh * G;  // first query head of the group
 
   // Query heads of the group as the MFMA B operand, in the channel order the
   // K tile registers hold (FP8: runs of 16 channels; fp16: runs of 8).
   f16x8 qop[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    if (j < G) {
+    if (qrow >= 0) {
       const int d0 = kFP8 ? (m >> 1) * 64 + qg * 16 + (m & 1) * 8 : m * 32 + qg * 8;
-      qop[m] = *reinterpret_cast<const f16x8*>(a.q + (head0 + j) * kD + d0);
+      qop[m] = *reinterpret_cast<const f16x8*>(a.q + (int64_t)qrow * kD + d0);
     } else {
       qop[m] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
@@ -408,15 +506,15 @@ decode_partition_kernel(DecodeArgs a) {
   // The sequence's last block is the last tile of wave (nblk - 1) % kNW of
   // the last partition: that wave writes the newest token and patches it
   // into its tile my_n - 1.
-  uint8_t* keep = reinterpret_cast<uint8_t*>(smem + kNW * G * kD + 2 * kNW * 16);
+  uint8_t* keep = reinterpret_cast<uint8_t*>(smem + kNW * CS * kD + 2 * kNW * 16);
   int patch_at = -1;
   if constexpr (kAppend) {
-    if (p == n_p - 1 && w == (nblk - 1) % kNW) patch_at = my_n - 1;
+    if (!item && pidx == n_p - 1 && w == (nblk - 1) % kNW) patch_at = my_n - 1;
     patch_at = __builtin_amdgcn_readfirstlane(patch_at);
   }
 
-  // logical blocks below this are shared with other sequences (cache hint)
-  const int shared_blocks = a.shared_prefix != nullptr ? a.shared_prefix[b] : 0;
+  // logical blocks below shared_blocks are read by other sequences or items
+  // too (cache hint)
   for (int c0 = 0; c0 < my_n; c0 += kWave) {
     const int cnt = min(kWave, my_n - c0);
     // the newest token's rows, issued ahead of the table load whose wait
@@ -496,13 +594,13 @@ decode_partition_kernel(DecodeArgs a) {
   }
 
   // merge the kNW waves through LDS
-  float* so = smem;                        // [kNW][G][D]
-  float* sm = smem + kNW * G * kD;         // [kNW][16]
+  float* so = smem;                        // [kNW][CS][D]
+  float* sm = smem + kNW * CS * kD;        // [kNW][16]
   float* sl = sm + kNW * 16;               // [kNW][16]
-  if (j < G) {
+  if (j < ncol) {
 #pragma unroll
     for (int n = 0; n < 8; ++n)
-      *reinterpret_cast<f32x4*>(so + (w * G + j) * kD + n * 16 + qg * 4) = st.acc[n];
+      *reinterpret_cast<f32x4*>(so + (w * CS + j) * kD + n * 16 + qg * 4) = st.acc[n];
     if (qg == 0) {
       sm[w * 16 + j] = st.m_ref;
       sl[w * 16 + j] = l_run;
@@ -510,10 +608,11 @@ decode_partition_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const bool single = n_p == 1;
-  // the G rows of this partition's partial output (not used when single)
-  const __amdgpu_buffer_rsrc_t orows =
-      partial_rows(single ? nullptr : a.ws_o + part_row(a, b, kvh, p, 0) * kD, G * kD * 4);
-  for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) {
+  // the G rows of this partition's partial output (not used when single,
+  // nor by a prefix item, whose columns belong to several sequences)
+  const __amdgpu_buffer_rsrc_t orows = partial_rows(
+      single || item ? nullptr : a.ws_o + part_row(a, b, kvh, pidx, 0) * kD, G * kD * 4);
+  for (int i = threadIdx.x; i < ncol * kD; i += kNW * kWave) {
     const int gg = i / kD, d = i - gg * kD;
     float mx = -INFINITY;
 #pragma unroll
@@ -522,14 +621,28 @@ decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ww = 0; ww < kNW; ++ww) {
       const float f = __builtin_amdgcn_exp2f(sm[ww * 16 + gg] - mx);
-      num += so[(ww * G + gg) * kD + d] * f;
+      num += so[(ww * CS + gg) * kD + d] * f;
       den += sl[ww * 16 + gg] * f;
     }
     const int64_t hrow = head0 + gg;
+    if constexpr (kCasc) {
+      if (item) {  // column gg: head gg % G of member gg / G
+        const int m = memb[gg];
+        if (m >= 0) {
+          const int64_t prow = part_row(a, m, kvh, pidx, gg % G);
+          a.ws_o[prow * kD + d] = num;
+          if (d == 0) {
+            a.ws_ml[prow * 2] = mx;
+            a.ws_ml[prow * 2 + 1] = den;
+          }
+        }
+        continue;
+      }
+    }
     if (single) {
       a.out[hrow * kD + d] = num / den * a.out_scale;
     } else {
-      const int64_t prow = part_row(a, b, kvh, p, gg);
+      const int64_t prow = part_row(a, b, kvh, pidx, gg);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(num), orows, i * 4, 0, kWriteThrough);
       if (d == 0) {
         a.ws_ml[prow * 2] = mx;
@@ -708,7 +821,7 @@ __global__ void __launch_bounds__(kRW * kWave) decode_reduce_kernel(DecodeArgs a
   const int64_t bh = kSplit ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kRW + w;
   if (bh >= rows) return;                    // only when !kSplit: whole waves leave
   const int b = (int)(bh / a.hq);
-  const int n_p = seq_split(a, clamp_len(a, b)).n_p;
+  const int n_p = seq_parts(a, b, clamp_len(a, b));
   if (n_p <= 1) return;                      // written by the partition kernel
   const int h = (int)(bh - (int64_t)b * a.hq);
   const int64_t row0 = part_row(a, b, h / a.g, 0, h % a.g);
@@ -844,6 +957,34 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32
   return w;
 }
 
+// Cascade workspace: every sequence may have a prefix of up to max_prefix
+// blocks (each split into ceil(S / (part / 16)) partitions) before its tail
+// partitions.  Also gives the grid's partition dimension (x_dim).
+struct CascLayout {
+  WsLayout ws;
+  int32_t s_max, x_dim;
+};
+
+CascLayout casc_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32_t part,
+                       int32_t max_prefix) {
+  CascLayout c{};
+  const int64_t nblk = ((int64_t)std::max(max_ctx, 0) + kBS - 1) / kBS;
+  const int64_t pb = part / kBS;
+  // a prefix leaves at least one token to the tail
+  c.s_max = (int32_t)std::max<int64_t>(
+      0, std::min<int64_t>(max_prefix, ((int64_t)std::max(max_ctx, 1) - 1) / kBS));
+  const int64_t n_pp = (c.s_max + pb - 1) / pb;
+  const int64_t n_pt = nblk == 0 ? 1 : (nblk + pb - 1) / pb;
+  c.x_dim = (int32_t)std::max(n_pp, n_pt);
+  c.ws.n_p_max = (int32_t)(n_pp + n_pt);
+  if (c.ws.n_p_max <= 1) return c;
+  const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)c.ws.n_p_max;
+  c.ws.ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+  c.ws.o_bytes = rows * kD * sizeof(float);
+  c.ws.total = c.ws.ml_bytes + c.ws.o_bytes;
+  return c;
+}
+
 // Kernel variants, chosen once per process.  Environment overrides exist for
 // measurement (A/B runs of the same build); the defaults are the measured
 // best.
@@ -964,6 +1105,11 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   a.v_bscale = plan->dyn ? v_bscale : nullptr;
   a.new_k = a.new_v = nullptr;
   a.k_wr = a.v_wr = nullptr;
+  a.casc_prefix = nullptr;
+  a.casc_groups = nullptr;
+  a.casc_items = a.casc_chunks = a.casc_cap = a.casc_m = a.casc_max = 0;
+  a.seq_order = nullptr;
+  a.nseq = num_seqs;
   a.k_enc_scale = k_scale;
   a.v_enc_scale = v_scale;
   // FP8 tiles decoded by bit operations hold code / 256: fold the 256 back
@@ -1000,13 +1146,31 @@ extern "C" uint64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_h
 }
 
 
+// LDS of a partition workgroup: the wave merge for `cols` columns per wave,
+// the kept bytes of the newest token, the prefix item's member per column.
+static size_t partition_lds(int nw, int cols, bool append, bool casc) {
+  return (size_t)(nw * cols * kD + 2 * nw * 16) * sizeof(float) +
+         (append || casc ? kKeepBytes : 0) + (casc ? kMaxG * sizeof(int) : 0);
+}
+
 template <bool kFP8, bool kHw, bool kSplit, int kPD, int kNW, bool kDyn = false,
-          bool kAppend = false>
+          bool kAppend = false, bool kCasc = false>
 static void launch_partition_v(dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  const size_t lds = (size_t)(kNW * a.g * kD + 2 * kNW * 16) * sizeof(float) +
-                     (kAppend ? kKeepBytes : 0);
-  decode_partition_kernel<kFP8, kHw, kSplit, kPD, kNW, kDyn, kAppend>
+  const size_t lds = partition_lds(kNW, kCasc ? kMaxG : a.g, kAppend, kCasc);
+  decode_partition_kernel<kFP8, kHw, kSplit, kPD, kNW, kDyn, kAppend, kCasc>
       <<<grid, dim3(kNW * kWave), lds, s>>>(a);
+}
+
+// Cascade over shared prefixes: the default family (FP8: hardware convert,
+// split probabilities; one tile in flight), with or without the newest
+// token's write.
+template <bool kFP8, bool kAppend>
+static void launch_partition_casc(int nw, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  switch (nw) {
+    case 1: return launch_partition_v<kFP8, kFP8, true, 1, 1, false, kAppend, true>(grid, s, a);
+    case 2: return launch_partition_v<kFP8, kFP8, true, 1, 2, false, kAppend, true>(grid, s, a);
+    default: return launch_partition_v<kFP8, kFP8, true, 1, 4, false, kAppend, true>(grid, s, a);
+  }
 }
 
 // Writing the newest token too: the default family (FP8: hardware convert,
@@ -1300,6 +1464,90 @@ extern "C" pkv_status pkv_paged_attention_decode_append(
   if (st != PKV_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_partitions_append(pl, num_seqs, s);
+  if (st != PKV_OK) return st;
+  return run_reduce(pl, num_seqs, s);
+}
+
+extern "C" uint64_t pkv_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                       int32_t num_kv_heads,
+                                                       int32_t max_context_len,
+                                                       int32_t max_prefix_blocks, int32_t dtype,
+                                                       int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      max_prefix_blocks < 0)
+    return 0;
+  if (dtype != PKV_F16 && dtype != PKV_FP8_E4M3FN) return 0;
+  const int32_t part =
+      resolve_partition(num_seqs, num_kv_heads, max_context_len, dtype, partition_size);
+  if (part <= 0) return 0;
+  return casc_layout(num_seqs, num_q_heads, max_context_len, part, max_prefix_blocks).ws.total;
+}
+
+extern "C" pkv_status pkv_paged_attention_decode_cascade(
+    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, const int32_t* prefix_blocks,
+    const int32_t* prefix_groups, int32_t num_groups, int32_t group_cap,
+    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream) {
+  if ((key == nullptr) != (value == nullptr)) return PKV_ERR_INVALID_ARG;
+  if (num_groups < 0 || max_prefix_blocks < 0) return PKV_ERR_INVALID_ARG;
+  if (num_groups > 0 && (group_cap <= 0 || !prefix_groups || !prefix_blocks))
+    return PKV_ERR_INVALID_ARG;
+  DecodePlan pl;
+  // the plain plan's workspace is never larger than the cascade's
+  pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                              context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
+                              max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (key) {
+    st = set_append(&pl, num_seqs, key, value, k_pool, v_pool);
+    if (st != PKV_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeArgs& a = pl.a;
+  const int32_t part = a.part_blocks * kBS;
+  const CascLayout cl =
+      casc_layout(num_seqs, num_q_heads, max_context_len, part,
+                  num_groups > 0 ? max_prefix_blocks : 0);
+  if (cl.ws.total > 0) {
+    if (!workspace || workspace_bytes < cl.ws.total) return PKV_ERR_WORKSPACE;
+    a.ws_ml = static_cast<float*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + cl.ws.ml_bytes);
+  }
+  a.n_p_max = cl.ws.n_p_max;
+  a.seq_order = seq_order;
+  pl.need_reduce = cl.ws.n_p_max > 1;
+  const int members = kMaxG / a.g;  // MFMA columns of one wave, G per member
+  const int64_t chunks = num_groups > 0 ? (group_cap + members - 1) / members : 0;
+  const int64_t items = (int64_t)num_groups * chunks;
+  if (items + num_seqs > 65535) return PKV_ERR_INVALID_ARG;  // grid z
+  if (num_groups > 0 && cl.s_max > 0) {
+    a.casc_prefix = prefix_blocks;
+    a.casc_groups = prefix_groups;
+    a.casc_items = (int32_t)items;
+    a.casc_chunks = (int32_t)chunks;
+    a.casc_cap = group_cap;
+    a.casc_m = members;
+    a.casc_max = cl.s_max;
+  }
+  // waves per workgroup as for the plain kernel, within 64 KiB of LDS at 16
+  // columns per wave
+  int nw = waves_for(pl);
+  while (nw > 1 && partition_lds(nw, kMaxG, key != nullptr, true) > 65536) nw /= 2;
+  const dim3 grid((unsigned)cl.x_dim, (unsigned)a.hkv, (unsigned)(a.casc_items + num_seqs));
+  (void)hipGetLastError();
+  if (pl.fp8)
+    key ? launch_partition_casc<true, true>(nw, grid, s, a)
+        : launch_partition_casc<true, false>(nw, grid, s, a);
+  else
+    key ? launch_partition_casc<false, true>(nw, grid, s, a)
+        : launch_partition_casc<false, false>(nw, grid, s, a);
+  st = launch_status();
   if (st != PKV_OK) return st;
   return run_reduce(pl, num_seqs, s);
 }

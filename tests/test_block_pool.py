@@ -176,3 +176,81 @@ def test_shared_prefix_blocks_after_forks():
     pool.free(a)
     assert pool.shared_prefix_blocks(b) == 0
     assert pool.shared_prefix_blocks(999) == -1
+
+
+def test_prefix_groups_from_forks():
+    """Forks of one prompt form a group whose prefix is the blocks they all
+    still hold: the prompt's partial last block is copied on the first
+    private appends, so only its whole blocks stay shared."""
+    pool = pkv.BlockPool(64)
+    root = pool.create()
+    pool.append(root, 40)               # blocks 0, 1 full; block 2 holds 8 tokens
+    kids = [pool.fork(root) for _ in range(2)]
+    for s in [root] + kids:
+        pool.append(s, 5)               # copy-on-write of block 2 for two of them
+    solo = pool.create()
+    pool.append(solo, 100)
+    batch = [solo, kids[0], root, kids[1]]
+    prefix, groups, mx = pool.prefix_groups(batch, 8)
+    assert list(prefix) == [0, 2, 2, 2] and mx == 2
+    assert groups.tolist() == [[1, 2, 3, -1, -1, -1, -1, -1]]
+
+
+def test_prefix_groups_keep_a_token_after_the_prefix():
+    """A fork with nothing appended holds the whole prompt: the prefix stops
+    one token short of every member's end (a block before it here)."""
+    pool = pkv.BlockPool(16)
+    root = pool.create()
+    pool.append(root, 32)
+    kid = pool.fork(root)               # both: 2 full shared blocks, L = 32
+    prefix, groups, mx = pool.prefix_groups([root, kid], 4)
+    assert list(prefix) == [1, 1] and mx == 1 and groups.tolist() == [[0, 1, -1, -1]]
+    one = pool.create()
+    pool.append(one, 16)
+    kid1 = pool.fork(one)               # L = 16: no whole block can go before a token
+    prefix, groups, mx = pool.prefix_groups([one, kid1], 4)
+    assert list(prefix) == [0, 0] and groups.shape == (0, 4) and mx == 0
+
+
+def test_prefix_groups_split_at_the_cap_and_errors():
+    pool = pkv.BlockPool(64)
+    root = pool.create()
+    pool.append(root, 64)
+    fam = [root] + [pool.fork(root) for _ in range(4)]
+    for s in fam:
+        pool.append(s, 3)
+    prefix, groups, mx = pool.prefix_groups(fam, 2)
+    assert list(prefix) == [4] * 5 and mx == 4
+    assert groups.tolist() == [[0, 1], [2, 3], [4, -1]]
+    # group arrays too small: counts set, INVALID_ARG
+    import ctypes
+    import numpy as np
+    L = pkv.load_library()
+    seqs = np.array(fam, dtype=np.int32)
+    pre = np.zeros(5, dtype=np.int32)
+    g = np.zeros((2, 2), dtype=np.int32)
+    ng, m = ctypes.c_int32(), ctypes.c_int32()
+    st = L.pkv_pool_prefix_groups(pool._h, seqs.ctypes.data, 5, 2, 2, pre.ctypes.data,
+                                  g.ctypes.data, ctypes.byref(ng), ctypes.byref(m), None)
+    assert st == pkv.PKV_ERR_INVALID_ARG and ng.value == 3 and m.value == 4
+    with pytest.raises(pkv.PkvError):
+        pool.prefix_groups([root, 12345], 2)
+
+
+def test_prefix_groups_order_longest_tail_first():
+    """The scheduling order: decreasing tokens after each entry's prefix
+    (the whole length for entries in no group), ties in batch order."""
+    pool = pkv.BlockPool(64)
+    root = pool.create()
+    pool.append(root, 48)               # 3 shared whole blocks
+    kid = pool.fork(root)
+    pool.append(root, 10)               # tail 10 (+ nothing copied: block-aligned)
+    pool.append(kid, 30)                # tail 30
+    solo = pool.create()
+    pool.append(solo, 20)               # no group: tail = 20
+    tie = pool.create()
+    pool.append(tie, 10)                # 10, after root's 10 in batch order
+    prefix, groups, mx, order = pool.prefix_groups([root, solo, kid, tie], 4,
+                                                   with_order=True)
+    assert list(prefix) == [3, 0, 3, 0] and mx == 3
+    assert list(order) == [2, 1, 0, 3]
