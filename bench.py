@@ -403,8 +403,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cascade", choices=("auto", "on", "off"), default="auto",
                     help="decode each group's shared prefix once for the group "
-                         "(pkv_paged_attention_decode_cascade); auto = when the host pool "
-                         "finds prefix groups in the batch and the scales are per tensor")
+                         "(pkv_paged_attention_decode_cascade[_dynamic]); auto = when the "
+                         "host pool finds prefix groups in the batch")
     ap.add_argument("--graph", action="store_true",
                     help="replay the decode step as one captured HIP graph instead of "
                          "launching its kernels one by one")
@@ -482,10 +482,7 @@ def main() -> int:
     P = pkv.pkv_decode_partition_size(B, Hkv, Lmax, layout.dtype, req)
     # prefix groups of the batch, found by the host pool from the forks
     prefix, garr, max_pre, order = pool.prefix_groups(seqs, 8, with_order=True)
-    cascade = args.cascade == "on" or (args.cascade == "auto" and garr.shape[0] > 0 and not dyn)
-    if cascade and dyn:
-        print("bench.py: the cascade decode takes per-tensor scales", file=sys.stderr)
-        return 2
+    cascade = args.cascade == "on" or (args.cascade == "auto" and garr.shape[0] > 0)
     if cascade:
         d_prefix = torch.from_numpy(prefix).to(dev)
         d_groups = torch.from_numpy(garr).to(dev) if garr.shape[0] else None
@@ -523,6 +520,17 @@ def main() -> int:
     del key_src, val_src
 
     def step(ev=None):
+        if dyn and cascade:
+            write(new_k, new_v, d_step_slots)
+            if ev is not None:
+                ev[0].record()
+            pkv.pkv_paged_attention_decode_cascade_dynamic(
+                out, q, k_pool, v_pool, k_bs, v_bs, d_tables, d_lens, Lmax, layout, sm_scale,
+                d_prefix, d_groups, max_pre, P, ws, shared_prefix_blocks=d_shared,
+                seq_order=d_order)
+            if ev is not None:
+                ev[1].record()
+            return
         if dyn:
             write(new_k, new_v, d_step_slots)
             if ev is not None:

@@ -302,6 +302,22 @@ pkv_status pkv_paged_attention_decode_cascade(
     float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
     void* stream);
 
+/* The cascade over a cache with per-(block, KV head) FP8 scales (the
+ * decode of pkv_paged_attention_decode_dynamic, with the prefix groups,
+ * order and workspace of pkv_paged_attention_decode_cascade; decode only:
+ * the newest rows are written first by pkv_reshape_and_cache_dynamic).
+ * FP8 layouts only (UNSUPPORTED otherwise); null block scales:
+ * INVALID_ARG. */
+pkv_status pkv_paged_attention_decode_cascade_dynamic(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const float* k_block_scales, const float* v_block_scales, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+    const int32_t* prefix_blocks, const int32_t* prefix_groups, int32_t num_groups,
+    int32_t group_cap, int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs,
+    int32_t num_q_heads, int32_t max_context_len, const pkv_cache_layout* layout,
+    float sm_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream);
+
 /* Workspace of pkv_paged_attention_decode_cascade: room for each sequence's
  * prefix partitions (ceil(16 * max_prefix_blocks / P)) and tail partitions;
  * 0 when no sequence needs a merge or on invalid arguments. */

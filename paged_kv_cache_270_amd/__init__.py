@@ -94,6 +94,9 @@ def load_library():
         "pkv_paged_attention_decode_cascade": ([P, P, P, P, P, P, P, i32, P, P, P, P, i32, i32,
                                                 i32, P, i32, i32, i32, LP, f32, f32, f32, i32,
                                                 P, u64, P], i32),
+        "pkv_paged_attention_decode_cascade_dynamic": ([P, P, P, P, P, P, P, i32, P, P, P, P,
+                                                        i32, i32, i32, P, i32, i32, i32, LP,
+                                                        f32, i32, P, u64, P], i32),
         "pkv_decode_cascade_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], u64),
         "pkv_pool_prefix_groups": ([P, P, i32, i32, i32, P, P, ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), P], i32),
@@ -358,15 +361,7 @@ def pkv_paged_attention_decode_cascade(out, q, key, value, k_pool, v_pool, block
         kp = vp = None
     else:
         kp, vp = _new_rows(key, value, B, layout)
-    if prefix_groups is None or prefix_groups.numel() == 0:
-        n_groups, cap, gp, pp = 0, 1, None, None
-    else:
-        _require(prefix_groups, torch.int32, "prefix_groups")
-        _require(prefix_blocks, torch.int32, "prefix_blocks")
-        if prefix_groups.dim() != 2 or prefix_blocks.numel() != B:
-            raise ValueError("prefix_groups must be [n_groups][group_cap], prefix_blocks [B]")
-        n_groups, cap = prefix_groups.shape
-        gp, pp = _ptr(prefix_groups), _ptr(prefix_blocks)
+    n_groups, cap, gp, pp = _cascade_groups(prefix_blocks, prefix_groups, B)
     if seq_order is not None:
         _require(seq_order, torch.int32, "seq_order")
         if seq_order.numel() != B:
@@ -384,6 +379,52 @@ def pkv_paged_attention_decode_cascade(out, q, key, value, k_pool, v_pool, block
         sm_scale, k_scale,
         v_scale, partition_size, _ptr(workspace), nbytes, _stream(stream)),
         "pkv_paged_attention_decode_cascade")
+
+
+def _cascade_groups(prefix_blocks, prefix_groups, B):
+    import torch
+    if prefix_groups is None or prefix_groups.numel() == 0:
+        return 0, 1, None, None
+    _require(prefix_groups, torch.int32, "prefix_groups")
+    _require(prefix_blocks, torch.int32, "prefix_blocks")
+    if prefix_groups.dim() != 2 or prefix_blocks.numel() != B:
+        raise ValueError("prefix_groups must be [n_groups][group_cap], prefix_blocks [B]")
+    n_groups, cap = prefix_groups.shape
+    return n_groups, cap, _ptr(prefix_groups), _ptr(prefix_blocks)
+
+
+def pkv_paged_attention_decode_cascade_dynamic(out, q, k_pool, v_pool, k_block_scales,
+                                               v_block_scales, block_tables, context_lens,
+                                               max_context_len: int, layout: CacheLayout,
+                                               sm_scale: float, prefix_blocks, prefix_groups,
+                                               max_prefix_blocks: int, partition_size: int = 0,
+                                               workspace=None, stream=None,
+                                               shared_prefix_blocks=None,
+                                               seq_order=None) -> None:
+    """The cascade decode over per-(block, KV head) scales (fp32
+    [num_blocks][Hkv] device tensors); decode only."""
+    import torch
+    B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
+    _require(k_block_scales, torch.float32, "k_block_scales")
+    _require(v_block_scales, torch.float32, "v_block_scales")
+    n_groups, cap, gp, pp = _cascade_groups(prefix_blocks, prefix_groups, B)
+    if seq_order is not None:
+        _require(seq_order, torch.int32, "seq_order")
+        if seq_order.numel() != B:
+            raise ValueError("seq_order must hold one entry per sequence")
+    need = pkv_decode_cascade_workspace_bytes(B, Hq, layout.num_kv_heads, max_context_len,
+                                              max_prefix_blocks if n_groups else 0,
+                                              layout.dtype, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().pkv_paged_attention_decode_cascade_dynamic(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_block_scales),
+        _ptr(v_block_scales), _ptr(block_tables), mb, _ptr(context_lens),
+        _hint(shared_prefix_blocks, B), pp, gp, n_groups, cap, max_prefix_blocks,
+        _ptr(seq_order), B, Hq, max_context_len, ctypes.byref(layout), sm_scale,
+        partition_size, _ptr(workspace), nbytes, _stream(stream)),
+        "pkv_paged_attention_decode_cascade_dynamic")
 
 
 def pkv_copy_blocks(k_pool, v_pool, layout: CacheLayout, src_dst_pairs, stream=None) -> None:

@@ -396,11 +396,14 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
 // kvh*G + j and, in each tile, tokens 4qg .. 4qg+3.  Each wave keeps kPD
 // tiles in flight while it computes on another.
 // With per-block scales the kernel is held to 128 VGPRs (4 waves per SIMD);
-// the compiler fits it without spilling.  kAppend: the kernel also writes
-// each sequence's newest token (steps 1-3 above).
+// the compiler fits it without spilling (the cascade variant, 2 VGPRs over,
+// to 168: 3 waves per SIMD).  kAppend: the kernel also writes each
+// sequence's newest token (steps 1-3 above).  kCasc: the cascade over shared
+// prefixes (prefix items, then tails).
 template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false,
           bool kAppend = false, bool kCasc = false>
-__global__ void __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kDyn ? 4 : 1)))
+__global__ void __launch_bounds__(kNW * kWave)
+__attribute__((amdgpu_waves_per_eu(kDyn ? (kCasc ? 3 : 4) : 1)))
 decode_partition_kernel(DecodeArgs a) {
   // [kNW][CS][D] outputs, then [kNW][16] max and sum, then (kAppend) the
   // newest token's kept bytes, then (kCasc) the item's member per column
@@ -411,8 +414,7 @@ decode_partition_kernel(DecodeArgs a) {
   const int qg = lane >> 4;
   const int p = blockIdx.x, kvh = blockIdx.y;
   const int G = a.g;
-  constexpr int kCS = kCasc ? kMaxG : 0;  // LDS column stride (0: G)
-  const int CS = kCasc ? kCS : G;
+  const int CS = kCasc ? kMaxG : G;  // LDS merge: columns per wave
   int* memb = reinterpret_cast<int*>(smem + kNW * CS * kD + 2 * kNW * 16 + kKeepBytes / 4);
 
   int b = blockIdx.z;  // the sequence (a prefix item: its group's first member)
@@ -1173,6 +1175,15 @@ static void launch_partition_casc(int nw, dim3 grid, hipStream_t s, const Decode
   }
 }
 
+// Cascade over per-block scales (FP8, decode only).
+static void launch_partition_casc_dyn(int nw, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  switch (nw) {
+    case 1: return launch_partition_v<true, true, true, 1, 1, true, false, true>(grid, s, a);
+    case 2: return launch_partition_v<true, true, true, 1, 2, true, false, true>(grid, s, a);
+    default: return launch_partition_v<true, true, true, 1, 4, true, false, true>(grid, s, a);
+  }
+}
+
 // Writing the newest token too: the default family (FP8: hardware convert,
 // split probabilities; one tile in flight) at every wave count.
 template <bool kFP8>
@@ -1483,37 +1494,20 @@ extern "C" uint64_t pkv_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t
   return casc_layout(num_seqs, num_q_heads, max_context_len, part, max_prefix_blocks).ws.total;
 }
 
-extern "C" pkv_status pkv_paged_attention_decode_cascade(
-    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
-    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* shared_prefix_blocks, const int32_t* prefix_blocks,
-    const int32_t* prefix_groups, int32_t num_groups, int32_t group_cap,
-    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
-    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
-    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-    void* stream) {
-  if ((key == nullptr) != (value == nullptr)) return PKV_ERR_INVALID_ARG;
-  if (num_groups < 0 || max_prefix_blocks < 0) return PKV_ERR_INVALID_ARG;
-  if (num_groups > 0 && (group_cap <= 0 || !prefix_groups || !prefix_blocks))
-    return PKV_ERR_INVALID_ARG;
-  DecodePlan pl;
-  // the plain plan's workspace is never larger than the cascade's
-  pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
-                              context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
-                              max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
-                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
-  if (st != PKV_OK) return st;
-  if (num_seqs == 0) return PKV_OK;
-  if (key) {
-    st = set_append(&pl, num_seqs, key, value, k_pool, v_pool);
-    if (st != PKV_OK) return st;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// The cascade after plan_decode: its workspace layout, the prefix items,
+// the partition kernel (per-tensor scales: with or without the newest
+// token's write; per-block scales: decode only), then the merge.
+static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
+                              const int32_t* prefix_groups, int32_t num_groups,
+                              int32_t group_cap, int32_t max_prefix_blocks,
+                              const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_context_len, void* workspace,
+                              uint64_t workspace_bytes, hipStream_t s) {
   DecodeArgs& a = pl.a;
+  const bool append = a.new_k != nullptr;
   const int32_t part = a.part_blocks * kBS;
-  const CascLayout cl =
-      casc_layout(num_seqs, num_q_heads, max_context_len, part,
-                  num_groups > 0 ? max_prefix_blocks : 0);
+  const CascLayout cl = casc_layout(num_seqs, num_q_heads, max_context_len, part,
+                                    num_groups > 0 ? max_prefix_blocks : 0);
   if (cl.ws.total > 0) {
     if (!workspace || workspace_bytes < cl.ws.total) return PKV_ERR_WORKSPACE;
     a.ws_ml = static_cast<float*>(workspace);
@@ -1538,18 +1532,83 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade(
   // waves per workgroup as for the plain kernel, within 64 KiB of LDS at 16
   // columns per wave
   int nw = waves_for(pl);
-  while (nw > 1 && partition_lds(nw, kMaxG, key != nullptr, true) > 65536) nw /= 2;
+  while (nw > 1 && partition_lds(nw, kMaxG, append, true) > 65536) nw /= 2;
   const dim3 grid((unsigned)cl.x_dim, (unsigned)a.hkv, (unsigned)(a.casc_items + num_seqs));
   (void)hipGetLastError();
-  if (pl.fp8)
-    key ? launch_partition_casc<true, true>(nw, grid, s, a)
-        : launch_partition_casc<true, false>(nw, grid, s, a);
+  if (pl.dyn)
+    launch_partition_casc_dyn(nw, grid, s, a);
+  else if (pl.fp8)
+    append ? launch_partition_casc<true, true>(nw, grid, s, a)
+           : launch_partition_casc<true, false>(nw, grid, s, a);
   else
-    key ? launch_partition_casc<false, true>(nw, grid, s, a)
-        : launch_partition_casc<false, false>(nw, grid, s, a);
-  st = launch_status();
+    append ? launch_partition_casc<false, true>(nw, grid, s, a)
+           : launch_partition_casc<false, false>(nw, grid, s, a);
+  const pkv_status st = launch_status();
   if (st != PKV_OK) return st;
   return run_reduce(pl, num_seqs, s);
+}
+
+static pkv_status check_groups(int32_t num_groups, int32_t group_cap, int32_t max_prefix_blocks,
+                               const int32_t* prefix_groups, const int32_t* prefix_blocks) {
+  if (num_groups < 0 || max_prefix_blocks < 0) return PKV_ERR_INVALID_ARG;
+  if (num_groups > 0 && (group_cap <= 0 || !prefix_groups || !prefix_blocks))
+    return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_paged_attention_decode_cascade(
+    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, const int32_t* prefix_blocks,
+    const int32_t* prefix_groups, int32_t num_groups, int32_t group_cap,
+    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream) {
+  if ((key == nullptr) != (value == nullptr)) return PKV_ERR_INVALID_ARG;
+  pkv_status st =
+      check_groups(num_groups, group_cap, max_prefix_blocks, prefix_groups, prefix_blocks);
+  if (st != PKV_OK) return st;
+  DecodePlan pl;
+  // the plain plan's workspace is never larger than the cascade's
+  st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                   shared_prefix_blocks, num_seqs, num_q_heads, max_context_len, layout,
+                   sm_scale, k_scale, v_scale, nullptr, nullptr, partition_size, workspace,
+                   workspace_bytes, true, &pl);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (key) {
+    st = set_append(&pl, num_seqs, key, value, k_pool, v_pool);
+    if (st != PKV_OK) return st;
+  }
+  return run_cascade(pl, prefix_blocks, prefix_groups, num_groups, group_cap,
+                     max_prefix_blocks, seq_order, num_seqs, num_q_heads, max_context_len,
+                     workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" pkv_status pkv_paged_attention_decode_cascade_dynamic(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const float* k_block_scales, const float* v_block_scales, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+    const int32_t* prefix_blocks, const int32_t* prefix_groups, int32_t num_groups,
+    int32_t group_cap, int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs,
+    int32_t num_q_heads, int32_t max_context_len, const pkv_cache_layout* layout,
+    float sm_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+    void* stream) {
+  if (!k_block_scales || !v_block_scales) return PKV_ERR_INVALID_ARG;
+  pkv_status st =
+      check_groups(num_groups, group_cap, max_prefix_blocks, prefix_groups, prefix_blocks);
+  if (st != PKV_OK) return st;
+  DecodePlan pl;
+  st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                   shared_prefix_blocks, num_seqs, num_q_heads, max_context_len, layout,
+                   sm_scale, 1.0f, 1.0f, k_block_scales, v_block_scales, partition_size,
+                   workspace, workspace_bytes, true, &pl);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  return run_cascade(pl, prefix_blocks, prefix_groups, num_groups, group_cap,
+                     max_prefix_blocks, seq_order, num_seqs, num_q_heads, max_context_len,
+                     workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" pkv_status pkv_paged_attention_decode_dynamic(

@@ -290,3 +290,44 @@ def test_cascade_rejects_bad_arguments():
         int(prefix.max()), None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
         prep.sm_scale, prep.k_scale, prep.v_scale, 64, None, 0, None)
     assert st in (pkv.PKV_ERR_INVALID_ARG, pkv.PKV_ERR_WORKSPACE)
+
+
+@pytest.mark.parametrize("ps", [0, 16, 512])
+def test_cascade_block_scales_matches_oracle(ps):
+    """Per-(block, KV head) FP8 scales: every slot of every block written by
+    the oracle's dynamic write from rows of varying magnitude (so scales
+    differ from block to block), then the cascade against the oracle's
+    decode with block scales."""
+    wl, groups, prefix = _grouped(SPEC, SOLO, 8, 2, True, seed=79 + ps)
+    NB, Hkv = wl.num_blocks, wl.num_kv_heads
+    rng = np.random.default_rng(80 + ps)
+    T = NB * 16
+    mag = np.exp(1.5 * rng.standard_normal((T, 1, 1)))
+    k = (rng.standard_normal((T, Hkv, D)) * mag).astype(np.float16)
+    v = (rng.standard_normal((T, Hkv, D)) * mag[::-1]).astype(np.float16)
+    n = NB * Hkv * 16 * D
+    kh, vh = np.zeros(n, np.uint8), np.zeros(n, np.uint8)
+    ksh, vsh = np.zeros((NB, Hkv), np.float32), np.zeros((NB, Hkv), np.float32)
+    oracle.reshape_and_cache_dynamic(k, v, kh, vh, ksh, vsh, np.arange(T, dtype=np.int64), Hkv)
+    layout = pkv.CacheLayout(NB, Hkv, pkv.PKV_FP8_E4M3FN)
+    q = workloads.randn_f16((wl.num_seqs, 8, D), 81 + ps, "cuda")
+    sm = float(np.float32(1 / np.sqrt(D)))
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    tail = wl.context_lens.astype(np.int64) - 16 * prefix
+    order = np.argsort(-tail, kind="stable").astype(np.int32)
+    pkv.pkv_paged_attention_decode_cascade_dynamic(
+        out, q, torch.from_numpy(kh).cuda(), torch.from_numpy(vh).cuda(),
+        torch.from_numpy(ksh).cuda(), torch.from_numpy(vsh).cuda(),
+        torch.from_numpy(wl.block_tables).cuda(), torch.from_numpy(wl.context_lens).cuda(),
+        wl.max_context_len, layout, sm, torch.from_numpy(prefix).cuda(),
+        torch.from_numpy(_group_array(groups, 8)).cuda(), int(prefix.max()), ps,
+        seq_order=torch.from_numpy(order).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.paged_attention_decode_dynamic(q.cpu().numpy(), kh, vh, ksh, vsh,
+                                                wl.block_tables, wl.context_lens, Hkv, sm,
+                                                THREADS)
+    got = out.cpu().numpy()
+    err = max_err(got, ref)
+    print(f"[parity] cascade block scales P={ps}: max abs err {err:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL[True]
