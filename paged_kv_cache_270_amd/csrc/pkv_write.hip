@@ -10,6 +10,7 @@
 //              generación"
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -102,18 +103,27 @@ constexpr int64_t kRowWriteMaxTokens = 512;
 // of the 16 rows and writes each tile as one contiguous run (2 KiB FP8 /
 // 4 KiB fp16), so the scattered layout costs no partial-line writes.  Other
 // groups (a decode step: one token per sequence) store row by row.
+constexpr int kFillWaves = 4;  // independent waves per workgroup
+
 template <bool kFP8>
-__global__ void __launch_bounds__(kWave)
+__global__ void __launch_bounds__(kFillWaves * kWave)
 reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                          const int64_t* __restrict__ slots, int64_t num_tokens, int hkv,
-                         int64_t num_slots, float k_scale, float v_scale) {
+                         int64_t num_slots, float k_scale, float v_scale, uint32_t units) {
   constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
-  __shared__ __align__(16) uint8_t lk[kTileBytes];
-  __shared__ __align__(16) uint8_t lv[kTileBytes];
-  const int lane = threadIdx.x;
-  const int h = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * kBS;
+  __shared__ __align__(16) uint8_t lk_all[kFillWaves][kTileBytes];
+  __shared__ __align__(16) uint8_t lv_all[kFillWaves][kTileBytes];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  uint8_t* lk = lk_all[w];
+  uint8_t* lv = lv_all[w];
+  // one (16-token group, KV head) unit per wave; the head varies fastest:
+  // neighbouring waves read neighbouring 256-byte parts of the same rows
+  const uint32_t unit = blockIdx.x * kFillWaves + w;
+  if (unit >= units) return;  // whole waves
+  const int h = (int)(unit % (unsigned)hkv);
+  const int64_t t0 = (int64_t)(unit / (unsigned)hkv) * kBS;
   const int ntok = (int)min<int64_t>(kBS, num_tokens - t0);
   const int64_t my_slot = lane < ntok ? slots[t0 + lane] : -1;
   const int64_t s0 = __shfl(my_slot, 0, kWave);
@@ -163,7 +173,10 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
       for (int e = 0; e < 8; ++e) vb[e * 8] = vh[e];
     }
   }
-  __syncthreads();
+  // the wave's own tiles: order its LDS writes before its reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int64_t tile = (s0 >> 4) * hkv + h;
   u32x4* kt = reinterpret_cast<u32x4*>(k_pool + tile * kTileBytes);
   u32x4* vt = reinterpret_cast<u32x4*>(v_pool + tile * kTileBytes);
@@ -455,7 +468,6 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
     return PKV_ERR_INVALID_ARG;
   const int64_t groups = ((int64_t)num_tokens + kBS - 1) / kBS;
   const int64_t num_slots = (int64_t)layout->num_blocks * kBS;
-  const dim3 grid((unsigned)groups, (unsigned)layout->num_kv_heads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const int64_t total = (int64_t)num_tokens * layout->num_kv_heads * 16;
@@ -473,17 +485,30 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
           (uint32_t)total, (uint32_t)layout->num_kv_heads, num_slots, 1.0f, 1.0f);
     return launch_status();
   }
-  if (fp8)
-    reshape_and_cache_kernel<true><<<grid, dim3(kWave), 0, s>>>(
-        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
-        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping, num_tokens,
-        layout->num_kv_heads, num_slots, k_scale, v_scale);
-  else
-    reshape_and_cache_kernel<false><<<grid, dim3(kWave), 0, s>>>(
-        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
-        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slot_mapping, num_tokens,
-        layout->num_kv_heads, num_slots, 1.0f, 1.0f);
-  return launch_status();
+  // one workgroup per (16-token group, KV head), in launches of at most
+  // 2^24 workgroups
+  const int hkv = layout->num_kv_heads;
+  const int64_t max_groups = std::max<int64_t>(1, ((int64_t)1 << 24) / hkv);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    const int64_t tok0 = g0 * kBS;
+    const int64_t ntok = std::min<int64_t>((int64_t)num_tokens - tok0, ng * kBS);
+    const u32x4* kin = static_cast<const u32x4*>(key) + tok0 * hkv * 16;
+    const u32x4* vin = static_cast<const u32x4*>(value) + tok0 * hkv * 16;
+    const uint32_t units = (uint32_t)(ng * hkv);
+    const dim3 grid((units + kFillWaves - 1) / kFillWaves);
+    if (fp8)
+      reshape_and_cache_kernel<true><<<grid, dim3(kFillWaves * kWave), 0, s>>>(
+          kin, vin, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+          slot_mapping + tok0, ntok, hkv, num_slots, k_scale, v_scale, units);
+    else
+      reshape_and_cache_kernel<false><<<grid, dim3(kFillWaves * kWave), 0, s>>>(
+          kin, vin, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+          slot_mapping + tok0, ntok, hkv, num_slots, 1.0f, 1.0f, units);
+    const pkv_status st2 = launch_status();
+    if (st2 != PKV_OK) return st2;
+  }
+  return PKV_OK;
 }
 
 extern "C" pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const pkv_cache_layout* layout,
