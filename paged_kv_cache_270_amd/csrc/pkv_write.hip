@@ -130,7 +130,39 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
   const bool in_order = lane >= kBS || my_slot == s0 + lane;
   const bool whole = ntok == kBS && s0 >= 0 && (s0 & (kBS - 1)) == 0 && s0 + kBS <= num_slots &&
                      __all(in_order);
-  if (!whole) {  // row by row: 16 runs of 8 channels per token
+  if (!whole) {
+    // At most two runs of consecutive slots, each inside one block (the end
+    // of one sequence, then the start of the next, as in a batched prefill
+    // whose lengths are not multiples of 16): write each run by aligned
+    // quads of block offsets, so that every store instruction covers whole
+    // 16-byte runs of the V tile wherever the run holds the quad's 4 tokens.
+    const int64_t prev = __shfl(my_slot, lane > 0 ? lane - 1 : 0, kWave);
+    const bool brk = lane > 0 && lane < ntok && my_slot != prev + 1;
+    const bool ok = lane >= ntok || (my_slot >= 0 && my_slot < num_slots);
+    const uint64_t breaks = __ballot(brk);
+    const int len_a = breaks ? (int)__builtin_ctzll(breaks) : ntok;  // run A: tokens [0, len_a)
+    const int64_t sb = __shfl(my_slot, len_a < kWave ? len_a : 0, kWave);
+    const int off_a = (int)(s0 & (kBS - 1)), off_b = (int)(sb & (kBS - 1));
+    if (__all(ok) && __popcll(breaks) <= 1 && off_a + len_a <= kBS &&
+        (len_a == ntok || off_b + (ntok - len_a) <= kBS)) {
+      for (int r = 0; r < (len_a == ntok ? 1 : 2); ++r) {  // wave-uniform
+        const int tok0 = r == 0 ? 0 : len_a;                // first token of the run
+        const int len = r == 0 ? len_a : ntok - len_a;
+        const int64_t slot0 = r == 0 ? s0 : sb;
+        const int off0 = (int)(slot0 & (kBS - 1));
+        const int64_t tile = (slot0 >> 4) * hkv + h;
+        const int c = lane & 15;
+        for (int q = off0 >> 2; q <= (off0 + len - 1) >> 2; ++q) {
+          const int o = q * 4 + (lane >> 4);                 // block offset of this lane
+          if (o < off0 || o >= off0 + len) continue;
+          const int64_t th = (t0 + tok0 + (o - off0)) * hkv + h;
+          store_rows8<kFP8>(k_pool, v_pool, tile, o, c, key[th * 16 + c], value[th * 16 + c],
+                            k_scale, v_scale);
+        }
+      }
+      return;
+    }
+    // anything else row by row: 16 runs of 8 channels per token
     for (int i = lane; i < ntok * 16; i += kWave) {
       const int64_t tok = t0 + (i >> 4);
       const int c = i & 15;

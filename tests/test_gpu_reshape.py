@@ -93,6 +93,32 @@ def test_whole_block_groups_and_row_by_row_groups_agree(fp8, hkv):
     assert np.array_equal(kd, kh) and np.array_equal(vd, vh)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("hkv", [1, 8])
+def test_batched_prefill_of_unaligned_sequences(fp8, hkv):
+    """One call writing several sequences' tokens back to back, as a batched
+    prefill does: each sequence fills its blocks from its current length on
+    (a fresh sequence from offset 0, a continued one from mid-block), and the
+    lengths are not multiples of 16, so most 16-token groups of the call hold
+    the end of one sequence and the start of the next (two runs in two
+    blocks).  Bit-exact against the oracle."""
+    rng = np.random.default_rng(70 + hkv + 10 * fp8)
+    nb = 200
+    free = list(rng.permutation(nb))
+    slots = []
+    for start, n in [(0, 37), (0, 5), (0, 16), (20, 100), (0, 1), (3, 63), (0, 250),
+                     (15, 2), (0, 47), (9, 90)]:
+        blocks = [free.pop() for _ in range(-(-(start + n) // 16))]
+        slots += [blocks[p // 16] * 16 + p % 16 for p in range(start, start + n)]
+    slots = np.asarray(slots, dtype=np.int64)
+    assert slots.size > 512                         # the tile-building kernel
+    T = slots.size
+    key = workloads.randn_f16((T, hkv, D), 71 + hkv)
+    value = workloads.randn_f16((T, hkv, D), 72 + hkv)
+    kd, vd, kh, vh = _write_both(key, value, slots, nb, hkv, fp8, 0.0123, 0.031)
+    assert np.array_equal(kd, kh) and np.array_equal(vd, vh)
+
+
 def test_fp16_write_is_a_raw_copy():
     x = torch.from_numpy(np.arange(65536, dtype=np.uint16).view(np.float16).reshape(256, 2, D)
                          .copy())
