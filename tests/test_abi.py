@@ -198,3 +198,56 @@ def test_append_entry_points_validate_before_launch():
         assert call(part=32, ws_bytes=16) == pkv.PKV_ERR_WORKSPACE
         assert fn(None, None, None, None, None, None, None, 4, None, None, 0, 4, 64,
                   ctypes.byref(f8), 0.1, 1.0, 1.0, 0, None, 0, None) == pkv.PKV_OK
+
+
+def test_cascade_workspace_closed_form():
+    """4 sequences x 8 query heads, contexts up to 1000 tokens (63 blocks),
+    256-token partitions (16 blocks), prefixes up to 20 blocks: 2 prefix
+    partitions + 4 tail partitions per sequence; rows of (max, sum) padded to
+    256 bytes, then rows of 128 floats."""
+    rows = 4 * 8 * (2 + 4)
+    want = (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
+    assert pkv.pkv_decode_cascade_workspace_bytes(4, 8, 2, 1000, 20, pkv.PKV_FP8_E4M3FN,
+                                                  256) == want == 99840
+    # no prefix: the plain decode's workspace
+    assert pkv.pkv_decode_cascade_workspace_bytes(4, 8, 2, 1000, 0, pkv.PKV_FP8_E4M3FN, 256) \
+        == pkv.pkv_decode_workspace_bytes(4, 8, 2, 1000, pkv.PKV_FP8_E4M3FN, 256) == 66560
+    # a prefix leaves a token to the tail: at most (1000 - 1) // 16 = 62 blocks
+    assert pkv.pkv_decode_cascade_workspace_bytes(4, 8, 2, 1000, 500, pkv.PKV_FP8_E4M3FN, 256) \
+        == pkv.pkv_decode_cascade_workspace_bytes(4, 8, 2, 1000, 62, pkv.PKV_FP8_E4M3FN, 256)
+    assert pkv.pkv_decode_cascade_workspace_bytes(4, 8, 2, 1000, -1, pkv.PKV_FP8_E4M3FN, 256) == 0
+
+
+def test_cascade_entry_points_validate_before_launch():
+    """Every call here is rejected (or is a no-op) before any HIP call."""
+    L = pkv.load_library()
+    f8 = pkv.CacheLayout(16, 2, pkv.PKV_FP8_E4M3FN)
+    f16 = pkv.CacheLayout(16, 2, pkv.PKV_F16)
+
+    # out, q, key, value, k_pool, v_pool, tables, max_blocks, lens, hint, prefix, groups,
+    # n_groups, cap, max_prefix, order, B, Hq, max_ctx, layout, sm, ks, vs, part, ws, bytes, s
+    def call(key=16, value=16, groups=16, prefix=16, ng=2, cap=8, mp=4, B=2, ws_bytes=1 << 20):
+        return L.pkv_paged_attention_decode_cascade(
+            16, 16, key, value, 16, 16, 16, 4, 16, None, prefix, groups, ng, cap, mp, None, B,
+            4, 64, ctypes.byref(f8), 0.1, 1.0, 1.0, 0, 256, ws_bytes, None)
+    assert call(key=None) == pkv.PKV_ERR_INVALID_ARG
+    assert call(value=None) == pkv.PKV_ERR_INVALID_ARG
+    assert call(ng=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert call(mp=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert call(groups=None) == pkv.PKV_ERR_INVALID_ARG
+    assert call(prefix=None) == pkv.PKV_ERR_INVALID_ARG
+    assert call(cap=0) == pkv.PKV_ERR_INVALID_ARG
+    assert call(ws_bytes=16) == pkv.PKV_ERR_WORKSPACE
+    # G = 2: one item per group of 8 members; 65534 items + 2 sequences exceed
+    # one grid dimension (65535)
+    assert call(ng=65534) == pkv.PKV_ERR_INVALID_ARG
+    assert call(B=0) == pkv.PKV_OK
+
+    def dyn(ks=16, vs=16, layout=f8, B=2):
+        return L.pkv_paged_attention_decode_cascade_dynamic(
+            16, 16, 16, 16, ks, vs, 16, 4, 16, None, 16, 16, 2, 8, 4, None, B, 4, 64,
+            ctypes.byref(layout), 0.1, 0, 256, 1 << 20, None)
+    assert dyn(ks=None) == pkv.PKV_ERR_INVALID_ARG
+    assert dyn(vs=None) == pkv.PKV_ERR_INVALID_ARG
+    assert dyn(layout=f16) == pkv.PKV_ERR_UNSUPPORTED
+    assert dyn(B=0) == pkv.PKV_OK

@@ -282,14 +282,19 @@ def test_cascade_rejects_bad_arguments():
         int(prefix.max()), None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
         prep.sm_scale, prep.k_scale, prep.v_scale, 64, ws.data_ptr(), ws.numel(), None)
     assert st == pkv.PKV_ERR_WORKSPACE
-    # more items plus sequences than one grid dimension holds
+    # more items plus sequences than one grid dimension holds (G = 4: one item
+    # per group of 4; 65535 items + the sequences > 65535), with a workspace
+    # large enough, so the count alone is rejected -- before any launch
+    big = torch.empty(pkv.pkv_decode_cascade_workspace_bytes(
+        wl.num_seqs, 8, 2, wl.max_context_len, int(prefix.max()), lay.dtype, 64),
+        dtype=torch.uint8, device="cuda")
     st = L.pkv_paged_attention_decode_cascade(
         out.data_ptr(), prep.q.data_ptr(), None, None, prep.k_pool.data_ptr(),
         prep.v_pool.data_ptr(), prep.tables.data_ptr(), prep.tables.shape[1],
-        prep.lens.data_ptr(), None, pre.data_ptr(), garr.data_ptr(), 40000, 4,
+        prep.lens.data_ptr(), None, pre.data_ptr(), garr.data_ptr(), 65535, 4,
         int(prefix.max()), None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
-        prep.sm_scale, prep.k_scale, prep.v_scale, 64, None, 0, None)
-    assert st in (pkv.PKV_ERR_INVALID_ARG, pkv.PKV_ERR_WORKSPACE)
+        prep.sm_scale, prep.k_scale, prep.v_scale, 64, big.data_ptr(), big.numel(), None)
+    assert st == pkv.PKV_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("ps", [0, 16, 512])

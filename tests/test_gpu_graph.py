@@ -53,3 +53,51 @@ def test_graph_replays_equal_the_eager_step(fp8, ps):
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.view(np.uint32)), r
         assert np.array_equal(prep.k_pool.cpu().numpy(), eager_k), r
+
+
+def test_graph_replays_equal_the_eager_cascade():
+    """The cascade step (newest tokens written, prefix items, tails in a given
+    order, merge) captured as one graph: every replay equals the eager call."""
+    from test_gpu_cascade import SOLO, SPEC, _group_array, _grouped
+
+    wl, groups, prefix = _grouped(SPEC, SOLO, 8, 2, True, seed=13)
+    prep = Prepared(wl)
+    B, Hkv, D = wl.num_seqs, wl.num_kv_heads, workloads.D
+    seqs = np.array([s for s, _ in wl.new_tokens], dtype=np.int64)
+    key = torch.zeros((B, Hkv, D), dtype=torch.float16, device="cuda")
+    val = torch.zeros_like(key)
+    key[torch.from_numpy(seqs).cuda()] = prep.new_k
+    val[torch.from_numpy(seqs).cuda()] = prep.new_v
+    garr = torch.from_numpy(_group_array(groups, 8)).cuda()
+    pre = torch.from_numpy(prefix).cuda()
+    tail = wl.context_lens.astype(np.int64) - 16 * prefix
+    order = torch.from_numpy(np.argsort(-tail, kind="stable").astype(np.int32)).cuda()
+    mp = int(prefix.max())
+    ws = torch.empty(pkv.pkv_decode_cascade_workspace_bytes(B, 8, Hkv, wl.max_context_len, mp,
+                                                            prep.layout.dtype, 64),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, 8, D), dtype=torch.float32, device="cuda")
+    k0, v0 = prep.k_pool.clone(), prep.v_pool.clone()
+
+    def step():
+        pkv.pkv_paged_attention_decode_cascade(
+            out, prep.q, key, val, prep.k_pool, prep.v_pool, prep.tables, prep.lens,
+            wl.max_context_len, prep.layout, prep.sm_scale, pre, garr, mp, prep.k_scale,
+            prep.v_scale, 64, ws, seq_order=order)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy().copy()
+    eager_k = prep.k_pool.cpu().numpy().copy()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(4):
+        out.fill_(float("nan"))                    # eager work between replays
+        prep.k_pool.copy_(k0)
+        prep.v_pool.copy_(v0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.view(np.uint32)), r
+        assert np.array_equal(prep.k_pool.cpu().numpy(), eager_k), r
