@@ -222,7 +222,7 @@ def run_prefill(args) -> int:
         # chunk over its prefix, on inputs the oracle writes itself
         import oracle
         rng = np.random.default_rng(406)
-        S = max(1, args.cpu_sample_seqs // 2)
+        S = max(1, args.cpu_sample_seqs // 4)
         b = B - 1
         L, n = int(wl.context_lens[b]), int(wl.chunk_lens[b])
         kh = np.zeros(pkv.pkv_pool_bytes(layout), dtype=np.uint8)
@@ -398,7 +398,7 @@ def main() -> int:
     ap.add_argument("--kv-scales", choices=("tensor", "block"), default="tensor",
                     help="FP8 scales: one per tensor (amax/448, default) or one per "
                          "(block, KV head) measured as the cache is written")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=8,
+    ap.add_argument("--cpu-sample-seqs", type=int, default=16,
                     help="sequences of the workload the CPU oracle baseline decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cascade", choices=("auto", "on", "off"), default="auto",
