@@ -119,16 +119,26 @@ __device__ __forceinline__ f16x8 v_operand(const TileRegs<kFP8>& ta, const TileR
 // hi + lo (two PV products, about 22 bits): dynamic scales are for values
 // with outliers, where one fp16 rounding of P is too coarse against the
 // absolute tolerance.  The normaliser sums the unscaled probabilities.
-template <bool kFP8, bool kDyn = false>
+// The pair's V tiles already loaded (the FP8 path).
+struct VLoaded {
+  static constexpr bool kLate = false;
+  template <class T>
+  __device__ void operator()(T&, T&) const {}
+};
+
+template <bool kFP8, bool kDyn = false, class LateV = VLoaded>
 __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb_,
                                              const f16x8 (&qop)[kHeadsPerWave][4],
                                              RowState (&st)[kHeadsPerWave], int tb, int qg,
                                              int pos_j, int L, bool masked, const float (&qk)[2],
-                                             const float (&vmul)[2]) {
-  if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
-    __asm__ volatile("" ::: "memory");  // keep this rare path a branch
-    mask_tail_values<kFP8>(ta, tb, qg, L);
-    mask_tail_values<kFP8>(tb_, tb + kBS, qg, L);
+                                             const float (&vmul)[2],
+                                             const LateV& late_v = LateV{}) {
+  if constexpr (!LateV::kLate) {
+    if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
+      __asm__ volatile("" ::: "memory");  // keep this rare path a branch
+      mask_tail_values<kFP8>(ta, tb, qg, L);
+      mask_tail_values<kFP8>(tb_, tb + kBS, qg, L);
+    }
   }
   f32x4 s[kHeadsPerWave][2];
   // matrix bursts run at raised priority, so the SIMD's other wave does its
@@ -147,6 +157,9 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
     }
   }
   __builtin_amdgcn_s_setprio(0);
+  // V loaded late: its loads overlap the softmax, into the K registers'
+  // place, which the products above no longer need
+  late_v(ta, tb_);
   if (masked) {  // wave-uniform; only the pairs that reach past the first position
     __asm__ volatile("" ::: "memory");
 #pragma unroll
@@ -202,6 +215,13 @@ __device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>&
       for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
     }
   }
+  if constexpr (LateV::kLate) {
+    if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
+      __asm__ volatile("" ::: "memory");
+      mask_tail_values<kFP8>(ta, tb, qg, L);
+      mask_tail_values<kFP8>(tb_, tb + kBS, qg, L);
+    }
+  }
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
@@ -253,6 +273,49 @@ __device__ __forceinline__ void load_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb
     if (!okb) zero_tile<kFP8>(tb);
   }
 }
+
+// One half (K or V) of both tiles of a pair, zeros for ids outside the pool
+// (and for tile b when `zero_b`: the pair reaches past the last tile).
+template <bool kFP8, bool kV>
+__device__ __forceinline__ void load_pair_half(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb,
+                                               const PrefillArgs& a, int pa, int pb, int kvh,
+                                               int lane, bool zero_b) {
+  constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
+  const bool oka = (unsigned)pa < (unsigned)a.num_blocks;
+  const bool okb = (unsigned)pb < (unsigned)a.num_blocks && !zero_b;
+  const uint8_t* pool = kV ? a.v_pool : a.k_pool;
+  const u32x4* xa = reinterpret_cast<const u32x4*>(
+                        pool + ((int64_t)(oka ? pa : 0) * a.hkv + kvh) * kTileBytes) + lane;
+  const u32x4* xb = reinterpret_cast<const u32x4*>(
+                        pool + ((int64_t)(okb ? pb : 0) * a.hkv + kvh) * kTileBytes) + lane;
+  u32x4* da = kV ? ta.v : ta.k;
+  u32x4* db = kV ? tb.v : tb.k;
+#pragma unroll
+  for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+    da[i] = xa[i * kWave];
+    db[i] = xb[i * kWave];
+  }
+  if (!oka || !okb) {
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+      if (!oka) da[i] = u32x4{0, 0, 0, 0};
+      if (!okb) db[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// fp16 tiles are twice the registers of FP8 ones: the V halves of a pair
+// are loaded after its QK^T products (process_pair calls this there).
+struct VLate {
+  static constexpr bool kLate = true;
+  const PrefillArgs* a;
+  int pa, pb, kvh, lane;
+  bool zero_b;
+  __device__ void operator()(TileRegs<false>& ta, TileRegs<false>& tb) const {
+    load_pair_half<false, true>(ta, tb, *a, pa, pb, kvh, lane, zero_b);
+  }
+};
 
 // The K and V scales of a pair's two (block, head) tiles; ids outside the
 // pool read as 0 (their tiles are zeros).
@@ -322,19 +385,17 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
   for (int c0 = 0; c0 < ntiles; c0 += kWave) {
     const int cnt = min(kWave, ntiles - c0);
     const int tbl = lane < cnt ? trow[c0 + lane] : -1;  // lane i: tile c0 + i
-    if constexpr (!kFP8) {  // fp16 tiles are twice the registers: one pair at a time
+    if constexpr (!kFP8) {  // fp16 tiles are twice the registers: one pair at a time,
+                            // its V halves loaded after its QK^T products
       for (int t = 0; t < cnt; t += 2) {
         TileRegs<kFP8> ta, tb;
         const int pa = __builtin_amdgcn_readlane(tbl, t);
         const int pb = t + 1 < cnt ? __builtin_amdgcn_readlane(tbl, t + 1) : pa;
-        load_pair<kFP8>(ta, tb, a, pa, pb, kvh, lane);
-        if (t + 1 >= cnt) {                 // past the last tile: all masked below
-          __asm__ volatile("" ::: "memory");
-          zero_tile<kFP8>(tb);
-        }
+        const bool past = t + 1 >= cnt;     // past the last tile: all masked below
+        load_pair_half<kFP8, false>(ta, tb, a, pa, pb, kvh, lane, past);
         const int tok0 = (c0 + t) * kBS;
         process_pair<kFP8>(ta, tb, qop, st, tok0, qg, pos_c, L, tok0 + 2 * kBS - 1 > first,
-                           qk_one, v_one);
+                           qk_one, v_one, VLate{&a, pa, pb, kvh, lane, past});
       }
       continue;
     }
