@@ -482,6 +482,19 @@ pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* child_out);
  * All or nothing: PKV_ERR_NO_FREE_BLOCKS leaves every state unchanged. */
 pkv_status pkv_seq_append(pkv_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_out,
                           int32_t* cow_pairs_out, int32_t* n_cow_out);
+/* One token for each of seqs[0..n), in that order: a decode step's slot
+ * assignment in one call ([PRIMER-8] §8.1, blocks allocated on demand).
+ * Each sequence is appended as by pkv_seq_append with one token.
+ *   slots_out      host int64 [n]: the new token's slot of each sequence
+ *   cow_pairs_out  host int32 [n][2]: the copy-on-write pairs, packed; their
+ *                  count in *n_cow_out (copy them before writing the tokens)
+ *   *n_done_out    sequences appended.  On an error (the first failing
+ *                  sequence's status, e.g. NO_FREE_BLOCKS) the sequences
+ *                  before it are appended and it and those after it are
+ *                  unchanged. */
+pkv_status pkv_seq_append_each(pkv_pool* pool, const int32_t* seqs, int32_t n,
+                               int64_t* slots_out, int32_t* cow_pairs_out, int32_t* n_cow_out,
+                               int32_t* n_done_out);
 /* Release a sequence: each of its blocks loses one reference; at zero it
  * returns to the free list, or becomes evictable if the prefix cache holds it
  * ([GLOSSARY] §4.02: pages of a cancelled request go back to the pool at once,

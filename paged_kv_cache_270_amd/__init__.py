@@ -127,6 +127,8 @@ def load_library():
         "pkv_seq_fork": ([P, i32, ctypes.POINTER(i32)], i32),
         "pkv_seq_append": ([P, i32, i32, P, P, ctypes.POINTER(i32)], i32),
         "pkv_seq_free": ([P, i32], i32),
+        "pkv_seq_append_each": ([P, P, i32, P, P, ctypes.POINTER(i32), ctypes.POINTER(i32)],
+                                i32),
         "pkv_seq_block_table": ([P, i32, P, i32, ctypes.POINTER(i32)], i32),
         "pkv_seq_len": ([P, i32], i64),
         "pkv_seq_shared_prefix_blocks": ([P, i32], i32),
@@ -623,6 +625,21 @@ class BlockPool:
                "pkv_seq_append")
         cow = [(pairs[0], pairs[1])] if n_cow.value else []
         return list(slots[:n_tokens]), cow
+
+    def append_each(self, seqs):
+        """One token for each sequence of `seqs`, in order.  Returns (slots
+        int64 [n], cow_pairs list of (old, new)); raises on the first failing
+        sequence (those before it are appended)."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = seqs.size
+        slots = np.zeros(max(1, n), dtype=np.int64)
+        pairs = np.zeros((max(1, n), 2), dtype=np.int32)
+        n_cow, n_done = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._L.pkv_seq_append_each(self._h, seqs.ctypes.data, n, slots.ctypes.data,
+                                           pairs.ctypes.data, ctypes.byref(n_cow),
+                                           ctypes.byref(n_done)), "pkv_seq_append_each")
+        return slots[:n].copy(), [tuple(int(x) for x in r) for r in pairs[:n_cow.value]]
 
     def free(self, seq: int) -> None:
         _check(self._L.pkv_seq_free(self._h, seq), "pkv_seq_free")

@@ -268,6 +268,26 @@ extern "C" pkv_status pkv_seq_append(pkv_pool* p, int32_t seq, int32_t n_tokens,
   return PKV_OK;
 }
 
+// One token for each listed sequence (a decode step's slots), in order.
+extern "C" pkv_status pkv_seq_append_each(pkv_pool* p, const int32_t* seqs, int32_t n,
+                                          int64_t* slots_out, int32_t* cow_pairs_out,
+                                          int32_t* n_cow_out, int32_t* n_done_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (n < 0 || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !n_cow_out || !n_done_out)
+    return PKV_ERR_INVALID_ARG;
+  *n_cow_out = 0;
+  *n_done_out = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t nc = 0;
+    const pkv_status st = pkv_seq_append(p, seqs[i], 1, slots_out + i,
+                                         cow_pairs_out + 2 * (size_t)*n_cow_out, &nc);
+    if (st != PKV_OK) return st;  // sequences before i are appended, i is unchanged
+    *n_cow_out += nc;
+    *n_done_out = i + 1;
+  }
+  return PKV_OK;
+}
+
 extern "C" pkv_status pkv_seq_free(pkv_pool* p, int32_t seq) {
   if (!p) return PKV_ERR_BAD_HANDLE;
   auto it = p->seqs.find(seq);

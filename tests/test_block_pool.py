@@ -254,3 +254,52 @@ def test_prefix_groups_order_longest_tail_first():
                                                    with_order=True)
     assert list(prefix) == [3, 0, 3, 0] and mx == 3
     assert list(order) == [2, 1, 0, 3]
+
+
+def test_append_each_equals_appends_one_by_one():
+    """A decode step's slots in one call: the same slots, copy-on-write pairs
+    and pool state as one append per sequence, forks with shared partial
+    tails included."""
+    import numpy as np
+    pools = [pkv.BlockPool(64, shuffle_seed=9), pkv.BlockPool(64, shuffle_seed=9)]
+    fam = []
+    for pool in pools:
+        a = pool.create()
+        pool.append(a, 40)              # a partial last block, shared by the forks
+        ids = [a, pool.fork(a), pool.fork(a), pool.create()]
+        pool.append(ids[3], 16)         # a full last block: the next token opens one
+        fam.append(ids)
+    slots, cow = pools[0].append_each(fam[0] * 2)
+    want_slots, want_cow = [], []
+    for s in fam[1] * 2:
+        sl, c = pools[1].append(s, 1)
+        want_slots += sl
+        want_cow += c
+    assert list(slots) == want_slots and cow == want_cow and len(cow) == 2
+    for s0, s1 in zip(fam[0], fam[1]):
+        assert pools[0].block_table(s0) == pools[1].block_table(s1)
+    assert pools[0].num_free() == pools[1].num_free()
+
+
+def test_append_each_stops_at_the_first_failure():
+    pool = pkv.BlockPool(3)
+    a, b, c = pool.create(), pool.create(), pool.create()
+    pool.append(a, 16)
+    pool.append(b, 16)
+    pool.append(c, 16)                  # every block taken, every last block full
+    with pytest.raises(pkv.PkvError) as e:
+        pool.append_each([a])
+    assert e.value.status == pkv.PKV_ERR_NO_FREE_BLOCKS
+    assert pool.seq_len(a) == 16        # unchanged
+    pool.free(c)                        # one block back: a gets it, b then fails
+    import ctypes
+    import numpy as np
+    L = pkv.load_library()
+    seqs = np.array([a, b], dtype=np.int32)
+    slots = np.zeros(2, dtype=np.int64)
+    pairs = np.zeros((2, 2), dtype=np.int32)
+    nc, nd = ctypes.c_int32(), ctypes.c_int32()
+    st = L.pkv_seq_append_each(pool._h, seqs.ctypes.data, 2, slots.ctypes.data,
+                               pairs.ctypes.data, ctypes.byref(nc), ctypes.byref(nd))
+    assert st == pkv.PKV_ERR_NO_FREE_BLOCKS and nd.value == 1 and nc.value == 0
+    assert pool.seq_len(a) == 17 and pool.seq_len(b) == 16
