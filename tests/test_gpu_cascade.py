@@ -336,3 +336,41 @@ def test_cascade_block_scales_matches_oracle(ps):
     print(f"[parity] cascade block scales P={ps}: max abs err {err:.3e}", flush=True)
     assert np.isfinite(got).all()
     assert err <= TOL[True]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cascade_random_groups(seed):
+    """Random batches: 1 to 6 groups of 1 to 10 members with prefixes of 1 to
+    40 blocks and tails of 1 to 600 tokens, sequences in no group, random
+    head groupings, fp16 or FP8, random split sizes, groups in random slots
+    of a padded group table, tails in a random order; against the oracle."""
+    rng = np.random.default_rng(900 + seed)
+    spec = [(16 * int(rng.integers(1, 41)), [int(t) for t in rng.integers(1, 601,
+                                                                          rng.integers(1, 11))])
+            for _ in range(int(rng.integers(1, 7)))]
+    solo = [int(x) for x in rng.integers(0, 900, int(rng.integers(0, 6)))]
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    fp8 = bool(seed % 2)
+    wl, groups, prefix = _grouped(spec, solo, g * hkv, hkv, fp8, seed=910 + seed)
+    cap = int(rng.integers(max(len(m) for m in groups), 13))
+    garr = _group_array(groups, cap)
+    # groups in random rows, among rows of empty slots (skipped items)
+    rows = np.full((garr.shape[0] + 2, cap), -1, dtype=np.int32)
+    rows[rng.permutation(rows.shape[0])[:garr.shape[0]]] = garr
+    prep = Prepared(wl)
+    order = rng.permutation(wl.num_seqs).astype(np.int32)
+    ps = int(rng.choice([0, 16, 48, 256]))
+    out = torch.full(prep.q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    pkv.pkv_paged_attention_decode_cascade(
+        out, prep.q, None, None, prep.k_pool, prep.v_pool, prep.tables, prep.lens,
+        wl.max_context_len, prep.layout, prep.sm_scale, torch.from_numpy(prefix).cuda(),
+        torch.from_numpy(rows).cuda(), int(prefix.max()), prep.k_scale, prep.v_scale, ps,
+        seq_order=torch.from_numpy(order).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = max_err(got, prep.oracle_decode())
+    print(f"[parity] cascade random seed={seed} G={g} Hkv={hkv} fp8={fp8} P={ps}: "
+          f"max abs err {err:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL[fp8]
