@@ -267,7 +267,9 @@ pkv_status pkv_decode_partitions_append(
  *                  decoded on its own, and groups must leave it out.
  *   prefix_groups  device int32 [num_groups][group_cap]: the batch indices
  *                  of each group's members, -1 for an empty slot.  The first
- *                  slot of a group holds a member; all members of a group
+ *                  slot of a group holds a member (a row starting with -1,
+ *                  or with a sequence that has no prefix, is skipped whole);
+ *                  all members of a group
  *                  have the same S_b and the same first S_b table entries;
  *                  every sequence with a used S_b > 0 is in exactly one
  *                  group.  (pkv_pool_prefix_groups builds these.)  Results
@@ -290,7 +292,7 @@ pkv_status pkv_decode_partitions_append(
  * variant is the default family whatever PKV_* variant switches say.
  * Errors: INVALID_ARG for one of key/value null, negative counts, groups
  * without arrays, or more than 65535 items plus sequences
- * (num_groups * ceil(group_cap / (16 / G)) + num_seqs); WORKSPACE if the
+ * (num_groups * ceil(group_cap / floor(16 / G)) + num_seqs); WORKSPACE if the
  * workspace is smaller than pkv_decode_cascade_workspace_bytes. */
 pkv_status pkv_paged_attention_decode_cascade(
     float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
