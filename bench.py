@@ -79,6 +79,61 @@ def copy_probe(mib: int) -> int:
     return 0
 
 
+def read_probe(mib: int) -> int:
+    """Only the streaming-read ceiling: mib MiB read 20 times after 3 warm-up
+    reads, one JSON line with the rate."""
+    import torch
+    import paged_kv_cache_270_amd as pkv
+    torch.cuda.set_device(0)
+    gbs = stream_read_gbs(pkv, mib << 20)
+    print(json.dumps({"stream_read_bytes_per_launch": mib << 20, "stream_read_gbs": gbs}),
+          flush=True)
+    return 0
+
+
+def timed_launches(fn, reps: int, warmup: int = 3) -> float:
+    """Milliseconds per call of `fn` over `reps` back-to-back calls between two
+    events on the current stream (nothing else in between)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def stream_read_gbs(pkv, nbytes: int = 2 << 30) -> float:
+    """Streaming-read ceiling: a contiguous buffer (far larger than the 256 MB
+    last-level cache) read once per launch with 16-byte non-temporal loads."""
+    import torch
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ms = timed_launches(lambda: pkv.pkv_hbm_read_probe(buf, sink), 20)
+    del buf
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sha256_of(a) -> str:
+    import numpy as np
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
 def build_sequences(pkv, wl):
     """Grow the workload's sequences in the library's block pool.
 
@@ -184,18 +239,17 @@ def run_prefill(args) -> int:
     sm = float(np.float32(1 / np.sqrt(D)))
     maxq, maxl = int(wl.chunk_lens.max()), int(wl.context_lens.max())
 
-    def step(ev=None):
-        write(new_k, new_v, d_chunk)
-        if ev is not None:
-            ev[0].record()
+    def attention():
         if dyn:
             pkv.pkv_paged_prefill_attention_dynamic(out, q, k_pool, v_pool, k_bs, v_bs, d_tables,
                                                     d_lens, d_qs, maxq, maxl, layout, sm)
         else:
             pkv.pkv_paged_prefill_attention(out, q, k_pool, v_pool, d_tables, d_lens, d_qs, maxq,
                                             maxl, layout, sm, ks, vs)
-        if ev is not None:
-            ev[1].record()
+
+    def step():
+        write(new_k, new_v, d_chunk)
+        attention()
 
     for _ in range(args.warmup):
         step()
@@ -207,12 +261,8 @@ def run_prefill(args) -> int:
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / args.steps
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(kev[i])
-    torch.cuda.synchronize()
-    attn_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+    # the attention kernel alone: K back-to-back launches, no event between
+    attn_ms = min(timed_launches(attention, args.steps, warmup=1), step_ms)
     flops = wl.flops()
     value = flops / (step_ms * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
@@ -412,9 +462,14 @@ def main() -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, 5 times (the "
                          "reference kernel for scaling HBM byte counters), then exit")
+    ap.add_argument("--read-probe-mib", type=int, default=0,
+                    help="only measure the streaming-read ceiling over this many MiB, "
+                         "then exit")
     args = ap.parse_args()
     if args.copy_probe_mib:
         return copy_probe(args.copy_probe_mib)
+    if args.read_probe_mib:
+        return read_probe(args.read_probe_mib)
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence or KV head with no exchange; see DESIGN.md)",
@@ -520,51 +575,35 @@ def main() -> int:
     bulk_bytes = T * Hkv * D * 2 * (2 + e) + T * 8   # fp16 rows in, cache rows out, slots
     del key_src, val_src
 
-    def step(ev=None):
-        if dyn and cascade:
-            write(new_k, new_v, d_step_slots)
-            if ev is not None:
-                ev[0].record()
-            pkv.pkv_paged_attention_decode_cascade_dynamic(
-                out, q, k_pool, v_pool, k_bs, v_bs, d_tables, d_lens, Lmax, layout, sm_scale,
-                d_prefix, d_groups, max_pre, P, ws, shared_prefix_blocks=d_shared,
-                seq_order=d_order)
-            if ev is not None:
-                ev[1].record()
-            return
+    def step():
         if dyn:
+            # the newest rows first (the dynamic write's own launch), then
+            # one decode call: the partition kernel, and the merge when a
+            # sequence spans several partitions (none at the default workload)
             write(new_k, new_v, d_step_slots)
-            if ev is not None:
-                ev[0].record()
-            # one call: the partition kernel, then the merge when a sequence
-            # spans several partitions (none at the default workload)
-            pkv.pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_bs, v_bs, d_tables,
-                                                   d_lens, Lmax, layout, sm_scale, P, ws,
-                                                   shared_prefix_blocks=d_shared)
-            if ev is not None:
-                ev[1].record()
+            if cascade:
+                pkv.pkv_paged_attention_decode_cascade_dynamic(
+                    out, q, k_pool, v_pool, k_bs, v_bs, d_tables, d_lens, Lmax, layout, sm_scale,
+                    d_prefix, d_groups, max_pre, P, ws, shared_prefix_blocks=d_shared,
+                    seq_order=d_order)
+            else:
+                pkv.pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_bs, v_bs,
+                                                       d_tables, d_lens, Lmax, layout, sm_scale,
+                                                       P, ws, shared_prefix_blocks=d_shared)
             return
         if cascade:
             # one call: the partition kernel (prefix items and tails, writing
-            # the newest tokens), then the merge; events span both
-            if ev is not None:
-                ev[0].record()
+            # the newest tokens), then the merge
             pkv.pkv_paged_attention_decode_cascade(
                 out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens, Lmax, layout, sm_scale,
                 d_prefix, d_groups, max_pre, k_scale, v_scale, P, ws,
                 shared_prefix_blocks=d_shared, seq_order=d_order)
-            if ev is not None:
-                ev[1].record()
             return
         # the newest token of each sequence (position L - 1, the slot
         # pool.append gave it) is written by the partition kernel itself
-        if ev is not None:
-            ev[0].record()
         pkv.pkv_decode_partitions_append(out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens,
                                          Lmax, layout, sm_scale, k_scale, v_scale, P, ws,
                                          shared_prefix_blocks=d_shared)
-        if ev is not None:
-            ev[1].record()
         pkv.pkv_decode_reduce(out, d_lens, Lmax, tables.shape[1], layout, v_scale, P, ws)
 
     def timed(fn):
@@ -590,20 +629,78 @@ def main() -> int:
         run = graph.replay
     # the timed region: K whole steps back to back, nothing else on the stream
     step_ms = timed(run)
-    # a second timed region of K steps with events around the partition kernel
-    # (same stream) for its own duration; events add a few microseconds per
-    # step, so the step time above is taken without them
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(kev[i])
-    torch.cuda.synchronize()
-    part_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+    # the dominant kernel's own time, with no event between its launches:
+    # where the step is one launch of the partition kernel, the step's timed
+    # region is exactly that kernel's; otherwise K back-to-back launches of
+    # the partition kernel alone (the per-block-scale decode and the cascade
+    # have no entry point for their partition kernel alone: there the decode
+    # call -- partitions, and the merge when one is needed -- is timed)
+    need_merge = ws_bytes > 0
+    if not dyn and not cascade and not need_merge:
+        part_ms = step_ms
+        part_covers = "partition kernel (the step is one launch of it: the step's timed region)"
+    else:
+        if dyn and cascade:
+            def kernel_only():
+                pkv.pkv_paged_attention_decode_cascade_dynamic(
+                    out, q, k_pool, v_pool, k_bs, v_bs, d_tables, d_lens, Lmax, layout,
+                    sm_scale, d_prefix, d_groups, max_pre, P, ws, shared_prefix_blocks=d_shared,
+                    seq_order=d_order)
+            part_covers = "partition + merge kernels (the cascade decode call)"
+        elif dyn:
+            def kernel_only():
+                pkv.pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_bs, v_bs,
+                                                       d_tables, d_lens, Lmax, layout, sm_scale,
+                                                       P, ws, shared_prefix_blocks=d_shared)
+            part_covers = "partition kernel" + (" + merge" if need_merge else "") + \
+                " (the decode call, without the separate write launch)"
+        elif cascade:
+            def kernel_only():
+                pkv.pkv_paged_attention_decode_cascade(
+                    out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens, Lmax, layout,
+                    sm_scale, d_prefix, d_groups, max_pre, k_scale, v_scale, P, ws,
+                    shared_prefix_blocks=d_shared, seq_order=d_order)
+            part_covers = "partition + merge kernels (the cascade call)"
+        else:
+            def kernel_only():
+                pkv.pkv_decode_partitions_append(out, q, new_k, new_v, k_pool, v_pool, d_tables,
+                                                 d_lens, Lmax, layout, sm_scale, k_scale,
+                                                 v_scale, P, ws, shared_prefix_blocks=d_shared)
+            part_covers = "partition kernel (K back-to-back launches of it alone)"
+        part_ms = timed_launches(kernel_only, args.steps, warmup=2)
+        if part_ms > step_ms:   # timing noise: never report the kernel faster than measured
+            print(f"bench.py: kernel-only region {part_ms * 1e3:.2f} us > step "
+                  f"{step_ms * 1e3:.2f} us; the step time is used for the roofline",
+                  file=sys.stderr)
+            part_ms = step_ms
+            part_covers += "; bounded by the step time"
 
     tokens = int(lens.astype(np.int64).sum())
     logical = tokens * Hkv * D * 2 * e                  # every token of every sequence
     unique = (T + B) * Hkv * D * 2 * e                  # each stored token once
+    # ---- memory ceilings on the same part: a contiguous streaming read, and
+    # the decode's own table-driven tile reads without arithmetic
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    gather_ms = timed_launches(lambda: pkv.pkv_tile_gather_probe(k_pool, v_pool, d_tables, d_lens,
+                                                                 Lmax, layout, sink), args.steps)
+    gather_gbs = logical / (gather_ms * 1e-3) / 1e9
+    stream_gbs = stream_read_gbs(pkv)
+    # ---- bytes besides the KV tiles: queries, outputs, table entries and
+    # lengths read, the newest rows in and out, split-KV partials written and
+    # read back by the merge (max and sum, 128 floats)
+    pb = P // 16
+    nblk_b = -(-lens.astype(np.int64) // 16)
+    if cascade:
+        S = np.where((prefix > 0) & (prefix <= max_pre) & (16 * prefix.astype(np.int64) < lens),
+                     prefix, 0).astype(np.int64)
+        parts = -(-S // pb) + -(-(nblk_b - S) // pb)
+    else:
+        parts = -(-nblk_b // pb)
+    partial_rows = int(np.where(parts > 1, parts, 0).sum()) * Hq
+    other = {"q": B * Hq * D * 2, "out": B * Hq * D * 4, "table_entries": int(nblk_b.sum()) * 4,
+             "context_lens": B * 4, "new_rows_in": B * Hkv * D * 2 * 2,
+             "new_rows_out": B * Hkv * D * e * 2,
+             "partials_written_and_read": 2 * partial_rows * (2 + D) * 4}
     if dyn:  # plus one K and one V fp32 scale per (block, KV head) tile read
         nblk = -(-lens.astype(np.int64) // 16)
         used = np.unique(np.concatenate([tables[i, :nblk[i]] for i in range(B)]))
@@ -645,7 +742,7 @@ def main() -> int:
         cpu_s = time.perf_counter() - t0
         sample_bytes = int(lens[:S].astype(np.int64).sum()) * Hkv * D * 2 * e
         cpu = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
-               "cores": threads, "kind": "oracle",
+               "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"{S} of {B} sequences (all {Hq} query heads, "
                          f"{int(lens[:S].sum())} tokens): {cpu_s:.2f} s fp64 decode on the host"}
 
@@ -681,8 +778,17 @@ def main() -> int:
         "kv_bytes_per_step_logical": logical,
         "kv_gbs_logical": round(logical / (step_ms * 1e-3) / 1e9, 2),
         "decode_partition_us": round(part_ms * 1e3, 2),
-        "decode_partition_us_covers": "partition + merge kernels" if cascade
-        else "partition kernel",
+        "decode_partition_us_covers": part_covers,
+        "hbm_ceilings": {"stream_read_gbs": stream_gbs,
+                         "tile_gather_gbs": round(gather_gbs, 1),
+                         "tile_gather_bytes": logical - (0 if not dyn else
+                                                         int(nblk_b.sum()) * Hkv * 8),
+                         "value_frac_of_stream_read": round(value / stream_gbs, 4),
+                         "kernel_frac_of_stream_read": round(achieved / stream_gbs, 4)},
+        "other_bytes_per_step": other,
+        "inputs": {"structure_seed": wl.seed, "value_seeds": [301, 302, 303, 304, 305],
+                   "context_lens_sha256": sha256_of(lens),
+                   "block_tables_sha256": sha256_of(tables)},
         "shared_prefix_blocks_hint": int(shared.max()) if B else 0,
         "host_slot_assignment_us": round(host_slot_us, 1),
         "bulk_fill_gbs": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),

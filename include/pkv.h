@@ -19,7 +19,8 @@
  *   The decode kernel takes that table as an extra input and gathers keys and
  *   values through it instead of slicing a contiguous slab ([PRIMER-8] §8.1).
  *   New K/V rows can be stored as fp16 or converted on the fly to 8-bit
- *   floating point E4M3, halving the cache ([FP8-128K] §4, §6.2, §8).
+ *   floating point E4M3, halving the cache ([FP8-128K] §4; the E4M3 format
+ *   is named in §6.2 and §8).
  *   One query token per sequence is decoded per call ([PRIMER-8], closing
  *   section on Chapter 9; [KV-SLOW] "¿Qué es el KV cache?").
  *
@@ -126,6 +127,33 @@ uint64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t max_context_len,
                                     int32_t dtype, int32_t partition_size);
 
+/* ------------------------------------------------------------ table checks */
+
+/* Check block tables and lengths held in HOST memory: for every sequence b,
+ * 0 <= context_lens[b] <= min(max_context_len, 16 * max_blocks_per_seq) and
+ * each of its first ceil(L_b / 16) entries names a block of the pool,
+ * 0 <= id < num_blocks (the decode kernel reads the table as an extra input
+ * to find each token's physical block: [PRIMER-8] §8.1).  Returns
+ * INVALID_ARG at the first sequence that breaks this (its index in
+ * *bad_seq_out, else -1 there; bad_seq_out may be NULL) or for bad sizes
+ * (num_seqs < 0, max_blocks_per_seq <= 0, num_blocks <= 0, null arrays with
+ * num_seqs > 0).  Pure host function. */
+pkv_status pkv_validate_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_context_len, int32_t num_blocks,
+                               int32_t* bad_seq_out);
+
+/* Debug checks of device tables.  While on, every decode and prefill call
+ * first copies its block table and lengths to the host (synchronising its
+ * stream) and returns INVALID_ARG, launching nothing, if pkv_validate_tables
+ * rejects them; without it the kernels clamp lengths and skip ids outside
+ * the pool.  Off by default; the environment variable PKV_DEBUG_CHECKS set to
+ * anything but "" or "0" turns it on at load.  A debug call cannot be
+ * captured into a HIP graph (it copies to the host).  pkv_set_debug_checks
+ * returns the previous setting; process-wide. */
+int32_t pkv_set_debug_checks(int32_t on);
+int32_t pkv_get_debug_checks(void);
+
 /* ------------------------------------------------------------ device calls */
 
 /* Store new K/V rows into their cache slots ([FP8-128K] §4: the new rows are
@@ -214,7 +242,8 @@ pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens, int32_t nu
 
 /* A decode step in one call: write each sequence's newest token into the
  * cache, then attend over its whole context, that token included -- the
- * cache write of [FP8-128K] §6.2 followed by the decode attention above.
+ * cache write of [FP8-128K] §4 (new rows converted to 8 bits as they are
+ * stored) followed by the decode attention above.
  * Sequence b's newest token is at position L_b - 1 (L_b = context_lens[b]
  * after the clamp described above); its slot is
  *   block_tables[b][(L_b - 1) / 16] * 16 + (L_b - 1) % 16,
@@ -632,6 +661,27 @@ pkv_status pkv_swap_blocks(void* k_pool, void* v_pool, void* host_k, void* host_
                            int32_t num_host_blocks, const pkv_cache_layout* layout,
                            const int32_t* pairs, int32_t num_pairs, int32_t to_host,
                            void* stream);
+
+/* ------------------------------------------------------ memory ceilings */
+
+/* Reads that bound the decode from above, for measurement.  [PRIMER-8] §8.1
+ * compares a paged kernel with one reading a contiguous slab; these two give
+ * both sides of that comparison without attention arithmetic.
+ * pkv_hbm_read_probe streams `bytes` (a multiple of 16) of device memory at
+ * `buf` (16-byte aligned) once with 16-byte non-temporal lane loads.
+ * pkv_tile_gather_probe reads every K and V tile of every sequence through
+ * its block table, as the decode kernel does (same loads, same cache policy;
+ * arguments as in pkv_paged_attention_decode; ids outside the pool read
+ * nothing).  Both fold what they read into one word per lane and store it to
+ * sink[0] (device uint32) only if it equals `key`, so nothing measurable is
+ * written.  Asynchronous on `stream`. */
+pkv_status pkv_hbm_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, uint32_t key,
+                              void* stream);
+pkv_status pkv_tile_gather_probe(const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t max_context_len, const pkv_cache_layout* layout,
+                                 uint32_t* sink, uint32_t key, void* stream);
 
 #ifdef __cplusplus
 }

@@ -75,6 +75,20 @@ double oracle_e4m3_decode(uint8_t c) {
   return s ? -v : v;
 }
 
+/* The values of the 127 finite non-negative codes and of all 65536 fp16 bit
+ * patterns, filled once when the library is loaded, from the two definitions
+ * above: a lookup gives exactly what calling them gives, without repeating
+ * the exponent arithmetic for every element of a large pool. */
+static double orc_code_value[0x7F];
+static double orc_f16_value[65536];
+static void orc_fill_tables(void) __attribute__((constructor));
+static void orc_fill_tables(void) {
+  for (int c = 0; c <= 0x7E; ++c)
+    orc_code_value[c] = oracle_e4m3_decode((uint8_t)c);
+  for (int h = 0; h < 65536; ++h)
+    orc_f16_value[h] = oracle_f16_to_double((uint16_t)h);
+}
+
 /* Nearest E4M3FN code to the fp32 value u, found by trying every finite
  * non-negative code (the definition of round-to-nearest written out).  On an
  * exact tie the code with mantissa LSB 0 (the even code) wins.  Values whose
@@ -90,7 +104,7 @@ uint8_t oracle_e4m3_encode(float u) {
   int best = 0;
   double best_d = INFINITY;
   for (int c = 0; c <= 0x7E; ++c) {
-    double d = fabs(oracle_e4m3_decode((uint8_t)c) - a);
+    double d = fabs(orc_code_value[c] - a);
     if (d < best_d || (d == best_d && (c & 1) == 0)) {
       best_d = d;
       best = c;
@@ -425,7 +439,7 @@ void oracle_paged_prefill_attention_dynamic(double* out, const uint16_t* q,
  * Slots must be distinct within a call; negative or out-of-pool slots are
  * skipped. */
 static double orc_abs_finite(uint16_t bits) {
-  double x = oracle_f16_to_double(bits);
+  double x = orc_f16_value[bits];
   return isfinite(x) ? fabs(x) : 0.0;
 }
 
@@ -437,24 +451,30 @@ void oracle_reshape_and_cache_dynamic(const uint16_t* key, const uint16_t* value
   uint32_t* written = (uint32_t*)calloc((size_t)num_blocks, sizeof(uint32_t));
   double* amax = (double*)calloc((size_t)num_blocks * Hkv * 2, sizeof(double));
   float* s_new = (float*)calloc((size_t)num_blocks * Hkv * 2, sizeof(float));
-  /* 1. offsets written and MaxAbs of the new rows, per (block, head, K/V) */
+  /* 1. offsets written, then MaxAbs of the new rows per (block, head, K/V)
+   *    (each head's maxima are its own: heads run in parallel) */
   for (int i = 0; i < T; ++i) {
     int64_t sl = slots[i];
-    if (sl < 0 || sl >= (int64_t)num_blocks * ORC_BS)
-      continue;
-    int64_t b = sl / ORC_BS;
-    written[b] |= 1u << (sl % ORC_BS);
-    for (int h = 0; h < Hkv; ++h)
+    if (sl >= 0 && sl < (int64_t)num_blocks * ORC_BS)
+      written[sl / ORC_BS] |= 1u << (sl % ORC_BS);
+  }
+#pragma omp parallel for schedule(static)
+  for (int h = 0; h < Hkv; ++h)
+    for (int i = 0; i < T; ++i) {
+      int64_t sl = slots[i];
+      if (sl < 0 || sl >= (int64_t)num_blocks * ORC_BS)
+        continue;
+      int64_t b = sl / ORC_BS;
+      double* ak = &amax[(b * Hkv + h) * 2];
       for (int d = 0; d < D; ++d) {
         int64_t src = ((int64_t)i * Hkv + h) * D + d;
-        double* ak = &amax[(b * Hkv + h) * 2];
         double xk = orc_abs_finite(key[src]), xv = orc_abs_finite(value[src]);
         if (xk > ak[0])
           ak[0] = xk;
         if (xv > ak[1])
           ak[1] = xv;
       }
-  }
+    }
   /* 2-4. new scales, and old slots re-encoded where a scale grew */
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t b = 0; b < num_blocks; ++b) {
@@ -501,9 +521,9 @@ void oracle_reshape_and_cache_dynamic(const uint16_t* key, const uint16_t* value
         int64_t src = ((int64_t)i * Hkv + h) * D + d;
         float sk = s_new[(b * Hkv + h) * 2], sv = s_new[(b * Hkv + h) * 2 + 1];
         k_pool[orc_addr(0, b, h, t, d, Hkv, D, 1)] =
-            oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double(key[src]), sk));
+            oracle_e4m3_encode(oracle_quotient(orc_f16_value[key[src]], sk));
         v_pool[orc_addr(1, b, h, t, d, Hkv, D, 1)] =
-            oracle_e4m3_encode(oracle_quotient(oracle_f16_to_double(value[src]), sv));
+            oracle_e4m3_encode(oracle_quotient(orc_f16_value[value[src]], sv));
       }
   }
   free(written);

@@ -20,7 +20,9 @@ __all__ = [
     "pkv_paged_attention_decode_append", "pkv_decode_partitions_append",
     "pkv_copy_blocks", "pkv_reshape_dynamic_workspace_bytes", "pkv_reshape_and_cache_dynamic",
     "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic", "pkv_paged_prefill_attention",
-    "pkv_paged_prefill_attention_dynamic", "pkv_swap_blocks",
+    "pkv_paged_prefill_attention_dynamic", "pkv_swap_blocks", "pkv_validate_tables",
+    "pkv_set_debug_checks", "pkv_get_debug_checks", "pkv_hbm_read_probe",
+    "pkv_tile_gather_probe",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +83,11 @@ def load_library():
         "pkv_pool_bytes": ([LP], u64),
         "pkv_decode_partition_size": ([i32, i32, i32, i32, i32], i32),
         "pkv_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], u64),
+        "pkv_validate_tables": ([P, i32, P, i32, i32, i32, ctypes.POINTER(i32)], i32),
+        "pkv_set_debug_checks": ([i32], i32),
+        "pkv_hbm_read_probe": ([P, u64, P, ctypes.c_uint32, P], i32),
+        "pkv_tile_gather_probe": ([P, P, P, i32, P, i32, i32, LP, P, ctypes.c_uint32, P], i32),
+        "pkv_get_debug_checks": ([], i32),
         "pkv_reshape_and_cache": ([P, P, P, P, P, i32, LP, f32, f32, P], i32),
         "pkv_paged_attention_decode": ([P, P, P, P, P, i32, P, P, i32, i32, i32, LP, f32, f32,
                                         f32, i32, P, u64, P], i32),
@@ -205,6 +212,55 @@ def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_context_
 
 
 # --------------------------------------------------------- device calls
+
+def pkv_validate_tables(block_tables, context_lens, max_context_len: int, num_blocks: int) -> int:
+    """Host check of block tables and lengths (numpy int32 arrays): -1 if
+    every length fits the table and every used entry names a pool block,
+    else the first offending sequence.  Raises on bad sizes."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if bt.ndim != 2 or lens.ndim != 1 or lens.shape[0] != bt.shape[0]:
+        raise ValueError("block_tables [B][max_blocks] and context_lens [B] expected")
+    bad = ctypes.c_int32(-1)
+    st = load_library().pkv_validate_tables(bt.ctypes.data, bt.shape[1], lens.ctypes.data,
+                                            lens.shape[0], max_context_len, num_blocks,
+                                            ctypes.byref(bad))
+    if st != PKV_OK and bad.value < 0:
+        _check(st, "pkv_validate_tables")
+    return bad.value
+
+
+def pkv_set_debug_checks(on: bool) -> bool:
+    """Turn the debug table checks of the device calls on or off; returns the
+    previous setting."""
+    return bool(load_library().pkv_set_debug_checks(1 if on else 0))
+
+
+def pkv_get_debug_checks() -> bool:
+    return bool(load_library().pkv_get_debug_checks())
+
+
+_PROBE_KEY = 0x9E3779B9   # stored only if the folded data equals it
+
+
+def pkv_hbm_read_probe(buf, sink, stream=None) -> None:
+    """Stream the bytes of device tensor `buf` once (the streaming-read
+    ceiling); `sink` is a device int32/uint32 tensor of at least one word."""
+    _check(load_library().pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
+                                             _ptr(sink), _PROBE_KEY, _stream(stream)),
+           "pkv_hbm_read_probe")
+
+
+def pkv_tile_gather_probe(k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                          layout: CacheLayout, sink, stream=None) -> None:
+    """Read every K and V tile the decode of this batch reads, through the
+    block table, without arithmetic (the gather ceiling)."""
+    _check(load_library().pkv_tile_gather_probe(
+        _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), context_lens.shape[0], max_context_len, ctypes.byref(layout),
+        _ptr(sink), _PROBE_KEY, _stream(stream)), "pkv_tile_gather_probe")
+
 
 def pkv_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, layout: CacheLayout,
                           k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <vector>
 
 #include "pkv.h"
 
@@ -29,6 +30,24 @@ inline pkv_status check_layout(const pkv_cache_layout* l) {
 // Status of the launches since the last (void)hipGetLastError().
 inline pkv_status launch_status() {
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// The debug path of the table checks (pkv_set_debug_checks): copy the device
+// block table and lengths to the host, waiting for `s`, and validate them.
+// Without the switch nothing is copied.
+inline pkv_status debug_check_tables(const int32_t* block_tables, int32_t max_blocks,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t max_ctx, int32_t num_blocks, hipStream_t s) {
+  if (num_seqs <= 0 || !pkv_get_debug_checks()) return PKV_OK;
+  std::vector<int32_t> tables((size_t)num_seqs * (size_t)max_blocks), lens((size_t)num_seqs);
+  if (hipMemcpyAsync(tables.data(), block_tables, tables.size() * sizeof(int32_t),
+                     hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(lens.data(), context_lens, lens.size() * sizeof(int32_t),
+                     hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return PKV_ERR_HIP;
+  return pkv_validate_tables(tables.data(), max_blocks, lens.data(), num_seqs, max_ctx,
+                             num_blocks, nullptr);
 }
 
 }  // namespace pkv_check

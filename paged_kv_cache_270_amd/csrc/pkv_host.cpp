@@ -8,10 +8,12 @@
 // PagedAttention: por qué se reduce la velocidad de tu servidor LLM", and the
 // release-on-cancel rule of "PagedAttention y Gestión de KV-Cache" §4.02.
 // No HIP here: this file is plain C++17 and runs without a GPU.
+#include <algorithm>
+#include <atomic>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <deque>
-#include <algorithm>
 #include <new>
 #include <set>
 #include <unordered_map>
@@ -58,6 +60,54 @@ extern "C" uint64_t pkv_pool_bytes(const pkv_cache_layout* l) {
   return (uint64_t)l->num_blocks * (uint64_t)l->num_kv_heads * (uint64_t)l->block_size *
          (uint64_t)l->head_dim * e;
 }
+
+// ----------------------------------------------------- table checks (debug)
+//
+// The decode kernel takes the block table as an extra input ("LLM Primer VI
+// ...", §8.1); a table entry names a physical block of the pool and a length
+// may not run past the table.  The kernels clamp lengths and skip ids outside
+// the pool; these checks turn such contents into an error instead.
+
+extern "C" pkv_status pkv_validate_tables(const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t max_context_len, int32_t num_blocks,
+                                          int32_t* bad_seq_out) {
+  if (bad_seq_out) *bad_seq_out = -1;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return PKV_ERR_INVALID_ARG;
+  const int64_t cap =
+      std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * 16);
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t L = context_lens[b];
+    bool ok = L >= 0 && L <= cap;
+    const int32_t* row = block_tables + (int64_t)b * max_blocks_per_seq;
+    for (int64_t j = 0; ok && j < (L + 15) / 16; ++j)
+      ok = row[j] >= 0 && row[j] < num_blocks;
+    if (!ok) {
+      if (bad_seq_out) *bad_seq_out = b;
+      return PKV_ERR_INVALID_ARG;
+    }
+  }
+  return PKV_OK;
+}
+
+namespace {
+std::atomic<int32_t>& debug_checks_flag() {
+  static std::atomic<int32_t> flag([] {
+    const char* e = std::getenv("PKV_DEBUG_CHECKS");
+    return (int32_t)(e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0);
+  }());
+  return flag;
+}
+}  // namespace
+
+extern "C" int32_t pkv_set_debug_checks(int32_t on) {
+  return debug_checks_flag().exchange(on != 0 ? 1 : 0);
+}
+
+extern "C" int32_t pkv_get_debug_checks(void) { return debug_checks_flag().load(); }
 
 // ------------------------------------------------------------- block pool
 //

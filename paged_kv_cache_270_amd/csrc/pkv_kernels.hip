@@ -165,7 +165,7 @@ __device__ __forceinline__ int seq_parts(const DecodeArgs& a, int b, int L) {
 // ------------------------------------------- newest token, written in place
 //
 // A decode step first stores the new token's K and V rows in its slot
-// ([FP8-128K] §6.2, the cache write) and then attends over the whole
+// ([FP8-128K] §4, the cache write) and then attends over the whole
 // context, that token included.  The decode kernels do both in one launch.
 // The wave that reads the sequence's last block
 //   1. loads the token's rows (one dword of K and one of V per lane) with
@@ -1046,7 +1046,8 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
                        int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale,
                        float k_scale, float v_scale, const float* k_bscale,
                        const float* v_bscale, int32_t partition_size, void* workspace,
-                       uint64_t workspace_bytes, bool need_pools, DecodePlan* plan) {
+                       uint64_t workspace_bytes, bool need_pools, DecodePlan* plan,
+                       hipStream_t stream) {
   pkv_status st = check_layout(layout);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_seqs > 65535 || max_context_len < 0 || num_q_heads <= 0)
@@ -1069,6 +1070,9 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
     if (!std::isfinite(sm_scale)) return PKV_ERR_INVALID_ARG;
     if (plan->dyn && (!k_bscale || !v_bscale || !aligned(k_bscale, 4) || !aligned(v_bscale, 4)))
       return PKV_ERR_INVALID_ARG;
+    st = debug_check_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                            max_context_len, layout->num_blocks, stream);
+    if (st != PKV_OK) return st;
   } else if (max_blocks_per_seq <= 0) {
     return PKV_ERR_INVALID_ARG;
   }
@@ -1389,7 +1393,8 @@ extern "C" pkv_status pkv_decode_partitions(float* out, const void* q, const voi
   pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                               context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
                               max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
-                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl,
+                              static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
   return run_partitions(pl, num_seqs, static_cast<hipStream_t>(stream));
 }
@@ -1404,7 +1409,8 @@ extern "C" pkv_status pkv_decode_reduce(float* out, const int32_t* context_lens,
   pkv_status st = plan_decode(out, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq,
                               context_lens, nullptr, num_seqs, num_q_heads, max_context_len,
                               layout, 1.0f, 1.0f, v_scale, nullptr, nullptr, partition_size,
-                              workspace, workspace_bytes, false, &pl);
+                              workspace, workspace_bytes, false, &pl,
+                              static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
   return run_reduce(pl, num_seqs, static_cast<hipStream_t>(stream));
 }
@@ -1420,7 +1426,8 @@ extern "C" pkv_status pkv_paged_attention_decode(
   pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                               context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
                               max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
-                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl,
+                              static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_partitions(pl, num_seqs, s);
@@ -1451,7 +1458,8 @@ extern "C" pkv_status pkv_decode_partitions_append(
   pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                               context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
                               max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
-                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl,
+                              static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
   st = set_append(&pl, num_seqs, key, value, k_pool, v_pool);
   if (st != PKV_OK) return st;
@@ -1469,7 +1477,8 @@ extern "C" pkv_status pkv_paged_attention_decode_append(
   pkv_status st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                               context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
                               max_context_len, layout, sm_scale, k_scale, v_scale, nullptr,
-                              nullptr, partition_size, workspace, workspace_bytes, true, &pl);
+                              nullptr, partition_size, workspace, workspace_bytes, true, &pl,
+                              static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
   st = set_append(&pl, num_seqs, key, value, k_pool, v_pool);
   if (st != PKV_OK) return st;
@@ -1510,6 +1519,8 @@ static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
                                     num_groups > 0 ? max_prefix_blocks : 0);
   if (cl.ws.total > 0) {
     if (!workspace || workspace_bytes < cl.ws.total) return PKV_ERR_WORKSPACE;
+    // the output rows start ml_bytes (a multiple of 256) past the base
+    if (!aligned(workspace, 256)) return PKV_ERR_INVALID_ARG;
     a.ws_ml = static_cast<float*>(workspace);
     a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + cl.ws.ml_bytes);
   }
@@ -1574,7 +1585,8 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade(
   st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                    shared_prefix_blocks, num_seqs, num_q_heads, max_context_len, layout,
                    sm_scale, k_scale, v_scale, nullptr, nullptr, partition_size, workspace,
-                   workspace_bytes, true, &pl);
+                   workspace_bytes, true, &pl,
+                              static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
   if (key) {
@@ -1603,7 +1615,8 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade_dynamic(
   st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                    shared_prefix_blocks, num_seqs, num_q_heads, max_context_len, layout,
                    sm_scale, 1.0f, 1.0f, k_block_scales, v_block_scales, partition_size,
-                   workspace, workspace_bytes, true, &pl);
+                   workspace, workspace_bytes, true, &pl,
+                              static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
   return run_cascade(pl, prefix_blocks, prefix_groups, num_groups, group_cap,
@@ -1624,7 +1637,8 @@ extern "C" pkv_status pkv_paged_attention_decode_dynamic(
                               context_lens, shared_prefix_blocks, num_seqs, num_q_heads,
                               max_context_len, layout, sm_scale, 1.0f, 1.0f, k_block_scales,
                               v_block_scales, partition_size, workspace, workspace_bytes, true,
-                              &pl);
+                              &pl,
+                              static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_partitions(pl, num_seqs, s);

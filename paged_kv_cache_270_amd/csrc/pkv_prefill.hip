@@ -552,6 +552,10 @@ extern "C" pkv_status pkv_paged_prefill_attention(
                                      num_q_heads, max_query_len, max_context_len, layout,
                                      sm_scale, k_scale, v_scale, a, empty);
   if (st != PKV_OK || empty) return st;
+  const pkv_status chk =
+      debug_check_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                         max_context_len, layout->num_blocks, static_cast<hipStream_t>(stream));
+  if (chk != PKV_OK) return chk;
   return layout->dtype == PKV_FP8_E4M3FN
              ? launch_prefill<true, false>(a, max_query_len, num_seqs, stream)
              : launch_prefill<false, false>(a, max_query_len, num_seqs, stream);
@@ -571,5 +575,9 @@ extern "C" pkv_status pkv_paged_prefill_attention_dynamic(
                                      query_start, num_seqs, num_q_heads, max_query_len,
                                      max_context_len, layout, sm_scale, 1.0f, 1.0f, a, empty);
   if (st != PKV_OK || empty) return st;
+  const pkv_status chk =
+      debug_check_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                         max_context_len, layout->num_blocks, static_cast<hipStream_t>(stream));
+  if (chk != PKV_OK) return chk;
   return launch_prefill<true, true>(a, max_query_len, num_seqs, stream);
 }

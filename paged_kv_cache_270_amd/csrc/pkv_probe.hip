@@ -1,0 +1,152 @@
+// pkv_probe.hip — memory ceilings the decode kernel is measured against (gfx950).
+//
+// "LLM Primer VI, Capítulo 8 — Gestión de caché KV de nueva generación" §8.1
+// compares a paged attention kernel with one that reads a contiguous slab:
+// on a GPU whose L2 absorbs the scattered accesses the paged kernel comes
+// within a few percent.  Two reads give the two sides of that comparison on
+// this part, without any attention arithmetic:
+//   * pkv_hbm_read_probe: a contiguous buffer streamed once, 16 bytes per
+//     lane per load, non-temporal -- the streaming-read ceiling;
+//   * pkv_tile_gather_probe: the decode kernel's own reads -- every K and V
+//     tile of every sequence, gathered through the block table with the same
+//     16-byte lane loads and cache policy, one workgroup of four waves per
+//     (sequence, KV head), two tiles in flight per wave.
+// Both fold what they read into one word per lane and store it only when it
+// equals a value the host passes and the data never produces in practice,
+// so the loads cannot be dropped and nothing measurable is written.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pkv.h"
+#include "pkv_check.h"
+#include "pkv_tile.h"
+
+namespace {
+
+using namespace pkv_dev;
+using namespace pkv_check;
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 8;   // 16-byte loads in flight per lane
+
+__global__ void __launch_bounds__(kProbeThreads)
+stream_read_kernel(const u32x4* __restrict__ buf, uint64_t n_vec, uint32_t* sink, uint32_t key) {
+  const uint64_t stride = (uint64_t)gridDim.x * kProbeThreads;
+  uint64_t i = (uint64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kProbeUnroll - 1) * stride < n_vec; i += kProbeUnroll * stride) {
+    u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n_vec; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(buf + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == key) sink[0] = acc;
+}
+
+struct GatherArgs {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t max_blocks, num_blocks, hkv, max_ctx;
+  uint32_t* sink;
+  uint32_t key;
+};
+
+template <bool kFP8>
+__global__ void __launch_bounds__(4 * kWave) tile_gather_kernel(GatherArgs a) {
+  constexpr int kPD = 2;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  int L = a.context_lens[b];
+  const int cap = min(a.max_ctx, a.max_blocks * kBS);
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int nblk = (L + kBS - 1) / kBS;
+  const int my_n = w < nblk ? (nblk - w + 3) / 4 : 0;
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + w;
+  uint32_t acc = 0;
+  for (int c0 = 0; c0 < my_n; c0 += kWave) {
+    const int cnt = min(kWave, my_n - c0);
+    const int tbl = lane < cnt ? trow[(int64_t)(c0 + lane) * 4] : 0;
+    TileRegs<kFP8> buf[kPD];
+#pragma unroll
+    for (int r = 0; r < kPD; ++r)
+      if (r < cnt)
+        load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                        __builtin_amdgcn_readlane(tbl, r), kvh, lane, false);
+    for (int base = 0; base < cnt; base += kPD) {
+#pragma unroll
+      for (int r = 0; r < kPD; ++r) {
+        const int ii = base + r;
+        if (ii < cnt) {
+#pragma unroll
+          for (int v = 0; v < TileRegs<kFP8>::kVecs; ++v)
+            acc ^= buf[r].k[v].x ^ buf[r].k[v].w ^ buf[r].v[v].y ^ buf[r].v[v].z;
+          if (ii + kPD < cnt)
+            load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                            __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane, false);
+        }
+      }
+    }
+  }
+  if (acc == a.key) a.sink[0] = acc;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_hbm_read_probe(const void* buf, uint64_t bytes, uint32_t* sink,
+                                         uint32_t key, void* stream) {
+  if (bytes == 0) return PKV_OK;
+  if (!buf || !sink || !aligned(buf, 16) || bytes % 16 != 0) return PKV_ERR_INVALID_ARG;
+  const uint64_t n_vec = bytes / 16;
+  // eight workgroups per CU of the 256 on MI355X; each lane keeps eight
+  // 16-byte loads in flight
+  const uint64_t want = (n_vec + (uint64_t)kProbeThreads * kProbeUnroll - 1) /
+                        ((uint64_t)kProbeThreads * kProbeUnroll);
+  const unsigned grid = (unsigned)(want < 2048 ? (want == 0 ? 1 : want) : 2048);
+  (void)hipGetLastError();
+  stream_read_kernel<<<grid, kProbeThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4*>(buf), n_vec, sink, key);
+  return launch_status();
+}
+
+extern "C" pkv_status pkv_tile_gather_probe(const void* k_pool, const void* v_pool,
+                                            const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t num_seqs,
+                                            int32_t max_context_len,
+                                            const pkv_cache_layout* layout, uint32_t* sink,
+                                            uint32_t key, void* stream) {
+  pkv_status st = check_layout(layout);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_seqs > 65535 || max_context_len < 0) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !block_tables || !context_lens || !sink ||
+      max_blocks_per_seq <= 0 || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return PKV_ERR_INVALID_ARG;
+  GatherArgs a;
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = layout->num_blocks;
+  a.hkv = layout->num_kv_heads;
+  a.max_ctx = max_context_len;
+  a.sink = sink;
+  a.key = key;
+  const dim3 grid((unsigned)a.hkv, (unsigned)num_seqs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (layout->dtype == PKV_FP8_E4M3FN)
+    tile_gather_kernel<true><<<grid, 4 * kWave, 0, s>>>(a);
+  else
+    tile_gather_kernel<false><<<grid, 4 * kWave, 0, s>>>(a);
+  return launch_status();
+}

@@ -226,28 +226,52 @@ def test_cascade_from_pool_forks():
     _cascade(prep, groups, prefix, 8, 0, True, "pool forks", order)
 
 
-def test_cascade_shared_prefix_full():
+def _pool_built(wl):
+    """The workload's sequences grown in the library's host block pool as
+    the benchmark grows them: each group's leader takes the prefix, the
+    other members fork it, every member appends its tail, then one call
+    assigns every sequence's newest token.  Returns the tables, lengths,
+    prefix groups and the longest-tail-first order the pool reports."""
+    pool = pkv.BlockPool(wl.num_blocks, shuffle_seed=wl.seed)
+    lens = [int(x) for x in wl.context_lens]
+    seqs = []
+    for members in wl.groups:
+        leader = pool.create()
+        pool.append(leader, wl.prefix_blocks * 16)
+        ids = [leader] + [pool.fork(leader) for _ in members[1:]]
+        for sid, b in zip(ids, members):
+            pool.append(sid, lens[b] - wl.prefix_blocks * 16 - 1)
+            seqs.append(sid)
+    pool.append_each(seqs)
+    got = np.array([pool.seq_len(s) for s in seqs], dtype=np.int32)
+    assert np.array_equal(got, wl.context_lens)
+    rows = [pool.block_table(s) for s in seqs]
+    tables = np.zeros((len(seqs), max(len(r) for r in rows)), dtype=np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = r
+    prefix, garr, max_pre, order = pool.prefix_groups(seqs, 8, with_order=True)
+    return tables, got, prefix, garr, max_pre, order
+
+
+def test_cascade_shared_prefix_full_step():
     """The 256-sequence shared-prefix batch at full size (FP8, 32 groups of 8
-    with a 125-block prefix): sampled sequences against the oracle, and every
-    output within the bound of the plain decode."""
-    wl = workloads.shared_prefix()
+    with a 125-block prefix), run as the benchmark's step runs it: sequences
+    grown in the host pool, groups and the longest-tail order from the pool,
+    the automatic partition size, and each sequence's newest K/V rows written
+    by the cascade call itself.  Both pools must equal the oracle's write
+    byte for byte, and all 256 outputs must match the oracle's decode."""
+    base = workloads.shared_prefix()
+    tables, lens, prefix, garr, max_pre, order = _pool_built(base)
+    assert garr.shape[0] == 32 and max_pre == base.prefix_blocks
+    B = base.num_seqs
+    new = [(b, int(L) - 1) for b, L in enumerate(lens)]
+    wl = workloads.Workload(base.name, base.seed, base.num_q_heads, base.num_kv_heads, True,
+                            base.num_blocks, lens, tables, new_tokens=new)
     prep = Prepared(wl)
-    B = wl.num_seqs
-    prefix = np.full(B, wl.prefix_blocks, dtype=np.int32)
-    garr = _group_array(wl.groups, 8)
-    out = torch.empty(prep.q.shape, dtype=torch.float32, device="cuda")
-    pkv.pkv_paged_attention_decode_cascade(
-        out, prep.q, None, None, prep.k_pool, prep.v_pool, prep.tables, prep.lens,
-        wl.max_context_len, prep.layout, prep.sm_scale, torch.from_numpy(prefix).cuda(),
-        torch.from_numpy(garr).cuda(), wl.prefix_blocks, prep.k_scale, prep.v_scale, 0)
-    plain = prep.gpu_decode(partition_size=0)
-    got = out.cpu().numpy()
-    assert max_err(got, plain.astype(np.float64)) <= TOL[True]
-    sample = np.array([0, 7, 8, 100, 131, 255])
-    ref = prep.oracle_decode(sample)
-    err = max_err(got[sample], ref)
-    print(f"[parity] cascade shared-prefix B=256 sampled: max abs err {err:.3e}", flush=True)
-    assert err <= TOL[True]
+    groups = [[int(m) for m in g if m >= 0] for g in garr]
+    assert sorted(m for g in groups for m in g) == list(range(B))
+    got = _cascade(prep, groups, prefix, 8, 0, True, "shared-prefix B=256 full step", order)
+    assert got.shape == (B, wl.num_q_heads, D)
 
 
 def test_cascade_rejects_bad_arguments():
