@@ -109,11 +109,14 @@ def timed_launches(fn, reps: int, warmup: int = 3) -> float:
 
 def stream_read_gbs(pkv, nbytes: int = 2 << 30) -> float:
     """Streaming-read ceiling: a contiguous buffer (far larger than the 256 MB
-    last-level cache) read once per launch with 16-byte non-temporal loads."""
+    last-level cache) read once per launch with 16-byte non-temporal loads,
+    the best of four grid sizes."""
     import torch
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ms = timed_launches(lambda: pkv.pkv_hbm_read_probe(buf, sink), 20)
+    # the best of a few launch shapes (workgroups of 256 lanes, each its own slab)
+    ms = min(timed_launches(lambda: pkv.pkv_hbm_read_probe(buf, sink, wg), 20)
+             for wg in (1024, 2048, 4096, 8192))
     del buf
     return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
@@ -539,10 +542,13 @@ def main() -> int:
     # prefix groups of the batch, found by the host pool from the forks
     prefix, garr, max_pre, order = pool.prefix_groups(seqs, 8, with_order=True)
     cascade = args.cascade == "on" or (args.cascade == "auto" and garr.shape[0] > 0)
+    tail_units = 0
     if cascade:
         d_prefix = torch.from_numpy(prefix).to(dev)
         d_groups = torch.from_numpy(garr).to(dev) if garr.shape[0] else None
         d_order = torch.from_numpy(order).to(dev)   # longest tails first
+        # the tail work the launch holds, counted by the pool from its lengths
+        tail_units = pool.cascade_tail_units(seqs, prefix, max_pre, P)
         ws_bytes = pkv.pkv_decode_cascade_workspace_bytes(B, Hq, Hkv, Lmax, max_pre,
                                                           layout.dtype, P)
     else:
@@ -585,7 +591,7 @@ def main() -> int:
                 pkv.pkv_paged_attention_decode_cascade_dynamic(
                     out, q, k_pool, v_pool, k_bs, v_bs, d_tables, d_lens, Lmax, layout, sm_scale,
                     d_prefix, d_groups, max_pre, P, ws, shared_prefix_blocks=d_shared,
-                    seq_order=d_order)
+                    seq_order=d_order, tail_units=tail_units)
             else:
                 pkv.pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_bs, v_bs,
                                                        d_tables, d_lens, Lmax, layout, sm_scale,
@@ -597,7 +603,7 @@ def main() -> int:
             pkv.pkv_paged_attention_decode_cascade(
                 out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens, Lmax, layout, sm_scale,
                 d_prefix, d_groups, max_pre, k_scale, v_scale, P, ws,
-                shared_prefix_blocks=d_shared, seq_order=d_order)
+                shared_prefix_blocks=d_shared, seq_order=d_order, tail_units=tail_units)
             return
         # the newest token of each sequence (position L - 1, the slot
         # pool.append gave it) is written by the partition kernel itself
@@ -645,7 +651,7 @@ def main() -> int:
                 pkv.pkv_paged_attention_decode_cascade_dynamic(
                     out, q, k_pool, v_pool, k_bs, v_bs, d_tables, d_lens, Lmax, layout,
                     sm_scale, d_prefix, d_groups, max_pre, P, ws, shared_prefix_blocks=d_shared,
-                    seq_order=d_order)
+                    seq_order=d_order, tail_units=tail_units)
             part_covers = "partition + merge kernels (the cascade decode call)"
         elif dyn:
             def kernel_only():
@@ -659,7 +665,7 @@ def main() -> int:
                 pkv.pkv_paged_attention_decode_cascade(
                     out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens, Lmax, layout,
                     sm_scale, d_prefix, d_groups, max_pre, k_scale, v_scale, P, ws,
-                    shared_prefix_blocks=d_shared, seq_order=d_order)
+                    shared_prefix_blocks=d_shared, seq_order=d_order, tail_units=tail_units)
             part_covers = "partition + merge kernels (the cascade call)"
         else:
             def kernel_only():
@@ -770,7 +776,8 @@ def main() -> int:
                    "launch": "hip graph" if args.graph else "eager",
                    "new_token_write": "separate launch" if dyn else "in the decode kernel",
                    "decode": ("cascade: each shared prefix once per group "
-                              f"({garr.shape[0]} groups, {max_pre} prefix blocks)")
+                              f"({garr.shape[0]} groups, {max_pre} prefix blocks, "
+                              f"{tail_units} tail units)")
                    if cascade else "per sequence"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tok_per_s": round(tokens / (step_ms * 1e-3), 1),

@@ -314,12 +314,25 @@ pkv_status pkv_decode_partitions_append(
  *                  entry outside [0, num_seqs) is skipped; a sequence not
  *                  listed gets unspecified output (no memory outside the
  *                  arguments is touched).
+ *   tail_units     host: the tail work of the batch, summed over the
+ *                  sequences seq_order lists (every one without it) of
+ *                  max(1, ceil(tail blocks / (P / 16))) -- the partitions of
+ *                  each tail, one for a sequence with no tail tokens to
+ *                  write zeros -- as pkv_pool_cascade_tail_units counts it
+ *                  from the pool; 0 = unknown.  It sizes the launch: with
+ *                  the exact count every workgroup takes one unit, and
+ *                  prefix and tail units follow each other with no empty
+ *                  workgroups.  Any positive value gives the same result (a
+ *                  smaller one makes workgroups take several units, a larger
+ *                  one leaves some idle); 0 launches an upper bound derived
+ *                  from max_context_len.
  *   key, value     the newest tokens' rows as in
  *                  pkv_paged_attention_decode_append, written in the same
  *                  launch; both null = decode only.
  * Other arguments as in pkv_paged_attention_decode_append.  The kernel
  * variant is the default family whatever PKV_* variant switches say.
- * Errors: INVALID_ARG for one of key/value null, negative counts, groups
+ * Errors: INVALID_ARG for one of key/value null, negative counts (tail_units
+ * included), groups
  * without arrays, or more than 65535 items plus sequences
  * (num_groups * ceil(group_cap / floor(16 / G)) + num_seqs); WORKSPACE if the
  * workspace is smaller than pkv_decode_cascade_workspace_bytes. */
@@ -328,10 +341,10 @@ pkv_status pkv_paged_attention_decode_cascade(
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
     const int32_t* shared_prefix_blocks, const int32_t* prefix_blocks,
     const int32_t* prefix_groups, int32_t num_groups, int32_t group_cap,
-    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
-    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
-    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-    void* stream);
+    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units, int32_t num_seqs,
+    int32_t num_q_heads, int32_t max_context_len, const pkv_cache_layout* layout,
+    float sm_scale, float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    uint64_t workspace_bytes, void* stream);
 
 /* The cascade over a cache with per-(block, KV head) FP8 scales (the
  * decode of pkv_paged_attention_decode_dynamic, with the prefix groups,
@@ -344,10 +357,10 @@ pkv_status pkv_paged_attention_decode_cascade_dynamic(
     const float* k_block_scales, const float* v_block_scales, const int32_t* block_tables,
     int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* shared_prefix_blocks,
     const int32_t* prefix_blocks, const int32_t* prefix_groups, int32_t num_groups,
-    int32_t group_cap, int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs,
-    int32_t num_q_heads, int32_t max_context_len, const pkv_cache_layout* layout,
-    float sm_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-    void* stream);
+    int32_t group_cap, int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units,
+    int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const pkv_cache_layout* layout, float sm_scale, int32_t partition_size, void* workspace,
+    uint64_t workspace_bytes, void* stream);
 
 /* Workspace of pkv_paged_attention_decode_cascade: room for each sequence's
  * prefix partitions (ceil(16 * max_prefix_blocks / P)) and tail partitions;
@@ -526,6 +539,19 @@ pkv_status pkv_seq_append(pkv_pool* pool, int32_t seq, int32_t n_tokens, int64_t
 pkv_status pkv_seq_append_each(pkv_pool* pool, const int32_t* seqs, int32_t n,
                                int64_t* slots_out, int32_t* cow_pairs_out, int32_t* n_cow_out,
                                int32_t* n_done_out);
+/* The tail work of a cascade decode of seqs[0..n) (pkv_pool_prefix_groups'
+ * batch, whose prefix_blocks and max_prefix_blocks it takes): for each
+ * sequence, with L its length in the pool and S its prefix blocks where
+ * 0 < S <= max_prefix_blocks and 16 * S < L (else S = 0), the count
+ * max(1, ceil((ceil(L / 16) - S) / (partition_size / 16))), summed into
+ * *units_out -- the tail_units argument of
+ * pkv_paged_attention_decode_cascade.  partition_size: the split the decode
+ * uses (pkv_decode_partition_size), a positive multiple of 16.
+ * BAD_HANDLE for an unknown sequence; INVALID_ARG for bad sizes. */
+pkv_status pkv_pool_cascade_tail_units(const pkv_pool* pool, const int32_t* seqs, int32_t n,
+                                       const int32_t* prefix_blocks,
+                                       int32_t max_prefix_blocks, int32_t partition_size,
+                                       int64_t* units_out);
 /* Release a sequence: each of its blocks loses one reference; at zero it
  * returns to the free list, or becomes evictable if the prefix cache holds it
  * ([GLOSSARY] §4.02: pages of a cancelled request go back to the pool at once,
@@ -668,15 +694,17 @@ pkv_status pkv_swap_blocks(void* k_pool, void* v_pool, void* host_k, void* host_
  * compares a paged kernel with one reading a contiguous slab; these two give
  * both sides of that comparison without attention arithmetic.
  * pkv_hbm_read_probe streams `bytes` (a multiple of 16) of device memory at
- * `buf` (16-byte aligned) once with 16-byte non-temporal lane loads.
+ * `buf` (16-byte aligned) once with 16-byte non-temporal lane loads: each of
+ * `workgroups` workgroups (0 = 2048) reads its own contiguous slab in 32 KiB
+ * steps.
  * pkv_tile_gather_probe reads every K and V tile of every sequence through
  * its block table, as the decode kernel does (same loads, same cache policy;
  * arguments as in pkv_paged_attention_decode; ids outside the pool read
  * nothing).  Both fold what they read into one word per lane and store it to
  * sink[0] (device uint32) only if it equals `key`, so nothing measurable is
  * written.  Asynchronous on `stream`. */
-pkv_status pkv_hbm_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, uint32_t key,
-                              void* stream);
+pkv_status pkv_hbm_read_probe(const void* buf, uint64_t bytes, int32_t workgroups,
+                              uint32_t* sink, uint32_t key, void* stream);
 pkv_status pkv_tile_gather_probe(const void* k_pool, const void* v_pool,
                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
                                  const int32_t* context_lens, int32_t num_seqs,

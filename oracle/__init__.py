@@ -25,7 +25,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpkv_oracle.so")
+# PKV_ORACLE_LIBRARY names another build of pkv_oracle.c (the sanitizer
+# build of the CPU tests)
+_LIB_PATH = os.environ.get("PKV_ORACLE_LIBRARY") or os.path.join(_HERE, "libpkv_oracle.so")
 _lib = None
 
 BLOCK_SIZE = 16

@@ -22,11 +22,15 @@ __all__ = [
     "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic", "pkv_paged_prefill_attention",
     "pkv_paged_prefill_attention_dynamic", "pkv_swap_blocks", "pkv_validate_tables",
     "pkv_set_debug_checks", "pkv_get_debug_checks", "pkv_hbm_read_probe",
-    "pkv_tile_gather_probe",
+    "pkv_tile_gather_probe"
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libpkv.so")
+# PKV_LIBRARY names another build of the library, e.g. the host half alone
+# built with sanitizers for the CPU tests; functions it lacks then raise when
+# called
+_OVERRIDE = os.environ.get("PKV_LIBRARY", "")
+lib_path = _OVERRIDE or os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = -1
@@ -85,7 +89,7 @@ def load_library():
         "pkv_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], u64),
         "pkv_validate_tables": ([P, i32, P, i32, i32, i32, ctypes.POINTER(i32)], i32),
         "pkv_set_debug_checks": ([i32], i32),
-        "pkv_hbm_read_probe": ([P, u64, P, ctypes.c_uint32, P], i32),
+        "pkv_hbm_read_probe": ([P, u64, i32, P, ctypes.c_uint32, P], i32),
         "pkv_tile_gather_probe": ([P, P, P, i32, P, i32, i32, LP, P, ctypes.c_uint32, P], i32),
         "pkv_get_debug_checks": ([], i32),
         "pkv_reshape_and_cache": ([P, P, P, P, P, i32, LP, f32, f32, P], i32),
@@ -99,11 +103,12 @@ def load_library():
         "pkv_decode_partitions_append": ([P, P, P, P, P, P, P, i32, P, P, i32, i32, i32, LP,
                                           f32, f32, f32, i32, P, u64, P], i32),
         "pkv_paged_attention_decode_cascade": ([P, P, P, P, P, P, P, i32, P, P, P, P, i32, i32,
-                                                i32, P, i32, i32, i32, LP, f32, f32, f32, i32,
-                                                P, u64, P], i32),
+                                                i32, P, i32, i32, i32, i32, LP, f32, f32, f32,
+                                                i32, P, u64, P], i32),
         "pkv_paged_attention_decode_cascade_dynamic": ([P, P, P, P, P, P, P, i32, P, P, P, P,
-                                                        i32, i32, i32, P, i32, i32, i32, LP,
-                                                        f32, i32, P, u64, P], i32),
+                                                        i32, i32, i32, P, i32, i32, i32, i32,
+                                                        LP, f32, i32, P, u64, P], i32),
+        "pkv_pool_cascade_tail_units": ([P, P, i32, P, i32, i32, ctypes.POINTER(i64)], i32),
         "pkv_decode_cascade_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], u64),
         "pkv_pool_prefix_groups": ([P, P, i32, i32, i32, P, P, ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), P], i32),
@@ -146,7 +151,11 @@ def load_library():
         "pkv_prefix_cache_clear": ([P], None),
     }
     for name, (args, res) in sig.items():
-        fn = getattr(L, name)
+        fn = getattr(L, name, None)
+        if fn is None and _OVERRIDE:
+            continue
+        if fn is None:
+            raise ImportError(f"{lib_path} does not export {name}; rebuild it")
         fn.argtypes = args
         fn.restype = res
     _lib = L
@@ -244,12 +253,13 @@ def pkv_get_debug_checks() -> bool:
 _PROBE_KEY = 0x9E3779B9   # stored only if the folded data equals it
 
 
-def pkv_hbm_read_probe(buf, sink, stream=None) -> None:
+def pkv_hbm_read_probe(buf, sink, workgroups: int = 0, stream=None) -> None:
     """Stream the bytes of device tensor `buf` once (the streaming-read
-    ceiling); `sink` is a device int32/uint32 tensor of at least one word."""
+    ceiling), each workgroup its own contiguous slab; `sink` is a device
+    int32/uint32 tensor of at least one word."""
     _check(load_library().pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
-                                             _ptr(sink), _PROBE_KEY, _stream(stream)),
-           "pkv_hbm_read_probe")
+                                             workgroups, _ptr(sink), _PROBE_KEY,
+                                             _stream(stream)), "pkv_hbm_read_probe")
 
 
 def pkv_tile_gather_probe(k_pool, v_pool, block_tables, context_lens, max_context_len: int,
@@ -407,12 +417,15 @@ def pkv_paged_attention_decode_cascade(out, q, key, value, k_pool, v_pool, block
                                        max_prefix_blocks: int, k_scale: float = 1.0,
                                        v_scale: float = 1.0, partition_size: int = 0,
                                        workspace=None, stream=None,
-                                       shared_prefix_blocks=None, seq_order=None) -> None:
+                                       shared_prefix_blocks=None, seq_order=None,
+                                       tail_units: int = 0) -> None:
     """Decode with each group's shared prefix attended once for the group.
     prefix_blocks: device int32 [B]; prefix_groups: device int32
     [n_groups][group_cap] (or None for no groups); key/value: the newest
     tokens' rows to write in the same launch, or both None; seq_order:
-    optional device int32 [B], the order the tails are scheduled in."""
+    optional device int32 [B], the order the tails are scheduled in;
+    tail_units: the batch's tail work (BlockPool.cascade_tail_units), 0 =
+    unknown."""
     import torch
     B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
     if key is None and value is None:
@@ -433,10 +446,9 @@ def pkv_paged_attention_decode_cascade(out, q, key, value, k_pool, v_pool, block
     _check(load_library().pkv_paged_attention_decode_cascade(
         _ptr(out), _ptr(q), kp, vp, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
         _ptr(context_lens), _hint(shared_prefix_blocks, B), pp, gp, n_groups, cap,
-        max_prefix_blocks, _ptr(seq_order), B, Hq, max_context_len, ctypes.byref(layout),
-        sm_scale, k_scale,
-        v_scale, partition_size, _ptr(workspace), nbytes, _stream(stream)),
-        "pkv_paged_attention_decode_cascade")
+        max_prefix_blocks, _ptr(seq_order), tail_units, B, Hq, max_context_len,
+        ctypes.byref(layout), sm_scale, k_scale, v_scale, partition_size, _ptr(workspace), nbytes,
+        _stream(stream)), "pkv_paged_attention_decode_cascade")
 
 
 def _cascade_groups(prefix_blocks, prefix_groups, B):
@@ -458,7 +470,7 @@ def pkv_paged_attention_decode_cascade_dynamic(out, q, k_pool, v_pool, k_block_s
                                                max_prefix_blocks: int, partition_size: int = 0,
                                                workspace=None, stream=None,
                                                shared_prefix_blocks=None,
-                                               seq_order=None) -> None:
+                                               seq_order=None, tail_units: int = 0) -> None:
     """The cascade decode over per-(block, KV head) scales (fp32
     [num_blocks][Hkv] device tensors); decode only."""
     import torch
@@ -480,7 +492,7 @@ def pkv_paged_attention_decode_cascade_dynamic(out, q, k_pool, v_pool, k_block_s
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_block_scales),
         _ptr(v_block_scales), _ptr(block_tables), mb, _ptr(context_lens),
         _hint(shared_prefix_blocks, B), pp, gp, n_groups, cap, max_prefix_blocks,
-        _ptr(seq_order), B, Hq, max_context_len, ctypes.byref(layout), sm_scale,
+        _ptr(seq_order), tail_units, B, Hq, max_context_len, ctypes.byref(layout), sm_scale,
         partition_size, _ptr(workspace), nbytes, _stream(stream)),
         "pkv_paged_attention_decode_cascade_dynamic")
 
@@ -735,6 +747,22 @@ class BlockPool:
             "pkv_pool_prefix_groups")
         res = (prefix[:n].copy(), groups[:ng.value].copy(), mx.value)
         return res + (order[:n].copy(),) if with_order else res
+
+    def cascade_tail_units(self, seqs, prefix_blocks, max_prefix_blocks: int,
+                           partition_size: int) -> int:
+        """The tail_units argument of the cascade decode for this batch and
+        the prefix_groups result (prefix_blocks, max_prefix_blocks)."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        pre = np.ascontiguousarray(prefix_blocks, dtype=np.int32)
+        if pre.size != seqs.size:
+            raise ValueError("one prefix length per sequence")
+        out = ctypes.c_int64()
+        _check(self._L.pkv_pool_cascade_tail_units(self._h, seqs.ctypes.data, seqs.size,
+                                                   pre.ctypes.data, max_prefix_blocks,
+                                                   partition_size, ctypes.byref(out)),
+               "pkv_pool_cascade_tail_units")
+        return out.value
 
     # ---- swap space (page-granular eviction to host memory)
 

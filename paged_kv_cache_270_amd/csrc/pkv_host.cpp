@@ -10,6 +10,7 @@
 // No HIP here: this file is plain C++17 and runs without a GPU.
 #include <algorithm>
 #include <atomic>
+#include <cstddef>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -375,6 +376,29 @@ extern "C" int64_t pkv_seq_len(const pkv_pool* p, int32_t seq) {
   return it == p->seqs.end() ? -1 : it->second.len;
 }
 
+extern "C" pkv_status pkv_pool_cascade_tail_units(const pkv_pool* p, const int32_t* seqs,
+                                                  int32_t n, const int32_t* prefix_blocks,
+                                                  int32_t max_prefix_blocks,
+                                                  int32_t partition_size, int64_t* units_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (n < 0 || !units_out || (n > 0 && !seqs) || partition_size <= 0 ||
+      partition_size % 16 != 0 || max_prefix_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  const int64_t pb = partition_size / 16;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+    const int64_t L = it->second.len;
+    int64_t S = prefix_blocks ? prefix_blocks[i] : 0;
+    if (!(S > 0 && S <= max_prefix_blocks && 16 * S < L)) S = 0;
+    const int64_t tail = (L + 15) / 16 - S;
+    total += std::max<int64_t>(1, (tail + pb - 1) / pb);
+  }
+  *units_out = total;
+  return PKV_OK;
+}
+
 extern "C" int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* p, int32_t seq) {
   if (!p) return -1;
   auto it = p->seqs.find(seq);
@@ -434,8 +458,8 @@ extern "C" pkv_status pkv_pool_prefix_groups(const pkv_pool* p, const int32_t* s
     }
     if (S <= 0) continue;
     for (size_t c = 0; c < mem.size(); c += (size_t)group_cap) {
-      std::vector<int32_t> g(mem.begin() + (ptrdiff_t)c,
-                             mem.begin() + (ptrdiff_t)std::min(mem.size(), c + group_cap));
+      std::vector<int32_t> g(mem.begin() + (std::ptrdiff_t)c,
+                             mem.begin() + (std::ptrdiff_t)std::min(mem.size(), c + group_cap));
       for (int32_t i : g) prefix[(size_t)i] = (int32_t)S;
       groups.push_back(std::move(g));
     }

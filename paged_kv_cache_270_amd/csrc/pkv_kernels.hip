@@ -88,12 +88,19 @@ struct DecodeArgs {
   const int32_t* casc_prefix;  // [B] prefix blocks of each sequence, 0 = none
   const int32_t* casc_groups;  // [n_groups][casc_cap] member sequences, -1 = none
   int32_t casc_items;          // n_groups * casc_chunks
-  int32_t casc_chunks;         // items per group: ceil(casc_cap / casc_m)
+  int32_t casc_chunks;         // items per group: ceil(casc_cap / casc_mi)
   int32_t casc_cap;            // member slots per group
-  int32_t casc_m;              // members per item: 16 / G, one MFMA column each
+  int32_t casc_m;              // members per wave: 16 / G, one MFMA column each
+  int32_t casc_mi;             // members per item: casc_m, or kNW * casc_m when
+                               // the item's waves share its tiles (item_shared)
   int32_t casc_max;            // largest prefix (blocks) the workspace is sized for
   const int32_t* seq_order;    // [B] or null: the sequence of each tail z-slice
   int32_t nseq;                // B
+  // Flat cascade grid (casc_flat != 0): one dimension, KV head fastest; the
+  // first casc_items * casc_pp units are (item, prefix partition), the rest
+  // the tails' partitions in seq_order, each sequence's together.
+  int32_t casc_flat;
+  int32_t casc_pp;             // prefix partitions per item (flat grid)
 };
 
 // Partials are stored write-through to memory (cache policy sc0 sc1, through
@@ -160,6 +167,60 @@ __device__ __forceinline__ int seq_parts(const DecodeArgs& a, int b, int L) {
   if (S == 0) return seq_split(a, L).n_p;
   const int tail = (L + kBS - 1) / kBS - S;
   return prefix_split(a, S).n_p + (tail + a.part_blocks - 1) / a.part_blocks;
+}
+
+// Flat cascade grid: the (sequence, tail partition) of tail unit j, or
+// (-1, -1) past the last one, and in *total the number of tail units.
+// Units run through the sequences in seq_order (batch order without one),
+// each sequence's partitions together: one unit for an empty sequence (it
+// writes zeros), none for an order entry outside the batch.  Every lane of
+// the wave takes four sequences of a chunk of 256, counts their units, and a
+// wave-wide scan of the counts locates j; the result is the same on every
+// wave.
+__device__ int2 casc_tail_unit(const DecodeArgs& a, int j, int lane, int* total_out) {
+  int base = 0;
+  int2 found = make_int2(-1, -1);
+  for (int c0 = 0; c0 < a.nseq; c0 += 4 * kWave) {
+    int cnt[4], sq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = c0 + lane * 4 + e;
+      int sid = -1;
+      if (i < a.nseq) sid = a.seq_order != nullptr ? a.seq_order[i] : i;
+      if ((unsigned)sid >= (unsigned)a.nseq) sid = -1;
+      sq[e] = sid;
+      cnt[e] = 0;
+      if (sid >= 0) {
+        const int L = clamp_len(a, sid);
+        const int S = casc_blocks(a, sid, L);
+        cnt[e] = max(seq_split(a, L - S * kBS).n_p, 1);
+      }
+    }
+    const int local = (cnt[0] + cnt[1]) + (cnt[2] + cnt[3]);
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += y;
+    }
+    const int total = __shfl(incl, kWave - 1, kWave);
+    const int jj = j - base;
+    if (jj >= 0 && jj < total) {  // wave-uniform
+      // the first lane whose running count passes jj holds the unit
+      const int t = __builtin_ctzll((unsigned long long)__ballot(jj < incl));
+      int rem = jj - (__shfl(incl, t, kWave) - __shfl(local, t, kWave));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ce = __shfl(cnt[e], t, kWave);
+        const int se = __shfl(sq[e], t, kWave);
+        if (rem >= 0 && rem < ce) found = make_int2(se, rem);
+        rem -= ce;
+      }
+    }
+    base += total;
+  }
+  *total_out = base;
+  return found;
 }
 
 // ------------------------------------------- newest token, written in place
@@ -370,7 +431,13 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
     st.l += ((float)ph[0] + (float)ph[1]) + ((float)ph[2] + (float)ph[3]);
   }
   }
-  // O^T[d][g] += sum_t V^T[d][t] P^T[t][g]: 8 MFMAs of 16 channels
+  // O^T[d][g] += sum_t V^T[d][t] P^T[t][g]: 8 MFMAs of 16 channels.  With
+  // P split into hi + lo the contraction runs over K = 32 = 16 tokens x
+  // (hi, lo): lane (j, qg) supplies k = 8qg .. 8qg+7 as its four tokens'
+  // values twice (A) against their hi then their lo parts (B), so one
+  // 16x16x32 MFMA does the work of two 16x16x16 ones.
+  f16x8 pp;
+  if constexpr (kSplitP) pp = f16x8{ph[0], ph[1], ph[2], ph[3], pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     f16x4 va;
@@ -383,43 +450,143 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
       two.y = raw[(n & 1) * 2 + 1];
       va = __builtin_bit_cast(f16x4, two);
     }
-    st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, st.acc[n], 0, 0, 0);
-    if constexpr (kSplitP)
-      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, st.acc[n], 0, 0, 0);
+    if constexpr (kSplitP) {
+      const f16x8 vv = f16x8{va[0], va[1], va[2], va[3], va[0], va[1], va[2], va[3]};
+      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv, pp, st.acc[n], 0, 0, 0);
+    } else {
+      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, st.acc[n], 0, 0, 0);
+    }
   }
 }
 
-// Decode partition kernel.  Grid (n_p_max, Hkv, B); kNW waves per workgroup.
-// Workgroup (p, kvh, b) covers tokens [p*P, min(L, (p+1)*P)) of sequence b
-// for the G query heads of KV head kvh.  Wave w takes the partition's blocks
-// w, w + kNW, ...  Lane (j = lane % 16, qg = lane / 16) serves query head
-// kvh*G + j and, in each tile, tokens 4qg .. 4qg+3.  Each wave keeps kPD
-// tiles in flight while it computes on another.
-// With per-block scales the kernel is held to 128 VGPRs (4 waves per SIMD);
-// the compiler fits it without spilling (the cascade variant, 2 VGPRs over,
-// to 168: 3 waves per SIMD).  kAppend: the kernel also writes each
-// sequence's newest token (steps 1-3 above).  kCasc: the cascade over shared
-// prefixes (prefix items, then tails).
-template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false,
-          bool kAppend = false, bool kCasc = false>
-__global__ void __launch_bounds__(kNW * kWave)
-__attribute__((amdgpu_waves_per_eu(kDyn ? (kCasc ? 3 : 4) : 1)))
-decode_partition_kernel(DecodeArgs a) {
+// A prefix item whose four waves share its tiles (FP8, per-tensor scales):
+// every wave serves its own members (16 MFMA columns) over every tile of the
+// item's prefix partition.  Each tile is loaded once per workgroup -- a
+// 1 KiB quarter per wave: K bytes 0-1023, K 1024-2047, V 0-1023, V 1024-2047
+// -- converted to fp16 and staged in LDS as the fp16 image of each lane's
+// 16 bytes (32 bytes per lane), two buffers with one barrier per tile; every
+// wave reads the whole tile back in the order the fp16 tile registers hold,
+// so the fp16 arithmetic of process_tile applies unchanged.  Compared with an
+// item per wave, a tile is loaded and converted once instead of four times.
+// kRing tiles' quarters are in flight per wave.  The wave stores its
+// members' partials from registers at the end.
+constexpr int kItemWaves = 4;
+constexpr int kItemRing = 4;
+constexpr int kItemBuf = 8192;  // bytes of one staged fp16 tile
+
+__device__ __forceinline__ u32x4 item_quarter(const DecodeArgs& a, int phys, int kvh, int w,
+                                              int lane) {
+  if ((unsigned)phys >= (unsigned)a.num_blocks) return u32x4{0u, 0u, 0u, 0u};
+  const uint8_t* pool = w < 2 ? a.k_pool : a.v_pool;
+  const u32x4* src = reinterpret_cast<const u32x4*>(
+      pool + ((int64_t)phys * a.hkv + kvh) * (kBS * kD) + (w & 1) * 1024);
+  return src[lane];  // through the caches: every item of the group reads it
+}
+
+__device__ __forceinline__ void item_stage(uint8_t* buf, u32x4 raw, int w, int lane) {
+  const f16x4 h0 = dequant4<true>(raw.x), h1 = dequant4<true>(raw.y);
+  const f16x4 h2 = dequant4<true>(raw.z), h3 = dequant4<true>(raw.w);
+  u32x4* dst = reinterpret_cast<u32x4*>(buf + w * 2048 + 32 * lane);
+  dst[0] = __builtin_bit_cast(u32x4, f16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]});
+  dst[1] = __builtin_bit_cast(u32x4, f16x8{h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]});
+}
+
+__device__ void item_shared(const DecodeArgs& a, const f16x8 (&qop)[4], SoftmaxState& st,
+                            const int32_t* trow, int kvh, int nblk, int pidx, int member,
+                            int lane, int w, uint8_t* lds) {
+  const int j = lane & 15, qg = lane >> 4;
+  // An item's waves share their SIMDs with tail waves, which mostly wait on
+  // HBM; the item runs a tile-by-tile dependency chain from L2 in lock step.
+  // Issuing it first keeps it from holding its slot for the whole launch.
+  __builtin_amdgcn_s_setprio(2);
+  int g = 0;  // tiles staged so far: the parity of the LDS buffer
+  for (int c0 = 0; c0 < nblk; c0 += kWave) {
+    const int cnt = min(kWave, nblk - c0);
+    const int tbl = lane < cnt ? trow[c0 + lane] : 0;
+    u32x4 raw[kItemRing];
+#pragma unroll
+    for (int r = 0; r < kItemRing; ++r)
+      if (r < cnt) raw[r] = item_quarter(a, __builtin_amdgcn_readlane(tbl, r), kvh, w, lane);
+    item_stage(lds + (g & 1) * kItemBuf, raw[0], w, lane);
+    if (kItemRing < cnt)
+      raw[0] = item_quarter(a, __builtin_amdgcn_readlane(tbl, kItemRing), kvh, w, lane);
+    for (int base = 0; base < cnt; base += kItemRing) {
+#pragma unroll
+      for (int r = 0; r < kItemRing; ++r) {
+        const int ii = base + r;
+        if (ii < cnt) {
+          __syncthreads();  // tile ii staged; the other buffer is free
+          const uint8_t* buf = lds + (g & 1) * kItemBuf;
+          TileRegs<false> t;
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            t.k[m] = *reinterpret_cast<const u32x4*>(buf + (m >> 1) * 2048 + 32 * lane +
+                                                     16 * (m & 1));
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            t.v[q] = *reinterpret_cast<const u32x4*>(buf + (2 + (q >> 1)) * 2048 + 32 * lane +
+                                                     16 * (q & 1));
+          // prefix tokens are all valid: L is the prefix length
+          process_tile<false, true, true>(t, qop, st, 0, qg, kBS, a.qk_scale);
+          ++g;
+          if (ii + 1 < cnt) {
+            const int kNext = (r + 1) % kItemRing;  // static once unrolled
+            item_stage(lds + (g & 1) * kItemBuf, raw[kNext], w, lane);
+            if (ii + 1 + kItemRing < cnt)
+              raw[kNext] = item_quarter(a, __builtin_amdgcn_readlane(tbl, ii + 1 + kItemRing),
+                                        kvh, w, lane);
+          }
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+  // the members' partials, straight from registers
+  float l_run = st.l;
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (member >= 0) {
+    const int64_t prow = part_row(a, member, kvh, pidx, j % a.g);
+    float* dst = a.ws_o + prow * kD + qg * 4;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4*>(dst + n * 16) = st.acc[n];
+    if (qg == 0) {
+      a.ws_ml[prow * 2] = st.m_ref;
+      a.ws_ml[prow * 2 + 1] = l_run;
+    }
+  }
+}
+
+// One unit of the decode partition kernel: partition p of KV head kvh of
+// z-slice b, kNW waves.  The unit covers tokens [p*P, min(L, (p+1)*P)) of
+// sequence b for the G query heads of KV head kvh.  Wave w takes the
+// partition's blocks w, w + kNW, ...  Lane (j = lane % 16, qg = lane / 16)
+// serves query head kvh*G + j and, in each tile, tokens 4qg .. 4qg+3.  Each
+// wave keeps kPD tiles in flight while it computes on another.
+// kAppend: the unit also writes the sequence's newest token (steps 1-3
+// above).  kCasc: the cascade over shared prefixes -- z-slices below
+// casc_items are prefix items, the rest sequences, through seq_order unless
+// `ordered` says b - casc_items is the sequence itself.  Every return below
+// is uniform over the workgroup.
+template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn, bool kAppend,
+          bool kCasc>
+__device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem, int p, int kvh,
+                                               int b, bool ordered) {
   // [kNW][CS][D] outputs, then [kNW][16] max and sum, then (kAppend) the
   // newest token's kept bytes, then (kCasc) the item's member per column
-  extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int j = lane & 15;
   const int qg = lane >> 4;
-  const int p = blockIdx.x, kvh = blockIdx.y;
   const int G = a.g;
   const int CS = kCasc ? kMaxG : G;  // LDS merge: columns per wave
   int* memb = reinterpret_cast<int*>(smem + kNW * CS * kD + 2 * kNW * 16 + kKeepBytes / 4);
 
-  int b = blockIdx.z;  // the sequence (a prefix item: its group's first member)
   int L, n_p, pidx, blk0, nblk, ncol = G, shared_blocks;
   bool item = false;
+  int item_member = -1;  // a prefix item: the member of this lane's column
+  // prefix items whose waves share the tiles (item_shared)
+  constexpr bool kSharedItem = kCasc && kFP8 && !kDyn && kNW == kItemWaves;
   int qrow = -1;       // this lane's query row [B*Hq], -1 = column unused
   if constexpr (kCasc) {
     if (b < a.casc_items) {
@@ -443,17 +610,18 @@ decode_partition_kernel(DecodeArgs a) {
       nblk = min(S, blk0 + ps.per) - blk0;
       ncol = a.casc_m * G;
       shared_blocks = S;  // every item of the group reads these tiles
-      const int slot = ch * a.casc_m + j / G;
+      const int slot = ch * a.casc_mi + (kSharedItem ? w * a.casc_m : 0) + j / G;
       int m = -1;
       if (j < ncol && slot < a.casc_cap) {
         m = grp[slot];
         if ((unsigned)m >= (unsigned)a.nseq || casc_blocks(a, m, clamp_len(a, m)) != S) m = -1;
       }
       if (m >= 0) qrow = m * a.hq + kvh * G + (j - (j / G) * G);
+      item_member = m;
       if (w == 0 && qg == 0) memb[j] = m;
     } else {
       b -= a.casc_items;
-      if (a.seq_order != nullptr) {  // tails in the caller's order (longest first)
+      if (a.seq_order != nullptr && !ordered) {  // tails in the caller's order (longest first)
         b = a.seq_order[b];
         if ((unsigned)b >= (unsigned)a.nseq) return;
       }
@@ -501,6 +669,14 @@ decode_partition_kernel(DecodeArgs a) {
   st.vref = 0.0f;
 #pragma unroll
   for (int n = 0; n < 8; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (kSharedItem) {
+    if (item) {  // workgroup-uniform
+      item_shared(a, qop, st, a.block_tables + (int64_t)b * a.max_blocks + blk0, kvh, nblk,
+                  pidx, item_member, lane, w, reinterpret_cast<uint8_t*>(smem));
+      return;
+    }
+  }
 
   const int my_n = w < nblk ? (nblk - w + kNW - 1) / kNW : 0;
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk0 + w;
@@ -652,6 +828,60 @@ decode_partition_kernel(DecodeArgs a) {
       }
     }
   }
+}
+
+// With per-block scales the kernel is held to 128 VGPRs (4 waves per SIMD);
+// the compiler fits it without spilling.  The FP8 cascade variants are held
+// to 168 (3 waves per SIMD): the loop over units of the flat grid otherwise
+// grows them past it.
+// Decode partition kernel: one unit per workgroup, grid (n_p_max, Hkv, B) or
+// (n_p_max, Hkv, items + B) for the cascade; or, with the cascade's flat
+// grid, Hkv * n workgroups, KV head fastest: workgroup i takes unit i / Hkv
+// and then every n-th unit after it until none is left, so the grid may hold
+// exactly the units there are (the host's count) or any other number.
+template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false,
+          bool kAppend = false, bool kCasc = false>
+__global__ void __launch_bounds__(kNW * kWave)
+__attribute__((amdgpu_waves_per_eu(kDyn ? (kCasc ? 3 : 4) : (kCasc && kFP8 ? 3 : 1))))
+decode_partition_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  if constexpr (kCasc) {
+    if (a.casc_flat) {
+      const int lane = threadIdx.x & 63;
+      const int n_wg = gridDim.x / a.hkv;
+      const int kvh = blockIdx.x % a.hkv;
+      const int iu = a.casc_items * a.casc_pp;
+      int tails = -1;  // tail units, once a scan has counted them
+      for (int u = blockIdx.x / a.hkv;; u += n_wg) {
+        int b, p;
+        bool ordered = false;
+        if (u < iu) {
+          b = u / a.casc_pp;
+          p = u - b * a.casc_pp;
+        } else {
+          if (tails >= 0 && u - iu >= tails) break;  // past the last unit (uniform)
+          int2 unit = casc_tail_unit(a, u - iu, lane, &tails);
+          // the scan's results are the same on every lane: say so, so that
+          // everything derived from them stays in scalar registers
+          unit.x = __builtin_amdgcn_readfirstlane(unit.x);
+          unit.y = __builtin_amdgcn_readfirstlane(unit.y);
+          tails = __builtin_amdgcn_readfirstlane(tails);
+          if (unit.x < 0) break;
+          b = a.casc_items + unit.x;
+          p = unit.y;
+          ordered = true;
+        }
+        partition_unit<kFP8, kHwCvt, kSplitP, kPD, kNW, kDyn, kAppend, kCasc>(a, smem, p, kvh,
+                                                                              b, ordered);
+        // a launch that holds every unit needs no second pass
+        if (tails >= 0 && u + n_wg - iu >= tails) break;
+        __syncthreads();  // the next unit reuses the LDS
+      }
+      return;
+    }
+  }
+  partition_unit<kFP8, kHwCvt, kSplitP, kPD, kNW, kDyn, kAppend, kCasc>(
+      a, smem, blockIdx.x, blockIdx.y, blockIdx.z, false);
 }
 
 // Short partitions (an explicit split-KV length of a few hundred tokens):
@@ -807,111 +1037,166 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
 // Merge kernel: for each (sequence, query head) whose sequence spans n_p > 1
 // partitions, M = max_p m_p and
 //   out = out_scale * sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
-// kSplit = false: each of the 4 waves of a workgroup merges its own (b, h);
-// kSplit = true: the 4 waves share one (b, h), wave w taking partitions
-// w, w + 4, ..., and combine through LDS (for many partitions).
-// Lane i owns channels 2i, 2i+1; partition weights live one per lane and are
-// broadcast with readlane.  The summation order is fixed, so results do not
-// depend on timing.
-constexpr int kFewPartitions = 8;
+// Half a wave (32 lanes x 16 bytes) reads one partition's 128-float output
+// row, so one wave instruction covers two partitions.  Every load is issued
+// at once -- the rows of all n_p_max partitions the workspace holds, with the
+// sequence's length -- and rows past the sequence's own n_p are dropped by
+// selection afterwards (never multiplied: a stale row may hold anything), so
+// a merge costs one round trip to memory.
+//   kMany = false: one wave per (b, h); its two halves take the even and the
+//     odd partitions, n_p_max <= kFewPartitions.
+//   kMany = true: four waves per (b, h); half-wave hw (0..7) takes
+//     partitions hw, hw + 8, ... (up to kManyPartitions), the maximum and the
+//     partition weights go through LDS, and the eight half-sums combine
+//     through LDS.
+// The summation order is fixed, so results do not depend on timing.
+constexpr int kFewPartitions = 16;
+constexpr int kManyPartitions = 8 * 32;  // 32 rows per lane of the kMany kernel
 
-template <bool kSplit>
+template <bool kMany>
 __global__ void __launch_bounds__(kRW * kWave) decode_reduce_kernel(DecodeArgs a, int64_t rows) {
-  __shared__ float2 part[kRW][kWave];
-  __shared__ float dens[kRW];
+  __shared__ float wgt_s[kMany ? kManyPartitions : 1];  // partition weights (kMany)
+  __shared__ f32x4 half_s[kMany ? 2 * kRW : 1][32];      // half-wave sums (kMany)
+  __shared__ float red_s[kMany ? kRW : 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t bh = kSplit ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kRW + w;
-  if (bh >= rows) return;                    // only when !kSplit: whole waves leave
+  const int half = lane >> 5, c4 = lane & 31;        // channels 4 c4 .. 4 c4 + 3
+  const int64_t bh = kMany ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kRW + w;
+  if (bh >= rows) return;                    // only when !kMany: whole waves leave
   const int b = (int)(bh / a.hq);
-  const int n_p = seq_parts(a, b, clamp_len(a, b));
-  if (n_p <= 1) return;                      // written by the partition kernel
   const int h = (int)(bh - (int64_t)b * a.hq);
   const int64_t row0 = part_row(a, b, h / a.g, 0, h % a.g);
   const int64_t pst = a.g;                   // rows from one partition to the next
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+  const f32x4* orow = reinterpret_cast<const f32x4*>(a.ws_o + row0 * kD) + c4;
+  const int64_t ost = pst * (kD / 4);        // f32x4 steps from one partition to the next
+  const int npm = a.n_p_max;               // >= 2: the merge runs only then
 
-  if (!kSplit && n_p <= kFewPartitions) {
-    // few partitions: issue every load before the max reduction
-    const float2 mine = lane < n_p ? ml[row0 + lane * pst] : make_float2(-INFINITY, 0.0f);
-    const float2* orow = reinterpret_cast<const float2*>(a.ws_o + row0 * kD) + lane;
-    float2 o[kFewPartitions];
+  if constexpr (!kMany) {
+    // the first two partitions' rows (every merged row has them) with the
+    // ml pairs and the length; the others once the length says they exist
+    const float2 mine = lane < npm ? ml[row0 + lane * pst] : make_float2(-INFINITY, 0.0f);
+    f32x4 o[kFewPartitions / 2];
+    o[0] = orow[half * ost];
+    const int n_p = seq_parts(a, b, clamp_len(a, b));
+    if (n_p <= 1) return;                    // written by the partition kernel
 #pragma unroll
-    for (int k = 0; k < kFewPartitions; ++k)
-      o[k] = k < n_p ? orow[k * pst * (kD / 2)] : make_float2(0.f, 0.f);
-    const float mx = wave_max(mine.x);
-    const float wgt = lane < n_p ? __builtin_amdgcn_exp2f(mine.x - mx) : 0.0f;
-    const float den = wave_sum(mine.y * wgt);
-    float2 acc = make_float2(0.f, 0.f);
-#pragma unroll
-    for (int k = 0; k < kFewPartitions; ++k) {
-      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
-      acc.x += o[k].x * g;
-      acc.y += o[k].y * g;
+    for (int k = 1; k < kFewPartitions / 2; ++k) {
+      const int pp = 2 * k + half;
+      o[k] = pp < n_p ? orow[pp * ost] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float scale = a.out_scale / den;
-    reinterpret_cast<float2*>(a.out + bh * kD)[lane] = make_float2(acc.x * scale, acc.y * scale);
+    const bool valid = lane < n_p;
+    const float mx = wave_max(valid ? mine.x : -INFINITY);
+    const float wgt = valid ? __builtin_amdgcn_exp2f(mine.x - mx) : 0.0f;
+    const float den = wave_sum(valid ? mine.y * wgt : 0.0f);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kFewPartitions / 2; ++k) {
+      const int pp = 2 * k + half;
+      // weight of partition 2k (lower half) or 2k + 1 (upper half)
+      const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), 2 * k));
+      const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), 2 * k + 1));
+      if (pp < n_p) acc += o[k] * (half ? g1 : g0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32, kWave);
+    if (half == 0)
+      reinterpret_cast<f32x4*>(a.out + bh * kD)[c4] = acc * (a.out_scale / den);
     return;
+  } else {
+    const int tid = threadIdx.x;
+    const int hw = w * 2 + half;             // half-wave 0..7
+    constexpr int kPer = kManyPartitions / 8;
+    // every row at once: thread tid's ml pair, this half-wave's output rows
+    const float2 mine = tid < npm ? ml[row0 + tid * pst] : make_float2(-INFINITY, 0.0f);
+    f32x4 o[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pp = hw + 8 * u;
+      o[u] = pp < npm ? orow[(int64_t)pp * ost] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int n_p = seq_parts(a, b, clamp_len(a, b));
+    if (n_p <= 1) return;                    // written by the partition kernel (uniform)
+    const bool valid = tid < n_p;
+    float mx = wave_max(valid ? mine.x : -INFINITY);
+    if (lane == 0) red_s[w] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+    const float g = valid ? __builtin_amdgcn_exp2f(mine.x - mx) : 0.0f;
+    wgt_s[tid] = g;
+    const float den_part = wave_sum(valid ? mine.y * g : 0.0f);
+    __syncthreads();                         // weights in LDS; red_s read by all
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pp = hw + 8 * u;
+      if (pp < n_p) acc += o[u] * wgt_s[pp];
+    }
+    half_s[hw][c4] = acc;
+    if (lane == 0) red_s[w] = den_part;
+    __syncthreads();
+    if (w == 0 && half == 0) {
+      f32x4 t = half_s[0][c4];
+#pragma unroll
+      for (int k = 1; k < 2 * kRW; ++k) t += half_s[k][c4];
+      const float dd = (red_s[0] + red_s[1]) + (red_s[2] + red_s[3]);
+      reinterpret_cast<f32x4*>(a.out + bh * kD)[c4] = t * (a.out_scale / dd);
+    }
   }
+}
 
+// Merge of sequences with more partitions than one launch of the kMany
+// kernel takes (n_p_max > kManyPartitions): one workgroup of four waves per
+// (b, h), chunks of kManyPartitions partitions, the same arithmetic in the
+// same fixed order.
+__global__ void __launch_bounds__(kRW * kWave) decode_reduce_long_kernel(DecodeArgs a,
+                                                                          int64_t rows) {
+  __shared__ float wgt_s[kManyPartitions];
+  __shared__ f32x4 half_s[2 * kRW][32];
+  __shared__ float red_s[kRW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+  const int half = lane >> 5, c4 = lane & 31, hw = w * 2 + half;
+  const int64_t bh = blockIdx.x;
+  if (bh >= rows) return;
+  const int b = (int)(bh / a.hq);
+  const int n_p = seq_parts(a, b, clamp_len(a, b));
+  if (n_p <= 1) return;
+  const int h = (int)(bh - (int64_t)b * a.hq);
+  const int64_t row0 = part_row(a, b, h / a.g, 0, h % a.g);
+  const int64_t pst = a.g;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+  const f32x4* orow = reinterpret_cast<const f32x4*>(a.ws_o + row0 * kD) + c4;
+  const int64_t ost = pst * (kD / 4);
   float mx = -INFINITY;
-  for (int pp = lane; pp < n_p; pp += kWave) mx = fmaxf(mx, ml[row0 + pp * pst].x);
+  for (int pp = tid; pp < n_p; pp += kRW * kWave) mx = fmaxf(mx, ml[row0 + pp * pst].x);
   mx = wave_max(mx);
-
-  const int p0 = kSplit ? w : 0, ps = kSplit ? kRW : 1;
-  float2 acc = make_float2(0.f, 0.f);
+  if (lane == 0) red_s[w] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+  __syncthreads();
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float den = 0.0f;
-  for (int c = p0; c < n_p; c += kWave * ps) {
-    const int mine = c + lane * ps;          // this lane's partition of the chunk
-    float wgt = 0.0f;
-    if (mine < n_p) {
-      const float2 v = ml[row0 + mine * pst];
-      wgt = __builtin_amdgcn_exp2f(v.x - mx);
-      den += v.y * wgt;
+  for (int c = 0; c < n_p; c += kManyPartitions) {
+    const int cn = min(kManyPartitions, n_p - c);
+    for (int pp = tid; pp < cn; pp += kRW * kWave) {
+      const float2 v = ml[row0 + (int64_t)(c + pp) * pst];
+      const float g = __builtin_amdgcn_exp2f(v.x - mx);
+      wgt_s[pp] = g;
+      den += v.y * g;
     }
-    const int cnt = min(kWave, (n_p - c + ps - 1) / ps);
-    const float2* orow = reinterpret_cast<const float2*>(a.ws_o + (row0 + c * pst) * kD) + lane;
-    const int64_t ost = ps * pst * (kD / 2);  // float2 steps between this wave's partitions
-    // kBatch partial rows in flight per wave; summed in partition order
-    constexpr int kBatch = 16;
-    int k = 0;
-    for (; k + kBatch <= cnt; k += kBatch) {
-      float2 o[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) o[u] = orow[(int64_t)(k + u) * ost];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k + u));
-        acc.x += o[u].x * g;
-        acc.y += o[u].y * g;
-      }
-    }
-    for (; k < cnt; ++k) {
-      const float2 o = orow[(int64_t)k * ost];
-      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
-      acc.x += o.x * g; acc.y += o.y * g;
-    }
+    __syncthreads();
+    for (int pp = hw; pp < cn; pp += 8) acc += orow[(int64_t)(c + pp) * ost] * wgt_s[pp];
+    __syncthreads();
   }
   den = wave_sum(den);
-  float2* dst = reinterpret_cast<float2*>(a.out + bh * kD) + lane;
-  if constexpr (!kSplit) {
-    const float scale = a.out_scale / den;
-    *dst = make_float2(acc.x * scale, acc.y * scale);
-  } else {
-    part[w][lane] = acc;
-    if (lane == 0) dens[w] = den;
-    __syncthreads();
-    if (w == 0) {
-      float2 t = part[0][lane];
-      float dd = dens[0];
+  half_s[hw][c4] = acc;
+  if (lane == 0) red_s[w] = den;
+  __syncthreads();
+  if (w == 0 && half == 0) {
+    f32x4 t = half_s[0][c4];
 #pragma unroll
-      for (int ww = 1; ww < kRW; ++ww) {
-        t.x += part[ww][lane].x;
-        t.y += part[ww][lane].y;
-        dd += dens[ww];
-      }
-      const float scale = a.out_scale / dd;
-      *dst = make_float2(t.x * scale, t.y * scale);
-    }
+    for (int k = 1; k < 2 * kRW; ++k) t += half_s[k][c4];
+    const float dd = (red_s[0] + red_s[1]) + (red_s[2] + red_s[3]);
+    reinterpret_cast<f32x4*>(a.out + bh * kD)[c4] = t * (a.out_scale / dd);
   }
 }
 
@@ -965,6 +1250,7 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32
 struct CascLayout {
   WsLayout ws;
   int32_t s_max, x_dim;
+  int32_t n_pp, n_pt;  // most prefix partitions, most tail partitions
 };
 
 CascLayout casc_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, int32_t part,
@@ -978,6 +1264,8 @@ CascLayout casc_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, i
   const int64_t n_pp = (c.s_max + pb - 1) / pb;
   const int64_t n_pt = nblk == 0 ? 1 : (nblk + pb - 1) / pb;
   c.x_dim = (int32_t)std::max(n_pp, n_pt);
+  c.n_pp = (int32_t)n_pp;
+  c.n_pt = (int32_t)n_pt;
   c.ws.n_p_max = (int32_t)(n_pp + n_pt);
   if (c.ws.n_p_max <= 1) return c;
   const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)c.ws.n_p_max;
@@ -1113,9 +1401,11 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   a.k_wr = a.v_wr = nullptr;
   a.casc_prefix = nullptr;
   a.casc_groups = nullptr;
-  a.casc_items = a.casc_chunks = a.casc_cap = a.casc_m = a.casc_max = 0;
+  a.casc_items = a.casc_chunks = a.casc_cap = a.casc_m = a.casc_mi = a.casc_max = 0;
   a.seq_order = nullptr;
   a.nseq = num_seqs;
+  a.casc_flat = 0;
+  a.casc_pp = 1;
   a.k_enc_scale = k_scale;
   a.v_enc_scale = v_scale;
   // FP8 tiles decoded by bit operations hold code / 256: fold the 256 back
@@ -1370,7 +1660,9 @@ static pkv_status run_reduce(const DecodePlan& pl, int32_t num_seqs, hipStream_t
   if (num_seqs == 0 || !pl.need_reduce) return PKV_OK;
   (void)hipGetLastError();
   const int64_t rows = (int64_t)num_seqs * pl.a.hq;
-  if (pl.a.n_p_max > 32) {
+  if (pl.a.n_p_max > kManyPartitions) {
+    decode_reduce_long_kernel<<<dim3((unsigned)rows), dim3(kRW * kWave), 0, s>>>(pl.a, rows);
+  } else if (pl.a.n_p_max > kFewPartitions) {
     decode_reduce_kernel<true><<<dim3((unsigned)rows), dim3(kRW * kWave), 0, s>>>(pl.a, rows);
   } else {
     const int64_t grid = (rows + kRW - 1) / kRW;
@@ -1503,13 +1795,18 @@ extern "C" uint64_t pkv_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t
   return casc_layout(num_seqs, num_q_heads, max_context_len, part, max_prefix_blocks).ws.total;
 }
 
+// Largest batch for the flat cascade grid: each workgroup scans the batch
+// (four sequences per lane per pass) to find its unit.
+constexpr int32_t kFlatCascadeSeqs = 2048;
+
 // The cascade after plan_decode: its workspace layout, the prefix items,
 // the partition kernel (per-tensor scales: with or without the newest
 // token's write; per-block scales: decode only), then the merge.
 static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
                               const int32_t* prefix_groups, int32_t num_groups,
                               int32_t group_cap, int32_t max_prefix_blocks,
-                              const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
+                              const int32_t* seq_order, int32_t tail_units,
+                              int32_t num_seqs, int32_t num_q_heads,
                               int32_t max_context_len, void* workspace,
                               uint64_t workspace_bytes, hipStream_t s) {
   DecodeArgs& a = pl.a;
@@ -1528,9 +1825,23 @@ static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
   a.seq_order = seq_order;
   pl.need_reduce = cl.ws.n_p_max > 1;
   const int members = kMaxG / a.g;  // MFMA columns of one wave, G per member
-  const int64_t chunks = num_groups > 0 ? (group_cap + members - 1) / members : 0;
+  // waves per workgroup as for the plain kernel, within 64 KiB of LDS at 16
+  // columns per wave
+  int nw = waves_for(pl);
+  while (nw > 1 && partition_lds(nw, kMaxG, append, true) > 65536) nw /= 2;
+  // FP8 per-tensor items with four waves share their tiles: each wave takes
+  // its own members
+  const bool shared_items = pl.fp8 && !pl.dyn && nw == kItemWaves;
+  const int per_item = shared_items ? nw * members : members;
+  const int64_t chunks = num_groups > 0 ? (group_cap + per_item - 1) / per_item : 0;
   const int64_t items = (int64_t)num_groups * chunks;
   if (items + num_seqs > 65535) return PKV_ERR_INVALID_ARG;  // grid z
+  // the cascade always runs the hardware FP8 conversion: no factor 256 in
+  // the scales whatever the A/B switch chose for the plain kernels
+  if (pl.fp8 && !pl.dyn && !pl.cfg.hw_cvt) {
+    a.qk_scale *= 1.0f / 256.0f;
+    a.out_scale *= 1.0f / 256.0f;
+  }
   if (num_groups > 0 && cl.s_max > 0) {
     a.casc_prefix = prefix_blocks;
     a.casc_groups = prefix_groups;
@@ -1538,13 +1849,24 @@ static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
     a.casc_chunks = (int32_t)chunks;
     a.casc_cap = group_cap;
     a.casc_m = members;
+    a.casc_mi = per_item;
     a.casc_max = cl.s_max;
   }
-  // waves per workgroup as for the plain kernel, within 64 KiB of LDS at 16
-  // columns per wave
-  int nw = waves_for(pl);
-  while (nw > 1 && partition_lds(nw, kMaxG, append, true) > 65536) nw /= 2;
-  const dim3 grid((unsigned)cl.x_dim, (unsigned)a.hkv, (unsigned)(a.casc_items + num_seqs));
+  // Batches of up to kFlatCascadeSeqs sequences: a flat grid, KV head
+  // fastest, that holds the prefix items and then the tail partitions in the
+  // given order with no gaps: as many as the caller counted (tail_units), or
+  // else an upper bound from max_context_len, past which the workgroups find
+  // nothing and leave.  Larger batches: (partition, KV head, item or
+  // sequence).
+  dim3 grid((unsigned)cl.x_dim, (unsigned)a.hkv, (unsigned)(a.casc_items + num_seqs));
+  const int64_t units =
+      (int64_t)a.casc_items * std::max(1, cl.n_pp) +
+      (tail_units > 0 ? (int64_t)tail_units : (int64_t)num_seqs * std::max(1, cl.n_pt));
+  if (num_seqs <= kFlatCascadeSeqs && units * a.hkv < (1ll << 24)) {
+    a.casc_flat = 1;
+    a.casc_pp = std::max(1, cl.n_pp);
+    grid = dim3((unsigned)(units * a.hkv));
+  }
   (void)hipGetLastError();
   if (pl.dyn)
     launch_partition_casc_dyn(nw, grid, s, a);
@@ -1560,8 +1882,9 @@ static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
 }
 
 static pkv_status check_groups(int32_t num_groups, int32_t group_cap, int32_t max_prefix_blocks,
-                               const int32_t* prefix_groups, const int32_t* prefix_blocks) {
-  if (num_groups < 0 || max_prefix_blocks < 0) return PKV_ERR_INVALID_ARG;
+                               const int32_t* prefix_groups, const int32_t* prefix_blocks,
+                               int32_t tail_units) {
+  if (num_groups < 0 || max_prefix_blocks < 0 || tail_units < 0) return PKV_ERR_INVALID_ARG;
   if (num_groups > 0 && (group_cap <= 0 || !prefix_groups || !prefix_blocks))
     return PKV_ERR_INVALID_ARG;
   return PKV_OK;
@@ -1572,13 +1895,14 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade(
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
     const int32_t* shared_prefix_blocks, const int32_t* prefix_blocks,
     const int32_t* prefix_groups, int32_t num_groups, int32_t group_cap,
-    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
-    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
-    float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-    void* stream) {
+    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units, int32_t num_seqs,
+    int32_t num_q_heads, int32_t max_context_len, const pkv_cache_layout* layout,
+    float sm_scale, float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    uint64_t workspace_bytes, void* stream) {
   if ((key == nullptr) != (value == nullptr)) return PKV_ERR_INVALID_ARG;
   pkv_status st =
-      check_groups(num_groups, group_cap, max_prefix_blocks, prefix_groups, prefix_blocks);
+      check_groups(num_groups, group_cap, max_prefix_blocks, prefix_groups, prefix_blocks,
+                   tail_units);
   if (st != PKV_OK) return st;
   DecodePlan pl;
   // the plain plan's workspace is never larger than the cascade's
@@ -1594,7 +1918,8 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade(
     if (st != PKV_OK) return st;
   }
   return run_cascade(pl, prefix_blocks, prefix_groups, num_groups, group_cap,
-                     max_prefix_blocks, seq_order, num_seqs, num_q_heads, max_context_len,
+                     max_prefix_blocks, seq_order, tail_units, num_seqs, num_q_heads,
+                     max_context_len,
                      workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -1603,13 +1928,14 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade_dynamic(
     const float* k_block_scales, const float* v_block_scales, const int32_t* block_tables,
     int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* shared_prefix_blocks,
     const int32_t* prefix_blocks, const int32_t* prefix_groups, int32_t num_groups,
-    int32_t group_cap, int32_t max_prefix_blocks, const int32_t* seq_order, int32_t num_seqs,
-    int32_t num_q_heads, int32_t max_context_len, const pkv_cache_layout* layout,
-    float sm_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-    void* stream) {
+    int32_t group_cap, int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units,
+    int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const pkv_cache_layout* layout, float sm_scale, int32_t partition_size, void* workspace,
+    uint64_t workspace_bytes, void* stream) {
   if (!k_block_scales || !v_block_scales) return PKV_ERR_INVALID_ARG;
   pkv_status st =
-      check_groups(num_groups, group_cap, max_prefix_blocks, prefix_groups, prefix_blocks);
+      check_groups(num_groups, group_cap, max_prefix_blocks, prefix_groups, prefix_blocks,
+                   tail_units);
   if (st != PKV_OK) return st;
   DecodePlan pl;
   st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
@@ -1620,7 +1946,8 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade_dynamic(
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
   return run_cascade(pl, prefix_blocks, prefix_groups, num_groups, group_cap,
-                     max_prefix_blocks, seq_order, num_seqs, num_q_heads, max_context_len,
+                     max_prefix_blocks, seq_order, tail_units, num_seqs, num_q_heads,
+                     max_context_len,
                      workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 

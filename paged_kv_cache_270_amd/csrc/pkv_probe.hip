@@ -10,12 +10,13 @@
 //   * pkv_tile_gather_probe: the decode kernel's own reads -- every K and V
 //     tile of every sequence, gathered through the block table with the same
 //     16-byte lane loads and cache policy, one workgroup of four waves per
-//     (sequence, KV head), two tiles in flight per wave.
+//     256 blocks of a (sequence, KV head), two tiles in flight per wave.
 // Both fold what they read into one word per lane and store it only when it
 // equals a value the host passes and the data never produces in practice,
 // so the loads cannot be dropped and nothing measurable is written.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "pkv.h"
@@ -29,21 +30,28 @@ using namespace pkv_check;
 
 constexpr int kProbeThreads = 256;
 constexpr int kProbeUnroll = 8;   // 16-byte loads in flight per lane
+constexpr uint64_t kStepVecs = (uint64_t)kProbeThreads * kProbeUnroll;  // 32 KiB per step
 
+// Workgroup i streams its own contiguous slab of the buffer in steps of
+// 32 KiB: each wave instruction covers 1 KiB of consecutive bytes, and a lane
+// keeps eight 16-byte loads in flight.
 __global__ void __launch_bounds__(kProbeThreads)
-stream_read_kernel(const u32x4* __restrict__ buf, uint64_t n_vec, uint32_t* sink, uint32_t key) {
-  const uint64_t stride = (uint64_t)gridDim.x * kProbeThreads;
-  uint64_t i = (uint64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+stream_read_kernel(const u32x4* __restrict__ buf, uint64_t n_vec, uint64_t slab_vecs,
+                   uint32_t* sink, uint32_t key) {
+  const uint64_t begin = (uint64_t)blockIdx.x * slab_vecs;
+  const uint64_t end = begin + slab_vecs < n_vec ? begin + slab_vecs : n_vec;
   uint32_t acc = 0;
-  for (; i + (kProbeUnroll - 1) * stride < n_vec; i += kProbeUnroll * stride) {
+  uint64_t i = begin;
+  for (; i + kStepVecs <= end; i += kStepVecs) {
     u32x4 v[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+    for (int u = 0; u < kProbeUnroll; ++u)
+      v[u] = __builtin_nontemporal_load(buf + i + u * kProbeThreads + threadIdx.x);
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n_vec; i += stride) {
-    const u32x4 v = __builtin_nontemporal_load(buf + i);
+  for (uint64_t j = i + threadIdx.x; j < end; j += kProbeThreads) {
+    const u32x4 v = __builtin_nontemporal_load(buf + j);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == key) sink[0] = acc;
@@ -59,17 +67,22 @@ struct GatherArgs {
   uint32_t key;
 };
 
+// Workgroup (c, kvh, b) reads blocks [256c, 256c + 256) of sequence b for KV
+// head kvh; wave w takes blocks w, w + 4, ... of them.
+constexpr int kGatherBlocks = 256;
+
 template <bool kFP8>
 __global__ void __launch_bounds__(4 * kWave) tile_gather_kernel(GatherArgs a) {
   constexpr int kPD = 2;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int kvh = blockIdx.y, b = blockIdx.z;
   int L = a.context_lens[b];
   const int cap = min(a.max_ctx, a.max_blocks * kBS);
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int nblk = (L + kBS - 1) / kBS;
+  const int blk0 = blockIdx.x * kGatherBlocks;
+  const int nblk = min((L + kBS - 1) / kBS - blk0, kGatherBlocks);
   const int my_n = w < nblk ? (nblk - w + 3) / 4 : 0;
-  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + w;
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk0 + w;
   uint32_t acc = 0;
   for (int c0 = 0; c0 < my_n; c0 += kWave) {
     const int cnt = min(kWave, my_n - c0);
@@ -100,19 +113,21 @@ __global__ void __launch_bounds__(4 * kWave) tile_gather_kernel(GatherArgs a) {
 
 }  // namespace
 
-extern "C" pkv_status pkv_hbm_read_probe(const void* buf, uint64_t bytes, uint32_t* sink,
-                                         uint32_t key, void* stream) {
+extern "C" pkv_status pkv_hbm_read_probe(const void* buf, uint64_t bytes, int32_t workgroups,
+                                         uint32_t* sink, uint32_t key, void* stream) {
   if (bytes == 0) return PKV_OK;
-  if (!buf || !sink || !aligned(buf, 16) || bytes % 16 != 0) return PKV_ERR_INVALID_ARG;
+  if (!buf || !sink || !aligned(buf, 16) || bytes % 16 != 0 || workgroups < 0)
+    return PKV_ERR_INVALID_ARG;
   const uint64_t n_vec = bytes / 16;
-  // eight workgroups per CU of the 256 on MI355X; each lane keeps eight
-  // 16-byte loads in flight
-  const uint64_t want = (n_vec + (uint64_t)kProbeThreads * kProbeUnroll - 1) /
-                        ((uint64_t)kProbeThreads * kProbeUnroll);
-  const unsigned grid = (unsigned)(want < 2048 ? (want == 0 ? 1 : want) : 2048);
+  // slabs of whole 32 KiB steps, one per workgroup
+  const uint64_t steps = (n_vec + kStepVecs - 1) / kStepVecs;
+  uint64_t wg = workgroups > 0 ? (uint64_t)workgroups : 2048;
+  if (wg > steps) wg = steps;
+  const uint64_t slab = (steps + wg - 1) / wg * kStepVecs;
+  wg = (n_vec + slab - 1) / slab;
   (void)hipGetLastError();
-  stream_read_kernel<<<grid, kProbeThreads, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const u32x4*>(buf), n_vec, sink, key);
+  stream_read_kernel<<<(unsigned)wg, kProbeThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4*>(buf), n_vec, slab, sink, key);
   return launch_status();
 }
 
@@ -141,7 +156,9 @@ extern "C" pkv_status pkv_tile_gather_probe(const void* k_pool, const void* v_po
   a.max_ctx = max_context_len;
   a.sink = sink;
   a.key = key;
-  const dim3 grid((unsigned)a.hkv, (unsigned)num_seqs);
+  const int64_t max_nblk = ((int64_t)max_context_len + kBS - 1) / kBS;
+  const int64_t chunks = std::max<int64_t>(1, (max_nblk + kGatherBlocks - 1) / kGatherBlocks);
+  const dim3 grid((unsigned)chunks, (unsigned)a.hkv, (unsigned)num_seqs);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (layout->dtype == PKV_FP8_E4M3FN)

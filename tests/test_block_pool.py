@@ -303,3 +303,33 @@ def test_append_each_stops_at_the_first_failure():
                                pairs.ctypes.data, ctypes.byref(nc), ctypes.byref(nd))
     assert st == pkv.PKV_ERR_NO_FREE_BLOCKS and nd.value == 1 and nc.value == 0
     assert pool.seq_len(a) == 17 and pool.seq_len(b) == 16
+
+
+def test_cascade_tail_units_counts_each_tails_partitions():
+    """Hand-worked: a 40-token prompt forked twice; the two full blocks are the
+    group's prefix (the partly filled third is copied on each member's first
+    append).  At 32-token partitions (2 blocks) the tails of 140, 70 and 41
+    tokens take ceil(7/2) = 4, ceil(3/2) = 2 and 1 units; an empty sequence
+    still takes one (it writes zeros); a prefix past max_prefix_blocks is not
+    used, so that sequence's whole length counts."""
+    pool = pkv.BlockPool(64)
+    root = pool.create()
+    pool.append(root, 40)
+    a, b = pool.fork(root), pool.fork(root)
+    pool.append(root, 100)
+    pool.append(a, 30)
+    pool.append(b, 1)
+    empty = pool.create()
+    seqs = [root, a, b, empty]
+    prefix, groups, max_pre = pool.prefix_groups(seqs, 8)
+    assert list(prefix) == [2, 2, 2, 0] and max_pre == 2
+    assert pool.cascade_tail_units(seqs, prefix, max_pre, 32) == 4 + 2 + 1 + 1
+    # one partition per tail at 4096 tokens
+    assert pool.cascade_tail_units(seqs, prefix, max_pre, 4096) == 4
+    # prefixes longer than max_prefix_blocks are not cascaded: 9, 5 and 3
+    # blocks at 2 per partition
+    assert pool.cascade_tail_units(seqs, prefix, 1, 32) == 5 + 3 + 2 + 1
+    with pytest.raises(pkv.PkvError):
+        pool.cascade_tail_units(seqs, prefix, max_pre, 24)
+    with pytest.raises(pkv.PkvError):
+        pool.cascade_tail_units([root, 12345], [0, 0], max_pre, 32)

@@ -76,7 +76,7 @@ def _group_array(groups, cap):
     return np.asarray(out, dtype=np.int32).reshape(-1, cap)
 
 
-def _cascade(prep, groups, prefix, cap, ps, write, name, order=None):
+def _cascade(prep, groups, prefix, cap, ps, write, name, order=None, tail_units=0):
     wl = prep.wl
     B, Hkv, fp8 = wl.num_seqs, wl.num_kv_heads, wl.fp8
     garr = _group_array(groups, cap)
@@ -102,7 +102,8 @@ def _cascade(prep, groups, prefix, cap, ps, write, name, order=None):
         out, prep.q, key, val, prep.k_pool, prep.v_pool, prep.tables, prep.lens,
         wl.max_context_len, prep.layout, prep.sm_scale, d_prefix, d_groups,
         int(prefix.max()) if prefix.size else 0, prep.k_scale, prep.v_scale, ps,
-        seq_order=None if order is None else torch.from_numpy(order).cuda())
+        seq_order=None if order is None else torch.from_numpy(order).cuda(),
+        tail_units=tail_units)
     torch.cuda.synchronize()
     if write:
         assert np.array_equal(prep.k_pool.cpu().numpy(), k_exp)
@@ -250,7 +251,10 @@ def _pool_built(wl):
     for i, r in enumerate(rows):
         tables[i, :len(r)] = r
     prefix, garr, max_pre, order = pool.prefix_groups(seqs, 8, with_order=True)
-    return tables, got, prefix, garr, max_pre, order
+    P = pkv.pkv_decode_partition_size(len(seqs), wl.num_kv_heads, int(got.max()),
+                                      pkv.PKV_FP8_E4M3FN, 0)
+    units = pool.cascade_tail_units(seqs, prefix, max_pre, P)
+    return tables, got, prefix, garr, max_pre, order, units
 
 
 def test_cascade_shared_prefix_full_step():
@@ -261,7 +265,7 @@ def test_cascade_shared_prefix_full_step():
     by the cascade call itself.  Both pools must equal the oracle's write
     byte for byte, and all 256 outputs must match the oracle's decode."""
     base = workloads.shared_prefix()
-    tables, lens, prefix, garr, max_pre, order = _pool_built(base)
+    tables, lens, prefix, garr, max_pre, order, units = _pool_built(base)
     assert garr.shape[0] == 32 and max_pre == base.prefix_blocks
     B = base.num_seqs
     new = [(b, int(L) - 1) for b, L in enumerate(lens)]
@@ -270,7 +274,8 @@ def test_cascade_shared_prefix_full_step():
     prep = Prepared(wl)
     groups = [[int(m) for m in g if m >= 0] for g in garr]
     assert sorted(m for g in groups for m in g) == list(range(B))
-    got = _cascade(prep, groups, prefix, 8, 0, True, "shared-prefix B=256 full step", order)
+    got = _cascade(prep, groups, prefix, 8, 0, True, "shared-prefix B=256 full step", order,
+                   tail_units=units)
     assert got.shape == (B, wl.num_q_heads, D)
 
 
@@ -289,7 +294,7 @@ def test_cascade_rejects_bad_arguments():
         out.data_ptr(), prep.q.data_ptr(), key.data_ptr(), None, prep.k_pool.data_ptr(),
         prep.v_pool.data_ptr(), prep.tables.data_ptr(), prep.tables.shape[1],
         prep.lens.data_ptr(), None, pre.data_ptr(), garr.data_ptr(), garr.shape[0], 8,
-        int(prefix.max()), None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
+        int(prefix.max()), None, 0, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
         prep.sm_scale, prep.k_scale, prep.v_scale, 0, None, 0, None)
     assert st == pkv.PKV_ERR_INVALID_ARG
     # workspace smaller than the cascade needs (the plain size is smaller)
@@ -303,7 +308,7 @@ def test_cascade_rejects_bad_arguments():
         out.data_ptr(), prep.q.data_ptr(), None, None, prep.k_pool.data_ptr(),
         prep.v_pool.data_ptr(), prep.tables.data_ptr(), prep.tables.shape[1],
         prep.lens.data_ptr(), None, pre.data_ptr(), garr.data_ptr(), garr.shape[0], 8,
-        int(prefix.max()), None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
+        int(prefix.max()), None, 0, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
         prep.sm_scale, prep.k_scale, prep.v_scale, 64, ws.data_ptr(), ws.numel(), None)
     assert st == pkv.PKV_ERR_WORKSPACE
     # more items plus sequences than one grid dimension holds (G = 4: one item
@@ -316,7 +321,7 @@ def test_cascade_rejects_bad_arguments():
         out.data_ptr(), prep.q.data_ptr(), None, None, prep.k_pool.data_ptr(),
         prep.v_pool.data_ptr(), prep.tables.data_ptr(), prep.tables.shape[1],
         prep.lens.data_ptr(), None, pre.data_ptr(), garr.data_ptr(), 65535, 4,
-        int(prefix.max()), None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
+        int(prefix.max()), None, 0, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
         prep.sm_scale, prep.k_scale, prep.v_scale, 64, big.data_ptr(), big.numel(), None)
     assert st == pkv.PKV_ERR_INVALID_ARG
 
@@ -398,3 +403,42 @@ def test_cascade_random_groups(seed):
           f"max abs err {err:.3e}", flush=True)
     assert np.isfinite(got).all()
     assert err <= TOL[fp8]
+
+
+def test_cascade_batch_above_the_flat_grid():
+    """2100 short sequences (groups of 8 over 1- or 2-block prefixes, and
+    sequences in no group): more than the flat grid's batch limit, so the
+    (partition, KV head, item or sequence) grid runs; against the oracle."""
+    rng = np.random.default_rng(95)
+    spec = [(16 * int(rng.integers(1, 3)), [int(t) for t in rng.integers(1, 40, 8)])
+            for _ in range(250)]
+    solo = [int(x) for x in rng.integers(0, 60, 100)]
+    wl, groups, prefix = _grouped(spec, solo, 8, 2, True, seed=96)
+    assert wl.num_seqs == 2100
+    prep = Prepared(wl)
+    tail = wl.context_lens.astype(np.int64) - 16 * prefix
+    order = np.argsort(-tail, kind="stable").astype(np.int32)
+    _cascade(prep, groups, prefix, 8, 0, True, "B=2100", order)
+
+
+def test_cascade_tail_units_change_no_result():
+    """The launch sized by the exact tail count, by an underestimate (each
+    workgroup then takes several units), by an overestimate and by the
+    default bound: the same outputs bit for bit, and the oracle's."""
+    rng = np.random.default_rng(97)
+    spec = [(16 * int(rng.integers(1, 30)), [int(t) for t in rng.integers(1, 900, 6)])
+            for _ in range(5)]
+    solo = [0, 5, 1200]
+    wl, groups, prefix = _grouped(spec, solo, 8, 2, True, seed=98)
+    prep = Prepared(wl)
+    tail = wl.context_lens.astype(np.int64) - 16 * prefix
+    order = np.argsort(-tail, kind="stable").astype(np.int32)
+    ps = 64
+    nblk = -(-wl.context_lens.astype(np.int64) // 16) - prefix
+    exact = int(np.maximum(1, -(-nblk // (ps // 16))).sum())
+    outs = []
+    for tu in (exact, 1, 3, exact + 40, 0):
+        outs.append(_cascade(prep, groups, prefix, 8, ps, False, f"tail_units={tu}", order,
+                             tail_units=tu))
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
