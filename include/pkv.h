@@ -279,6 +279,25 @@ pkv_status pkv_decode_partitions_append(
     float v_scale, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
     void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pkv_paged_attention_decode_append with no workspace argument.  Its
+ * split-KV partials live in a fixed array of PKV_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each device it runs on until the process ends; the
+ * call itself allocates nothing.  Same arguments, kernels and results as
+ * pkv_paged_attention_decode_append.  WORKSPACE if the shape needs more than
+ * the array (pkv_decode_workspace_bytes tells), HIP if the array's address
+ * cannot be found.  Every call on a device uses that device's one array:
+ * calls that overlap in time on one device (other streams, other threads)
+ * race and must not be made. */
+#define PKV_NOALLOC_SCRATCH_BYTES (64ull << 20)
+pkv_status pkv_paged_attention_decode_append_noalloc(
+    float* out, const void* q, const void* key, const void* value, void* k_pool, void* v_pool,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* shared_prefix_blocks, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_context_len, const pkv_cache_layout* layout, float sm_scale, float k_scale,
+    float v_scale, int32_t partition_size, void* stream);
+
 /* Decode over shared prefixes as a cascade.  Sequences that share their
  * leading blocks (a common system prompt, or the branches of a parallel
  * sample: [PRIMER-8] §8.1, [GLOSSARY] §3.02) hold the same physical blocks

@@ -22,7 +22,8 @@ __all__ = [
     "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic", "pkv_paged_prefill_attention",
     "pkv_paged_prefill_attention_dynamic", "pkv_swap_blocks", "pkv_validate_tables",
     "pkv_set_debug_checks", "pkv_get_debug_checks", "pkv_hbm_read_probe",
-    "pkv_tile_gather_probe"
+    "pkv_tile_gather_probe", "pkv_paged_attention_decode_append_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +45,7 @@ PKV_F16 = 0
 PKV_FP8_E4M3FN = 1
 BLOCK_SIZE = 16
 HEAD_DIM = 128
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 
 
 class CacheLayout(ctypes.Structure):
@@ -102,6 +104,8 @@ def load_library():
                                                LP, f32, f32, f32, i32, P, u64, P], i32),
         "pkv_decode_partitions_append": ([P, P, P, P, P, P, P, i32, P, P, i32, i32, i32, LP,
                                           f32, f32, f32, i32, P, u64, P], i32),
+        "pkv_paged_attention_decode_append_noalloc": ([P, P, P, P, P, P, P, i32, P, P, i32, i32,
+                                                       i32, LP, f32, f32, f32, i32, P], i32),
         "pkv_paged_attention_decode_cascade": ([P, P, P, P, P, P, P, i32, P, P, P, P, i32, i32,
                                                 i32, P, i32, i32, i32, i32, LP, f32, f32, f32,
                                                 i32, P, u64, P], i32),
@@ -401,6 +405,25 @@ def pkv_decode_partitions_append(out, q, key, value, k_pool, v_pool, block_table
         _ptr(context_lens), _hint(shared_prefix_blocks, B), B, Hq, max_context_len,
         ctypes.byref(layout), sm_scale, k_scale, v_scale, partition_size, _ptr(workspace),
         nbytes, _stream(stream)), "pkv_decode_partitions_append")
+
+
+def pkv_paged_attention_decode_append_noalloc(out, q, key, value, k_pool, v_pool, block_tables,
+                                              context_lens, max_context_len: int,
+                                              layout: CacheLayout, sm_scale: float,
+                                              k_scale: float = 1.0, v_scale: float = 1.0,
+                                              partition_size: int = 0, stream=None,
+                                              shared_prefix_blocks=None) -> None:
+    """pkv_paged_attention_decode_append with its split-KV partials in the
+    library's own fixed array (NOALLOC_SCRATCH_BYTES per device): no
+    workspace argument and no allocation.  Calls overlapping in time on one
+    device race."""
+    B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
+    kp, vp = _new_rows(key, value, B, layout)
+    _check(load_library().pkv_paged_attention_decode_append_noalloc(
+        _ptr(out), _ptr(q), kp, vp, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
+        _ptr(context_lens), _hint(shared_prefix_blocks, B), B, Hq, max_context_len,
+        ctypes.byref(layout), sm_scale, k_scale, v_scale, partition_size, _stream(stream)),
+        "pkv_paged_attention_decode_append_noalloc")
 
 
 def pkv_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_context_len,

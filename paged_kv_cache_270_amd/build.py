@@ -29,7 +29,8 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src, dev in (("pkv_host.cpp", False), ("pkv_kernels.hip", True),
                      ("pkv_write.hip", True), ("pkv_prefill.hip", True),
-                     ("pkv_swap.hip", True), ("pkv_probe.hip", True)):
+                     ("pkv_swap.hip", True), ("pkv_probe.hip", True),
+                     ("pkv_noalloc.hip", True)):
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC] + COMMON + (DEVICE_FLAGS + ["-x", "hip"] if dev else []) + \
               ["-c", os.path.join(CSRC, src), "-o", obj]
