@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BULK_REPS = 7   # timed bulk fills; the median is reported
 METRIC = "KV GB/s read (% of HBM peak) + decode seqs·tok/s, 70B-layer shape, FP8 KV"
 CSRC = os.path.join(ROOT, "paged_kv_cache_270_amd", "csrc")
 # the sources each measured kernel is built from
@@ -119,6 +120,20 @@ def stream_read_gbs(pkv, nbytes: int = 2 << 30) -> float:
              for wg in (1024, 2048, 4096, 8192))
     del buf
     return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def write_mix_gbs(pkv, reads_per_write: int, dst_bytes: int = 1 << 30) -> float:
+    """Ceiling for a write that reads `reads_per_write` bytes per byte it
+    writes (the cache write: 2 for FP8, 1 for fp16): contiguous planes
+    streamed into a destination, non-temporal both ways, the best of four grid
+    sizes; GB/s counts the bytes read and written."""
+    import torch
+    src = torch.empty(reads_per_write * dst_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(dst_bytes, dtype=torch.uint8, device="cuda")
+    ms = min(timed_launches(lambda: pkv.pkv_hbm_mix_probe(src, dst, reads_per_write, wg), 10)
+             for wg in (1024, 2048, 4096, 8192))
+    del src, dst
+    return round((reads_per_write + 1) * dst_bytes / (ms * 1e-3) / 1e9, 1)
 
 
 def cpu_model() -> str:
@@ -568,16 +583,22 @@ def main() -> int:
             pkv.pkv_reshape_and_cache(k, v, k_pool, v_pool, slots, layout, k_scale, v_scale)
 
     # ---- bulk fill (a prefill-sized write of every cached token), timed on its
-    # own: the first fill loads the kernel and fills the pool, the second
-    # (same bytes again) is timed
-    write(key_src, val_src, d_bulk_slots)  # (every block starts at offset 0: fresh again)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    # own: the first fill loads the kernel and fills the pool, the next ones
+    # (same bytes again; every block starts at offset 0, so it is fresh again)
+    # are timed one by one and the median is reported
     write(key_src, val_src, d_bulk_slots)
-    e1.record()
     torch.cuda.synchronize()
-    bulk_ms = e0.elapsed_time(e1)
+    bulk_times = []
+    for _ in range(BULK_REPS):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        write(key_src, val_src, d_bulk_slots)
+        e1.record()
+        torch.cuda.synchronize()
+        bulk_times.append(e0.elapsed_time(e1))
+    bulk_ms = float(np.median(bulk_times))
+    print("bulk fill ms per launch: " + " ".join(f"{t:.3f}" for t in bulk_times),
+          file=sys.stderr)
     bulk_bytes = T * Hkv * D * 2 * (2 + e) + T * 8   # fp16 rows in, cache rows out, slots
     del key_src, val_src
 
@@ -691,6 +712,8 @@ def main() -> int:
                                                                  Lmax, layout, sink), args.steps)
     gather_gbs = logical / (gather_ms * 1e-3) / 1e9
     stream_gbs = stream_read_gbs(pkv)
+    mix_rpw = 2 // e                                    # fp16 rows in per cache byte out
+    mix_gbs = write_mix_gbs(pkv, mix_rpw)
     # ---- bytes besides the KV tiles: queries, outputs, table entries and
     # lengths read, the newest rows in and out, split-KV partials written and
     # read back by the merge (max and sum, 128 floats)
@@ -791,7 +814,10 @@ def main() -> int:
                          "tile_gather_bytes": logical - (0 if not dyn else
                                                          int(nblk_b.sum()) * Hkv * 8),
                          "value_frac_of_stream_read": round(value / stream_gbs, 4),
-                         "kernel_frac_of_stream_read": round(achieved / stream_gbs, 4)},
+                         "kernel_frac_of_stream_read": round(achieved / stream_gbs, 4),
+                         "write_mix_gbs": mix_gbs, "write_mix_reads_per_write": mix_rpw,
+                         "bulk_fill_frac_of_write_mix":
+                             round(bulk_bytes / (bulk_ms * 1e-3) / 1e9 / mix_gbs, 4)},
         "other_bytes_per_step": other,
         "inputs": {"structure_seed": wl.seed, "value_seeds": [301, 302, 303, 304, 305],
                    "context_lens_sha256": sha256_of(lens),
@@ -799,6 +825,8 @@ def main() -> int:
         "shared_prefix_blocks_hint": int(shared.max()) if B else 0,
         "host_slot_assignment_us": round(host_slot_us, 1),
         "bulk_fill_gbs": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),
+        "bulk_fill_gbs_range": [round(bulk_bytes / (t * 1e-3) / 1e9, 1)
+                                for t in (max(bulk_times), min(bulk_times))],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      # counters were taken at the workload's own partition size

@@ -721,9 +721,19 @@ pkv_status pkv_swap_blocks(void* k_pool, void* v_pool, void* host_k, void* host_
  * arguments as in pkv_paged_attention_decode; ids outside the pool read
  * nothing).  Both fold what they read into one word per lane and store it to
  * sink[0] (device uint32) only if it equals `key`, so nothing measurable is
- * written.  Asynchronous on `stream`. */
+ * written.
+ * pkv_hbm_mix_probe is the ceiling for the cache write (§4 of [FP8-128K]
+ * moves fp16 rows into the cache): it reads `reads_per_write` (1 or 2)
+ * source planes of `dst_bytes` each, laid one after the other at `src`, and
+ * writes their XOR, `dst_bytes` (a multiple of 16), to `dst`, every load and
+ * store non-temporal, each of `workgroups` (0 = 2048) workgroups streaming
+ * its own slab.  Both buffers 16-byte aligned device memory, owned by the
+ * caller; they must not overlap.  All three are asynchronous on `stream`;
+ * bad arguments return PKV_ERR_INVALID_ARG before any launch. */
 pkv_status pkv_hbm_read_probe(const void* buf, uint64_t bytes, int32_t workgroups,
                               uint32_t* sink, uint32_t key, void* stream);
+pkv_status pkv_hbm_mix_probe(const void* src, void* dst, uint64_t dst_bytes,
+                             int32_t reads_per_write, int32_t workgroups, void* stream);
 pkv_status pkv_tile_gather_probe(const void* k_pool, const void* v_pool,
                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
                                  const int32_t* context_lens, int32_t num_seqs,

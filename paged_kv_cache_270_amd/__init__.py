@@ -22,7 +22,7 @@ __all__ = [
     "pkv_paged_attention_decode_dynamic", "pkv_copy_blocks_dynamic", "pkv_paged_prefill_attention",
     "pkv_paged_prefill_attention_dynamic", "pkv_swap_blocks", "pkv_validate_tables",
     "pkv_set_debug_checks", "pkv_get_debug_checks", "pkv_hbm_read_probe",
-    "pkv_tile_gather_probe", "pkv_paged_attention_decode_append_noalloc",
+    "pkv_hbm_mix_probe", "pkv_tile_gather_probe", "pkv_paged_attention_decode_append_noalloc",
     "NOALLOC_SCRATCH_BYTES",
 ]
 
@@ -92,6 +92,7 @@ def load_library():
         "pkv_validate_tables": ([P, i32, P, i32, i32, i32, ctypes.POINTER(i32)], i32),
         "pkv_set_debug_checks": ([i32], i32),
         "pkv_hbm_read_probe": ([P, u64, i32, P, ctypes.c_uint32, P], i32),
+        "pkv_hbm_mix_probe": ([P, P, u64, i32, i32, P], i32),
         "pkv_tile_gather_probe": ([P, P, P, i32, P, i32, i32, LP, P, ctypes.c_uint32, P], i32),
         "pkv_get_debug_checks": ([], i32),
         "pkv_reshape_and_cache": ([P, P, P, P, P, i32, LP, f32, f32, P], i32),
@@ -264,6 +265,18 @@ def pkv_hbm_read_probe(buf, sink, workgroups: int = 0, stream=None) -> None:
     _check(load_library().pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
                                              workgroups, _ptr(sink), _PROBE_KEY,
                                              _stream(stream)), "pkv_hbm_read_probe")
+
+
+def pkv_hbm_mix_probe(src, dst, reads_per_write: int, workgroups: int = 0,
+                      stream=None) -> None:
+    """Stream `reads_per_write` planes of `dst`'s size from device tensor `src`
+    into `dst` (their XOR), non-temporal both ways: the ceiling for a write
+    with that mix of reads and writes."""
+    nbytes = dst.numel() * dst.element_size()
+    if src.numel() * src.element_size() < reads_per_write * nbytes:
+        raise ValueError("pkv_hbm_mix_probe: src holds fewer than reads_per_write planes")
+    _check(load_library().pkv_hbm_mix_probe(_ptr(src), _ptr(dst), nbytes, reads_per_write,
+                                            workgroups, _stream(stream)), "pkv_hbm_mix_probe")
 
 
 def pkv_tile_gather_probe(k_pool, v_pool, block_tables, context_lens, max_context_len: int,

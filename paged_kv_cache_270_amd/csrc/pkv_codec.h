@@ -17,19 +17,54 @@ namespace pkv_dev {
 // at or above 448 (and infinities) saturate to +-448, NaN -> 0x7F | sign.
 // Written from the format definition: below 2^-6 the codes are a uniform
 // grid of 2^-9 (subnormals), above it 3 mantissa bits are kept.
+// Every case is computed and the right one selected, so a wave never splits.
 __device__ __forceinline__ uint32_t e4m3_from_f32(float u) {
   const uint32_t bits = __float_as_uint(u);
   const uint32_t sign = (bits >> 24) & 0x80u;
   const uint32_t abits = bits & 0x7FFFFFFFu;
-  if (abits > 0x7F800000u) return sign | 0x7Fu;              // NaN
   const float a = __uint_as_float(abits);
-  if (a >= 448.0f) return sign | 0x7Eu;                      // saturate
-  if (a < 0.015625f)                                         // < 2^-6
-    return sign | (uint32_t)__builtin_rintf(a * 512.0f);     // 0..8, exact scaling
-  // keep the top 3 mantissa bits, round the 20 dropped bits half-to-even;
-  // a carry moves into the exponent, which is what the code needs
-  const uint32_t r = abits + 0x7FFFFu + ((abits >> 20) & 1u);
-  return sign | ((r >> 20) - (120u << 3));                   // rebias 127 -> 7
+  // below 2^-6: 0..8, exact scaling
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
+  // from 2^-6: keep the top 3 mantissa bits, round the 20 dropped bits
+  // half-to-even; a carry moves into the exponent, which is what the code
+  // needs (rebias 127 -> 7)
+  const uint32_t nrm = ((abits + 0x7FFFFu + ((abits >> 20) & 1u)) >> 20) - (120u << 3);
+  uint32_t code = a < 0.015625f ? sub : nrm;
+  code = a >= 448.0f ? 0x7Eu : code;                         // saturate (and infinities)
+  code = abits > 0x7F800000u ? 0x7Fu : code;                 // NaN
+  return sign | code;
+}
+
+// Division of many values by one positive finite scale s, rounded as IEEE
+// fp32 division rounds x / s, with no division per value.  With s = m * 2^e,
+// m in [1, 2), and y = fp32(1 / m) correctly rounded, for each x:
+//   q0 = x * y                 (within one ulp of x / m)
+//   r  = x - q0 * m            (one fused multiply-add; exact)
+//   q  = q0 + r * y            (one fused multiply-add)
+// q is x / m correctly rounded (Markstein's theorem: y within half an ulp of
+// 1 / m and q0 within one ulp of the quotient suffice); for x of at most 11
+// significant bits -- every fp16 value -- this was also checked against
+// double-precision division for every pair of significands.  Then x / s =
+// q * 2^-e, exact while the quotient is a normal fp32 number; below 2^-126
+// (where ldexp may round once more) every quotient encodes to a signed zero
+// E4M3 code all the same.
+struct ScaleDiv {
+  float m, y;
+  int e;
+};
+
+__device__ __forceinline__ ScaleDiv scale_div(float s) {
+  int e = 0;
+  const float m = 2.0f * __builtin_frexpf(s, &e);  // s = (m / 2) * 2^e, m / 2 in [0.5, 1)
+  return ScaleDiv{m, 1.0f / m, e - 1};
+}
+
+__device__ __forceinline__ float div_by(float x, const ScaleDiv& d) {
+  const float q0 = x * d.y;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, d.m, x), d.y, q0);
+  // +-0 keeps its sign; an infinite x gives its infinity (q1 is NaN there)
+  const float q = __builtin_isfinite(q1) ? __builtin_copysignf(q1, x) : q0;
+  return __builtin_ldexpf(q, -d.e);
 }
 
 }  // namespace pkv_dev

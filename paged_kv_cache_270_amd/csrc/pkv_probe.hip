@@ -7,6 +7,10 @@
 // this part, without any attention arithmetic:
 //   * pkv_hbm_read_probe: a contiguous buffer streamed once, 16 bytes per
 //     lane per load, non-temporal -- the streaming-read ceiling;
+//   * pkv_hbm_mix_probe: one or two contiguous source planes streamed into a
+//     destination, non-temporal both ways -- the ceiling for a write with the
+//     cache write's mix of reads and writes (fp16 rows in, FP8 rows out: two
+//     bytes read per byte written);
 //   * pkv_tile_gather_probe: the decode kernel's own reads -- every K and V
 //     tile of every sequence, gathered through the block table with the same
 //     16-byte lane loads and cache policy, one workgroup of four waves per
@@ -55,6 +59,51 @@ stream_read_kernel(const u32x4* __restrict__ buf, uint64_t n_vec, uint64_t slab_
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == key) sink[0] = acc;
+}
+
+// Workgroup i streams its own slab of the destination in 32 KiB steps and
+// the same slab of each of the kPlanes source planes (plane p starts n_vec
+// vectors after plane p - 1): kPlanes bytes read per byte written, every load
+// and store non-temporal, eight 16-byte vectors in flight per lane and plane.
+template <int kPlanes>
+__global__ void __launch_bounds__(kProbeThreads)
+stream_mix_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n_vec,
+                  uint64_t slab_vecs) {
+  const uint64_t begin = (uint64_t)blockIdx.x * slab_vecs;
+  const uint64_t end = begin + slab_vecs < n_vec ? begin + slab_vecs : n_vec;
+  uint64_t i = begin;
+  for (; i + kStepVecs <= end; i += kStepVecs) {
+    u32x4 v[kPlanes][kProbeUnroll];
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+      for (int u = 0; u < kProbeUnroll; ++u)
+        v[p][u] = __builtin_nontemporal_load(src + p * n_vec + i + u * kProbeThreads +
+                                             threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      u32x4 r = v[0][u];
+#pragma unroll
+      for (int p = 1; p < kPlanes; ++p) r ^= v[p][u];
+      __builtin_nontemporal_store(r, dst + i + u * kProbeThreads + threadIdx.x);
+    }
+  }
+  for (uint64_t j = i + threadIdx.x; j < end; j += kProbeThreads) {
+    u32x4 r = __builtin_nontemporal_load(src + j);
+#pragma unroll
+    for (int p = 1; p < kPlanes; ++p) r ^= __builtin_nontemporal_load(src + p * n_vec + j);
+    __builtin_nontemporal_store(r, dst + j);
+  }
+}
+
+// Whole 32 KiB steps per slab, one slab per workgroup (0 = 2048 workgroups).
+void stream_slabs(uint64_t n_vec, int32_t workgroups, uint64_t* wg_out, uint64_t* slab_out) {
+  const uint64_t steps = (n_vec + kStepVecs - 1) / kStepVecs;
+  uint64_t wg = workgroups > 0 ? (uint64_t)workgroups : 2048;
+  if (wg > steps) wg = steps;
+  const uint64_t slab = (steps + wg - 1) / wg * kStepVecs;
+  *wg_out = (n_vec + slab - 1) / slab;
+  *slab_out = slab;
 }
 
 struct GatherArgs {
@@ -119,15 +168,32 @@ extern "C" pkv_status pkv_hbm_read_probe(const void* buf, uint64_t bytes, int32_
   if (!buf || !sink || !aligned(buf, 16) || bytes % 16 != 0 || workgroups < 0)
     return PKV_ERR_INVALID_ARG;
   const uint64_t n_vec = bytes / 16;
-  // slabs of whole 32 KiB steps, one per workgroup
-  const uint64_t steps = (n_vec + kStepVecs - 1) / kStepVecs;
-  uint64_t wg = workgroups > 0 ? (uint64_t)workgroups : 2048;
-  if (wg > steps) wg = steps;
-  const uint64_t slab = (steps + wg - 1) / wg * kStepVecs;
-  wg = (n_vec + slab - 1) / slab;
+  uint64_t wg = 0, slab = 0;
+  stream_slabs(n_vec, workgroups, &wg, &slab);
   (void)hipGetLastError();
   stream_read_kernel<<<(unsigned)wg, kProbeThreads, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const u32x4*>(buf), n_vec, slab, sink, key);
+  return launch_status();
+}
+
+extern "C" pkv_status pkv_hbm_mix_probe(const void* src, void* dst, uint64_t dst_bytes,
+                                        int32_t reads_per_write, int32_t workgroups,
+                                        void* stream) {
+  if (dst_bytes == 0) return PKV_OK;
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16) || dst_bytes % 16 != 0 ||
+      workgroups < 0 || reads_per_write < 1 || reads_per_write > 2)
+    return PKV_ERR_INVALID_ARG;
+  const uint64_t n_vec = dst_bytes / 16;
+  uint64_t wg = 0, slab = 0;
+  stream_slabs(n_vec, workgroups, &wg, &slab);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  u32x4* d = static_cast<u32x4*>(dst);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (reads_per_write == 1)
+    stream_mix_kernel<1><<<(unsigned)wg, kProbeThreads, 0, st>>>(s, d, n_vec, slab);
+  else
+    stream_mix_kernel<2><<<(unsigned)wg, kProbeThreads, 0, st>>>(s, d, n_vec, slab);
   return launch_status();
 }
 

@@ -50,11 +50,13 @@ __device__ __forceinline__ void store_rows8(uint8_t* __restrict__ k_pool,
     uint8_t* vp = v_pool + tile * (kBS * kD);
     const _Float16* kh = reinterpret_cast<const _Float16*>(&kin);
     const _Float16* vh = reinterpret_cast<const _Float16*>(&vin);
+    // x / scale rounded as fp32 division rounds it (one division per scale)
+    const ScaleDiv kd = scale_div(k_scale), vd = scale_div(v_scale);
     uint32_t kc[8], vc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      kc[i] = e4m3_from_f32((float)kh[i] / k_scale);  // correctly rounded fp32 division
-      vc[i] = e4m3_from_f32((float)vh[i] / v_scale);
+      kc[i] = e4m3_from_f32(div_by((float)kh[i], kd));
+      vc[i] = e4m3_from_f32(div_by((float)vh[i], vd));
     }
     // K, x = 16: (d/16)*256 + t*16 + d%16 -> 8 contiguous bytes
     u32x2 kw;
@@ -125,6 +127,27 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
   const int h = (int)(unit % (unsigned)hkv);
   const int64_t t0 = (int64_t)(unit / (unsigned)hkv) * kBS;
   const int ntok = (int)min<int64_t>(kBS, num_tokens - t0);
+  // FP8: the group's 16 rows are requested with its slots (their addresses
+  // do not depend on the slots), so a whole block -- every group of a bulk
+  // fill -- costs one round trip to memory; each row is read once, past the
+  // caches.  The other groups load their rows again below.  fp16 loads them
+  // once the slots are known: its batched prefills mostly take the two-run
+  // path, and the early loads measured slower there.
+  u32x4 kin[4], vin[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = lane + kWave * j;  // (token, run of 8 channels)
+    const int t = i >> 4, c = i & 15;
+    if constexpr (kFP8) {
+      if (t < ntok) {
+        const int64_t th = (t0 + t) * hkv + h;
+        kin[j] = __builtin_nontemporal_load(key + th * 16 + c);
+        vin[j] = __builtin_nontemporal_load(value + th * 16 + c);
+      } else {
+        kin[j] = vin[j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
   const int64_t my_slot = lane < ntok ? slots[t0 + lane] : -1;
   const int64_t s0 = __shfl(my_slot, 0, kWave);
   const bool in_order = lane >= kBS || my_slot == s0 + lane;
@@ -179,26 +202,29 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
   for (int j = 0; j < 4; ++j) {
     const int i = lane + kWave * j;  // (token, run of 8 channels)
     const int t = i >> 4, c = i & 15;
-    const int64_t th = (t0 + t) * hkv + h;
-    const u32x4 kin = key[th * 16 + c];
-    const u32x4 vin = value[th * 16 + c];
     const int n = c >> 1, j0 = (c & 1) * 8;
+    if constexpr (!kFP8) {
+      const int64_t th = (t0 + t) * hkv + h;
+      kin[j] = key[th * 16 + c];
+      vin[j] = value[th * 16 + c];
+    }
     if constexpr (kFP8) {
-      const _Float16* kh = reinterpret_cast<const _Float16*>(&kin);
-      const _Float16* vh = reinterpret_cast<const _Float16*>(&vin);
+      const _Float16* kh = reinterpret_cast<const _Float16*>(&kin[j]);
+      const _Float16* vh = reinterpret_cast<const _Float16*>(&vin[j]);
+      const ScaleDiv kd = scale_div(k_scale), vd = scale_div(v_scale);
       uint32_t kc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kc[e] = e4m3_from_f32((float)kh[e] / k_scale);
+      for (int e = 0; e < 8; ++e) kc[e] = e4m3_from_f32(div_by((float)kh[e], kd));
       u32x2 kw;
       kw.x = kc[0] | (kc[1] << 8) | (kc[2] << 16) | (kc[3] << 24);
       kw.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
       *reinterpret_cast<u32x2*>(lk + n * 256 + t * 16 + j0) = kw;  // K: 8 contiguous bytes
       uint8_t* vb = lv + (n >> 2) * 1024 + ((t >> 2) * 16 + j0) * 16 + (n & 3) * 4 + (t & 3);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vb[e * 16] = (uint8_t)e4m3_from_f32((float)vh[e] / v_scale);
+      for (int e = 0; e < 8; ++e) vb[e * 16] = (uint8_t)e4m3_from_f32(div_by((float)vh[e], vd));
     } else {
-      *reinterpret_cast<u32x4*>(lk + (c * 128 + t * 8) * 2) = kin;  // K: 16 contiguous bytes
-      const uint16_t* vh = reinterpret_cast<const uint16_t*>(&vin);
+      *reinterpret_cast<u32x4*>(lk + (c * 128 + t * 8) * 2) = kin[j];  // K: 16 contiguous bytes
+      const uint16_t* vh = reinterpret_cast<const uint16_t*>(&vin[j]);
       uint16_t* vb = reinterpret_cast<uint16_t*>(lv) + (n >> 1) * 512 +
                      ((t >> 2) * 16 + j0) * 8 + (n & 1) * 4 + (t & 3);
 #pragma unroll
@@ -214,10 +240,11 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
   u32x4* vt = reinterpret_cast<u32x4*>(v_pool + tile * kTileBytes);
   const u32x4* sk = reinterpret_cast<const u32x4*>(lk);
   const u32x4* sv = reinterpret_cast<const u32x4*>(lv);
+  // the tiles are not read again by this call: stored past the caches
 #pragma unroll
   for (int j = 0; j < kTileBytes / 16 / kWave; ++j) {
-    kt[lane + kWave * j] = sk[lane + kWave * j];
-    vt[lane + kWave * j] = sv[lane + kWave * j];
+    __builtin_nontemporal_store(sk[lane + kWave * j], kt + lane + kWave * j);
+    __builtin_nontemporal_store(sv[lane + kWave * j], vt + lane + kWave * j);
   }
 }
 

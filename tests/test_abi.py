@@ -319,3 +319,28 @@ def test_debug_checks_from_the_environment():
         out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
                              text=True, check=True).stdout.strip()
         assert out == want, (val, out)
+
+
+def test_probes_validate_before_launch():
+    """The memory-ceiling probes reject bad arguments before any HIP call."""
+    L = pkv.load_library()
+    lay = pkv.CacheLayout(16, 2, pkv.PKV_FP8_E4M3FN)
+    # mix probe: one or two source planes only, 16-byte sizes and alignment
+    for rpw in (0, 3):
+        assert L.pkv_hbm_mix_probe(16, 32, 16, rpw, 0, None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_hbm_mix_probe(16, 32, 24, 1, 0, None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_hbm_mix_probe(8, 32, 16, 1, 0, None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_hbm_mix_probe(16, 40, 16, 2, 0, None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_hbm_mix_probe(16, 32, 16, 1, -1, None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_hbm_mix_probe(None, None, 0, 1, 0, None) == pkv.PKV_OK   # nothing to do
+    # read probe
+    assert L.pkv_hbm_read_probe(16, 24, 0, 16, 0, None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_hbm_read_probe(None, 32, 0, 16, 0, None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_hbm_read_probe(None, 0, 0, None, 0, None) == pkv.PKV_OK
+    # gather probe
+    assert L.pkv_tile_gather_probe(16, 16, 16, 4, 16, -1, 64, ctypes.byref(lay), 16, 0,
+                                   None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_tile_gather_probe(16, 16, 16, 0, 16, 2, 64, ctypes.byref(lay), 16, 0,
+                                   None) == pkv.PKV_ERR_INVALID_ARG
+    assert L.pkv_tile_gather_probe(None, None, None, 4, None, 0, 64, ctypes.byref(lay), None, 0,
+                                   None) == pkv.PKV_OK

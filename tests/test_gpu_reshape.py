@@ -45,13 +45,23 @@ def test_random_slots_bit_exact(fp8, hkv):
     assert (kd == SENTINEL).sum() > 0      # untouched bytes kept
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.0110, 0.125, 0.37, 1e-3, 7.0, 3.0e-5])
+@pytest.mark.parametrize("scale", [1.0, 0.0110, 0.125, 0.37, 1e-3, 7.0, 3.0e-5,
+                                   # significand all ones / just above one
+                                   float(np.nextafter(np.float32(2.0), np.float32(0.0))),
+                                   float(np.nextafter(np.float32(1.0), np.float32(2.0))),
+                                   # the ends of fp32: subnormal, tiny, huge scales
+                                   float(np.float32(2.0 ** -149)), float(np.float32(1e-40)),
+                                   float(np.float32(2.0 ** -126)), 1e-30, 1e30,
+                                   float(np.finfo(np.float32).max)])
 @pytest.mark.parametrize("order", ["blocks", "rows"])
 def test_fp8_encode_every_fp16_value(scale, order):
     """All 65536 fp16 inputs (zeros, subnormals, infinities, NaNs) through
     the device encoder, for several scales, against the oracle's encoder --
     written as whole blocks in order (the tile-building kernel: 1024 tokens)
-    and token by token (the row kernel: 512 tokens, reversed slots)."""
+    and token by token (the row kernel: 512 tokens, reversed slots).  The
+    scales include the ends of the fp32 range, where the kernels' division
+    (a reciprocal of the scale's significand, one correction step and an
+    exponent shift) meets overflow and underflow."""
     bits = np.arange(65536, dtype=np.uint16)
     x = torch.from_numpy(bits.view(np.float16).reshape(512, 1, D).copy())
     if order == "blocks":
