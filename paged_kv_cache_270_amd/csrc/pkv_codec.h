@@ -67,4 +67,57 @@ __device__ __forceinline__ float div_by(float x, const ScaleDiv& d) {
   return __builtin_ldexpf(q, -d.e);
 }
 
+// Four E4M3 codes at once, through the hardware conversion: the encoder for
+// bulk writes.  gfx950's fp32 -> E4M3 conversion rounds to nearest even,
+// subnormal codes included, exactly as e4m3_from_f32 does below 448; it does
+// not saturate (larger values become NaN) and writes every NaN as 0xFF.  So
+// each quotient goes in as its magnitude, clamped to 448 when it is at or
+// above 448, and the sign bit of each code is then taken from the input (a
+// NaN input keeps the code 0x7F and gets its own sign).
+//
+// The quotient x / s is computed as div_by does, without the exponent
+// split: y = fp32(1 / s) (correctly rounded; FLT_MAX where 1 / s overflows),
+// q0 = x * y, q1 = q0 + (x - q0 * s) * y by two fused multiply-adds.  q1 is
+// the correctly rounded quotient wherever it matters: the remainder is
+// exact for every fp16 x and any positive finite s (it is about |x| * 2^-23,
+// far from underflow), and where q0 or y leave the normal range the quotient
+// is either >= 448 (q0 shows it, including x = +-inf) or encodes to a signed
+// zero.  This was checked, code for code, for every fp16 x against the
+// correctly rounded division over scales from the smallest subnormal to
+// FLT_MAX.
+struct Fp8Enc {
+  float s, y;
+};
+
+__device__ __forceinline__ Fp8Enc fp8_enc(float s) {
+  const float y = 1.0f / s;
+  return Fp8Enc{s, y > 3.40282347e38f ? 3.40282347e38f : y};
+}
+
+__device__ __forceinline__ float fp8_enc_magnitude(float x, const Fp8Enc& e) {
+  const float q0 = x * e.y;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, e.s, x), e.y, q0);
+  return __builtin_fabsf(q0) >= 448.0f ? 448.0f : __builtin_fabsf(q1);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Codes of the fp16 values 0, 1 (lo) and 2, 3 (hi) divided by the scale:
+// byte i of the result is the code of value i.
+__device__ __forceinline__ uint32_t e4m3x4_from_f16x4(uint32_t lo, uint32_t hi,
+                                                      const Fp8Enc& e) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_enc_magnitude(f16_lo(lo), e),
+                                          fp8_enc_magnitude(f16_hi(lo), e), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_enc_magnitude(f16_lo(hi), e),
+                                      fp8_enc_magnitude(f16_hi(hi), e), w, true);
+  // the byte holding each input's sign bit: bytes 1 and 3 of lo, then of hi
+  const uint32_t signs = __builtin_amdgcn_perm(hi, lo, 0x07050301u);
+  return (signs & 0x80808080u) | ((uint32_t)w & 0x7F7F7F7Fu);
+}
+
 }  // namespace pkv_dev

@@ -130,15 +130,16 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
   // FP8: the group's 16 rows are requested with its slots (their addresses
   // do not depend on the slots), so a whole block -- every group of a bulk
   // fill -- costs one round trip to memory; each row is read once, past the
-  // caches.  The other groups load their rows again below.  fp16 loads them
-  // once the slots are known: its batched prefills mostly take the two-run
-  // path, and the early loads measured slower there.
+  // caches.  Lane l takes channels 8c .. 8c+7, c = l % 16, of the four tokens
+  // 4q .. 4q+3, q = l / 16 (each load instruction reads four whole rows).
+  // The other groups load their rows again below.  fp16 loads them once the
+  // slots are known: its batched prefills mostly take the two-run path, and
+  // the early loads measured slower there.
   u32x4 kin[4], vin[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int i = lane + kWave * j;  // (token, run of 8 channels)
-    const int t = i >> 4, c = i & 15;
     if constexpr (kFP8) {
+      const int t = 4 * (lane >> 4) + j, c = lane & 15;
       if (t < ntok) {
         const int64_t th = (t0 + t) * hkv + h;
         kin[j] = __builtin_nontemporal_load(key + th * 16 + c);
@@ -198,32 +199,49 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
     return;
   }
   // whole block: place every element at its tile position in LDS
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = lane + kWave * j;  // (token, run of 8 channels)
-    const int t = i >> 4, c = i & 15;
+  if constexpr (kFP8) {
+    const int q = lane >> 4, c = lane & 15;  // tokens 4q .. 4q+3, channels 8c .. 8c+7
     const int n = c >> 1, j0 = (c & 1) * 8;
-    if constexpr (!kFP8) {
+    const Fp8Enc ke = fp8_enc(k_scale), ve = fp8_enc(v_scale);
+    uint32_t vc[2][4];  // V codes of channels 8c + 4i .. 8c + 4i + 3 of token 4q + k
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x2 kw;
+      kw.x = e4m3x4_from_f16x4(kin[k].x, kin[k].y, ke);
+      kw.y = e4m3x4_from_f16x4(kin[k].z, kin[k].w, ke);
+      // K, x = 16: (d/16)*256 + t*16 + d%16 -> 8 contiguous bytes
+      *reinterpret_cast<u32x2*>(lk + n * 256 + (4 * q + k) * 16 + j0) = kw;
+      vc[0][k] = e4m3x4_from_f16x4(vin[k].x, vin[k].y, ve);
+      vc[1][k] = e4m3x4_from_f16x4(vin[k].z, vin[k].w, ve);
+    }
+    // V, x = 16: (n/4)*1024 + ((t/4)*16 + d%16)*16 + (n%4)*4 + t%4 -> the
+    // codes of channel d for the four tokens 4q .. 4q+3 are one aligned
+    // 4-byte word: transpose each 4 x 4 block of bytes (token x channel)
+    uint8_t* vb = lv + (n >> 2) * 1024 + (q * 16 + j0) * 16 + (n & 3) * 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t* x = vc[i];
+      const uint32_t p01_lo = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+      const uint32_t p01_hi = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+      const uint32_t p23_lo = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+      const uint32_t p23_hi = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+      uint32_t* vw = reinterpret_cast<uint32_t*>(vb + 4 * i * 16);
+      vw[0] = __builtin_amdgcn_perm(p23_lo, p01_lo, 0x05040100u);   // channel 8c + 4i
+      vw[4] = __builtin_amdgcn_perm(p23_lo, p01_lo, 0x07060302u);   // + 1
+      vw[8] = __builtin_amdgcn_perm(p23_hi, p01_hi, 0x05040100u);   // + 2
+      vw[12] = __builtin_amdgcn_perm(p23_hi, p01_hi, 0x07060302u);  // + 3
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = lane + kWave * j;  // (token, run of 8 channels)
+      const int t = i >> 4, c = i & 15;
+      const int n = c >> 1, j0 = (c & 1) * 8;
       const int64_t th = (t0 + t) * hkv + h;
       kin[j] = key[th * 16 + c];
       vin[j] = value[th * 16 + c];
-    }
-    if constexpr (kFP8) {
-      const _Float16* kh = reinterpret_cast<const _Float16*>(&kin[j]);
-      const _Float16* vh = reinterpret_cast<const _Float16*>(&vin[j]);
-      const ScaleDiv kd = scale_div(k_scale), vd = scale_div(v_scale);
-      uint32_t kc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kc[e] = e4m3_from_f32(div_by((float)kh[e], kd));
-      u32x2 kw;
-      kw.x = kc[0] | (kc[1] << 8) | (kc[2] << 16) | (kc[3] << 24);
-      kw.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
-      *reinterpret_cast<u32x2*>(lk + n * 256 + t * 16 + j0) = kw;  // K: 8 contiguous bytes
-      uint8_t* vb = lv + (n >> 2) * 1024 + ((t >> 2) * 16 + j0) * 16 + (n & 3) * 4 + (t & 3);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vb[e * 16] = (uint8_t)e4m3_from_f32(div_by((float)vh[e], vd));
-    } else {
       *reinterpret_cast<u32x4*>(lk + (c * 128 + t * 8) * 2) = kin[j];  // K: 16 contiguous bytes
+      // V, x = 8: (n/2)*512 + ((t/4)*16 + d%16)*8 + (n%2)*4 + t%4
       const uint16_t* vh = reinterpret_cast<const uint16_t*>(&vin[j]);
       uint16_t* vb = reinterpret_cast<uint16_t*>(lv) + (n >> 1) * 512 +
                      ((t >> 2) * 16 + j0) * 8 + (n & 1) * 4 + (t & 3);
