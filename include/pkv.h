@@ -168,7 +168,11 @@ int32_t pkv_get_debug_checks(void);
  *   k_scale/v_scale  per-tensor scales, used only for PKV_FP8_E4M3FN; must be
  *                 finite and > 0 then.
  * fp16 pools receive the 16 input bits unchanged; FP8 pools receive the code
- * defined under "FP8 encoding" above.  num_tokens == 0 is a no-op. */
+ * defined under "FP8 encoding" above.  A slot named twice in one call holds
+ * one of the two rows afterwards, which one unspecified.  Blocks whose 16
+ * slots the call fills in order from consecutive tokens (any alignment of
+ * the tokens within the call) are written as whole tiles; other slots row
+ * by row.  num_tokens == 0 is a no-op. */
 pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
                                  void* v_pool, const int64_t* slot_mapping,
                                  int32_t num_tokens, const pkv_cache_layout* layout,

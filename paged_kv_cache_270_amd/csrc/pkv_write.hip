@@ -99,16 +99,50 @@ reshape_rows_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ val
 // fills, prefill chunks) the tile-building kernel below.
 constexpr int64_t kRowWriteMaxTokens = 512;
 
-// One wave per (group of 16 consecutive tokens of the call, KV head).  When
-// the group's slots are one whole block in order (a bulk fill or a prefill
-// chunk), the wave builds the (block, head) tiles in LDS from coalesced loads
-// of the 16 rows and writes each tile as one contiguous run (2 KiB FP8 /
-// 4 KiB fp16), so the scattered layout costs no partial-line writes.  Other
-// groups (a decode step: one token per sequence) store row by row.
+// Lane (q, c) holds channels 8c .. 8c+7 of tokens 4q .. 4q+3 of a group in
+// r[0..3]; afterwards it holds those of tokens 4q + d .. 4q + d + 3, the rows
+// of tokens tf + 4q .. tf + 4q + 3 (tf: the group's first token + d).  Rows
+// of the group pass through LDS; those past it are read from `src`.
+__device__ __forceinline__ void shift_rows(u32x4 (&r)[4], const u32x4* __restrict__ src,
+                                           uint8_t* lo, uint8_t* hi, int64_t tf, int hkv,
+                                           int h, int q, int c, int d) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = 4 * q + k;
+    *reinterpret_cast<u32x4*>((t < 8 ? lo : hi) + (t & 7) * 256 + c * 16) = r[k];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = 4 * q + k + d;  // token of the group (t >= 16: of the next group)
+    if (t < kBS)
+      r[k] = *reinterpret_cast<const u32x4*>((t < 8 ? lo : hi) + (t & 7) * 256 + c * 16);
+    else
+      r[k] = __builtin_nontemporal_load(src + ((tf + 4 * q + k) * hkv + h) * 16 + c);
+  }
+  // the reads before the next writes to the same LDS
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave per (group of 16 consecutive tokens of the call, KV head).  Each
+// cache block whose 16 slots the call writes in order, from 16 consecutive
+// tokens, is written by the wave whose group holds the block's first token:
+// it builds the (block, head) tiles in LDS from coalesced loads of the 16
+// rows and stores each tile as one contiguous run (2 KiB FP8 / 4 KiB fp16),
+// so the scattered layout costs no partial-line writes.  In a bulk fill the
+// groups are the blocks; in a batched prefill whose sequences are not
+// multiples of 16 long each block starts inside a group and takes rows from
+// the next.  Tokens of blocks the call only partly writes (a sequence's
+// first and last blocks, a decode step's one token per sequence) are stored
+// row by row by the wave of their own group.
 constexpr int kFillWaves = 4;  // independent waves per workgroup
 
 template <bool kFP8>
-__global__ void __launch_bounds__(kFillWaves * kWave)
+__global__ void __launch_bounds__(kFillWaves * kWave) __attribute__((amdgpu_waves_per_eu(kFP8 ? 4 : 1)))
 reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                          const int64_t* __restrict__ slots, int64_t num_tokens, int hkv,
@@ -127,14 +161,13 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
   const int h = (int)(unit % (unsigned)hkv);
   const int64_t t0 = (int64_t)(unit / (unsigned)hkv) * kBS;
   const int ntok = (int)min<int64_t>(kBS, num_tokens - t0);
-  // FP8: the group's 16 rows are requested with its slots (their addresses
-  // do not depend on the slots), so a whole block -- every group of a bulk
-  // fill -- costs one round trip to memory; each row is read once, past the
-  // caches.  Lane l takes channels 8c .. 8c+7, c = l % 16, of the four tokens
+  // FP8: the group's own 16 rows -- the rows of its block when the group is
+  // one whole block, as in every group of a bulk fill -- are requested with
+  // the slots (their addresses do not depend on the slots), so such a block
+  // costs one round trip to memory; each row is read once, past the caches.
+  // Lane l takes channels 8c .. 8c+7, c = l % 16, of the four tokens
   // 4q .. 4q+3, q = l / 16 (each load instruction reads four whole rows).
-  // The other groups load their rows again below.  fp16 loads them once the
-  // slots are known: its batched prefills mostly take the two-run path, and
-  // the early loads measured slower there.
+  // fp16 loads its rows once the slots are known.
   u32x4 kin[4], vin[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -149,58 +182,53 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
       }
     }
   }
-  const int64_t my_slot = lane < ntok ? slots[t0 + lane] : -1;
-  const int64_t s0 = __shfl(my_slot, 0, kWave);
-  const bool in_order = lane >= kBS || my_slot == s0 + lane;
-  const bool whole = ntok == kBS && s0 >= 0 && (s0 & (kBS - 1)) == 0 && s0 + kBS <= num_slots &&
-                     __all(in_order);
-  if (!whole) {
-    // At most two runs of consecutive slots, each inside one block (the end
-    // of one sequence, then the start of the next, as in a batched prefill
-    // whose lengths are not multiples of 16): write each run by aligned
-    // quads of block offsets, so that every store instruction covers whole
-    // 16-byte runs of the V tile wherever the run holds the quad's 4 tokens.
-    const int64_t prev = __shfl(my_slot, lane > 0 ? lane - 1 : 0, kWave);
-    const bool brk = lane > 0 && lane < ntok && my_slot != prev + 1;
-    const bool ok = lane >= ntok || (my_slot >= 0 && my_slot < num_slots);
-    const uint64_t breaks = __ballot(brk);
-    const int len_a = breaks ? (int)__builtin_ctzll(breaks) : ntok;  // run A: tokens [0, len_a)
-    const int64_t sb = __shfl(my_slot, len_a < kWave ? len_a : 0, kWave);
-    const int off_a = (int)(s0 & (kBS - 1)), off_b = (int)(sb & (kBS - 1));
-    if (__all(ok) && __popcll(breaks) <= 1 && off_a + len_a <= kBS &&
-        (len_a == ntok || off_b + (ntok - len_a) <= kBS)) {
-      for (int r = 0; r < (len_a == ntok ? 1 : 2); ++r) {  // wave-uniform
-        const int tok0 = r == 0 ? 0 : len_a;                // first token of the run
-        const int len = r == 0 ? len_a : ntok - len_a;
-        const int64_t slot0 = r == 0 ? s0 : sb;
-        const int off0 = (int)(slot0 & (kBS - 1));
-        const int64_t tile = (slot0 >> 4) * hkv + h;
-        const int c = lane & 15;
-        for (int q = off0 >> 2; q <= (off0 + len - 1) >> 2; ++q) {
-          const int o = q * 4 + (lane >> 4);                 // block offset of this lane
-          if (o < off0 || o >= off0 + len) continue;
-          const int64_t th = (t0 + tok0 + (o - off0)) * hkv + h;
-          store_rows8<kFP8>(k_pool, v_pool, tile, o, c, key[th * 16 + c], value[th * 16 + c],
-                            k_scale, v_scale);
-        }
-      }
-      return;
-    }
-    // anything else row by row: 16 runs of 8 channels per token
+  // the slots of tokens t0 - 16 .. t0 + 47 (lane l: token t0 - 16 + l); -1
+  // outside the call
+  const int64_t tl = t0 - kBS + lane;
+  const int64_t sl = tl >= 0 && tl < num_tokens ? slots[tl] : -1;
+  const bool valid = sl >= 0 && sl < num_slots;
+  const int64_t s_next = __shfl_down(sl, 1, kWave);
+  // bit l: token l + 1's slot follows token l's
+  const uint64_t follows = __ballot(valid && lane < kWave - 1 && s_next == sl + 1);
+  // bit l: a block starts at token l and the next 15 tokens fill it in order
+  // (its last slot is then inside the pool as well)
+  const uint64_t starts =
+      __ballot(valid && (sl & (kBS - 1)) == 0 && lane <= kWave - kBS &&
+               ((follows >> lane) & 0x7FFFull) == 0x7FFFull);
+  // the group's tokens (lanes 16 .. 16 + ntok - 1) that no such block holds
+  const bool mine = lane >= kBS && lane < kBS + ntok;
+  const uint64_t near = lane >= kBS - 1 ? starts >> (lane - (kBS - 1)) : 0;  // starts l-15 .. l
+  const uint64_t rows = __ballot(mine && valid && (near & 0xFFFFull) == 0);
+  if (rows) {
+    // row by row: 16 runs of 8 channels per token
     for (int i = lane; i < ntok * 16; i += kWave) {
+      if (!((rows >> (kBS + (i >> 4))) & 1)) continue;
       const int64_t tok = t0 + (i >> 4);
       const int c = i & 15;
       const int64_t slot = slots[tok];
-      if (slot < 0 || slot >= num_slots) continue;
       const int64_t th = tok * hkv + h;
       store_rows8<kFP8>(k_pool, v_pool, (slot >> 4) * hkv + h, (int)(slot & 15), c,
                         key[th * 16 + c], value[th * 16 + c], k_scale, v_scale);
     }
-    return;
   }
+  const uint64_t block = starts & (0xFFFFull << kBS);  // at most one start in the group
+  if (!block) return;
+  const int f = (int)__builtin_ctzll(block);
+  const int64_t tf = t0 - kBS + f;                     // the block's first token
+  const int64_t s0 = __shfl(sl, f, kWave);
   // whole block: place every element at its tile position in LDS
   if constexpr (kFP8) {
     const int q = lane >> 4, c = lane & 15;  // tokens 4q .. 4q+3, channels 8c .. 8c+7
+    if (f != kBS) {
+      // The block starts inside the group, d tokens in: its rows are the
+      // group's last 16 - d rows, already loaded, then the next group's
+      // first d.  K, then V, goes through the wave's LDS (rows 0-7 in lk,
+      // 8-15 in lv, 256 bytes each) to move each kept row to the lane that
+      // needs it; only the next group's rows are read from memory.
+      const int d = f - kBS;
+      shift_rows(kin, key, lk, lv, tf, hkv, h, q, c, d);
+      shift_rows(vin, value, lk, lv, tf, hkv, h, q, c, d);
+    }
     const int n = c >> 1, j0 = (c & 1) * 8;
     const Fp8Enc ke = fp8_enc(k_scale), ve = fp8_enc(v_scale);
     uint32_t vc[2][4];  // V codes of channels 8c + 4i .. 8c + 4i + 3 of token 4q + k
@@ -237,7 +265,7 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
       const int i = lane + kWave * j;  // (token, run of 8 channels)
       const int t = i >> 4, c = i & 15;
       const int n = c >> 1, j0 = (c & 1) * 8;
-      const int64_t th = (t0 + t) * hkv + h;
+      const int64_t th = (tf + t) * hkv + h;
       kin[j] = key[th * 16 + c];
       vin[j] = value[th * 16 + c];
       *reinterpret_cast<u32x4*>(lk + (c * 128 + t * 8) * 2) = kin[j];  // K: 16 contiguous bytes

@@ -129,6 +129,31 @@ def test_batched_prefill_of_unaligned_sequences(fp8, hkv):
     assert np.array_equal(kd, kh) and np.array_equal(vd, vh)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_batched_prefill_blocks_start_inside_groups(fp8):
+    """Sequences of 4095 tokens written back to back (the fp16 benchmark's
+    fill): after the first sequence every cache block starts inside a
+    16-token group of the call and takes its last rows from the next group.
+    A skipped token and a slot past the pool inside would-be whole blocks,
+    and a sequence continuing mid-block, send those blocks row by row.
+    Bit-exact against the oracle."""
+    rng = np.random.default_rng(77 + fp8)
+    hkv, nb = 8, 8 * 256 + 8
+    free = list(rng.permutation(nb))
+    slots = []
+    for start, n in [(0, 4095)] * 5 + [(7, 4095 - 7), (0, 4095), (0, 4095)]:
+        blocks = [free.pop() for _ in range(-(-(start + n) // 16))]
+        slots += [blocks[p // 16] * 16 + p % 16 for p in range(start, start + n)]
+    slots = np.asarray(slots, dtype=np.int64)
+    slots[5000] = -1                                 # a skipped token
+    slots[9001] = nb * 16 + 5                        # past the pool: skipped
+    T = slots.size
+    key = workloads.randn_f16((T, hkv, D), 81)
+    value = workloads.randn_f16((T, hkv, D), 82)
+    kd, vd, kh, vh = _write_both(key, value, slots, nb, hkv, fp8, 0.0123, 0.031)
+    assert np.array_equal(kd, kh) and np.array_equal(vd, vh)
+
+
 def test_fp16_write_is_a_raw_copy():
     x = torch.from_numpy(np.arange(65536, dtype=np.uint16).view(np.float16).reshape(256, 2, D)
                          .copy())
