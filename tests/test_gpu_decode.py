@@ -353,6 +353,21 @@ def test_long_partitions_merged_across_waves(fp8):
     assert err <= TOL[fp8]
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("blocks", [(2, 16, 1), (17, 200, 256), (257, 300, 3)])
+def test_merge_paths_by_partition_count(fp8, blocks):
+    """16-token partitions, so a sequence of n blocks has n partials: the
+    merge takes its path from the call's most partitions -- at most 16, 17
+    to 256, beyond 256 -- and every path must merge the shorter sequences
+    of the call too."""
+    wl = _small_workload([16 * n - 5 for n in blocks], hq=16, hkv=2, fp8=fp8, seed=83)
+    wl.partition_size = 16
+    prep = Prepared(wl)
+    err = max_err(prep.gpu_decode(), prep.oracle_decode())
+    _report(f"P=16, {blocks} partitions fp8={fp8}", err, TOL[fp8])
+    assert err <= TOL[fp8]
+
+
 @pytest.mark.parametrize("ps", [0, 256])
 def test_shared_prefix_cache_hint_changes_nothing(ps):
     """The shared-prefix hint only picks a cache policy: bit-identical output
