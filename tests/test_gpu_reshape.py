@@ -154,6 +154,39 @@ def test_batched_prefill_blocks_start_inside_groups(fp8):
     assert np.array_equal(kd, kh) and np.array_equal(vd, vh)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("seed", range(12))
+def test_random_batched_writes(fp8, seed):
+    """Seeded random calls of the tile-building kernel: sequences of random
+    lengths (1 to 120 tokens), each continuing its blocks at a random offset,
+    back to back in one call, with random skipped slots and slots past the
+    pool, 1 or 8 KV heads.  Whole blocks start anywhere in the call's 16-token
+    groups; every other token goes row by row.  Bit-exact against the
+    oracle."""
+    rng = np.random.default_rng(900 + seed + 50 * fp8)
+    hkv = 1 if seed % 3 == 0 else 8
+    nb = 200
+    free = list(rng.permutation(nb))
+    slots = []
+    while len(slots) < 600 and len(free) > 12:
+        start = int(rng.integers(0, 16)) if rng.random() < 0.4 else 0
+        n = int(rng.integers(1, 121))
+        blocks = [free.pop() for _ in range(min(len(free), -(-(start + n) // 16)))]
+        n = min(n, 16 * len(blocks) - start)
+        slots += [blocks[p // 16] * 16 + p % 16 for p in range(start, start + n)]
+    slots = np.asarray(slots, dtype=np.int64)
+    assert slots.size > 512                          # the tile-building kernel
+    skip = rng.random(slots.size) < 0.02
+    slots[skip] = -1
+    past = rng.random(slots.size) < 0.005
+    slots[past] = nb * 16 + rng.integers(0, 64, past.sum())
+    T = slots.size
+    key = workloads.randn_f16((T, hkv, D), 910 + seed)
+    value = workloads.randn_f16((T, hkv, D), 930 + seed)
+    kd, vd, kh, vh = _write_both(key, value, slots, nb, hkv, fp8, 0.0123, 0.031)
+    assert np.array_equal(kd, kh) and np.array_equal(vd, vh)
+
+
 def test_fp16_write_is_a_raw_copy():
     x = torch.from_numpy(np.arange(65536, dtype=np.uint16).view(np.float16).reshape(256, 2, D)
                          .copy())
