@@ -99,6 +99,29 @@ reshape_rows_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ val
 // fills, prefill chunks) the tile-building kernel below.
 constexpr int64_t kRowWriteMaxTokens = 512;
 
+// Largest finite magnitude among 8 fp16 values, as fp16 bits (integer order
+// of non-negative fp16 bit patterns is their numeric order).
+__device__ __forceinline__ uint32_t max_abs_bits8(u32x4 x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = x[i];
+    const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+    if (lo < 0x7C00u) m = max(m, lo);
+    if (hi < 0x7C00u) m = max(m, hi);
+  }
+  return m;
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// A block the call fills whole under per-block scales (the tile-building
+// kernel's dynamic mode) is marked in the write's scratch (bit 31 of its
+// written-offsets word): the MaxAbs and encode launches then leave it alone.
+constexpr uint32_t kWholeBlock = 0x80000000u | 0xFFFFu;
+
 // Lane (q, c) holds channels 8c .. 8c+7 of tokens 4q .. 4q+3 of a group in
 // r[0..3]; afterwards it holds those of tokens 4q + d .. 4q + d + 3, the rows
 // of tokens tf + 4q .. tf + 4q + 3 (tf: the group's first token + d).  Rows
@@ -141,12 +164,22 @@ __device__ __forceinline__ void shift_rows(u32x4 (&r)[4], const u32x4* __restric
 // row by row by the wave of their own group.
 constexpr int kFillWaves = 4;  // independent waves per workgroup
 
-template <bool kFP8>
+// Per-block scales (kDyn): the tiles' scales and the write's written-offsets
+// scratch, where whole blocks are marked.
+struct DynTiles {
+  float* k_bscale;
+  float* v_bscale;
+  uint32_t* written;
+};
+
+template <bool kFP8, bool kDyn = false>
 __global__ void __launch_bounds__(kFillWaves * kWave) __attribute__((amdgpu_waves_per_eu(kFP8 ? 4 : 1)))
 reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                          const int64_t* __restrict__ slots, int64_t num_tokens, int hkv,
-                         int64_t num_slots, float k_scale, float v_scale, uint32_t units) {
+                         int64_t num_slots, float k_scale, float v_scale, uint32_t units,
+                         DynTiles dt) {
+  static_assert(kFP8 || !kDyn, "per-block scales are for FP8 pools");
   constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
   __shared__ __align__(16) uint8_t lk_all[kFillWaves][kTileBytes];
   __shared__ __align__(16) uint8_t lv_all[kFillWaves][kTileBytes];
@@ -199,7 +232,8 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
   const bool mine = lane >= kBS && lane < kBS + ntok;
   const uint64_t near = lane >= kBS - 1 ? starts >> (lane - (kBS - 1)) : 0;  // starts l-15 .. l
   const uint64_t rows = __ballot(mine && valid && (near & 0xFFFFull) == 0);
-  if (rows) {
+  // (with per-block scales the three-launch write takes these tokens)
+  if (!kDyn && rows) {
     // row by row: 16 runs of 8 channels per token
     for (int i = lane; i < ntok * 16; i += kWave) {
       if (!((rows >> (kBS + (i >> 4))) & 1)) continue;
@@ -230,7 +264,36 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
       shift_rows(vin, value, lk, lv, tf, hkv, h, q, c, d);
     }
     const int n = c >> 1, j0 = (c & 1) * 8;
-    const Fp8Enc ke = fp8_enc(k_scale), ve = fp8_enc(v_scale);
+    Fp8Enc ke, ve;
+    if constexpr (kDyn) {
+      // [FP8-128K] §8: the block is fresh (the call writes its offset 0), so
+      // each tile's scale is max(fp32(MaxAbs of its finite values / 448),
+      // 2^-126), as the three-launch write computes it
+      uint32_t km = 0, vm = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        km = max(km, max_abs_bits8(kin[k]));
+        vm = max(vm, max_abs_bits8(vin[k]));
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        km = max(km, (uint32_t)__shfl_xor((int)km, m, kWave));
+        vm = max(vm, (uint32_t)__shfl_xor((int)vm, m, kWave));
+      }
+      const float sk = fmaxf(f16_bits_to_float(km) / 448.0f, 0x1p-126f);
+      const float sv = fmaxf(f16_bits_to_float(vm) / 448.0f, 0x1p-126f);
+      ke = fp8_enc(sk);
+      ve = fp8_enc(sv);
+      if (lane == 0) {
+        const int64_t tile = (s0 >> 4) * hkv + h;
+        dt.k_bscale[tile] = sk;
+        dt.v_bscale[tile] = sv;
+        dt.written[s0 >> 4] = kWholeBlock;  // every head's wave stores the same word
+      }
+    } else {
+      ke = fp8_enc(k_scale);
+      ve = fp8_enc(v_scale);
+    }
     uint32_t vc[2][4];  // V codes of channels 8c + 4i .. 8c + 4i + 3 of token 4q + k
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -328,24 +391,6 @@ __device__ __forceinline__ uint32_t requant_code(uint32_t c, float r) {
   return e4m3_from_f32(e4m3_value(c) * r);
 }
 
-// Largest finite magnitude among 8 fp16 values, as fp16 bits (integer order
-// of non-negative fp16 bit patterns is their numeric order).
-__device__ __forceinline__ uint32_t max_abs_bits8(u32x4 x) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = x[i];
-    const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
-    if (lo < 0x7C00u) m = max(m, lo);
-    if (hi < 0x7C00u) m = max(m, hi);
-  }
-  return m;
-}
-
-__device__ __forceinline__ float f16_bits_to_float(uint32_t b) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-}
-
 __global__ void __launch_bounds__(256)
 dyn_clear_kernel(const int64_t* __restrict__ slots, int64_t total, int per_block,
                  int64_t num_slots, uint32_t* __restrict__ amax, uint32_t* __restrict__ written) {
@@ -376,6 +421,7 @@ dyn_amax_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
   const int h = (int)(th - tok * hkv);
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= num_slots) return;  // the same for all 16 lanes of the row
+  if (written[slot >> 4] & 0x80000000u) return;  // a whole block, already written
   uint32_t km = max_abs_bits8(key[th * 16 + c]);
   uint32_t vm = max_abs_bits8(value[th * 16 + c]);
 #pragma unroll
@@ -440,6 +486,7 @@ dyn_write_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
   const int off = (int)(slot & 15);
   const int64_t tile = blk * hkv + h;
   const uint32_t mask = written[blk];
+  if (mask & 0x80000000u) return;            // a whole block, already written
   const bool fresh = (mask & 1u) != 0;
   const float min_scale = 0x1p-126f;
   const float sk_old = fresh ? 0.0f : k_bscale[tile];
@@ -555,6 +602,35 @@ copy_blocks_kernel(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
 
 // ------------------------------------------------------------------ C ABI
 
+// The tile-building kernel over a call: one workgroup per (16-token group,
+// KV head), in launches of at most 2^24 workgroups.  A block that straddles
+// two launches is written row by row by both.
+template <bool kFP8, bool kDyn>
+static pkv_status launch_fill(const void* key, const void* value, void* k_pool, void* v_pool,
+                              const int64_t* slot_mapping, int32_t num_tokens,
+                              const pkv_cache_layout* layout, float k_scale, float v_scale,
+                              DynTiles dt, hipStream_t s) {
+  const int64_t groups = ((int64_t)num_tokens + kBS - 1) / kBS;
+  const int64_t num_slots = (int64_t)layout->num_blocks * kBS;
+  const int hkv = layout->num_kv_heads;
+  const int64_t max_groups = std::max<int64_t>(1, ((int64_t)1 << 24) / hkv);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    const int64_t tok0 = g0 * kBS;
+    const int64_t ntok = std::min<int64_t>((int64_t)num_tokens - tok0, ng * kBS);
+    const u32x4* kin = static_cast<const u32x4*>(key) + tok0 * hkv * 16;
+    const u32x4* vin = static_cast<const u32x4*>(value) + tok0 * hkv * 16;
+    const uint32_t units = (uint32_t)(ng * hkv);
+    const dim3 grid((units + kFillWaves - 1) / kFillWaves);
+    reshape_and_cache_kernel<kFP8, kDyn><<<grid, dim3(kFillWaves * kWave), 0, s>>>(
+        kin, vin, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+        slot_mapping + tok0, ntok, hkv, num_slots, k_scale, v_scale, units, dt);
+    const pkv_status st = launch_status();
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
 extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
                                             void* v_pool, const int64_t* slot_mapping,
                                             int32_t num_tokens, const pkv_cache_layout* layout,
@@ -571,7 +647,6 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
   if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
                v_scale > 0.0f))
     return PKV_ERR_INVALID_ARG;
-  const int64_t groups = ((int64_t)num_tokens + kBS - 1) / kBS;
   const int64_t num_slots = (int64_t)layout->num_blocks * kBS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -590,30 +665,11 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
           (uint32_t)total, (uint32_t)layout->num_kv_heads, num_slots, 1.0f, 1.0f);
     return launch_status();
   }
-  // one workgroup per (16-token group, KV head), in launches of at most
-  // 2^24 workgroups
-  const int hkv = layout->num_kv_heads;
-  const int64_t max_groups = std::max<int64_t>(1, ((int64_t)1 << 24) / hkv);
-  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
-    const int64_t ng = std::min(max_groups, groups - g0);
-    const int64_t tok0 = g0 * kBS;
-    const int64_t ntok = std::min<int64_t>((int64_t)num_tokens - tok0, ng * kBS);
-    const u32x4* kin = static_cast<const u32x4*>(key) + tok0 * hkv * 16;
-    const u32x4* vin = static_cast<const u32x4*>(value) + tok0 * hkv * 16;
-    const uint32_t units = (uint32_t)(ng * hkv);
-    const dim3 grid((units + kFillWaves - 1) / kFillWaves);
-    if (fp8)
-      reshape_and_cache_kernel<true><<<grid, dim3(kFillWaves * kWave), 0, s>>>(
-          kin, vin, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
-          slot_mapping + tok0, ntok, hkv, num_slots, k_scale, v_scale, units);
-    else
-      reshape_and_cache_kernel<false><<<grid, dim3(kFillWaves * kWave), 0, s>>>(
-          kin, vin, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
-          slot_mapping + tok0, ntok, hkv, num_slots, 1.0f, 1.0f, units);
-    const pkv_status st2 = launch_status();
-    if (st2 != PKV_OK) return st2;
-  }
-  return PKV_OK;
+  if (fp8)
+    return launch_fill<true, false>(key, value, k_pool, v_pool, slot_mapping, num_tokens,
+                                    layout, k_scale, v_scale, DynTiles{}, s);
+  return launch_fill<false, false>(key, value, k_pool, v_pool, slot_mapping, num_tokens,
+                                   layout, 1.0f, 1.0f, DynTiles{}, s);
 }
 
 extern "C" pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const pkv_cache_layout* layout,
@@ -679,6 +735,15 @@ extern "C" pkv_status pkv_reshape_and_cache_dynamic(
   }
   dyn_clear_kernel<<<dim3((unsigned)clear_blocks), dim3(256), 0, s>>>(
       slot_mapping, clear_total, 2 * hkv, num_slots, amax, written);
+  // blocks the call fills whole: tiles, scales and marks in one pass
+  if (num_tokens > kRowWriteMaxTokens) {
+    st = launch_status();
+    if (st != PKV_OK) return st;
+    st = launch_fill<true, true>(key, value, k_pool, v_pool, slot_mapping, num_tokens, layout,
+                                 1.0f, 1.0f, DynTiles{k_block_scales, v_block_scales, written},
+                                 s);
+    if (st != PKV_OK) return st;
+  }
   dyn_amax_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
       static_cast<const u32x4*>(key), static_cast<const u32x4*>(value), slot_mapping, total, hkv,
       num_slots, amax, written);
