@@ -468,12 +468,21 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
 // wave reads the whole tile back in the order the fp16 tile registers hold,
 // so the fp16 arithmetic of process_tile applies unchanged.  Compared with an
 // item per wave, a tile is loaded and converted once instead of four times.
-// kRing tiles' quarters are in flight per wave.  The wave stores its
-// members' partials from registers at the end.
+// The quarters are requested kItemRing tiles ahead, but the loads are
+// conditional, so the wait before a tile is staged covers all of them: an
+// item advances about one memory round trip per tile.  Letting the ring
+// really run ahead (unconditional loads, as in the tails' loop) made the
+// cascade launch slower, 182 against 175.5 us on the shared-prefix batch:
+// the items then take HBM bandwidth from the tails, whose longest streams
+// set the launch's length; a ring of 1 or 2 tiles measured in between.
+// The wave stores its members' partials from registers at the end.
 constexpr int kItemWaves = 4;
 constexpr int kItemRing = 4;
 constexpr int kItemBuf = 8192;  // bytes of one staged fp16 tile
 
+// Quarter w of tile `phys` (K bytes 0-1023, K 1024-2047, V 0-1023, V
+// 1024-2047 for w = 0..3), through the caches; zeros, with the same load
+// instruction and no memory access, when phys is not a pool block.
 __device__ __forceinline__ u32x4 item_quarter(const DecodeArgs& a, int phys, int kvh, int w,
                                               int lane) {
   if ((unsigned)phys >= (unsigned)a.num_blocks) return u32x4{0u, 0u, 0u, 0u};
@@ -575,7 +584,7 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
   // [kNW][CS][D] outputs, then [kNW][16] max and sum, then (kAppend) the
   // newest token's kept bytes, then (kCasc) the item's member per column
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int j = lane & 15;
   const int qg = lane >> 4;
   const int G = a.g;
@@ -701,7 +710,7 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
     if constexpr (kAppend)
       if (c0 == 0 && patch_at >= 0) rows = append_load(a, b, kvh, lane);
     // lane i holds the physical id of this wave's block c0 + i
-    const int tbl = lane < cnt ? trow[(int64_t)(c0 + lane) * kNW] : 0;
+    const int tbl = load_table(trow + (int64_t)c0 * kNW, cnt, kNW, lane);
     const int lb0 = blk0 + w + c0 * kNW;  // logical block of this chunk's tile 0
     // per-block scales: lane i holds block i's K scale and its V scale
     // relative to the wave's reference (the largest V scale so far)
@@ -722,42 +731,56 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
       k_mul = ks;
       v_mul = vs / ref;
     }
-    TileRegs<kFP8> buf[kPD + 1];
+    // Every tile slot issues its loads, past the chunk's end too (a tile
+    // that is not there loads zeros without touching memory), so the waits
+    // for a tile never cover the prefetch issued after it.  The chunk's
+    // tiles take one cache policy: through the caches when all of them are
+    // shared (below shared_blocks), streamed otherwise.
+    auto chunk = [&](auto policy) {
+      constexpr int kAux = decltype(policy)::value;
+      TileRegs<kFP8> buf[kPD + 1];
 #pragma unroll
-    for (int r = 0; r < kPD; ++r)
-      if (r < cnt)
-        load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
-                        __builtin_amdgcn_readlane(tbl, r), kvh, lane,
-                        lb0 + r * kNW < shared_blocks);
-    if constexpr (kAppend)
-      if (c0 == 0 && patch_at >= 0) append_keep<kFP8>(a, rows, lane, keep);
-    for (int base = 0; base < cnt; base += kPD + 1) {
+      for (int r = 0; r < kPD; ++r)
+        load_tile<kFP8, kAux>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                              r < cnt ? __builtin_amdgcn_readlane(tbl, r) : -1, kvh, lane);
+      if constexpr (kAppend)
+        if (c0 == 0 && patch_at >= 0) append_keep<kFP8>(a, rows, lane, keep);
+      for (int base = 0; base < cnt; base += kPD + 1) {
 #pragma unroll
-      for (int r = 0; r <= kPD; ++r) {
-        const int ii = base + r;
-        if (ii < cnt) {
-          if (ii + kPD < cnt)
-            load_tile<kFP8>(buf[(r + kPD) % (kPD + 1)], a.k_pool, a.v_pool, a.num_blocks,
-                            a.hkv, __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane,
-                            lb0 + (ii + kPD) * kNW < shared_blocks);
-          const int tb = (blk0 + w + (c0 + ii) * kNW) * kBS;  // first token of the tile
-          if constexpr (kAppend)
-            if (c0 + ii == patch_at) {
-              const int phys = __builtin_amdgcn_readlane(tbl, ii);
-              if ((unsigned)phys < (unsigned)a.num_blocks) {  // else nothing is written
-                patch_tile<kFP8>(buf[r], keep, lane, (L - 1) & 15);
-                append_store<kFP8>(a, buf[r], phys, kvh, lane, (L - 1) & 15);
+        for (int r = 0; r <= kPD; ++r) {
+          const int ii = base + r;
+          const int nx = ii + kPD;
+          load_tile<kFP8, kAux>(buf[(r + kPD) % (kPD + 1)], a.k_pool, a.v_pool, a.num_blocks,
+                                a.hkv, nx < cnt ? __builtin_amdgcn_readlane(tbl, nx) : -1, kvh,
+                                lane);
+          if (ii < cnt) {
+            const int tb = (blk0 + w + (c0 + ii) * kNW) * kBS;  // first token of the tile
+            if constexpr (kAppend)
+              if (c0 + ii == patch_at) {
+                const int phys = __builtin_amdgcn_readlane(tbl, ii);
+                if ((unsigned)phys < (unsigned)a.num_blocks) {  // else nothing is written
+                  patch_tile<kFP8>(buf[r], keep, lane, (L - 1) & 15);
+                  append_store<kFP8>(a, buf[r], phys, kvh, lane, (L - 1) & 15);
+                }
               }
-            }
-          if constexpr (kDyn)
-            process_tile<kFP8, kHwCvt, kSplitP, true>(
-                buf[r], qop, st, tb, qg, L, a.qk_scale,
-                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k_mul), ii)),
-                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_mul), ii)));
-          else
-            process_tile<kFP8, kHwCvt, kSplitP>(buf[r], qop, st, tb, qg, L, a.qk_scale);
+            if constexpr (kDyn)
+              process_tile<kFP8, kHwCvt, kSplitP, true>(
+                  buf[r], qop, st, tb, qg, L, a.qk_scale,
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k_mul), ii)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_mul), ii)));
+            else
+              process_tile<kFP8, kHwCvt, kSplitP>(buf[r], qop, st, tb, qg, L, a.qk_scale);
+          }
         }
       }
+    };
+    if constexpr (kCasc) {
+      chunk(std::integral_constant<int, kLoadNT>{});  // a tail: the prefix is the items'
+    } else {
+      if (lb0 + (cnt - 1) * kNW < shared_blocks)
+        chunk(std::integral_constant<int, 0>{});
+      else
+        chunk(std::integral_constant<int, kLoadNT>{});
     }
   }
 
@@ -905,7 +928,7 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
   constexpr int kPD = 1;
   __shared__ __align__(16) uint8_t keep[kAppend ? kKeepBytes : 16];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int j = lane & 15;
   const int qg = lane >> 4;
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -960,77 +983,84 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
     u32x2 rows = u32x2{0u, 0u};  // the newest token's rows, ahead of the table load
     if constexpr (kAppend)
       if (c0 == 0 && patch_at >= 0) rows = append_load(a, b, kvh, lane);
-    const int tbl = lane < cnt ? trow[c0 + lane] : 0;
+    const int tbl = load_table(trow + c0, cnt, 1, lane);
     const int lb0 = blk_begin + c0;
-    TileRegs<kFP8> buf[kPD + 1];
+    // unconditional loads and one cache policy per chunk, as in partition_unit
+    auto chunk = [&](auto policy) {
+      constexpr int kAux = decltype(policy)::value;
+      TileRegs<kFP8> buf[kPD + 1];
 #pragma unroll
-    for (int r = 0; r < kPD; ++r)
-      if (r < cnt)
-        load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
-                        __builtin_amdgcn_readlane(tbl, r), kvh, lane, lb0 + r < shared_blocks);
-    if constexpr (kAppend)
-      if (c0 == 0 && patch_at >= 0) append_keep<kFP8>(a, rows, lane, keep);
-    for (int base = 0; base < cnt; base += kPD + 1) {
+      for (int r = 0; r < kPD; ++r)
+        load_tile<kFP8, kAux>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                              r < cnt ? __builtin_amdgcn_readlane(tbl, r) : -1, kvh, lane);
+      if constexpr (kAppend)
+        if (c0 == 0 && patch_at >= 0) append_keep<kFP8>(a, rows, lane, keep);
+      for (int base = 0; base < cnt; base += kPD + 1) {
 #pragma unroll
-      for (int r = 0; r <= kPD; ++r) {
-        const int ii = base + r;
-        if (ii < cnt) {
-          if (ii + kPD < cnt)
-            load_tile<kFP8>(buf[(r + kPD) % (kPD + 1)], a.k_pool, a.v_pool, a.num_blocks,
-                            a.hkv, __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane,
-                            lb0 + ii + kPD < shared_blocks);
-          if constexpr (kAppend)
-            if (c0 + ii == patch_at) {
-              const int phys = __builtin_amdgcn_readlane(tbl, ii);
-              if ((unsigned)phys < (unsigned)a.num_blocks) {  // else nothing is written
-                patch_tile<kFP8>(buf[r], keep, lane, (L - 1) & 15);
-                append_store<kFP8>(a, buf[r], phys, kvh, lane, (L - 1) & 15);
-              }
-            }
-          process_tile<kFP8, true, true>(buf[r], qop, st, (lb0 + ii) * kBS, qg, L, a.qk_scale);
-          if (lb0 + ii + 1 == part_end) {  // wave-uniform: partition `part` is complete
-            float l_run = st.l;
-            l_run += __shfl_xor(l_run, 16, kWave);
-            l_run += __shfl_xor(l_run, 32, kWave);
-            const int64_t hrow = head0 + j;
-            // the G rows of this partition's partial output (not used when single)
-            // (part is wave-uniform; readfirstlane lets the compiler know)
-            const int part_u = __builtin_amdgcn_readfirstlane(part);
-            const __amdgpu_buffer_rsrc_t orows = partial_rows(
-                single ? nullptr : a.ws_o + part_row(a, b, kvh, part_u, 0) * kD, G * kD * 4);
-            if (j < G) {
-              if (single) {
-                float* dst = a.out + hrow * kD + qg * 4;
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                  f32x4 o;
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) o[e] = st.acc[n][e] / l_run * a.out_scale;
-                  *reinterpret_cast<f32x4*>(dst + n * 16) = o;
-                }
-              } else {
-                const int64_t prow = part_row(a, b, kvh, part, j);
-#pragma unroll
-                for (int n = 0; n < 8; ++n)
-                  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st.acc[n]),
-                                                         orows, (j * kD + n * 16 + qg * 4) * 4, 0,
-                                                         kWriteThrough);
-                if (qg == 0) {
-                  a.ws_ml[prow * 2] = st.m_ref;
-                  a.ws_ml[prow * 2 + 1] = l_run;
+        for (int r = 0; r <= kPD; ++r) {
+          const int ii = base + r;
+          const int nx = ii + kPD;
+          load_tile<kFP8, kAux>(buf[(r + kPD) % (kPD + 1)], a.k_pool, a.v_pool, a.num_blocks,
+                                a.hkv, nx < cnt ? __builtin_amdgcn_readlane(tbl, nx) : -1, kvh,
+                                lane);
+          if (ii < cnt) {
+            if constexpr (kAppend)
+              if (c0 + ii == patch_at) {
+                const int phys = __builtin_amdgcn_readlane(tbl, ii);
+                if ((unsigned)phys < (unsigned)a.num_blocks) {  // else nothing is written
+                  patch_tile<kFP8>(buf[r], keep, lane, (L - 1) & 15);
+                  append_store<kFP8>(a, buf[r], phys, kvh, lane, (L - 1) & 15);
                 }
               }
-            }
-            st.m_ref = -INFINITY;
-            st.l = 0.0f;
+            process_tile<kFP8, true, true>(buf[r], qop, st, (lb0 + ii) * kBS, qg, L, a.qk_scale);
+            if (lb0 + ii + 1 == part_end) {  // wave-uniform: partition `part` is complete
+              float l_run = st.l;
+              l_run += __shfl_xor(l_run, 16, kWave);
+              l_run += __shfl_xor(l_run, 32, kWave);
+              const int64_t hrow = head0 + j;
+              // the G rows of this partition's partial output (not used when single)
+              // (part is wave-uniform; readfirstlane lets the compiler know)
+              const int part_u = __builtin_amdgcn_readfirstlane(part);
+              const __amdgpu_buffer_rsrc_t orows = partial_rows(
+                  single ? nullptr : a.ws_o + part_row(a, b, kvh, part_u, 0) * kD, G * kD * 4);
+              if (j < G) {
+                if (single) {
+                  float* dst = a.out + hrow * kD + qg * 4;
 #pragma unroll
-            for (int n = 0; n < 8; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            ++part;
-            part_end = min(sp.nblk, part_end + sp.per);
+                  for (int n = 0; n < 8; ++n) {
+                    f32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = st.acc[n][e] / l_run * a.out_scale;
+                    *reinterpret_cast<f32x4*>(dst + n * 16) = o;
+                  }
+                } else {
+                  const int64_t prow = part_row(a, b, kvh, part, j);
+#pragma unroll
+                  for (int n = 0; n < 8; ++n)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st.acc[n]),
+                                                           orows, (j * kD + n * 16 + qg * 4) * 4, 0,
+                                                           kWriteThrough);
+                  if (qg == 0) {
+                    a.ws_ml[prow * 2] = st.m_ref;
+                    a.ws_ml[prow * 2 + 1] = l_run;
+                  }
+                }
+              }
+              st.m_ref = -INFINITY;
+              st.l = 0.0f;
+#pragma unroll
+              for (int n = 0; n < 8; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+              ++part;
+              part_end = min(sp.nblk, part_end + sp.per);
+            }
           }
         }
       }
-    }
+    };
+    if (lb0 + cnt - 1 < shared_blocks)
+      chunk(std::integral_constant<int, 0>{});
+    else
+      chunk(std::integral_constant<int, kLoadNT>{});
   }
 }
 

@@ -123,7 +123,8 @@ constexpr int kGatherBlocks = 256;
 template <bool kFP8>
 __global__ void __launch_bounds__(4 * kWave) tile_gather_kernel(GatherArgs a) {
   constexpr int kPD = 2;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int kvh = blockIdx.y, b = blockIdx.z;
   int L = a.context_lens[b];
   const int cap = min(a.max_ctx, a.max_blocks * kBS);
@@ -135,25 +136,24 @@ __global__ void __launch_bounds__(4 * kWave) tile_gather_kernel(GatherArgs a) {
   uint32_t acc = 0;
   for (int c0 = 0; c0 < my_n; c0 += kWave) {
     const int cnt = min(kWave, my_n - c0);
-    const int tbl = lane < cnt ? trow[(int64_t)(c0 + lane) * 4] : 0;
+    const int tbl = load_table(trow + (int64_t)c0 * 4, cnt, 4, lane);
+    // every tile slot issues its loads (zeros past the end), as the decode
+    // kernels do, so a wait never covers the loads issued after it
     TileRegs<kFP8> buf[kPD];
 #pragma unroll
     for (int r = 0; r < kPD; ++r)
-      if (r < cnt)
-        load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
-                        __builtin_amdgcn_readlane(tbl, r), kvh, lane, false);
+      load_tile<kFP8, kLoadNT>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                               r < cnt ? __builtin_amdgcn_readlane(tbl, r) : -1, kvh, lane);
     for (int base = 0; base < cnt; base += kPD) {
 #pragma unroll
       for (int r = 0; r < kPD; ++r) {
         const int ii = base + r;
-        if (ii < cnt) {
 #pragma unroll
-          for (int v = 0; v < TileRegs<kFP8>::kVecs; ++v)
-            acc ^= buf[r].k[v].x ^ buf[r].k[v].w ^ buf[r].v[v].y ^ buf[r].v[v].z;
-          if (ii + kPD < cnt)
-            load_tile<kFP8>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
-                            __builtin_amdgcn_readlane(tbl, ii + kPD), kvh, lane, false);
-        }
+        for (int v = 0; v < TileRegs<kFP8>::kVecs; ++v)
+          acc ^= buf[r].k[v].x ^ buf[r].k[v].w ^ buf[r].v[v].y ^ buf[r].v[v].z;
+        const int nx = ii + kPD;
+        load_tile<kFP8, kLoadNT>(buf[r], a.k_pool, a.v_pool, a.num_blocks, a.hkv,
+                                 nx < cnt ? __builtin_amdgcn_readlane(tbl, nx) : -1, kvh, lane);
       }
     }
   }

@@ -52,39 +52,52 @@ struct TileRegs {
   u32x4 v[kVecs];
 };
 
+// A raw buffer resource over `bytes` bytes at `base`.  A load through it
+// that falls past `bytes` (every load when bytes is 0) returns zeros and
+// touches no memory.  The decode loops use this to issue the same loads on
+// every path: the compiler counts outstanding vector memory operations at
+// each control-flow join as the fewest that any incoming path leaves, so a
+// load issued on one path only (a prefetch past the last tile, a block id
+// outside the pool) made every later wait also wait for the loads issued
+// after the one it needed -- the next tile's, which defeated the prefetch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+constexpr int kLoadNT = 2;  // buffer load cache policy: non-temporal (stream past the caches)
+
 // Load one (block, kv head) tile: each lane reads 16 bytes at i * 1 KiB +
-// 16 * lane.  Tiles only this sequence reads are streamed past the caches
-// (non-temporal); tiles of a shared prefix go through them, so the sibling
-// sequences that read the same tile shortly after can hit.
-template <bool kFP8>
+// 16 * lane, with cache policy kAux: tiles only this sequence reads are
+// streamed past the caches (kLoadNT); tiles of a shared prefix go through
+// them (0), so the sibling sequences that read the same tile shortly after
+// can hit.  The policy is a template argument because a branch between two
+// policies is itself a path the compiler may count as issuing no load.  A
+// phys outside [0, num_blocks) -- no tile, or a prefetch past the end --
+// loads zeros, with the same instructions.  phys and kvh are wave-uniform.
+template <bool kFP8, int kAux>
 __device__ __forceinline__ void load_tile(TileRegs<kFP8>& r, const uint8_t* k_pool,
                                           const uint8_t* v_pool, int num_blocks, int hkv,
-                                          int phys, int kvh, int lane, bool cached) {
+                                          int phys, int kvh, int lane) {
   constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
-  if ((unsigned)phys < (unsigned)num_blocks) {
-    const int64_t off = ((int64_t)phys * hkv + kvh) * kTileBytes;
-    const u32x4* kt = reinterpret_cast<const u32x4*>(k_pool + off);
-    const u32x4* vt = reinterpret_cast<const u32x4*>(v_pool + off);
-    if (cached) {
+  // uniform by contract; said so, the resources stay scalar
+  phys = __builtin_amdgcn_readfirstlane(phys);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  const bool ok = (unsigned)phys < (unsigned)num_blocks;
+  const int64_t off = ok ? ((int64_t)phys * hkv + kvh) * kTileBytes : 0;
+  const __amdgpu_buffer_rsrc_t kr = byte_range(k_pool + off, ok ? kTileBytes : 0);
+  const __amdgpu_buffer_rsrc_t vr = byte_range(v_pool + off, ok ? kTileBytes : 0);
 #pragma unroll
-      for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
-        r.k[i] = kt[i * kWave + lane];
-        r.v[i] = vt[i * kWave + lane];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
-        r.k[i] = __builtin_nontemporal_load(kt + i * kWave + lane);
-        r.v[i] = __builtin_nontemporal_load(vt + i * kWave + lane);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
-      r.k[i] = u32x4{0, 0, 0, 0};
-      r.v[i] = u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
+    r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, (i * kWave + lane) * 16, 0, kAux);
+    r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, (i * kWave + lane) * 16, 0, kAux);
   }
+}
+
+// Entries [first, first + n * stride) of a block-table row, lane i taking
+// entry first + i * stride (i < n <= 64); lanes past n read 0.
+__device__ __forceinline__ int load_table(const int32_t* first, int n, int stride, int lane) {
+  const __amdgpu_buffer_rsrc_t tr = byte_range(first, n > 0 ? ((n - 1) * stride + 1) * 4 : 0);
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(tr, lane * stride * 4, 0, 0);
 }
 
 // FP8 dequantisation of four codes (one dword) to fp16.  Two exact ways:
