@@ -911,28 +911,43 @@ decode_partition_kernel(DecodeArgs a) {
 // launching one workgroup per partition leaves each wave a stream of a few
 // tiles, and the stream drains at every partition end.  Here each wave owns
 // `chain` consecutive partitions of one (sequence, KV head) instead -- a
-// contiguous run of logical blocks -- and streams them back to back; at the
-// end of each partition it stores that partition's (max, sum, unnormalised
-// output) straight from registers, so there is no LDS merge and no barrier.
-// The partials, and the merge kernel that combines them, are the same as
-// with one workgroup per partition.  Per-tensor scales only: with per-block
-// scales the extra registers spill and one workgroup per partition is faster.
-// Grid (ceil(n_p_max / (kChainWaves * chain)), Hkv, B); kChainWaves waves per
-// workgroup, each independent of the others.  kAppend: the kernel also
-// writes each sequence's newest token (steps 1-3 above).
-constexpr int kChainWaves = 4;
+// contiguous run of logical blocks -- and streams them back to back.  At the
+// end of each partition it puts that partition's (max, sum, unnormalised
+// output) into its own LDS staging area, and when the run ends it stores the
+// run's partials together: they are adjacent rows of the workspace, so the
+// wave writes one contiguous span.  Storing each partial when its partition
+// ends cost the 128K-context batch at 512-token partitions 184 against 170
+// us: a wave's vector memory operations complete in order for its wait
+// counts, so the wait for the next tile, whose loads were issued after the
+// stores, waited for the stores too.  The partials, and the merge kernel
+// that combines them, are the same as with one workgroup per partition.
+// Per-tensor scales only: with per-block scales the extra registers spill
+// and one workgroup per partition is faster.  Grid (ceil(n_p_max /
+// (kChainWaves * chain)), Hkv, B); kChainWaves waves per workgroup, each
+// independent of the others; chain_lds_bytes of dynamic LDS.  kAppend: the
+// kernel also writes each sequence's newest token (steps 1-3 above).
+constexpr int kChainWaves = 2;
+constexpr size_t kChainLdsMax = 65536;
+
+// LDS staging of the chained kernel: [kChainWaves][chain][G][kD] outputs,
+// then [kChainWaves][chain][G] (max, sum) pairs.
+static inline size_t chain_lds_bytes(int chain, int g) {
+  return (size_t)kChainWaves * chain * g * (kD + 2) * sizeof(float);
+}
 
 template <bool kFP8, bool kAppend = false>
 __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(DecodeArgs a,
                                                                            int chain) {
   constexpr int kPD = 1;
   __shared__ __align__(16) uint8_t keep[kAppend ? kKeepBytes : 16];
+  extern __shared__ __align__(16) float stage[];  // chain_lds_bytes(chain, G)
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int j = lane & 15;
   const int qg = lane >> 4;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.g;
+  float2* ml_stage = reinterpret_cast<float2*>(stage + kChainWaves * chain * G * kD);
 
   const int L = clamp_len(a, b);
   const SeqSplit sp = seq_split(a, L);
@@ -1018,11 +1033,6 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
               l_run += __shfl_xor(l_run, 16, kWave);
               l_run += __shfl_xor(l_run, 32, kWave);
               const int64_t hrow = head0 + j;
-              // the G rows of this partition's partial output (not used when single)
-              // (part is wave-uniform; readfirstlane lets the compiler know)
-              const int part_u = __builtin_amdgcn_readfirstlane(part);
-              const __amdgpu_buffer_rsrc_t orows = partial_rows(
-                  single ? nullptr : a.ws_o + part_row(a, b, kvh, part_u, 0) * kD, G * kD * 4);
               if (j < G) {
                 if (single) {
                   float* dst = a.out + hrow * kD + qg * 4;
@@ -1034,16 +1044,11 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
                     *reinterpret_cast<f32x4*>(dst + n * 16) = o;
                   }
                 } else {
-                  const int64_t prow = part_row(a, b, kvh, part, j);
+                  const int k = (w * chain + part - p_first) * G + j;  // staged row
 #pragma unroll
                   for (int n = 0; n < 8; ++n)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st.acc[n]),
-                                                           orows, (j * kD + n * 16 + qg * 4) * 4, 0,
-                                                           kWriteThrough);
-                  if (qg == 0) {
-                    a.ws_ml[prow * 2] = st.m_ref;
-                    a.ws_ml[prow * 2 + 1] = l_run;
-                  }
+                    *reinterpret_cast<f32x4*>(stage + k * kD + n * 16 + qg * 4) = st.acc[n];
+                  if (qg == 0) ml_stage[k] = make_float2(st.m_ref, l_run);
                 }
               }
               st.m_ref = -INFINITY;
@@ -1061,6 +1066,22 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
       chunk(std::integral_constant<int, 0>{});
     else
       chunk(std::integral_constant<int, kLoadNT>{});
+  }
+  if (!single) {
+    // the run's partials: rows part_row(b, kvh, p_first, 0) onward, adjacent
+    // in the workspace; lanes read rows other lanes staged (one wave)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int rows = __builtin_amdgcn_readfirstlane((part - p_first) * G);
+    const int64_t row0 = part_row(a, b, kvh, p_first, 0);
+    const __amdgpu_buffer_rsrc_t run = partial_rows(a.ws_o + row0 * kD, rows * kD * 4);
+    const float* src = stage + w * chain * G * kD;
+    for (int i = lane * 4; i < rows * kD; i += kWave * 4)
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src + i), run, i * 4,
+                                             0, kWriteThrough);
+    for (int i = lane; i < rows; i += kWave)
+      reinterpret_cast<float2*>(a.ws_ml)[row0 + i] = ml_stage[w * chain * G + i];
   }
 }
 
@@ -1586,11 +1607,17 @@ static int chain_for(const DecodePlan& pl, int32_t num_seqs) {
   const KernelConfig& c = pl.cfg;
   if (c.chain == 0 || pl.a.n_p_max <= 1 || pl.dyn) return 0;
   if (pl.fp8 && !(c.hw_cvt && c.split_p_fp8)) return 0;
-  if (c.chain > 0) return c.chain;
+  if (c.chain > 0) {  // explicit, down to what the LDS staging holds
+    int chain = c.chain;
+    while (chain > 1 && chain_lds_bytes(chain, pl.a.g) > kChainLdsMax) chain /= 2;
+    return chain;
+  }
   const int64_t pairs = (int64_t)num_seqs * pl.a.hkv;
   if (c.prefetch != 1 || c.waves != 0 || pl.a.part_blocks > 64 || pairs >= 1024) return 0;
   int chain = std::max(1, 128 / pl.a.part_blocks);
-  while (chain > 1 && pairs * ((pl.a.n_p_max + chain - 1) / chain) < 2048) chain /= 2;
+  while (chain > 1 && (pairs * ((pl.a.n_p_max + chain - 1) / chain) < 2048 ||
+                       chain_lds_bytes(chain, pl.a.g) > kChainLdsMax))
+    chain /= 2;
   // one partition per wave is fewer waves than a workgroup per partition
   // gives (measured: 64 x 2 KV heads x 8193 tokens at 1024-token partitions,
   // 59.6 us against 53.8 us)
@@ -1602,7 +1629,8 @@ static void launch_chain(int chain, int32_t num_seqs, hipStream_t s, const Decod
   const int per_wg = kChainWaves * chain;
   const dim3 grid((unsigned)((a.n_p_max + per_wg - 1) / per_wg), (unsigned)a.hkv,
                   (unsigned)num_seqs);
-  decode_chain_kernel<kFP8, kAppend><<<grid, dim3(kChainWaves * kWave), 0, s>>>(a, chain);
+  decode_chain_kernel<kFP8, kAppend>
+      <<<grid, dim3(kChainWaves * kWave), chain_lds_bytes(chain, a.g), s>>>(a, chain);
 }
 
 // The newest token alone, one wave per (KV head, sequence), for the kernel
