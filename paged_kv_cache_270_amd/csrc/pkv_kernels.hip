@@ -700,10 +700,13 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
     patch_at = __builtin_amdgcn_readfirstlane(patch_at);
   }
 
-  // logical blocks below shared_blocks are read by other sequences or items
-  // too (cache hint)
-  for (int c0 = 0; c0 < my_n; c0 += kWave) {
-    const int cnt = min(kWave, my_n - c0);
+  // Logical blocks below shared_blocks are read by other sequences or items
+  // too (cache hint).  A chunk ends where this wave's shared tiles end, so
+  // each chunk takes one cache policy.
+  const int n_sh = min(my_n, max(0, shared_blocks - blk0 - w + kNW - 1) / kNW);
+  int cnt = 0;
+  for (int c0 = 0; c0 < my_n; c0 += cnt) {
+    cnt = min(kWave, (c0 < n_sh ? n_sh : my_n) - c0);
     // the newest token's rows, issued ahead of the table load whose wait
     // then covers them too
     u32x2 rows = u32x2{0u, 0u};
@@ -774,7 +777,7 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
         }
       }
     };
-    if constexpr (kCasc) {
+    if constexpr (kSharedItem) {
       chunk(std::integral_constant<int, kLoadNT>{});  // a tail: the prefix is the items'
     } else {
       if (lb0 + (cnt - 1) * kNW < shared_blocks)
@@ -853,10 +856,11 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
   }
 }
 
-// With per-block scales the kernel is held to 128 VGPRs (4 waves per SIMD);
-// the compiler fits it without spilling.  The FP8 cascade variants are held
-// to 168 (3 waves per SIMD): the loop over units of the flat grid otherwise
-// grows them past it.
+// With per-block scales, and for the FP8 cascade, the kernel is held to 168
+// VGPRs (3 waves per SIMD).  The per-block-scale variant fits in about 150
+// without spilling; held to 128 (4 waves), it spilled once the next tile's
+// loads stayed in flight across the current tile's arithmetic.  The cascade's
+// loop over units of the flat grid otherwise grows it past 168.
 // Decode partition kernel: one unit per workgroup, grid (n_p_max, Hkv, B) or
 // (n_p_max, Hkv, items + B) for the cascade; or, with the cascade's flat
 // grid, Hkv * n workgroups, KV head fastest: workgroup i takes unit i / Hkv
@@ -865,7 +869,7 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
 template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false,
           bool kAppend = false, bool kCasc = false>
 __global__ void __launch_bounds__(kNW * kWave)
-__attribute__((amdgpu_waves_per_eu(kDyn ? (kCasc ? 3 : 4) : (kCasc && kFP8 ? 3 : 1))))
+__attribute__((amdgpu_waves_per_eu(kDyn || (kCasc && kFP8) ? 3 : 1)))
 decode_partition_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   if constexpr (kCasc) {
@@ -993,8 +997,11 @@ __global__ void __launch_bounds__(kChainWaves * kWave) decode_chain_kernel(Decod
   int part_end = min(sp.nblk, (part + 1) * sp.per);     // its first block past the end
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk_begin;
   const int shared_blocks = a.shared_prefix != nullptr ? a.shared_prefix[b] : 0;
-  for (int c0 = 0; c0 < my_n; c0 += kWave) {
-    const int cnt = min(kWave, my_n - c0);
+  // chunks end where the shared tiles end, as in partition_unit
+  const int n_sh = min(my_n, max(0, shared_blocks - blk_begin));
+  int cnt = 0;
+  for (int c0 = 0; c0 < my_n; c0 += cnt) {
+    cnt = min(kWave, (c0 < n_sh ? n_sh : my_n) - c0);
     u32x2 rows = u32x2{0u, 0u};  // the newest token's rows, ahead of the table load
     if constexpr (kAppend)
       if (c0 == 0 && patch_at >= 0) rows = append_load(a, b, kvh, lane);
