@@ -92,6 +92,29 @@ def read_probe(mib: int) -> int:
     return 0
 
 
+SETTLE_MS = 60.0
+
+
+def settle(fn, min_ms: float = SETTLE_MS) -> int:
+    """Untimed calls of `fn`, in batches of 8, until at least `min_ms` of GPU
+    time has passed; returns how many ran.  Run before the W warmup steps:
+    after the setup's idle gaps the part takes some milliseconds to come back
+    to full speed, longer than a few warmup steps last (the 70B FP8 step
+    measured 168-171 us after 10 warmup steps, 163.5-163.8 us after 200)."""
+    import torch
+    n, spent = 0, 0.0
+    while spent < min_ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(8):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        spent += a.elapsed_time(b)
+        n += 8
+    return n
+
+
 def timed_launches(fn, reps: int, warmup: int = 3) -> float:
     """Milliseconds per call of `fn` over `reps` back-to-back calls between two
     events on the current stream (nothing else in between)."""
@@ -269,6 +292,7 @@ def run_prefill(args) -> int:
         write(new_k, new_v, d_chunk)
         attention()
 
+    settle_steps = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -332,6 +356,7 @@ def run_prefill(args) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -643,6 +668,7 @@ def main() -> int:
         torch.cuda.synchronize()
         return start.elapsed_time(end) / args.steps
 
+    settle_steps = settle(step)
     for _ in range(args.warmup):
         step()
     # optionally the step as one HIP graph (write, partitions, merge),
@@ -782,6 +808,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(step_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -1202,6 +1202,97 @@ __global__ void __launch_bounds__(kRW * kWave) decode_reduce_kernel(DecodeArgs a
   }
 }
 
+// Merge of up to kFewPartitions partitions, one wave per (sequence, KV
+// head): the G query heads of a group share the sequence's partition count,
+// and their partial rows are adjacent in the workspace (partition p's G
+// rows, then partition p + 1's).  Lane l serves head g = l / kLH of the
+// group and, in each of its rows, the 16-byte pieces sub, sub + kLH, ...
+// (kLH lanes a head: 64 / G rounded up to a power of two, at most 32).  The
+// sequence's length, the (max, sum) pairs of every partition the workspace
+// holds and the first kChunk partitions' rows are requested at once, so a
+// sequence of at most kChunk partitions costs one round trip to memory;
+// rows past the sequence's own partition count are dropped by selection
+// (never multiplied: a stale row may hold anything).  Partitions are summed
+// in order, so results do not depend on timing.  One wave per row (the
+// decode_reduce_kernel<false> layout) leaves 16,384 short waves for a
+// 256-sequence batch, 13 us under the profiler, most of it waves waiting for
+// a slot.
+// The group merge is used from this many (sequence, KV head) groups on: at
+// 128 groups (one GPU's share of a 4-way tensor-parallel 70B step) its 128
+// waves took longer than the per-row kernel's 1,024 (step 49.4-49.6 against
+// 48.7-49.2 us); at 2,048 (the 256-sequence batch) it saved 1.5 us.
+constexpr int64_t kGroupMergeMin = 1024;
+
+template <int kV>  // 16-byte pieces a lane takes of each row: 32 / kLH
+__global__ void __launch_bounds__(kRW * kWave) decode_reduce_group_kernel(DecodeArgs a,
+                                                                          int64_t groups) {
+  constexpr int kLH = 32 / kV;
+  constexpr int kChunk = kFewPartitions / kV;  // partitions whose rows are in flight at once
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t bk = (int64_t)blockIdx.x * kRW + w;  // (sequence, KV head)
+  if (bk >= groups) return;                          // whole waves leave
+  const int b = (int)(bk / a.hkv);
+  const int kvh = (int)(bk - (int64_t)b * a.hkv);
+  const int G = a.g;
+  const int g = lane / kLH, sub = lane - g * kLH;
+  const bool head = g < G;
+  const int npm = a.n_p_max;  // >= 2: the merge runs only then
+  const int64_t row0 = part_row(a, b, kvh, 0, 0) + g;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row0;
+  const f32x4* orow = reinterpret_cast<const f32x4*>(a.ws_o + row0 * kD) + sub;
+  const int64_t pst = (int64_t)G * (kD / 4);  // f32x4 steps from one partition to the next
+
+  float2 mlp[kFewPartitions];
+#pragma unroll
+  for (int p = 0; p < kFewPartitions; ++p)
+    mlp[p] = head && p < npm ? ml[p * G] : make_float2(-INFINITY, 0.0f);
+  f32x4 o[kChunk][kV];
+#pragma unroll
+  for (int p = 0; p < kChunk; ++p)
+#pragma unroll
+    for (int v = 0; v < kV; ++v)
+      o[p][v] = head && p < npm ? orow[p * pst + v * kLH] : f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n_p = seq_parts(a, b, clamp_len(a, b));
+  if (n_p <= 1) return;  // written by the partition kernel (uniform)
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kFewPartitions; ++p)
+    if (p < n_p) mx = fmaxf(mx, mlp[p].x);
+  float wgt[kFewPartitions];
+  float den = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kFewPartitions; ++p) {
+    wgt[p] = p < n_p ? __builtin_amdgcn_exp2f(mlp[p].x - mx) : 0.0f;
+    if (p < n_p) den += mlp[p].y * wgt[p];
+  }
+  f32x4 acc[kV];
+#pragma unroll
+  for (int v = 0; v < kV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kFewPartitions; c += kChunk) {
+    if (c >= n_p) break;  // uniform
+    if (c > 0) {          // a further chunk: one more round trip
+#pragma unroll
+      for (int p = 0; p < kChunk; ++p)
+#pragma unroll
+        for (int v = 0; v < kV; ++v)
+          o[p][v] = head && c + p < n_p ? orow[(c + p) * pst + v * kLH]
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int p = 0; p < kChunk; ++p)
+      if (c + p < n_p)
+#pragma unroll
+        for (int v = 0; v < kV; ++v) acc[v] += o[p][v] * wgt[c + p];
+  }
+  if (head) {
+    f32x4* dst = reinterpret_cast<f32x4*>(a.out + ((int64_t)b * a.hq + kvh * G + g) * kD) + sub;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) dst[v * kLH] = acc[v] * (a.out_scale / den);
+  }
+}
+
 // Merge of sequences with more partitions than one launch of the kMany
 // kernel takes (n_p_max > kManyPartitions): one workgroup of four waves per
 // (b, h), chunks of kManyPartitions partitions, the same arithmetic in the
@@ -1729,9 +1820,24 @@ static pkv_status run_reduce(const DecodePlan& pl, int32_t num_seqs, hipStream_t
     decode_reduce_long_kernel<<<dim3((unsigned)rows), dim3(kRW * kWave), 0, s>>>(pl.a, rows);
   } else if (pl.a.n_p_max > kFewPartitions) {
     decode_reduce_kernel<true><<<dim3((unsigned)rows), dim3(kRW * kWave), 0, s>>>(pl.a, rows);
-  } else {
+  } else if ((int64_t)num_seqs * pl.a.hkv < kGroupMergeMin) {
+    // few groups: a wave per (sequence, query head) keeps more waves busy
     const int64_t grid = (rows + kRW - 1) / kRW;
     decode_reduce_kernel<false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(pl.a, rows);
+  } else {
+    // one wave per (sequence, KV head); lanes a head: 64 / G rounded up to
+    // a power of two, at most 32
+    const int64_t groups = (int64_t)num_seqs * pl.a.hkv;
+    const dim3 grid((unsigned)((groups + kRW - 1) / kRW));
+    const int g = pl.a.g;
+    if (g <= 2)
+      decode_reduce_group_kernel<1><<<grid, dim3(kRW * kWave), 0, s>>>(pl.a, groups);
+    else if (g <= 4)
+      decode_reduce_group_kernel<2><<<grid, dim3(kRW * kWave), 0, s>>>(pl.a, groups);
+    else if (g <= 8)
+      decode_reduce_group_kernel<4><<<grid, dim3(kRW * kWave), 0, s>>>(pl.a, groups);
+    else
+      decode_reduce_group_kernel<8><<<grid, dim3(kRW * kWave), 0, s>>>(pl.a, groups);
   }
   return launch_status();
 }

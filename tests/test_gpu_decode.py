@@ -368,6 +368,26 @@ def test_merge_paths_by_partition_count(fp8, blocks):
     assert err <= TOL[fp8]
 
 
+@pytest.mark.parametrize("hq", [8, 24, 64, 128])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_group_merge(fp8, hq):
+    """From 1024 (sequence, KV head) groups on, the merge gives each group one
+    wave, a head's lanes being 64 / G rounded up to a power of two.  G = 1,
+    3, 8 and 16 query heads per KV head, over 128 sequences and 8 KV heads.
+    16-token partitions give a sequence of n blocks n partials, 1 to 16 of
+    them: more than each G's rows in flight at once.  Empty and one-token
+    sequences are included."""
+    rng = np.random.default_rng(1000 + hq)
+    lens = rng.integers(0, 257, 128)
+    lens[:4] = [0, 1, 256, 17]
+    wl = _small_workload(lens, hq=hq, hkv=8, fp8=fp8, seed=91)
+    wl.partition_size = 16
+    prep = Prepared(wl)
+    err = max_err(prep.gpu_decode(), prep.oracle_decode())
+    _report(f"group merge G={hq // 8} fp8={fp8}", err, TOL[fp8])
+    assert err <= TOL[fp8]
+
+
 @pytest.mark.parametrize("ps", [0, 256])
 def test_shared_prefix_cache_hint_changes_nothing(ps):
     """The shared-prefix hint only picks a cache policy: bit-identical output
