@@ -495,6 +495,9 @@ def main() -> int:
     ap.add_argument("--cpu-sample-seqs", type=int, default=16,
                     help="sequences of the workload the CPU oracle baseline decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tail-map", choices=("on", "off"), default="on",
+                    help="cascade: pass the host pool's list of tail units (on) or let "
+                         "each workgroup find its unit by a scan over the lengths (off)")
     ap.add_argument("--cascade", choices=("auto", "on", "off"), default="auto",
                     help="decode each group's shared prefix once for the group "
                          "(pkv_paged_attention_decode_cascade[_dynamic]); auto = when the "
@@ -587,8 +590,14 @@ def main() -> int:
         d_prefix = torch.from_numpy(prefix).to(dev)
         d_groups = torch.from_numpy(garr).to(dev) if garr.shape[0] else None
         d_order = torch.from_numpy(order).to(dev)   # longest tails first
-        # the tail work the launch holds, counted by the pool from its lengths
+        # the tail work the launch holds, counted by the pool from its lengths,
+        # and (by default) the list of those units, so that no workgroup
+        # searches the batch for its own
         tail_units = pool.cascade_tail_units(seqs, prefix, max_pre, P)
+        d_tail_map = None
+        if args.tail_map == "on":
+            d_tail_map = torch.from_numpy(
+                pool.cascade_tail_map(seqs, prefix, max_pre, P, order)).to(dev)
         ws_bytes = pkv.pkv_decode_cascade_workspace_bytes(B, Hq, Hkv, Lmax, max_pre,
                                                           layout.dtype, P)
     else:
@@ -637,7 +646,8 @@ def main() -> int:
                 pkv.pkv_paged_attention_decode_cascade_dynamic(
                     out, q, k_pool, v_pool, k_bs, v_bs, d_tables, d_lens, Lmax, layout, sm_scale,
                     d_prefix, d_groups, max_pre, P, ws, shared_prefix_blocks=d_shared,
-                    seq_order=d_order, tail_units=tail_units)
+                    seq_order=d_order, tail_units=tail_units,
+                    tail_map=d_tail_map)
             else:
                 pkv.pkv_paged_attention_decode_dynamic(out, q, k_pool, v_pool, k_bs, v_bs,
                                                        d_tables, d_lens, Lmax, layout, sm_scale,
@@ -649,7 +659,8 @@ def main() -> int:
             pkv.pkv_paged_attention_decode_cascade(
                 out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens, Lmax, layout, sm_scale,
                 d_prefix, d_groups, max_pre, k_scale, v_scale, P, ws,
-                shared_prefix_blocks=d_shared, seq_order=d_order, tail_units=tail_units)
+                shared_prefix_blocks=d_shared, seq_order=d_order, tail_units=tail_units,
+                tail_map=d_tail_map)
             return
         # the newest token of each sequence (position L - 1, the slot
         # pool.append gave it) is written by the partition kernel itself
@@ -698,7 +709,8 @@ def main() -> int:
                 pkv.pkv_paged_attention_decode_cascade_dynamic(
                     out, q, k_pool, v_pool, k_bs, v_bs, d_tables, d_lens, Lmax, layout,
                     sm_scale, d_prefix, d_groups, max_pre, P, ws, shared_prefix_blocks=d_shared,
-                    seq_order=d_order, tail_units=tail_units)
+                    seq_order=d_order, tail_units=tail_units,
+                    tail_map=d_tail_map)
             part_covers = "partition + merge kernels (the cascade decode call)"
         elif dyn:
             def kernel_only():
@@ -712,7 +724,8 @@ def main() -> int:
                 pkv.pkv_paged_attention_decode_cascade(
                     out, q, new_k, new_v, k_pool, v_pool, d_tables, d_lens, Lmax, layout,
                     sm_scale, d_prefix, d_groups, max_pre, k_scale, v_scale, P, ws,
-                    shared_prefix_blocks=d_shared, seq_order=d_order, tail_units=tail_units)
+                    shared_prefix_blocks=d_shared, seq_order=d_order, tail_units=tail_units,
+                tail_map=d_tail_map)
             part_covers = "partition + merge kernels (the cascade call)"
         else:
             def kernel_only():
@@ -827,7 +840,8 @@ def main() -> int:
                    "new_token_write": "separate launch" if dyn else "in the decode kernel",
                    "decode": ("cascade: each shared prefix once per group "
                               f"({garr.shape[0]} groups, {max_pre} prefix blocks, "
-                              f"{tail_units} tail units)")
+                              f"{tail_units} tail units"
+                              f"{', listed by the host' if args.tail_map == 'on' else ''})")
                    if cascade else "per sequence"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tok_per_s": round(tokens / (step_ms * 1e-3), 1),

@@ -349,6 +349,19 @@ pkv_status pkv_paged_attention_decode_append_noalloc(
  *                  smaller one makes workgroups take several units, a larger
  *                  one leaves some idle); 0 launches an upper bound derived
  *                  from max_context_len.
+ *   tail_map       optional device int32 [tail_units][2], 8-byte aligned:
+ *                  the (batch index, tail partition) of every tail unit in
+ *                  schedule order, as pkv_pool_cascade_tail_map writes it
+ *                  for this batch, order and partition size; tail_units is
+ *                  then its length (INVALID_ARG if 0).  With it, a
+ *                  workgroup finds its tail unit with one load instead of a
+ *                  scan over the lengths (two dependent round trips to
+ *                  memory).  NULL = the scan.  An entry outside the batch or
+ *                  with a negative partition is skipped; a map that does not
+ *                  list every tail partition gives unspecified output for
+ *                  those sequences (no memory outside the arguments is
+ *                  touched).  Used with batches of at most 4096 sequences
+ *                  (larger ones need no unit search).
  *   key, value     the newest tokens' rows as in
  *                  pkv_paged_attention_decode_append, written in the same
  *                  launch; both null = decode only.
@@ -364,10 +377,10 @@ pkv_status pkv_paged_attention_decode_cascade(
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
     const int32_t* shared_prefix_blocks, const int32_t* prefix_blocks,
     const int32_t* prefix_groups, int32_t num_groups, int32_t group_cap,
-    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units, int32_t num_seqs,
-    int32_t num_q_heads, int32_t max_context_len, const pkv_cache_layout* layout,
-    float sm_scale, float k_scale, float v_scale, int32_t partition_size, void* workspace,
-    uint64_t workspace_bytes, void* stream);
+    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units,
+    const int32_t* tail_map, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const pkv_cache_layout* layout, float sm_scale, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* The cascade over a cache with per-(block, KV head) FP8 scales (the
  * decode of pkv_paged_attention_decode_dynamic, with the prefix groups,
@@ -381,7 +394,7 @@ pkv_status pkv_paged_attention_decode_cascade_dynamic(
     int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* shared_prefix_blocks,
     const int32_t* prefix_blocks, const int32_t* prefix_groups, int32_t num_groups,
     int32_t group_cap, int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units,
-    int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const int32_t* tail_map, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
     const pkv_cache_layout* layout, float sm_scale, int32_t partition_size, void* workspace,
     uint64_t workspace_bytes, void* stream);
 
@@ -575,6 +588,24 @@ pkv_status pkv_pool_cascade_tail_units(const pkv_pool* pool, const int32_t* seqs
                                        const int32_t* prefix_blocks,
                                        int32_t max_prefix_blocks, int32_t partition_size,
                                        int64_t* units_out);
+/* The tail_map argument of pkv_paged_attention_decode_cascade: the tail
+ * units pkv_pool_cascade_tail_units counts, listed in the decode's schedule
+ * order.  For each batch index b in order[0..n) (0..n-1 when order is NULL),
+ * its tail partitions 0 .. max(1, ceil((ceil(L / 16) - S) / (P / 16))) - 1
+ * as pairs (b, partition), L and S as for pkv_pool_cascade_tail_units.
+ *   prefix_blocks  host int32 [n], max_prefix_blocks: as returned by
+ *                  pkv_pool_prefix_groups for seqs;
+ *   order          host int32 [n] or NULL: the seq_order the decode gets (a
+ *                  permutation of 0..n-1);
+ *   map_out        host int32 [map_cap][2];
+ *   *units_out     the units listed (the decode's tail_units).
+ * BAD_HANDLE for an unknown sequence; INVALID_ARG for bad sizes, an order
+ * entry outside [0, n), or more units than map_cap (nothing is written
+ * past map_cap). */
+pkv_status pkv_pool_cascade_tail_map(const pkv_pool* pool, const int32_t* seqs, int32_t n,
+                                     const int32_t* prefix_blocks, int32_t max_prefix_blocks,
+                                     int32_t partition_size, const int32_t* order,
+                                     int32_t* map_out, int64_t map_cap, int64_t* units_out);
 /* Release a sequence: each of its blocks loses one reference; at zero it
  * returns to the free list, or becomes evictable if the prefix cache holds it
  * ([GLOSSARY] §4.02: pages of a cancelled request go back to the pool at once,

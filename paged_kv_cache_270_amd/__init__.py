@@ -108,12 +108,14 @@ def load_library():
         "pkv_paged_attention_decode_append_noalloc": ([P, P, P, P, P, P, P, i32, P, P, i32, i32,
                                                        i32, LP, f32, f32, f32, i32, P], i32),
         "pkv_paged_attention_decode_cascade": ([P, P, P, P, P, P, P, i32, P, P, P, P, i32, i32,
-                                                i32, P, i32, i32, i32, i32, LP, f32, f32, f32,
-                                                i32, P, u64, P], i32),
+                                                i32, P, i32, P, i32, i32, i32, LP, f32, f32,
+                                                f32, i32, P, u64, P], i32),
         "pkv_paged_attention_decode_cascade_dynamic": ([P, P, P, P, P, P, P, i32, P, P, P, P,
-                                                        i32, i32, i32, P, i32, i32, i32, i32,
-                                                        LP, f32, i32, P, u64, P], i32),
+                                                        i32, i32, i32, P, i32, P, i32, i32,
+                                                        i32, LP, f32, i32, P, u64, P], i32),
         "pkv_pool_cascade_tail_units": ([P, P, i32, P, i32, i32, ctypes.POINTER(i64)], i32),
+        "pkv_pool_cascade_tail_map": ([P, P, i32, P, i32, i32, P, P, i64,
+                                       ctypes.POINTER(i64)], i32),
         "pkv_decode_cascade_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], u64),
         "pkv_pool_prefix_groups": ([P, P, i32, i32, i32, P, P, ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), P], i32),
@@ -454,14 +456,15 @@ def pkv_paged_attention_decode_cascade(out, q, key, value, k_pool, v_pool, block
                                        v_scale: float = 1.0, partition_size: int = 0,
                                        workspace=None, stream=None,
                                        shared_prefix_blocks=None, seq_order=None,
-                                       tail_units: int = 0) -> None:
+                                       tail_units: int = 0, tail_map=None) -> None:
     """Decode with each group's shared prefix attended once for the group.
     prefix_blocks: device int32 [B]; prefix_groups: device int32
     [n_groups][group_cap] (or None for no groups); key/value: the newest
     tokens' rows to write in the same launch, or both None; seq_order:
     optional device int32 [B], the order the tails are scheduled in;
     tail_units: the batch's tail work (BlockPool.cascade_tail_units), 0 =
-    unknown."""
+    unknown; tail_map: optional device int32 [tail_units][2]
+    (BlockPool.cascade_tail_map)."""
     import torch
     B, Hq, mb = _decode_args(out, q, block_tables, context_lens)
     if key is None and value is None:
@@ -469,10 +472,7 @@ def pkv_paged_attention_decode_cascade(out, q, key, value, k_pool, v_pool, block
     else:
         kp, vp = _new_rows(key, value, B, layout)
     n_groups, cap, gp, pp = _cascade_groups(prefix_blocks, prefix_groups, B)
-    if seq_order is not None:
-        _require(seq_order, torch.int32, "seq_order")
-        if seq_order.numel() != B:
-            raise ValueError("seq_order must hold one entry per sequence")
+    _check_order(seq_order, tail_map, tail_units, B)
     need = pkv_decode_cascade_workspace_bytes(B, Hq, layout.num_kv_heads, max_context_len,
                                               max_prefix_blocks if n_groups else 0,
                                               layout.dtype, partition_size)
@@ -482,9 +482,21 @@ def pkv_paged_attention_decode_cascade(out, q, key, value, k_pool, v_pool, block
     _check(load_library().pkv_paged_attention_decode_cascade(
         _ptr(out), _ptr(q), kp, vp, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), mb,
         _ptr(context_lens), _hint(shared_prefix_blocks, B), pp, gp, n_groups, cap,
-        max_prefix_blocks, _ptr(seq_order), tail_units, B, Hq, max_context_len,
+        max_prefix_blocks, _ptr(seq_order), tail_units, _ptr(tail_map), B, Hq, max_context_len,
         ctypes.byref(layout), sm_scale, k_scale, v_scale, partition_size, _ptr(workspace), nbytes,
         _stream(stream)), "pkv_paged_attention_decode_cascade")
+
+
+def _check_order(seq_order, tail_map, tail_units, B):
+    import torch
+    if seq_order is not None:
+        _require(seq_order, torch.int32, "seq_order")
+        if seq_order.numel() != B:
+            raise ValueError("seq_order must hold one entry per sequence")
+    if tail_map is not None:
+        _require(tail_map, torch.int32, "tail_map")
+        if tail_map.numel() != 2 * tail_units:
+            raise ValueError("tail_map must hold tail_units (batch index, partition) pairs")
 
 
 def _cascade_groups(prefix_blocks, prefix_groups, B):
@@ -506,7 +518,8 @@ def pkv_paged_attention_decode_cascade_dynamic(out, q, k_pool, v_pool, k_block_s
                                                max_prefix_blocks: int, partition_size: int = 0,
                                                workspace=None, stream=None,
                                                shared_prefix_blocks=None,
-                                               seq_order=None, tail_units: int = 0) -> None:
+                                               seq_order=None, tail_units: int = 0,
+                                               tail_map=None) -> None:
     """The cascade decode over per-(block, KV head) scales (fp32
     [num_blocks][Hkv] device tensors); decode only."""
     import torch
@@ -514,10 +527,7 @@ def pkv_paged_attention_decode_cascade_dynamic(out, q, k_pool, v_pool, k_block_s
     _require(k_block_scales, torch.float32, "k_block_scales")
     _require(v_block_scales, torch.float32, "v_block_scales")
     n_groups, cap, gp, pp = _cascade_groups(prefix_blocks, prefix_groups, B)
-    if seq_order is not None:
-        _require(seq_order, torch.int32, "seq_order")
-        if seq_order.numel() != B:
-            raise ValueError("seq_order must hold one entry per sequence")
+    _check_order(seq_order, tail_map, tail_units, B)
     need = pkv_decode_cascade_workspace_bytes(B, Hq, layout.num_kv_heads, max_context_len,
                                               max_prefix_blocks if n_groups else 0,
                                               layout.dtype, partition_size)
@@ -528,8 +538,9 @@ def pkv_paged_attention_decode_cascade_dynamic(out, q, k_pool, v_pool, k_block_s
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_block_scales),
         _ptr(v_block_scales), _ptr(block_tables), mb, _ptr(context_lens),
         _hint(shared_prefix_blocks, B), pp, gp, n_groups, cap, max_prefix_blocks,
-        _ptr(seq_order), tail_units, B, Hq, max_context_len, ctypes.byref(layout), sm_scale,
-        partition_size, _ptr(workspace), nbytes, _stream(stream)),
+        _ptr(seq_order), tail_units, _ptr(tail_map), B, Hq, max_context_len,
+        ctypes.byref(layout), sm_scale, partition_size, _ptr(workspace), nbytes,
+        _stream(stream)),
         "pkv_paged_attention_decode_cascade_dynamic")
 
 
@@ -799,6 +810,29 @@ class BlockPool:
                                                    partition_size, ctypes.byref(out)),
                "pkv_pool_cascade_tail_units")
         return out.value
+
+    def cascade_tail_map(self, seqs, prefix_blocks, max_prefix_blocks: int,
+                         partition_size: int, order=None):
+        """The tail_map argument of the cascade decode: an int32 array
+        [units][2] of (batch index, tail partition) in the decode's schedule
+        order (order: the seq_order it gets, or None for batch order)."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        pre = np.ascontiguousarray(prefix_blocks, dtype=np.int32)
+        if pre.size != seqs.size:
+            raise ValueError("one prefix length per sequence")
+        if order is not None:
+            order = np.ascontiguousarray(order, dtype=np.int32)
+            if order.size != seqs.size:
+                raise ValueError("order must hold one entry per sequence")
+        cap = self.cascade_tail_units(seqs, pre, max_prefix_blocks, partition_size)
+        out = np.zeros((max(cap, 1), 2), dtype=np.int32)
+        units = ctypes.c_int64()
+        _check(self._L.pkv_pool_cascade_tail_map(
+            self._h, seqs.ctypes.data, seqs.size, pre.ctypes.data, max_prefix_blocks,
+            partition_size, None if order is None else order.ctypes.data, out.ctypes.data,
+            cap, ctypes.byref(units)), "pkv_pool_cascade_tail_map")
+        return out[:units.value].copy()
 
     # ---- swap space (page-granular eviction to host memory)
 

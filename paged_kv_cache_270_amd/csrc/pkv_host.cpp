@@ -399,6 +399,39 @@ extern "C" pkv_status pkv_pool_cascade_tail_units(const pkv_pool* p, const int32
   return PKV_OK;
 }
 
+extern "C" pkv_status pkv_pool_cascade_tail_map(const pkv_pool* p, const int32_t* seqs,
+                                                int32_t n, const int32_t* prefix_blocks,
+                                                int32_t max_prefix_blocks,
+                                                int32_t partition_size, const int32_t* order,
+                                                int32_t* map_out, int64_t map_cap,
+                                                int64_t* units_out) {
+  if (!p) return PKV_ERR_BAD_HANDLE;
+  if (n < 0 || !units_out || (n > 0 && !seqs) || partition_size <= 0 ||
+      partition_size % 16 != 0 || max_prefix_blocks < 0 || map_cap < 0 ||
+      (map_cap > 0 && !map_out))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t pb = partition_size / 16;
+  int64_t k = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = order ? order[i] : i;
+    if (b < 0 || b >= n) return PKV_ERR_INVALID_ARG;
+    auto it = p->seqs.find(seqs[b]);
+    if (it == p->seqs.end()) return PKV_ERR_BAD_HANDLE;
+    const int64_t L = it->second.len;
+    int64_t S = prefix_blocks ? prefix_blocks[b] : 0;
+    if (!(S > 0 && S <= max_prefix_blocks && 16 * S < L)) S = 0;
+    const int64_t tail = (L + 15) / 16 - S;
+    const int64_t units = std::max<int64_t>(1, (tail + pb - 1) / pb);
+    if (k + units > map_cap) return PKV_ERR_INVALID_ARG;
+    for (int64_t u = 0; u < units; ++u, ++k) {
+      map_out[2 * k] = b;
+      map_out[2 * k + 1] = (int32_t)u;
+    }
+  }
+  *units_out = k;
+  return PKV_OK;
+}
+
 extern "C" int32_t pkv_seq_shared_prefix_blocks(const pkv_pool* p, int32_t seq) {
   if (!p) return -1;
   auto it = p->seqs.find(seq);

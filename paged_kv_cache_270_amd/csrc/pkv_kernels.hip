@@ -101,6 +101,11 @@ struct DecodeArgs {
   // the tails' partitions in seq_order, each sequence's together.
   int32_t casc_flat;
   int32_t casc_pp;             // prefix partitions per item (flat grid)
+  // Flat grid only: the (batch index, tail partition) of each of the
+  // casc_tail_count tail units, in schedule order, or null: each workgroup
+  // then finds its tail unit by a scan over the lengths.
+  const int2* casc_tail_map;
+  int32_t casc_tail_count;
 };
 
 // Partials are stored write-through to memory (cache policy sc0 sc1, through
@@ -887,19 +892,30 @@ decode_partition_kernel(DecodeArgs a) {
           p = u - b * a.casc_pp;
         } else {
           if (tails >= 0 && u - iu >= tails) break;  // past the last unit (uniform)
-          int2 unit = casc_tail_unit(a, u - iu, lane, &tails);
-          // the scan's results are the same on every lane: say so, so that
-          // everything derived from them stays in scalar registers
+          int2 unit;
+          if (a.casc_tail_map != nullptr) {
+            // the host's map: one load instead of the scan's two dependent
+            // round trips (an entry outside the batch is skipped)
+            tails = a.casc_tail_count;
+            if (u - iu >= tails) break;
+            unit = a.casc_tail_map[u - iu];
+            if ((unsigned)unit.x >= (unsigned)a.nseq || unit.y < 0) unit = make_int2(-1, 0);
+          } else {
+            unit = casc_tail_unit(a, u - iu, lane, &tails);
+          }
+          // the same on every lane: say so, so that everything derived from
+          // them stays in scalar registers
           unit.x = __builtin_amdgcn_readfirstlane(unit.x);
           unit.y = __builtin_amdgcn_readfirstlane(unit.y);
           tails = __builtin_amdgcn_readfirstlane(tails);
-          if (unit.x < 0) break;
-          b = a.casc_items + unit.x;
+          if (unit.x < 0 && a.casc_tail_map == nullptr) break;  // the scan found no unit
+          b = unit.x < 0 ? -1 : a.casc_items + unit.x;
           p = unit.y;
           ordered = true;
         }
-        partition_unit<kFP8, kHwCvt, kSplitP, kPD, kNW, kDyn, kAppend, kCasc>(a, smem, p, kvh,
-                                                                              b, ordered);
+        if (b >= 0)
+          partition_unit<kFP8, kHwCvt, kSplitP, kPD, kNW, kDyn, kAppend, kCasc>(a, smem, p, kvh,
+                                                                                b, ordered);
         // a launch that holds every unit needs no second pass
         if (tails >= 0 && u + n_wg - iu >= tails) break;
         __syncthreads();  // the next unit reuses the LDS
@@ -1555,6 +1571,8 @@ pkv_status plan_decode(float* out, const void* q, const void* k_pool, const void
   a.nseq = num_seqs;
   a.casc_flat = 0;
   a.casc_pp = 1;
+  a.casc_tail_map = nullptr;
+  a.casc_tail_count = 0;
   a.k_enc_scale = k_scale;
   a.v_enc_scale = v_scale;
   // FP8 tiles decoded by bit operations hold code / 256: fold the 256 back
@@ -1977,7 +1995,7 @@ static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
                               const int32_t* prefix_groups, int32_t num_groups,
                               int32_t group_cap, int32_t max_prefix_blocks,
                               const int32_t* seq_order, int32_t tail_units,
-                              int32_t num_seqs, int32_t num_q_heads,
+                              const int32_t* tail_map, int32_t num_seqs, int32_t num_q_heads,
                               int32_t max_context_len, void* workspace,
                               uint64_t workspace_bytes, hipStream_t s) {
   DecodeArgs& a = pl.a;
@@ -2037,6 +2055,10 @@ static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
     a.casc_flat = 1;
     a.casc_pp = std::max(1, cl.n_pp);
     grid = dim3((unsigned)(units * a.hkv));
+    if (tail_map != nullptr) {  // tail_units is then its length
+      a.casc_tail_map = reinterpret_cast<const int2*>(tail_map);
+      a.casc_tail_count = tail_units;
+    }
   }
   (void)hipGetLastError();
   if (pl.dyn)
@@ -2054,8 +2076,10 @@ static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
 
 static pkv_status check_groups(int32_t num_groups, int32_t group_cap, int32_t max_prefix_blocks,
                                const int32_t* prefix_groups, const int32_t* prefix_blocks,
-                               int32_t tail_units) {
+                               int32_t tail_units, const int32_t* tail_map) {
   if (num_groups < 0 || max_prefix_blocks < 0 || tail_units < 0) return PKV_ERR_INVALID_ARG;
+  if (tail_map != nullptr && (tail_units == 0 || !aligned(tail_map, 8)))
+    return PKV_ERR_INVALID_ARG;
   if (num_groups > 0 && (group_cap <= 0 || !prefix_groups || !prefix_blocks))
     return PKV_ERR_INVALID_ARG;
   return PKV_OK;
@@ -2066,14 +2090,14 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade(
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
     const int32_t* shared_prefix_blocks, const int32_t* prefix_blocks,
     const int32_t* prefix_groups, int32_t num_groups, int32_t group_cap,
-    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units, int32_t num_seqs,
-    int32_t num_q_heads, int32_t max_context_len, const pkv_cache_layout* layout,
-    float sm_scale, float k_scale, float v_scale, int32_t partition_size, void* workspace,
-    uint64_t workspace_bytes, void* stream) {
+    int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units,
+    const int32_t* tail_map, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const pkv_cache_layout* layout, float sm_scale, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, uint64_t workspace_bytes, void* stream) {
   if ((key == nullptr) != (value == nullptr)) return PKV_ERR_INVALID_ARG;
   pkv_status st =
       check_groups(num_groups, group_cap, max_prefix_blocks, prefix_groups, prefix_blocks,
-                   tail_units);
+                   tail_units, tail_map);
   if (st != PKV_OK) return st;
   DecodePlan pl;
   // the plain plan's workspace is never larger than the cascade's
@@ -2089,7 +2113,7 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade(
     if (st != PKV_OK) return st;
   }
   return run_cascade(pl, prefix_blocks, prefix_groups, num_groups, group_cap,
-                     max_prefix_blocks, seq_order, tail_units, num_seqs, num_q_heads,
+                     max_prefix_blocks, seq_order, tail_units, tail_map, num_seqs, num_q_heads,
                      max_context_len,
                      workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
@@ -2100,13 +2124,13 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade_dynamic(
     int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* shared_prefix_blocks,
     const int32_t* prefix_blocks, const int32_t* prefix_groups, int32_t num_groups,
     int32_t group_cap, int32_t max_prefix_blocks, const int32_t* seq_order, int32_t tail_units,
-    int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    const int32_t* tail_map, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
     const pkv_cache_layout* layout, float sm_scale, int32_t partition_size, void* workspace,
     uint64_t workspace_bytes, void* stream) {
   if (!k_block_scales || !v_block_scales) return PKV_ERR_INVALID_ARG;
   pkv_status st =
       check_groups(num_groups, group_cap, max_prefix_blocks, prefix_groups, prefix_blocks,
-                   tail_units);
+                   tail_units, tail_map);
   if (st != PKV_OK) return st;
   DecodePlan pl;
   st = plan_decode(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
@@ -2117,7 +2141,7 @@ extern "C" pkv_status pkv_paged_attention_decode_cascade_dynamic(
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
   return run_cascade(pl, prefix_blocks, prefix_groups, num_groups, group_cap,
-                     max_prefix_blocks, seq_order, tail_units, num_seqs, num_q_heads,
+                     max_prefix_blocks, seq_order, tail_units, tail_map, num_seqs, num_q_heads,
                      max_context_len,
                      workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }

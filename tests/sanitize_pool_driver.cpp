@@ -173,6 +173,18 @@ void run(uint32_t seed, int32_t nb, int n_ops) {
                                                    groups.data(), &ng, &mp, order.data());
       CHECK(st == PKV_OK);
       g_groups += ng;
+      // the cascade's tail count and its listed units agree, in pool order
+      int64_t units = 0, listed = -1;
+      CHECK(pkv_pool_cascade_tail_units(p, batch.data(), n, pre.data(), mp, 32, &units) ==
+            PKV_OK);
+      std::vector<int32_t> tmap((size_t)units * 2 + 2);
+      CHECK(pkv_pool_cascade_tail_map(p, batch.data(), n, pre.data(), mp, 32, order.data(),
+                                      tmap.data(), units, &listed) == PKV_OK);
+      CHECK(listed == units);
+      if (units > 0)   // one unit short: refused
+        CHECK(pkv_pool_cascade_tail_map(p, batch.data(), n, pre.data(), mp, 32, order.data(),
+                                        tmap.data(), units - 1, &listed) ==
+              PKV_ERR_INVALID_ARG);
       int32_t width = 1;
       for (int32_t s : batch) width = std::max<int32_t>(width, (int32_t)table_of(p, s).size());
       std::vector<int32_t> tables((size_t)n * (size_t)width + 1, 0), lens((size_t)n + 1, 0);

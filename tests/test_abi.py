@@ -225,13 +225,13 @@ def test_cascade_entry_points_validate_before_launch():
     f16 = pkv.CacheLayout(16, 2, pkv.PKV_F16)
 
     # out, q, key, value, k_pool, v_pool, tables, max_blocks, lens, hint, prefix, groups,
-    # n_groups, cap, max_prefix, order, tail_units, B, Hq, max_ctx, layout, sm, ks, vs, part,
-    # ws, bytes, s
+    # n_groups, cap, max_prefix, order, tail_units, tail_map, B, Hq, max_ctx, layout, sm, ks,
+    # vs, part, ws, bytes, s
     def call(key=16, value=16, groups=16, prefix=16, ng=2, cap=8, mp=4, B=2, ws_bytes=1 << 20,
-             tu=0):
+             tu=0, tmap=None):
         return L.pkv_paged_attention_decode_cascade(
             16, 16, key, value, 16, 16, 16, 4, 16, None, prefix, groups, ng, cap, mp, None, tu,
-            B, 4, 64, ctypes.byref(f8), 0.1, 1.0, 1.0, 0, 256, ws_bytes, None)
+            tmap, B, 4, 64, ctypes.byref(f8), 0.1, 1.0, 1.0, 0, 256, ws_bytes, None)
     assert call(key=None) == pkv.PKV_ERR_INVALID_ARG
     assert call(value=None) == pkv.PKV_ERR_INVALID_ARG
     assert call(ng=-1) == pkv.PKV_ERR_INVALID_ARG
@@ -241,6 +241,9 @@ def test_cascade_entry_points_validate_before_launch():
     assert call(cap=0) == pkv.PKV_ERR_INVALID_ARG
     assert call(ws_bytes=16) == pkv.PKV_ERR_WORKSPACE
     assert call(tu=-1) == pkv.PKV_ERR_INVALID_ARG
+    # a tail map needs its length in tail_units, and 8-byte alignment
+    assert call(tmap=16, tu=0) == pkv.PKV_ERR_INVALID_ARG
+    assert call(tmap=20, tu=2) == pkv.PKV_ERR_INVALID_ARG
     # G = 2: one item per group of 8 members; 65534 items + 2 sequences exceed
     # one grid dimension (65535)
     assert call(ng=65534) == pkv.PKV_ERR_INVALID_ARG
@@ -248,7 +251,7 @@ def test_cascade_entry_points_validate_before_launch():
 
     def dyn(ks=16, vs=16, layout=f8, B=2):
         return L.pkv_paged_attention_decode_cascade_dynamic(
-            16, 16, 16, 16, ks, vs, 16, 4, 16, None, 16, 16, 2, 8, 4, None, 0, B, 4, 64,
+            16, 16, 16, 16, ks, vs, 16, 4, 16, None, 16, 16, 2, 8, 4, None, 0, None, B, 4, 64,
             ctypes.byref(layout), 0.1, 0, 256, 1 << 20, None)
     assert dyn(ks=None) == pkv.PKV_ERR_INVALID_ARG
     assert dyn(vs=None) == pkv.PKV_ERR_INVALID_ARG
@@ -266,10 +269,10 @@ def test_cascade_rejects_a_misaligned_workspace():
     need = pkv.pkv_decode_cascade_workspace_bytes(2, 4, 2, 64, 2, pkv.PKV_FP8_E4M3FN, 0)
     assert need > 0
     # out, q, key, value, k_pool, v_pool, tables, max_blocks, lens, hint, prefix, groups,
-    # n_groups, cap, max_prefix, order, tail_units, B, Hq, max_ctx, layout, sm, ks, vs, part,
-    # ws, bytes, s
+    # n_groups, cap, max_prefix, order, tail_units, tail_map, B, Hq, max_ctx, layout, sm, ks,
+    # vs, part, ws, bytes, s
     st = L.pkv_paged_attention_decode_cascade(
-        16, 16, None, None, 16, 16, 16, 4, 16, None, 16, 16, 1, 2, 2, None, 0, 2, 4, 64,
+        16, 16, None, None, 16, 16, 16, 4, 16, None, 16, 16, 1, 2, 2, None, 0, None, 2, 4, 64,
         ctypes.byref(f8), 0.1, 1.0, 1.0, 0, 256 + 16, need + 256, None)
     assert st == pkv.PKV_ERR_INVALID_ARG
 

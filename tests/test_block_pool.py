@@ -333,3 +333,33 @@ def test_cascade_tail_units_counts_each_tails_partitions():
         pool.cascade_tail_units(seqs, prefix, max_pre, 24)
     with pytest.raises(pkv.PkvError):
         pool.cascade_tail_units([root, 12345], [0, 0], max_pre, 32)
+
+
+def test_cascade_tail_map_lists_each_tails_partitions():
+    """The same hand-worked batch: the map lists, in the given order, each
+    sequence's tail partitions as (batch index, partition) pairs -- 4, 2, 1
+    and 1 of them at 32-token partitions -- as many as cascade_tail_units
+    counts; batch order without an order; order entries outside the batch
+    are rejected."""
+    pool = pkv.BlockPool(64)
+    root = pool.create()
+    pool.append(root, 40)
+    a, b = pool.fork(root), pool.fork(root)
+    pool.append(root, 100)
+    pool.append(a, 30)
+    pool.append(b, 1)
+    empty = pool.create()
+    seqs = [root, a, b, empty]
+    prefix, groups, max_pre = pool.prefix_groups(seqs, 8)
+    m = pool.cascade_tail_map(seqs, prefix, max_pre, 32, order=[1, 0, 3, 2])
+    assert m.tolist() == [[1, 0], [1, 1], [0, 0], [0, 1], [0, 2], [0, 3], [3, 0], [2, 0]]
+    m = pool.cascade_tail_map(seqs, prefix, max_pre, 32)
+    assert m.tolist() == [[0, 0], [0, 1], [0, 2], [0, 3], [1, 0], [1, 1], [2, 0], [3, 0]]
+    assert len(m) == pool.cascade_tail_units(seqs, prefix, max_pre, 32)
+    # prefixes past max_prefix_blocks are not cascaded: whole lengths count
+    m = pool.cascade_tail_map(seqs, prefix, 1, 32)
+    assert [int((m[:, 0] == i).sum()) for i in range(4)] == [5, 3, 2, 1]
+    with pytest.raises(pkv.PkvError):
+        pool.cascade_tail_map(seqs, prefix, max_pre, 32, order=[0, 1, 2, 4])
+    with pytest.raises(pkv.PkvError):
+        pool.cascade_tail_map(seqs, prefix, max_pre, 24)

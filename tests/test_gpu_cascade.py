@@ -76,7 +76,8 @@ def _group_array(groups, cap):
     return np.asarray(out, dtype=np.int32).reshape(-1, cap)
 
 
-def _cascade(prep, groups, prefix, cap, ps, write, name, order=None, tail_units=0):
+def _cascade(prep, groups, prefix, cap, ps, write, name, order=None, tail_units=0,
+             tail_map=None):
     wl = prep.wl
     B, Hkv, fp8 = wl.num_seqs, wl.num_kv_heads, wl.fp8
     garr = _group_array(groups, cap)
@@ -103,7 +104,8 @@ def _cascade(prep, groups, prefix, cap, ps, write, name, order=None, tail_units=
         wl.max_context_len, prep.layout, prep.sm_scale, d_prefix, d_groups,
         int(prefix.max()) if prefix.size else 0, prep.k_scale, prep.v_scale, ps,
         seq_order=None if order is None else torch.from_numpy(order).cuda(),
-        tail_units=tail_units)
+        tail_units=tail_units,
+        tail_map=None if tail_map is None else torch.from_numpy(tail_map).cuda())
     torch.cuda.synchronize()
     if write:
         assert np.array_equal(prep.k_pool.cpu().numpy(), k_exp)
@@ -254,18 +256,21 @@ def _pool_built(wl):
     P = pkv.pkv_decode_partition_size(len(seqs), wl.num_kv_heads, int(got.max()),
                                       pkv.PKV_FP8_E4M3FN, 0)
     units = pool.cascade_tail_units(seqs, prefix, max_pre, P)
-    return tables, got, prefix, garr, max_pre, order, units
+    tmap = pool.cascade_tail_map(seqs, prefix, max_pre, P, order)
+    assert len(tmap) == units
+    return tables, got, prefix, garr, max_pre, order, units, tmap
 
 
 def test_cascade_shared_prefix_full_step():
     """The 256-sequence shared-prefix batch at full size (FP8, 32 groups of 8
     with a 125-block prefix), run as the benchmark's step runs it: sequences
-    grown in the host pool, groups and the longest-tail order from the pool,
-    the automatic partition size, and each sequence's newest K/V rows written
-    by the cascade call itself.  Both pools must equal the oracle's write
-    byte for byte, and all 256 outputs must match the oracle's decode."""
+    grown in the host pool, groups, the longest-tail order and the list of
+    tail units from the pool, the automatic partition size, and each
+    sequence's newest K/V rows written by the cascade call itself.  Both
+    pools must equal the oracle's write byte for byte, and all 256 outputs
+    must match the oracle's decode."""
     base = workloads.shared_prefix()
-    tables, lens, prefix, garr, max_pre, order, units = _pool_built(base)
+    tables, lens, prefix, garr, max_pre, order, units, tmap = _pool_built(base)
     assert garr.shape[0] == 32 and max_pre == base.prefix_blocks
     B = base.num_seqs
     new = [(b, int(L) - 1) for b, L in enumerate(lens)]
@@ -275,7 +280,7 @@ def test_cascade_shared_prefix_full_step():
     groups = [[int(m) for m in g if m >= 0] for g in garr]
     assert sorted(m for g in groups for m in g) == list(range(B))
     got = _cascade(prep, groups, prefix, 8, 0, True, "shared-prefix B=256 full step", order,
-                   tail_units=units)
+                   tail_units=units, tail_map=tmap)
     assert got.shape == (B, wl.num_q_heads, D)
 
 
@@ -294,7 +299,7 @@ def test_cascade_rejects_bad_arguments():
         out.data_ptr(), prep.q.data_ptr(), key.data_ptr(), None, prep.k_pool.data_ptr(),
         prep.v_pool.data_ptr(), prep.tables.data_ptr(), prep.tables.shape[1],
         prep.lens.data_ptr(), None, pre.data_ptr(), garr.data_ptr(), garr.shape[0], 8,
-        int(prefix.max()), None, 0, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
+        int(prefix.max()), None, 0, None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
         prep.sm_scale, prep.k_scale, prep.v_scale, 0, None, 0, None)
     assert st == pkv.PKV_ERR_INVALID_ARG
     # workspace smaller than the cascade needs (the plain size is smaller)
@@ -308,7 +313,7 @@ def test_cascade_rejects_bad_arguments():
         out.data_ptr(), prep.q.data_ptr(), None, None, prep.k_pool.data_ptr(),
         prep.v_pool.data_ptr(), prep.tables.data_ptr(), prep.tables.shape[1],
         prep.lens.data_ptr(), None, pre.data_ptr(), garr.data_ptr(), garr.shape[0], 8,
-        int(prefix.max()), None, 0, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
+        int(prefix.max()), None, 0, None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
         prep.sm_scale, prep.k_scale, prep.v_scale, 64, ws.data_ptr(), ws.numel(), None)
     assert st == pkv.PKV_ERR_WORKSPACE
     # more items plus sequences than one grid dimension holds (G = 4: one item
@@ -321,7 +326,7 @@ def test_cascade_rejects_bad_arguments():
         out.data_ptr(), prep.q.data_ptr(), None, None, prep.k_pool.data_ptr(),
         prep.v_pool.data_ptr(), prep.tables.data_ptr(), prep.tables.shape[1],
         prep.lens.data_ptr(), None, pre.data_ptr(), garr.data_ptr(), 65535, 4,
-        int(prefix.max()), None, 0, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
+        int(prefix.max()), None, 0, None, wl.num_seqs, 8, wl.max_context_len, ctypes.byref(lay),
         prep.sm_scale, prep.k_scale, prep.v_scale, 64, big.data_ptr(), big.numel(), None)
     assert st == pkv.PKV_ERR_INVALID_ARG
 
@@ -440,5 +445,17 @@ def test_cascade_tail_units_change_no_result():
     for tu in (exact, 1, 3, exact + 40, 0):
         outs.append(_cascade(prep, groups, prefix, 8, ps, False, f"tail_units={tu}", order,
                              tail_units=tu))
+    # the same units listed by a map, and the map with entries outside the
+    # batch (skipped) mixed in
+    per = ps // 16
+    tmap = np.array([(b, u) for b in order for u in range(max(1, -(-int(nblk[b]) // per)))],
+                    dtype=np.int32)
+    assert len(tmap) == exact
+    outs.append(_cascade(prep, groups, prefix, 8, ps, False, "tail map", order,
+                         tail_units=exact, tail_map=tmap))
+    junk = np.array([(-1, 0), (wl.num_seqs, 0), (0, -1)], dtype=np.int32)
+    mixed = np.concatenate([tmap[:5], junk, tmap[5:]])
+    outs.append(_cascade(prep, groups, prefix, 8, ps, False, "tail map with junk", order,
+                         tail_units=len(mixed), tail_map=mixed))
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
