@@ -413,12 +413,23 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int tt = t + 2 * u;
+        if constexpr (kDyn) {
+          // With per-block scales the next pair's loads are issued on every
+          // path (ids past the chunk are -1: zeros), so the wait for the
+          // current pair never covers them: 714-724 against 677-687 TFLOP/s on the
+          // 128K chunk.  Without scales the same change measured 1-2 %
+          // slower (1029-1037 against 1051-1056): the kernel is bound by
+          // its vector and matrix issue, not by these loads.
+          const int pa = tt + 2 < cnt ? __builtin_amdgcn_readlane(tbl, tt + 2) : -1;
+          const int pb = tt + 3 < cnt ? __builtin_amdgcn_readlane(tbl, tt + 3) : -1;
+          load_pair<kFP8>(buf[u ^ 1][0], buf[u ^ 1][1], a, pa, pb, kvh, lane);
+          pair_scales(a, pa, pb, kvh, bsk[u ^ 1], bsv[u ^ 1]);
+        }
         if (tt < cnt) {
-          if (tt + 2 < cnt) {
+          if (!kDyn && tt + 2 < cnt) {
             const int pa = __builtin_amdgcn_readlane(tbl, tt + 2);
             const int pb = tt + 3 < cnt ? __builtin_amdgcn_readlane(tbl, tt + 3) : pa;
             load_pair<kFP8>(buf[u ^ 1][0], buf[u ^ 1][1], a, pa, pb, kvh, lane);
-            if constexpr (kDyn) pair_scales(a, pa, pb, kvh, bsk[u ^ 1], bsv[u ^ 1]);
           }
           if (tt + 1 >= cnt) {              // past the last tile: all masked below
             __asm__ volatile("" ::: "memory");
