@@ -585,6 +585,10 @@ def main() -> int:
     # prefix groups of the batch, found by the host pool from the forks
     prefix, garr, max_pre, order = pool.prefix_groups(seqs, 8, with_order=True)
     cascade = args.cascade == "on" or (args.cascade == "auto" and garr.shape[0] > 0)
+    # the library's vector-ALU decode kernel (an environment switch read by
+    # the library) covers FP8 per-tensor decode of groups of at most 8 heads
+    valu = (os.environ.get("PKV_DECODE_MATH") == "valu" and wl.fp8 and not dyn and not cascade
+            and Hq // Hkv <= 8)
     tail_units = 0
     if cascade:
         d_prefix = torch.from_numpy(prefix).to(dev)
@@ -835,7 +839,9 @@ def main() -> int:
                    "kv_dtype": "fp8_e4m3fn" if wl.fp8 else "f16",
                    "kv_scales": ("per (block, kv head)" if dyn else "per tensor")
                    if wl.fp8 else None,
-                   "arith": "f16 MFMA inputs, f32 accumulate", "parallelism": "single GPU",
+                   "arith": "f16 2-element dot products (QK^T) and f32 FMAs (PV) on the "
+                            "vector ALUs" if valu else "f16 MFMA inputs, f32 accumulate",
+                   "parallelism": "single GPU",
                    "launch": "hip graph" if args.graph else "eager",
                    "new_token_write": "separate launch" if dyn else "in the decode kernel",
                    "decode": ("cascade: each shared prefix once per group "
@@ -870,11 +876,12 @@ def main() -> int:
                                 for t in (max(bulk_times), min(bulk_times))],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     # counters were taken at the workload's own partition size
+                     # counters were taken at the workload's own partition size,
+                     # on the matrix-core kernels
                      "traffic": measured_traffic("decode_partition_" + args.workload +
                                                  ("_block_scales" if dyn else "") +
                                                  ("_cascade" if cascade else ""))
-                     if args.partition_size is None else None},
+                     if args.partition_size is None and not valu else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

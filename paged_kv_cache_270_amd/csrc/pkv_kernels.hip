@@ -927,6 +927,319 @@ decode_partition_kernel(DecodeArgs a) {
       a, smem, blockIdx.x, blockIdx.y, blockIdx.z, false);
 }
 
+// The same partition unit with both contractions on the vector ALUs instead
+// of the matrix cores -- kept to measure that choice (PKV_DECODE_MATH=valu).
+// FP8, per-tensor scales, G <= 8 (groups of fewer heads compute eight, the
+// missing ones on zero queries); grid (n_p_max, Hkv, B), kValuWaves waves,
+// wave w taking the partition's blocks w, w + kValuWaves, ...  One tile in
+// flight besides the one being computed, as in the default family.  One
+// cache policy per launch (kAux): through the caches when the caller names
+// shared prefixes, streamed otherwise -- a per-chunk choice, as the
+// partition kernel makes it, cost this kernel 67 more VGPRs.
+//  * QK^T: lane (cg, hg, tp) = lane / 16, lane / 8 % 2, lane % 8 takes
+//    tokens tp and tp + 8, heads 4hg .. 4hg+3 and the 32 channels 16cg ..
+//    16cg+15, 64 + 16cg .. 64 + 16cg + 15.  It loads those K bytes itself
+//    (the two lanes of a (cg, tp) pair read the same bytes; each load
+//    instruction covers whole 128-byte lines), converts them to fp16 and
+//    takes 2-element dot products with fp32 sums against the same channels
+//    of its four queries, which stay in registers (64 VGPRs).  A
+//    reduce-scatter over cg then leaves it the full logits of token
+//    tp + 8 (cg / 2), heads 4hg + 2 (cg % 2) and the next.
+//  * Softmax: the partition kernel's reference-max scheme, per head.
+//  * PV: lane (j, qg) = lane % 16, lane / 16 holds channels 16c + j
+//    (c = 0..7), tokens 4qg .. +3 of the V tile (the tile load's layout).  It
+//    reads its four tokens' probabilities of all eight heads from an LDS row
+//    the lanes wrote, and accumulates 8 heads x 8 channels in fp32 fused
+//    multiply-adds on the values converted to fp32 exactly.
+constexpr int kValuG = 8;
+constexpr int kValuWaves = 4;
+
+struct ValuTile {
+  u32x4 k[4];  // [i][token tp + 8tt]: channels 64i + 16cg .. +15
+  u32x4 v[2];  // as TileRegs<true>::v
+};
+
+template <int kAux>
+__device__ __forceinline__ void valu_load(ValuTile& r, const DecodeArgs& a, int phys, int kvh,
+                                          int koff, int lane) {
+  constexpr int kTileBytes = kBS * kD;
+  phys = __builtin_amdgcn_readfirstlane(phys);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+  const int64_t off = ok ? ((int64_t)phys * a.hkv + kvh) * kTileBytes : 0;
+  const __amdgpu_buffer_rsrc_t kr = byte_range(a.k_pool + off, ok ? kTileBytes : 0);
+  const __amdgpu_buffer_rsrc_t vr = byte_range(a.v_pool + off, ok ? kTileBytes : 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+      r.k[2 * i + tt] =
+          __builtin_amdgcn_raw_buffer_load_b128(kr, i * 1024 + koff + tt * 128, 0, kAux);
+    r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, (i * kWave + lane) * 16, 0, kAux);
+  }
+}
+
+template <int kAux>
+__global__ void __launch_bounds__(kValuWaves * kWave) decode_valu_kernel(DecodeArgs a) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  constexpr int kNW = kValuWaves;
+  extern __shared__ float smem[];                 // [kNW][G][D], [kNW][16] max, [kNW][16] sum
+  __shared__ __align__(16) float pst[kNW][kBS * kValuG];  // per wave: p[token][head]
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // QK^T roles
+  const int tp = lane & 7, hg = (lane >> 3) & 1, cg = lane >> 4;
+  const int b0 = cg & 1, b1 = cg >> 1;
+  const int hsel = 2 * hg + b0;  // this lane's logits: heads 2 hsel, 2 hsel + 1
+  // PV roles
+  const int j = lane & 15, qg = lane >> 4;
+  const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.g;
+  const int L = clamp_len(a, b);
+  const SeqSplit sp = seq_split(a, L);
+  const int64_t head0 = (int64_t)b * a.hq + (int64_t)kvh * G;
+  if (p >= sp.n_p) {
+    if (p == 0)
+      for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) a.out[head0 * kD + i] = 0.0f;
+    return;
+  }
+  const int n_p = sp.n_p;
+  const int blk0 = p * sp.per;
+  const int nblk = min(sp.nblk, blk0 + sp.per) - blk0;
+  const int koff = cg * 256 + tp * 16;
+
+  // queries 4hg .. 4hg+3: channels 64i + 16cg .. +15 as 8 fp16 pairs per i
+  h2 q[4][16];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int g = 4 * hg + h;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        f16x8 v = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (g < G)
+          v = *reinterpret_cast<const f16x8*>(a.q + (head0 + g) * kD + 64 * i + 16 * cg + 8 * x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[h][i * 8 + x * 4 + e] = h2{v[2 * e], v[2 * e + 1]};
+      }
+    }
+  }
+
+  float acc[kValuG][8];  // head g, channel 16c + j, over this lane's tokens
+#pragma unroll
+  for (int g = 0; g < kValuG; ++g)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[g][c] = 0.0f;
+  // heads 2hsel, 2hsel + 1: reference max (equal on the lanes of the head)
+  // and the sum over this lane's tokens
+  float m0 = -INFINITY, m1 = -INFINITY;
+  float l0 = 0.0f, l1 = 0.0f;
+  float* prow = &pst[w][0];
+
+  auto tile = [&](ValuTile& t, int tb) {
+    if (tb + kBS > L) {  // wave-uniform: zero the values of tokens >= L
+      const int nv = min(max(L - (tb + qg * 4), 0), 4);
+      const uint32_t mk = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) t.v[i] &= u32x4{mk, mk, mk, mk};
+    }
+    float s[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) s[tt][h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int d = (int)t.k[2 * i + tt][c];
+          const h2 k01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false);
+          const h2 k23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            s[tt][h] = __builtin_amdgcn_fdot2(k01, q[h][8 * i + 2 * c], s[tt][h], false);
+            s[tt][h] = __builtin_amdgcn_fdot2(k23, q[h][8 * i + 2 * c + 1], s[tt][h], false);
+          }
+        }
+    // reduce-scatter over cg: across cg bit 1 (lanes 32 apart) keeping token
+    // tp + 8b1, then across bit 0 keeping heads 4hg + 2b0, +1
+    float r4[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float keep = b1 ? s[1][h] : s[0][h];
+      const float give = b1 ? s[0][h] : s[1][h];
+      r4[h] = keep + __shfl_xor(give, 32, kWave);
+    }
+    float r2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float keep = b0 ? r4[2 + e] : r4[e];
+      const float give = b0 ? r4[e] : r4[2 + e];
+      r2[e] = keep + __shfl_xor(give, 16, kWave);
+    }
+    const int tok = tp + 8 * b1;
+    const bool valid = tb + tok < L;
+    const float s0 = valid ? r2[0] * a.qk_scale : -INFINITY;
+    const float s1 = valid ? r2[1] * a.qk_scale : -INFINITY;
+    if (__any(s0 - m0 > kLazyMaxSlack || s1 - m1 > kLazyMaxSlack)) {  // wave-uniform
+      // the lanes of one head pair differ in tp and b1
+      float x0 = s0, x1 = s1;
+#pragma unroll
+      for (int x = 1; x <= 32; x <<= 1) {
+        if (x == 8 || x == 16) continue;
+        x0 = fmaxf(x0, __shfl_xor(x0, x, kWave));
+        x1 = fmaxf(x1, __shfl_xor(x1, x, kWave));
+      }
+      const float n0 = fmaxf(m0, x0), n1 = fmaxf(m1, x1);
+      const float f0 = __builtin_amdgcn_exp2f(m0 - n0), f1 = __builtin_amdgcn_exp2f(m1 - n1);
+      l0 *= f0;
+      l1 *= f1;
+      m0 = n0;
+      m1 = n1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // heads 2e, 2e + 1: hsel = e on lane 16 (e % 2) + 8 (e / 2)
+        const int src = 16 * (e & 1) + 8 * (e >> 1);
+        const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f0), src));
+        const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f1), src));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          acc[2 * e][c] *= g0;
+          acc[2 * e + 1][c] *= g1;
+        }
+      }
+    }
+    const float p0 = __builtin_amdgcn_exp2f(s0 - m0);
+    const float p1 = __builtin_amdgcn_exp2f(s1 - m1);
+    l0 += p0;
+    l1 += p1;
+    // p[tok][2 hsel, 2 hsel + 1]; one wave writes and then reads its own row
+    *reinterpret_cast<f2*>(prow + tok * kValuG + 2 * hsel) = f2{p0, p1};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {  // tokens 4qg + 2rr, +1
+      float pp[2][kValuG];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const f32x4 v4 =
+              *reinterpret_cast<const f32x4*>(prow + (4 * qg + 2 * rr + r) * kValuG + 4 * x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pp[r][4 * x + e] = v4[e];
+        }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int d = (int)t.v[c >> 2][c & 3];
+        const f2 v = rr ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d, 1.0f, false);
+#pragma unroll
+        for (int g = 0; g < kValuG; ++g) {
+          acc[g][c] = __builtin_fmaf(pp[0][g], v[0], acc[g][c]);
+          acc[g][c] = __builtin_fmaf(pp[1][g], v[1], acc[g][c]);
+        }
+      }
+    }
+    // the next tile's writes come after every lane's reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  const int my_n = w < nblk ? (nblk - w + kNW - 1) / kNW : 0;
+  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks + blk0 + w;
+  for (int c0 = 0; c0 < my_n; c0 += kWave) {
+    const int cnt = min(kWave, my_n - c0);
+    const int tbl = load_table(trow + (int64_t)c0 * kNW, cnt, kNW, lane);
+    const int lb0 = blk0 + w + c0 * kNW;
+    ValuTile buf[2];
+    valu_load<kAux>(buf[0], a, __builtin_amdgcn_readlane(tbl, 0), kvh, koff, lane);
+    for (int base = 0; base < cnt; base += 2) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int ii = base + r;
+        valu_load<kAux>(buf[r ^ 1], a, ii + 1 < cnt ? __builtin_amdgcn_readlane(tbl, ii + 1) : -1,
+                        kvh, koff, lane);
+        if (ii < cnt) tile(buf[r], (lb0 + ii * kNW) * kBS);
+      }
+    }
+  }
+
+  // sums over the lanes of each head pair (tp, b1); outputs over qg by the
+  // reduce-scatter of the logits (lane (j, qg) keeps heads 2qg, 2qg + 1)
+#pragma unroll
+  for (int x = 1; x <= 32; x <<= 1) {
+    if (x == 8 || x == 16) continue;
+    l0 += __shfl_xor(l0, x, kWave);
+    l1 += __shfl_xor(l1, x, kWave);
+  }
+  const int hi = qg >> 1, lo = qg & 1;
+  float o4[4][8], o2[2][8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float keep = hi ? acc[4 + e][c] : acc[e][c];
+      const float give = hi ? acc[e][c] : acc[4 + e][c];
+      o4[e][c] = keep + __shfl_xor(give, 32, kWave);
+    }
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float keep = lo ? o4[2 + e][c] : o4[e][c];
+      const float give = lo ? o4[e][c] : o4[2 + e][c];
+      o2[e][c] = keep + __shfl_xor(give, 16, kWave);
+    }
+
+  // merge the waves through LDS, as the partition kernel does
+  float* so = smem;                  // [kNW][G][D]
+  float* sm = smem + kNW * G * kD;   // [kNW][16]
+  float* sl = sm + kNW * 16;         // [kNW][16]
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (2 * qg + e < G) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) so[(w * G + 2 * qg + e) * kD + 16 * c + j] = o2[e][c];
+    }
+    // lane 16 b0 + 8 hg (tp = b1 = 0) holds heads 2 hsel, 2 hsel + 1
+    if (tp == 0 && b1 == 0 && 2 * hsel + e < G) {
+      sm[w * 16 + 2 * hsel + e] = e ? m1 : m0;
+      sl[w * 16 + 2 * hsel + e] = e ? l1 : l0;
+    }
+  }
+  __syncthreads();
+  const bool single = n_p == 1;
+  for (int i = threadIdx.x; i < G * kD; i += kNW * kWave) {
+    const int gg = i / kD, d = i - gg * kD;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kNW; ++ww) mx = fmaxf(mx, sm[ww * 16 + gg]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kNW; ++ww) {
+      const float f = __builtin_amdgcn_exp2f(sm[ww * 16 + gg] - mx);
+      num += so[(ww * G + gg) * kD + d] * f;
+      den += sl[ww * 16 + gg] * f;
+    }
+    if (single) {
+      a.out[(head0 + gg) * kD + d] = num / den * a.out_scale;
+    } else {
+      const int64_t prow2 = part_row(a, b, kvh, p, gg);
+      a.ws_o[prow2 * kD + d] = num;
+      if (d == 0) {
+        a.ws_ml[prow2 * 2] = mx;
+        a.ws_ml[prow2 * 2 + 1] = den;
+      }
+    }
+  }
+}
+
 // Short partitions (an explicit split-KV length of a few hundred tokens):
 // launching one workgroup per partition leaves each wave a stream of a few
 // tiles, and the stream drains at every partition end.  Here each wave owns
@@ -1454,17 +1767,22 @@ CascLayout casc_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx, i
 //   PKV_DECODE_CHAIN = 0 | n      partitions per wave for short partitions:
 //                                 0 = one workgroup per partition, n = fixed
 //                                 (default: from the shape)
+//   PKV_DECODE_MATH = mfma | valu the contractions on the matrix cores or on
+//                                 the vector ALUs (decode_valu_kernel: FP8,
+//                                 per-tensor scales, G <= 8; other shapes and
+//                                 the cascade keep the matrix cores)
 struct KernelConfig {
   bool hw_cvt;
   bool split_p_fp8;
   int prefetch;
   int waves;
   int chain;  // -1 = automatic
+  bool valu;
 };
 
 KernelConfig kernel_config() {
   static const KernelConfig cfg = [] {
-    KernelConfig k{true, true, 1, 0, -1};
+    KernelConfig k{true, true, 1, 0, -1, false};
     if (const char* e = std::getenv("PKV_FP8_DEQUANT")) k.hw_cvt = std::strcmp(e, "hw") == 0;
     if (const char* e = std::getenv("PKV_FP8_SPLIT_P")) k.split_p_fp8 = std::atoi(e) != 0;
     if (const char* e = std::getenv("PKV_DECODE_PREFETCH")) {
@@ -1478,6 +1796,10 @@ KernelConfig kernel_config() {
     if (const char* e = std::getenv("PKV_DECODE_WAVES")) {
       const int v = std::atoi(e);
       if (v == 1 || v == 2 || v == 4 || v == 8) k.waves = v;
+    }
+    if (const char* e = std::getenv("PKV_DECODE_MATH")) {
+      k.valu = std::strcmp(e, "valu") == 0;
+      if (k.valu) k.hw_cvt = true;  // the vector kernel converts to code values
     }
     return k;
   }();
@@ -1771,13 +2093,25 @@ __global__ void __launch_bounds__(kWave) append_kernel(DecodeArgs a) {
   append_store<kFP8>(a, t, phys, kvh, lane, (L - 1) & 15);
 }
 
+// The vector-ALU measurement variant covers FP8 per-tensor decode of groups
+// of at most eight query heads.
+static bool use_valu(const DecodePlan& pl) {
+  return pl.cfg.valu && pl.fp8 && !pl.dyn && pl.a.g <= kValuG;
+}
+
 static pkv_status run_partitions(const DecodePlan& pl, int32_t num_seqs, hipStream_t s) {
   if (num_seqs == 0) return PKV_OK;
   const dim3 grid((unsigned)pl.a.n_p_max, (unsigned)pl.a.hkv, (unsigned)num_seqs);
   (void)hipGetLastError();
   const KernelConfig& c = pl.cfg;
   const int nw = waves_for(pl);
-  if (const int chain = chain_for(pl, num_seqs)) {
+  if (use_valu(pl)) {
+    const size_t lds = partition_lds(kValuWaves, pl.a.g, false, false);
+    if (pl.a.shared_prefix != nullptr)
+      decode_valu_kernel<0><<<grid, dim3(kValuWaves * kWave), lds, s>>>(pl.a);
+    else
+      decode_valu_kernel<kLoadNT><<<grid, dim3(kValuWaves * kWave), lds, s>>>(pl.a);
+  } else if (const int chain = chain_for(pl, num_seqs)) {
     if (pl.fp8)
       launch_chain<true>(chain, num_seqs, s, pl.a);
     else
@@ -1803,14 +2137,15 @@ static pkv_status run_partitions_append(const DecodePlan& pl, int32_t num_seqs,
   if (num_seqs == 0) return PKV_OK;
   (void)hipGetLastError();
   const KernelConfig& c = pl.cfg;
-  if (const int chain = chain_for(pl, num_seqs)) {
+  if (const int chain = use_valu(pl) ? 0 : chain_for(pl, num_seqs)) {
     if (pl.fp8)
       launch_chain<true, true>(chain, num_seqs, s, pl.a);
     else
       launch_chain<false, true>(chain, num_seqs, s, pl.a);
     return launch_status();
   }
-  const bool default_family = c.prefetch == 1 && (!pl.fp8 || (c.hw_cvt && c.split_p_fp8));
+  const bool default_family =
+      !use_valu(pl) && c.prefetch == 1 && (!pl.fp8 || (c.hw_cvt && c.split_p_fp8));
   if (!default_family) {
     const dim3 grid((unsigned)pl.a.hkv, (unsigned)num_seqs);
     if (pl.fp8)
