@@ -67,6 +67,26 @@ def measured_traffic(key: str, sources=DECODE_SRCS):
     return t.get("hbm_bytes_per_launch")
 
 
+def library_gemm_tfs(n: int = 8192, reps: int = 20) -> float:
+    """An fp16 n x n x n product through torch.matmul (the ROCm BLAS library):
+    the matrix-core rate a vendor-tuned dense kernel reaches on this part,
+    next to which the prefill kernel's rate is read."""
+    import torch
+    a = torch.randn((n, n), dtype=torch.float16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    t1.record()
+    torch.cuda.synchronize()
+    del a, b, c
+    return 2.0 * n ** 3 / (t0.elapsed_time(t1) / reps * 1e-3) / 1e12
+
+
 def copy_probe(mib: int) -> int:
     """A plain copy of known size: reads and writes mib MiB per launch."""
     import torch
@@ -308,6 +328,7 @@ def run_prefill(args) -> int:
     flops = wl.flops()
     value = flops / (step_ms * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
+    gemm_tfs = library_gemm_tfs()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -378,6 +399,9 @@ def run_prefill(args) -> int:
                      "traffic": measured_traffic("prefill_" + args.workload +
                                                  ("_block_scales" if dyn else ""),
                                                  PREFILL_SRCS)},
+        "mfma_ceilings": {"library_f16_gemm_tfs": round(gemm_tfs, 1),
+                          "library_gemm": "torch.matmul, fp16 8192 x 8192 x 8192",
+                          "kernel_frac_of_library_gemm": round(achieved / gemm_tfs, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

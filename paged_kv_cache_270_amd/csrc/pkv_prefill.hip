@@ -27,8 +27,13 @@
 //     the decode kernel does, tested on each lane's largest logit;
 //   * only the pairs that reach past the row tile's first position apply
 //     the causal mask; value slots past the sequence's end are zeroed;
-//   * the matrix bursts of a wave run at raised priority (s_setprio), so the
-//     two waves of a SIMD tend to alternate matrix and vector phases.
+//   * FP8 with per-tensor scales runs the pairs as a software pipeline: one
+//     straight-line block takes pair i's exponentials, pair i+1's QK^T
+//     products and pair i's PV products, so the compiler interleaves vector
+//     and matrix work within each wave;
+//   * elsewhere the matrix bursts of a wave run at raised priority
+//     (s_setprio), so the two waves of a SIMD tend to alternate matrix and
+//     vector phases.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -320,16 +325,151 @@ struct VLate {
   }
 };
 
-// The K and V scales of a pair's two (block, head) tiles; ids outside the
-// pool read as 0 (their tiles are zeros).
+// The K and V scales of a pair's two (block, head) tiles.  A tile outside
+// the pool (an id past the sequence's last tile, or out of range) reads as
+// zeros; its V scale is 0 and its K scale 1: the causal mask sets such a
+// tile's logits to -inf before they are multiplied by the K scale, and -inf
+// times 0 would be NaN.
 __device__ __forceinline__ void pair_scales(const PrefillArgs& a, int pa, int pb, int kvh,
                                             float (&sk)[2], float (&sv)[2]) {
   const bool oka = (unsigned)pa < (unsigned)a.num_blocks;
   const bool okb = (unsigned)pb < (unsigned)a.num_blocks;
-  sk[0] = oka ? a.k_bscale[(int64_t)pa * a.hkv + kvh] : 0.0f;
+  sk[0] = oka ? a.k_bscale[(int64_t)pa * a.hkv + kvh] : 1.0f;
   sv[0] = oka ? a.v_bscale[(int64_t)pa * a.hkv + kvh] : 0.0f;
-  sk[1] = okb ? a.k_bscale[(int64_t)pb * a.hkv + kvh] : 0.0f;
+  sk[1] = okb ? a.k_bscale[(int64_t)pb * a.hkv + kvh] : 1.0f;
   sv[1] = okb ? a.v_bscale[(int64_t)pb * a.hkv + kvh] : 0.0f;
+}
+
+// ---- FP8, per-tensor scales: pairs in a software pipeline ---------------
+// Each iteration takes the softmax of pair i, the QK^T products of pair
+// i + 1 and the PV products of pair i in one straight-line block, so the
+// matrix cores work on pair i + 1 while the vector ALUs take pair i's
+// exponentials.  K halves are loaded three pairs ahead and V halves two,
+// through buffer resources (ids outside the pool: 0 bytes, zeros), so every
+// path issues the same loads and each wait covers only the pair it needs.
+// Nothing in this path may be an inline asm statement: the compiler takes
+// one as a write to memory, and then loads the table entries through the
+// vector memory path (whose waits also cover the tiles in flight) instead
+// of the scalar one.  The rare branches stay branches without it.
+template <bool kV>
+__device__ __forceinline__ void load_half_pipe(TileRegs<true>& ta, TileRegs<true>& tb,
+                                               const PrefillArgs& a, int pa, int pb, int kvh,
+                                               int lane) {
+  constexpr int kTileBytes = kBS * kD;
+  pa = __builtin_amdgcn_readfirstlane(pa);
+  pb = __builtin_amdgcn_readfirstlane(pb);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  const bool oka = (unsigned)pa < (unsigned)a.num_blocks;
+  const bool okb = (unsigned)pb < (unsigned)a.num_blocks;
+  const uint8_t* pool = kV ? a.v_pool : a.k_pool;
+  // a resource of 0 bytes never touches memory, so its base may be anything:
+  // no branch around the address arithmetic
+  const __amdgpu_buffer_rsrc_t ra =
+      byte_range(pool + ((int64_t)pa * a.hkv + kvh) * kTileBytes, oka ? kTileBytes : 0);
+  const __amdgpu_buffer_rsrc_t rb =
+      byte_range(pool + ((int64_t)pb * a.hkv + kvh) * kTileBytes, okb ? kTileBytes : 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const u32x4 xa = __builtin_amdgcn_raw_buffer_load_b128(ra, (i * kWave + lane) * 16, 0, 0);
+    const u32x4 xb = __builtin_amdgcn_raw_buffer_load_b128(rb, (i * kWave + lane) * 16, 0, 0);
+    if constexpr (kV) {
+      ta.v[i] = xa;
+      tb.v[i] = xb;
+    } else {
+      ta.k[i] = xa;
+      tb.k[i] = xb;
+    }
+  }
+}
+
+// S^T of both tiles of a pair for the wave's heads: 16 MFMAs.
+__device__ __forceinline__ void qk_pair(const TileRegs<true>& ta, const TileRegs<true>& tb,
+                                        const f16x8 (&qop)[kHeadsPerWave][4],
+                                        f32x4 (&s)[kHeadsPerWave][2]) {
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) s[h][0] = s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const f16x8 ka = k_operand<true>(ta, m);
+    const f16x8 kb = k_operand<true>(tb, m);
+#pragma unroll
+    for (int h = 0; h < kHeadsPerWave; ++h) {
+      s[h][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[h][m], s[h][0], 0, 0, 0);
+      s[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qop[h][m], s[h][1], 0, 0, 0);
+    }
+  }
+}
+
+// Causal mask of a pair's logits (tokens after the lane's row position).
+__device__ __forceinline__ void mask_pair(f32x4 (&s)[kHeadsPerWave][2], int tb, int qg,
+                                          int pos_j) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int tok = tb + (r >> 2) * kBS + qg * 4 + (r & 3);
+    if (tok > pos_j) {
+#pragma unroll
+      for (int h = 0; h < kHeadsPerWave; ++h) s[h][r >> 2][r & 3] = -INFINITY;
+    }
+  }
+}
+
+// Exponents of a pair's weights relative to each row's reference max (log2
+// units), after rescaling a row whose logits overshoot it (rare: a branch).
+__device__ __forceinline__ void check_pair(const f32x4 (&s)[kHeadsPerWave][2],
+                                           RowState (&st)[kHeadsPerWave], float qk,
+                                           float (&y)[kHeadsPerWave][8]) {
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    const float neg_m = -st[h].m_ref;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) y[h][r] = fmaf(s[h][r >> 2][r & 3], qk, neg_m);
+    float ymax = y[h][0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) ymax = fmaxf(ymax, y[h][r]);
+    if (__any(ymax > kLazyMaxSlack)) {
+      float top = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) top = fmaxf(top, s[h][r >> 2][r & 3] * qk);
+      top = fmaxf(top, __shfl_xor(top, 16, kWave));
+      top = fmaxf(top, __shfl_xor(top, 32, kWave));
+      const float m_upd = fmaxf(st[h].m_ref, top);
+      const float alpha = __builtin_amdgcn_exp2f(st[h].m_ref - m_upd);
+      st[h].l *= alpha;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st[h].acc[n] *= alpha;
+      st[h].m_ref = m_upd;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) y[h][r] = fmaf(s[h][r >> 2][r & 3], qk, -m_upd);
+    }
+  }
+}
+
+// Probabilities as fp16 (the PV product's B operand) and the normaliser.
+__device__ __forceinline__ void probs_pair(const float (&y)[kHeadsPerWave][8],
+                                           RowState (&st)[kHeadsPerWave],
+                                           f16x8 (&p)[kHeadsPerWave]) {
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    float e[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(y[h][r]);
+    st[h].l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
+  }
+}
+
+// O^T += V^T P^T over a pair: 16 MFMAs.
+__device__ __forceinline__ void pv_pair(const TileRegs<true>& ta, const TileRegs<true>& tb,
+                                        const f16x8 (&p)[kHeadsPerWave],
+                                        RowState (&st)[kHeadsPerWave]) {
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const f16x8 v = v_operand<true>(ta, tb, n);
+#pragma unroll
+    for (int h = 0; h < kHeadsPerWave; ++h)
+      st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
+  }
 }
 
 // Grid (ceil(max chunk / (16 rt)), Hkv, B); rt 16-row tiles of ceil(G / 2)
@@ -389,6 +529,53 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
   float vref = 0.0f;  // per-block scales: the largest V scale seen so far
   float inv_vref = 0.0f;
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
+  if constexpr (kFP8 && !kDyn) {
+    // pairs 0 .. np - 1, run two at a time (the buffers alternate); an odd
+    // count adds one pair past the last tile, all of it masked
+    const int np = (ntiles + 1) >> 1;
+    // table entries by scalar loads, from a clamped index so the load is
+    // unconditional (no branch splits the block the loads feed)
+    auto tile_id = [&](int t) {
+      const int v = trow[min(t, ntiles - 1)];
+      return t < ntiles ? v : -1;
+    };
+    if (np > 0) {
+      TileRegs<true> kb[2][2], vb[2][2];
+      load_half_pipe<false>(kb[0][0], kb[0][1], a, tile_id(0), tile_id(1), kvh, lane);
+      load_half_pipe<true>(vb[0][0], vb[0][1], a, tile_id(0), tile_id(1), kvh, lane);
+      load_half_pipe<false>(kb[1][0], kb[1][1], a, tile_id(2), tile_id(3), kvh, lane);
+      load_half_pipe<true>(vb[1][0], vb[1][1], a, tile_id(2), tile_id(3), kvh, lane);
+      f32x4 s[kHeadsPerWave][2];
+      qk_pair(kb[0][0], kb[0][1], qop, s);
+      load_half_pipe<false>(kb[0][0], kb[0][1], a, tile_id(4), tile_id(5), kvh, lane);
+      if (31 > first) {
+        mask_pair(s, 0, qg, pos_c);
+      }
+      // pair i: K of pair i + 1 in kb[(i + 1) % 2], V of pair i in vb[i % 2]
+      auto step = [&](int i, TileRegs<true> (&kn)[2], TileRegs<true> (&vc)[2]) {
+        const int tb = i * 2 * kBS;
+        float y[kHeadsPerWave][8];
+        check_pair(s, st, a.qk_scale, y);
+        if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
+          mask_tail_values<true>(vc[0], tb, qg, L);
+          mask_tail_values<true>(vc[1], tb + kBS, qg, L);
+        }
+        f16x8 p[kHeadsPerWave];
+        probs_pair(y, st, p);
+        qk_pair(kn[0], kn[1], qop, s);
+        load_half_pipe<false>(kn[0], kn[1], a, tile_id(2 * i + 6), tile_id(2 * i + 7), kvh, lane);
+        pv_pair(vc[0], vc[1], p, st);
+        load_half_pipe<true>(vc[0], vc[1], a, tile_id(2 * i + 4), tile_id(2 * i + 5), kvh, lane);
+        if (tb + 4 * kBS - 1 > first) {  // pair i + 1 reaches past the first position
+          mask_pair(s, tb + 2 * kBS, qg, pos_c);
+        }
+      };
+      for (int i = 0; i < np; i += 2) {
+        step(i, kb[1], vb[0]);
+        step(i + 1, kb[0], vb[1]);
+      }
+    }
+  } else {
   for (int c0 = 0; c0 < ntiles; c0 += kWave) {
     const int cnt = min(kWave, ntiles - c0);
     const int tbl = lane < cnt ? trow[c0 + lane] : -1;  // lane i: tile c0 + i
@@ -470,6 +657,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
         }
       }
     }
+  }
   }
 
   if (!row_ok) return;
