@@ -27,13 +27,13 @@
 //     the decode kernel does, tested on each lane's largest logit;
 //   * only the pairs that reach past the row tile's first position apply
 //     the causal mask; value slots past the sequence's end are zeroed;
-//   * FP8 with per-tensor scales runs the pairs as a software pipeline: one
-//     straight-line block takes pair i's exponentials, pair i+1's QK^T
-//     products and pair i's PV products, so the compiler interleaves vector
-//     and matrix work within each wave;
-//   * elsewhere the matrix bursts of a wave run at raised priority
-//     (s_setprio), so the two waves of a SIMD tend to alternate matrix and
-//     vector phases.
+//   * FP8 caches (per-tensor or per-block scales) run the pairs as a software
+//     pipeline: one straight-line block takes pair i's exponentials, pair
+//     i+1's QK^T products and pair i's PV products, so the compiler
+//     interleaves vector and matrix work within each wave;
+//   * the fp16 cache's loop takes one pair at a time and runs its matrix
+//     bursts at raised priority (s_setprio), so the two waves of a SIMD tend
+//     to alternate matrix and vector phases.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -117,171 +117,6 @@ __device__ __forceinline__ f16x8 v_operand(const TileRegs<kFP8>& ta, const TileR
   }
 }
 
-// One pair of tiles (tokens tb .. tb+31) for the wave's query heads.
-// pos_j: position of this lane's query row.  masked: the pair reaches past
-// the workgroup's first position, so tokens after pos_j are dropped.  qk[t]
-// is tile t's logit scale (per-block scales: times the tile's K scale); it
-// is positive, so a row's largest logit is qk times its largest dot product.
-// With per-block scales (kDyn) tile t's probabilities are also multiplied by
-// vmul[t], its V scale relative to the wave's reference, and taken as fp16
-// hi + lo (two PV products, about 22 bits): dynamic scales are for values
-// with outliers, where one fp16 rounding of P is too coarse against the
-// absolute tolerance.  The normaliser sums the unscaled probabilities.
-// The pair's V tiles already loaded (the FP8 path).
-struct VLoaded {
-  static constexpr bool kLate = false;
-  template <class T>
-  __device__ void operator()(T&, T&) const {}
-};
-
-template <bool kFP8, bool kDyn = false, class LateV = VLoaded>
-__device__ __forceinline__ void process_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb_,
-                                             const f16x8 (&qop)[kHeadsPerWave][4],
-                                             RowState (&st)[kHeadsPerWave], int tb, int qg,
-                                             int pos_j, int L, bool masked, const float (&qk)[2],
-                                             const float (&vmul)[2],
-                                             const LateV& late_v = LateV{}) {
-  if constexpr (!LateV::kLate) {
-    if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
-      __asm__ volatile("" ::: "memory");  // keep this rare path a branch
-      mask_tail_values<kFP8>(ta, tb, qg, L);
-      mask_tail_values<kFP8>(tb_, tb + kBS, qg, L);
-    }
-  }
-  f32x4 s[kHeadsPerWave][2];
-  // matrix bursts run at raised priority, so the SIMD's other wave does its
-  // vector work meanwhile instead of both reaching their softmax together
-  __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-  for (int h = 0; h < kHeadsPerWave; ++h) s[h][0] = s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const f16x8 ka = k_operand<kFP8>(ta, m);
-    const f16x8 kb = k_operand<kFP8>(tb_, m);
-#pragma unroll
-    for (int h = 0; h < kHeadsPerWave; ++h) {
-      s[h][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[h][m], s[h][0], 0, 0, 0);
-      s[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qop[h][m], s[h][1], 0, 0, 0);
-    }
-  }
-  __builtin_amdgcn_s_setprio(0);
-  // V loaded late: its loads overlap the softmax, into the K registers'
-  // place, which the products above no longer need
-  late_v(ta, tb_);
-  if (masked) {  // wave-uniform; only the pairs that reach past the first position
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int tok = tb + (r >> 2) * kBS + qg * 4 + (r & 3);
-      if (tok > pos_j) {
-#pragma unroll
-        for (int h = 0; h < kHeadsPerWave; ++h) s[h][r >> 2][r & 3] = -INFINITY;
-      }
-    }
-  }
-  f16x8 p[kHeadsPerWave], plo[kHeadsPerWave];
-#pragma unroll
-  for (int h = 0; h < kHeadsPerWave; ++h) {
-    // exponent of each weight relative to the reference max (log2 units)
-    float y[8];
-    const float neg_m = -st[h].m_ref;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk[r >> 2], neg_m);
-    float ymax = y[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) ymax = fmaxf(ymax, y[r]);
-    if (__any(ymax > kLazyMaxSlack)) {
-      __asm__ volatile("" ::: "memory");  // rare: keep the rescale a branch
-      // the row's new reference: its largest logit so far
-      float top = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) top = fmaxf(top, s[h][r >> 2][r & 3] * qk[r >> 2]);
-      top = fmaxf(top, __shfl_xor(top, 16, kWave));
-      top = fmaxf(top, __shfl_xor(top, 32, kWave));
-      const float m_upd = fmaxf(st[h].m_ref, top);
-      const float alpha = __builtin_amdgcn_exp2f(st[h].m_ref - m_upd);
-      st[h].l *= alpha;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) st[h].acc[n] *= alpha;
-      st[h].m_ref = m_upd;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk[r >> 2], -m_upd);
-    }
-    float e[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(y[r]);
-    st[h].l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    if constexpr (kDyn) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float w = e[r] * vmul[r >> 2];
-        p[h][r] = (_Float16)w;
-        plo[h][r] = (_Float16)(w - (float)p[h][r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
-    }
-  }
-  if constexpr (LateV::kLate) {
-    if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
-      __asm__ volatile("" ::: "memory");
-      mask_tail_values<kFP8>(ta, tb, qg, L);
-      mask_tail_values<kFP8>(tb_, tb + kBS, qg, L);
-    }
-  }
-  __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const f16x8 v = v_operand<kFP8>(ta, tb_, n);
-#pragma unroll
-    for (int h = 0; h < kHeadsPerWave; ++h) {
-      st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
-      if constexpr (kDyn)
-        st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, plo[h], st[h].acc[n], 0, 0, 0);
-    }
-  }
-  __builtin_amdgcn_s_setprio(0);
-}
-
-template <bool kFP8>
-__device__ __forceinline__ void zero_tile(TileRegs<kFP8>& t) {
-#pragma unroll
-  for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
-    t.k[i] = u32x4{0, 0, 0, 0};
-    t.v[i] = u32x4{0, 0, 0, 0};
-  }
-}
-
-// Both tiles of a pair.  Table entries outside the pool read as zeros (the
-// uncommon case takes a branch, so the common path has no zeroing moves).
-template <bool kFP8>
-__device__ __forceinline__ void load_pair(TileRegs<kFP8>& ta, TileRegs<kFP8>& tb,
-                                          const PrefillArgs& a, int pa, int pb, int kvh,
-                                          int lane) {
-  constexpr int kTileBytes = kBS * kD * (kFP8 ? 1 : 2);
-  const bool oka = (unsigned)pa < (unsigned)a.num_blocks;
-  const bool okb = (unsigned)pb < (unsigned)a.num_blocks;
-  const int64_t oa = ((int64_t)(oka ? pa : 0) * a.hkv + kvh) * kTileBytes;
-  const int64_t ob = ((int64_t)(okb ? pb : 0) * a.hkv + kvh) * kTileBytes;
-  const u32x4* ka = reinterpret_cast<const u32x4*>(a.k_pool + oa) + lane;
-  const u32x4* va = reinterpret_cast<const u32x4*>(a.v_pool + oa) + lane;
-  const u32x4* kb = reinterpret_cast<const u32x4*>(a.k_pool + ob) + lane;
-  const u32x4* vb = reinterpret_cast<const u32x4*>(a.v_pool + ob) + lane;
-#pragma unroll
-  for (int i = 0; i < TileRegs<kFP8>::kVecs; ++i) {
-    ta.k[i] = ka[i * kWave];
-    ta.v[i] = va[i * kWave];
-    tb.k[i] = kb[i * kWave];
-    tb.v[i] = vb[i * kWave];
-  }
-  if (!oka || !okb) {
-    __asm__ volatile("" ::: "memory");
-    if (!oka) zero_tile<kFP8>(ta);
-    if (!okb) zero_tile<kFP8>(tb);
-  }
-}
-
 // One half (K or V) of both tiles of a pair, zeros for ids outside the pool
 // (and for tile b when `zero_b`: the pair reaches past the last tile).
 template <bool kFP8, bool kV>
@@ -316,7 +151,6 @@ __device__ __forceinline__ void load_pair_half(TileRegs<kFP8>& ta, TileRegs<kFP8
 // fp16 tiles are twice the registers of FP8 ones: the V halves of a pair
 // are loaded after its QK^T products (process_pair calls this there).
 struct VLate {
-  static constexpr bool kLate = true;
   const PrefillArgs* a;
   int pa, pb, kvh, lane;
   bool zero_b;
@@ -325,22 +159,99 @@ struct VLate {
   }
 };
 
-// The K and V scales of a pair's two (block, head) tiles.  A tile outside
-// the pool (an id past the sequence's last tile, or out of range) reads as
-// zeros; its V scale is 0 and its K scale 1: the causal mask sets such a
-// tile's logits to -inf before they are multiplied by the K scale, and -inf
-// times 0 would be NaN.
-__device__ __forceinline__ void pair_scales(const PrefillArgs& a, int pa, int pb, int kvh,
-                                            float (&sk)[2], float (&sv)[2]) {
-  const bool oka = (unsigned)pa < (unsigned)a.num_blocks;
-  const bool okb = (unsigned)pb < (unsigned)a.num_blocks;
-  sk[0] = oka ? a.k_bscale[(int64_t)pa * a.hkv + kvh] : 1.0f;
-  sv[0] = oka ? a.v_bscale[(int64_t)pa * a.hkv + kvh] : 0.0f;
-  sk[1] = okb ? a.k_bscale[(int64_t)pb * a.hkv + kvh] : 1.0f;
-  sv[1] = okb ? a.v_bscale[(int64_t)pb * a.hkv + kvh] : 0.0f;
+// One pair of fp16 tiles (tokens tb .. tb+31) for the wave's query heads.
+// pos_j: position of this lane's query row.  masked: the pair reaches past
+// the workgroup's first position, so tokens after pos_j are dropped.  qk is
+// the logit scale; it is positive, so a row's largest logit is qk times its
+// largest dot product.  fp16 tiles take twice the registers of FP8 ones: the
+// pair's V halves are loaded (late_v) only after its QK^T products, into the
+// registers K no longer needs, so those loads overlap the softmax.
+__device__ __forceinline__ void process_pair(TileRegs<false>& ta, TileRegs<false>& tb_,
+                                             const f16x8 (&qop)[kHeadsPerWave][4],
+                                             RowState (&st)[kHeadsPerWave], int tb, int qg,
+                                             int pos_j, int L, bool masked, float qk,
+                                             const VLate& late_v) {
+  f32x4 s[kHeadsPerWave][2];
+  // matrix bursts run at raised priority, so the SIMD's other wave does its
+  // vector work meanwhile instead of both reaching their softmax together
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) s[h][0] = s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const f16x8 ka = k_operand<false>(ta, m);
+    const f16x8 kb = k_operand<false>(tb_, m);
+#pragma unroll
+    for (int h = 0; h < kHeadsPerWave; ++h) {
+      s[h][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qop[h][m], s[h][0], 0, 0, 0);
+      s[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qop[h][m], s[h][1], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+  late_v(ta, tb_);
+  if (masked) {  // wave-uniform; only the pairs that reach past the first position
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int tok = tb + (r >> 2) * kBS + qg * 4 + (r & 3);
+      if (tok > pos_j) {
+#pragma unroll
+        for (int h = 0; h < kHeadsPerWave; ++h) s[h][r >> 2][r & 3] = -INFINITY;
+      }
+    }
+  }
+  f16x8 p[kHeadsPerWave];
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    // exponent of each weight relative to the reference max (log2 units)
+    float y[8];
+    const float neg_m = -st[h].m_ref;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk, neg_m);
+    float ymax = y[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) ymax = fmaxf(ymax, y[r]);
+    if (__any(ymax > kLazyMaxSlack)) {
+      __asm__ volatile("" ::: "memory");  // rare: keep the rescale a branch
+      // the row's new reference: its largest logit so far
+      float top = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) top = fmaxf(top, s[h][r >> 2][r & 3] * qk);
+      top = fmaxf(top, __shfl_xor(top, 16, kWave));
+      top = fmaxf(top, __shfl_xor(top, 32, kWave));
+      const float m_upd = fmaxf(st[h].m_ref, top);
+      const float alpha = __builtin_amdgcn_exp2f(st[h].m_ref - m_upd);
+      st[h].l *= alpha;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st[h].acc[n] *= alpha;
+      st[h].m_ref = m_upd;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) y[r] = fmaf(s[h][r >> 2][r & 3], qk, -m_upd);
+    }
+    float e[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(y[r]);
+    st[h].l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
+  }
+  if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
+    __asm__ volatile("" ::: "memory");
+    mask_tail_values<false>(ta, tb, qg, L);
+    mask_tail_values<false>(tb_, tb + kBS, qg, L);
+  }
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const f16x8 v = v_operand<false>(ta, tb_, n);
+#pragma unroll
+    for (int h = 0; h < kHeadsPerWave; ++h)
+      st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
+  }
+  __builtin_amdgcn_s_setprio(0);
 }
 
-// ---- FP8, per-tensor scales: pairs in a software pipeline ---------------
+// ---- FP8 caches: pairs in a software pipeline ---------------------------
 // Each iteration takes the softmax of pair i, the QK^T products of pair
 // i + 1 and the PV products of pair i in one straight-line block, so the
 // matrix cores work on pair i + 1 while the vector ALUs take pair i's
@@ -416,20 +327,20 @@ __device__ __forceinline__ void mask_pair(f32x4 (&s)[kHeadsPerWave][2], int tb, 
 // Exponents of a pair's weights relative to each row's reference max (log2
 // units), after rescaling a row whose logits overshoot it (rare: a branch).
 __device__ __forceinline__ void check_pair(const f32x4 (&s)[kHeadsPerWave][2],
-                                           RowState (&st)[kHeadsPerWave], float qk,
+                                           RowState (&st)[kHeadsPerWave], const float (&qk)[2],
                                            float (&y)[kHeadsPerWave][8]) {
 #pragma unroll
   for (int h = 0; h < kHeadsPerWave; ++h) {
     const float neg_m = -st[h].m_ref;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) y[h][r] = fmaf(s[h][r >> 2][r & 3], qk, neg_m);
+    for (int r = 0; r < 8; ++r) y[h][r] = fmaf(s[h][r >> 2][r & 3], qk[r >> 2], neg_m);
     float ymax = y[h][0];
 #pragma unroll
     for (int r = 1; r < 8; ++r) ymax = fmaxf(ymax, y[h][r]);
     if (__any(ymax > kLazyMaxSlack)) {
       float top = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) top = fmaxf(top, s[h][r >> 2][r & 3] * qk);
+      for (int r = 0; r < 8; ++r) top = fmaxf(top, s[h][r >> 2][r & 3] * qk[r >> 2]);
       top = fmaxf(top, __shfl_xor(top, 16, kWave));
       top = fmaxf(top, __shfl_xor(top, 32, kWave));
       const float m_upd = fmaxf(st[h].m_ref, top);
@@ -439,36 +350,59 @@ __device__ __forceinline__ void check_pair(const f32x4 (&s)[kHeadsPerWave][2],
       for (int n = 0; n < 8; ++n) st[h].acc[n] *= alpha;
       st[h].m_ref = m_upd;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) y[h][r] = fmaf(s[h][r >> 2][r & 3], qk, -m_upd);
+      for (int r = 0; r < 8; ++r) y[h][r] = fmaf(s[h][r >> 2][r & 3], qk[r >> 2], -m_upd);
     }
   }
 }
 
 // Probabilities as fp16 (the PV product's B operand) and the normaliser.
+// With per-block scales (kDyn) each tile's weights are multiplied by its V
+// scale relative to the wave's reference (vm[t]) and taken as fp16 hi + lo,
+// two PV products of about 22 bits together: dynamic scales are for values
+// with outliers, where one fp16 rounding of P is too coarse against the
+// absolute tolerance.  The normaliser sums the unscaled weights.
+template <bool kDyn>
 __device__ __forceinline__ void probs_pair(const float (&y)[kHeadsPerWave][8],
-                                           RowState (&st)[kHeadsPerWave],
-                                           f16x8 (&p)[kHeadsPerWave]) {
+                                           RowState (&st)[kHeadsPerWave], const float (&vm)[2],
+                                           f16x8 (&p)[kHeadsPerWave],
+                                           f16x8 (&plo)[kHeadsPerWave]) {
 #pragma unroll
   for (int h = 0; h < kHeadsPerWave; ++h) {
     float e[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(y[h][r]);
     st[h].l += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    if constexpr (kDyn) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
+      for (int r = 0; r < 8; ++r) {
+        const float w = e[r] * vm[r >> 2];
+        p[h][r] = (_Float16)w;
+        plo[h][r] = (_Float16)(w - (float)p[h][r]);
+      }
+    } else {
+      (void)vm;
+      (void)plo;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
+    }
   }
 }
 
-// O^T += V^T P^T over a pair: 16 MFMAs.
+// O^T += V^T P^T over a pair: 16 MFMAs (32 with the lo halves, kDyn).
+template <bool kDyn>
 __device__ __forceinline__ void pv_pair(const TileRegs<true>& ta, const TileRegs<true>& tb,
                                         const f16x8 (&p)[kHeadsPerWave],
+                                        const f16x8 (&plo)[kHeadsPerWave],
                                         RowState (&st)[kHeadsPerWave]) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const f16x8 v = v_operand<true>(ta, tb, n);
 #pragma unroll
-    for (int h = 0; h < kHeadsPerWave; ++h)
+    for (int h = 0; h < kHeadsPerWave; ++h) {
       st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
+      if constexpr (kDyn)
+        st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, plo[h], st[h].acc[n], 0, 0, 0);
+    }
   }
 }
 
@@ -525,11 +459,10 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
   // its max is finite
   const int pos_c = pos < 0 ? 0 : (pos > L - 1 ? L - 1 : pos);
   const int ntiles = last >= 0 ? last / kBS + 1 : 0;
-  const float qk_one[2] = {a.qk_scale, a.qk_scale}, v_one[2] = {1.0f, 1.0f};
   float vref = 0.0f;  // per-block scales: the largest V scale seen so far
   float inv_vref = 0.0f;
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks;
-  if constexpr (kFP8 && !kDyn) {
+  if constexpr (kFP8) {
     // pairs 0 .. np - 1, run two at a time (the buffers alternate); an odd
     // count adds one pair past the last tile, all of it masked
     const int np = (ntiles + 1) >> 1;
@@ -539,125 +472,102 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
       const int v = trow[min(t, ntiles - 1)];
       return t < ntiles ? v : -1;
     };
+    // per-block scales of a pair (kDyn), by unconditional scalar loads.  A
+    // tile outside the pool (past the sequence's last tile, or an id out of
+    // range) reads as zeros; its V scale is 0 and its K scale 1: the causal
+    // mask sets such a tile's logits to -inf before the K scale multiplies
+    // them, and -inf times 0 would be NaN.
+    auto scales = [&](int i, float (&sk)[2], float (&sv)[2]) {
+      if constexpr (kDyn) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int id = tile_id(2 * i + t);
+          const bool ok = (unsigned)id < (unsigned)a.num_blocks;
+          const int64_t o = (int64_t)(ok ? id : 0) * a.hkv + kvh;
+          const float ks = a.k_bscale[o], vs = a.v_bscale[o];
+          sk[t] = ok ? ks : 1.0f;
+          sv[t] = ok ? vs : 0.0f;
+        }
+      }
+    };
     if (np > 0) {
       TileRegs<true> kb[2][2], vb[2][2];
+      float sk[2][2] = {{1.f, 1.f}, {1.f, 1.f}}, sv[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
       load_half_pipe<false>(kb[0][0], kb[0][1], a, tile_id(0), tile_id(1), kvh, lane);
       load_half_pipe<true>(vb[0][0], vb[0][1], a, tile_id(0), tile_id(1), kvh, lane);
       load_half_pipe<false>(kb[1][0], kb[1][1], a, tile_id(2), tile_id(3), kvh, lane);
       load_half_pipe<true>(vb[1][0], vb[1][1], a, tile_id(2), tile_id(3), kvh, lane);
+      scales(0, sk[0], sv[0]);
+      scales(1, sk[1], sv[1]);
       f32x4 s[kHeadsPerWave][2];
       qk_pair(kb[0][0], kb[0][1], qop, s);
       load_half_pipe<false>(kb[0][0], kb[0][1], a, tile_id(4), tile_id(5), kvh, lane);
-      if (31 > first) {
-        mask_pair(s, 0, qg, pos_c);
-      }
-      // pair i: K of pair i + 1 in kb[(i + 1) % 2], V of pair i in vb[i % 2]
-      auto step = [&](int i, TileRegs<true> (&kn)[2], TileRegs<true> (&vc)[2]) {
+      if (31 > first) mask_pair(s, 0, qg, pos_c);
+      // pair i: K of pair i + 1 in kb[(i + 1) % 2], V of pair i in vb[i % 2],
+      // its scales in sk/sv[i % 2]
+      auto step = [&](int i, TileRegs<true> (&kn)[2], TileRegs<true> (&vc)[2], float (&ski)[2],
+                      float (&svi)[2]) {
         const int tb = i * 2 * kBS;
+        float qk[2] = {a.qk_scale, a.qk_scale}, vm[2] = {1.0f, 1.0f};
+        if constexpr (kDyn) {
+          // the accumulators hold sum p * (V scale / vref) * code: when a
+          // tile's V scale exceeds the reference, rescale them to the new one
+          const float ref = fmaxf(fmaxf(vref, fmaxf(svi[0], svi[1])), 0x1p-126f);
+          if (ref > vref) {  // wave-uniform, rare
+            if (vref > 0.0f) {
+              const float f = vref / ref;
+#pragma unroll
+              for (int h = 0; h < kHeadsPerWave; ++h)
+#pragma unroll
+                for (int nn = 0; nn < 8; ++nn) st[h].acc[nn] *= f;
+            }
+            vref = ref;
+            inv_vref = 1.0f / ref;
+          }
+          qk[0] = a.qk_scale * ski[0];
+          qk[1] = a.qk_scale * ski[1];
+          vm[0] = svi[0] * inv_vref;
+          vm[1] = svi[1] * inv_vref;
+        }
         float y[kHeadsPerWave][8];
-        check_pair(s, st, a.qk_scale, y);
+        check_pair(s, st, qk, y);
         if (tb + 2 * kBS > L) {  // the sequence's last tiles: slots past L may hold anything
           mask_tail_values<true>(vc[0], tb, qg, L);
           mask_tail_values<true>(vc[1], tb + kBS, qg, L);
         }
-        f16x8 p[kHeadsPerWave];
-        probs_pair(y, st, p);
+        f16x8 p[kHeadsPerWave], plo[kHeadsPerWave];
+        probs_pair<kDyn>(y, st, vm, p, plo);
         qk_pair(kn[0], kn[1], qop, s);
         load_half_pipe<false>(kn[0], kn[1], a, tile_id(2 * i + 6), tile_id(2 * i + 7), kvh, lane);
-        pv_pair(vc[0], vc[1], p, st);
+        pv_pair<kDyn>(vc[0], vc[1], p, plo, st);
         load_half_pipe<true>(vc[0], vc[1], a, tile_id(2 * i + 4), tile_id(2 * i + 5), kvh, lane);
+        scales(i + 2, ski, svi);
         if (tb + 4 * kBS - 1 > first) {  // pair i + 1 reaches past the first position
           mask_pair(s, tb + 2 * kBS, qg, pos_c);
         }
       };
       for (int i = 0; i < np; i += 2) {
-        step(i, kb[1], vb[0]);
-        step(i + 1, kb[0], vb[1]);
+        step(i, kb[1], vb[0], sk[0], sv[0]);
+        step(i + 1, kb[0], vb[1], sk[1], sv[1]);
       }
     }
   } else {
-  for (int c0 = 0; c0 < ntiles; c0 += kWave) {
-    const int cnt = min(kWave, ntiles - c0);
-    const int tbl = lane < cnt ? trow[c0 + lane] : -1;  // lane i: tile c0 + i
-    if constexpr (!kFP8) {  // fp16 tiles are twice the registers: one pair at a time,
-                            // its V halves loaded after its QK^T products
+    // fp16 tiles are twice the registers: one pair at a time, its V halves
+    // loaded after its QK^T products
+    for (int c0 = 0; c0 < ntiles; c0 += kWave) {
+      const int cnt = min(kWave, ntiles - c0);
+      const int tbl = lane < cnt ? trow[c0 + lane] : -1;  // lane i: tile c0 + i
       for (int t = 0; t < cnt; t += 2) {
-        TileRegs<kFP8> ta, tb;
+        TileRegs<false> ta, tb;
         const int pa = __builtin_amdgcn_readlane(tbl, t);
         const int pb = t + 1 < cnt ? __builtin_amdgcn_readlane(tbl, t + 1) : pa;
         const bool past = t + 1 >= cnt;     // past the last tile: all masked below
-        load_pair_half<kFP8, false>(ta, tb, a, pa, pb, kvh, lane, past);
+        load_pair_half<false, false>(ta, tb, a, pa, pb, kvh, lane, past);
         const int tok0 = (c0 + t) * kBS;
-        process_pair<kFP8>(ta, tb, qop, st, tok0, qg, pos_c, L, tok0 + 2 * kBS - 1 > first,
-                           qk_one, v_one, VLate{&a, pa, pb, kvh, lane, past});
-      }
-      continue;
-    }
-    // FP8: two pairs in flight, the next pair's loads issued before the
-    // current pair is computed
-    TileRegs<kFP8> buf[2][2];
-    float bsk[2][2], bsv[2][2];  // per-block scales of the pairs in buf (kDyn)
-    {
-      const int pa = __builtin_amdgcn_readlane(tbl, 0);
-      const int pb = cnt > 1 ? __builtin_amdgcn_readlane(tbl, 1) : pa;
-      load_pair<kFP8>(buf[0][0], buf[0][1], a, pa, pb, kvh, lane);
-      if constexpr (kDyn) pair_scales(a, pa, pb, kvh, bsk[0], bsv[0]);
-    }
-    for (int t = 0; t < cnt; t += 4) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tt = t + 2 * u;
-        if constexpr (kDyn) {
-          // With per-block scales the next pair's loads are issued on every
-          // path (ids past the chunk are -1: zeros), so the wait for the
-          // current pair never covers them: 714-724 against 677-687 TFLOP/s on the
-          // 128K chunk.  Without scales the same change measured 1-2 %
-          // slower (1029-1037 against 1051-1056): the kernel is bound by
-          // its vector and matrix issue, not by these loads.
-          const int pa = tt + 2 < cnt ? __builtin_amdgcn_readlane(tbl, tt + 2) : -1;
-          const int pb = tt + 3 < cnt ? __builtin_amdgcn_readlane(tbl, tt + 3) : -1;
-          load_pair<kFP8>(buf[u ^ 1][0], buf[u ^ 1][1], a, pa, pb, kvh, lane);
-          pair_scales(a, pa, pb, kvh, bsk[u ^ 1], bsv[u ^ 1]);
-        }
-        if (tt < cnt) {
-          if (!kDyn && tt + 2 < cnt) {
-            const int pa = __builtin_amdgcn_readlane(tbl, tt + 2);
-            const int pb = tt + 3 < cnt ? __builtin_amdgcn_readlane(tbl, tt + 3) : pa;
-            load_pair<kFP8>(buf[u ^ 1][0], buf[u ^ 1][1], a, pa, pb, kvh, lane);
-          }
-          if (tt + 1 >= cnt) {              // past the last tile: all masked below
-            __asm__ volatile("" ::: "memory");
-            zero_tile<kFP8>(buf[u][1]);
-          }
-          const int tok0 = (c0 + tt) * kBS;
-          if constexpr (kDyn) {
-            // the accumulators hold sum p * (V scale / vref) * code: when a
-            // tile's V scale exceeds the reference, rescale them to the new one
-            const float ref = fmaxf(fmaxf(vref, fmaxf(bsv[u][0], bsv[u][1])), 0x1p-126f);
-            if (ref > vref) {  // wave-uniform, rare
-              __asm__ volatile("" ::: "memory");
-              if (vref > 0.0f) {
-                const float f = vref / ref;
-#pragma unroll
-                for (int h = 0; h < kHeadsPerWave; ++h)
-#pragma unroll
-                  for (int nn = 0; nn < 8; ++nn) st[h].acc[nn] *= f;
-              }
-              vref = ref;
-              inv_vref = 1.0f / ref;
-            }
-            const float qk[2] = {a.qk_scale * bsk[u][0], a.qk_scale * bsk[u][1]};
-            const float vm[2] = {bsv[u][0] * inv_vref, bsv[u][1] * inv_vref};
-            process_pair<kFP8, true>(buf[u][0], buf[u][1], qop, st, tok0, qg, pos_c, L,
-                                     tok0 + 2 * kBS - 1 > first, qk, vm);
-          } else {
-            process_pair<kFP8>(buf[u][0], buf[u][1], qop, st, tok0, qg, pos_c, L,
-                               tok0 + 2 * kBS - 1 > first, qk_one, v_one);
-          }
-        }
+        process_pair(ta, tb, qop, st, tok0, qg, pos_c, L, tok0 + 2 * kBS - 1 > first,
+                     a.qk_scale, VLate{&a, pa, pb, kvh, lane, past});
       }
     }
-  }
   }
 
   if (!row_ok) return;
@@ -737,7 +647,8 @@ pkv_status launch_prefill(const PrefillArgs& a, int32_t max_query_len, int32_t n
   // fp16 tiles: several 16-row tiles per workgroup (up to 8 waves), so each
   // K/V tile is fetched from L2 once for them all: 800 against 770 TFLOP/s
   // on the 128K chunk.  FP8 measured slower that way (987-989 against
-  // 1054-1059): its pairs stay in flight and the loads are not what binds it.
+  // 1054-1059 TFLOP/s, with the loop that preceded its pipeline): its pairs
+  // stay in flight and the loads are not what binds it.
   PrefillArgs c = a;
   c.wpt = (a.g + kHeadsPerWave - 1) / kHeadsPerWave;
   c.rt = kFP8 ? 1 : std::max(1, 8 / c.wpt);
