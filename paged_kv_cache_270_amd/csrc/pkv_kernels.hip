@@ -464,7 +464,7 @@ __device__ __forceinline__ void process_tile(TileRegs<kFP8>& t, const f16x8 (&qo
   }
 }
 
-// A prefix item whose four waves share its tiles (FP8, per-tensor scales):
+// A prefix item whose four waves share its tiles (FP8; per-tensor or per-block scales):
 // every wave serves its own members (16 MFMA columns) over every tile of the
 // item's prefix partition.  Each tile is loaded once per workgroup -- a
 // 1 KiB quarter per wave: K bytes 0-1023, K 1024-2047, V 0-1023, V 1024-2047
@@ -505,6 +505,7 @@ __device__ __forceinline__ void item_stage(uint8_t* buf, u32x4 raw, int w, int l
   dst[1] = __builtin_bit_cast(u32x4, f16x8{h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]});
 }
 
+template <bool kDyn>
 __device__ void item_shared(const DecodeArgs& a, const f16x8 (&qop)[4], SoftmaxState& st,
                             const int32_t* trow, int kvh, int nblk, int pidx, int member,
                             int lane, int w, uint8_t* lds) {
@@ -517,6 +518,25 @@ __device__ void item_shared(const DecodeArgs& a, const f16x8 (&qop)[4], SoftmaxS
   for (int c0 = 0; c0 < nblk; c0 += kWave) {
     const int cnt = min(kWave, nblk - c0);
     const int tbl = lane < cnt ? trow[c0 + lane] : 0;
+    // per-block scales, as the tails take them: lane i holds tile c0 + i's K
+    // scale and its V scale relative to the wave's reference
+    float k_mul = 1.0f, v_mul = 1.0f;
+    if constexpr (kDyn) {
+      float ks = 0.0f, vs = 0.0f;
+      if (lane < cnt && (unsigned)tbl < (unsigned)a.num_blocks) {
+        ks = a.k_bscale[(int64_t)tbl * a.hkv + kvh];
+        vs = a.v_bscale[(int64_t)tbl * a.hkv + kvh];
+      }
+      const float ref = fmaxf(fmaxf(st.vref, wave_max(vs)), 0x1p-126f);
+      if (ref > st.vref && st.vref > 0.0f) {  // wave-uniform: rescale what is accumulated
+        const float f = st.vref / ref;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) st.acc[n] *= f;
+      }
+      st.vref = ref;
+      k_mul = ks;
+      v_mul = vs / ref;
+    }
     u32x4 raw[kItemRing];
 #pragma unroll
     for (int r = 0; r < kItemRing; ++r)
@@ -541,7 +561,13 @@ __device__ void item_shared(const DecodeArgs& a, const f16x8 (&qop)[4], SoftmaxS
             t.v[q] = *reinterpret_cast<const u32x4*>(buf + (2 + (q >> 1)) * 2048 + 32 * lane +
                                                      16 * (q & 1));
           // prefix tokens are all valid: L is the prefix length
-          process_tile<false, true, true>(t, qop, st, 0, qg, kBS, a.qk_scale);
+          if constexpr (kDyn)
+            process_tile<false, true, true, true>(
+                t, qop, st, 0, qg, kBS, a.qk_scale,
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k_mul), ii)),
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_mul), ii)));
+          else
+            process_tile<false, true, true>(t, qop, st, 0, qg, kBS, a.qk_scale);
           ++g;
           if (ii + 1 < cnt) {
             const int kNext = (r + 1) % kItemRing;  // static once unrolled
@@ -555,6 +581,10 @@ __device__ void item_shared(const DecodeArgs& a, const f16x8 (&qop)[4], SoftmaxS
     }
   }
   __builtin_amdgcn_s_setprio(0);
+  if constexpr (kDyn) {  // back from units of the wave's V reference
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.acc[n] *= st.vref;
+  }
   // the members' partials, straight from registers
   float l_run = st.l;
   l_run += __shfl_xor(l_run, 16, kWave);
@@ -600,7 +630,7 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
   bool item = false;
   int item_member = -1;  // a prefix item: the member of this lane's column
   // prefix items whose waves share the tiles (item_shared)
-  constexpr bool kSharedItem = kCasc && kFP8 && !kDyn && kNW == kItemWaves;
+  constexpr bool kSharedItem = kCasc && kFP8 && kNW == kItemWaves;
   int qrow = -1;       // this lane's query row [B*Hq], -1 = column unused
   if constexpr (kCasc) {
     if (b < a.casc_items) {
@@ -686,8 +716,8 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
 
   if constexpr (kSharedItem) {
     if (item) {  // workgroup-uniform
-      item_shared(a, qop, st, a.block_tables + (int64_t)b * a.max_blocks + blk0, kvh, nblk,
-                  pidx, item_member, lane, w, reinterpret_cast<uint8_t*>(smem));
+      item_shared<kDyn>(a, qop, st, a.block_tables + (int64_t)b * a.max_blocks + blk0, kvh,
+                        nblk, pidx, item_member, lane, w, reinterpret_cast<uint8_t*>(smem));
       return;
     }
   }
@@ -865,7 +895,10 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
 // VGPRs (3 waves per SIMD).  The per-block-scale variant fits in about 150
 // without spilling; held to 128 (4 waves), it spilled once the next tile's
 // loads stayed in flight across the current tile's arithmetic.  The cascade's
-// loop over units of the flat grid otherwise grows it past 168.
+// loop over units of the flat grid otherwise grows it past 168.  The FP8
+// cascade with fewer than kItemWaves waves (short partitions; its items then
+// do not share their tiles) needs more than 168 and is held to 256 (2 waves
+// per SIMD) instead of spilling.
 // Decode partition kernel: one unit per workgroup, grid (n_p_max, Hkv, B) or
 // (n_p_max, Hkv, items + B) for the cascade; or, with the cascade's flat
 // grid, Hkv * n workgroups, KV head fastest: workgroup i takes unit i / Hkv
@@ -874,7 +907,9 @@ __device__ __forceinline__ void partition_unit(const DecodeArgs& a, float* smem,
 template <bool kFP8, bool kHwCvt, bool kSplitP, int kPD, int kNW, bool kDyn = false,
           bool kAppend = false, bool kCasc = false>
 __global__ void __launch_bounds__(kNW * kWave)
-__attribute__((amdgpu_waves_per_eu(kDyn || (kCasc && kFP8) ? 3 : 1)))
+__attribute__((amdgpu_waves_per_eu((kCasc && kFP8 && kNW < kItemWaves)
+                                       ? 2
+                                       : (kDyn || (kCasc && kFP8) ? 3 : 1))))
 decode_partition_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   if constexpr (kCasc) {
@@ -2353,9 +2388,9 @@ static pkv_status run_cascade(DecodePlan& pl, const int32_t* prefix_blocks,
   // columns per wave
   int nw = waves_for(pl);
   while (nw > 1 && partition_lds(nw, kMaxG, append, true) > 65536) nw /= 2;
-  // FP8 per-tensor items with four waves share their tiles: each wave takes
-  // its own members
-  const bool shared_items = pl.fp8 && !pl.dyn && nw == kItemWaves;
+  // FP8 items with four waves share their tiles: each wave takes its own
+  // members
+  const bool shared_items = pl.fp8 && nw == kItemWaves;
   const int per_item = shared_items ? nw * members : members;
   const int64_t chunks = num_groups > 0 ? (group_cap + per_item - 1) / per_item : 0;
   const int64_t items = (int64_t)num_groups * chunks;
