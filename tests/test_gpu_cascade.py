@@ -284,6 +284,51 @@ def test_cascade_shared_prefix_full_step():
     assert got.shape == (B, wl.num_q_heads, D)
 
 
+def test_cascade_block_scales_shared_prefix_full():
+    """The 256-sequence shared-prefix batch at full size over per-(block, KV
+    head) FP8 scales, decoded as the benchmark's block-scale step decodes it
+    (groups, longest-tail order and tail units from the host pool, the
+    automatic partition size; the prefix items' four waves share each tile).
+    Every slot of the pool is written by the oracle's dynamic write from rows
+    whose magnitude varies from slot to slot, so the scales differ from block
+    to block and the waves' V reference grows; all 256 outputs must match the
+    oracle's decode with block scales."""
+    base = workloads.shared_prefix()
+    tables, lens, prefix, garr, max_pre, order, units, tmap = _pool_built(base)
+    B, Hq, Hkv, NB = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.num_blocks
+    T = NB * 16
+    mag = torch.exp(1.5 * torch.randn((T, 1, 1), generator=torch.Generator().manual_seed(83)))
+    mag = mag.cuda()
+    k = (workloads.randn_f16((T, Hkv, D), 84, "cuda").float() * mag).half().cpu().numpy()
+    v = (workloads.randn_f16((T, Hkv, D), 85, "cuda").float() * mag.flip(0)).half().cpu().numpy()
+    torch.cuda.empty_cache()
+    n = NB * Hkv * 16 * D
+    kh, vh = np.zeros(n, np.uint8), np.zeros(n, np.uint8)
+    ksh, vsh = np.zeros((NB, Hkv), np.float32), np.zeros((NB, Hkv), np.float32)
+    oracle.reshape_and_cache_dynamic(k, v, kh, vh, ksh, vsh, np.arange(T, dtype=np.int64), Hkv)
+    del k, v
+    layout = pkv.CacheLayout(NB, Hkv, pkv.PKV_FP8_E4M3FN)
+    q = workloads.randn_f16((B, Hq, D), 86, "cuda")
+    sm = float(np.float32(1 / np.sqrt(D)))
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    pkv.pkv_paged_attention_decode_cascade_dynamic(
+        out, q, torch.from_numpy(kh).cuda(), torch.from_numpy(vh).cuda(),
+        torch.from_numpy(ksh).cuda(), torch.from_numpy(vsh).cuda(),
+        torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), int(lens.max()),
+        layout, sm, torch.from_numpy(prefix).cuda(), torch.from_numpy(garr).cuda(), max_pre, 0,
+        seq_order=torch.from_numpy(order).cuda(), tail_units=units,
+        tail_map=torch.from_numpy(tmap).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.paged_attention_decode_dynamic(q.cpu().numpy(), kh, vh, ksh, vsh, tables, lens,
+                                                Hkv, sm, THREADS)
+    got = out.cpu().numpy()
+    err = max_err(got, ref)
+    print(f"[parity] cascade block scales, shared-prefix B=256 full: max abs err {err:.3e}",
+          flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL[True]
+
+
 def test_cascade_rejects_bad_arguments():
     wl, groups, prefix = _grouped(SPEC, SOLO, 8, 2, True, seed=76)
     prep = Prepared(wl)
