@@ -274,3 +274,52 @@ def test_prefill_with_block_scales_matches_oracle(hq, hkv):
     print(f"[parity] dynamic prefill Hq={hq} Hkv={hkv}: max abs err {err:.3e}", flush=True)
     assert np.isfinite(got).all()
     assert err <= TOL[True]
+
+
+def test_prefill_with_block_scales_out_of_range_ids_read_as_zeros():
+    """Table entries outside [0, num_blocks) inside a sequence's used tiles
+    read as zero tiles whatever scales the pool holds; the other sequences
+    are untouched.  The oracle sees those entries pointing at an appended
+    all-zero block."""
+    NB, hkv, hq = 64, 2, 8
+    pool = DynPool(NB, hkv, 77)
+    lens = np.array([75, 333, 17], np.int32)
+    chunks = np.array([75, 150, 17], np.int32)
+    perm = np.random.default_rng(78).permutation(NB)
+    tables, pos = np.zeros((len(lens), 24), np.int32), 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // BS)
+        tables[b, :n] = perm[pos:pos + n]
+        tables[b, n:] = perm[(pos + n) % NB]
+        pos += n
+    for b, L in enumerate(lens):
+        sl = oracle.slots_for(tables, [b] * int(L), range(int(L)))
+        pool.write(_rows(int(L), hkv, 600 + 7 * b), _rows(int(L), hkv, 603 + 7 * b), sl)
+    pool.check_equal()
+    bad = tables.copy()
+    bad[1, 3] = NB + 1000
+    bad[1, 10] = -7
+    bad[1, 11] = 2 ** 31 - 1
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = workloads.randn_f16((int(qs[-1]), hq, D), 611, "cuda")
+    out = torch.empty((int(qs[-1]), hq, D), dtype=torch.float32, device="cuda")
+    sm = float(np.float32(1 / np.sqrt(D)))
+    pkv.pkv_paged_prefill_attention_dynamic(out, q, pool.kd, pool.vd, pool.ksd, pool.vsd,
+                                            torch.from_numpy(bad).cuda(),
+                                            torch.from_numpy(lens).cuda(),
+                                            torch.from_numpy(qs).cuda(), int(chunks.max()),
+                                            int(lens.max()), pool.layout, sm)
+    torch.cuda.synchronize()
+    tile = hkv * BS * D
+    zero = np.zeros(tile, np.uint8)
+    one = np.ones((1, hkv), np.float32)
+    ref_bt = np.where((bad < 0) | (bad >= NB), NB, bad).astype(np.int32)
+    ref = oracle.paged_prefill_attention_dynamic(
+        q.cpu().numpy(), np.concatenate([pool.kh, zero]), np.concatenate([pool.vh, zero]),
+        np.concatenate([pool.ksh, one]), np.concatenate([pool.vsh, one]), ref_bt, lens, qs,
+        hkv, sm, THREADS)
+    got = out.cpu().numpy()
+    err = max_err(got, ref)
+    print(f"[parity] dynamic prefill, ids out of range: max abs err {err:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL[True]

@@ -165,3 +165,33 @@ def test_prefill_mixed_batch_sampled_rows():
     err = _sampled_rows_check(wl, rows, 900)
     print(f"[parity] prefill mixed batch (sampled rows): max abs err {err:.3e}", flush=True)
     assert err <= TOL[True]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_out_of_range_block_ids_read_as_zeros(fp8):
+    """Table entries outside [0, num_blocks) inside a sequence's used tiles
+    read as zero tiles (zero K rows, zero V rows); the other sequences of the
+    batch are untouched.  The oracle sees the same table with those entries
+    pointing at an appended all-zero block."""
+    lens = [75, 333, 17]
+    NB, Hkv, Hq = 48, 2, 8
+    kh, vh, bt, ks, vs = _pool(lens, Hkv, fp8, NB, 41)
+    bad = bt.copy()
+    bad[1, 3] = NB + 1000
+    bad[1, 10] = -7
+    bad[1, 11] = 2 ** 31 - 1
+    chunks = [75, 150, 17]
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = workloads.randn_f16((int(qs[-1]), Hq, D), 43 + int(fp8), "cuda")
+    got = _run(q, kh, vh, bad, lens, qs, Hkv, fp8, ks, vs, NB)
+    tile = Hkv * BS * D * (1 if fp8 else 2)
+    zero = np.zeros(tile, np.uint8)
+    ref_bt = np.where((bad < 0) | (bad >= NB), NB, bad).astype(np.int32)
+    ref = oracle.paged_prefill_attention(q.cpu().numpy(), np.concatenate([kh, zero]),
+                                         np.concatenate([vh, zero]), ref_bt, lens, qs, Hkv,
+                                         fp8, float(np.float32(1 / np.sqrt(D))), ks, vs,
+                                         THREADS)
+    err = max_err(got, ref)
+    print(f"[parity] prefill fp8={fp8} ids out of range: max abs err {err:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL[fp8]
