@@ -370,7 +370,9 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
 //
 // Three launches (one for calls of at most 64 tokens, dyn_write_small_kernel
 // below), because the new scale of a block depends on every token the call
-// writes into it:
+// writes into it; calls of more than 512 tokens first write the blocks they
+// fill whole in the tile-building pass, which marks them, and the row passes
+// skip those:
 //   1. clear the scratch entries of the touched blocks;
 //   2. MaxAbs of each new row into the scratch (integer atomic max of the
 //      non-negative float bits) and the written offsets (atomic or);
@@ -391,37 +393,30 @@ __device__ __forceinline__ uint32_t requant_code(uint32_t c, float r) {
   return e4m3_from_f32(e4m3_value(c) * r);
 }
 
+// One thread per token.  A block's scratch entries need clearing once, by
+// any of the call's tokens in it; a token clears them where it starts a run
+// of consecutive slots (offset 0, or the previous token's slot not the one
+// before its own).  Following any token's run back leads to such a token in
+// the same block, and a bulk fill clears each block once instead of 16 times.
 __global__ void __launch_bounds__(256)
-dyn_clear_kernel(const int64_t* __restrict__ slots, int64_t total, int per_block,
+dyn_clear_kernel(const int64_t* __restrict__ slots, int64_t num_tokens, int per_block,
                  int64_t num_slots, uint32_t* __restrict__ amax, uint32_t* __restrict__ written) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;
-  const int64_t tok = gid / (per_block + 1);
-  const int j = (int)(gid - tok * (per_block + 1));
+  const int64_t tok = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tok >= num_tokens) return;
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= num_slots) return;
+  if ((slot & 15) != 0 && tok > 0 && slots[tok - 1] == slot - 1) return;
   const int64_t blk = slot >> 4;
-  if (j < per_block)
-    amax[blk * per_block + j] = 0u;
-  else
-    written[blk] = 0u;
+  for (int j = 0; j < per_block; ++j) amax[blk * per_block + j] = 0u;
+  written[blk] = 0u;
 }
 
-// One thread per (token, kv head, run of 8 channels), as the plain write;
-// the 16 threads of a row are 16 consecutive lanes.
-__global__ void __launch_bounds__(256)
-dyn_amax_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
-                const int64_t* __restrict__ slots, int64_t total, int hkv, int64_t num_slots,
-                uint32_t* __restrict__ amax, uint32_t* __restrict__ written) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;                  // total is a multiple of 16: whole rows leave
-  const int c = (int)(gid & 15);
-  const int64_t th = gid >> 4;
-  const int64_t tok = th / hkv;
-  const int h = (int)(th - tok * hkv);
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;  // the same for all 16 lanes of the row
-  if (written[slot >> 4] & 0x80000000u) return;  // a whole block, already written
+// MaxAbs of one (token th / hkv, kv head h) row into the scratch: 16
+// consecutive lanes, lane c a run of 8 channels, as the plain write.
+__device__ __forceinline__ void amax_row(const u32x4* __restrict__ key,
+                                         const u32x4* __restrict__ value, int64_t th, int h,
+                                         int64_t slot, int c, int hkv, uint32_t* __restrict__ amax,
+                                         uint32_t* __restrict__ written) {
   uint32_t km = max_abs_bits8(key[th * 16 + c]);
   uint32_t vm = max_abs_bits8(value[th * 16 + c]);
 #pragma unroll
@@ -436,6 +431,25 @@ dyn_amax_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
     atomicMax(a + 1, __float_as_uint(f16_bits_to_float(vm)));
     if (h == 0) atomicOr(written + blk, 1u << (slot & 15));
   }
+}
+
+// Rows of calls of up to kDynManyRows rows: one 16-lane group per row.
+// Larger calls (bulk fills, long prefill chunks) go through dyn_by_token
+// below.
+__global__ void __launch_bounds__(256)
+dyn_amax_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                const int64_t* __restrict__ slots, int64_t total, int hkv, int64_t num_slots,
+                uint32_t* __restrict__ amax, uint32_t* __restrict__ written) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;                  // total is a multiple of 16: whole rows leave
+  const int c = (int)(gid & 15);
+  const int64_t th = gid >> 4;
+  const int64_t tok = th / hkv;
+  const int h = (int)(th - tok * hkv);
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;  // the same for all 16 lanes of the row
+  if (written[slot >> 4] & 0x80000000u) return;  // a whole block, already written
+  amax_row(key, value, th, h, slot, c, hkv, amax, written);
 }
 
 // Re-encode channels 8c .. 8c+7 of every slot of one FP8 tile outside `keep`.
@@ -468,25 +482,20 @@ __device__ __forceinline__ void requant_v_rows(uint8_t* vp, int c, uint32_t keep
   }
 }
 
-__global__ void __launch_bounds__(256)
-dyn_write_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
-                 uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-                 float* __restrict__ k_bscale, float* __restrict__ v_bscale,
-                 const int64_t* __restrict__ slots, int64_t total, int hkv, int64_t num_slots,
-                 const uint32_t* __restrict__ amax, const uint32_t* __restrict__ written) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;
-  const int c = (int)(gid & 15);
-  const int64_t th = gid >> 4;
-  const int64_t tok = th / hkv;
-  const int h = (int)(th - tok * hkv);
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;
+// Encode one row with its tile's new scale; the call's token with the
+// lowest offset in the block re-encodes the other slots and stores the new
+// scales.  mask: the block's mark (bit t: offset t written by this call).
+__device__ __forceinline__ void write_row(const u32x4* __restrict__ key,
+                                          const u32x4* __restrict__ value,
+                                          uint8_t* __restrict__ k_pool,
+                                          uint8_t* __restrict__ v_pool,
+                                          float* __restrict__ k_bscale,
+                                          float* __restrict__ v_bscale, int64_t th, int h,
+                                          int64_t slot, uint32_t mask, int c, int hkv,
+                                          const uint32_t* __restrict__ amax) {
   const int64_t blk = slot >> 4;
   const int off = (int)(slot & 15);
   const int64_t tile = blk * hkv + h;
-  const uint32_t mask = written[blk];
-  if (mask & 0x80000000u) return;            // a whole block, already written
   const bool fresh = (mask & 1u) != 0;
   const float min_scale = 0x1p-126f;
   const float sk_old = fresh ? 0.0f : k_bscale[tile];
@@ -505,6 +514,70 @@ dyn_write_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
   }
 }
 
+__global__ void __launch_bounds__(256)
+dyn_write_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                 uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                 float* __restrict__ k_bscale, float* __restrict__ v_bscale,
+                 const int64_t* __restrict__ slots, int64_t total, int hkv, int64_t num_slots,
+                 const uint32_t* __restrict__ amax, const uint32_t* __restrict__ written) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int c = (int)(gid & 15);
+  const int64_t th = gid >> 4;
+  const int64_t tok = th / hkv;
+  const int h = (int)(th - tok * hkv);
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const uint32_t mask = written[slot >> 4];
+  if (mask & 0x80000000u) return;            // a whole block, already written
+  write_row(key, value, k_pool, v_pool, k_bscale, v_bscale, th, h, slot, mask, c, hkv, amax);
+}
+
+// Both passes for calls of more than kDynManyRows rows.  There the
+// tile-building pass has usually written nearly every block whole, and one
+// 16-lane group per row spent the launch on waves that only found that out
+// (110 us of dispatch and two dependent loads each for the 524,288-token
+// fill).  Here a wave takes kDynWaveTokens consecutive tokens: one lane per
+// token reads its slot and its block's mark, and the wave then works only
+// on the tokens left, four rows (kv heads) at a time.
+constexpr int kDynWaveTokens = 16;
+
+template <bool kWrite>
+__global__ void __launch_bounds__(256)
+dyn_by_token_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                    float* __restrict__ k_bscale, float* __restrict__ v_bscale,
+                    const int64_t* __restrict__ slots, int64_t num_tokens, int hkv,
+                    int64_t num_slots, uint32_t* __restrict__ amax,
+                    uint32_t* __restrict__ written) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kDynWaveTokens;
+  int64_t my_slot = -1;
+  if (lane < kDynWaveTokens && t0 + lane < num_tokens) my_slot = slots[t0 + lane];
+  const bool valid = my_slot >= 0 && my_slot < num_slots;
+  // the amax pass only reads the whole-block bit (it sets the others itself);
+  // the write pass reads the final mark
+  const uint32_t my_mark = valid ? written[my_slot >> 4] : 0x80000000u;
+  uint64_t left = __ballot(!(my_mark & 0x80000000u));
+  const int c = lane & 15, q = lane >> 4;
+  while (left != 0) {                        // uniform over the wave
+    const int i = __builtin_ctzll(left);
+    left &= left - 1;
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)my_slot, i, kWave);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)((uint64_t)my_slot >> 32), i, kWave);
+    const int64_t slot = (int64_t)(((uint64_t)hi << 32) | lo);
+    const uint32_t mark = (uint32_t)__shfl((int)my_mark, i, kWave);
+    for (int h = q; h < hkv; h += 4) {       // the same for the 16 lanes of a row
+      const int64_t th = (t0 + i) * hkv + h;
+      if constexpr (kWrite)
+        write_row(key, value, k_pool, v_pool, k_bscale, v_bscale, th, h, slot, mark, c, hkv,
+                  amax);
+      else
+        amax_row(key, value, th, h, slot, c, hkv, amax, written);
+    }
+  }
+}
+
 // Calls of at most one wave of tokens (a decode step) in one launch: each row
 // finds the call's tokens in its block by comparing the call's slots, which
 // one wave holds (lane l: token l), and computes the block's MaxAbs and
@@ -512,6 +585,7 @@ dyn_write_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
 // dyn_write_kernel: the same scale, codes and re-encoding.  Thread mapping
 // as the plain write: 16 lanes per (token, kv head) row, 4 rows per wave.
 constexpr int kDynSmallTokens = kWave;
+constexpr int64_t kDynManyRows = (int64_t)1 << 17;
 
 __global__ void __launch_bounds__(256)
 dyn_write_small_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
@@ -718,9 +792,8 @@ extern "C" pkv_status pkv_reshape_and_cache_dynamic(
   const int hkv = layout->num_kv_heads;
   const int64_t total = (int64_t)num_tokens * hkv * 16;
   const int64_t blocks = (total + 255) / 256;
-  const int64_t clear_total = (int64_t)num_tokens * (2 * hkv + 1);
-  const int64_t clear_blocks = (clear_total + 255) / 256;
-  if (blocks > 0x7FFFFFFF || clear_blocks > 0x7FFFFFFF) return PKV_ERR_INVALID_ARG;
+  const int64_t clear_blocks = ((int64_t)num_tokens + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return PKV_ERR_INVALID_ARG;
   const int64_t num_slots = (int64_t)layout->num_blocks * kBS;
   uint32_t* amax = static_cast<uint32_t*>(workspace);
   uint32_t* written = amax + (int64_t)layout->num_blocks * 2 * hkv;
@@ -734,7 +807,7 @@ extern "C" pkv_status pkv_reshape_and_cache_dynamic(
     return launch_status();
   }
   dyn_clear_kernel<<<dim3((unsigned)clear_blocks), dim3(256), 0, s>>>(
-      slot_mapping, clear_total, 2 * hkv, num_slots, amax, written);
+      slot_mapping, (int64_t)num_tokens, 2 * hkv, num_slots, amax, written);
   // blocks the call fills whole: tiles, scales and marks in one pass
   if (num_tokens > kRowWriteMaxTokens) {
     st = launch_status();
@@ -744,13 +817,25 @@ extern "C" pkv_status pkv_reshape_and_cache_dynamic(
                                  s);
     if (st != PKV_OK) return st;
   }
-  dyn_amax_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-      static_cast<const u32x4*>(key), static_cast<const u32x4*>(value), slot_mapping, total, hkv,
-      num_slots, amax, written);
-  dyn_write_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-      static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
-      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_block_scales,
-      v_block_scales, slot_mapping, total, hkv, num_slots, amax, written);
+  if ((int64_t)num_tokens * hkv > kDynManyRows) {
+    const int64_t waves = ((int64_t)num_tokens + kDynWaveTokens - 1) / kDynWaveTokens;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    dyn_by_token_kernel<false><<<grid, dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value), nullptr, nullptr,
+        nullptr, nullptr, slot_mapping, num_tokens, hkv, num_slots, amax, written);
+    dyn_by_token_kernel<true><<<grid, dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
+        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_block_scales,
+        v_block_scales, slot_mapping, num_tokens, hkv, num_slots, amax, written);
+  } else {
+    dyn_amax_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value), slot_mapping, total,
+        hkv, num_slots, amax, written);
+    dyn_write_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(key), static_cast<const u32x4*>(value),
+        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_block_scales,
+        v_block_scales, slot_mapping, total, hkv, num_slots, amax, written);
+  }
   return launch_status();
 }
 

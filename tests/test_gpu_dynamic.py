@@ -323,3 +323,35 @@ def test_prefill_with_block_scales_out_of_range_ids_read_as_zeros():
     print(f"[parity] dynamic prefill, ids out of range: max abs err {err:.3e}", flush=True)
     assert np.isfinite(got).all()
     assert err <= TOL[True]
+
+
+def test_large_scattered_calls_are_bit_exact():
+    """Calls of more than 2^17 (token, head) rows, where each lane of the
+    MaxAbs and encode launches takes several rows: whole blocks in order
+    (the tile-building pass) mixed with scattered slots, skipped and
+    out-of-pool slots; then a second call whose larger values grow the
+    scales of blocks the first one wrote (re-encoding their other slots)."""
+    NB, hkv = 2048, 8
+    pool = DynPool(NB, hkv, 31)
+    rng = np.random.default_rng(32)
+    perm = rng.permutation(NB)
+    whole = perm[:256]
+    rest = np.sort(perm[256:])
+    whole_slots = (whole[:, None].astype(np.int64) * BS + np.arange(BS)).reshape(-1)
+    free = (rest[:, None].astype(np.int64) * BS + np.arange(BS)).reshape(-1)
+    scat = rng.choice(free, 16000, replace=False)
+    slots = np.concatenate([whole_slots, scat, [-1, NB * BS, NB * BS + 5, -3]])
+    order = rng.permutation(slots.size - 4096) + 4096     # whole blocks stay in order
+    slots = np.concatenate([slots[:4096], slots[order]])
+    T = slots.size
+    assert T * hkv > (1 << 17)
+    pool.write(_rows(T, hkv, 700), _rows(T, hkv, 702), slots)
+    pool.check_equal()
+    # second call: other slots of the same blocks and some slots again, values 8x larger
+    scat2 = rng.choice(np.concatenate([free, whole_slots]), 18000, replace=False)
+    k2 = (_rows(scat2.size, hkv, 704).float() * 8).clamp(-60000, 60000).half()
+    v2 = (_rows(scat2.size, hkv, 706).float() * 8).clamp(-60000, 60000).half()
+    pool.write(k2, v2, scat2)
+    pool.check_equal()
+    print(f"[parity] dynamic write, {T} + {scat2.size} scattered tokens x {hkv} heads: "
+          "pools and scales bit-exact", flush=True)
