@@ -39,6 +39,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pkv.h"
 #include "pkv_check.h"
@@ -357,15 +358,17 @@ __device__ __forceinline__ void check_pair(const f32x4 (&s)[kHeadsPerWave][2],
 
 // Probabilities as fp16 (the PV product's B operand) and the normaliser.
 // With per-block scales (kDyn) each tile's weights are multiplied by its V
-// scale relative to the wave's reference (vm[t]) and taken as fp16 hi + lo,
-// two PV products of about 22 bits together: dynamic scales are for values
-// with outliers, where one fp16 rounding of P is too coarse against the
-// absolute tolerance.  The normaliser sums the unscaled weights.
-template <bool kDyn>
+// scale relative to the wave's reference (vm[t]).  kLo: the weights are taken
+// as fp16 hi + lo, two PV products of about 22 bits together, for rows whose
+// V values are large (see kHiOnlyVRef): there one fp16 rounding of P is too
+// coarse against the absolute tolerance.  The normaliser sums the unscaled
+// weights.
+template <bool kDyn, bool kLo>
 __device__ __forceinline__ void probs_pair(const float (&y)[kHeadsPerWave][8],
                                            RowState (&st)[kHeadsPerWave], const float (&vm)[2],
                                            f16x8 (&p)[kHeadsPerWave],
                                            f16x8 (&plo)[kHeadsPerWave]) {
+  static_assert(kDyn || !kLo, "the lo halves are for per-block scales");
 #pragma unroll
   for (int h = 0; h < kHeadsPerWave; ++h) {
     float e[8];
@@ -377,19 +380,19 @@ __device__ __forceinline__ void probs_pair(const float (&y)[kHeadsPerWave][8],
       for (int r = 0; r < 8; ++r) {
         const float w = e[r] * vm[r >> 2];
         p[h][r] = (_Float16)w;
-        plo[h][r] = (_Float16)(w - (float)p[h][r]);
+        if constexpr (kLo) plo[h][r] = (_Float16)(w - (float)p[h][r]);
       }
     } else {
       (void)vm;
-      (void)plo;
 #pragma unroll
       for (int r = 0; r < 8; ++r) p[h][r] = (_Float16)e[r];
     }
+    (void)plo;
   }
 }
 
-// O^T += V^T P^T over a pair: 16 MFMAs (32 with the lo halves, kDyn).
-template <bool kDyn>
+// O^T += V^T P^T over a pair: 16 MFMAs (32 with the lo halves, kLo).
+template <bool kLo>
 __device__ __forceinline__ void pv_pair(const TileRegs<true>& ta, const TileRegs<true>& tb,
                                         const f16x8 (&p)[kHeadsPerWave],
                                         const f16x8 (&plo)[kHeadsPerWave],
@@ -400,11 +403,21 @@ __device__ __forceinline__ void pv_pair(const TileRegs<true>& ta, const TileRegs
 #pragma unroll
     for (int h = 0; h < kHeadsPerWave; ++h) {
       st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, p[h], st[h].acc[n], 0, 0, 0);
-      if constexpr (kDyn)
+      if constexpr (kLo)
         st[h].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, plo[h], st[h].acc[n], 0, 0, 0);
     }
   }
+  (void)plo;
 }
+
+// Per-block scales: while the largest V scale a wave has met (its reference)
+// is at most this, every V value it has accumulated is at most 16 in
+// magnitude, and rounding each weight once to fp16 (relative error 2^-12)
+// moves an output by at most 2^-12 * 16 < 4e-3 (the FP8 tolerance is 1e-2;
+// the per-tensor kernel has the same bound for its own scale).  The
+// reference only grows, so from the first pair past it every pair takes the
+// hi + lo products.
+constexpr float kHiOnlyVRef = 16.0f / 448.0f;
 
 // Grid (ceil(max chunk / (16 rt)), Hkv, B); rt 16-row tiles of ceil(G / 2)
 // waves each per workgroup (a.wpt waves a tile).  Wave v takes heads 2 (v %
@@ -505,25 +518,32 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
       if (31 > first) mask_pair(s, 0, qg, pos_c);
       // pair i: K of pair i + 1 in kb[(i + 1) % 2], V of pair i in vb[i % 2],
       // its scales in sk/sv[i % 2]
-      auto step = [&](int i, TileRegs<true> (&kn)[2], TileRegs<true> (&vc)[2], float (&ski)[2],
-                      float (&svi)[2]) {
+      // per-block scales: when a tile's V scale exceeds the reference,
+      // rescale the accumulators (they hold sum p * (V scale / vref) * code)
+      // to the new one
+      auto raise_vref = [&](const float (&sa)[2], const float (&sb)[2]) {
+        const float ref =
+            fmaxf(fmaxf(vref, fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sb[0], sb[1]))), 0x1p-126f);
+        if (ref > vref) {  // wave-uniform, rare
+          if (vref > 0.0f) {
+            const float f = vref / ref;
+#pragma unroll
+            for (int h = 0; h < kHeadsPerWave; ++h)
+#pragma unroll
+              for (int nn = 0; nn < 8; ++nn) st[h].acc[nn] *= f;
+          }
+          vref = ref;
+          inv_vref = 1.0f / ref;
+        }
+      };
+      // lo: std::true_type for the hi + lo products (per-block scales with
+      // large values), std::false_type otherwise; one straight-line block each
+      auto step = [&](auto lo, int i, TileRegs<true> (&kn)[2], TileRegs<true> (&vc)[2],
+                      float (&ski)[2], float (&svi)[2]) {
+        constexpr bool kLo = decltype(lo)::value;
         const int tb = i * 2 * kBS;
         float qk[2] = {a.qk_scale, a.qk_scale}, vm[2] = {1.0f, 1.0f};
         if constexpr (kDyn) {
-          // the accumulators hold sum p * (V scale / vref) * code: when a
-          // tile's V scale exceeds the reference, rescale them to the new one
-          const float ref = fmaxf(fmaxf(vref, fmaxf(svi[0], svi[1])), 0x1p-126f);
-          if (ref > vref) {  // wave-uniform, rare
-            if (vref > 0.0f) {
-              const float f = vref / ref;
-#pragma unroll
-              for (int h = 0; h < kHeadsPerWave; ++h)
-#pragma unroll
-                for (int nn = 0; nn < 8; ++nn) st[h].acc[nn] *= f;
-            }
-            vref = ref;
-            inv_vref = 1.0f / ref;
-          }
           qk[0] = a.qk_scale * ski[0];
           qk[1] = a.qk_scale * ski[1];
           vm[0] = svi[0] * inv_vref;
@@ -536,19 +556,38 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillArgs a) {
           mask_tail_values<true>(vc[1], tb + kBS, qg, L);
         }
         f16x8 p[kHeadsPerWave], plo[kHeadsPerWave];
-        probs_pair<kDyn>(y, st, vm, p, plo);
+        probs_pair<kDyn, kLo>(y, st, vm, p, plo);
         qk_pair(kn[0], kn[1], qop, s);
         load_half_pipe<false>(kn[0], kn[1], a, tile_id(2 * i + 6), tile_id(2 * i + 7), kvh, lane);
-        pv_pair<kDyn>(vc[0], vc[1], p, plo, st);
+        pv_pair<kLo>(vc[0], vc[1], p, plo, st);
         load_half_pipe<true>(vc[0], vc[1], a, tile_id(2 * i + 4), tile_id(2 * i + 5), kvh, lane);
         scales(i + 2, ski, svi);
         if (tb + 4 * kBS - 1 > first) {  // pair i + 1 reaches past the first position
           mask_pair(s, tb + 2 * kBS, qg, pos_c);
         }
       };
-      for (int i = 0; i < np; i += 2) {
-        step(i, kb[1], vb[0], sk[0], sv[0]);
-        step(i + 1, kb[0], vb[1], sk[1], sv[1]);
+      // two pairs per iteration (the buffers alternate); with per-block
+      // scales the reference is raised to both pairs' V scales first, and
+      // the rows run one fp16 product per pair until it passes kHiOnlyVRef,
+      // then hi + lo to the end (two loops: no branch inside a pair's block)
+      int i = 0;
+      if constexpr (kDyn) {
+        for (; i < np; i += 2) {
+          raise_vref(sv[0], sv[1]);
+          if (vref > kHiOnlyVRef) break;  // wave-uniform
+          step(std::false_type{}, i, kb[1], vb[0], sk[0], sv[0]);
+          step(std::false_type{}, i + 1, kb[0], vb[1], sk[1], sv[1]);
+        }
+        for (; i < np; i += 2) {
+          raise_vref(sv[0], sv[1]);
+          step(std::true_type{}, i, kb[1], vb[0], sk[0], sv[0]);
+          step(std::true_type{}, i + 1, kb[0], vb[1], sk[1], sv[1]);
+        }
+      } else {
+        for (; i < np; i += 2) {
+          step(std::false_type{}, i, kb[1], vb[0], sk[0], sv[0]);
+          step(std::false_type{}, i + 1, kb[0], vb[1], sk[1], sv[1]);
+        }
       }
     }
   } else {
