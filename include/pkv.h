@@ -505,8 +505,8 @@ pkv_status pkv_paged_attention_decode_dynamic(
  * scale read from the arrays in place of the per-tensor scales.  Within a
  * workgroup the probabilities of a tile are multiplied by its V scale over
  * the largest V scale met so far before rounding to fp16: as one fp16 value
- * while that largest scale is at most 16/448, as an fp16 hi + lo pair after
- * it (one rounding moves an output by at most 2^-12 of the largest |V| it
+ * while that largest scale is at most 8/448, as an fp16 hi + lo pair after
+ * it (one rounding moves an output by at most 2^-11 of the largest |V| it
  * multiplies).  No workspace;
  * PKV_ERR_UNSUPPORTED for fp16 pools, PKV_ERR_INVALID_ARG for a null scale
  * array. */

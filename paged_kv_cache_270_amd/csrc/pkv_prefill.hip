@@ -411,13 +411,13 @@ __device__ __forceinline__ void pv_pair(const TileRegs<true>& ta, const TileRegs
 }
 
 // Per-block scales: while the largest V scale a wave has met (its reference)
-// is at most this, every V value it has accumulated is at most 16 in
-// magnitude, and rounding each weight once to fp16 (relative error 2^-12)
-// moves an output by at most 2^-12 * 16 < 4e-3 (the FP8 tolerance is 1e-2;
-// the per-tensor kernel has the same bound for its own scale).  The
+// is at most this, every V value it has accumulated is at most 8 in
+// magnitude, and rounding each weight once to fp16 (relative error at most
+// 2^-11) moves an output by at most 2^-11 * 8 < 4e-3 (the FP8 tolerance is
+// 1e-2; the per-tensor kernel has the same bound for its own scale).  The
 // reference only grows, so from the first pair past it every pair takes the
 // hi + lo products.
-constexpr float kHiOnlyVRef = 16.0f / 448.0f;
+constexpr float kHiOnlyVRef = 8.0f / 448.0f;
 
 // Grid (ceil(max chunk / (16 rt)), Hkv, B); rt 16-row tiles of ceil(G / 2)
 // waves each per workgroup (a.wpt waves a tile).  Wave v takes heads 2 (v %

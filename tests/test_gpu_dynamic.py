@@ -355,3 +355,45 @@ def test_large_scattered_calls_are_bit_exact():
     pool.check_equal()
     print(f"[parity] dynamic write, {T} + {scat2.size} scattered tokens x {hkv} heads: "
           "pools and scales bit-exact", flush=True)
+
+
+def test_prefill_with_block_scales_single_fp16_product_at_its_largest_values():
+    """Values clamped to [-8, 8], so every block's V scale is at most 8/448
+    and every pair takes one fp16 PV product: the error stays within
+    2^-11 * 8 < 4e-3 (fp16's unit roundoff times the largest |v|), well
+    inside the FP8 tolerance, at the largest values that path serves."""
+    NB, hkv, hq = 96, 2, 16
+    pool = DynPool(NB, hkv, 51)
+    lens = np.array([40, 333, 700], np.int32)
+    chunks = np.array([40, 200, 333], np.int32)
+    perm = np.random.default_rng(52).permutation(NB)
+    tables, pos = np.zeros((len(lens), 48), np.int32), 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // BS)
+        tables[b, :n] = perm[pos:pos + n]
+        tables[b, n:] = perm[(pos + n) % NB]
+        pos += n
+    for b, L in enumerate(lens):
+        sl = oracle.slots_for(tables, [b] * int(L), range(int(L)))
+        k = (workloads.randn_f16((int(L), hkv, D), 800 + b, "cuda").float() * 3).clamp(-8, 8)
+        v = (workloads.randn_f16((int(L), hkv, D), 810 + b, "cuda").float() * 3).clamp(-8, 8)
+        pool.write(k.half(), v.half(), sl)
+    pool.check_equal()
+    used = np.concatenate([tables[b, :-(-int(L) // BS)] for b, L in enumerate(lens)])
+    assert (pool.vsh[used] <= np.float32(8 / 448)).all()
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = workloads.randn_f16((int(qs[-1]), hq, D), 821, "cuda")
+    out = torch.empty((int(qs[-1]), hq, D), dtype=torch.float32, device="cuda")
+    sm = float(np.float32(1 / np.sqrt(D)))
+    pkv.pkv_paged_prefill_attention_dynamic(out, q, pool.kd, pool.vd, pool.ksd, pool.vsd,
+                                            torch.from_numpy(tables).cuda(),
+                                            torch.from_numpy(lens).cuda(),
+                                            torch.from_numpy(qs).cuda(), int(chunks.max()),
+                                            int(lens.max()), pool.layout, sm)
+    torch.cuda.synchronize()
+    ref = oracle.paged_prefill_attention_dynamic(q.cpu().numpy(), pool.kh, pool.vh, pool.ksh,
+                                                 pool.vsh, tables, lens, qs, hkv, sm, THREADS)
+    err = max_err(out.cpu().numpy(), ref)
+    print(f"[parity] dynamic prefill, |v| up to 8 (one fp16 product): max abs err {err:.3e}",
+          flush=True)
+    assert err <= 4e-3
